@@ -1,0 +1,221 @@
+"""Benchmark: one clustered-sparse-attention layer (all four stages) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload cog76k] [--no-cpu] [--no-dense]
+
+A step is one cold layer call on seeded synthetic Q/K/V already resident in HBM:
+cluster_q -> cluster_k (threshold-adaptive) -> select (TensorQuest + top-p) ->
+sparse_attn. The headline value is the dense-equivalent throughput
+4 H N^2 D / t_layer. Prints one JSON line (last line of stdout).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "clustered-attn layer latency (ms) + dense-equiv TFLOP/s at 75.6K tokens"
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="cog76k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense comparisons")
+    ap.add_argument("--profile-steps", action="store_true",
+                    help="only warmup + timed steps (for profiler runs)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads would be sharded across GPUs with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import clustered_sparse_attention_cosine_amd as adc
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    g = synth.generate(w, seed=args.seed)
+    log(f"generated {w.name} inputs in {time.time() - t0:.1f}s")
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v = (to_dev(g[t]) for t in "qkv")
+    nmax = w.k_max
+    cfg = adc.LayerConfig(q_clusters=w.q_clusters, k_base=w.k_base, k_max=nmax, top_p=w.top_p,
+                          iters=w.iters, init=w.init, adaptive=w.k_adaptive, seed=args.seed)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(record=None):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record is not None else None
+        if ev:
+            ev[0].record(stream)
+        Q = adc.cluster_q(q, cfg.q_clusters, cfg.iters, cfg.init, cfg.seed)
+        if ev:
+            ev[1].record(stream)
+        K = adc.cluster_k(k, v, cfg.k_base, cfg.k_max, cfg.iters, cfg.tau_mult, cfg.adaptive,
+                          cfg.init, cfg.seed)
+        if ev:
+            ev[2].record(stream)
+        S = adc.select(Q["qrep"], K, cfg.top_p)
+        if ev:
+            ev[3].record(stream)
+        out, lse = adc.sparse_attn(q, Q["perm"], Q["offsets"], K["k_perm"], K["v_perm"],
+                                   K["offsets"], S["mask"])
+        if ev:
+            ev[4].record(stream)
+            record.append(ev)
+        return Q, K, S, out
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{args.warmup} done")
+    events = []
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        Q, K, S, out = step(events)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    log(f"timed {args.steps} steps in {t_total:.3f}s")
+    ms = t_total * 1e3 / args.steps
+    stage_names = ["cluster_q", "cluster_k", "select", "sparse_attn"]
+    stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events]))
+                for i, n in enumerate(stage_names)}
+
+    # workload facts from the last step
+    sizes_q = Q["sizes"].double()
+    sel_keys = S["sel_keys"].double()
+    pairs = float((sizes_q * sel_keys).sum().item())
+    density = pairs / (w.B * w.H * float(w.N) ** 2)
+    slots = K["n_clusters"].flatten().tolist()
+    full_heads = int(K["full"].sum().item())
+    dense_flops = w.dense_flops()
+    value = dense_flops / (ms * 1e-3) / 1e12
+    attn_flops = 4.0 * w.D * pairs
+    attn_tflops = attn_flops / (stage_ms["sparse_attn"] * 1e-3) / 1e12
+    if args.profile_steps:
+        log(json.dumps(dict(ms_per_step=ms, stages_ms=stage_ms)))
+        return
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s (dense-equivalent, 4*H*N^2*D / layer time)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded smooth fields + noise, shapes of the workload)",
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H} N={w.N} D={w.D} grid={w.grid}",
+                   "q_clusters": w.q_clusters,
+                   "k_clusters": f"adaptive {{{w.k_base},{2 * w.k_base},{4 * w.k_base}}}"
+                   if w.k_adaptive else str(w.k_base),
+                   "top_p": w.top_p, "lloyd_iters": w.iters, "init": w.init,
+                   "layer_ms": round(ms, 4)},
+        "stages_ms": {k2: round(v2, 4) for k2, v2 in stage_ms.items()},
+        "selection": {"pairs": pairs, "density": round(density, 5), "full_heads": full_heads,
+                      "k_slots": {str(s): slots.count(s) for s in sorted(set(slots))}},
+        "roofline": {"kernel": "sparse_attn (run build + work list + attention)",
+                     "bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops": attn_flops},
+    }
+
+    if not args.no_dense:
+        result["dense"] = dense_compare(torch, adc, q, k, v, w, dev, stream)
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, g, args.seed)
+
+    print(json.dumps(result), flush=True)
+
+
+def dense_compare(torch, adc, q, k, v, w, dev, stream):
+    """Dense attention on the same GPU: this library's kernel with everything
+    selected, and PyTorch's fused SDPA (flash backend only)."""
+    res = {}
+    B, H, N, D = q.shape
+    ident = torch.arange(N, dtype=torch.int32, device=dev).repeat(B, H, 1).contiguous()
+    offs = torch.tensor([0, N], dtype=torch.int32, device=dev).repeat(B, H, 1).contiguous()
+    mask = torch.ones(B, H, 1, 1, dtype=torch.int32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    adc.sparse_attn(q, ident, offs, k, v, offs, mask, want_lse=False)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    adc.sparse_attn(q, ident, offs, k, v, offs, mask, want_lse=False)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1)
+    res["own_select_all_ms"] = round(t, 3)
+    res["own_select_all_tflops"] = round(w.dense_flops() / (t * 1e-3) / 1e12, 2)
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            torch.nn.functional.scaled_dot_product_attention(q, k, v)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            torch.nn.functional.scaled_dot_product_attention(q, k, v)
+            e1.record(stream)
+            torch.cuda.synchronize()
+        t = e0.elapsed_time(e1)
+        res["torch_sdpa_flash_ms"] = round(t, 3)
+        res["torch_sdpa_flash_tflops"] = round(w.dense_flops() / (t * 1e-3) / 1e12, 2)
+    except Exception as exc:  # flash backend unavailable: report, never fall back to math
+        res["torch_sdpa_flash_ms"] = None
+        res["torch_sdpa_error"] = str(exc)[:200]
+    return res
+
+
+def cpu_baseline(w, g, seed):
+    """The CPU oracle (as it stands) on head 0 of the same workload, all four
+    stages; scaled to the dense-equivalent unit as (4 N^2 D) / t_head."""
+    import oracle
+    import synth
+    threads = len(os.sched_getaffinity(0))
+    threads = min(threads, 16)
+    oracle.set_threads(threads)
+    qh, kh, vh = (synth.as_f32(g[t][0, 0]) for t in "qkv")
+    t0 = time.perf_counter()
+    oracle.layer_head(qh, kh, vh, cq=w.q_clusters, m0=w.k_base, nmax=w.k_max, iters=w.iters,
+                      top_p=w.top_p, init=w.init, adaptive=w.k_adaptive, seed=seed, h=0)
+    t = time.perf_counter() - t0
+    per_head_flops = 4.0 * float(w.N) ** 2 * w.D
+    return {"value": round(per_head_flops / t / 1e12, 6), "unit": "TFLOP/s (dense-equivalent)",
+            "cores": oracle.get_threads(), "kind": "oracle",
+            "sample": f"head 0 of {w.H}, all four stages, N={w.N}: {t:.1f} s "
+                      f"(layer estimate {t * w.H:.0f} s)",
+            "seconds": round(t, 2)}
+
+
+if __name__ == "__main__":
+    main()

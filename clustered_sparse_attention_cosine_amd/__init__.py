@@ -1,0 +1,303 @@
+"""MI355X (gfx950) clustered sparse attention: Python binding of libadacluster.so.
+
+Thin ctypes marshalling over the C ABI in include/adacluster.h: every stage runs
+in the library's HIP kernels; PyTorch only allocates device memory and supplies
+the current stream. There is no CPU fallback: if the library is missing, or a
+tensor is not on a ROCm device, the calls raise.
+
+Stages (AdaCluster paper, arXiv 2604.18348v1):
+    cluster_q     section 3.1, Algorithm 3 step 1
+    cluster_k     section 3.2.2 Algorithm 1, section 4.1 (tau)
+    select        section 3.2.3 Eq. (1)/(2), Algorithm 3 steps 6-7
+    sparse_attn   Algorithm 3 steps 8-9
+    layer         the four in order
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libadacluster.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "adacluster.h")
+
+ADC_F32, ADC_BF16 = 0, 1
+INIT = {"kmeanspp": 0, "sample": 1, "caller": 2}
+SCORE = {"quest": 0, "centroid": 1}
+RULE = {"topp": 0, "topk": 1}
+STATUS = {0: "ADC_OK", -1: "ADC_EINVAL", -2: "ADC_ESHAPE", -3: "ADC_EDTYPE",
+          -4: "ADC_EWORKSPACE", -5: "ADC_EHIP", -6: "ADC_EUNSUPPORTED"}
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class QParams(ctypes.Structure):
+    _fields_ = [("n_clusters", ctypes.c_int32), ("iters", ctypes.c_int32),
+                ("init", ctypes.c_int32), ("pad_", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+
+
+class KParams(ctypes.Structure):
+    _fields_ = [("base_clusters", ctypes.c_int32), ("max_clusters", ctypes.c_int32),
+                ("iters", ctypes.c_int32), ("tau_mult", ctypes.c_float),
+                ("adaptive", ctypes.c_int32), ("init", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+
+
+_lib = None
+_VP = ctypes.c_void_p
+_SZ = ctypes.c_size_t
+_I32 = ctypes.c_int32
+_F32 = ctypes.c_float
+_SIGS = {
+    "adacluster_abi_version": (_I32, []),
+    "adacluster_last_error": (ctypes.c_char_p, []),
+    "adacluster_cluster_q_workspace": (_SZ, [_VP, _VP]),
+    "adacluster_cluster_q": (_I32, [_VP, _VP] + [_VP] * 8 + [_VP, _SZ, _VP]),
+    "adacluster_cluster_k_workspace": (_SZ, [_VP, _VP]),
+    "adacluster_cluster_k": (_I32, [_VP, _VP] + [_VP] * 16 + [_VP, _SZ, _VP]),
+    "adacluster_select_workspace": (_SZ, [_VP, _I32, _I32]),
+    "adacluster_select": (_I32, [_VP, _I32, _I32] + [_VP] * 7 + [_I32, _I32, _F32, _I32, _F32]
+                          + [_VP, _VP, _VP, _SZ, _VP]),
+    "adacluster_sparse_attn_workspace": (_SZ, [_VP, _I32, _I32]),
+    "adacluster_sparse_attn": (_I32, [_VP, _I32, _I32] + [_VP] * 7 + [_F32, _VP, _VP, _VP, _SZ, _VP]),
+    "adacluster_assign_workspace": (_SZ, [_VP, _I32]),
+    "adacluster_assign": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "adacluster_permute_workspace": (_SZ, [_VP, _I32]),
+    "adacluster_permute": (_I32, [_VP, _I32] + [_VP] * 11 + [_VP, _SZ, _VP]),
+}
+
+
+def lib():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m clustered_sparse_attention_cosine_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_symbols():
+    """Names of the entry points declared in include/adacluster.h."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(adacluster_\w+)\s*\(", text)))
+
+
+class AdaClusterError(RuntimeError):
+    pass
+
+
+def _check(status):
+    if status != 0:
+        msg = lib().adacluster_last_error().decode(errors="replace")
+        raise AdaClusterError(f"{STATUS.get(status, status)}: {msg}")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _shape(x: torch.Tensor) -> Shape:
+    if x.dim() != 4:
+        raise ValueError("expected a [B, H, N, D] tensor")
+    if not x.is_cuda:
+        raise ValueError("tensors must live on a ROCm device (no CPU path exists)")
+    if not x.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    if x.dtype == torch.bfloat16:
+        dt = ADC_BF16
+    elif x.dtype == torch.float32:
+        dt = ADC_F32
+    else:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    B, H, N, D = x.shape
+    return Shape(B, H, N, D, dt)
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------- stages
+def cluster_q(q, n_clusters, iters=5, init="sample", seed=0, init_centroids=None):
+    sh = _shape(q)
+    B, H, N, D = q.shape
+    dev = q.device
+    prm = QParams(n_clusters, iters, INIT[init], 0, seed & (2**64 - 1))
+    ws_n = lib().adacluster_cluster_q_workspace(ctypes.byref(sh), ctypes.byref(prm))
+    if ws_n == 0:
+        raise AdaClusterError("invalid cluster_q arguments: " + lib().adacluster_last_error().decode())
+    out = dict(
+        assign=torch.empty(B, H, N, dtype=torch.int32, device=dev),
+        centroids=torch.empty(B, H, n_clusters, D, dtype=torch.float32, device=dev),
+        sizes=torch.empty(B, H, n_clusters, dtype=torch.int32, device=dev),
+        qrep=torch.empty(B, H, n_clusters, D, dtype=torch.float32, device=dev),
+        perm=torch.empty(B, H, N, dtype=torch.int32, device=dev),
+        offsets=torch.empty(B, H, n_clusters + 1, dtype=torch.int32, device=dev),
+    )
+    ws = _workspace(ws_n, dev)
+    ic = None if init_centroids is None else init_centroids.contiguous().float()
+    _check(lib().adacluster_cluster_q(ctypes.byref(sh), ctypes.byref(prm), _p(q), _p(ic),
+                                      _p(out["assign"]), _p(out["centroids"]), _p(out["sizes"]),
+                                      _p(out["qrep"]), _p(out["perm"]), _p(out["offsets"]),
+                                      _p(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def cluster_k(k, v, base_clusters, max_clusters=None, iters=5, tau_mult=1.5, adaptive=True,
+              init="sample", seed=0, init_centroids=None):
+    sh = _shape(k)
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k and v must share shape and dtype")
+    _shape(v)
+    B, H, N, D = k.shape
+    dev = k.device
+    nmax = max_clusters if max_clusters is not None else (4 * base_clusters if adaptive else base_clusters)
+    prm = KParams(base_clusters, nmax, iters, tau_mult, int(bool(adaptive)), INIT[init],
+                  seed & (2**64 - 1))
+    ws_n = lib().adacluster_cluster_k_workspace(ctypes.byref(sh), ctypes.byref(prm))
+    if ws_n == 0:
+        raise AdaClusterError("invalid cluster_k arguments: " + lib().adacluster_last_error().decode())
+    out = dict(
+        n_clusters=torch.empty(B, H, dtype=torch.int32, device=dev),
+        full=torch.empty(B, H, dtype=torch.uint8, device=dev),
+        tau=torch.empty(B, H, dtype=torch.float32, device=dev),
+        assign=torch.empty(B, H, N, dtype=torch.int32, device=dev),
+        centroids=torch.empty(B, H, nmax, D, dtype=torch.float32, device=dev),
+        sizes=torch.empty(B, H, nmax, dtype=torch.int32, device=dev),
+        kmax=torch.empty(B, H, nmax, D, dtype=k.dtype, device=dev),
+        kmin=torch.empty(B, H, nmax, D, dtype=k.dtype, device=dev),
+        perm=torch.empty(B, H, N, dtype=torch.int32, device=dev),
+        offsets=torch.empty(B, H, nmax + 1, dtype=torch.int32, device=dev),
+        k_perm=torch.empty_like(k),
+        v_perm=torch.empty_like(v),
+        stage_sizes=torch.empty(B, H, 8, dtype=torch.int32, device=dev),
+    )
+    ws = _workspace(ws_n, dev)
+    ic = None if init_centroids is None else init_centroids.contiguous().float()
+    _check(lib().adacluster_cluster_k(
+        ctypes.byref(sh), ctypes.byref(prm), _p(k), _p(v), _p(ic), _p(out["n_clusters"]),
+        _p(out["full"]), _p(out["tau"]), _p(out["assign"]), _p(out["centroids"]), _p(out["sizes"]),
+        _p(out["kmax"]), _p(out["kmin"]), _p(out["perm"]), _p(out["offsets"]), _p(out["k_perm"]),
+        _p(out["v_perm"]), _p(out["stage_sizes"]), _p(ws), ws.numel(), _stream(dev)))
+    out["max_clusters"] = nmax
+    return out
+
+
+def select(qrep, K, top_p=0.9, score="quest", rule="topp", top_k=64, scale=None):
+    """K: the dict returned by cluster_k (or the same keys)."""
+    B, H, Cq, D = qrep.shape
+    kmax = K["kmax"]
+    Ck = kmax.shape[2]
+    sh = Shape(B, H, 1, D, ADC_BF16 if kmax.dtype == torch.bfloat16 else ADC_F32)
+    dev = qrep.device
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    words = (Ck + 31) // 32
+    out = dict(mask=torch.empty(B, H, Cq, words, dtype=torch.int32, device=dev),
+               sel_keys=torch.empty(B, H, Cq, dtype=torch.int32, device=dev))
+    ws = _workspace(lib().adacluster_select_workspace(ctypes.byref(sh), Cq, Ck), dev)
+    _check(lib().adacluster_select(
+        ctypes.byref(sh), Cq, Ck, _p(qrep.contiguous()), _p(kmax), _p(K["kmin"]),
+        _p(K.get("centroids")), _p(K["sizes"]), _p(K["n_clusters"]), _p(K["full"]), SCORE[score],
+        RULE[rule], float(top_p), int(top_k), float(scale), _p(out["mask"]), _p(out["sel_keys"]),
+        _p(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def sparse_attn(q, q_perm, q_offsets, k_perm, v_perm, k_offsets, sel_mask, scale=None,
+                out=None, lse=None, want_lse=True):
+    sh = _shape(q)
+    B, H, N, D = q.shape
+    Cq = q_offsets.shape[-1] - 1
+    Ck = k_offsets.shape[-1] - 1
+    dev = q.device
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    ws = _workspace(lib().adacluster_sparse_attn_workspace(ctypes.byref(sh), Cq, Ck), dev)
+    _check(lib().adacluster_sparse_attn(
+        ctypes.byref(sh), Cq, Ck, _p(q), _p(q_perm), _p(q_offsets), _p(k_perm), _p(v_perm),
+        _p(k_offsets), _p(sel_mask), float(scale), _p(out), _p(lse), _p(ws), ws.numel(),
+        _stream(dev)))
+    return out, lse
+
+
+def assign(x, centroids, valid=None, normalize=False):
+    sh = _shape(x)
+    B, H, N, D = x.shape
+    M = centroids.shape[2]
+    dev = x.device
+    lab = torch.empty(B, H, N, dtype=torch.int32, device=dev)
+    ws = _workspace(lib().adacluster_assign_workspace(ctypes.byref(sh), M), dev)
+    _check(lib().adacluster_assign(ctypes.byref(sh), M, int(bool(normalize)), _p(x),
+                                   _p(centroids.contiguous().float()), _p(valid), _p(lab), _p(ws),
+                                   ws.numel(), _stream(dev)))
+    return lab
+
+
+def permute(labels, M, x, v=None):
+    sh = _shape(x)
+    B, H, N, D = x.shape
+    dev = x.device
+    out = dict(sizes=torch.empty(B, H, M, dtype=torch.int32, device=dev),
+               offsets=torch.empty(B, H, M + 1, dtype=torch.int32, device=dev),
+               perm=torch.empty(B, H, N, dtype=torch.int32, device=dev),
+               means=torch.zeros(B, H, M, D, dtype=torch.float32, device=dev),
+               xmax=torch.empty(B, H, M, D, dtype=x.dtype, device=dev),
+               xmin=torch.empty(B, H, M, D, dtype=x.dtype, device=dev),
+               x_perm=torch.empty_like(x),
+               v_perm=None if v is None else torch.empty_like(v))
+    ws = _workspace(lib().adacluster_permute_workspace(ctypes.byref(sh), M), dev)
+    _check(lib().adacluster_permute(ctypes.byref(sh), M, _p(labels.contiguous()), _p(x), _p(v),
+                                    _p(out["sizes"]), _p(out["offsets"]), _p(out["perm"]),
+                                    _p(out["means"]), _p(out["xmax"]), _p(out["xmin"]),
+                                    _p(out["x_perm"]), _p(out["v_perm"]), _p(ws), ws.numel(),
+                                    _stream(dev)))
+    return out
+
+
+@dataclasses.dataclass
+class LayerConfig:
+    q_clusters: int
+    k_base: int
+    k_max: int
+    top_p: float = 0.9
+    iters: int = 5
+    init: str = "sample"
+    adaptive: bool = True
+    tau_mult: float = 1.5
+    seed: int = 0
+    score: str = "quest"
+    rule: str = "topp"
+    top_k: int = 64
+
+
+def layer(q, k, v, cfg: LayerConfig):
+    """One clustered-sparse-attention layer (Algorithm 3): returns (out, lse, state)."""
+    Q = cluster_q(q, cfg.q_clusters, cfg.iters, cfg.init, cfg.seed)
+    K = cluster_k(k, v, cfg.k_base, cfg.k_max, cfg.iters, cfg.tau_mult, cfg.adaptive, cfg.init,
+                  cfg.seed)
+    S = select(Q["qrep"], K, cfg.top_p, cfg.score, cfg.rule, cfg.top_k)
+    out, lse = sparse_attn(q, Q["perm"], Q["offsets"], K["k_perm"], K["v_perm"], K["offsets"],
+                           S["mask"])
+    return out, lse, dict(Q=Q, K=K, S=S)

@@ -1,0 +1,59 @@
+"""Build the gfx950 HIP library in-tree: clustered_sparse_attention_cosine_amd/libadacluster.so.
+
+    python -m clustered_sparse_attention_cosine_amd.build
+
+Every source is compiled by hipcc for gfx950 only; packed-f32 instructions are
+disabled for all device code.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libadacluster.so")
+SOURCES = ["kmeans.hip", "permute.hip", "select.hip", "attn.hip", "api.cpp"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", os.path.join(ROOT, "include")]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link the shared library; returns its path."""
+    with tempfile.TemporaryDirectory(prefix="adc_build_") as tmp:
+        procs = []
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+            objs.append(obj)
+        failed = []
+        for src, p in procs:
+            out, _ = p.communicate()
+            text = out.decode(errors="replace")
+            # hipcc's host pass does not know the device-only feature flag
+            lines = [ln for ln in text.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
+            if p.returncode != 0:
+                failed.append(src)
+                print("\n".join(lines), file=sys.stderr)
+            elif verbose and lines:
+                print("\n".join(lines))
+        if failed:
+            raise RuntimeError("hipcc failed for: " + ", ".join(failed))
+        tmp_lib = LIB + ".tmp"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_lib]
+        subprocess.run(cmd, check=True, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+        os.replace(tmp_lib, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

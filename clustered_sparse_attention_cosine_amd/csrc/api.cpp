@@ -1,0 +1,558 @@
+// C ABI of the clustered sparse attention library: argument checks (all before
+// the first launch), workspace carving and the order of kernel launches for
+// each stage. The method follows "AdaCluster: Adaptive Query-Key Clustering for
+// Sparse Attention in Video Generation" (arXiv 2604.18348v1); the per-stage
+// citations are in include/adacluster.h and next to each kernel.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+#include <algorithm>
+
+#include "../../include/adacluster.h"
+#include "kernels.hpp"
+
+using namespace adc;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+#define HIPCHK(expr)                                                                      \
+    do {                                                                                  \
+        hipError_t e_ = (expr);                                                           \
+        if (e_ != hipSuccess) return fail(ADC_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+constexpr int MAX_CLUSTERS = 8192;
+constexpr int MAX_N = 1 << 21;
+
+// Bump allocator over the caller's workspace (256-byte aligned pieces). With
+// base == nullptr it only measures.
+struct Carver {
+    char* base;
+    size_t used = 0;
+    explicit Carver(void* b) : base((char*)b) {}
+    template <typename T>
+    T* take(size_t count) {
+        size_t off = (used + 255) & ~size_t(255);
+        used = off + count * sizeof(T);
+        return base ? reinterpret_cast<T*>(base + off) : nullptr;
+    }
+};
+
+int32_t check_shape(const adc_shape* s) {
+    if (!s) return fail(ADC_EINVAL, "shape is NULL");
+    if (s->B < 1 || s->H < 1 || s->N < 1)
+        return fail(ADC_ESHAPE, "B, H, N must be >= 1 (got %d, %d, %d)", s->B, s->H, s->N);
+    if (s->N > MAX_N) return fail(ADC_ESHAPE, "N = %d exceeds %d", s->N, MAX_N);
+    if (s->D != 64 && s->D != 128) return fail(ADC_ESHAPE, "D must be 64 or 128 (got %d)", s->D);
+    if (s->dtype != ADC_F32 && s->dtype != ADC_BF16)
+        return fail(ADC_EDTYPE, "dtype must be ADC_F32 or ADC_BF16 (got %d)", s->dtype);
+    if ((int64_t)s->B * s->H > 65535) return fail(ADC_ESHAPE, "B*H = %lld exceeds 65535",
+                                                   (long long)s->B * s->H);
+    return ADC_OK;
+}
+
+int32_t check_clusters(const char* what, int32_t c) {
+    if (c < 1 || c > MAX_CLUSTERS) return fail(ADC_ESHAPE, "%s = %d outside [1, %d]", what, c, MAX_CLUSTERS);
+    return ADC_OK;
+}
+
+Prob make_prob(const adc_shape* s) {
+    Prob p;
+    p.BH = s->B * s->H;
+    p.H = s->H;
+    p.N = s->N;
+    p.D = s->D;
+    p.bf16 = s->dtype == ADC_BF16;
+    return p;
+}
+
+#define REQ(ptr) \
+    if (!(ptr)) return fail(ADC_EINVAL, "%s is NULL", #ptr)
+
+// ------------------------------------------------------------------ workspace plans
+struct KmeansWs {
+    float* inv_norm = nullptr;
+    int32_t* flag_list = nullptr;
+    int32_t* flag_count = nullptr;
+    uint8_t* valid = nullptr;
+    uint16_t* c_hi = nullptr;
+    uint16_t* c_lo = nullptr;
+    float* cn2 = nullptr;
+    float* sums = nullptr;
+    int32_t* cnt = nullptr;
+    float* xhat = nullptr;
+    double* d2 = nullptr;
+    uint8_t* chosen = nullptr;
+    int32_t* hist = nullptr;
+};
+
+void plan_kmeans(Carver& c, const Prob& p, int cap, bool want_inv, bool kpp, bool want_xhat,
+                 KmeansWs& w) {
+    const size_t bhn = (size_t)p.BH * p.N;
+    const size_t bhc = (size_t)p.BH * cap;
+    if (want_inv) w.inv_norm = c.take<float>(bhn);
+    w.flag_list = c.take<int32_t>(bhn);
+    w.flag_count = c.take<int32_t>(p.BH);
+    w.valid = c.take<uint8_t>(bhc);
+    w.c_hi = c.take<uint16_t>(bhc * p.D);
+    w.c_lo = c.take<uint16_t>(bhc * p.D);
+    w.cn2 = c.take<float>(bhc);
+    w.sums = c.take<float>(bhc * p.D);
+    w.cnt = c.take<int32_t>(bhc);
+    w.hist = c.take<int32_t>(bhc);
+    if (kpp) {
+        if (want_xhat) w.xhat = c.take<float>(bhn * p.D);
+        w.d2 = c.take<double>(bhn);
+        w.chosen = c.take<uint8_t>(bhn);
+    }
+}
+
+struct StageWs {
+    StageState st{};
+    int32_t* labels_u = nullptr;
+};
+
+void plan_stages(Carver& c, const Prob& p, StageWs& w) {
+    const size_t bhn = (size_t)p.BH * p.N;
+    w.st.nu = c.take<int32_t>(p.BH);
+    w.st.slots = c.take<int32_t>(p.BH);
+    w.st.full = c.take<uint8_t>(p.BH);
+    w.st.active = c.take<uint8_t>(p.BH);
+    w.st.n_stages = c.take<int32_t>(p.BH);
+    w.st.tau = c.take<double>(p.BH);
+    w.st.u_a = c.take<int32_t>(bhn);
+    w.st.u_b = c.take<int32_t>(bhn);
+    w.st.dist = c.take<double>(bhn);
+    w.labels_u = c.take<int32_t>(bhn);
+}
+
+CentView make_view(float* cent, const KmeansWs& w, int cap, int base, int m) {
+    CentView v;
+    v.cent = cent;
+    v.valid = w.valid;
+    v.c_hi = w.c_hi;
+    v.c_lo = w.c_lo;
+    v.cn2 = w.cn2;
+    v.sums = w.sums;
+    v.cnt = w.cnt;
+    v.cap = cap;
+    v.base = base;
+    v.m = m;
+    return v;
+}
+
+// Lloyd rounds on one centroid view. With final_update the last round also
+// moves the centres (multi-stage stages need the stage centres); otherwise the
+// last centres are left to the exact member means of the layout pass.
+hipError_t lloyd(const Prob& p, const void* x, int normalize, RowSet rs, const float* inv_norm,
+                 CentView cv, int iters, bool final_update, int32_t* labels, const KmeansWs& w,
+                 hipStream_t s) {
+    hipError_t e;
+    for (int it = 0; it < iters; ++it) {
+        if ((e = launch_assign(p, x, rs, inv_norm, cv, nullptr, labels, w.flag_list, w.flag_count, s)))
+            return e;
+        if ((e = launch_refine(p, x, normalize, rs, cv, nullptr, w.flag_list, w.flag_count, labels, s)))
+            return e;
+        if (it + 1 < iters || final_update) {
+            if ((e = launch_update_accum(p, x, rs, inv_norm, labels, cv, s))) return e;
+            if ((e = launch_finalize(p, cv, rs.active, 1, s))) return e;
+        }
+    }
+    return hipSuccess;
+}
+
+hipError_t init_centres(const Prob& p, const void* x, int normalize, RowSet rs, CentView cv, int init,
+                        const float* init_cent, uint64_t seed, uint32_t tensor, uint32_t stage,
+                        const KmeansWs& w, hipStream_t s) {
+    hipError_t e = hipSuccess;
+    if (init == ADC_INIT_SAMPLE) {
+        e = launch_init_sample(p, x, normalize, rs, cv, seed, tensor, stage, s);
+    } else if (init == ADC_INIT_KMEANSPP) {
+        const float* xf = nullptr;
+        if (normalize) {
+            if ((e = launch_normalize(p, x, w.xhat, s))) return e;
+            xf = w.xhat;
+        }
+        e = launch_init_kmeanspp(p, x, xf, rs, cv, seed, tensor, stage, w.d2, w.chosen, s);
+    } else {
+        // caller centres: [BH][m][D] copied into slots [base, base + m)
+        for (int bh = 0; bh < p.BH; ++bh) {
+            e = hipMemcpyAsync(cv.cent + ((size_t)bh * cv.cap + cv.base) * p.D,
+                               init_cent + (size_t)bh * cv.m * p.D, sizeof(float) * cv.m * p.D,
+                               hipMemcpyDeviceToDevice, s);
+            if (e) return e;
+            e = fill_u8(cv.valid + (size_t)bh * cv.cap + cv.base, cv.m, 1, s);
+            if (e) return e;
+        }
+    }
+    return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t adacluster_abi_version(void) { return ADACLUSTER_ABI_VERSION; }
+
+const char* adacluster_last_error(void) { return g_err; }
+
+// ====================================================================== cluster_q
+static int32_t check_q(const adc_shape* shape, const adc_q_params* prm) {
+    int32_t st = check_shape(shape);
+    if (st) return st;
+    if (!prm) return fail(ADC_EINVAL, "params is NULL");
+    if ((st = check_clusters("n_clusters", prm->n_clusters))) return st;
+    if (prm->iters < 1 || prm->iters > 1000) return fail(ADC_EINVAL, "iters = %d outside [1, 1000]", prm->iters);
+    if (prm->init < 0 || prm->init > 2) return fail(ADC_EINVAL, "init = %d unknown", prm->init);
+    return ADC_OK;
+}
+
+static void plan_q(Carver& c, const adc_shape* shape, const adc_q_params* prm, KmeansWs& w) {
+    Prob p = make_prob(shape);
+    plan_kmeans(c, p, prm->n_clusters, true, prm->init == ADC_INIT_KMEANSPP, true, w);
+}
+
+size_t adacluster_cluster_q_workspace(const adc_shape* shape, const adc_q_params* prm) {
+    if (check_q(shape, prm)) return 0;
+    Carver c(nullptr);
+    KmeansWs w;
+    plan_q(c, shape, prm, w);
+    return c.used + 256;
+}
+
+int32_t adacluster_cluster_q(const adc_shape* shape, const adc_q_params* prm, const void* q,
+                             const float* init_centroids, int32_t* assign, float* centroids,
+                             int32_t* sizes, float* qrep, int32_t* perm, int32_t* offsets,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    int32_t st = check_q(shape, prm);
+    if (st) return st;
+    REQ(q); REQ(assign); REQ(centroids); REQ(sizes); REQ(qrep); REQ(perm); REQ(offsets); REQ(workspace);
+    if (prm->init == ADC_INIT_CALLER && !init_centroids)
+        return fail(ADC_EINVAL, "init == ADC_INIT_CALLER needs init_centroids");
+    if (workspace_bytes < adacluster_cluster_q_workspace(shape, prm))
+        return fail(ADC_EWORKSPACE, "workspace of %zu bytes is below the %zu required", workspace_bytes,
+                    adacluster_cluster_q_workspace(shape, prm));
+    hipStream_t s = (hipStream_t)stream;
+    Prob p = make_prob(shape);
+    const int Cq = prm->n_clusters;
+    Carver c(workspace);
+    KmeansWs w;
+    plan_q(c, shape, prm, w);
+
+    HIPCHK(launch_inv_norm(p, q, w.inv_norm, s));
+    HIPCHK(fill_i32((int32_t*)w.sums, (int64_t)p.BH * Cq * p.D, 0, s));
+    HIPCHK(fill_i32(w.cnt, (int64_t)p.BH * Cq, 0, s));
+    CentView cv = make_view(centroids, w, Cq, 0, Cq);
+    RowSet all{nullptr, nullptr, nullptr};
+    HIPCHK(init_centres(p, q, 1, all, cv, prm->init, init_centroids, prm->seed, TENSOR_Q, 0, w, s));
+    HIPCHK(launch_finalize(p, cv, nullptr, 0, s));
+    HIPCHK(lloyd(p, q, 1, all, w.inv_norm, cv, prm->iters, false, assign, w, s));
+    HIPCHK(launch_histogram(p, assign, Cq, w.hist, s));
+    HIPCHK(launch_scan_offsets(p, w.hist, Cq, sizes, offsets, s));
+    HIPCHK(launch_stable_rank(p, assign, Cq, offsets, perm, s));
+    HIPCHK(launch_gather_stats(p, Cq, offsets, perm, q, nullptr, 1, centroids, qrep, nullptr,
+                               nullptr, nullptr, nullptr, s));
+    return ADC_OK;
+}
+
+// ====================================================================== cluster_k
+static int32_t check_k(const adc_shape* shape, const adc_k_params* prm) {
+    int32_t st = check_shape(shape);
+    if (st) return st;
+    if (!prm) return fail(ADC_EINVAL, "params is NULL");
+    if ((st = check_clusters("base_clusters", prm->base_clusters))) return st;
+    if ((st = check_clusters("max_clusters", prm->max_clusters))) return st;
+    if (prm->max_clusters < prm->base_clusters)
+        return fail(ADC_ESHAPE, "max_clusters (%d) < base_clusters (%d)", prm->max_clusters,
+                    prm->base_clusters);
+    if (prm->iters < 1 || prm->iters > 1000) return fail(ADC_EINVAL, "iters = %d outside [1, 1000]", prm->iters);
+    if (prm->init < 0 || prm->init > 2) return fail(ADC_EINVAL, "init = %d unknown", prm->init);
+    if (!(prm->tau_mult >= 0.0f) || prm->tau_mult > 1e6f)
+        return fail(ADC_EINVAL, "tau_mult must be a finite value >= 0");
+    if (prm->adaptive && prm->init == ADC_INIT_CALLER)
+        return fail(ADC_EUNSUPPORTED, "caller centres need adaptive == 0 (warm steps keep counts fixed)");
+    return ADC_OK;
+}
+
+static void plan_k(Carver& c, const adc_shape* shape, const adc_k_params* prm, KmeansWs& w,
+                   StageWs& sw) {
+    Prob p = make_prob(shape);
+    plan_kmeans(c, p, prm->max_clusters, false, prm->init == ADC_INIT_KMEANSPP, false, w);
+    if (prm->adaptive) plan_stages(c, p, sw);
+}
+
+size_t adacluster_cluster_k_workspace(const adc_shape* shape, const adc_k_params* prm) {
+    if (check_k(shape, prm)) return 0;
+    Carver c(nullptr);
+    KmeansWs w;
+    StageWs sw;
+    plan_k(c, shape, prm, w, sw);
+    return c.used + 256;
+}
+
+int32_t adacluster_cluster_k(const adc_shape* shape, const adc_k_params* prm, const void* k,
+                             const void* v, const float* init_centroids, int32_t* n_clusters,
+                             uint8_t* full_attn, float* tau, int32_t* assign, float* centroids,
+                             int32_t* sizes, void* kmax, void* kmin, int32_t* perm,
+                             int32_t* offsets, void* k_perm, void* v_perm, int32_t* stage_sizes,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    int32_t st = check_k(shape, prm);
+    if (st) return st;
+    REQ(k); REQ(v); REQ(n_clusters); REQ(full_attn); REQ(tau); REQ(assign); REQ(centroids);
+    REQ(sizes); REQ(kmax); REQ(kmin); REQ(perm); REQ(offsets); REQ(k_perm); REQ(v_perm);
+    REQ(workspace);
+    if (prm->init == ADC_INIT_CALLER && !init_centroids)
+        return fail(ADC_EINVAL, "init == ADC_INIT_CALLER needs init_centroids");
+    const size_t need = adacluster_cluster_k_workspace(shape, prm);
+    if (workspace_bytes < need)
+        return fail(ADC_EWORKSPACE, "workspace of %zu bytes is below the %zu required", workspace_bytes, need);
+    hipStream_t s = (hipStream_t)stream;
+    Prob p = make_prob(shape);
+    const int nmax = prm->max_clusters, m0 = prm->base_clusters;
+    Carver c(workspace);
+    KmeansWs w;
+    StageWs sw;
+    plan_k(c, shape, prm, w, sw);
+
+    HIPCHK(fill_i32((int32_t*)centroids, (int64_t)p.BH * nmax * p.D, 0, s));
+    HIPCHK(fill_u8(w.valid, (int64_t)p.BH * nmax, 0, s));
+    HIPCHK(fill_i32((int32_t*)w.sums, (int64_t)p.BH * nmax * p.D, 0, s));
+    HIPCHK(fill_i32(w.cnt, (int64_t)p.BH * nmax, 0, s));
+    RowSet all{nullptr, nullptr, nullptr};
+
+    if (!prm->adaptive) {
+        CentView cv = make_view(centroids, w, nmax, 0, m0);
+        HIPCHK(init_centres(p, k, 0, all, cv, prm->init, init_centroids, prm->seed, TENSOR_K, 0, w, s));
+        HIPCHK(launch_finalize(p, cv, nullptr, 0, s));
+        HIPCHK(lloyd(p, k, 0, all, nullptr, cv, prm->iters, false, assign, w, s));
+        HIPCHK(launch_fixed_info(p.BH, p.N, m0, n_clusters, full_attn, tau, stage_sizes, s));
+    } else {
+        StageState S = sw.st;
+        S.stage_sizes = stage_sizes;
+        HIPCHK(launch_stage_reset(p, S, s));
+        int base = 0, t = 0;
+        int32_t* u_cur = S.u_a;
+        int32_t* u_next = S.u_b;
+        while (base < nmax) {
+            int mt = (t == 0) ? m0 : (m0 << std::min(t - 1, 20));
+            mt = std::min(mt, nmax - base);
+            HIPCHK(launch_stage_begin(p, S, t, nmax, s));
+            RowSet rs{t == 0 ? nullptr : u_cur, S.nu, S.active};
+            CentView cv = make_view(centroids, w, nmax, base, mt);
+            HIPCHK(init_centres(p, k, 0, rs, cv, prm->init, nullptr, prm->seed, TENSOR_K, (uint32_t)t, w, s));
+            HIPCHK(launch_finalize(p, cv, S.active, 0, s));
+            HIPCHK(lloyd(p, k, 0, rs, nullptr, cv, prm->iters, true, sw.labels_u, w, s));
+            HIPCHK(launch_stage_dist(p, k, rs, sw.labels_u, cv, S.dist, s));
+            if (t == 0) HIPCHK(launch_stage_tau(p, S, (double)prm->tau_mult, s));
+            HIPCHK(launch_stage_compact(p, S, t == 0 ? nullptr : u_cur, u_next, mt, s));
+            std::swap(u_cur, u_next);
+            base += mt;
+            ++t;
+        }
+        HIPCHK(launch_stage_end(p, S, t, nmax, n_clusters, full_attn, tau, s));
+        // final assignment over every slot that holds a centre (Algorithm 1 step 20)
+        CentView cvf = make_view(centroids, w, nmax, 0, nmax);
+        HIPCHK(launch_finalize(p, cvf, nullptr, 0, s));
+        HIPCHK(launch_assign(p, k, all, nullptr, cvf, n_clusters, assign, w.flag_list, w.flag_count, s));
+        HIPCHK(launch_refine(p, k, 0, all, cvf, n_clusters, w.flag_list, w.flag_count, assign, s));
+    }
+    HIPCHK(launch_histogram(p, assign, nmax, w.hist, s));
+    HIPCHK(launch_scan_offsets(p, w.hist, nmax, sizes, offsets, s));
+    HIPCHK(launch_stable_rank(p, assign, nmax, offsets, perm, s));
+    HIPCHK(launch_gather_stats(p, nmax, offsets, perm, k, v, 0, centroids, nullptr, kmax, kmin,
+                               k_perm, v_perm, s));
+    return ADC_OK;
+}
+
+// ====================================================================== select
+static int32_t check_sel_dims(const adc_shape* shape, int32_t Cq, int32_t Ck) {
+    int32_t st = check_shape(shape);
+    if (st) return st;
+    if ((st = check_clusters("Cq", Cq))) return st;
+    if ((st = check_clusters("Ck", Ck))) return st;
+    return ADC_OK;
+}
+
+size_t adacluster_select_workspace(const adc_shape* shape, int32_t Cq, int32_t Ck) {
+    if (check_sel_dims(shape, Cq, Ck)) return 0;
+    Carver c(nullptr);
+    c.take<float>((size_t)shape->B * shape->H * Cq * Ck);
+    return c.used + 256;
+}
+
+int32_t adacluster_select(const adc_shape* shape, int32_t Cq, int32_t Ck, const float* qrep,
+                          const void* kmax, const void* kmin, const float* centroids,
+                          const int32_t* k_sizes, const int32_t* n_clusters,
+                          const uint8_t* full_attn, int32_t score, int32_t rule, float top_p,
+                          int32_t top_k, float scale, uint32_t* sel_mask, int32_t* sel_keys,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    int32_t st = check_sel_dims(shape, Cq, Ck);
+    if (st) return st;
+    REQ(qrep); REQ(k_sizes); REQ(n_clusters); REQ(full_attn); REQ(sel_mask); REQ(sel_keys); REQ(workspace);
+    if (score == ADC_SCORE_QUEST) {
+        REQ(kmax); REQ(kmin);
+    } else if (score == ADC_SCORE_CENTROID) {
+        REQ(centroids);
+    } else {
+        return fail(ADC_EINVAL, "score = %d unknown", score);
+    }
+    if (rule == ADC_SELECT_TOPP) {
+        if (!(top_p > 0.0f && top_p <= 1.0f)) return fail(ADC_EINVAL, "top_p must be in (0, 1]");
+    } else if (rule == ADC_SELECT_TOPK) {
+        if (top_k < 1) return fail(ADC_EINVAL, "top_k must be >= 1");
+    } else {
+        return fail(ADC_EINVAL, "rule = %d unknown", rule);
+    }
+    if (!(scale > 0.0f) || scale > 1e30f) return fail(ADC_EINVAL, "scale must be a finite value > 0");
+    const size_t need = adacluster_select_workspace(shape, Cq, Ck);
+    if (workspace_bytes < need)
+        return fail(ADC_EWORKSPACE, "workspace of %zu bytes is below the %zu required", workspace_bytes, need);
+    hipStream_t s = (hipStream_t)stream;
+    Prob p = make_prob(shape);
+    Carver c(workspace);
+    float* S = c.take<float>((size_t)p.BH * Cq * Ck);
+    HIPCHK(launch_scores(p, Cq, Ck, qrep, kmax, kmin, centroids, score, k_sizes, n_clusters, S, s));
+    if (rule == ADC_SELECT_TOPP)
+        HIPCHK(launch_topp(p, Cq, Ck, S, k_sizes, n_clusters, full_attn, scale, top_p, sel_mask, sel_keys, s));
+    else
+        HIPCHK(launch_topk(p, Cq, Ck, S, k_sizes, n_clusters, full_attn, top_k, sel_mask, sel_keys, s));
+    return ADC_OK;
+}
+
+// ====================================================================== sparse attention
+struct AttnWs {
+    int run_cap;
+    int max_items;
+    int32_t* run_start;
+    int32_t* run_pos;
+    int32_t* n_runs;
+    int32_t* items;
+    int32_t* n_items;
+};
+
+static void plan_attn(Carver& c, const adc_shape* shape, int32_t Cq, int32_t Ck, AttnWs& w) {
+    const size_t rows = (size_t)shape->B * shape->H * Cq;
+    w.run_cap = Ck / 2 + 2;
+    w.max_items = (int)((size_t)shape->B * shape->H * (Cq + (shape->N + ATTN_ROWS - 1) / ATTN_ROWS));
+    w.run_start = c.take<int32_t>(rows * w.run_cap);
+    w.run_pos = c.take<int32_t>(rows * (w.run_cap + 1));
+    w.n_runs = c.take<int32_t>(rows);
+    w.items = c.take<int32_t>(2 * (size_t)w.max_items);
+    w.n_items = c.take<int32_t>(1);
+}
+
+size_t adacluster_sparse_attn_workspace(const adc_shape* shape, int32_t Cq, int32_t Ck) {
+    if (check_sel_dims(shape, Cq, Ck)) return 0;
+    Carver c(nullptr);
+    AttnWs w;
+    plan_attn(c, shape, Cq, Ck, w);
+    return c.used + 256;
+}
+
+int32_t adacluster_sparse_attn(const adc_shape* shape, int32_t Cq, int32_t Ck, const void* q,
+                               const int32_t* q_perm, const int32_t* q_offsets, const void* k_perm,
+                               const void* v_perm, const int32_t* k_offsets,
+                               const uint32_t* sel_mask, float scale, void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    int32_t st = check_sel_dims(shape, Cq, Ck);
+    if (st) return st;
+    REQ(q); REQ(q_perm); REQ(q_offsets); REQ(k_perm); REQ(v_perm); REQ(k_offsets); REQ(sel_mask);
+    REQ(out); REQ(workspace);
+    if (!(scale > 0.0f) || scale > 1e30f) return fail(ADC_EINVAL, "scale must be a finite value > 0");
+    const size_t need = adacluster_sparse_attn_workspace(shape, Cq, Ck);
+    if (workspace_bytes < need)
+        return fail(ADC_EWORKSPACE, "workspace of %zu bytes is below the %zu required", workspace_bytes, need);
+    hipStream_t s = (hipStream_t)stream;
+    Prob p = make_prob(shape);
+    Carver c(workspace);
+    AttnWs w;
+    plan_attn(c, shape, Cq, Ck, w);
+    HIPCHK(launch_build_runs(p, Cq, Ck, k_offsets, sel_mask, w.run_cap, w.run_start, w.run_pos, w.n_runs, s));
+    HIPCHK(launch_worklist(p, Cq, q_offsets, w.items, w.n_items, s));
+    HIPCHK(launch_attention(p, Cq, q, q_perm, q_offsets, k_perm, v_perm, w.run_start, w.run_pos,
+                            w.n_runs, w.run_cap, w.items, w.n_items, w.max_items, scale, out, lse, s));
+    return ADC_OK;
+}
+
+// ====================================================================== helpers
+size_t adacluster_assign_workspace(const adc_shape* shape, int32_t M) {
+    if (check_shape(shape) || check_clusters("M", M)) return 0;
+    Carver c(nullptr);
+    KmeansWs w;
+    plan_kmeans(c, make_prob(shape), M, true, false, false, w);
+    return c.used + 256;
+}
+
+int32_t adacluster_assign(const adc_shape* shape, int32_t M, int32_t normalize, const void* x,
+                          const float* centroids, const uint8_t* valid, int32_t* assign,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    int32_t st = check_shape(shape);
+    if (st) return st;
+    if ((st = check_clusters("M", M))) return st;
+    REQ(x); REQ(centroids); REQ(assign); REQ(workspace);
+    const size_t need = adacluster_assign_workspace(shape, M);
+    if (workspace_bytes < need)
+        return fail(ADC_EWORKSPACE, "workspace of %zu bytes is below the %zu required", workspace_bytes, need);
+    hipStream_t s = (hipStream_t)stream;
+    Prob p = make_prob(shape);
+    Carver c(workspace);
+    KmeansWs w;
+    plan_kmeans(c, p, M, true, false, false, w);
+    if (valid)
+        HIPCHK(hipMemcpyAsync(w.valid, valid, (size_t)p.BH * M, hipMemcpyDeviceToDevice, s));
+    else
+        HIPCHK(fill_u8(w.valid, (int64_t)p.BH * M, 1, s));
+    // centres are only read (finalize without sums does not write them)
+    CentView cv = make_view(const_cast<float*>(centroids), w, M, 0, M);
+    RowSet all{nullptr, nullptr, nullptr};
+    if (normalize) HIPCHK(launch_inv_norm(p, x, w.inv_norm, s));
+    HIPCHK(launch_finalize(p, cv, nullptr, 0, s));
+    HIPCHK(launch_assign(p, x, all, normalize ? w.inv_norm : nullptr, cv, nullptr, assign,
+                         w.flag_list, w.flag_count, s));
+    HIPCHK(launch_refine(p, x, normalize, all, cv, nullptr, w.flag_list, w.flag_count, assign, s));
+    return ADC_OK;
+}
+
+size_t adacluster_permute_workspace(const adc_shape* shape, int32_t M) {
+    if (check_shape(shape) || check_clusters("M", M)) return 0;
+    Carver c(nullptr);
+    c.take<int32_t>((size_t)shape->B * shape->H * M);
+    return c.used + 256;
+}
+
+int32_t adacluster_permute(const adc_shape* shape, int32_t M, const int32_t* assign, const void* x,
+                           const void* v, int32_t* sizes, int32_t* offsets, int32_t* perm,
+                           float* means, void* xmax, void* xmin, void* x_perm, void* v_perm,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    int32_t st = check_shape(shape);
+    if (st) return st;
+    if ((st = check_clusters("M", M))) return st;
+    REQ(assign); REQ(x); REQ(sizes); REQ(offsets); REQ(perm); REQ(workspace);
+    if (v_perm && !v) return fail(ADC_EINVAL, "v_perm needs v");
+    const size_t need = adacluster_permute_workspace(shape, M);
+    if (workspace_bytes < need)
+        return fail(ADC_EWORKSPACE, "workspace of %zu bytes is below the %zu required", workspace_bytes, need);
+    hipStream_t s = (hipStream_t)stream;
+    Prob p = make_prob(shape);
+    Carver c(workspace);
+    int32_t* hist = c.take<int32_t>((size_t)p.BH * M);
+    HIPCHK(launch_histogram(p, assign, M, hist, s));
+    HIPCHK(launch_scan_offsets(p, hist, M, sizes, offsets, s));
+    HIPCHK(launch_stable_rank(p, assign, M, offsets, perm, s));
+    HIPCHK(launch_gather_stats(p, M, offsets, perm, x, v, 0, means, nullptr, xmax, xmin, x_perm,
+                               v_perm, s));
+    return ADC_OK;
+}
+
+}  // extern "C"

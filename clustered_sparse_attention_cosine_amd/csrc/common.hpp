@@ -1,0 +1,114 @@
+// Device helpers shared by the gfx950 kernels of the clustered sparse attention library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace adc {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16;
+
+constexpr int WAVE = 64;
+
+// ------------------------------------------------------------------ bf16
+// Round-to-nearest-even float -> bf16 bit pattern (inputs here are finite).
+__device__ __forceinline__ u16 f2bf_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (u16)(u >> 16);
+}
+__device__ __forceinline__ float bf_bits2f(u16 b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ __bf16 f2bf(float f) { return __builtin_bit_cast(__bf16, f2bf_bits(f)); }
+__device__ __forceinline__ float bf2f(__bf16 b) { return bf_bits2f(__builtin_bit_cast(u16, b)); }
+
+// Element access for the two storage types (f32, or bf16 kept as raw 16-bit words).
+template <typename T> struct elem;
+template <> struct elem<float> {
+    __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+    __device__ __forceinline__ static void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct elem<u16> {
+    __device__ __forceinline__ static float load(const u16* p, int64_t i) { return bf_bits2f(p[i]); }
+    __device__ __forceinline__ static void store(u16* p, int64_t i, float v) { p[i] = f2bf_bits(v); }
+};
+
+// Load 8 consecutive elements (16-byte aligned for bf16, 32-byte for f32) as f32.
+template <typename T> __device__ __forceinline__ void load8(const T* p, float (&o)[8]);
+template <> __device__ __forceinline__ void load8<u16>(const u16* p, float (&o)[8]) {
+    uint4 r = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[2 * i] = __uint_as_float(w[i] << 16);
+        o[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+template <> __device__ __forceinline__ void load8<float>(const float* p, float (&o)[8]) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = *reinterpret_cast<const float4*>(p + 4);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+
+// Pack 8 floats to bf16x8 (RNE).
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float (&v)[8]) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = f2bf(v[i]);
+    return r;
+}
+
+// Raw 16-byte load of 8 bf16 words as a bf16x8 operand.
+__device__ __forceinline__ bf16x8 ld_bf16x8(const u16* p) {
+    uint4 r = *reinterpret_cast<const uint4*>(p);
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------ wave / block reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// ------------------------------------------------------------------ SplitMix64
+// Steele, Lea and Flood (OOPSLA 2014): output i (0-based) of a generator whose
+// state starts at s is mix(s + (i + 1) * golden-gamma).
+__host__ __device__ inline uint64_t sm64_mix(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+}
+__host__ __device__ inline uint64_t sm64_at(uint64_t s, uint64_t i) {
+    return sm64_mix(s + (i + 1) * 0x9E3779B97F4A7C15ULL);
+}
+// One independent draw stream per (tensor, stage, batch, head).
+__host__ __device__ inline uint64_t draw_stream(uint64_t seed, uint32_t tensor, uint32_t stage,
+                                                uint32_t b, uint32_t h) {
+    uint64_t key = ((uint64_t)(tensor & 0xF) << 60) | ((uint64_t)(stage & 0xFF) << 52) |
+                   ((uint64_t)(b & 0x3FFFFFF) << 26) | (uint64_t)(h & 0x3FFFFFF);
+    return sm64_at(seed ^ key, 0);
+}
+
+}  // namespace adc

@@ -1,0 +1,147 @@
+// Internal launchers of the gfx950 kernels (host side). Every launcher enqueues
+// on `stream` and returns the hipError_t of its launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace adc {
+
+// Draw-stream tags of the two clustered tensors.
+constexpr uint32_t TENSOR_Q = 1, TENSOR_K = 2;
+
+// Workload-independent problem descriptor for one batched launch.
+struct Prob {
+    int BH;     // B * H independent heads
+    int H;      // heads per batch entry (stream keys use b = bh / H, h = bh % H)
+    int N;      // rows per head
+    int D;      // 64 or 128
+    int bf16;   // 1: inputs are bf16 words, 0: f32
+};
+
+// ---------------------------------------------------------------- fills (kmeans.hip)
+hipError_t fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+hipError_t fill_u8(uint8_t* p, int64_t n, uint8_t v, hipStream_t s);
+hipError_t launch_fixed_info(int BH, int N, int m, int32_t* n_clusters, uint8_t* full, float* tau,
+                             int32_t* stage_sizes, hipStream_t s);
+
+// ---------------------------------------------------------------- k-means (kmeans.hip)
+// 1 / max(||x_i||, 1e-12) per row (norm in f64).
+hipError_t launch_inv_norm(const Prob& p, const void* x, float* inv_norm, hipStream_t s);
+// xhat_i = x_i / max(||x_i||, 1e-12) in f32 (norm summed in index order, f64).
+hipError_t launch_normalize(const Prob& p, const void* x, float* xhat, hipStream_t s);
+
+// Centroid-array view: cent/valid/c_hi/c_lo/cn2 hold `cap` slots per head;
+// kernels see slots [base, base + m).
+struct CentView {
+    float* cent;
+    uint8_t* valid;
+    uint16_t* c_hi;
+    uint16_t* c_lo;
+    float* cn2;
+    float* sums;
+    int32_t* cnt;
+    int cap;
+    int base;
+    int m;
+};
+
+// Rows a k-means call clusters: rows[bh*N + r] for r < nrows[bh] (NULL: all N
+// rows, identity), only for heads with active[bh] != 0 (NULL: all heads).
+struct RowSet {
+    const int32_t* rows;
+    const int32_t* nrows;
+    const uint8_t* active;
+};
+
+// Seeded systematic sample of min(m, n) rows; slots beyond hold no centre.
+hipError_t launch_init_sample(const Prob& p, const void* x, int normalize, RowSet rs,
+                              CentView cv, uint64_t seed, uint32_t tensor, uint32_t stage,
+                              hipStream_t s);
+// Seeded k-means++ (one workgroup per head). xf: f32 rows to cluster (the
+// normalised queries, or NULL to read `x` directly); d2/chosen are scratch.
+hipError_t launch_init_kmeanspp(const Prob& p, const void* x, const float* xf, RowSet rs,
+                                CentView cv, uint64_t seed, uint32_t tensor, uint32_t stage,
+                                double* d2, uint8_t* chosen, hipStream_t s);
+// Centroid prep: split into bf16 hi/lo, squared norms (+inf where no centre).
+// With sums != NULL it first moves centres to sums/cnt (cnt > 0) and clears the sums.
+hipError_t launch_finalize(const Prob& p, CentView cv, const uint8_t* active, int with_sums,
+                           hipStream_t s);
+// Nearest centre by a bf16 hi/lo matrix-core contraction with a certified error
+// bound; rows whose best two distances are not separated by the bound go to
+// the flag list for an exact f64 recheck (launch_refine).
+hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
+                         CentView cv, const int32_t* mcount, int32_t* labels,
+                         int32_t* flag_list, int32_t* flag_count, hipStream_t s);
+hipError_t launch_refine(const Prob& p, const void* x, int normalize, RowSet rs, CentView cv,
+                         const int32_t* mcount, const int32_t* flag_list,
+                         const int32_t* flag_count, int32_t* labels, hipStream_t s);
+// Centroid sums (f32 atomics) and member counts for the current labels.
+hipError_t launch_update_accum(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
+                               const int32_t* labels, CentView cv, hipStream_t s);
+
+// ---------------------------------------------------------------- multi-stage state
+struct StageState {
+    int32_t* nu;         // [BH] |U|
+    int32_t* slots;      // [BH] slots used so far
+    uint8_t* full;       // [BH] F
+    uint8_t* active;     // [BH] stage runs for this head
+    int32_t* n_stages;   // [BH]
+    double* tau;         // [BH]
+    int32_t* u_a;        // [BH][N] U lists (ping-pong)
+    int32_t* u_b;
+    double* dist;        // [BH][N] stage distances
+    int32_t* stage_sizes;  // [BH][8] or NULL
+};
+hipError_t launch_stage_reset(const Prob& p, StageState st, hipStream_t s);
+hipError_t launch_stage_begin(const Prob& p, StageState st, int t, int nmax, hipStream_t s);
+hipError_t launch_stage_dist(const Prob& p, const void* k, RowSet rs, const int32_t* labels,
+                             CentView cv, double* dist, hipStream_t s);
+hipError_t launch_stage_tau(const Prob& p, StageState st, double tau_mult, hipStream_t s);
+hipError_t launch_stage_compact(const Prob& p, StageState st, const int32_t* u_in,
+                                int32_t* u_out, int m_t, hipStream_t s);
+hipError_t launch_stage_end(const Prob& p, StageState st, int t_total, int nmax,
+                            int32_t* n_clusters, uint8_t* full_out, float* tau_out,
+                            hipStream_t s);
+
+// ---------------------------------------------------------------- layout (permute.hip)
+hipError_t launch_histogram(const Prob& p, const int32_t* labels, int M, int32_t* cnt,
+                            hipStream_t s);
+hipError_t launch_scan_offsets(const Prob& p, const int32_t* cnt, int M, int32_t* sizes_out,
+                               int32_t* offsets, hipStream_t s);
+hipError_t launch_stable_rank(const Prob& p, const int32_t* labels, int M,
+                              const int32_t* offsets, int32_t* perm, hipStream_t s);
+// Per cluster: member means (of normalised rows when normalize), raw means,
+// per-dimension max/min and the permuted copies of x and v.
+hipError_t launch_gather_stats(const Prob& p, int M, const int32_t* offsets, const int32_t* perm,
+                               const void* x, const void* v, int normalize, float* means,
+                               float* raw_means, void* xmax, void* xmin, void* x_perm,
+                               void* v_perm, hipStream_t s);
+
+// ---------------------------------------------------------------- selection (select.hip)
+hipError_t launch_scores(const Prob& p, int Cq, int Ck, const float* qrep, const void* kmax,
+                         const void* kmin, const float* kcent, int score_mode,
+                         const int32_t* k_sizes, const int32_t* n_clusters, float* S,
+                         hipStream_t s);
+hipError_t launch_topp(const Prob& p, int Cq, int Ck, const float* S, const int32_t* k_sizes,
+                       const int32_t* n_clusters, const uint8_t* full, float scale, float top_p,
+                       uint32_t* mask, int32_t* sel_keys, hipStream_t s);
+hipError_t launch_topk(const Prob& p, int Cq, int Ck, const float* S, const int32_t* k_sizes,
+                       const int32_t* n_clusters, const uint8_t* full, int top_k,
+                       uint32_t* mask, int32_t* sel_keys, hipStream_t s);
+
+// ---------------------------------------------------------------- attention (attn.hip)
+hipError_t launch_build_runs(const Prob& p, int Cq, int Ck, const int32_t* k_offsets,
+                             const uint32_t* mask, int run_cap, int32_t* run_start,
+                             int32_t* run_pos, int32_t* n_runs, hipStream_t s);
+hipError_t launch_worklist(const Prob& p, int Cq, const int32_t* q_offsets, int32_t* items,
+                           int32_t* n_items, hipStream_t s);
+hipError_t launch_attention(const Prob& p, int Cq, const void* q, const int32_t* q_perm,
+                            const int32_t* q_offsets, const void* k_perm, const void* v_perm,
+                            const int32_t* run_start, const int32_t* run_pos,
+                            const int32_t* n_runs, int run_cap, const int32_t* items,
+                            const int32_t* n_items, int max_items, float scale, void* out,
+                            float* lse, hipStream_t s);
+
+constexpr int ATTN_ROWS = 64;  // query rows per attention work item
+
+}  // namespace adc

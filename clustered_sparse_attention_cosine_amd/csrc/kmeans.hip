@@ -1,0 +1,851 @@
+// k-means kernels for gfx950: query normalisation, cold initialisation, the
+// assignment step as a bf16 matrix-core contraction with a certified argmin,
+// an exact f64 recheck of uncertain rows, the centroid update, and the
+// bookkeeping of the multi-stage key clustering.
+//
+// Method: "AdaCluster: Adaptive Query-Key Clustering for Sparse Attention in
+// Video Generation" (arXiv 2604.18348v1), section 3.1 (queries are clustered
+// on the unit sphere), section 3.2.2 / Algorithm 1 (keys: stages of k-means on
+// the still-unassigned keys, threshold tau) and section 4.1 (tau = 1.5 x mean
+// distance).
+#include <math.h>
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace adc {
+
+// ------------------------------------------------------------------ helpers
+template <typename T>
+__device__ __forceinline__ const T* row_ptr(const T* x, int N, int D, int bh, int64_t tok) {
+    return x + ((int64_t)bh * N + tok) * D;
+}
+
+// ||x||, summed in index order in f64, floored at 1e-12 (query normalisation).
+template <typename T>
+__device__ double seq_norm(const T* r, int D) {
+#pragma clang fp contract(off)
+    double s = 0.0;
+    for (int j = 0; j < D; ++j) {
+        double v = (double)elem<T>::load(r, j);
+        s += v * v;
+    }
+    double n = sqrt(s);
+    return n < 1e-12 ? 1e-12 : n;
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+hipError_t fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
+__global__ void fill_u8_kernel(uint8_t* p, int64_t n, uint8_t v) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+hipError_t fill_u8(uint8_t* p, int64_t n, uint8_t v, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_u8_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
+// Fixed-count key clustering: n_clusters = m, F = 0, tau = 0, stage sizes [N].
+__global__ void fixed_info_kernel(int BH, int N, int m, int32_t* n_clusters, uint8_t* full,
+                                  float* tau, int32_t* stage_sizes) {
+    int bh = blockIdx.x * blockDim.x + threadIdx.x;
+    if (bh >= BH) return;
+    n_clusters[bh] = m;
+    full[bh] = 0;
+    tau[bh] = 0.0f;
+    if (stage_sizes) {
+        stage_sizes[bh * 8] = N;
+        for (int i = 1; i < 8; ++i) stage_sizes[bh * 8 + i] = -1;
+    }
+}
+
+hipError_t launch_fixed_info(int BH, int N, int m, int32_t* n_clusters, uint8_t* full, float* tau,
+                             int32_t* stage_sizes, hipStream_t s) {
+    hipLaunchKernelGGL(fixed_info_kernel, dim3((BH + 63) / 64), dim3(64), 0, s, BH, N, m, n_clusters,
+                       full, tau, stage_sizes);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ norms
+template <typename T>
+__global__ __launch_bounds__(256) void inv_norm_kernel(const T* __restrict__ x, int64_t rows,
+                                                       int D, float* __restrict__ inv) {
+    int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    int sub = threadIdx.x & 15;
+    if (row >= rows) return;
+    const T* r = x + row * D;
+    double s = 0.0;
+    for (int j = sub; j < D; j += 16) {
+        double v = (double)elem<T>::load(r, j);
+        s += v * v;
+    }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    if (sub == 0) {
+        double n = sqrt(s);
+        if (n < 1e-12) n = 1e-12;
+        inv[row] = (float)(1.0 / n);
+    }
+}
+
+hipError_t launch_inv_norm(const Prob& p, const void* x, float* inv, hipStream_t s) {
+    int64_t rows = (int64_t)p.BH * p.N;
+    dim3 grid((unsigned)((rows + 15) / 16));
+    if (p.bf16)
+        hipLaunchKernelGGL(inv_norm_kernel<u16>, grid, dim3(256), 0, s, (const u16*)x, rows, p.D, inv);
+    else
+        hipLaunchKernelGGL(inv_norm_kernel<float>, grid, dim3(256), 0, s, (const float*)x, rows, p.D, inv);
+    return hipGetLastError();
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void normalize_kernel(const T* __restrict__ x, int64_t rows,
+                                                        int D, float* __restrict__ out) {
+#pragma clang fp contract(off)
+    int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= rows) return;
+    const T* r = x + row * D;
+    double n = seq_norm(r, D);
+    for (int j = 0; j < D; ++j) out[row * D + j] = (float)((double)elem<T>::load(r, j) / n);
+}
+
+hipError_t launch_normalize(const Prob& p, const void* x, float* xhat, hipStream_t s) {
+    int64_t rows = (int64_t)p.BH * p.N;
+    dim3 grid((unsigned)((rows + 255) / 256));
+    if (p.bf16)
+        hipLaunchKernelGGL(normalize_kernel<u16>, grid, dim3(256), 0, s, (const u16*)x, rows, p.D, xhat);
+    else
+        hipLaunchKernelGGL(normalize_kernel<float>, grid, dim3(256), 0, s, (const float*)x, rows, p.D, xhat);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ SAMPLE init
+// Slot j < min(m, n) takes row floor((j n + r) / m) of the clustered rows (row j
+// when n < m), r = draw 0 mod n; slots beyond hold no centre.
+template <typename T>
+__global__ __launch_bounds__(256) void init_sample_kernel(const T* __restrict__ x, int N, int D,
+                                                          int H, int normalize, RowSet rs,
+                                                          CentView cv, uint64_t seed,
+                                                          uint32_t tensor, uint32_t stage) {
+#pragma clang fp contract(off)
+    const int bh = blockIdx.y;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int j = blockIdx.x * 4 + w;
+    if (rs.active && !rs.active[bh]) return;
+    if (j >= cv.m) return;
+    const int n = rs.nrows ? rs.nrows[bh] : N;
+    const int cm = n < cv.m ? n : cv.m;
+    const int64_t slot = (int64_t)bh * cv.cap + cv.base + j;
+    float* c = cv.cent + slot * D;
+    if (j >= cm) {
+        for (int d = l; d < D; d += 64) c[d] = 0.0f;
+        if (l == 0) cv.valid[slot] = 0;
+        return;
+    }
+    uint64_t strm = draw_stream(seed, tensor, stage, (uint32_t)(bh / H), (uint32_t)(bh % H));
+    uint64_t r = sm64_at(strm, 0) % (uint64_t)n;
+    int64_t idx = (n >= cv.m) ? (int64_t)(((uint64_t)j * (uint64_t)n + r) / (uint64_t)cv.m) : j;
+    int64_t tok = rs.rows ? rs.rows[(int64_t)bh * N + idx] : idx;
+    const T* xr = row_ptr(x, N, D, bh, tok);
+    double nrm = 1.0;
+    if (normalize) {
+        double v = (l == 0) ? seq_norm(xr, D) : 0.0;
+        nrm = __shfl(v, 0);
+    }
+    for (int d = l; d < D; d += 64) {
+        float xv = elem<T>::load(xr, d);
+        c[d] = normalize ? (float)((double)xv / nrm) : xv;
+    }
+    if (l == 0) cv.valid[slot] = 1;
+}
+
+hipError_t launch_init_sample(const Prob& p, const void* x, int normalize, RowSet rs, CentView cv,
+                              uint64_t seed, uint32_t tensor, uint32_t stage, hipStream_t s) {
+    dim3 grid((unsigned)((cv.m + 3) / 4), (unsigned)p.BH);
+    if (p.bf16)
+        hipLaunchKernelGGL(init_sample_kernel<u16>, grid, dim3(256), 0, s, (const u16*)x, p.N, p.D,
+                           p.H, normalize, rs, cv, seed, tensor, stage);
+    else
+        hipLaunchKernelGGL(init_sample_kernel<float>, grid, dim3(256), 0, s, (const float*)x, p.N,
+                           p.D, p.H, normalize, rs, cv, seed, tensor, stage);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ KMEANSPP init
+// D^2 sampling (Arthur and Vassilvitskii 2007), one workgroup per head. The
+// running sums and the search run in one thread in row order, in f64, so the
+// chosen rows follow exactly from the draws.
+template <typename T>
+__device__ __forceinline__ float kpp_val(const T* x, const float* xf, int N, int D, int bh,
+                                         int64_t tok, int d) {
+    return xf ? xf[((int64_t)bh * N + tok) * D + d] : elem<T>::load(row_ptr(x, N, D, bh, tok), d);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void init_kmeanspp_kernel(const T* __restrict__ x,
+                                                            const float* __restrict__ xf, int N,
+                                                            int D, int H, RowSet rs, CentView cv,
+                                                            uint64_t seed, uint32_t tensor,
+                                                            uint32_t stage, double* __restrict__ d2g,
+                                                            uint8_t* __restrict__ chosen_g) {
+#pragma clang fp contract(off)
+    __shared__ float cvec[128];
+    __shared__ int64_t sh_idx;
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (rs.active && !rs.active[bh]) return;
+    const int n = rs.nrows ? rs.nrows[bh] : N;
+    const int cm = n < cv.m ? n : cv.m;
+    double* d2 = d2g + (int64_t)bh * N;
+    uint8_t* chosen = chosen_g + (int64_t)bh * N;
+    for (int i = tid; i < n; i += blockDim.x) chosen[i] = 0;
+    uint64_t strm = draw_stream(seed, tensor, stage, (uint32_t)(bh / H), (uint32_t)(bh % H));
+    __syncthreads();
+    for (int t = 0; t < cm; ++t) {
+        if (tid == 0) {
+            int64_t idx;
+            if (t == 0) {
+                idx = (int64_t)(sm64_at(strm, 0) % (uint64_t)n);
+            } else {
+                double S = 0.0;
+                for (int i = 0; i < n; ++i) S += d2[i];
+                if (S == 0.0) {
+                    idx = -1;
+                    for (int i = 0; i < n; ++i)
+                        if (!chosen[i]) { idx = i; break; }
+                } else {
+                    double u = (double)(sm64_at(strm, (uint64_t)t) >> 11) * 0x1.0p-53 * S;
+                    double run = 0.0;
+                    idx = n - 1;
+                    for (int i = 0; i < n; ++i) {
+                        run += d2[i];
+                        if (run > u) { idx = i; break; }
+                    }
+                }
+            }
+            chosen[idx] = 1;
+            sh_idx = idx;
+        }
+        __syncthreads();
+        const int64_t idx = sh_idx;
+        const int64_t tok_c = rs.rows ? rs.rows[(int64_t)bh * N + idx] : idx;
+        const int64_t slot = (int64_t)bh * cv.cap + cv.base + t;
+        for (int d = tid; d < D; d += blockDim.x) {
+            float v = kpp_val(x, xf, N, D, bh, tok_c, d);
+            cvec[d] = v;
+            cv.cent[slot * D + d] = v;
+        }
+        if (tid == 0) cv.valid[slot] = 1;
+        __syncthreads();
+        for (int i = tid; i < n; i += blockDim.x) {
+            const int64_t tok = rs.rows ? rs.rows[(int64_t)bh * N + i] : i;
+            double s = 0.0;
+            for (int d = 0; d < D; ++d) {
+                double df = (double)kpp_val(x, xf, N, D, bh, tok, d) - (double)cvec[d];
+                s += df * df;
+            }
+            if (t == 0 || s < d2[i]) d2[i] = s;
+        }
+        __syncthreads();
+    }
+    for (int j = cm; j < cv.m; ++j) {
+        const int64_t slot = (int64_t)bh * cv.cap + cv.base + j;
+        for (int d = tid; d < D; d += blockDim.x) cv.cent[slot * D + d] = 0.0f;
+        if (tid == 0) cv.valid[slot] = 0;
+    }
+}
+
+hipError_t launch_init_kmeanspp(const Prob& p, const void* x, const float* xf, RowSet rs,
+                                CentView cv, uint64_t seed, uint32_t tensor, uint32_t stage,
+                                double* d2, uint8_t* chosen, hipStream_t s) {
+    if (p.bf16)
+        hipLaunchKernelGGL(init_kmeanspp_kernel<u16>, dim3(p.BH), dim3(256), 0, s, (const u16*)x,
+                           xf, p.N, p.D, p.H, rs, cv, seed, tensor, stage, d2, chosen);
+    else
+        hipLaunchKernelGGL(init_kmeanspp_kernel<float>, dim3(p.BH), dim3(256), 0, s,
+                           (const float*)x, xf, p.N, p.D, p.H, rs, cv, seed, tensor, stage, d2,
+                           chosen);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ finalize / prep
+// One wave per slot: optional move to sums/cnt, then bf16 hi/lo split and the
+// squared norm (+inf where the slot holds no centre).
+template <int D>
+__global__ __launch_bounds__(256) void finalize_kernel(CentView cv, const uint8_t* active,
+                                                       int with_sums) {
+    const int bh = blockIdx.y;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int j = blockIdx.x * 4 + w;
+    if (active && !active[bh]) return;
+    if (j >= cv.m) return;
+    const int64_t slot = (int64_t)bh * cv.cap + cv.base + j;
+    float* c = cv.cent + slot * D;
+    constexpr int E = D / 64;
+    float cvv[E];
+    if (with_sums) {
+        int n = cv.cnt[slot];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float* sp = cv.sums + slot * D + l + 64 * e;
+            if (n > 0) c[l + 64 * e] = *sp / (float)n;
+            *sp = 0.0f;
+        }
+        if (l == 0) cv.cnt[slot] = 0;
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        float v = c[l + 64 * e];
+        cvv[e] = v;
+        u16 h = f2bf_bits(v);
+        u16 lo = f2bf_bits(v - bf_bits2f(h));
+        cv.c_hi[slot * D + l + 64 * e] = h;
+        cv.c_lo[slot * D + l + 64 * e] = lo;
+        ss += (double)v * (double)v;
+    }
+    ss = wave_sum_d(ss);
+    if (l == 0) cv.cn2[slot] = cv.valid[slot] ? (float)ss : INFINITY;
+}
+
+hipError_t launch_finalize(const Prob& p, CentView cv, const uint8_t* active, int with_sums,
+                           hipStream_t s) {
+    dim3 grid((unsigned)((cv.m + 3) / 4), (unsigned)p.BH);
+    if (p.D == 64)
+        hipLaunchKernelGGL(finalize_kernel<64>, grid, dim3(256), 0, s, cv, active, with_sums);
+    else
+        hipLaunchKernelGGL(finalize_kernel<128>, grid, dim3(256), 0, s, cv, active, with_sums);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ assignment
+// Workgroup = 4 waves x 64 rows. The centres stream through LDS in tiles of 64
+// (bf16 hi and lo parts); each wave computes S^T = C . X^T with 16x16x32 bf16
+// MFMAs (rows of the MFMA = centres, columns = points), so a lane owns one
+// point per 16-point block and tracks the best and second-best
+//   d_j = ||c_j||^2 - 2 s (x . c_j)      (s = 1 / ||x|| for queries, else 1)
+// The contraction error of one d_j is at most ERR_X s||x|| max||c|| +
+// ERR_C max||c||^2 (hi/lo residual 2^-16 plus f32 accumulation, with margin);
+// a row whose two best values are not separated by twice that is flagged and
+// rechecked exactly.
+template <typename T, int D, bool F32X>
+__global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
+                                                     const float* __restrict__ inv_norm,
+                                                     CentView cv, const int32_t* __restrict__ mcount,
+                                                     int32_t* __restrict__ labels,
+                                                     int32_t* __restrict__ flag_list,
+                                                     int32_t* __restrict__ flag_count) {
+    constexpr int KC = D / 32;
+    constexpr int LD = D + 8;
+    constexpr float ERR_X = F32X ? 0x1.0p-12f : 0x1.0p-13f;
+    constexpr float ERR_C = 0x1.0p-21f;
+    __shared__ __attribute__((aligned(16))) u16 sh_hi[64 * LD];
+    __shared__ __attribute__((aligned(16))) u16 sh_lo[64 * LD];
+    __shared__ float sh_c2[64];
+
+    const int bh = blockIdx.y;
+    if (rs.active && !rs.active[bh]) return;
+    const int n = rs.nrows ? rs.nrows[bh] : N;
+    const int row_base = blockIdx.x * 256;
+    if (row_base >= n) return;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c16 = l & 15;
+    const int M = mcount ? min(mcount[bh], cv.m) : cv.m;
+
+    bf16x8 xh[4][KC];
+    bf16x8 xl[4][F32X ? KC : 1];
+    float sc[4], xn[4];
+    int rr[4];
+    bool ok[4];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+        const int r = row_base + w * 64 + pb * 16 + c16;
+        ok[pb] = r < n;
+        rr[pb] = r;
+        int64_t tok = 0;
+        if (ok[pb]) tok = rs.rows ? rs.rows[(int64_t)bh * N + r] : r;
+        const T* xp = row_ptr(X, N, D, bh, tok);
+        float ss = 0.0f;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            float v[8];
+            if (ok[pb]) {
+                load8<T>(xp + kc * 32 + g * 8, v);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
+            xh[pb][kc] = pack_bf16x8(v);
+            if constexpr (F32X) {
+                float lo[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) lo[i] = v[i] - bf2f(xh[pb][kc][i]);
+                xl[pb][kc] = pack_bf16x8(lo);
+            }
+        }
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        sc[pb] = (inv_norm && ok[pb]) ? inv_norm[(int64_t)bh * N + tok] : 1.0f;
+        xn[pb] = sc[pb] * sqrtf(ss);
+    }
+
+    float b1[4], b2[4];
+    int bi[4];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) { b1[pb] = INFINITY; b2[pb] = INFINITY; bi[pb] = 0x7fffffff; }
+    float c2max = 0.0f;
+    const int64_t cbase = (int64_t)bh * cv.cap + cv.base;
+    const int ntiles = (M + 63) / 64;
+
+    for (int tile = 0; tile < ntiles; ++tile) {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) {
+            const int c = tid + i * 256;
+            const int row = c / (D / 8), col8 = c % (D / 8);
+            const int j = tile * 64 + row;
+            uint4 vh = make_uint4(0, 0, 0, 0), vl = make_uint4(0, 0, 0, 0);
+            if (j < M) {
+                vh = *reinterpret_cast<const uint4*>(cv.c_hi + (cbase + j) * D + col8 * 8);
+                vl = *reinterpret_cast<const uint4*>(cv.c_lo + (cbase + j) * D + col8 * 8);
+            }
+            *reinterpret_cast<uint4*>(&sh_hi[row * LD + col8 * 8]) = vh;
+            *reinterpret_cast<uint4*>(&sh_lo[row * LD + col8 * 8]) = vl;
+        }
+        if (tid < 64) {
+            const int j = tile * 64 + tid;
+            sh_c2[tid] = (j < M) ? cv.cn2[cbase + j] : INFINITY;
+        }
+        __syncthreads();
+
+        f32x4 acc[4][4];
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) acc[pb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const int off = (cb * 16 + c16) * LD + kc * 32 + g * 8;
+                bf16x8 ah = *reinterpret_cast<const bf16x8*>(&sh_hi[off]);
+                bf16x8 al = *reinterpret_cast<const bf16x8*>(&sh_lo[off]);
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) {
+                    acc[pb][cb] = mfma16(ah, xh[pb][kc], acc[pb][cb]);
+                    acc[pb][cb] = mfma16(al, xh[pb][kc], acc[pb][cb]);
+                    if constexpr (F32X) acc[pb][cb] = mfma16(ah, xl[pb][kc], acc[pb][cb]);
+                }
+            }
+        }
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int jl = cb * 16 + g * 4 + i;
+                const float c2 = sh_c2[jl];
+                if (c2 < INFINITY) c2max = fmaxf(c2max, c2);
+                const int j = tile * 64 + jl;
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) {
+                    const float dv = fmaf(-2.0f * sc[pb], acc[pb][cb][i], c2);
+                    b2[pb] = fmaxf(b1[pb], fminf(b2[pb], dv));
+                    if (dv < b1[pb]) { b1[pb] = dv; bi[pb] = j; }
+                }
+            }
+        }
+    }
+
+    c2max = fmaxf(c2max, __shfl_xor(c2max, 16));
+    c2max = fmaxf(c2max, __shfl_xor(c2max, 32));
+    const float err_c = ERR_X * sqrtf(c2max);
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+#pragma unroll
+        for (int o = 16; o <= 32; o <<= 1) {
+            const float ob1 = __shfl_xor(b1[pb], o);
+            const float ob2 = __shfl_xor(b2[pb], o);
+            const int obi = __shfl_xor(bi[pb], o);
+            const bool take = ob1 < b1[pb] || (ob1 == b1[pb] && obi < bi[pb]);
+            const float nb2 = take ? fminf(b1[pb], ob2) : fminf(b2[pb], ob1);
+            if (take) { b1[pb] = ob1; bi[pb] = obi; }
+            b2[pb] = nb2;
+        }
+        if (g == 0 && ok[pb]) {
+            // no finite distance (no centre, or a NaN row): slot 0, and the row is flagged
+            labels[(int64_t)bh * N + rr[pb]] = bi[pb] == 0x7fffffff ? 0 : bi[pb];
+            const float err = err_c * xn[pb] + ERR_C * c2max;
+            if (!(b2[pb] - b1[pb] > 2.0f * err)) {
+                const int pos = atomicAdd(&flag_count[bh], 1);
+                flag_list[(int64_t)bh * N + pos] = rr[pb];
+            }
+        }
+    }
+}
+
+hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
+                         CentView cv, const int32_t* mcount, int32_t* labels, int32_t* flag_list,
+                         int32_t* flag_count, hipStream_t s) {
+    hipError_t e = fill_i32(flag_count, p.BH, 0, s);
+    if (e != hipSuccess) return e;
+    dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)p.BH);
+    if (p.bf16) {
+        if (p.D == 64)
+            hipLaunchKernelGGL((assign_kernel<u16, 64, false>), grid, dim3(256), 0, s, (const u16*)x,
+                               p.N, rs, inv_norm, cv, mcount, labels, flag_list, flag_count);
+        else
+            hipLaunchKernelGGL((assign_kernel<u16, 128, false>), grid, dim3(256), 0, s,
+                               (const u16*)x, p.N, rs, inv_norm, cv, mcount, labels, flag_list,
+                               flag_count);
+    } else {
+        if (p.D == 64)
+            hipLaunchKernelGGL((assign_kernel<float, 64, true>), grid, dim3(256), 0, s,
+                               (const float*)x, p.N, rs, inv_norm, cv, mcount, labels, flag_list,
+                               flag_count);
+        else
+            hipLaunchKernelGGL((assign_kernel<float, 128, true>), grid, dim3(256), 0, s,
+                               (const float*)x, p.N, rs, inv_norm, cv, mcount, labels, flag_list,
+                               flag_count);
+    }
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ exact recheck
+// One wave per flagged row: squared distances to every slot holding a centre,
+// summed over dimensions in index order in f64 (as the definition), argmin
+// with ties to the lowest slot.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void refine_kernel(const T* __restrict__ X, int N, int normalize,
+                                                     RowSet rs, CentView cv,
+                                                     const int32_t* __restrict__ mcount,
+                                                     const int32_t* __restrict__ flag_list,
+                                                     const int32_t* __restrict__ flag_count,
+                                                     int32_t* __restrict__ labels) {
+#pragma clang fp contract(off)
+    __shared__ float xs[4][D];
+    const int bh = blockIdx.y;
+    if (rs.active && !rs.active[bh]) return;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int cnt = flag_count[bh];
+    const int M = mcount ? min(mcount[bh], cv.m) : cv.m;
+    const int64_t cbase = (int64_t)bh * cv.cap + cv.base;
+    for (int base = blockIdx.x * 4; base < cnt; base += gridDim.x * 4) {
+        const int e = base + w;
+        const bool live = e < cnt;
+        int r = 0;
+        if (live) {
+            r = flag_list[(int64_t)bh * N + e];
+            const int64_t tok = rs.rows ? rs.rows[(int64_t)bh * N + r] : r;
+            const T* xr = row_ptr(X, N, D, bh, tok);
+            double nrm = 1.0;
+            if (normalize) {
+                double v = (l == 0) ? seq_norm(xr, D) : 0.0;
+                nrm = __shfl(v, 0);
+            }
+            for (int d = l; d < D; d += 64) {
+                float xv = elem<T>::load(xr, d);
+                xs[w][d] = normalize ? (float)((double)xv / nrm) : xv;
+            }
+        }
+        __syncthreads();
+        if (live) {
+            double best = INFINITY;
+            int bj = 0x7fffffff;
+            for (int j = l; j < M; j += 64) {
+                if (!(cv.cn2[cbase + j] < INFINITY)) continue;
+                const float* cp = cv.cent + (cbase + j) * D;
+                double s = 0.0;
+                for (int d = 0; d < D; ++d) {
+                    double df = (double)xs[w][d] - (double)cp[d];
+                    s += df * df;
+                }
+                if (s < best) { best = s; bj = j; }
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const double ob = __shfl_xor(best, o);
+                const int oj = __shfl_xor(bj, o);
+                if (ob < best || (ob == best && oj < bj)) { best = ob; bj = oj; }
+            }
+            if (l == 0 && bj != 0x7fffffff) labels[(int64_t)bh * N + r] = bj;
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_refine(const Prob& p, const void* x, int normalize, RowSet rs, CentView cv,
+                         const int32_t* mcount, const int32_t* flag_list, const int32_t* flag_count,
+                         int32_t* labels, hipStream_t s) {
+    // enough workgroups to cover a few percent of the rows in one pass
+    int gx = (p.N / 4 + 255) / 256;
+    if (gx < 4) gx = 4;
+    if (gx > 256) gx = 256;
+    dim3 grid((unsigned)gx, (unsigned)p.BH);
+    if (p.bf16) {
+        if (p.D == 64)
+            hipLaunchKernelGGL((refine_kernel<u16, 64>), grid, dim3(256), 0, s, (const u16*)x, p.N,
+                               normalize, rs, cv, mcount, flag_list, flag_count, labels);
+        else
+            hipLaunchKernelGGL((refine_kernel<u16, 128>), grid, dim3(256), 0, s, (const u16*)x, p.N,
+                               normalize, rs, cv, mcount, flag_list, flag_count, labels);
+    } else {
+        if (p.D == 64)
+            hipLaunchKernelGGL((refine_kernel<float, 64>), grid, dim3(256), 0, s, (const float*)x,
+                               p.N, normalize, rs, cv, mcount, flag_list, flag_count, labels);
+        else
+            hipLaunchKernelGGL((refine_kernel<float, 128>), grid, dim3(256), 0, s, (const float*)x,
+                               p.N, normalize, rs, cv, mcount, flag_list, flag_count, labels);
+    }
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ update
+// Each wave walks 64 consecutive rows with one lane per dimension, folding
+// runs of equal labels in registers before one atomic add per run.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__ X, int N, RowSet rs,
+                                                           const float* __restrict__ inv_norm,
+                                                           const int32_t* __restrict__ labels,
+                                                           CentView cv) {
+    constexpr int E = D / 64;
+    const int bh = blockIdx.y;
+    if (rs.active && !rs.active[bh]) return;
+    const int n = rs.nrows ? rs.nrows[bh] : N;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int base = blockIdx.x * 256 + w * 64;
+    if (base >= n) return;
+    const int r = base + l;
+    const bool okr = r < n;
+    const int lab_l = okr ? labels[(int64_t)bh * N + r] : -1;
+    const int tok_l = okr ? (rs.rows ? rs.rows[(int64_t)bh * N + r] : r) : 0;
+    const float s_l = (inv_norm && okr) ? inv_norm[(int64_t)bh * N + tok_l] : 1.0f;
+    const int rows_here = min(64, n - base);
+    const int64_t cbase = (int64_t)bh * cv.cap + cv.base;
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+    int cur = -1, run = 0;
+    for (int q = 0; q < rows_here; ++q) {
+        const int lab = __shfl(lab_l, q);
+        const int tok = __shfl(tok_l, q);
+        const float s = __shfl(s_l, q);
+        if (lab != cur) {
+            if (cur >= 0) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) atomicAdd(&cv.sums[(cbase + cur) * D + l + 64 * e], acc[e]);
+                if (l == 0) atomicAdd(&cv.cnt[cbase + cur], run);
+            }
+            cur = lab;
+            run = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+        }
+        const T* xp = row_ptr(X, N, D, bh, tok);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += s * elem<T>::load(xp, l + 64 * e);
+        run++;
+    }
+    if (cur >= 0) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) atomicAdd(&cv.sums[(cbase + cur) * D + l + 64 * e], acc[e]);
+        if (l == 0) atomicAdd(&cv.cnt[cbase + cur], run);
+    }
+}
+
+hipError_t launch_update_accum(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
+                               const int32_t* labels, CentView cv, hipStream_t s) {
+    dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)p.BH);
+    if (p.bf16) {
+        if (p.D == 64)
+            hipLaunchKernelGGL((update_accum_kernel<u16, 64>), grid, dim3(256), 0, s, (const u16*)x,
+                               p.N, rs, inv_norm, labels, cv);
+        else
+            hipLaunchKernelGGL((update_accum_kernel<u16, 128>), grid, dim3(256), 0, s,
+                               (const u16*)x, p.N, rs, inv_norm, labels, cv);
+    } else {
+        if (p.D == 64)
+            hipLaunchKernelGGL((update_accum_kernel<float, 64>), grid, dim3(256), 0, s,
+                               (const float*)x, p.N, rs, inv_norm, labels, cv);
+        else
+            hipLaunchKernelGGL((update_accum_kernel<float, 128>), grid, dim3(256), 0, s,
+                               (const float*)x, p.N, rs, inv_norm, labels, cv);
+    }
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ multi-stage bookkeeping
+__global__ void stage_reset_kernel(int BH, int N, StageState st) {
+    int bh = blockIdx.x * blockDim.x + threadIdx.x;
+    if (bh >= BH) return;
+    st.nu[bh] = N;
+    st.slots[bh] = 0;
+    st.full[bh] = 0;
+    st.active[bh] = 1;
+    st.n_stages[bh] = 0;
+    st.tau[bh] = 0.0;
+    if (st.stage_sizes)
+        for (int i = 0; i < 8; ++i) st.stage_sizes[bh * 8 + i] = -1;
+}
+
+hipError_t launch_stage_reset(const Prob& p, StageState st, hipStream_t s) {
+    hipLaunchKernelGGL(stage_reset_kernel, dim3((p.BH + 63) / 64), dim3(64), 0, s, p.BH, p.N, st);
+    return hipGetLastError();
+}
+
+// Algorithm 1 loop head: a head runs stage t while U is non-empty and fewer
+// than Nmax slots are used; U non-empty at Nmax sets F.
+__global__ void stage_begin_kernel(int BH, StageState st, int t, int nmax) {
+    int bh = blockIdx.x * blockDim.x + threadIdx.x;
+    if (bh >= BH) return;
+    const int nu = st.nu[bh], slots = st.slots[bh];
+    const bool act = nu > 0 && slots < nmax;
+    if (nu > 0 && slots >= nmax) st.full[bh] = 1;
+    st.active[bh] = act ? 1 : 0;
+    if (act) {
+        st.n_stages[bh] = t + 1;
+        if (st.stage_sizes && t < 8) st.stage_sizes[bh * 8 + t] = nu;
+    }
+}
+
+hipError_t launch_stage_begin(const Prob& p, StageState st, int t, int nmax, hipStream_t s) {
+    hipLaunchKernelGGL(stage_begin_kernel, dim3((p.BH + 63) / 64), dim3(64), 0, s, p.BH, st, t, nmax);
+    return hipGetLastError();
+}
+
+// Euclidean distance of each clustered row to its stage centre (f64, index order).
+template <typename T>
+__global__ __launch_bounds__(256) void stage_dist_kernel(const T* __restrict__ x, int N, int D,
+                                                         RowSet rs, const int32_t* __restrict__ labels,
+                                                         CentView cv, double* __restrict__ dist) {
+#pragma clang fp contract(off)
+    const int bh = blockIdx.y;
+    if (rs.active && !rs.active[bh]) return;
+    const int n = rs.nrows ? rs.nrows[bh] : N;
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= n) return;
+    const int64_t tok = rs.rows ? rs.rows[(int64_t)bh * N + r] : r;
+    const T* xr = row_ptr(x, N, D, bh, tok);
+    const float* c = cv.cent + ((int64_t)bh * cv.cap + cv.base + labels[(int64_t)bh * N + r]) * D;
+    double s = 0.0;
+    for (int d = 0; d < D; ++d) {
+        double df = (double)elem<T>::load(xr, d) - (double)c[d];
+        s += df * df;
+    }
+    dist[(int64_t)bh * N + r] = sqrt(s);
+}
+
+hipError_t launch_stage_dist(const Prob& p, const void* k, RowSet rs, const int32_t* labels,
+                             CentView cv, double* dist, hipStream_t s) {
+    dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)p.BH);
+    if (p.bf16)
+        hipLaunchKernelGGL(stage_dist_kernel<u16>, grid, dim3(256), 0, s, (const u16*)k, p.N, p.D,
+                           rs, labels, cv, dist);
+    else
+        hipLaunchKernelGGL(stage_dist_kernel<float>, grid, dim3(256), 0, s, (const float*)k, p.N,
+                           p.D, rs, labels, cv, dist);
+    return hipGetLastError();
+}
+
+// tau = tau_mult x mean distance over all N keys (stage 0 clusters every key).
+// Fixed reduction order: strided per-thread sums, then a tree.
+__global__ __launch_bounds__(256) void stage_tau_kernel(int N, StageState st, double tau_mult) {
+    __shared__ double part[256];
+    const int bh = blockIdx.x;
+    if (!st.active[bh]) return;
+    const double* dd = st.dist + (int64_t)bh * N;
+    double s = 0.0;
+    for (int r = threadIdx.x; r < N; r += 256) s += dd[r];
+    part[threadIdx.x] = s;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (threadIdx.x < o) part[threadIdx.x] += part[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) st.tau[bh] = tau_mult * part[0] / (double)N;
+}
+
+hipError_t launch_stage_tau(const Prob& p, StageState st, double tau_mult, hipStream_t s) {
+    hipLaunchKernelGGL(stage_tau_kernel, dim3(p.BH), dim3(256), 0, s, p.N, st, tau_mult);
+    return hipGetLastError();
+}
+
+// U <- {u in U : dist(u) >= tau}, order kept (Algorithm 1 steps 11-16); slots += m_t.
+__global__ __launch_bounds__(1024) void stage_compact_kernel(int N, StageState st,
+                                                             const int32_t* __restrict__ u_in,
+                                                             int32_t* __restrict__ u_out, int m_t) {
+    __shared__ int wsum[16];
+    __shared__ int sh_total;
+    const int bh = blockIdx.x;
+    if (!st.active[bh]) return;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int nu = st.nu[bh];
+    const double tau = st.tau[bh];
+    const double* dd = st.dist + (int64_t)bh * N;
+    int running = 0;
+    for (int base = 0; base < nu; base += 1024) {
+        const int r = base + tid;
+        const bool keep = r < nu && !(dd[r] < tau);
+        const uint64_t bal = __ballot(keep);
+        const int in_wave = __popcll(bal & ((1ull << l) - 1ull));
+        if (l == 0) wsum[w] = __popcll(bal);
+        __syncthreads();
+        int before = 0;
+        for (int i = 0; i < w; ++i) before += wsum[i];
+        if (tid == 0) {
+            int tot = 0;
+            for (int i = 0; i < 16; ++i) tot += wsum[i];
+            sh_total = tot;
+        }
+        if (keep) {
+            const int id = u_in ? u_in[(int64_t)bh * N + r] : r;
+            u_out[(int64_t)bh * N + running + before + in_wave] = id;
+        }
+        __syncthreads();
+        running += sh_total;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        st.nu[bh] = running;
+        st.slots[bh] += m_t;
+    }
+}
+
+hipError_t launch_stage_compact(const Prob& p, StageState st, const int32_t* u_in, int32_t* u_out,
+                                int m_t, hipStream_t s) {
+    hipLaunchKernelGGL(stage_compact_kernel, dim3(p.BH), dim3(1024), 0, s, p.N, st, u_in, u_out, m_t);
+    return hipGetLastError();
+}
+
+__global__ void stage_end_kernel(int BH, StageState st, int nmax, int32_t* n_clusters,
+                                 uint8_t* full_out, float* tau_out) {
+    int bh = blockIdx.x * blockDim.x + threadIdx.x;
+    if (bh >= BH) return;
+    const int nu = st.nu[bh], slots = st.slots[bh];
+    if (nu > 0 && slots >= nmax) st.full[bh] = 1;
+    n_clusters[bh] = slots;
+    full_out[bh] = st.full[bh];
+    tau_out[bh] = (float)st.tau[bh];
+    const int t = st.n_stages[bh];
+    if (st.stage_sizes && t < 8) st.stage_sizes[bh * 8 + t] = nu;
+}
+
+hipError_t launch_stage_end(const Prob& p, StageState st, int t_total, int nmax,
+                            int32_t* n_clusters, uint8_t* full_out, float* tau_out, hipStream_t s) {
+    (void)t_total;
+    hipLaunchKernelGGL(stage_end_kernel, dim3((p.BH + 63) / 64), dim3(64), 0, s, p.BH, st, nmax,
+                       n_clusters, full_out, tau_out);
+    return hipGetLastError();
+}
+
+}  // namespace adc

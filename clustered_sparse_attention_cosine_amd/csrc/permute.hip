@@ -1,0 +1,224 @@
+// Cluster-contiguous layout for gfx950: member counts, offsets, a stable
+// permutation (ascending id inside a cluster) and a gather that writes the
+// permuted K/V copies together with per-cluster means and per-dimension
+// max/min. This is the "K* <- K[Index], V* <- V[Index]" gather of Algorithm 3
+// (AdaCluster paper, section 3.3) laid out once per layer instead of per query.
+#include <math.h>
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace adc {
+
+hipError_t fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+
+__global__ __launch_bounds__(256) void histogram_kernel(const int32_t* __restrict__ labels,
+                                                        int64_t total, int N, int M,
+                                                        int32_t* __restrict__ cnt) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int64_t bh = i / N;
+    const int lab = labels[i];
+    if (lab >= 0 && lab < M) atomicAdd(&cnt[bh * M + lab], 1);
+}
+
+hipError_t launch_histogram(const Prob& p, const int32_t* labels, int M, int32_t* cnt,
+                            hipStream_t s) {
+    hipError_t e = fill_i32(cnt, (int64_t)p.BH * M, 0, s);
+    if (e != hipSuccess) return e;
+    int64_t total = (int64_t)p.BH * p.N;
+    hipLaunchKernelGGL(histogram_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                       labels, total, p.N, M, cnt);
+    return hipGetLastError();
+}
+
+// Exclusive scan of the counts (one workgroup per head, M <= 8192).
+__global__ __launch_bounds__(1024) void scan_offsets_kernel(const int32_t* __restrict__ cnt, int M,
+                                                            int32_t* __restrict__ sizes_out,
+                                                            int32_t* __restrict__ offsets) {
+    __shared__ int wsum[16];
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int per = (M + 1023) / 1024;
+    const int beg = tid * per;
+    const int32_t* c = cnt + (int64_t)bh * M;
+    int local = 0;
+    for (int i = 0; i < per; ++i)
+        if (beg + i < M) local += c[beg + i];
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int v = __shfl_up(incl, o);
+        if (l >= o) incl += v;
+    }
+    if (l == 63) wsum[w] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int i = 0; i < w; ++i) before += wsum[i];
+    int run = before + incl - local;
+    int32_t* off = offsets + (int64_t)bh * (M + 1);
+    for (int i = 0; i < per; ++i) {
+        const int j = beg + i;
+        if (j < M) {
+            off[j] = run;
+            run += c[j];
+            if (sizes_out) sizes_out[(int64_t)bh * M + j] = c[j];
+        }
+    }
+    if (tid == 1023) off[M] = run;
+}
+
+hipError_t launch_scan_offsets(const Prob& p, const int32_t* cnt, int M, int32_t* sizes_out,
+                               int32_t* offsets, hipStream_t s) {
+    hipLaunchKernelGGL(scan_offsets_kernel, dim3(p.BH), dim3(1024), 0, s, cnt, M, sizes_out, offsets);
+    return hipGetLastError();
+}
+
+// Stable rank: one workgroup per head sweeps the rows in chunks of 1024.
+// Inside a wave, lanes with equal labels are matched with ballots; the waves
+// of a chunk then take positions from per-label running counters in LDS in
+// wave order, so a row's rank counts exactly the earlier rows of its cluster.
+__global__ __launch_bounds__(1024) void stable_rank_kernel(const int32_t* __restrict__ labels,
+                                                           int N, int M,
+                                                           const int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ perm) {
+    __shared__ int running[8192];
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    for (int j = tid; j < M; j += 1024) running[j] = 0;
+    int nbits = 0;
+    while ((1 << nbits) < M) ++nbits;
+    const int32_t* lab_h = labels + (int64_t)bh * N;
+    const int32_t* off = offsets + (int64_t)bh * (M + 1);
+    const uint64_t lt = (l == 0) ? 0ull : (~0ull >> (64 - l));
+    __syncthreads();
+    for (int base = 0; base < N; base += 1024) {
+        const int i = base + tid;
+        const int raw = i < N ? lab_h[i] : -1;
+        const bool ok = raw >= 0 && raw < M;   // rows with out-of-range labels are left out
+        const int lab = ok ? raw : 0;
+        uint64_t m = __ballot(ok);
+        for (int bit = 0; bit < nbits; ++bit) {
+            const bool set = (lab >> bit) & 1;
+            const uint64_t b = __ballot(ok && set);
+            m &= set ? b : ~b;
+        }
+        const int rank = __popcll(m & lt);
+        const int gsize = __popcll(m);
+        const int leader = m ? __ffsll((unsigned long long)m) - 1 : 0;
+        int pos = 0;
+        for (int ww = 0; ww < 16; ++ww) {
+            if (w == ww) {
+                const bool is_leader = ok && l == leader;
+                const int bv = is_leader ? running[lab] : 0;
+                const int gb = __shfl(bv, leader);
+                if (is_leader) running[lab] = gb + gsize;
+                pos = gb + rank;
+            }
+            __syncthreads();
+        }
+        if (ok) perm[(int64_t)bh * N + off[lab] + pos] = i;
+    }
+}
+
+hipError_t launch_stable_rank(const Prob& p, const int32_t* labels, int M, const int32_t* offsets,
+                              int32_t* perm, hipStream_t s) {
+    hipLaunchKernelGGL(stable_rank_kernel, dim3(p.BH), dim3(1024), 0, s, labels, p.N, M, offsets, perm);
+    return hipGetLastError();
+}
+
+// One wave per cluster walks its members in permuted order.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void gather_stats_kernel(int N, int M,
+                                                           const int32_t* __restrict__ offsets,
+                                                           const int32_t* __restrict__ perm,
+                                                           const T* __restrict__ x,
+                                                           const T* __restrict__ v, int normalize,
+                                                           float* __restrict__ means,
+                                                           float* __restrict__ raw_means,
+                                                           T* __restrict__ xmax, T* __restrict__ xmin,
+                                                           T* __restrict__ x_perm,
+                                                           T* __restrict__ v_perm) {
+    constexpr int E = D / 64;
+    const int bh = blockIdx.y;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int j = blockIdx.x * 4 + w;
+    if (j >= M) return;
+    const int32_t* off = offsets + (int64_t)bh * (M + 1);
+    const int beg = off[j], end = off[j + 1];
+    double sum[E], rsum[E];
+    float mx[E], mn[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) { sum[e] = 0.0; rsum[e] = 0.0; mx[e] = -INFINITY; mn[e] = INFINITY; }
+    for (int r = beg; r < end; ++r) {
+        const int64_t tok = perm[(int64_t)bh * N + r];
+        const T* xr = x + ((int64_t)bh * N + tok) * D;
+        T raw[E];
+        float val[E];
+        double ss = 0.0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            raw[e] = xr[l + 64 * e];
+            val[e] = elem<T>::load(raw, e);
+            ss += (double)val[e] * (double)val[e];
+        }
+        if (normalize) {
+            ss = wave_sum_d(ss);
+            double nrm = sqrt(ss);
+            if (nrm < 1e-12) nrm = 1e-12;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                sum[e] += (double)(float)((double)val[e] / nrm);
+                rsum[e] += (double)val[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) sum[e] += (double)val[e];
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            mx[e] = fmaxf(mx[e], val[e]);
+            mn[e] = fminf(mn[e], val[e]);
+        }
+        if (x_perm) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) x_perm[((int64_t)bh * N + r) * D + l + 64 * e] = raw[e];
+        }
+        if (v_perm) {
+            const T* vr = v + ((int64_t)bh * N + tok) * D;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                v_perm[((int64_t)bh * N + r) * D + l + 64 * e] = vr[l + 64 * e];
+        }
+    }
+    const int cnt = end - beg;
+    const int64_t slot = ((int64_t)bh * M + j) * D;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int d = l + 64 * e;
+        if (cnt > 0 && means) means[slot + d] = (float)(sum[e] / (double)cnt);
+        if (raw_means) raw_means[slot + d] = cnt > 0 ? (float)(rsum[e] / (double)cnt) : 0.0f;
+        if (xmax) elem<T>::store(xmax, slot + d, cnt > 0 ? mx[e] : 0.0f);
+        if (xmin) elem<T>::store(xmin, slot + d, cnt > 0 ? mn[e] : 0.0f);
+    }
+}
+
+hipError_t launch_gather_stats(const Prob& p, int M, const int32_t* offsets, const int32_t* perm,
+                               const void* x, const void* v, int normalize, float* means,
+                               float* raw_means, void* xmax, void* xmin, void* x_perm, void* v_perm,
+                               hipStream_t s) {
+    dim3 grid((unsigned)((M + 3) / 4), (unsigned)p.BH);
+    if (p.bf16) {
+        auto k = p.D == 64 ? gather_stats_kernel<u16, 64> : gather_stats_kernel<u16, 128>;
+        hipLaunchKernelGGL(k, grid, dim3(256), 0, s, p.N, M, offsets, perm, (const u16*)x,
+                           (const u16*)v, normalize, means, raw_means, (u16*)xmax, (u16*)xmin,
+                           (u16*)x_perm, (u16*)v_perm);
+    } else {
+        auto k = p.D == 64 ? gather_stats_kernel<float, 64> : gather_stats_kernel<float, 128>;
+        hipLaunchKernelGGL(k, grid, dim3(256), 0, s, p.N, M, offsets, perm, (const float*)x,
+                           (const float*)v, normalize, means, raw_means, (float*)xmax,
+                           (float*)xmin, (float*)x_perm, (float*)v_perm);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace adc

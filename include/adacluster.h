@@ -1,0 +1,242 @@
+/*
+ * adacluster.h - C ABI of the MI355X (gfx950) clustered sparse attention library.
+ *
+ * The library implements, for one attention layer of a video diffusion
+ * transformer, the four stages of AdaCluster ("AdaCluster: Adaptive Query-Key
+ * Clustering for Sparse Attention in Video Generation", arXiv 2604.18348v1):
+ *   adacluster_cluster_q    section 3.1 and Algorithm 3 step 1
+ *   adacluster_cluster_k    section 3.2.2, Algorithm 1, and section 4.1 (tau)
+ *   adacluster_select       section 3.2.3 Eq. (1)/(2) and Algorithm 3 step 7
+ *   adacluster_sparse_attn  Algorithm 3 steps 3-9
+ * plus helpers that expose single steps (adacluster_assign, adacluster_permute).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major arrays; the
+ *     leading dimensions are [B, H] (one independent problem per (b, h)).
+ *     Scalar shape/parameter structs are HOST pointers.
+ *   - Ownership: the caller allocates every buffer, including the workspace,
+ *     whose size the matching *_workspace() call returns. The library
+ *     allocates no device memory and keeps no state between calls.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *     stream). All work is enqueued on it; no call synchronises the host or
+ *     copies device data to the host. Outputs are valid when the stream
+ *     reaches the end of the call.
+ *   - Errors: arguments are validated before the first launch; on ADC_EINVAL,
+ *     ADC_ESHAPE, ADC_EDTYPE, ADC_EWORKSPACE or ADC_EUNSUPPORTED nothing is
+ *     launched and no output is written. ADC_EHIP reports a failed launch; the
+ *     outputs are then undefined. adacluster_last_error() returns a
+ *     thread-local, library-owned message describing the last failure.
+ *   - Supported: D in {64, 128}; dtype ADC_F32 or ADC_BF16 (Q, K, V, the
+ *     per-cluster max/min, the permuted K/V and the output share it);
+ *     1 <= clusters <= 8192; N >= 1.
+ */
+#ifndef ADACLUSTER_H
+#define ADACLUSTER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ADACLUSTER_ABI_VERSION 1
+
+typedef enum {
+    ADC_OK = 0,
+    ADC_EINVAL = -1,       /* null pointer or out-of-range parameter */
+    ADC_ESHAPE = -2,       /* unsupported B/H/N/D or cluster count */
+    ADC_EDTYPE = -3,       /* unsupported dtype */
+    ADC_EWORKSPACE = -4,   /* workspace smaller than *_workspace() */
+    ADC_EHIP = -5,         /* a HIP launch failed */
+    ADC_EUNSUPPORTED = -6  /* parameter combination not implemented */
+} adc_status;
+
+typedef enum { ADC_F32 = 0, ADC_BF16 = 1 } adc_dtype;
+
+/* Cold k-means initialisation (the paper describes only the warm start of
+ * section 3.2.2 "Efficient initialization"; see the DESIGN notes):
+ *   KMEANSPP  seeded D^2 sampling (Arthur and Vassilvitskii 2007)
+ *   SAMPLE    seeded systematic sample: slot j takes row floor((j n + r) / m)
+ *   CALLER    centres supplied by the caller (warm start, fixed counts only) */
+typedef enum { ADC_INIT_KMEANSPP = 0, ADC_INIT_SAMPLE = 1, ADC_INIT_CALLER = 2 } adc_init;
+
+/* Cluster significance: QUEST = Eq. (1) of section 3.2.3 evaluated as the
+ * two-matmul form of Eq. (2) with K+ / K- the per-cluster max / min;
+ * CENTROID = qrep . key-centre (the prior clustering method's estimate). */
+typedef enum { ADC_SCORE_QUEST = 0, ADC_SCORE_CENTROID = 1 } adc_score;
+
+/* Selection rule: TOPP = shortest prefix (by l_b = score*scale + ln n_b)
+ * whose softmax mass reaches top_p; TOPK = argtopk of Algorithm 3 step 7. */
+typedef enum { ADC_SELECT_TOPP = 0, ADC_SELECT_TOPK = 1 } adc_select;
+
+typedef struct {
+    int32_t B, H, N, D;
+    int32_t dtype;          /* adc_dtype */
+} adc_shape;
+
+typedef struct {
+    int32_t n_clusters;     /* Cq */
+    int32_t iters;          /* Lloyd iterations, >= 1 */
+    int32_t init;           /* adc_init */
+    int32_t pad_;
+    uint64_t seed;
+} adc_q_params;
+
+typedef struct {
+    int32_t base_clusters;  /* m0: first-stage count (the fixed count when adaptive == 0) */
+    int32_t max_clusters;   /* Nmax: slot capacity; adaptive stages are m0, m0, 2 m0, ... */
+    int32_t iters;          /* Lloyd iterations per k-means call, >= 1 */
+    float tau_mult;         /* tau = tau_mult x mean stage-0 distance (1.5 in section 4.1) */
+    int32_t adaptive;       /* 1: Algorithm 1 multi-stage, 0: one k-means with m0 */
+    int32_t init;           /* adc_init (CALLER requires adaptive == 0) */
+    uint64_t seed;
+} adc_k_params;
+
+int32_t adacluster_abi_version(void);
+const char* adacluster_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Query clustering: A_q, C_q <- KMeans(Normalize(Q)) (section 3.1, Algorithm 3
+ * step 1). Queries are scaled to unit length; Lloyd's algorithm runs
+ * `iters` rounds of (assign to the nearest centre, move centres to member
+ * means) in the normalised space. Centres are NOT renormalised.
+ *   q              [B,H,N,D] dtype            raw queries
+ *   init_centroids [B,H,Cq,D] f32 iff init == CALLER, else NULL
+ *   assign         [B,H,N] int32   out: cluster of each query (last assignment)
+ *   centroids      [B,H,Cq,D] f32  out: member means of the normalised queries
+ *                                  (clusters with no members keep their centre)
+ *   sizes          [B,H,Cq] int32  out: member counts
+ *   qrep           [B,H,Cq,D] f32  out: member means of the RAW queries (the
+ *                                  cluster representative used for scoring; 0 if empty)
+ *   perm           [B,H,N] int32   out: query ids in cluster-contiguous order,
+ *                                  ascending id inside a cluster
+ *   offsets        [B,H,Cq+1] int32 out: start of each cluster in perm
+ */
+size_t adacluster_cluster_q_workspace(const adc_shape* shape, const adc_q_params* params);
+int32_t adacluster_cluster_q(const adc_shape* shape, const adc_q_params* params,
+                             const void* q, const float* init_centroids,
+                             int32_t* assign, float* centroids, int32_t* sizes,
+                             float* qrep, int32_t* perm, int32_t* offsets,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Key clustering, Algorithm 1 (MultiStageClustering) with tau from section 4.1.
+ * Stage t clusters the keys still unassigned (U) into m_t = m0 (t = 0),
+ * m0 * 2^(t-1) (t >= 1) new slots; tau = tau_mult x the mean Euclidean
+ * distance of all keys to their stage-0 centre; a key leaves U when strictly
+ * closer than tau to its stage centre. The loop ends when U is empty, or when
+ * the slot count reaches Nmax with U non-empty (then full_attn = 1: the head
+ * is hard to compress and gets dense attention). Finally every key goes to
+ * its nearest slot holding a centre, centres are refreshed to member means,
+ * and per-slot max/min and the cluster-contiguous K/V copies are built.
+ *   k, v           [B,H,N,D] dtype
+ *   init_centroids [B,H,m0,D] f32 iff init == CALLER (adaptive == 0), else NULL
+ *   n_clusters     [B,H] int32   out: slots used (m0, 2 m0, 4 m0, ... <= Nmax)
+ *   full_attn      [B,H] uint8   out: F of Algorithm 1
+ *   tau            [B,H] f32     out: threshold (0 when adaptive == 0)
+ *   assign         [B,H,N] int32 out: slot of each key
+ *   centroids      [B,H,Nmax,D] f32 out: slot centres (unused slots: 0)
+ *   sizes          [B,H,Nmax] int32 out: members per slot (0 for empty/unused)
+ *   kmax, kmin     [B,H,Nmax,D] dtype out: per-slot, per-dimension max / min
+ *                  of the member keys (0 for empty slots)
+ *   perm           [B,H,N] int32 out: key ids in slot-contiguous order
+ *   offsets        [B,H,Nmax+1] int32 out: slot starts in perm (entries past
+ *                  n_clusters repeat N)
+ *   k_perm, v_perm [B,H,N,D] dtype out: K and V rows in perm order
+ *   stage_sizes    [B,H,8] int32 out (may be NULL): |U| at the start of each
+ *                  stage and after the last one, -1 past the end
+ */
+size_t adacluster_cluster_k_workspace(const adc_shape* shape, const adc_k_params* params);
+int32_t adacluster_cluster_k(const adc_shape* shape, const adc_k_params* params,
+                             const void* k, const void* v, const float* init_centroids,
+                             int32_t* n_clusters, uint8_t* full_attn, float* tau,
+                             int32_t* assign, float* centroids, int32_t* sizes,
+                             void* kmax, void* kmin, int32_t* perm, int32_t* offsets,
+                             void* k_perm, void* v_perm, int32_t* stage_sizes,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Critical-cluster selection (section 3.2.3 and Algorithm 3 steps 6-7).
+ * For q-cluster a and slot b with members (b < n_clusters[b,h]):
+ *   QUEST     S_ab = qrep_a+ . kmax_b + qrep_a- . kmin_b   (Eq. (2) == Eq. (1))
+ *   CENTROID  S_ab = qrep_a . centroid_b
+ * TOPP: l_b = S_ab * scale + ln sizes_b; the shortest prefix in descending l
+ * (ties to the lower b) whose softmax mass reaches top_p, at least one slot.
+ * TOPK: the top_k largest S_ab (ties to the lower b).
+ * Heads with full_attn = 1, and top_p >= 1, select every slot with members.
+ *   qrep       [B,H,Cq,D] f32          kmax, kmin [B,H,Ck,D] dtype (QUEST)
+ *   centroids  [B,H,Ck,D] f32 (CENTROID; may be NULL for QUEST)
+ *   k_sizes    [B,H,Ck] int32          n_clusters [B,H] int32   full_attn [B,H] uint8
+ *   sel_mask   [B,H,Cq,ceil(Ck/32)] uint32 out: bit b of row a set = selected
+ *   sel_keys   [B,H,Cq] int32 out: keys covered by the selected slots
+ * Ck is the slot capacity (Nmax); scale is normally 1/sqrt(D).
+ */
+size_t adacluster_select_workspace(const adc_shape* shape, int32_t Cq, int32_t Ck);
+int32_t adacluster_select(const adc_shape* shape, int32_t Cq, int32_t Ck,
+                          const float* qrep, const void* kmax, const void* kmin,
+                          const float* centroids, const int32_t* k_sizes,
+                          const int32_t* n_clusters, const uint8_t* full_attn,
+                          int32_t score, int32_t rule, float top_p, int32_t top_k,
+                          float scale, uint32_t* sel_mask, int32_t* sel_keys,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Sparse attention over the selected key clusters (Algorithm 3 steps 8-9):
+ * every query i of q-cluster a attends, with an exact softmax at scale
+ * `scale`, to all keys of the slots selected in row a of sel_mask:
+ *   o_i = sum_j softmax_j(scale q_i.k_j) v_j,   lse_i = log sum_j exp(scale q_i.k_j)
+ * Queries are read through q_perm/q_offsets (cluster-contiguous order) and
+ * outputs are written in the original token order. A row with no selected
+ * key gets o = 0 and lse = -inf.
+ *   q          [B,H,N,D] dtype         q_perm [B,H,N], q_offsets [B,H,Cq+1] int32
+ *   k_perm, v_perm [B,H,N,D] dtype     (slot-contiguous copies from cluster_k)
+ *   k_offsets  [B,H,Ck+1] int32        sel_mask [B,H,Cq,ceil(Ck/32)] uint32
+ *   out        [B,H,N,D] dtype out     lse [B,H,N] f32 out (may be NULL)
+ * Computation: bf16 matrix-core products with f32 accumulation (f32 inputs
+ * are rounded to bf16 when staged), online softmax in f32.
+ */
+size_t adacluster_sparse_attn_workspace(const adc_shape* shape, int32_t Cq, int32_t Ck);
+int32_t adacluster_sparse_attn(const adc_shape* shape, int32_t Cq, int32_t Ck,
+                               const void* q, const int32_t* q_perm, const int32_t* q_offsets,
+                               const void* k_perm, const void* v_perm,
+                               const int32_t* k_offsets, const uint32_t* sel_mask,
+                               float scale, void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Helper: one assignment step (argmin_j ||x_i - c_j||^2, ties to the lowest j)
+ * of the k-means used by both cluster calls. normalize != 0 scales each row of
+ * x to unit length first (the query side).
+ *   x          [B,H,N,D] dtype     centroids [B,H,M,D] f32
+ *   valid      [B,H,M] uint8 (NULL = all slots hold a centre)
+ *   assign     [B,H,N] int32 out
+ */
+size_t adacluster_assign_workspace(const adc_shape* shape, int32_t M);
+int32_t adacluster_assign(const adc_shape* shape, int32_t M, int32_t normalize,
+                          const void* x, const float* centroids, const uint8_t* valid,
+                          int32_t* assign, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* ------------------------------------------------------------------------
+ * Helper: cluster-contiguous layout from given labels (the gather of
+ * Algorithm 3 step 8): sizes, offsets (exclusive scan), a stable permutation
+ * (ascending id inside a cluster), member means, per-dimension max/min and
+ * the permuted copies of x and v. Optional outputs may be NULL.
+ *   assign   [B,H,N] int32 (values in [0, M))
+ *   x        [B,H,N,D] dtype; v [B,H,N,D] dtype or NULL
+ *   sizes [B,H,M] int32, offsets [B,H,M+1] int32, perm [B,H,N] int32 out
+ *   means [B,H,M,D] f32 out or NULL (empty clusters: left unchanged)
+ *   xmax, xmin [B,H,M,D] dtype out or NULL; x_perm, v_perm [B,H,N,D] dtype out or NULL
+ */
+size_t adacluster_permute_workspace(const adc_shape* shape, int32_t M);
+int32_t adacluster_permute(const adc_shape* shape, int32_t M, const int32_t* assign,
+                           const void* x, const void* v, int32_t* sizes, int32_t* offsets,
+                           int32_t* perm, float* means, void* xmax, void* xmin,
+                           void* x_perm, void* v_perm, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ADACLUSTER_H */
