@@ -66,7 +66,8 @@ _SIGS = {
     "adacluster_select": (_I32, [_VP, _I32, _I32] + [_VP] * 7 + [_I32, _I32, _F32, _I32, _F32]
                           + [_VP, _VP, _VP, _SZ, _VP]),
     "adacluster_sparse_attn_workspace": (_SZ, [_VP, _I32, _I32]),
-    "adacluster_sparse_attn": (_I32, [_VP, _I32, _I32] + [_VP] * 7 + [_F32, _VP, _VP, _VP, _SZ, _VP]),
+    "adacluster_sparse_attn": (_I32, [_VP, _I32, _I32] + [_VP] * 7
+                               + [_F32, _VP, _I32, _VP, _VP, _SZ, _VP]),
     "adacluster_assign_workspace": (_SZ, [_VP, _I32]),
     "adacluster_assign": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "adacluster_permute_workspace": (_SZ, [_VP, _I32]),
@@ -223,7 +224,9 @@ def select(qrep, K, top_p=0.9, score="quest", rule="topp", top_k=64, scale=None)
 
 
 def sparse_attn(q, q_perm, q_offsets, k_perm, v_perm, k_offsets, sel_mask, scale=None,
-                out=None, lse=None, want_lse=True):
+                out=None, lse=None, want_lse=True, out_dtype=torch.float32):
+    """Attention of each q-cluster over its selected key slots. The output is f32
+    by default (bf16 allowed for bf16 inputs: out_dtype=torch.bfloat16)."""
     sh = _shape(q)
     B, H, N, D = q.shape
     Cq = q_offsets.shape[-1] - 1
@@ -231,13 +234,14 @@ def sparse_attn(q, q_perm, q_offsets, k_perm, v_perm, k_offsets, sel_mask, scale
     dev = q.device
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=out_dtype, device=dev)
+    odt = ADC_F32 if out.dtype == torch.float32 else ADC_BF16
     if want_lse and lse is None:
         lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
     ws = _workspace(lib().adacluster_sparse_attn_workspace(ctypes.byref(sh), Cq, Ck), dev)
     _check(lib().adacluster_sparse_attn(
         ctypes.byref(sh), Cq, Ck, _p(q), _p(q_perm), _p(q_offsets), _p(k_perm), _p(v_perm),
-        _p(k_offsets), _p(sel_mask), float(scale), _p(out), _p(lse), _p(ws), ws.numel(),
+        _p(k_offsets), _p(sel_mask), float(scale), _p(out), odt, _p(lse), _p(ws), ws.numel(),
         _stream(dev)))
     return out, lse
 

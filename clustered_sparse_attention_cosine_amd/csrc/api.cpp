@@ -463,13 +463,16 @@ size_t adacluster_sparse_attn_workspace(const adc_shape* shape, int32_t Cq, int3
 int32_t adacluster_sparse_attn(const adc_shape* shape, int32_t Cq, int32_t Ck, const void* q,
                                const int32_t* q_perm, const int32_t* q_offsets, const void* k_perm,
                                const void* v_perm, const int32_t* k_offsets,
-                               const uint32_t* sel_mask, float scale, void* out, float* lse,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+                               const uint32_t* sel_mask, float scale, void* out,
+                               int32_t out_dtype, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream) {
     int32_t st = check_sel_dims(shape, Cq, Ck);
     if (st) return st;
     REQ(q); REQ(q_perm); REQ(q_offsets); REQ(k_perm); REQ(v_perm); REQ(k_offsets); REQ(sel_mask);
     REQ(out); REQ(workspace);
     if (!(scale > 0.0f) || scale > 1e30f) return fail(ADC_EINVAL, "scale must be a finite value > 0");
+    if (out_dtype != ADC_F32 && !(out_dtype == ADC_BF16 && shape->dtype == ADC_BF16))
+        return fail(ADC_EDTYPE, "out_dtype must be ADC_F32, or ADC_BF16 with bf16 inputs");
     const size_t need = adacluster_sparse_attn_workspace(shape, Cq, Ck);
     if (workspace_bytes < need)
         return fail(ADC_EWORKSPACE, "workspace of %zu bytes is below the %zu required", workspace_bytes, need);
@@ -481,7 +484,8 @@ int32_t adacluster_sparse_attn(const adc_shape* shape, int32_t Cq, int32_t Ck, c
     HIPCHK(launch_build_runs(p, Cq, Ck, k_offsets, sel_mask, w.run_cap, w.run_start, w.run_pos, w.n_runs, s));
     HIPCHK(launch_worklist(p, Cq, q_offsets, w.items, w.n_items, s));
     HIPCHK(launch_attention(p, Cq, q, q_perm, q_offsets, k_perm, v_perm, w.run_start, w.run_pos,
-                            w.n_runs, w.run_cap, w.items, w.n_items, w.max_items, scale, out, lse, s));
+                            w.n_runs, w.run_cap, w.items, w.n_items, w.max_items, scale, out,
+                            out_dtype == ADC_F32, lse, s));
     return ADC_OK;
 }
 

@@ -97,13 +97,22 @@ hipError_t launch_worklist(const Prob& p, int Cq, const int32_t* q_offsets, int3
 }
 
 // ------------------------------------------------------------------ attention
-template <typename T> __device__ __forceinline__ void load_row8_bits(const T* p, bool ok, uint32_t (&w)[4]);
-template <> __device__ __forceinline__ void load_row8_bits<u16>(const u16* p, bool ok, uint32_t (&w)[4]) {
+// 8 consecutive elements as packed bf16 words: the value (hi) and, for f32
+// inputs, the rounding residual (lo), so f32 data is carried as hi + lo.
+template <typename T>
+__device__ __forceinline__ void load_row8_split(const T* p, bool ok, uint32_t (&hi)[4],
+                                                uint32_t (&lo)[4]);
+template <>
+__device__ __forceinline__ void load_row8_split<u16>(const u16* p, bool ok, uint32_t (&hi)[4],
+                                                     uint32_t (&lo)[4]) {
     uint4 r = make_uint4(0, 0, 0, 0);
     if (ok) r = *reinterpret_cast<const uint4*>(p);
-    w[0] = r.x; w[1] = r.y; w[2] = r.z; w[3] = r.w;
+    hi[0] = r.x; hi[1] = r.y; hi[2] = r.z; hi[3] = r.w;
+    lo[0] = lo[1] = lo[2] = lo[3] = 0;
 }
-template <> __device__ __forceinline__ void load_row8_bits<float>(const float* p, bool ok, uint32_t (&w)[4]) {
+template <>
+__device__ __forceinline__ void load_row8_split<float>(const float* p, bool ok, uint32_t (&hi)[4],
+                                                       uint32_t (&lo)[4]) {
     float v[8];
     if (ok) {
         load8<float>(p, v);
@@ -112,11 +121,19 @@ template <> __device__ __forceinline__ void load_row8_bits<float>(const float* p
         for (int i = 0; i < 8; ++i) v[i] = 0.0f;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        w[i] = (uint32_t)f2bf_bits(v[2 * i]) | ((uint32_t)f2bf_bits(v[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) {
+        const u16 h0 = f2bf_bits(v[2 * i]), h1 = f2bf_bits(v[2 * i + 1]);
+        const u16 l0 = f2bf_bits(v[2 * i] - bf_bits2f(h0));
+        const u16 l1 = f2bf_bits(v[2 * i + 1] - bf_bits2f(h1));
+        hi[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lo[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
 }
 
-template <typename T, int D>
+// PREC (f32 inputs): operands carried as bf16 hi + lo and every product of
+// order <= 1 accumulated (3 MFMAs per product instead of 1), which keeps the
+// result near f32 accuracy. TO is the output element type.
+template <typename T, int D, typename TO>
 __global__ __launch_bounds__(256) void attn_kernel(int N, int Cq, const T* __restrict__ Q,
                                                    const int32_t* __restrict__ q_perm,
                                                    const int32_t* __restrict__ q_off,
@@ -126,13 +143,15 @@ __global__ __launch_bounds__(256) void attn_kernel(int N, int Cq, const T* __res
                                                    const int32_t* __restrict__ n_runs, int run_cap,
                                                    const int32_t* __restrict__ items,
                                                    const int32_t* __restrict__ n_items, float sl2,
-                                                   T* __restrict__ O, float* __restrict__ lse) {
-    constexpr int KC = D / 32;   // 32-wide chunks of the head dimension
-    constexpr int DB = D / 16;   // 16-row blocks of O^T
-    constexpr int LDK = D + 8;   // padded LDS strides (elements)
+                                                   TO* __restrict__ O, float* __restrict__ lse) {
+    constexpr bool PREC = sizeof(T) == 4;
+    constexpr int NP = PREC ? 2 : 1;  // stored parts per operand
+    constexpr int KC = D / 32;        // 32-wide chunks of the head dimension
+    constexpr int DB = D / 16;        // 16-row blocks of O^T
+    constexpr int LDK = D + 8;        // padded LDS strides (elements)
     constexpr int LDV = 64 + 8;
-    __shared__ __attribute__((aligned(16))) u16 Ks[64 * LDK];
-    __shared__ __attribute__((aligned(16))) u16 Vt[D * LDV];
+    __shared__ __attribute__((aligned(16))) u16 Ks[NP][64 * LDK];
+    __shared__ __attribute__((aligned(16))) u16 Vt[NP][D * LDV];
     __shared__ int win_s[65], win_p[65];
     __shared__ int krow[64];
     __shared__ int sh_r0;
@@ -152,14 +171,16 @@ __global__ __launch_bounds__(256) void attn_kernel(int N, int Cq, const T* __res
     const bool wave_live = w * 16 < nrows;
     const int64_t qtok = qok ? q_perm[(int64_t)bh * N + row0 + rowi] : 0;
 
-    bf16x8 qf[KC];
+    bf16x8 qf[NP][KC];
     {
         const T* qr = Q + ((int64_t)bh * N + qtok) * D;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-            uint32_t wv[4];
-            load_row8_bits<T>(qr + kc * 32 + g * 8, qok, wv);
-            qf[kc] = __builtin_bit_cast(bf16x8, make_uint4(wv[0], wv[1], wv[2], wv[3]));
+            uint32_t hv[4], lv[4];
+            load_row8_split<T>(qr + kc * 32 + g * 8, qok, hv, lv);
+            qf[0][kc] = __builtin_bit_cast(bf16x8, make_uint4(hv[0], hv[1], hv[2], hv[3]));
+            if constexpr (PREC)
+                qf[NP - 1][kc] = __builtin_bit_cast(bf16x8, make_uint4(lv[0], lv[1], lv[2], lv[3]));
         }
     }
 
@@ -214,9 +235,11 @@ __global__ __launch_bounds__(256) void attn_kernel(int N, int Cq, const T* __res
             const int c = tid + i * 256;
             const int kr = c / (D / 8), c8 = c % (D / 8);
             const int row = krow[kr];
-            uint32_t wv[4];
-            load_row8_bits<T>(Kh + (int64_t)(row < 0 ? 0 : row) * D + c8 * 8, row >= 0, wv);
-            *reinterpret_cast<uint4*>(&Ks[kr * LDK + c8 * 8]) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+            uint32_t hv[4], lv[4];
+            load_row8_split<T>(Kh + (int64_t)(row < 0 ? 0 : row) * D + c8 * 8, row >= 0, hv, lv);
+            *reinterpret_cast<uint4*>(&Ks[0][kr * LDK + c8 * 8]) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+            if constexpr (PREC)
+                *reinterpret_cast<uint4*>(&Ks[NP - 1][kr * LDK + c8 * 8]) = make_uint4(lv[0], lv[1], lv[2], lv[3]);
         }
         // V tile, transposed: Vt[d][key]
 #pragma unroll
@@ -224,16 +247,29 @@ __global__ __launch_bounds__(256) void attn_kernel(int N, int Cq, const T* __res
             const int c = tid + i * 256;
             const int kk = c % 32, c8 = c / 32;
             const int ra = krow[2 * kk], rb = krow[2 * kk + 1];
-            uint32_t va[4], vb[4];
-            load_row8_bits<T>(Vh + (int64_t)(ra < 0 ? 0 : ra) * D + c8 * 8, ra >= 0, va);
-            load_row8_bits<T>(Vh + (int64_t)(rb < 0 ? 0 : rb) * D + c8 * 8, rb >= 0, vb);
+            uint32_t va[NP][4], vb[NP][4];
+            uint32_t scratch[4];
+            load_row8_split<T>(Vh + (int64_t)(ra < 0 ? 0 : ra) * D + c8 * 8, ra >= 0, va[0],
+                               PREC ? va[NP - 1] : scratch);
+            load_row8_split<T>(Vh + (int64_t)(rb < 0 ? 0 : rb) * D + c8 * 8, rb >= 0, vb[0],
+                               PREC ? vb[NP - 1] : scratch);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t lo_w = (va[j] & 0xFFFFu) | (vb[j] << 16);
-                const uint32_t hi_w = (va[j] >> 16) | (vb[j] & 0xFFFF0000u);
-                *reinterpret_cast<uint32_t*>(&Vt[(c8 * 8 + 2 * j) * LDV + 2 * kk]) = lo_w;
-                *reinterpret_cast<uint32_t*>(&Vt[(c8 * 8 + 2 * j + 1) * LDV + 2 * kk]) = hi_w;
-            }
+            for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    uint32_t lo_w, hi_w;
+                    if constexpr (PREC) {
+                        lo_w = (va[pp][j] & 0xFFFFu) | (vb[pp][j] << 16);
+                        hi_w = (va[pp][j] >> 16) | (vb[pp][j] & 0xFFFF0000u);
+                    } else {
+                        // bf16 -> fp16 is exact for |v| in the fp16 normal range
+                        lo_w = pack_h2(__uint_as_float(va[pp][j] << 16), __uint_as_float(vb[pp][j] << 16));
+                        hi_w = pack_h2(__uint_as_float(va[pp][j] & 0xFFFF0000u),
+                                       __uint_as_float(vb[pp][j] & 0xFFFF0000u));
+                    }
+                    *reinterpret_cast<uint32_t*>(&Vt[pp][(c8 * 8 + 2 * j) * LDV + 2 * kk]) = lo_w;
+                    *reinterpret_cast<uint32_t*>(&Vt[pp][(c8 * 8 + 2 * j + 1) * LDV + 2 * kk]) = hi_w;
+                }
         }
         __syncthreads();
         const int r0_next = sh_r0;
@@ -245,8 +281,14 @@ __global__ __launch_bounds__(256) void attn_kernel(int N, int Cq, const T* __res
                 sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kc = 0; kc < KC; ++kc) {
-                    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[(kb * 16 + c16) * LDK + kc * 32 + g * 8]);
-                    sc[kb] = mfma16(ka, qf[kc], sc[kb]);
+                    const int off = (kb * 16 + c16) * LDK + kc * 32 + g * 8;
+                    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[0][off]);
+                    if constexpr (PREC) {
+                        const bf16x8 kl = *reinterpret_cast<const bf16x8*>(&Ks[NP - 1][off]);
+                        sc[kb] = mfma16(kl, qf[0][kc], sc[kb]);
+                        sc[kb] = mfma16(ka, qf[NP - 1][kc], sc[kb]);
+                    }
+                    sc[kb] = mfma16(ka, qf[0][kc], sc[kb]);
                 }
             }
             float mx = -INFINITY;
@@ -278,19 +320,43 @@ __global__ __launch_bounds__(256) void attn_kernel(int N, int Cq, const T* __res
             for (int db = 0; db < DB; ++db) o[db] *= alpha;
 #pragma unroll
             for (int kc2 = 0; kc2 < 2; ++kc2) {
-                bf16x8 pb;
+                if constexpr (PREC) {
+                    bf16x8 pb, pl;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    pb[j] = f2bf(sc[2 * kc2][j]);
-                    pb[4 + j] = f2bf(sc[2 * kc2 + 1][j]);
-                }
+                    for (int j = 0; j < 4; ++j) {
+                        pb[j] = f2bf(sc[2 * kc2][j]);
+                        pb[4 + j] = f2bf(sc[2 * kc2 + 1][j]);
+                        pl[j] = f2bf(sc[2 * kc2][j] - bf2f(pb[j]));
+                        pl[4 + j] = f2bf(sc[2 * kc2 + 1][j] - bf2f(pb[4 + j]));
+                    }
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const u16* vp = &Vt[(db * 16 + c16) * LDV + kc2 * 32 + g * 4];
-                    const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-                    const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
-                    const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-                    o[db] = mfma16(va, pb, o[db]);
+                    for (int db = 0; db < DB; ++db) {
+                        const int off = (db * 16 + c16) * LDV + kc2 * 32 + g * 4;
+                        const uint2 lo0 = *reinterpret_cast<const uint2*>(&Vt[0][off]);
+                        const uint2 hi0 = *reinterpret_cast<const uint2*>(&Vt[0][off + 16]);
+                        const uint2 lo1 = *reinterpret_cast<const uint2*>(&Vt[NP - 1][off]);
+                        const uint2 hi1 = *reinterpret_cast<const uint2*>(&Vt[NP - 1][off + 16]);
+                        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo0.x, lo0.y, hi0.x, hi0.y));
+                        const bf16x8 vl = __builtin_bit_cast(bf16x8, make_uint4(lo1.x, lo1.y, hi1.x, hi1.y));
+                        o[db] = mfma16(vl, pb, o[db]);
+                        o[db] = mfma16(va, pl, o[db]);
+                        o[db] = mfma16(va, pb, o[db]);
+                    }
+                } else {
+                    // P.V in fp16 (11-bit significand): probabilities lose at most 2^-12
+                    const uint4 pw = make_uint4(pack_h2(sc[2 * kc2][0], sc[2 * kc2][1]),
+                                                pack_h2(sc[2 * kc2][2], sc[2 * kc2][3]),
+                                                pack_h2(sc[2 * kc2 + 1][0], sc[2 * kc2 + 1][1]),
+                                                pack_h2(sc[2 * kc2 + 1][2], sc[2 * kc2 + 1][3]));
+                    const f16x8 ph = __builtin_bit_cast(f16x8, pw);
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        const int off = (db * 16 + c16) * LDV + kc2 * 32 + g * 4;
+                        const uint2 lo0 = *reinterpret_cast<const uint2*>(&Vt[0][off]);
+                        const uint2 hi0 = *reinterpret_cast<const uint2*>(&Vt[0][off + 16]);
+                        const f16x8 vh = __builtin_bit_cast(f16x8, make_uint4(lo0.x, lo0.y, hi0.x, hi0.y));
+                        o[db] = mfma16h(vh, ph, o[db]);
+                    }
                 }
             }
             m_run = m_new;
@@ -303,35 +369,47 @@ __global__ __launch_bounds__(256) void attn_kernel(int N, int Cq, const T* __res
     l_tot += __shfl_xor(l_tot, 32);
     if (qok) {
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        T* orow = O + ((int64_t)bh * N + qtok) * D;
+        TO* orow = O + ((int64_t)bh * N + qtok) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) elem<T>::store(orow, db * 16 + g * 4 + i, o[db][i] * inv);
+            for (int i = 0; i < 4; ++i) elem<TO>::store(orow, db * 16 + g * 4 + i, o[db][i] * inv);
         if (g == 0 && lse)
             lse[(int64_t)bh * N + qtok] =
                 l_tot > 0.0f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
     }
 }
 
+template <typename T, typename TO>
+static void launch_attn_t(const Prob& p, dim3 grid, int Cq, const void* q, const int32_t* q_perm,
+                          const int32_t* q_offsets, const void* k_perm, const void* v_perm,
+                          const int32_t* run_start, const int32_t* run_pos, const int32_t* n_runs,
+                          int run_cap, const int32_t* items, const int32_t* n_items, float sl2,
+                          void* out, float* lse, hipStream_t s) {
+    auto k = p.D == 64 ? attn_kernel<T, 64, TO> : attn_kernel<T, 128, TO>;
+    hipLaunchKernelGGL(k, grid, dim3(256), 0, s, p.N, Cq, (const T*)q, q_perm, q_offsets,
+                       (const T*)k_perm, (const T*)v_perm, run_start, run_pos, n_runs, run_cap,
+                       items, n_items, sl2, (TO*)out, lse);
+}
+
 hipError_t launch_attention(const Prob& p, int Cq, const void* q, const int32_t* q_perm,
                             const int32_t* q_offsets, const void* k_perm, const void* v_perm,
                             const int32_t* run_start, const int32_t* run_pos, const int32_t* n_runs,
                             int run_cap, const int32_t* items, const int32_t* n_items, int max_items,
-                            float scale, void* out, float* lse, hipStream_t s) {
+                            float scale, void* out, int out_f32, float* lse, hipStream_t s) {
     if (max_items <= 0) return hipSuccess;
     const float sl2 = scale * 1.4426950408889634f;
     dim3 grid((unsigned)max_items);
     if (p.bf16) {
-        auto k = p.D == 64 ? attn_kernel<u16, 64> : attn_kernel<u16, 128>;
-        hipLaunchKernelGGL(k, grid, dim3(256), 0, s, p.N, Cq, (const u16*)q, q_perm, q_offsets,
-                           (const u16*)k_perm, (const u16*)v_perm, run_start, run_pos, n_runs,
-                           run_cap, items, n_items, sl2, (u16*)out, lse);
+        if (out_f32)
+            launch_attn_t<u16, float>(p, grid, Cq, q, q_perm, q_offsets, k_perm, v_perm, run_start,
+                                      run_pos, n_runs, run_cap, items, n_items, sl2, out, lse, s);
+        else
+            launch_attn_t<u16, u16>(p, grid, Cq, q, q_perm, q_offsets, k_perm, v_perm, run_start,
+                                    run_pos, n_runs, run_cap, items, n_items, sl2, out, lse, s);
     } else {
-        auto k = p.D == 64 ? attn_kernel<float, 64> : attn_kernel<float, 128>;
-        hipLaunchKernelGGL(k, grid, dim3(256), 0, s, p.N, Cq, (const float*)q, q_perm, q_offsets,
-                           (const float*)k_perm, (const float*)v_perm, run_start, run_pos, n_runs,
-                           run_cap, items, n_items, sl2, (float*)out, lse);
+        launch_attn_t<float, float>(p, grid, Cq, q, q_perm, q_offsets, k_perm, v_perm, run_start,
+                                    run_pos, n_runs, run_cap, items, n_items, sl2, out, lse, s);
     }
     return hipGetLastError();
 }

@@ -70,6 +70,19 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma16h(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Two floats -> packed fp16 pair (round to nearest even), x in the low half.
+__device__ __forceinline__ uint32_t pack_h2(float x, float y) {
+    f16x2 h = {(_Float16)x, (_Float16)y};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
 // ------------------------------------------------------------------ wave / block reductions
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -140,7 +140,7 @@ hipError_t launch_attention(const Prob& p, int Cq, const void* q, const int32_t*
                             const int32_t* run_start, const int32_t* run_pos,
                             const int32_t* n_runs, int run_cap, const int32_t* items,
                             const int32_t* n_items, int max_items, float scale, void* out,
-                            float* lse, hipStream_t s);
+                            int out_f32, float* lse, hipStream_t s);
 
 constexpr int ATTN_ROWS = 64;  // query rows per attention work item
 

@@ -192,16 +192,20 @@ int32_t adacluster_select(const adc_shape* shape, int32_t Cq, int32_t Ck,
  *   q          [B,H,N,D] dtype         q_perm [B,H,N], q_offsets [B,H,Cq+1] int32
  *   k_perm, v_perm [B,H,N,D] dtype     (slot-contiguous copies from cluster_k)
  *   k_offsets  [B,H,Ck+1] int32        sel_mask [B,H,Cq,ceil(Ck/32)] uint32
- *   out        [B,H,N,D] dtype out     lse [B,H,N] f32 out (may be NULL)
- * Computation: bf16 matrix-core products with f32 accumulation (f32 inputs
- * are rounded to bf16 when staged), online softmax in f32.
+ *   out        [B,H,N,D] out, element type out_dtype (ADC_F32, or ADC_BF16 only
+ *              when the inputs are bf16)
+ *   lse        [B,H,N] f32 out (may be NULL)
+ * Computation: bf16 matrix-core products with f32 accumulation and an online
+ * softmax in f32. bf16 inputs are exact operands (the probabilities are
+ * rounded to bf16 for the P.V product); f32 inputs are carried as bf16 hi + lo
+ * pairs with three products per contraction, close to f32 accuracy.
  */
 size_t adacluster_sparse_attn_workspace(const adc_shape* shape, int32_t Cq, int32_t Ck);
 int32_t adacluster_sparse_attn(const adc_shape* shape, int32_t Cq, int32_t Ck,
                                const void* q, const int32_t* q_perm, const int32_t* q_offsets,
                                const void* k_perm, const void* v_perm,
                                const int32_t* k_offsets, const uint32_t* sel_mask,
-                               float scale, void* out, float* lse,
+                               float scale, void* out, int32_t out_dtype, float* lse,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------

@@ -121,13 +121,15 @@ def test_select_and_attn_parameter_checks():
     assert sel(score=5) == -1
     assert sel(scale=-1.0) == -1
 
-    def attn(Cq=32, Ck=64, scale=0.125, ws=1 << 40):
-        return L.adacluster_sparse_attn(ctypes.byref(sh), Cq, Ck, P, P, P, P, P, P, P, scale, P, P,
-                                        P, ws, None)
+    def attn(Cq=32, Ck=64, scale=0.125, ws=1 << 40, odt=0, shape=sh):
+        return L.adacluster_sparse_attn(ctypes.byref(shape), Cq, Ck, P, P, P, P, P, P, P, scale, P,
+                                        odt, P, P, ws, None)
     assert attn(Cq=0) == -2
     assert attn(Ck=10000) == -2
     assert attn(scale=float("inf")) == -1
     assert attn(ws=1) == -4
+    assert attn(odt=5) == -3
+    assert attn(odt=adc.ADC_BF16, shape=_shape(dt=adc.ADC_F32)) == -3
 
 
 def test_binding_refuses_cpu_tensors():

@@ -85,7 +85,6 @@ def test_select_all_equals_dense(D, dtype):
     else:
         arrs = list(x)
         xf = [a.astype(np.float32) for a in arrs]
-        xf = [synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(a)) for a in xf]  # kernel stages bf16
     ident = np.tile(np.arange(N, dtype=np.int32), (1, H, 1))
     offs = np.tile(np.array([0, N], np.int32), (1, H, 1))
     mask = np.ones((1, H, 1, 1), np.int32)
