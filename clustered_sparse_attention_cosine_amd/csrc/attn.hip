@@ -130,31 +130,193 @@ __device__ __forceinline__ void load_row8_split<float>(const float* p, bool ok, 
     }
 }
 
+// Key rows of one 64-position tile of the concatenated selection, computed by
+// one wave without LDS. Lane k holds run r0 + k of the work item: its first
+// position wp (INT_MAX past the last run) and first key row ws; run r0 holds
+// position t0; wp64 is the first position of run r0 + 64. The run holding
+// position t0 + lane is (number of run starts <= t0 + lane) - 1, counted from a
+// 64-bit mask of the starts inside the tile. Writes krow[lane] (-1 past the
+// selection) and returns the run holding position t0 + 64.
+__device__ __forceinline__ int tile_rows(int lane, int t0, int total, int r0, int wp, int ws,
+                                         int wp64, int* krow) {
+    const int s = wp - t0;
+    uint32_t lo = 0, hi = 0;
+    if (lane == 0) lo = 1u;
+    if (s >= 0 && s < 32) lo |= 1u << s;
+    else if (s >= 32 && s < 64) hi |= 1u << (s - 32);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        lo |= __shfl_xor(lo, o);
+        hi |= __shfl_xor(hi, o);
+    }
+    const uint64_t starts = ((uint64_t)hi << 32) | lo;
+    const uint64_t upto = lane == 63 ? ~0ull : ((2ull << lane) - 1ull);
+    const int k = __popcll(starts & upto) - 1;
+    const int rs_k = __shfl(ws, k), rp_k = __shfl(wp, k);
+    const int P = t0 + lane;
+    krow[lane] = P < total ? rs_k + (P - rp_k) : -1;
+    const int c = __popcll(__ballot(wp <= t0 + 64));
+    return (c == 64 && wp64 <= t0 + 64) ? r0 + 64 : r0 + c - 1;
+}
+
+// Window of 64 runs starting at run r0 (one wave).
+__device__ __forceinline__ void load_window(int lane, int r0, int R, const int32_t* rs,
+                                            const int32_t* rp, int& wp, int& ws, int& wp64) {
+    const int k = r0 + lane;
+    wp = k <= R ? rp[k] : 0x7fffffff;
+    ws = k < R ? rs[k] : 0;
+    wp64 = r0 + 64 <= R ? rp[r0 + 64] : 0x7fffffff;
+}
+
+// Global -> register staging of one K/V tile (64 key rows), NT threads.
+template <typename T, int D, int NP, int NT>
+struct TileRegs {
+    static constexpr int KTASK = 64 * (D / 8);      // 16-byte chunks of the K tile
+    static constexpr int VTASK = 32 * (D / 8);      // (key pair, 8 dims) tasks of the V tile
+    static constexpr int KT = (KTASK + NT - 1) / NT;
+    static constexpr int VT = (VTASK + NT - 1) / NT;
+    uint32_t k[KT][NP][4];
+    uint32_t va[VT][NP][4], vb[VT][NP][4];
+};
+
+template <typename T, int D, int NP, int NT>
+__device__ __forceinline__ void tile_load(TileRegs<T, D, NP, NT>& r, int tid, const int* krow,
+                                          const T* Kh, const T* Vh) {
+    using TR = TileRegs<T, D, NP, NT>;
+    constexpr bool PREC = NP == 2;
+#pragma unroll
+    for (int i = 0; i < TR::KT; ++i) {
+        const int c = tid + i * NT;
+        if (TR::KTASK % NT != 0 && c >= TR::KTASK) break;
+        const int kr = c / (D / 8), c8 = c % (D / 8);
+        const int row = krow[kr];
+        uint32_t scratch[4];
+        load_row8_split<T>(Kh + (int64_t)(row < 0 ? 0 : row) * D + c8 * 8, row >= 0, r.k[i][0],
+                           PREC ? r.k[i][NP - 1] : scratch);
+    }
+#pragma unroll
+    for (int i = 0; i < TR::VT; ++i) {
+        const int c = tid + i * NT;
+        if (TR::VTASK % NT != 0 && c >= TR::VTASK) break;
+        const int kk = c % 32, c8 = c / 32;
+        const int ra = krow[2 * kk], rb = krow[2 * kk + 1];
+        uint32_t scratch[4];
+        load_row8_split<T>(Vh + (int64_t)(ra < 0 ? 0 : ra) * D + c8 * 8, ra >= 0, r.va[i][0],
+                           PREC ? r.va[i][NP - 1] : scratch);
+        load_row8_split<T>(Vh + (int64_t)(rb < 0 ? 0 : rb) * D + c8 * 8, rb >= 0, r.vb[i][0],
+                           PREC ? r.vb[i][NP - 1] : scratch);
+    }
+}
+
+// Register -> LDS: K row-major, V transposed (fp16 for bf16 inputs, bf16 hi/lo for f32).
+template <typename T, int D, int NP, int NT, int LDK, int LDV>
+__device__ __forceinline__ void tile_store(const TileRegs<T, D, NP, NT>& r, int tid,
+                                           u16 (*Ks)[64 * LDK], u16 (*Vt)[D * LDV]) {
+    using TR = TileRegs<T, D, NP, NT>;
+    constexpr bool PREC = NP == 2;
+#pragma unroll
+    for (int i = 0; i < TR::KT; ++i) {
+        const int c = tid + i * NT;
+        if (TR::KTASK % NT != 0 && c >= TR::KTASK) break;
+        const int kr = c / (D / 8), c8 = c % (D / 8);
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp)
+            *reinterpret_cast<uint4*>(&Ks[pp][kr * LDK + c8 * 8]) =
+                make_uint4(r.k[i][pp][0], r.k[i][pp][1], r.k[i][pp][2], r.k[i][pp][3]);
+    }
+#pragma unroll
+    for (int i = 0; i < TR::VT; ++i) {
+        const int c = tid + i * NT;
+        if (TR::VTASK % NT != 0 && c >= TR::VTASK) break;
+        const int kk = c % 32, c8 = c / 32;
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t a = r.va[i][pp][j], b = r.vb[i][pp][j];
+                uint32_t lo_w, hi_w;
+                if constexpr (PREC) {
+                    lo_w = (a & 0xFFFFu) | (b << 16);
+                    hi_w = (a >> 16) | (b & 0xFFFF0000u);
+                } else {
+                    // bf16 -> fp16 is exact for |v| inside the fp16 normal range
+                    lo_w = pack_h2(__uint_as_float(a << 16), __uint_as_float(b << 16));
+                    hi_w = pack_h2(__uint_as_float(a & 0xFFFF0000u), __uint_as_float(b & 0xFFFF0000u));
+                }
+                *reinterpret_cast<uint32_t*>(&Vt[pp][(c8 * 8 + 2 * j) * LDV + 2 * kk]) = lo_w;
+                *reinterpret_cast<uint32_t*>(&Vt[pp][(c8 * 8 + 2 * j + 1) * LDV + 2 * kk]) = hi_w;
+            }
+    }
+}
+
+// Online-softmax update of one 16-query block over one 64-key tile (the lane
+// holds query c16 and keys kb*16 + 4g + i). Scores come in raw; sl2 = scale *
+// log2(e) is applied inside the exponent.
+template <int DB>
+__device__ __forceinline__ void softmax_block(f32x4 (&sc)[4], float sl2, bool mask_tail, int t0,
+                                              int g, int total, float& m_run, float& l_part,
+                                              f32x4 (&o)[DB]) {
+    if (mask_tail) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (t0 + kb * 16 + g * 4 + i >= total) sc[kb][i] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3]));
+#pragma unroll
+    for (int kb = 1; kb < 4; ++kb)
+        mx = fmaxf(mx, fmaxf(fmaxf(sc[kb][0], sc[kb][1]), fmaxf(sc[kb][2], sc[kb][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * sl2);
+    const float base = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - base);
+    float lsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], sl2, -base));
+            sc[kb][i] = pv;
+            lsum += pv;
+        }
+    l_part = fmaf(l_part, alpha, lsum);
+    if (alpha != 1.0f) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    }
+    m_run = m_new;
+}
+
+// A work item is (head, q-cluster, chunk of ATTN_ROWS query rows); the NT/64
+// waves each own RB blocks of 16 rows (a block with no rows is skipped). K/V
+// tiles of 64 keys are double-buffered in LDS: the global loads of tile t+1
+// are in flight while tile t is computed, and the key rows of tile t+2 are
+// looked up by wave 0 at the same time, so one barrier per tile suffices.
 // PREC (f32 inputs): operands carried as bf16 hi + lo and every product of
-// order <= 1 accumulated (3 MFMAs per product instead of 1), which keeps the
-// result near f32 accuracy. TO is the output element type.
-template <typename T, int D, typename TO>
-__global__ __launch_bounds__(256) void attn_kernel(int N, int Cq, const T* __restrict__ Q,
-                                                   const int32_t* __restrict__ q_perm,
-                                                   const int32_t* __restrict__ q_off,
-                                                   const T* __restrict__ Kp, const T* __restrict__ Vp,
-                                                   const int32_t* __restrict__ run_start,
-                                                   const int32_t* __restrict__ run_pos,
-                                                   const int32_t* __restrict__ n_runs, int run_cap,
-                                                   const int32_t* __restrict__ items,
-                                                   const int32_t* __restrict__ n_items, float sl2,
-                                                   TO* __restrict__ O, float* __restrict__ lse) {
+// order <= 1 accumulated (3 MFMAs per product instead of 1), near f32 accuracy.
+template <typename T, int D, typename TO, int NT, int RB>
+__global__ __launch_bounds__(NT) void attn_kernel(int N, int Cq, const T* __restrict__ Q,
+                                                  const int32_t* __restrict__ q_perm,
+                                                  const int32_t* __restrict__ q_off,
+                                                  const T* __restrict__ Kp, const T* __restrict__ Vp,
+                                                  const int32_t* __restrict__ run_start,
+                                                  const int32_t* __restrict__ run_pos,
+                                                  const int32_t* __restrict__ n_runs, int run_cap,
+                                                  const int32_t* __restrict__ items,
+                                                  const int32_t* __restrict__ n_items, float sl2,
+                                                  TO* __restrict__ O, float* __restrict__ lse) {
+    static_assert((NT / 64) * RB * 16 == ATTN_ROWS, "waves x blocks must cover a work item");
     constexpr bool PREC = sizeof(T) == 4;
     constexpr int NP = PREC ? 2 : 1;  // stored parts per operand
     constexpr int KC = D / 32;        // 32-wide chunks of the head dimension
     constexpr int DB = D / 16;        // 16-row blocks of O^T
     constexpr int LDK = D + 8;        // padded LDS strides (elements)
     constexpr int LDV = 64 + 8;
-    __shared__ __attribute__((aligned(16))) u16 Ks[NP][64 * LDK];
-    __shared__ __attribute__((aligned(16))) u16 Vt[NP][D * LDV];
-    __shared__ int win_s[65], win_p[65];
-    __shared__ int krow[64];
-    __shared__ int sh_r0;
+    __shared__ __attribute__((aligned(16))) u16 Ks[2][NP][64 * LDK];
+    __shared__ __attribute__((aligned(16))) u16 Vt[2][NP][D * LDV];
+    __shared__ int krow[3][64];
 
     const int it = blockIdx.x;
     if (it >= *n_items) return;
@@ -166,21 +328,24 @@ __global__ __launch_bounds__(256) void attn_kernel(int N, int Cq, const T* __res
     const int32_t* qo = q_off + (int64_t)bh * (Cq + 1);
     const int row0 = qo[a] + ch * ATTN_ROWS;
     const int nrows = min(ATTN_ROWS, qo[a + 1] - row0);
-    const int rowi = w * 16 + c16;
-    const bool qok = rowi < nrows;
-    const bool wave_live = w * 16 < nrows;
-    const int64_t qtok = qok ? q_perm[(int64_t)bh * N + row0 + rowi] : 0;
-
-    bf16x8 qf[NP][KC];
-    {
-        const T* qr = Q + ((int64_t)bh * N + qtok) * D;
+    bool live[RB];
+    bf16x8 qf[RB][NP][KC];
+    int64_t qtok[RB];
+    bool qok[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        live[rb] = (w * RB + rb) * 16 < nrows;
+        const int rowi = (w * RB + rb) * 16 + c16;
+        qok[rb] = rowi < nrows;
+        qtok[rb] = qok[rb] ? q_perm[(int64_t)bh * N + row0 + rowi] : 0;
+        const T* qr = Q + ((int64_t)bh * N + qtok[rb]) * D;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
             uint32_t hv[4], lv[4];
-            load_row8_split<T>(qr + kc * 32 + g * 8, qok, hv, lv);
-            qf[0][kc] = __builtin_bit_cast(bf16x8, make_uint4(hv[0], hv[1], hv[2], hv[3]));
+            load_row8_split<T>(qr + kc * 32 + g * 8, qok[rb], hv, lv);
+            qf[rb][0][kc] = __builtin_bit_cast(bf16x8, make_uint4(hv[0], hv[1], hv[2], hv[3]));
             if constexpr (PREC)
-                qf[NP - 1][kc] = __builtin_bit_cast(bf16x8, make_uint4(lv[0], lv[1], lv[2], lv[3]));
+                qf[rb][NP - 1][kc] = __builtin_bit_cast(bf16x8, make_uint4(lv[0], lv[1], lv[2], lv[3]));
         }
     }
 
@@ -189,196 +354,160 @@ __global__ __launch_bounds__(256) void attn_kernel(int N, int Cq, const T* __res
     const int32_t* rs = run_start + rbase * run_cap;
     const int32_t* rp = run_pos + rbase * (run_cap + 1);
     const int total = rp[R];
+    const int ntiles = (total + 63) / 64;
     const T* Kh = Kp + (int64_t)bh * N * D;
     const T* Vh = Vp + (int64_t)bh * N * D;
 
-    float m_run = -INFINITY, l_part = 0.0f;
-    f32x4 o[DB];
+    float m_run[RB], l_part[RB];
+    f32x4 o[RB][DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    int r0 = 0;
+    for (int rb = 0; rb < RB; ++rb) {
+        m_run[rb] = -INFINITY;
+        l_part[rb] = 0.0f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
-    for (int t0 = 0; t0 < total; t0 += 64) {
-        // key rows of positions t0 .. t0+63 of the concatenated selection
-        if (tid < 65) {
-            const int k = r0 + tid;
-            win_p[tid] = k <= R ? rp[k] : 0x7fffffff;
-            win_s[tid] = k < R ? rs[k] : 0;
+    // wave 0: row lookup for tiles 0 and 1, window for tile 2
+    int wp = 0, ws = 0, wp64 = 0, r_next = 0;
+    if (w == 0 && ntiles > 0) {
+        load_window(l, 0, R, rs, rp, wp, ws, wp64);
+        r_next = tile_rows(l, 0, total, 0, wp, ws, wp64, krow[0]);
+        if (ntiles > 1) {
+            load_window(l, r_next, R, rs, rp, wp, ws, wp64);
+            r_next = tile_rows(l, 64, total, r_next, wp, ws, wp64, krow[1]);
+            if (ntiles > 2) load_window(l, r_next, R, rs, rp, wp, ws, wp64);
         }
-        __syncthreads();
-        if (tid < 64) {
-            const int P = t0 + tid;
-            int row = -1;
-            if (P < total) {
-                int lo = 0, hi = 64;
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) >> 1;
-                    if (win_p[mid] <= P) lo = mid; else hi = mid - 1;
-                }
-                row = win_s[lo] + (P - win_p[lo]);
-            }
-            krow[tid] = row;
-            if (tid == 0) {
-                const int nxt = t0 + 64;
-                int lo = 0, hi = 64;
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) >> 1;
-                    if (win_p[mid] <= nxt) lo = mid; else hi = mid - 1;
-                }
-                sh_r0 = r0 + lo;
-            }
-        }
-        __syncthreads();
-        // K tile, row-major
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) {
-            const int c = tid + i * 256;
-            const int kr = c / (D / 8), c8 = c % (D / 8);
-            const int row = krow[kr];
-            uint32_t hv[4], lv[4];
-            load_row8_split<T>(Kh + (int64_t)(row < 0 ? 0 : row) * D + c8 * 8, row >= 0, hv, lv);
-            *reinterpret_cast<uint4*>(&Ks[0][kr * LDK + c8 * 8]) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
-            if constexpr (PREC)
-                *reinterpret_cast<uint4*>(&Ks[NP - 1][kr * LDK + c8 * 8]) = make_uint4(lv[0], lv[1], lv[2], lv[3]);
-        }
-        // V tile, transposed: Vt[d][key]
-#pragma unroll
-        for (int i = 0; i < D / 64; ++i) {
-            const int c = tid + i * 256;
-            const int kk = c % 32, c8 = c / 32;
-            const int ra = krow[2 * kk], rb = krow[2 * kk + 1];
-            uint32_t va[NP][4], vb[NP][4];
-            uint32_t scratch[4];
-            load_row8_split<T>(Vh + (int64_t)(ra < 0 ? 0 : ra) * D + c8 * 8, ra >= 0, va[0],
-                               PREC ? va[NP - 1] : scratch);
-            load_row8_split<T>(Vh + (int64_t)(rb < 0 ? 0 : rb) * D + c8 * 8, rb >= 0, vb[0],
-                               PREC ? vb[NP - 1] : scratch);
-#pragma unroll
-            for (int pp = 0; pp < NP; ++pp)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    uint32_t lo_w, hi_w;
-                    if constexpr (PREC) {
-                        lo_w = (va[pp][j] & 0xFFFFu) | (vb[pp][j] << 16);
-                        hi_w = (va[pp][j] >> 16) | (vb[pp][j] & 0xFFFF0000u);
-                    } else {
-                        // bf16 -> fp16 is exact for |v| in the fp16 normal range
-                        lo_w = pack_h2(__uint_as_float(va[pp][j] << 16), __uint_as_float(vb[pp][j] << 16));
-                        hi_w = pack_h2(__uint_as_float(va[pp][j] & 0xFFFF0000u),
-                                       __uint_as_float(vb[pp][j] & 0xFFFF0000u));
-                    }
-                    *reinterpret_cast<uint32_t*>(&Vt[pp][(c8 * 8 + 2 * j) * LDV + 2 * kk]) = lo_w;
-                    *reinterpret_cast<uint32_t*>(&Vt[pp][(c8 * 8 + 2 * j + 1) * LDV + 2 * kk]) = hi_w;
-                }
-        }
-        __syncthreads();
-        const int r0_next = sh_r0;
+    }
+    __syncthreads();
+    TileRegs<T, D, NP, NT> tr;
+    if (ntiles > 0) {
+        tile_load<T, D, NP, NT>(tr, tid, krow[0], Kh, Vh);
+        tile_store<T, D, NP, NT, LDK, LDV>(tr, tid, Ks[0], Vt[0]);
+    }
+    __syncthreads();
 
-        if (wave_live) {
-            f32x4 sc[4];
+    for (int t = 0; t < ntiles; ++t) {
+        const int b = t & 1;
+        const int t0 = t * 64;
+        if (t + 1 < ntiles) tile_load<T, D, NP, NT>(tr, tid, krow[(t + 1) % 3], Kh, Vh);
+        if (w == 0 && t + 2 < ntiles) {
+            r_next = tile_rows(l, t0 + 128, total, r_next, wp, ws, wp64, krow[(t + 2) % 3]);
+            if (t + 3 < ntiles) load_window(l, r_next, R, rs, rp, wp, ws, wp64);
+        }
+        if (live[0]) {
+            const bool mask_tail = t0 + 64 > total;
+            f32x4 sc[RB][4];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) sc[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kc = 0; kc < KC; ++kc) {
                     const int off = (kb * 16 + c16) * LDK + kc * 32 + g * 8;
-                    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[0][off]);
-                    if constexpr (PREC) {
-                        const bf16x8 kl = *reinterpret_cast<const bf16x8*>(&Ks[NP - 1][off]);
-                        sc[kb] = mfma16(kl, qf[0][kc], sc[kb]);
-                        sc[kb] = mfma16(ka, qf[NP - 1][kc], sc[kb]);
+                    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[b][0][off]);
+                    bf16x8 kl;
+                    if constexpr (PREC) kl = *reinterpret_cast<const bf16x8*>(&Ks[b][NP - 1][off]);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) {
+                        if (rb > 0 && !live[rb]) continue;
+                        if constexpr (PREC) {
+                            sc[rb][kb] = mfma16(kl, qf[rb][0][kc], sc[rb][kb]);
+                            sc[rb][kb] = mfma16(ka, qf[rb][NP - 1][kc], sc[rb][kb]);
+                        }
+                        sc[rb][kb] = mfma16(ka, qf[rb][0][kc], sc[rb][kb]);
                     }
-                    sc[kb] = mfma16(ka, qf[0][kc], sc[kb]);
                 }
             }
-            float mx = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int pos = t0 + kb * 16 + g * 4 + i;
-                    const float v = pos < total ? sc[kb][i] * sl2 : -INFINITY;
-                    sc[kb][i] = v;
-                    mx = fmaxf(mx, v);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float base = (m_new == -INFINITY) ? 0.0f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - base);
-            float lsum = 0.0f;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float pv = __builtin_amdgcn_exp2f(sc[kb][i] - base);
-                    sc[kb][i] = pv;
-                    lsum += pv;
-                }
-            l_part = l_part * alpha + lsum;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) o[db] *= alpha;
+            for (int rb = 0; rb < RB; ++rb) {
+                if (rb > 0 && !live[rb]) continue;
+                softmax_block<DB>(sc[rb], sl2, mask_tail, t0, g, total, m_run[rb], l_part[rb], o[rb]);
+            }
 #pragma unroll
             for (int kc2 = 0; kc2 < 2; ++kc2) {
                 if constexpr (PREC) {
-                    bf16x8 pb, pl;
+                    bf16x8 pb[RB], pl[RB];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        pb[j] = f2bf(sc[2 * kc2][j]);
-                        pb[4 + j] = f2bf(sc[2 * kc2 + 1][j]);
-                        pl[j] = f2bf(sc[2 * kc2][j] - bf2f(pb[j]));
-                        pl[4 + j] = f2bf(sc[2 * kc2 + 1][j] - bf2f(pb[4 + j]));
-                    }
+                    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            pb[rb][j] = f2bf(sc[rb][2 * kc2][j]);
+                            pb[rb][4 + j] = f2bf(sc[rb][2 * kc2 + 1][j]);
+                            pl[rb][j] = f2bf(sc[rb][2 * kc2][j] - bf2f(pb[rb][j]));
+                            pl[rb][4 + j] = f2bf(sc[rb][2 * kc2 + 1][j] - bf2f(pb[rb][4 + j]));
+                        }
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
                         const int off = (db * 16 + c16) * LDV + kc2 * 32 + g * 4;
-                        const uint2 lo0 = *reinterpret_cast<const uint2*>(&Vt[0][off]);
-                        const uint2 hi0 = *reinterpret_cast<const uint2*>(&Vt[0][off + 16]);
-                        const uint2 lo1 = *reinterpret_cast<const uint2*>(&Vt[NP - 1][off]);
-                        const uint2 hi1 = *reinterpret_cast<const uint2*>(&Vt[NP - 1][off + 16]);
+                        const uint2 lo0 = *reinterpret_cast<const uint2*>(&Vt[b][0][off]);
+                        const uint2 hi0 = *reinterpret_cast<const uint2*>(&Vt[b][0][off + 16]);
+                        const uint2 lo1 = *reinterpret_cast<const uint2*>(&Vt[b][NP - 1][off]);
+                        const uint2 hi1 = *reinterpret_cast<const uint2*>(&Vt[b][NP - 1][off + 16]);
                         const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo0.x, lo0.y, hi0.x, hi0.y));
                         const bf16x8 vl = __builtin_bit_cast(bf16x8, make_uint4(lo1.x, lo1.y, hi1.x, hi1.y));
-                        o[db] = mfma16(vl, pb, o[db]);
-                        o[db] = mfma16(va, pl, o[db]);
-                        o[db] = mfma16(va, pb, o[db]);
+#pragma unroll
+                        for (int rb = 0; rb < RB; ++rb) {
+                            if (rb > 0 && !live[rb]) continue;
+                            o[rb][db] = mfma16(vl, pb[rb], o[rb][db]);
+                            o[rb][db] = mfma16(va, pl[rb], o[rb][db]);
+                            o[rb][db] = mfma16(va, pb[rb], o[rb][db]);
+                        }
                     }
                 } else {
                     // P.V in fp16 (11-bit significand): probabilities lose at most 2^-12
-                    const uint4 pw = make_uint4(pack_h2(sc[2 * kc2][0], sc[2 * kc2][1]),
-                                                pack_h2(sc[2 * kc2][2], sc[2 * kc2][3]),
-                                                pack_h2(sc[2 * kc2 + 1][0], sc[2 * kc2 + 1][1]),
-                                                pack_h2(sc[2 * kc2 + 1][2], sc[2 * kc2 + 1][3]));
-                    const f16x8 ph = __builtin_bit_cast(f16x8, pw);
+                    f16x8 ph[RB];
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        ph[rb] = __builtin_bit_cast(
+                            f16x8, make_uint4(pack_h2(sc[rb][2 * kc2][0], sc[rb][2 * kc2][1]),
+                                              pack_h2(sc[rb][2 * kc2][2], sc[rb][2 * kc2][3]),
+                                              pack_h2(sc[rb][2 * kc2 + 1][0], sc[rb][2 * kc2 + 1][1]),
+                                              pack_h2(sc[rb][2 * kc2 + 1][2], sc[rb][2 * kc2 + 1][3])));
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
                         const int off = (db * 16 + c16) * LDV + kc2 * 32 + g * 4;
-                        const uint2 lo0 = *reinterpret_cast<const uint2*>(&Vt[0][off]);
-                        const uint2 hi0 = *reinterpret_cast<const uint2*>(&Vt[0][off + 16]);
+                        const uint2 lo0 = *reinterpret_cast<const uint2*>(&Vt[b][0][off]);
+                        const uint2 hi0 = *reinterpret_cast<const uint2*>(&Vt[b][0][off + 16]);
                         const f16x8 vh = __builtin_bit_cast(f16x8, make_uint4(lo0.x, lo0.y, hi0.x, hi0.y));
-                        o[db] = mfma16h(vh, ph, o[db]);
+#pragma unroll
+                        for (int rb = 0; rb < RB; ++rb) {
+                            if (rb > 0 && !live[rb]) continue;
+                            o[rb][db] = mfma16h(vh, ph[rb], o[rb][db]);
+                        }
                     }
                 }
             }
-            m_run = m_new;
         }
+        if (t + 1 < ntiles) tile_store<T, D, NP, NT, LDK, LDV>(tr, tid, Ks[b ^ 1], Vt[b ^ 1]);
         __syncthreads();
-        r0 = r0_next;
     }
 
-    float l_tot = l_part + __shfl_xor(l_part, 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    if (qok) {
-        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        TO* orow = O + ((int64_t)bh * N + qtok) * D;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+    for (int rb = 0; rb < RB; ++rb) {
+        float l_tot = l_part[rb] + __shfl_xor(l_part[rb], 16);
+        l_tot += __shfl_xor(l_tot, 32);
+        if (qok[rb]) {
+            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+            TO* orow = O + ((int64_t)bh * N + qtok[rb]) * D;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) elem<TO>::store(orow, db * 16 + g * 4 + i, o[db][i] * inv);
-        if (g == 0 && lse)
-            lse[(int64_t)bh * N + qtok] =
-                l_tot > 0.0f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    elem<TO>::store(orow, db * 16 + g * 4 + i, o[rb][db][i] * inv);
+            if (g == 0 && lse)
+                lse[(int64_t)bh * N + qtok[rb]] =
+                    l_tot > 0.0f ? (m_run[rb] + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+        }
     }
 }
+
+// Threads per workgroup and 16-row blocks per wave of the attention kernel.
+#ifndef ADC_ATTN_NT
+#define ADC_ATTN_NT 512
+#endif
+constexpr int ATTN_NT = ADC_ATTN_NT;
+constexpr int ATTN_RB = ATTN_ROWS / 16 / (ATTN_NT / 64);
 
 template <typename T, typename TO>
 static void launch_attn_t(const Prob& p, dim3 grid, int Cq, const void* q, const int32_t* q_perm,
@@ -386,8 +515,8 @@ static void launch_attn_t(const Prob& p, dim3 grid, int Cq, const void* q, const
                           const int32_t* run_start, const int32_t* run_pos, const int32_t* n_runs,
                           int run_cap, const int32_t* items, const int32_t* n_items, float sl2,
                           void* out, float* lse, hipStream_t s) {
-    auto k = p.D == 64 ? attn_kernel<T, 64, TO> : attn_kernel<T, 128, TO>;
-    hipLaunchKernelGGL(k, grid, dim3(256), 0, s, p.N, Cq, (const T*)q, q_perm, q_offsets,
+    auto k = p.D == 64 ? attn_kernel<T, 64, TO, ATTN_NT, ATTN_RB> : attn_kernel<T, 128, TO, ATTN_NT, ATTN_RB>;
+    hipLaunchKernelGGL(k, grid, dim3(ATTN_NT), 0, s, p.N, Cq, (const T*)q, q_perm, q_offsets,
                        (const T*)k_perm, (const T*)v_perm, run_start, run_pos, n_runs, run_cap,
                        items, n_items, sl2, (TO*)out, lse);
 }

@@ -142,6 +142,6 @@ hipError_t launch_attention(const Prob& p, int Cq, const void* q, const int32_t*
                             const int32_t* n_items, int max_items, float scale, void* out,
                             int out_f32, float* lse, hipStream_t s);
 
-constexpr int ATTN_ROWS = 64;  // query rows per attention work item
+constexpr int ATTN_ROWS = 128;  // query rows per attention work item
 
 }  // namespace adc
