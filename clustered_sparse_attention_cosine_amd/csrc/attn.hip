@@ -102,24 +102,25 @@ hipError_t launch_worklist(const Prob& p, int Cq, const int32_t* q_offsets, int3
 template <typename T>
 __device__ __forceinline__ void load_row8_split(const T* p, bool ok, uint32_t (&hi)[4],
                                                 uint32_t (&lo)[4]);
+// The load is unconditional (p must be a valid address; callers clamp it) and
+// `ok` only selects zeros, so no branch hides the load from the counters.
 template <>
 __device__ __forceinline__ void load_row8_split<u16>(const u16* p, bool ok, uint32_t (&hi)[4],
                                                      uint32_t (&lo)[4]) {
-    uint4 r = make_uint4(0, 0, 0, 0);
-    if (ok) r = *reinterpret_cast<const uint4*>(p);
-    hi[0] = r.x; hi[1] = r.y; hi[2] = r.z; hi[3] = r.w;
+    const uint4 r = *reinterpret_cast<const uint4*>(p);
+    hi[0] = ok ? r.x : 0u;
+    hi[1] = ok ? r.y : 0u;
+    hi[2] = ok ? r.z : 0u;
+    hi[3] = ok ? r.w : 0u;
     lo[0] = lo[1] = lo[2] = lo[3] = 0;
 }
 template <>
 __device__ __forceinline__ void load_row8_split<float>(const float* p, bool ok, uint32_t (&hi)[4],
                                                        uint32_t (&lo)[4]) {
     float v[8];
-    if (ok) {
-        load8<float>(p, v);
-    } else {
+    load8<float>(p, v);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-    }
+    for (int i = 0; i < 8; ++i) v[i] = ok ? v[i] : 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const u16 h0 = f2bf_bits(v[2 * i]), h1 = f2bf_bits(v[2 * i + 1]);
@@ -130,15 +131,35 @@ __device__ __forceinline__ void load_row8_split<float>(const float* p, bool ok, 
     }
 }
 
+// Window of 64 runs starting at run r0, loaded by one wave: lane k fetches the
+// first position and first key row of run r0 + k, and every lane the first
+// position of run r0 + 64. Loads are clamped and unconditional; validity is
+// applied where the values are used (tile_rows), so nothing waits here.
+struct RunWindow {
+    int r0, vp, vs, v64;
+};
+
+__device__ __forceinline__ void load_window(int lane, int r0, int R, const int32_t* rs,
+                                            const int32_t* rp, RunWindow& wd) {
+    const int k = r0 + lane;
+    wd.r0 = r0;
+    wd.vp = rp[min(k, R)];
+    wd.vs = rs[max(min(k, R - 1), 0)];
+    wd.v64 = rp[min(r0 + 64, R)];
+}
+
 // Key rows of one 64-position tile of the concatenated selection, computed by
-// one wave without LDS. Lane k holds run r0 + k of the work item: its first
-// position wp (INT_MAX past the last run) and first key row ws; run r0 holds
-// position t0; wp64 is the first position of run r0 + 64. The run holding
-// position t0 + lane is (number of run starts <= t0 + lane) - 1, counted from a
-// 64-bit mask of the starts inside the tile. Writes krow[lane] (-1 past the
-// selection) and returns the run holding position t0 + 64.
-__device__ __forceinline__ int tile_rows(int lane, int t0, int total, int r0, int wp, int ws,
-                                         int wp64, int* krow) {
+// one wave without LDS. Lane k holds run r0 + k: its first position wp
+// (INT_MAX past the last run) and first key row ws; run r0 holds position t0.
+// The run holding position t0 + lane is (number of run starts <= t0 + lane) - 1,
+// counted from a 64-bit mask of the starts inside the tile. Writes krow[lane]
+// (-1 past the selection) and returns the run holding position t0 + 64.
+__device__ __forceinline__ int tile_rows(int lane, int t0, int total, int R, const RunWindow& wd,
+                                         int* krow, bool write) {
+    const int r0 = wd.r0;
+    const int wp = r0 + lane <= R ? wd.vp : 0x7fffffff;
+    const int ws = r0 + lane < R ? wd.vs : 0;
+    const int wp64 = r0 + 64 <= R ? wd.v64 : 0x7fffffff;
     const int s = wp - t0;
     uint32_t lo = 0, hi = 0;
     if (lane == 0) lo = 1u;
@@ -154,45 +175,71 @@ __device__ __forceinline__ int tile_rows(int lane, int t0, int total, int r0, in
     const int k = __popcll(starts & upto) - 1;
     const int rs_k = __shfl(ws, k), rp_k = __shfl(wp, k);
     const int P = t0 + lane;
-    krow[lane] = P < total ? rs_k + (P - rp_k) : -1;
+    if (write) krow[lane] = P < total ? rs_k + (P - rp_k) : -1;
     const int c = __popcll(__ballot(wp <= t0 + 64));
     return (c == 64 && wp64 <= t0 + 64) ? r0 + 64 : r0 + c - 1;
 }
 
-// Window of 64 runs starting at run r0 (one wave).
-__device__ __forceinline__ void load_window(int lane, int r0, int R, const int32_t* rs,
-                                            const int32_t* rp, int& wp, int& ws, int& wp64) {
-    const int k = r0 + lane;
-    wp = k <= R ? rp[k] : 0x7fffffff;
-    ws = k < R ? rs[k] : 0;
-    wp64 = r0 + 64 <= R ? rp[r0 + 64] : 0x7fffffff;
+// Raw 16-byte chunk: 8 bf16 words (4 registers) or 8 floats (8 registers).
+template <typename T> struct Raw8 { uint32_t w[4]; };
+template <> struct Raw8<float> { uint32_t w[8]; };
+
+template <typename T>
+__device__ __forceinline__ void load_raw8(const T* p, Raw8<T>& r) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+    if constexpr (sizeof(T) == 4) {
+        const uint4 b = *reinterpret_cast<const uint4*>(p + 4);
+        r.w[4] = b.x; r.w[5] = b.y; r.w[6] = b.z; r.w[7] = b.w;
+    }
 }
 
-// Global -> register staging of one K/V tile (64 key rows), NT threads.
-template <typename T, int D, int NP, int NT>
+// Raw chunk -> packed bf16 words (hi) and, for f32, the rounding residual (lo).
+template <typename T>
+__device__ __forceinline__ void split_raw8(const Raw8<T>& r, bool ok, uint32_t (&hi)[4],
+                                           uint32_t (&lo)[4]) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { hi[i] = ok ? r.w[i] : 0u; lo[i] = 0u; }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float v0 = ok ? __uint_as_float(r.w[2 * i]) : 0.0f;
+            const float v1 = ok ? __uint_as_float(r.w[2 * i + 1]) : 0.0f;
+            const u16 h0 = f2bf_bits(v0), h1 = f2bf_bits(v1);
+            const u16 l0 = f2bf_bits(v0 - bf_bits2f(h0)), l1 = f2bf_bits(v1 - bf_bits2f(h1));
+            hi[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            lo[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+    }
+}
+
+// Global -> register staging of one K/V tile (64 key rows), NT threads. Loads
+// are issued unconditionally from clamped rows and held raw; masking and
+// conversion happen in tile_store, so the loads stay in flight until then.
+template <typename T, int D, int NT>
 struct TileRegs {
     static constexpr int KTASK = 64 * (D / 8);      // 16-byte chunks of the K tile
     static constexpr int VTASK = 32 * (D / 8);      // (key pair, 8 dims) tasks of the V tile
     static constexpr int KT = (KTASK + NT - 1) / NT;
     static constexpr int VT = (VTASK + NT - 1) / NT;
-    uint32_t k[KT][NP][4];
-    uint32_t va[VT][NP][4], vb[VT][NP][4];
+    Raw8<T> k[KT];
+    Raw8<T> va[VT], vb[VT];
+    bool aok[VT], bok[VT];
 };
 
-template <typename T, int D, int NP, int NT>
-__device__ __forceinline__ void tile_load(TileRegs<T, D, NP, NT>& r, int tid, const int* krow,
+template <typename T, int D, int NT>
+__device__ __forceinline__ void tile_load(TileRegs<T, D, NT>& r, int tid, const int* krow,
                                           const T* Kh, const T* Vh) {
-    using TR = TileRegs<T, D, NP, NT>;
-    constexpr bool PREC = NP == 2;
+    // krow entries are -1 (past the selection) or key rows of this head
+    using TR = TileRegs<T, D, NT>;
 #pragma unroll
     for (int i = 0; i < TR::KT; ++i) {
         const int c = tid + i * NT;
         if (TR::KTASK % NT != 0 && c >= TR::KTASK) break;
         const int kr = c / (D / 8), c8 = c % (D / 8);
         const int row = krow[kr];
-        uint32_t scratch[4];
-        load_row8_split<T>(Kh + (int64_t)(row < 0 ? 0 : row) * D + c8 * 8, row >= 0, r.k[i][0],
-                           PREC ? r.k[i][NP - 1] : scratch);
+        load_raw8<T>(Kh + (int64_t)(row < 0 ? 0 : row) * D + c8 * 8, r.k[i]);
     }
 #pragma unroll
     for (int i = 0; i < TR::VT; ++i) {
@@ -200,40 +247,43 @@ __device__ __forceinline__ void tile_load(TileRegs<T, D, NP, NT>& r, int tid, co
         if (TR::VTASK % NT != 0 && c >= TR::VTASK) break;
         const int kk = c % 32, c8 = c / 32;
         const int ra = krow[2 * kk], rb = krow[2 * kk + 1];
-        uint32_t scratch[4];
-        load_row8_split<T>(Vh + (int64_t)(ra < 0 ? 0 : ra) * D + c8 * 8, ra >= 0, r.va[i][0],
-                           PREC ? r.va[i][NP - 1] : scratch);
-        load_row8_split<T>(Vh + (int64_t)(rb < 0 ? 0 : rb) * D + c8 * 8, rb >= 0, r.vb[i][0],
-                           PREC ? r.vb[i][NP - 1] : scratch);
+        r.aok[i] = ra >= 0;
+        r.bok[i] = rb >= 0;
+        load_raw8<T>(Vh + (int64_t)(ra < 0 ? 0 : ra) * D + c8 * 8, r.va[i]);
+        load_raw8<T>(Vh + (int64_t)(rb < 0 ? 0 : rb) * D + c8 * 8, r.vb[i]);
     }
 }
 
 // Register -> LDS: K row-major, V transposed (fp16 for bf16 inputs, bf16 hi/lo for f32).
 template <typename T, int D, int NP, int NT, int LDK, int LDV>
-__device__ __forceinline__ void tile_store(const TileRegs<T, D, NP, NT>& r, int tid,
+__device__ __forceinline__ void tile_store(const TileRegs<T, D, NT>& r, int tid,
                                            u16 (*Ks)[64 * LDK], u16 (*Vt)[D * LDV]) {
-    using TR = TileRegs<T, D, NP, NT>;
+    using TR = TileRegs<T, D, NT>;
     constexpr bool PREC = NP == 2;
 #pragma unroll
     for (int i = 0; i < TR::KT; ++i) {
         const int c = tid + i * NT;
         if (TR::KTASK % NT != 0 && c >= TR::KTASK) break;
         const int kr = c / (D / 8), c8 = c % (D / 8);
-#pragma unroll
-        for (int pp = 0; pp < NP; ++pp)
-            *reinterpret_cast<uint4*>(&Ks[pp][kr * LDK + c8 * 8]) =
-                make_uint4(r.k[i][pp][0], r.k[i][pp][1], r.k[i][pp][2], r.k[i][pp][3]);
+        uint32_t hv[4], lv[4];
+        split_raw8<T>(r.k[i], true, hv, lv);
+        *reinterpret_cast<uint4*>(&Ks[0][kr * LDK + c8 * 8]) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+        if constexpr (PREC)
+            *reinterpret_cast<uint4*>(&Ks[NP - 1][kr * LDK + c8 * 8]) = make_uint4(lv[0], lv[1], lv[2], lv[3]);
     }
 #pragma unroll
     for (int i = 0; i < TR::VT; ++i) {
         const int c = tid + i * NT;
         if (TR::VTASK % NT != 0 && c >= TR::VTASK) break;
         const int kk = c % 32, c8 = c / 32;
+        uint32_t va[2][4], vb[2][4];
+        split_raw8<T>(r.va[i], r.aok[i], va[0], va[1]);
+        split_raw8<T>(r.vb[i], r.bok[i], vb[0], vb[1]);
 #pragma unroll
         for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint32_t a = r.va[i][pp][j], b = r.vb[i][pp][j];
+                const uint32_t a = va[pp][j], b = vb[pp][j];
                 uint32_t lo_w, hi_w;
                 if constexpr (PREC) {
                     lo_w = (a & 0xFFFFu) | (b << 16);
@@ -316,7 +366,7 @@ __global__ __launch_bounds__(NT) void attn_kernel(int N, int Cq, const T* __rest
     constexpr int LDV = 64 + 8;
     __shared__ __attribute__((aligned(16))) u16 Ks[2][NP][64 * LDK];
     __shared__ __attribute__((aligned(16))) u16 Vt[2][NP][D * LDV];
-    __shared__ int krow[3][64];
+    __shared__ int krow[4][64];
 
     const int it = blockIdx.x;
     if (it >= *n_items) return;
@@ -368,119 +418,126 @@ __global__ __launch_bounds__(NT) void attn_kernel(int N, int Cq, const T* __rest
         for (int db = 0; db < DB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // wave 0: row lookup for tiles 0 and 1, window for tile 2
-    int wp = 0, ws = 0, wp64 = 0, r_next = 0;
-    if (w == 0 && ntiles > 0) {
-        load_window(l, 0, R, rs, rp, wp, ws, wp64);
-        r_next = tile_rows(l, 0, total, 0, wp, ws, wp64, krow[0]);
-        if (ntiles > 1) {
-            load_window(l, r_next, R, rs, rp, wp, ws, wp64);
-            r_next = tile_rows(l, 64, total, r_next, wp, ws, wp64, krow[1]);
-            if (ntiles > 2) load_window(l, r_next, R, rs, rp, wp, ws, wp64);
-        }
+    // Key rows are looked up three tiles ahead; tiles t+1 and t+2 are in flight
+    // in two register sets while tile t is computed from LDS. Every wave issues
+    // the same loads every step (tiles past the end read clamped, valid rows and
+    // are never used) so the load counters stay exact and no wait reaches back
+    // past the tile being consumed. Every wave computes the row lookup; wave 0
+    // writes it.
+    RunWindow wd;
+    load_window(l, 0, R, rs, rp, wd);
+    int r_next = tile_rows(l, 0, total, R, wd, krow[0], w == 0);
+#pragma unroll
+    for (int j = 1; j < 3; ++j) {
+        load_window(l, r_next, R, rs, rp, wd);
+        r_next = tile_rows(l, j * 64, total, R, wd, krow[j], w == 0);
     }
+    load_window(l, r_next, R, rs, rp, wd);
     __syncthreads();
-    TileRegs<T, D, NP, NT> tr;
-    if (ntiles > 0) {
-        tile_load<T, D, NP, NT>(tr, tid, krow[0], Kh, Vh);
-        tile_store<T, D, NP, NT, LDK, LDV>(tr, tid, Ks[0], Vt[0]);
-    }
+    TileRegs<T, D, NT> tr0, tr1;
+    tile_load<T, D, NT>(tr0, tid, krow[0], Kh, Vh);
+    tile_load<T, D, NT>(tr1, tid, krow[1], Kh, Vh);
+    tile_store<T, D, NP, NT, LDK, LDV>(tr0, tid, Ks[0], Vt[0]);
     __syncthreads();
 
-    for (int t = 0; t < ntiles; ++t) {
+    // one tile: look up t+3, prefetch t+2 into the register set tile t used,
+    // compute t, store t+1 into the other LDS buffer
+    auto step = [&](int t, auto& tr_mine, auto& tr_next) {
         const int b = t & 1;
         const int t0 = t * 64;
-        if (t + 1 < ntiles) tile_load<T, D, NP, NT>(tr, tid, krow[(t + 1) % 3], Kh, Vh);
-        if (w == 0 && t + 2 < ntiles) {
-            r_next = tile_rows(l, t0 + 128, total, r_next, wp, ws, wp64, krow[(t + 2) % 3]);
-            if (t + 3 < ntiles) load_window(l, r_next, R, rs, rp, wp, ws, wp64);
-        }
-        if (live[0]) {
-            const bool mask_tail = t0 + 64 > total;
-            f32x4 sc[RB][4];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) sc[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-                    const int off = (kb * 16 + c16) * LDK + kc * 32 + g * 8;
-                    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[b][0][off]);
-                    bf16x8 kl;
-                    if constexpr (PREC) kl = *reinterpret_cast<const bf16x8*>(&Ks[b][NP - 1][off]);
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) {
-                        if (rb > 0 && !live[rb]) continue;
-                        if constexpr (PREC) {
-                            sc[rb][kb] = mfma16(kl, qf[rb][0][kc], sc[rb][kb]);
-                            sc[rb][kb] = mfma16(ka, qf[rb][NP - 1][kc], sc[rb][kb]);
-                        }
-                        sc[rb][kb] = mfma16(ka, qf[rb][0][kc], sc[rb][kb]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                if (rb > 0 && !live[rb]) continue;
-                softmax_block<DB>(sc[rb], sl2, mask_tail, t0, g, total, m_run[rb], l_part[rb], o[rb]);
-            }
-#pragma unroll
-            for (int kc2 = 0; kc2 < 2; ++kc2) {
-                if constexpr (PREC) {
-                    bf16x8 pb[RB], pl[RB];
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            pb[rb][j] = f2bf(sc[rb][2 * kc2][j]);
-                            pb[rb][4 + j] = f2bf(sc[rb][2 * kc2 + 1][j]);
-                            pl[rb][j] = f2bf(sc[rb][2 * kc2][j] - bf2f(pb[rb][j]));
-                            pl[rb][4 + j] = f2bf(sc[rb][2 * kc2 + 1][j] - bf2f(pb[rb][4 + j]));
-                        }
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const int off = (db * 16 + c16) * LDV + kc2 * 32 + g * 4;
-                        const uint2 lo0 = *reinterpret_cast<const uint2*>(&Vt[b][0][off]);
-                        const uint2 hi0 = *reinterpret_cast<const uint2*>(&Vt[b][0][off + 16]);
-                        const uint2 lo1 = *reinterpret_cast<const uint2*>(&Vt[b][NP - 1][off]);
-                        const uint2 hi1 = *reinterpret_cast<const uint2*>(&Vt[b][NP - 1][off + 16]);
-                        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo0.x, lo0.y, hi0.x, hi0.y));
-                        const bf16x8 vl = __builtin_bit_cast(bf16x8, make_uint4(lo1.x, lo1.y, hi1.x, hi1.y));
-#pragma unroll
+        const int rn = tile_rows(l, t0 + 192, total, R, wd, krow[(t + 3) & 3], w == 0);
+        load_window(l, rn, R, rs, rp, wd);
+        tile_load<T, D, NT>(tr_mine, tid, krow[(t + 2) & 3], Kh, Vh);
+        if (t < ntiles && live[0]) {
+                const bool mask_tail = t0 + 64 > total;
+                f32x4 sc[RB][4];
+    #pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+    #pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) sc[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+                    for (int kc = 0; kc < KC; ++kc) {
+                        const int off = (kb * 16 + c16) * LDK + kc * 32 + g * 8;
+                        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[b][0][off]);
+                        bf16x8 kl;
+                        if constexpr (PREC) kl = *reinterpret_cast<const bf16x8*>(&Ks[b][NP - 1][off]);
+    #pragma unroll
                         for (int rb = 0; rb < RB; ++rb) {
                             if (rb > 0 && !live[rb]) continue;
-                            o[rb][db] = mfma16(vl, pb[rb], o[rb][db]);
-                            o[rb][db] = mfma16(va, pl[rb], o[rb][db]);
-                            o[rb][db] = mfma16(va, pb[rb], o[rb][db]);
-                        }
-                    }
-                } else {
-                    // P.V in fp16 (11-bit significand): probabilities lose at most 2^-12
-                    f16x8 ph[RB];
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-                        ph[rb] = __builtin_bit_cast(
-                            f16x8, make_uint4(pack_h2(sc[rb][2 * kc2][0], sc[rb][2 * kc2][1]),
-                                              pack_h2(sc[rb][2 * kc2][2], sc[rb][2 * kc2][3]),
-                                              pack_h2(sc[rb][2 * kc2 + 1][0], sc[rb][2 * kc2 + 1][1]),
-                                              pack_h2(sc[rb][2 * kc2 + 1][2], sc[rb][2 * kc2 + 1][3])));
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const int off = (db * 16 + c16) * LDV + kc2 * 32 + g * 4;
-                        const uint2 lo0 = *reinterpret_cast<const uint2*>(&Vt[b][0][off]);
-                        const uint2 hi0 = *reinterpret_cast<const uint2*>(&Vt[b][0][off + 16]);
-                        const f16x8 vh = __builtin_bit_cast(f16x8, make_uint4(lo0.x, lo0.y, hi0.x, hi0.y));
-#pragma unroll
-                        for (int rb = 0; rb < RB; ++rb) {
-                            if (rb > 0 && !live[rb]) continue;
-                            o[rb][db] = mfma16h(vh, ph[rb], o[rb][db]);
+                            if constexpr (PREC) {
+                                sc[rb][kb] = mfma16(kl, qf[rb][0][kc], sc[rb][kb]);
+                                sc[rb][kb] = mfma16(ka, qf[rb][NP - 1][kc], sc[rb][kb]);
+                            }
+                            sc[rb][kb] = mfma16(ka, qf[rb][0][kc], sc[rb][kb]);
                         }
                     }
                 }
+    #pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    if (rb > 0 && !live[rb]) continue;
+                    softmax_block<DB>(sc[rb], sl2, mask_tail, t0, g, total, m_run[rb], l_part[rb], o[rb]);
+                }
+    #pragma unroll
+                for (int kc2 = 0; kc2 < 2; ++kc2) {
+                    if constexpr (PREC) {
+                        bf16x8 pb[RB], pl[RB];
+    #pragma unroll
+                        for (int rb = 0; rb < RB; ++rb)
+    #pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                pb[rb][j] = f2bf(sc[rb][2 * kc2][j]);
+                                pb[rb][4 + j] = f2bf(sc[rb][2 * kc2 + 1][j]);
+                                pl[rb][j] = f2bf(sc[rb][2 * kc2][j] - bf2f(pb[rb][j]));
+                                pl[rb][4 + j] = f2bf(sc[rb][2 * kc2 + 1][j] - bf2f(pb[rb][4 + j]));
+                            }
+    #pragma unroll
+                        for (int db = 0; db < DB; ++db) {
+                            const int off = (db * 16 + c16) * LDV + kc2 * 32 + g * 4;
+                            const uint2 lo0 = *reinterpret_cast<const uint2*>(&Vt[b][0][off]);
+                            const uint2 hi0 = *reinterpret_cast<const uint2*>(&Vt[b][0][off + 16]);
+                            const uint2 lo1 = *reinterpret_cast<const uint2*>(&Vt[b][NP - 1][off]);
+                            const uint2 hi1 = *reinterpret_cast<const uint2*>(&Vt[b][NP - 1][off + 16]);
+                            const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo0.x, lo0.y, hi0.x, hi0.y));
+                            const bf16x8 vl = __builtin_bit_cast(bf16x8, make_uint4(lo1.x, lo1.y, hi1.x, hi1.y));
+    #pragma unroll
+                            for (int rb = 0; rb < RB; ++rb) {
+                                if (rb > 0 && !live[rb]) continue;
+                                o[rb][db] = mfma16(vl, pb[rb], o[rb][db]);
+                                o[rb][db] = mfma16(va, pl[rb], o[rb][db]);
+                                o[rb][db] = mfma16(va, pb[rb], o[rb][db]);
+                            }
+                        }
+                    } else {
+                        // P.V in fp16 (11-bit significand): probabilities lose at most 2^-12
+                        f16x8 ph[RB];
+    #pragma unroll
+                        for (int rb = 0; rb < RB; ++rb)
+                            ph[rb] = __builtin_bit_cast(
+                                f16x8, make_uint4(pack_h2(sc[rb][2 * kc2][0], sc[rb][2 * kc2][1]),
+                                                  pack_h2(sc[rb][2 * kc2][2], sc[rb][2 * kc2][3]),
+                                                  pack_h2(sc[rb][2 * kc2 + 1][0], sc[rb][2 * kc2 + 1][1]),
+                                                  pack_h2(sc[rb][2 * kc2 + 1][2], sc[rb][2 * kc2 + 1][3])));
+    #pragma unroll
+                        for (int db = 0; db < DB; ++db) {
+                            const int off = (db * 16 + c16) * LDV + kc2 * 32 + g * 4;
+                            const uint2 lo0 = *reinterpret_cast<const uint2*>(&Vt[b][0][off]);
+                            const uint2 hi0 = *reinterpret_cast<const uint2*>(&Vt[b][0][off + 16]);
+                            const f16x8 vh = __builtin_bit_cast(f16x8, make_uint4(lo0.x, lo0.y, hi0.x, hi0.y));
+    #pragma unroll
+                            for (int rb = 0; rb < RB; ++rb) {
+                                if (rb > 0 && !live[rb]) continue;
+                                o[rb][db] = mfma16h(vh, ph[rb], o[rb][db]);
+                            }
+                        }
+                    }
+                }
             }
-        }
-        if (t + 1 < ntiles) tile_store<T, D, NP, NT, LDK, LDV>(tr, tid, Ks[b ^ 1], Vt[b ^ 1]);
+            tile_store<T, D, NP, NT, LDK, LDV>(tr_next, tid, Ks[b ^ 1], Vt[b ^ 1]);
         __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, tr0, tr1);
+        step(t + 1, tr1, tr0);
     }
 
 #pragma unroll
