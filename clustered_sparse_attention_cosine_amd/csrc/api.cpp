@@ -85,6 +85,9 @@ struct KmeansWs {
     float* inv_norm = nullptr;
     int32_t* flag_list = nullptr;
     int32_t* flag_count = nullptr;
+    float* flag_thr = nullptr;
+    int32_t* over_list = nullptr;
+    int32_t* over_count = nullptr;
     uint8_t* valid = nullptr;
     uint16_t* c_hi = nullptr;
     uint16_t* c_lo = nullptr;
@@ -104,6 +107,9 @@ void plan_kmeans(Carver& c, const Prob& p, int cap, bool want_inv, bool kpp, boo
     if (want_inv) w.inv_norm = c.take<float>(bhn);
     w.flag_list = c.take<int32_t>(bhn);
     w.flag_count = c.take<int32_t>(p.BH);
+    w.flag_thr = c.take<float>(bhn);
+    w.over_list = c.take<int32_t>(bhn);
+    w.over_count = c.take<int32_t>(p.BH);
     w.valid = c.take<uint8_t>(bhc);
     w.c_hi = c.take<uint16_t>(bhc * p.D);
     w.c_lo = c.take<uint16_t>(bhc * p.D);
@@ -137,6 +143,10 @@ void plan_stages(Carver& c, const Prob& p, StageWs& w) {
     w.labels_u = c.take<int32_t>(bhn);
 }
 
+FlagSet flags_of(const KmeansWs& w) {
+    return FlagSet{w.flag_list, w.flag_count, w.flag_thr, w.over_list, w.over_count};
+}
+
 CentView make_view(float* cent, const KmeansWs& w, int cap, int base, int m) {
     CentView v;
     v.cent = cent;
@@ -160,9 +170,7 @@ hipError_t lloyd(const Prob& p, const void* x, int normalize, RowSet rs, const f
                  hipStream_t s) {
     hipError_t e;
     for (int it = 0; it < iters; ++it) {
-        if ((e = launch_assign(p, x, rs, inv_norm, cv, nullptr, labels, w.flag_list, w.flag_count, s)))
-            return e;
-        if ((e = launch_refine(p, x, normalize, rs, cv, nullptr, w.flag_list, w.flag_count, labels, s)))
+        if ((e = launch_assign(p, x, rs, inv_norm, normalize, cv, nullptr, labels, flags_of(w), s)))
             return e;
         if (it + 1 < iters || final_update) {
             if ((e = launch_update_accum(p, x, rs, inv_norm, labels, cv, s))) return e;
@@ -364,8 +372,7 @@ int32_t adacluster_cluster_k(const adc_shape* shape, const adc_k_params* prm, co
         // final assignment over every slot that holds a centre (Algorithm 1 step 20)
         CentView cvf = make_view(centroids, w, nmax, 0, nmax);
         HIPCHK(launch_finalize(p, cvf, nullptr, 0, s));
-        HIPCHK(launch_assign(p, k, all, nullptr, cvf, n_clusters, assign, w.flag_list, w.flag_count, s));
-        HIPCHK(launch_refine(p, k, 0, all, cvf, n_clusters, w.flag_list, w.flag_count, assign, s));
+        HIPCHK(launch_assign(p, k, all, nullptr, 0, cvf, n_clusters, assign, flags_of(w), s));
     }
     HIPCHK(launch_histogram(p, assign, nmax, w.hist, s));
     HIPCHK(launch_scan_offsets(p, w.hist, nmax, sizes, offsets, s));
@@ -433,7 +440,7 @@ int32_t adacluster_select(const adc_shape* shape, int32_t Cq, int32_t Ck, const 
 // ====================================================================== sparse attention
 struct AttnWs {
     int run_cap;
-    int max_items;
+    int cap;   // work items per head (upper bound)
     int32_t* run_start;
     int32_t* run_pos;
     int32_t* n_runs;
@@ -444,12 +451,12 @@ struct AttnWs {
 static void plan_attn(Carver& c, const adc_shape* shape, int32_t Cq, int32_t Ck, AttnWs& w) {
     const size_t rows = (size_t)shape->B * shape->H * Cq;
     w.run_cap = Ck / 2 + 2;
-    w.max_items = (int)((size_t)shape->B * shape->H * (Cq + (shape->N + ATTN_ROWS - 1) / ATTN_ROWS));
+    w.cap = Cq + (shape->N + ATTN_ROWS - 1) / ATTN_ROWS;
     w.run_start = c.take<int32_t>(rows * w.run_cap);
     w.run_pos = c.take<int32_t>(rows * (w.run_cap + 1));
     w.n_runs = c.take<int32_t>(rows);
-    w.items = c.take<int32_t>(2 * (size_t)w.max_items);
-    w.n_items = c.take<int32_t>(1);
+    w.items = c.take<int32_t>((size_t)shape->B * shape->H * w.cap);
+    w.n_items = c.take<int32_t>((size_t)shape->B * shape->H);
 }
 
 size_t adacluster_sparse_attn_workspace(const adc_shape* shape, int32_t Cq, int32_t Ck) {
@@ -482,9 +489,9 @@ int32_t adacluster_sparse_attn(const adc_shape* shape, int32_t Cq, int32_t Ck, c
     AttnWs w;
     plan_attn(c, shape, Cq, Ck, w);
     HIPCHK(launch_build_runs(p, Cq, Ck, k_offsets, sel_mask, w.run_cap, w.run_start, w.run_pos, w.n_runs, s));
-    HIPCHK(launch_worklist(p, Cq, q_offsets, w.items, w.n_items, s));
+    HIPCHK(launch_worklist(p, Cq, w.cap, q_offsets, w.items, w.n_items, s));
     HIPCHK(launch_attention(p, Cq, q, q_perm, q_offsets, k_perm, v_perm, w.run_start, w.run_pos,
-                            w.n_runs, w.run_cap, w.items, w.n_items, w.max_items, scale, out,
+                            w.n_runs, w.run_cap, w.items, w.n_items, w.cap, scale, out,
                             out_dtype == ADC_F32, lse, s));
     return ADC_OK;
 }
@@ -522,9 +529,8 @@ int32_t adacluster_assign(const adc_shape* shape, int32_t M, int32_t normalize, 
     RowSet all{nullptr, nullptr, nullptr};
     if (normalize) HIPCHK(launch_inv_norm(p, x, w.inv_norm, s));
     HIPCHK(launch_finalize(p, cv, nullptr, 0, s));
-    HIPCHK(launch_assign(p, x, all, normalize ? w.inv_norm : nullptr, cv, nullptr, assign,
-                         w.flag_list, w.flag_count, s));
-    HIPCHK(launch_refine(p, x, normalize, all, cv, nullptr, w.flag_list, w.flag_count, assign, s));
+    HIPCHK(launch_assign(p, x, all, normalize ? w.inv_norm : nullptr, normalize, cv, nullptr,
+                         assign, flags_of(w), s));
     return ADC_OK;
 }
 

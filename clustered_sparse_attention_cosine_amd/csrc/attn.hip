@@ -67,32 +67,45 @@ hipError_t launch_build_runs(const Prob& p, int Cq, int Ck, const int32_t* k_off
 }
 
 // ------------------------------------------------------------------ work list
-__global__ __launch_bounds__(256) void worklist_kernel(int64_t rows, int Cq,
+// Work items (q-cluster a, chunk c of ATTN_ROWS rows) of head bh are written in
+// q-cluster order to items[bh * cap ...] (cap = Cq + ceil(N / ATTN_ROWS) bounds
+// their number), one workgroup per head. Launching the attention grid over
+// heads in order keeps the workgroups in flight on one or two heads at a time,
+// so their K'/V' stay in the last-level cache.
+__global__ __launch_bounds__(256) void worklist_kernel(int Cq, int cap,
                                                        const int32_t* __restrict__ q_offsets,
                                                        int32_t* __restrict__ items,
                                                        int32_t* __restrict__ n_items) {
-    const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (row >= rows) return;
-    const int64_t bh = row / Cq;
-    const int a = (int)(row % Cq);
-    const int32_t* qo = q_offsets + bh * (Cq + 1);
-    const int na = qo[a + 1] - qo[a];
-    const int ch = (na + ATTN_ROWS - 1) / ATTN_ROWS;
-    if (ch == 0) return;
-    const int base = atomicAdd(n_items, ch);
-    for (int c = 0; c < ch; ++c) {
-        items[2 * (int64_t)(base + c)] = (int32_t)bh;
-        items[2 * (int64_t)(base + c) + 1] = a | (c << 16);
+    __shared__ int wsum[4];
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int32_t* qo = q_offsets + (int64_t)bh * (Cq + 1);
+    int32_t* out = items + (int64_t)bh * cap;
+    int running = 0;
+    for (int base = 0; base < Cq; base += 256) {
+        const int a = base + tid;
+        const int ch = a < Cq ? (qo[a + 1] - qo[a] + ATTN_ROWS - 1) / ATTN_ROWS : 0;
+        int incl = ch;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(incl, o);
+            if (l >= o) incl += v;
+        }
+        if (l == 63) wsum[w] = incl;
+        __syncthreads();
+        int before = running + incl - ch;
+        for (int i = 0; i < w; ++i) before += wsum[i];
+        for (int c = 0; c < ch; ++c) out[before + c] = a | (c << 16);
+        running += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        __syncthreads();
     }
+    if (tid == 0) n_items[bh] = running;
 }
 
-hipError_t launch_worklist(const Prob& p, int Cq, const int32_t* q_offsets, int32_t* items,
-                           int32_t* n_items, hipStream_t s) {
-    hipError_t e = fill_i32(n_items, 1, 0, s);
-    if (e != hipSuccess) return e;
-    const int64_t rows = (int64_t)p.BH * Cq;
-    hipLaunchKernelGGL(worklist_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, rows,
-                       Cq, q_offsets, items, n_items);
+hipError_t launch_worklist(const Prob& p, int Cq, int cap, const int32_t* q_offsets,
+                           int32_t* items, int32_t* n_items, hipStream_t s) {
+    hipLaunchKernelGGL(worklist_kernel, dim3((unsigned)p.BH), dim3(256), 0, s, Cq, cap, q_offsets,
+                       items, n_items);
     return hipGetLastError();
 }
 
@@ -355,8 +368,9 @@ __global__ __launch_bounds__(NT) void attn_kernel(int N, int Cq, const T* __rest
                                                   const int32_t* __restrict__ run_pos,
                                                   const int32_t* __restrict__ n_runs, int run_cap,
                                                   const int32_t* __restrict__ items,
-                                                  const int32_t* __restrict__ n_items, float sl2,
-                                                  TO* __restrict__ O, float* __restrict__ lse) {
+                                                  const int32_t* __restrict__ n_items, int cap,
+                                                  float sl2, TO* __restrict__ O,
+                                                  float* __restrict__ lse) {
     static_assert((NT / 64) * RB * 16 == ATTN_ROWS, "waves x blocks must cover a work item");
     constexpr bool PREC = sizeof(T) == 4;
     constexpr int NP = PREC ? 2 : 1;  // stored parts per operand
@@ -368,10 +382,9 @@ __global__ __launch_bounds__(NT) void attn_kernel(int N, int Cq, const T* __rest
     __shared__ __attribute__((aligned(16))) u16 Vt[2][NP][D * LDV];
     __shared__ int krow[4][64];
 
-    const int it = blockIdx.x;
-    if (it >= *n_items) return;
-    const int bh = items[2 * it];
-    const int packed = items[2 * it + 1];
+    const int bh = blockIdx.x / cap;
+    if ((int)(blockIdx.x % cap) >= n_items[bh]) return;
+    const int packed = items[blockIdx.x];
     const int a = packed & 0xFFFF, ch = packed >> 16;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c16 = l & 15;
 
@@ -570,32 +583,32 @@ template <typename T, typename TO>
 static void launch_attn_t(const Prob& p, dim3 grid, int Cq, const void* q, const int32_t* q_perm,
                           const int32_t* q_offsets, const void* k_perm, const void* v_perm,
                           const int32_t* run_start, const int32_t* run_pos, const int32_t* n_runs,
-                          int run_cap, const int32_t* items, const int32_t* n_items, float sl2,
-                          void* out, float* lse, hipStream_t s) {
+                          int run_cap, const int32_t* items, const int32_t* n_items, int cap,
+                          float sl2, void* out, float* lse, hipStream_t s) {
     auto k = p.D == 64 ? attn_kernel<T, 64, TO, ATTN_NT, ATTN_RB> : attn_kernel<T, 128, TO, ATTN_NT, ATTN_RB>;
     hipLaunchKernelGGL(k, grid, dim3(ATTN_NT), 0, s, p.N, Cq, (const T*)q, q_perm, q_offsets,
                        (const T*)k_perm, (const T*)v_perm, run_start, run_pos, n_runs, run_cap,
-                       items, n_items, sl2, (TO*)out, lse);
+                       items, n_items, cap, sl2, (TO*)out, lse);
 }
 
 hipError_t launch_attention(const Prob& p, int Cq, const void* q, const int32_t* q_perm,
                             const int32_t* q_offsets, const void* k_perm, const void* v_perm,
                             const int32_t* run_start, const int32_t* run_pos, const int32_t* n_runs,
-                            int run_cap, const int32_t* items, const int32_t* n_items, int max_items,
+                            int run_cap, const int32_t* items, const int32_t* n_items, int cap,
                             float scale, void* out, int out_f32, float* lse, hipStream_t s) {
-    if (max_items <= 0) return hipSuccess;
+    if (cap <= 0) return hipSuccess;
     const float sl2 = scale * 1.4426950408889634f;
-    dim3 grid((unsigned)max_items);
+    dim3 grid((unsigned)((int64_t)p.BH * cap));
     if (p.bf16) {
         if (out_f32)
             launch_attn_t<u16, float>(p, grid, Cq, q, q_perm, q_offsets, k_perm, v_perm, run_start,
-                                      run_pos, n_runs, run_cap, items, n_items, sl2, out, lse, s);
+                                      run_pos, n_runs, run_cap, items, n_items, cap, sl2, out, lse, s);
         else
             launch_attn_t<u16, u16>(p, grid, Cq, q, q_perm, q_offsets, k_perm, v_perm, run_start,
-                                    run_pos, n_runs, run_cap, items, n_items, sl2, out, lse, s);
+                                    run_pos, n_runs, run_cap, items, n_items, cap, sl2, out, lse, s);
     } else {
         launch_attn_t<float, float>(p, grid, Cq, q, q_perm, q_offsets, k_perm, v_perm, run_start,
-                                    run_pos, n_runs, run_cap, items, n_items, sl2, out, lse, s);
+                                    run_pos, n_runs, run_cap, items, n_items, cap, sl2, out, lse, s);
     }
     return hipGetLastError();
 }

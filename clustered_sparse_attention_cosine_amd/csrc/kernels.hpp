@@ -66,15 +66,20 @@ hipError_t launch_init_kmeanspp(const Prob& p, const void* x, const float* xf, R
 // With sums != NULL it first moves centres to sums/cnt (cnt > 0) and clears the sums.
 hipError_t launch_finalize(const Prob& p, CentView cv, const uint8_t* active, int with_sums,
                            hipStream_t s);
-// Nearest centre by a bf16 hi/lo matrix-core contraction with a certified error
-// bound; rows whose best two distances are not separated by the bound go to
-// the flag list for an exact f64 recheck (launch_refine).
+// Flag lists of the certified assignment (see kmeans.hip).
+struct FlagSet {
+    int32_t* list;
+    int32_t* count;
+    float* thr;
+    int32_t* over;
+    int32_t* over_count;
+};
+// Nearest centre by a bf16 hi/lo matrix-core contraction with a certified
+// error bound; uncertain rows are settled by exact f64 distances of the
+// centres inside their uncertainty band (labels are final on return).
 hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
-                         CentView cv, const int32_t* mcount, int32_t* labels,
-                         int32_t* flag_list, int32_t* flag_count, hipStream_t s);
-hipError_t launch_refine(const Prob& p, const void* x, int normalize, RowSet rs, CentView cv,
-                         const int32_t* mcount, const int32_t* flag_list,
-                         const int32_t* flag_count, int32_t* labels, hipStream_t s);
+                         int normalize, CentView cv, const int32_t* mcount, int32_t* labels,
+                         FlagSet fs, hipStream_t s);
 // Centroid sums (f32 atomics) and member counts for the current labels.
 hipError_t launch_update_accum(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
                                const int32_t* labels, CentView cv, hipStream_t s);
@@ -133,13 +138,13 @@ hipError_t launch_topk(const Prob& p, int Cq, int Ck, const float* S, const int3
 hipError_t launch_build_runs(const Prob& p, int Cq, int Ck, const int32_t* k_offsets,
                              const uint32_t* mask, int run_cap, int32_t* run_start,
                              int32_t* run_pos, int32_t* n_runs, hipStream_t s);
-hipError_t launch_worklist(const Prob& p, int Cq, const int32_t* q_offsets, int32_t* items,
-                           int32_t* n_items, hipStream_t s);
+hipError_t launch_worklist(const Prob& p, int Cq, int cap, const int32_t* q_offsets,
+                           int32_t* items, int32_t* n_items, hipStream_t s);
 hipError_t launch_attention(const Prob& p, int Cq, const void* q, const int32_t* q_perm,
                             const int32_t* q_offsets, const void* k_perm, const void* v_perm,
                             const int32_t* run_start, const int32_t* run_pos,
                             const int32_t* n_runs, int run_cap, const int32_t* items,
-                            const int32_t* n_items, int max_items, float scale, void* out,
+                            const int32_t* n_items, int cap, float scale, void* out,
                             int out_f32, float* lse, hipStream_t s);
 
 constexpr int ATTN_ROWS = 128;  // query rows per attention work item

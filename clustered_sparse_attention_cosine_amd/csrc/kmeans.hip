@@ -334,17 +334,38 @@ hipError_t launch_finalize(const Prob& p, CentView cv, const uint8_t* active, in
 // MFMAs (rows of the MFMA = centres, columns = points), so a lane owns one
 // point per 16-point block and tracks the best and second-best
 //   d_j = ||c_j||^2 - 2 s (x . c_j)      (s = 1 / ||x|| for queries, else 1)
-// The contraction error of one d_j is at most ERR_X s||x|| max||c|| +
-// ERR_C max||c||^2 (hi/lo residual 2^-16 plus f32 accumulation, with margin);
-// a row whose two best values are not separated by twice that is flagged and
-// rechecked exactly.
-template <typename T, int D, bool F32X>
+// The contraction error of one d_j is at most err = ERR_X s||x|| max||c|| +
+// ERR_C max||c||^2 (hi/lo residual 2^-16 plus f32 accumulation, with margin).
+// A row whose best two values are not separated by 2 err is flagged, with the
+// band edge thr = best + 3 err.
+//
+// CAND mode runs the same contraction (same operands, same order, so the same
+// d_j) over the flagged rows only and collects every centre with d_j <= thr.
+// The exact nearest centre is among them (|d_j - exact| <= err), so exact f64
+// distances of the candidates decide the label; a row with more than CAND_CAP
+// candidates goes to the full exact scan (launch_refine).
+constexpr int CAND_CAP = 16;
+
+template <typename T>
+__device__ double exact_d2(const T* xr, int D, int normalize, const float* c) {
+#pragma clang fp contract(off)
+    double nrm = normalize ? seq_norm(xr, D) : 1.0;
+    double s = 0.0;
+    for (int d = 0; d < D; ++d) {
+        const float xv = elem<T>::load(xr, d);
+        const float xh = normalize ? (float)((double)xv / nrm) : xv;
+        const double df = (double)xh - (double)c[d];
+        s += df * df;
+    }
+    return s;
+}
+
+template <typename T, int D, bool F32X, bool CAND>
 __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
                                                      const float* __restrict__ inv_norm,
-                                                     CentView cv, const int32_t* __restrict__ mcount,
-                                                     int32_t* __restrict__ labels,
-                                                     int32_t* __restrict__ flag_list,
-                                                     int32_t* __restrict__ flag_count) {
+                                                     int normalize, CentView cv,
+                                                     const int32_t* __restrict__ mcount,
+                                                     int32_t* __restrict__ labels, FlagSet fs) {
     constexpr int KC = D / 32;
     constexpr int LD = D + 8;
     constexpr float ERR_X = F32X ? 0x1.0p-12f : 0x1.0p-13f;
@@ -352,24 +373,33 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
     __shared__ __attribute__((aligned(16))) u16 sh_hi[64 * LD];
     __shared__ __attribute__((aligned(16))) u16 sh_lo[64 * LD];
     __shared__ float sh_c2[64];
+    __shared__ int cand[CAND ? 256 : 1][CAND_CAP];
+    __shared__ int ccount[CAND ? 256 : 1];
 
     const int bh = blockIdx.y;
     if (rs.active && !rs.active[bh]) return;
-    const int n = rs.nrows ? rs.nrows[bh] : N;
+    const int n = CAND ? fs.count[bh] : (rs.nrows ? rs.nrows[bh] : N);
     const int row_base = blockIdx.x * 256;
     if (row_base >= n) return;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c16 = l & 15;
     const int M = mcount ? min(mcount[bh], cv.m) : cv.m;
+    if constexpr (CAND) ccount[tid] = 0;
 
     bf16x8 xh[4][KC];
     bf16x8 xl[4][F32X ? KC : 1];
-    float sc[4], xn[4];
+    float sc[4], xn[4], thr[4];
     int rr[4];
     bool ok[4];
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) {
-        const int r = row_base + w * 64 + pb * 16 + c16;
-        ok[pb] = r < n;
+        const int e = row_base + w * 64 + pb * 16 + c16;
+        ok[pb] = e < n;
+        int r = e;
+        thr[pb] = 0.0f;
+        if constexpr (CAND) {
+            r = ok[pb] ? fs.list[(int64_t)bh * N + e] : 0;
+            thr[pb] = ok[pb] ? fs.thr[(int64_t)bh * N + e] : -INFINITY;
+        }
         rr[pb] = r;
         int64_t tok = 0;
         if (ok[pb]) tok = rs.rows ? rs.rows[(int64_t)bh * N + r] : r;
@@ -455,76 +485,101 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
             for (int i = 0; i < 4; ++i) {
                 const int jl = cb * 16 + g * 4 + i;
                 const float c2 = sh_c2[jl];
-                if (c2 < INFINITY) c2max = fmaxf(c2max, c2);
                 const int j = tile * 64 + jl;
+                if constexpr (!CAND) {
+                    if (c2 < INFINITY) c2max = fmaxf(c2max, c2);
+                }
 #pragma unroll
                 for (int pb = 0; pb < 4; ++pb) {
                     const float dv = fmaf(-2.0f * sc[pb], acc[pb][cb][i], c2);
-                    b2[pb] = fmaxf(b1[pb], fminf(b2[pb], dv));
-                    if (dv < b1[pb]) { b1[pb] = dv; bi[pb] = j; }
+                    if constexpr (CAND) {
+                        if (j < M && dv <= thr[pb]) {
+                            const int prow = w * 64 + pb * 16 + c16;
+                            const int pos = atomicAdd(&ccount[prow], 1);
+                            if (pos < CAND_CAP) cand[prow][pos] = j;
+                        }
+                    } else {
+                        b2[pb] = fmaxf(b1[pb], fminf(b2[pb], dv));
+                        if (dv < b1[pb]) { b1[pb] = dv; bi[pb] = j; }
+                    }
                 }
             }
         }
     }
 
-    c2max = fmaxf(c2max, __shfl_xor(c2max, 16));
-    c2max = fmaxf(c2max, __shfl_xor(c2max, 32));
-    const float err_c = ERR_X * sqrtf(c2max);
-#pragma unroll
-    for (int pb = 0; pb < 4; ++pb) {
-#pragma unroll
-        for (int o = 16; o <= 32; o <<= 1) {
-            const float ob1 = __shfl_xor(b1[pb], o);
-            const float ob2 = __shfl_xor(b2[pb], o);
-            const int obi = __shfl_xor(bi[pb], o);
-            const bool take = ob1 < b1[pb] || (ob1 == b1[pb] && obi < bi[pb]);
-            const float nb2 = take ? fminf(b1[pb], ob2) : fminf(b2[pb], ob1);
-            if (take) { b1[pb] = ob1; bi[pb] = obi; }
-            b2[pb] = nb2;
+    if constexpr (CAND) {
+        __syncthreads();
+        // one thread per row: exact f64 distances of its candidates
+        const int e = row_base + tid;
+        if (e < n) {
+            const int r = fs.list[(int64_t)bh * N + e];
+            const int nc = ccount[tid];
+            if (nc > CAND_CAP || nc == 0) {
+                const int pos = atomicAdd(&fs.over_count[bh], 1);
+                fs.over[(int64_t)bh * N + pos] = r;
+            } else {
+                const int64_t tok = rs.rows ? rs.rows[(int64_t)bh * N + r] : r;
+                const T* xr = row_ptr(X, N, D, bh, tok);
+                double best = INFINITY;
+                int bj = 0x7fffffff;
+                for (int q = 0; q < nc; ++q) {
+                    const int j = cand[tid][q];
+                    const double d2 = exact_d2(xr, D, normalize, cv.cent + (cbase + j) * D);
+                    if (d2 < best || (d2 == best && j < bj)) { best = d2; bj = j; }
+                }
+                labels[(int64_t)bh * N + r] = bj;
+            }
         }
-        if (g == 0 && ok[pb]) {
-            // no finite distance (no centre, or a NaN row): slot 0, and the row is flagged
-            labels[(int64_t)bh * N + rr[pb]] = bi[pb] == 0x7fffffff ? 0 : bi[pb];
-            const float err = err_c * xn[pb] + ERR_C * c2max;
-            if (!(b2[pb] - b1[pb] > 2.0f * err)) {
-                const int pos = atomicAdd(&flag_count[bh], 1);
-                flag_list[(int64_t)bh * N + pos] = rr[pb];
+    } else {
+        c2max = fmaxf(c2max, __shfl_xor(c2max, 16));
+        c2max = fmaxf(c2max, __shfl_xor(c2max, 32));
+        const float err_c = ERR_X * sqrtf(c2max);
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) {
+#pragma unroll
+            for (int o = 16; o <= 32; o <<= 1) {
+                const float ob1 = __shfl_xor(b1[pb], o);
+                const float ob2 = __shfl_xor(b2[pb], o);
+                const int obi = __shfl_xor(bi[pb], o);
+                const bool take = ob1 < b1[pb] || (ob1 == b1[pb] && obi < bi[pb]);
+                const float nb2 = take ? fminf(b1[pb], ob2) : fminf(b2[pb], ob1);
+                if (take) { b1[pb] = ob1; bi[pb] = obi; }
+                b2[pb] = nb2;
+            }
+            if (g == 0 && ok[pb]) {
+                // no finite distance (no centre, or a NaN row): slot 0, and the row is flagged
+                labels[(int64_t)bh * N + rr[pb]] = bi[pb] == 0x7fffffff ? 0 : bi[pb];
+                const float err = err_c * xn[pb] + ERR_C * c2max;
+                if (!(b2[pb] - b1[pb] > 2.0f * err)) {
+                    const int pos = atomicAdd(&fs.count[bh], 1);
+                    fs.list[(int64_t)bh * N + pos] = rr[pb];
+                    fs.thr[(int64_t)bh * N + pos] = b1[pb] + 3.0f * err;
+                }
             }
         }
     }
 }
 
-hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
-                         CentView cv, const int32_t* mcount, int32_t* labels, int32_t* flag_list,
-                         int32_t* flag_count, hipStream_t s) {
-    hipError_t e = fill_i32(flag_count, p.BH, 0, s);
-    if (e != hipSuccess) return e;
-    dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)p.BH);
+template <bool CAND>
+static void launch_assign_t(const Prob& p, dim3 grid, const void* x, RowSet rs,
+                            const float* inv_norm, int normalize, CentView cv,
+                            const int32_t* mcount, int32_t* labels, FlagSet fs, hipStream_t s) {
     if (p.bf16) {
-        if (p.D == 64)
-            hipLaunchKernelGGL((assign_kernel<u16, 64, false>), grid, dim3(256), 0, s, (const u16*)x,
-                               p.N, rs, inv_norm, cv, mcount, labels, flag_list, flag_count);
-        else
-            hipLaunchKernelGGL((assign_kernel<u16, 128, false>), grid, dim3(256), 0, s,
-                               (const u16*)x, p.N, rs, inv_norm, cv, mcount, labels, flag_list,
-                               flag_count);
+        auto k = p.D == 64 ? assign_kernel<u16, 64, false, CAND> : assign_kernel<u16, 128, false, CAND>;
+        hipLaunchKernelGGL(k, grid, dim3(256), 0, s, (const u16*)x, p.N, rs, inv_norm, normalize, cv,
+                           mcount, labels, fs);
     } else {
-        if (p.D == 64)
-            hipLaunchKernelGGL((assign_kernel<float, 64, true>), grid, dim3(256), 0, s,
-                               (const float*)x, p.N, rs, inv_norm, cv, mcount, labels, flag_list,
-                               flag_count);
-        else
-            hipLaunchKernelGGL((assign_kernel<float, 128, true>), grid, dim3(256), 0, s,
-                               (const float*)x, p.N, rs, inv_norm, cv, mcount, labels, flag_list,
-                               flag_count);
+        auto k = p.D == 64 ? assign_kernel<float, 64, true, CAND> : assign_kernel<float, 128, true, CAND>;
+        hipLaunchKernelGGL(k, grid, dim3(256), 0, s, (const float*)x, p.N, rs, inv_norm, normalize,
+                           cv, mcount, labels, fs);
     }
-    return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ exact recheck
-// One wave per flagged row: squared distances to every slot holding a centre,
-// summed over dimensions in index order in f64 (as the definition), argmin
-// with ties to the lowest slot.
+// One wave per row: squared distances to every slot holding a centre, summed
+// over dimensions in index order in f64 (as the definition), argmin with ties
+// to the lowest slot. Used for rows whose uncertainty band holds too many
+// centres (degenerate data such as repeated points).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void refine_kernel(const T* __restrict__ X, int N, int normalize,
                                                      RowSet rs, CentView cv,
@@ -584,30 +639,34 @@ __global__ __launch_bounds__(256) void refine_kernel(const T* __restrict__ X, in
     }
 }
 
-hipError_t launch_refine(const Prob& p, const void* x, int normalize, RowSet rs, CentView cv,
-                         const int32_t* mcount, const int32_t* flag_list, const int32_t* flag_count,
-                         int32_t* labels, hipStream_t s) {
-    // enough workgroups to cover a few percent of the rows in one pass
-    int gx = (p.N / 4 + 255) / 256;
-    if (gx < 4) gx = 4;
-    if (gx > 256) gx = 256;
-    dim3 grid((unsigned)gx, (unsigned)p.BH);
+static hipError_t launch_refine_full(const Prob& p, const void* x, int normalize, RowSet rs,
+                                     CentView cv, const int32_t* mcount, const int32_t* list,
+                                     const int32_t* count, int32_t* labels, hipStream_t s) {
+    dim3 grid(8u, (unsigned)p.BH);
     if (p.bf16) {
-        if (p.D == 64)
-            hipLaunchKernelGGL((refine_kernel<u16, 64>), grid, dim3(256), 0, s, (const u16*)x, p.N,
-                               normalize, rs, cv, mcount, flag_list, flag_count, labels);
-        else
-            hipLaunchKernelGGL((refine_kernel<u16, 128>), grid, dim3(256), 0, s, (const u16*)x, p.N,
-                               normalize, rs, cv, mcount, flag_list, flag_count, labels);
+        auto k = p.D == 64 ? refine_kernel<u16, 64> : refine_kernel<u16, 128>;
+        hipLaunchKernelGGL(k, grid, dim3(256), 0, s, (const u16*)x, p.N, normalize, rs, cv, mcount,
+                           list, count, labels);
     } else {
-        if (p.D == 64)
-            hipLaunchKernelGGL((refine_kernel<float, 64>), grid, dim3(256), 0, s, (const float*)x,
-                               p.N, normalize, rs, cv, mcount, flag_list, flag_count, labels);
-        else
-            hipLaunchKernelGGL((refine_kernel<float, 128>), grid, dim3(256), 0, s, (const float*)x,
-                               p.N, normalize, rs, cv, mcount, flag_list, flag_count, labels);
+        auto k = p.D == 64 ? refine_kernel<float, 64> : refine_kernel<float, 128>;
+        hipLaunchKernelGGL(k, grid, dim3(256), 0, s, (const float*)x, p.N, normalize, rs, cv, mcount,
+                           list, count, labels);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
+                         int normalize, CentView cv, const int32_t* mcount, int32_t* labels,
+                         FlagSet fs, hipStream_t s) {
+    hipError_t e = fill_i32(fs.count, p.BH, 0, s);
+    if (e != hipSuccess) return e;
+    if ((e = fill_i32(fs.over_count, p.BH, 0, s)) != hipSuccess) return e;
+    dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)p.BH);
+    launch_assign_t<false>(p, grid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    launch_assign_t<true>(p, grid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return launch_refine_full(p, x, normalize, rs, cv, mcount, fs.over, fs.over_count, labels, s);
 }
 
 // ------------------------------------------------------------------ update
