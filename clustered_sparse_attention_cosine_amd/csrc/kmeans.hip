@@ -330,20 +330,27 @@ hipError_t launch_finalize(const Prob& p, CentView cv, const uint8_t* active, in
 
 // ------------------------------------------------------------------ assignment
 // Workgroup = 4 waves x 64 rows. The centres stream through LDS in tiles of 64
-// (bf16 hi and lo parts); each wave computes S^T = C . X^T with 16x16x32 bf16
-// MFMAs (rows of the MFMA = centres, columns = points), so a lane owns one
-// point per 16-point block and tracks the best and second-best
-//   d_j = ||c_j||^2 - 2 s (x . c_j)      (s = 1 / ||x|| for queries, else 1)
-// The contraction error of one d_j is at most err = ERR_X s||x|| max||c|| +
-// ERR_C max||c||^2 (hi/lo residual 2^-16 plus f32 accumulation, with margin).
-// A row whose best two values are not separated by 2 err is flagged, with the
-// band edge thr = best + 3 err.
+// (bf16 hi and lo parts, double-buffered, the next tile loaded while the
+// current one is contracted); each wave computes S^T = C . X^T with 16x16x32
+// bf16 MFMAs (rows of the MFMA = centres, columns = points), so a lane owns
+// one point per 16-point block and 16 centres per tile. For each centre it
+// forms
+//   d'_j = ||c_j||^2 + B - 2 s (x . c_j)      (s = 1 / ||x|| for queries, else 1)
+// with a per-workgroup offset B that makes every d' positive, and keeps the
+// smallest and second-smallest sort keys of d' (bits of d' with the centre's
+// position in the tile in the 4 low mantissa bits; 4 VALU ops per distance).
+// The contraction error of one d' is at most err = ERR_X s||x|| max||c|| +
+// ERR_C max||c||^2 + 2^-22 (max||c||^2 + B + 2 s||x|| max||c||) (hi/lo residual,
+// f32 accumulation, rounding of ||c||^2 + B and of the final fma, with margin),
+// and the key moves a value by less than 2^-19 of itself. A row whose best two
+// keys are not separated by 2 err + 2^-17 d2 is flagged, with the band edge
+// thr = best - B + 3 err + 2^-17 best (in units of ||c||^2 - 2 s x.c).
 //
-// CAND mode runs the same contraction (same operands, same order, so the same
-// d_j) over the flagged rows only and collects every centre with d_j <= thr.
-// The exact nearest centre is among them (|d_j - exact| <= err), so exact f64
-// distances of the candidates decide the label; a row with more than CAND_CAP
-// candidates goes to the full exact scan (launch_refine).
+// CAND mode runs the same contraction over the flagged rows only, without the
+// offset, and collects every centre with ||c_j||^2 - 2 s x.c_j <= thr. The
+// exact nearest centre is among them, so exact f64 distances of the candidates
+// decide the label; a row with more than CAND_CAP candidates goes to the full
+// exact scan (launch_refine).
 constexpr int CAND_CAP = 16;
 
 template <typename T>
@@ -360,6 +367,19 @@ __device__ double exact_d2(const T* xr, int D, int normalize, const float* c) {
     return s;
 }
 
+// Sort key of one distance for the running minimum: d' >= 0 (see below), so
+// its bit pattern orders as an unsigned integer; the 4 low mantissa bits are
+// replaced by the position of the centre among the lane's 16 in the tile.
+__device__ __forceinline__ uint32_t dist_key(float d, uint32_t pos) {
+    return (__float_as_uint(d) & ~15u) | pos;
+}
+// Second smallest of {a, b, c} given a <= b: the median.
+__device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t r;
+    asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 template <typename T, int D, bool F32X, bool CAND>
 __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
                                                      const float* __restrict__ inv_norm,
@@ -370,9 +390,10 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
     constexpr int LD = D + 8;
     constexpr float ERR_X = F32X ? 0x1.0p-12f : 0x1.0p-13f;
     constexpr float ERR_C = 0x1.0p-21f;
-    __shared__ __attribute__((aligned(16))) u16 sh_hi[64 * LD];
-    __shared__ __attribute__((aligned(16))) u16 sh_lo[64 * LD];
-    __shared__ float sh_c2[64];
+    __shared__ __attribute__((aligned(16))) u16 sh_hi[2][64 * LD];
+    __shared__ __attribute__((aligned(16))) u16 sh_lo[2][64 * LD];
+    __shared__ float sh_c2[2][64];
+    __shared__ float sh_red[2][4];
     __shared__ int cand[CAND ? 256 : 1][CAND_CAP];
     __shared__ int ccount[CAND ? 256 : 1];
 
@@ -383,6 +404,7 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
     if (row_base >= n) return;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c16 = l & 15;
     const int M = mcount ? min(mcount[bh], cv.m) : cv.m;
+    const int64_t cbase = (int64_t)bh * cv.cap + cv.base;
     if constexpr (CAND) ccount[tid] = 0;
 
     bf16x8 xh[4][KC];
@@ -407,21 +429,33 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
         float ss = 0.0f;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-            float v[8];
-            if (ok[pb]) {
-                load8<T>(xp + kc * 32 + g * 8, v);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
-            xh[pb][kc] = pack_bf16x8(v);
             if constexpr (F32X) {
+                float v[8];
+                if (ok[pb]) {
+                    load8<T>(xp + kc * 32 + g * 8, v);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
+                xh[pb][kc] = pack_bf16x8(v);
                 float lo[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) lo[i] = v[i] - bf2f(xh[pb][kc][i]);
                 xl[pb][kc] = pack_bf16x8(lo);
+            } else {
+                // bf16 rows are MFMA operands as they stand
+                uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+                if (ok[pb]) raw = *reinterpret_cast<const uint4*>(xp + kc * 32 + g * 8);
+                xh[pb][kc] = __builtin_bit_cast(bf16x8, raw);
+                const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float a = __uint_as_float(wd[i] << 16), b = __uint_as_float(wd[i] & 0xFFFF0000u);
+                    ss += a * a;
+                    ss += b * b;
+                }
             }
         }
         ss += __shfl_xor(ss, 16);
@@ -430,82 +464,121 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
         xn[pb] = sc[pb] * sqrtf(ss);
     }
 
-    float b1[4], b2[4];
-    int bi[4];
+    // Assignment pass: d'_j = ||c_j||^2 + B - 2 s (x . c_j) with one offset B per
+    // workgroup, B = max_rows (s||x||)^2 + 2^-10 (max_rows s||x|| + max||c||)^2.
+    // d'_j - B + (s||x||)^2 is the squared distance, so d' > 0 by a margin far
+    // above the contraction error and the argmin is unchanged.
+    float c2max = 0.0f, bwg = 0.0f;
+    if constexpr (!CAND) {
+        float cm = 0.0f, xm = 0.0f;
+        for (int j = tid; j < M; j += 256) {
+            const float c2 = cv.cn2[cbase + j];
+            if (c2 < INFINITY) cm = fmaxf(cm, c2);
+        }
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb) { b1[pb] = INFINITY; b2[pb] = INFINITY; bi[pb] = 0x7fffffff; }
-    float c2max = 0.0f;
-    const int64_t cbase = (int64_t)bh * cv.cap + cv.base;
+        for (int pb = 0; pb < 4; ++pb) xm = fmaxf(xm, xn[pb]);
+        cm = wave_max(cm);
+        xm = wave_max(xm);
+        if (l == 0) { sh_red[0][w] = cm; sh_red[1][w] = xm; }
+        __syncthreads();
+        c2max = fmaxf(fmaxf(sh_red[0][0], sh_red[0][1]), fmaxf(sh_red[0][2], sh_red[0][3]));
+        xm = fmaxf(fmaxf(sh_red[1][0], sh_red[1][1]), fmaxf(sh_red[1][2], sh_red[1][3]));
+        const float t = xm + sqrtf(c2max);
+        bwg = xm * xm + 0x1.0p-10f * t * t;
+    }
+    float kx[4];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) kx[pb] = -2.0f * sc[pb];
+    uint32_t b1[4], b2[4];
+    int tb[4];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) { b1[pb] = 0xffffffffu; b2[pb] = 0xffffffffu; tb[pb] = 0; }
     const int ntiles = (M + 63) / 64;
 
-    for (int tile = 0; tile < ntiles; ++tile) {
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) {
-            const int c = tid + i * 256;
-            const int row = c / (D / 8), col8 = c % (D / 8);
-            const int j = tile * 64 + row;
-            uint4 vh = make_uint4(0, 0, 0, 0), vl = make_uint4(0, 0, 0, 0);
-            if (j < M) {
-                vh = *reinterpret_cast<const uint4*>(cv.c_hi + (cbase + j) * D + col8 * 8);
-                vl = *reinterpret_cast<const uint4*>(cv.c_lo + (cbase + j) * D + col8 * 8);
-            }
-            *reinterpret_cast<uint4*>(&sh_hi[row * LD + col8 * 8]) = vh;
-            *reinterpret_cast<uint4*>(&sh_lo[row * LD + col8 * 8]) = vl;
-        }
-        if (tid < 64) {
-            const int j = tile * 64 + tid;
-            sh_c2[tid] = (j < M) ? cv.cn2[cbase + j] : INFINITY;
-        }
-        __syncthreads();
+    // Centre tiles: double-buffered in LDS, the next tile in flight in registers
+    // while the current one is contracted. The loads are unconditional, from
+    // clamped slots; slots past M get ||c||^2 = +inf.
+    uint4 ph[D / 32], pl[D / 32];
+    float pc2;
+#define ADC_LOAD_TILE(TILE)                                                                  \
+    do {                                                                                   \
+        _Pragma("unroll") for (int i = 0; i < D / 32; ++i) {                               \
+            const int c = tid + i * 256;                                                   \
+            const int64_t j = cbase + min((TILE) * 64 + c / (D / 8), M - 1);               \
+            ph[i] = *reinterpret_cast<const uint4*>(cv.c_hi + j * D + (c % (D / 8)) * 8);  \
+            pl[i] = *reinterpret_cast<const uint4*>(cv.c_lo + j * D + (c % (D / 8)) * 8);  \
+        }                                                                                  \
+        pc2 = cv.cn2[cbase + min((TILE) * 64 + (tid & 63), M - 1)];                        \
+    } while (0)
+#define ADC_STORE_TILE(TILE, BUF)                                                          \
+    do {                                                                                   \
+        _Pragma("unroll") for (int i = 0; i < D / 32; ++i) {                               \
+            const int c = tid + i * 256;                                                   \
+            const int o = (c / (D / 8)) * LD + (c % (D / 8)) * 8;                          \
+            *reinterpret_cast<uint4*>(&sh_hi[BUF][o]) = ph[i];                             \
+            *reinterpret_cast<uint4*>(&sh_lo[BUF][o]) = pl[i];                             \
+        }                                                                                  \
+        if (tid < 64) sh_c2[BUF][tid] = (TILE) * 64 + tid < M ? pc2 + bwg : INFINITY;      \
+    } while (0)
+    if (ntiles > 0) {
+        ADC_LOAD_TILE(0);
+        ADC_STORE_TILE(0, 0);
+    }
+    __syncthreads();
 
-        f32x4 acc[4][4];
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const int buf = tile & 1;
+        ADC_LOAD_TILE(min(tile + 1, ntiles - 1));
+        uint32_t prev[4];
 #pragma unroll
-        for (int pb = 0; pb < 4; ++pb)
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) acc[pb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int pb = 0; pb < 4; ++pb) prev[pb] = b1[pb];
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
+            f32x4 acc[4];
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 const int off = (cb * 16 + c16) * LD + kc * 32 + g * 8;
-                bf16x8 ah = *reinterpret_cast<const bf16x8*>(&sh_hi[off]);
-                bf16x8 al = *reinterpret_cast<const bf16x8*>(&sh_lo[off]);
+                const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&sh_hi[buf][off]);
+                const bf16x8 al = *reinterpret_cast<const bf16x8*>(&sh_lo[buf][off]);
 #pragma unroll
                 for (int pb = 0; pb < 4; ++pb) {
-                    acc[pb][cb] = mfma16(ah, xh[pb][kc], acc[pb][cb]);
-                    acc[pb][cb] = mfma16(al, xh[pb][kc], acc[pb][cb]);
-                    if constexpr (F32X) acc[pb][cb] = mfma16(ah, xl[pb][kc], acc[pb][cb]);
+                    acc[pb] = mfma16(ah, xh[pb][kc], acc[pb]);
+                    acc[pb] = mfma16(al, xh[pb][kc], acc[pb]);
+                    if constexpr (F32X) acc[pb] = mfma16(ah, xl[pb][kc], acc[pb]);
                 }
             }
-        }
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
+            const f32x4 c2v = *reinterpret_cast<const f32x4*>(&sh_c2[buf][cb * 16 + g * 4]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int jl = cb * 16 + g * 4 + i;
-                const float c2 = sh_c2[jl];
-                const int j = tile * 64 + jl;
-                if constexpr (!CAND) {
-                    if (c2 < INFINITY) c2max = fmaxf(c2max, c2);
-                }
 #pragma unroll
                 for (int pb = 0; pb < 4; ++pb) {
-                    const float dv = fmaf(-2.0f * sc[pb], acc[pb][cb][i], c2);
+                    const float dv = fmaf(kx[pb], acc[pb][i], c2v[i]);
                     if constexpr (CAND) {
+                        const int j = tile * 64 + cb * 16 + g * 4 + i;
                         if (j < M && dv <= thr[pb]) {
                             const int prow = w * 64 + pb * 16 + c16;
                             const int pos = atomicAdd(&ccount[prow], 1);
                             if (pos < CAND_CAP) cand[prow][pos] = j;
                         }
                     } else {
-                        b2[pb] = fmaxf(b1[pb], fminf(b2[pb], dv));
-                        if (dv < b1[pb]) { b1[pb] = dv; bi[pb] = j; }
+                        const uint32_t key = dist_key(dv, (uint32_t)(cb * 4 + i));
+                        b2[pb] = med3_u32(b1[pb], b2[pb], key);
+                        b1[pb] = min(b1[pb], key);
                     }
                 }
             }
         }
+        if constexpr (!CAND) {
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) tb[pb] = b1[pb] != prev[pb] ? tile : tb[pb];
+        }
+        ADC_STORE_TILE(tile + 1, buf ^ 1);
+        __syncthreads();
     }
+#undef ADC_LOAD_TILE
+#undef ADC_STORE_TILE
 
     if constexpr (CAND) {
         __syncthreads();
@@ -531,29 +604,37 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
             }
         }
     } else {
-        c2max = fmaxf(c2max, __shfl_xor(c2max, 16));
-        c2max = fmaxf(c2max, __shfl_xor(c2max, 32));
-        const float err_c = ERR_X * sqrtf(c2max);
+        const float cmax = sqrtf(c2max);
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) {
+            const uint32_t pos = b1[pb] & 15u;
+            int bj = tb[pb] * 64 + (int)(pos >> 2) * 16 + g * 4 + (int)(pos & 3u);
 #pragma unroll
             for (int o = 16; o <= 32; o <<= 1) {
-                const float ob1 = __shfl_xor(b1[pb], o);
-                const float ob2 = __shfl_xor(b2[pb], o);
-                const int obi = __shfl_xor(bi[pb], o);
-                const bool take = ob1 < b1[pb] || (ob1 == b1[pb] && obi < bi[pb]);
-                const float nb2 = take ? fminf(b1[pb], ob2) : fminf(b2[pb], ob1);
-                if (take) { b1[pb] = ob1; bi[pb] = obi; }
-                b2[pb] = nb2;
+                const uint32_t ob1 = __shfl_xor(b1[pb], o);
+                const uint32_t ob2 = __shfl_xor(b2[pb], o);
+                const int obj = __shfl_xor(bj, o);
+                const bool take = ob1 < b1[pb] || (ob1 == b1[pb] && obj < bj);
+                b2[pb] = min(max(b1[pb], ob1), min(b2[pb], ob2));
+                if (take) { b1[pb] = ob1; bj = obj; }
             }
             if (g == 0 && ok[pb]) {
+                const bool finite = b1[pb] < 0x7f800000u;
                 // no finite distance (no centre, or a NaN row): slot 0, and the row is flagged
-                labels[(int64_t)bh * N + rr[pb]] = bi[pb] == 0x7fffffff ? 0 : bi[pb];
-                const float err = err_c * xn[pb] + ERR_C * c2max;
-                if (!(b2[pb] - b1[pb] > 2.0f * err)) {
-                    const int pos = atomicAdd(&fs.count[bh], 1);
-                    fs.list[(int64_t)bh * N + pos] = rr[pb];
-                    fs.thr[(int64_t)bh * N + pos] = b1[pb] + 3.0f * err;
+                labels[(int64_t)bh * N + rr[pb]] = finite ? bj : 0;
+                const float d1 = __uint_as_float(b1[pb]);
+                const float d2 = b2[pb] < 0x7f800000u ? __uint_as_float(b2[pb]) : INFINITY;
+                // contraction error of one d' (hi/lo residual and f32 accumulation,
+                // plus the rounding of ||c||^2 + B and of the final fma); the key
+                // truncation moves a value by less than 2^-19 of itself
+                const float err = ERR_X * xn[pb] * cmax + ERR_C * c2max +
+                                  0x1.0p-22f * (c2max + bwg + 2.0f * xn[pb] * cmax);
+                if (!finite || !(d2 - d1 > 2.0f * err + 0x1.0p-17f * d2)) {
+                    const int fpos = atomicAdd(&fs.count[bh], 1);
+                    fs.list[(int64_t)bh * N + fpos] = rr[pb];
+                    // band edge in the units of ||c||^2 - 2 s x.c (the CAND pass has no B)
+                    fs.thr[(int64_t)bh * N + fpos] =
+                        finite ? (d1 - bwg) + 3.0f * err + 0x1.0p-17f * d1 : -INFINITY;
                 }
             }
         }
