@@ -12,6 +12,7 @@
 // S^T = K Q^T with 16x16x32 bf16 MFMAs so that a lane owns one query column,
 // the output as O^T += V^T P^T reusing the score registers as the B operand.
 #include <math.h>
+#include <type_traits>
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -102,10 +103,87 @@ __global__ __launch_bounds__(256) void worklist_kernel(int Cq, int cap,
     if (tid == 0) n_items[bh] = running;
 }
 
+// head_pos[bh] = number of work items of the heads before bh; head_pos[BH] = total.
+__global__ __launch_bounds__(1024) void head_scan_kernel(int BH, const int32_t* __restrict__ n_items,
+                                                         int32_t* __restrict__ head_pos) {
+    __shared__ int wsum[16];
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    int running = 0;
+    if (tid == 0) head_pos[0] = 0;
+    for (int base = 0; base < BH; base += 1024) {
+        const int i = base + tid;
+        const int v = i < BH ? n_items[i] : 0;
+        int incl = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(incl, o);
+            if (l >= o) incl += u;
+        }
+        if (l == 63) wsum[w] = incl;
+        __syncthreads();
+        int before = running;
+        for (int k = 0; k < w; ++k) before += wsum[k];
+        if (i < BH) head_pos[i + 1] = before + incl;
+        for (int k = 0; k < 16; ++k) running += wsum[k];
+        __syncthreads();
+    }
+}
+
 hipError_t launch_worklist(const Prob& p, int Cq, int cap, const int32_t* q_offsets,
-                           int32_t* items, int32_t* n_items, hipStream_t s) {
+                           int32_t* items, int32_t* n_items, int32_t* head_pos, hipStream_t s) {
     hipLaunchKernelGGL(worklist_kernel, dim3((unsigned)p.BH), dim3(256), 0, s, Cq, cap, q_offsets,
                        items, n_items);
+    hipLaunchKernelGGL(head_scan_kernel, dim3(1), dim3(1024), 0, s, p.BH, n_items, head_pos);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ operand planes
+// The attention kernel reads 16-bit operand planes. bf16 inputs: K' is used as
+// it is and V' is converted once to fp16 here (the P.V product runs in fp16;
+// the conversion is exact for |v| in the fp16 normal range). f32 inputs: K' and
+// V' are split into bf16 hi + lo planes (x = hi + lo to 2^-16 relative).
+__global__ __launch_bounds__(256) void planes_f16_kernel(const u16* __restrict__ x, int64_t n8,
+                                                         u16* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n8) return;
+    const uint4 r = *reinterpret_cast<const uint4*>(x + i * 8);
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        o[k] = pack_h2(__uint_as_float(w[k] << 16), __uint_as_float(w[k] & 0xFFFF0000u));
+    *reinterpret_cast<uint4*>(out + i * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__global__ __launch_bounds__(256) void planes_split_kernel(const float* __restrict__ x, int64_t n8,
+                                                           u16* __restrict__ hi, u16* __restrict__ lo) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n8) return;
+    float v[8];
+    load8<float>(x + i * 8, v);
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const u16 h0 = f2bf_bits(v[2 * k]), h1 = f2bf_bits(v[2 * k + 1]);
+        const u16 l0 = f2bf_bits(v[2 * k] - bf_bits2f(h0)), l1 = f2bf_bits(v[2 * k + 1] - bf_bits2f(h1));
+        h[k] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        l[k] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
+    *reinterpret_cast<uint4*>(hi + i * 8) = make_uint4(h[0], h[1], h[2], h[3]);
+    *reinterpret_cast<uint4*>(lo + i * 8) = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+hipError_t launch_planes(const Prob& p, const void* k, const void* v, u16* k_hi, u16* k_lo,
+                         u16* v_hi, u16* v_lo, hipStream_t s) {
+    const int64_t n8 = (int64_t)p.BH * p.N * p.D / 8;
+    if (n8 <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((n8 + 255) / 256));
+    if (p.bf16) {
+        hipLaunchKernelGGL(planes_f16_kernel, grid, dim3(256), 0, s, (const u16*)v, n8, v_hi);
+    } else {
+        hipLaunchKernelGGL(planes_split_kernel, grid, dim3(256), 0, s, (const float*)k, n8, k_hi, k_lo);
+        hipLaunchKernelGGL(planes_split_kernel, grid, dim3(256), 0, s, (const float*)v, n8, v_hi, v_lo);
+    }
     return hipGetLastError();
 }
 
@@ -147,7 +225,7 @@ __device__ __forceinline__ void load_row8_split<float>(const float* p, bool ok, 
 // Window of 64 runs starting at run r0, loaded by one wave: lane k fetches the
 // first position and first key row of run r0 + k, and every lane the first
 // position of run r0 + 64. Loads are clamped and unconditional; validity is
-// applied where the values are used (tile_rows), so nothing waits here.
+// applied where the values are used (tile_rows).
 struct RunWindow {
     int r0, vp, vs, v64;
 };
@@ -168,7 +246,7 @@ __device__ __forceinline__ void load_window(int lane, int r0, int R, const int32
 // counted from a 64-bit mask of the starts inside the tile. Writes krow[lane]
 // (-1 past the selection) and returns the run holding position t0 + 64.
 __device__ __forceinline__ int tile_rows(int lane, int t0, int total, int R, const RunWindow& wd,
-                                         int* krow, bool write) {
+                                         int* krow) {
     const int r0 = wd.r0;
     const int wp = r0 + lane <= R ? wd.vp : 0x7fffffff;
     const int ws = r0 + lane < R ? wd.vs : 0;
@@ -188,209 +266,180 @@ __device__ __forceinline__ int tile_rows(int lane, int t0, int total, int R, con
     const int k = __popcll(starts & upto) - 1;
     const int rs_k = __shfl(ws, k), rp_k = __shfl(wp, k);
     const int P = t0 + lane;
-    if (write) krow[lane] = P < total ? rs_k + (P - rp_k) : -1;
+    krow[lane] = P < total ? rs_k + (P - rp_k) : -1;
     const int c = __popcll(__ballot(wp <= t0 + 64));
     return (c == 64 && wp64 <= t0 + 64) ? r0 + 64 : r0 + c - 1;
 }
 
-// Raw 16-byte chunk: 8 bf16 words (4 registers) or 8 floats (8 registers).
-template <typename T> struct Raw8 { uint32_t w[4]; };
-template <> struct Raw8<float> { uint32_t w[8]; };
+// Global -> register staging of one K/V tile (64 key rows, NP 16-bit planes
+// each), NT threads, 16-byte chunks. Rows past the selection (krow = -1) read
+// row 0: their scores are masked to -inf, so their probabilities are exactly 0
+// and the finite values they carry never reach the output.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <typename T>
-__device__ __forceinline__ void load_raw8(const T* p, Raw8<T>& r) {
-    const uint4 a = *reinterpret_cast<const uint4*>(p);
-    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
-    if constexpr (sizeof(T) == 4) {
-        const uint4 b = *reinterpret_cast<const uint4*>(p + 4);
-        r.w[4] = b.x; r.w[5] = b.y; r.w[6] = b.z; r.w[7] = b.w;
-    }
-}
+template <int D, int NP, int NT>
+struct TileRegs {
+    static constexpr int TASK = 64 * (D / 8);
+    static constexpr int CT = TASK / NT;
+    static_assert(TASK % NT == 0, "tile chunks must divide among the threads");
+    u32x4 k[NP][CT], v[NP][CT];
+};
 
-// Raw chunk -> packed bf16 words (hi) and, for f32, the rounding residual (lo).
-template <typename T>
-__device__ __forceinline__ void split_raw8(const Raw8<T>& r, bool ok, uint32_t (&hi)[4],
-                                           uint32_t (&lo)[4]) {
-    if constexpr (sizeof(T) == 2) {
+template <int D, int NP, int NT>
+__device__ __forceinline__ void tile_load(TileRegs<D, NP, NT>& r, int tid, const int* krow,
+                                          const u16* K0, const u16* K1, const u16* V0,
+                                          const u16* V1) {
+    using TR = TileRegs<D, NP, NT>;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { hi[i] = ok ? r.w[i] : 0u; lo[i] = 0u; }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float v0 = ok ? __uint_as_float(r.w[2 * i]) : 0.0f;
-            const float v1 = ok ? __uint_as_float(r.w[2 * i + 1]) : 0.0f;
-            const u16 h0 = f2bf_bits(v0), h1 = f2bf_bits(v1);
-            const u16 l0 = f2bf_bits(v0 - bf_bits2f(h0)), l1 = f2bf_bits(v1 - bf_bits2f(h1));
-            hi[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            lo[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    for (int i = 0; i < TR::CT; ++i) {
+        const int c = tid + i * NT;
+        const int row = max(krow[c / (D / 8)], 0);
+        const int64_t off = (int64_t)row * D + (c % (D / 8)) * 8;
+        r.k[0][i] = *reinterpret_cast<const u32x4*>(K0 + off);
+        r.v[0][i] = *reinterpret_cast<const u32x4*>(V0 + off);
+        if constexpr (NP == 2) {
+            r.k[NP - 1][i] = *reinterpret_cast<const u32x4*>(K1 + off);
+            r.v[NP - 1][i] = *reinterpret_cast<const u32x4*>(V1 + off);
         }
     }
 }
 
-// Global -> register staging of one K/V tile (64 key rows), NT threads. Loads
-// are issued unconditionally from clamped rows and held raw; masking and
-// conversion happen in tile_store, so the loads stay in flight until then.
-template <typename T, int D, int NT>
-struct TileRegs {
-    static constexpr int KTASK = 64 * (D / 8);      // 16-byte chunks of the K tile
-    static constexpr int VTASK = 32 * (D / 8);      // (key pair, 8 dims) tasks of the V tile
-    static constexpr int KT = (KTASK + NT - 1) / NT;
-    static constexpr int VT = (VTASK + NT - 1) / NT;
-    Raw8<T> k[KT];
-    Raw8<T> va[VT], vb[VT];
-    bool aok[VT], bok[VT];
-};
-
-template <typename T, int D, int NT>
-__device__ __forceinline__ void tile_load(TileRegs<T, D, NT>& r, int tid, const int* krow,
-                                          const T* Kh, const T* Vh) {
-    // krow entries are -1 (past the selection) or key rows of this head
-    using TR = TileRegs<T, D, NT>;
+// Register -> LDS, both K and V row-major (padded stride LDK).
+template <int D, int NP, int NT, int LDK>
+__device__ __forceinline__ void tile_store(const TileRegs<D, NP, NT>& r, int tid,
+                                           u16 (*Ks)[64 * LDK], u16 (*Vs)[64 * LDK]) {
+    using TR = TileRegs<D, NP, NT>;
 #pragma unroll
-    for (int i = 0; i < TR::KT; ++i) {
+    for (int i = 0; i < TR::CT; ++i) {
         const int c = tid + i * NT;
-        if (TR::KTASK % NT != 0 && c >= TR::KTASK) break;
-        const int kr = c / (D / 8), c8 = c % (D / 8);
-        const int row = krow[kr];
-        load_raw8<T>(Kh + (int64_t)(row < 0 ? 0 : row) * D + c8 * 8, r.k[i]);
-    }
+        const int o = (c / (D / 8)) * LDK + (c % (D / 8)) * 8;
 #pragma unroll
-    for (int i = 0; i < TR::VT; ++i) {
-        const int c = tid + i * NT;
-        if (TR::VTASK % NT != 0 && c >= TR::VTASK) break;
-        const int kk = c % 32, c8 = c / 32;
-        const int ra = krow[2 * kk], rb = krow[2 * kk + 1];
-        r.aok[i] = ra >= 0;
-        r.bok[i] = rb >= 0;
-        load_raw8<T>(Vh + (int64_t)(ra < 0 ? 0 : ra) * D + c8 * 8, r.va[i]);
-        load_raw8<T>(Vh + (int64_t)(rb < 0 ? 0 : rb) * D + c8 * 8, r.vb[i]);
+        for (int pl = 0; pl < NP; ++pl) {
+            *reinterpret_cast<u32x4*>(&Ks[pl][o]) = r.k[pl][i];
+            *reinterpret_cast<u32x4*>(&Vs[pl][o]) = r.v[pl][i];
+        }
     }
 }
 
-// Register -> LDS: K row-major, V transposed (fp16 for bf16 inputs, bf16 hi/lo for f32).
-template <typename T, int D, int NP, int NT, int LDK, int LDV>
-__device__ __forceinline__ void tile_store(const TileRegs<T, D, NT>& r, int tid,
-                                           u16 (*Ks)[64 * LDK], u16 (*Vt)[D * LDV]) {
-    using TR = TileRegs<T, D, NT>;
-    constexpr bool PREC = NP == 2;
-#pragma unroll
-    for (int i = 0; i < TR::KT; ++i) {
-        const int c = tid + i * NT;
-        if (TR::KTASK % NT != 0 && c >= TR::KTASK) break;
-        const int kr = c / (D / 8), c8 = c % (D / 8);
-        uint32_t hv[4], lv[4];
-        split_raw8<T>(r.k[i], true, hv, lv);
-        *reinterpret_cast<uint4*>(&Ks[0][kr * LDK + c8 * 8]) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
-        if constexpr (PREC)
-            *reinterpret_cast<uint4*>(&Ks[NP - 1][kr * LDK + c8 * 8]) = make_uint4(lv[0], lv[1], lv[2], lv[3]);
-    }
-#pragma unroll
-    for (int i = 0; i < TR::VT; ++i) {
-        const int c = tid + i * NT;
-        if (TR::VTASK % NT != 0 && c >= TR::VTASK) break;
-        const int kk = c % 32, c8 = c / 32;
-        uint32_t va[2][4], vb[2][4];
-        split_raw8<T>(r.va[i], r.aok[i], va[0], va[1]);
-        split_raw8<T>(r.vb[i], r.bok[i], vb[0], vb[1]);
-#pragma unroll
-        for (int pp = 0; pp < NP; ++pp)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t a = va[pp][j], b = vb[pp][j];
-                uint32_t lo_w, hi_w;
-                if constexpr (PREC) {
-                    lo_w = (a & 0xFFFFu) | (b << 16);
-                    hi_w = (a >> 16) | (b & 0xFFFF0000u);
-                } else {
-                    // bf16 -> fp16 is exact for |v| inside the fp16 normal range
-                    lo_w = pack_h2(__uint_as_float(a << 16), __uint_as_float(b << 16));
-                    hi_w = pack_h2(__uint_as_float(a & 0xFFFF0000u), __uint_as_float(b & 0xFFFF0000u));
-                }
-                *reinterpret_cast<uint32_t*>(&Vt[pp][(c8 * 8 + 2 * j) * LDV + 2 * kk]) = lo_w;
-                *reinterpret_cast<uint32_t*>(&Vt[pp][(c8 * 8 + 2 * j + 1) * LDV + 2 * kk]) = hi_w;
-            }
-    }
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Transposed 16x32 fragment of a row-major V tile (stride LDK) for the A
+// operand of O^T += V^T P^T. Lane L (group G = L/16) receives V[key][d] for
+// d = L%16 of a 16-column block and the 8 keys 32c + 4G + {0..3},
+// 32c + 16 + 4G + {0..3}: the key order of the lane's probabilities. In each
+// 16-lane group of a ds_read_tr16_b64, source lane a + 4j points at columns
+// 4a..4a+3 of key row j and destination lane 4a + b collects column b of
+// source lanes a, a + 4, a + 8, a + 12. `p` is the lane's address for the
+// first four keys (row 32c + 4G + j, column block start + 4a).
+template <int LDK>
+__device__ __forceinline__ uint4 v_frag(const u16* p) {
+    const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+    const v4i16 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 16 * LDK));
+    const uint2 xu = __builtin_bit_cast(uint2, x), yu = __builtin_bit_cast(uint2, y);
+    return make_uint4(xu.x, xu.y, yu.x, yu.y);
 }
 
 // Online-softmax update of one 16-query block over one 64-key tile (the lane
 // holds query c16 and keys kb*16 + 4g + i). Scores come in raw; sl2 = scale *
-// log2(e) is applied inside the exponent.
-template <int DB>
-__device__ __forceinline__ void softmax_block(f32x4 (&sc)[4], float sl2, bool mask_tail, int t0,
-                                              int g, int total, float& m_run, float& l_part,
-                                              f32x4 (&o)[DB]) {
-    if (mask_tail) {
+// log2(e) is applied inside the exponent. MASK: the tile runs past the last
+// selected key (positions >= total get probability 0).
+//
+// The running maximum m (log2 units) is raised only when some row of the wave
+// sees a score above m + 8; otherwise the stale m is kept, so every
+// probability is at most 2^8 (exact as an f32 summand, finite in fp16) and the
+// rescale of O is skipped. The result is the same softmax: numerator and
+// denominator share the factor 2^-m whatever m is. The row sums are
+// accumulated by the matrix cores (a block of ones in the P.V product), so
+// they are part of o and rescaled with it.
+template <int DB, bool MASK>
+__device__ __forceinline__ void softmax_block(f32x4 (&sc)[4], float sl2, int t0, int g, int total,
+                                              float& m_run, f32x4 (&o)[DB + 1]) {
+    if constexpr (MASK) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (t0 + kb * 16 + g * 4 + i >= total) sc[kb][i] = -INFINITY;
     }
-    float mx = fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3]));
-#pragma unroll
-    for (int kb = 1; kb < 4; ++kb)
-        mx = fmaxf(mx, fmaxf(fmaxf(sc[kb][0], sc[kb][1]), fmaxf(sc[kb][2], sc[kb][3])));
+    float mx = fmaxf(fmaxf(sc[0][0], sc[0][1]), sc[0][2]);
+    mx = fmaxf(fmaxf(mx, sc[0][3]), sc[1][0]);
+    mx = fmaxf(fmaxf(mx, sc[1][1]), sc[1][2]);
+    mx = fmaxf(fmaxf(mx, sc[1][3]), sc[2][0]);
+    mx = fmaxf(fmaxf(mx, sc[2][1]), sc[2][2]);
+    mx = fmaxf(fmaxf(mx, sc[2][3]), sc[3][0]);
+    mx = fmaxf(fmaxf(mx, sc[3][1]), sc[3][2]);
+    mx = fmaxf(mx, sc[3][3]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * sl2);
-    const float base = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - base);
-    float lsum = 0.0f;
+    const float ms = mx * sl2;
+    if (__ballot(ms > m_run + 8.0f) != 0) {
+        const float m_new = fmaxf(m_run, ms);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+        for (int db = 0; db <= DB; ++db) o[db] *= alpha;
+        m_run = m_new;
+    }
+    const float nb = (m_run == -INFINITY) ? 0.0f : -m_run;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float pv = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], sl2, -base));
-            sc[kb][i] = pv;
-            lsum += pv;
-        }
-    l_part = fmaf(l_part, alpha, lsum);
-    if (alpha != 1.0f) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= alpha;
-    }
-    m_run = m_new;
+        for (int i = 0; i < 4; ++i) sc[kb][i] = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], sl2, nb));
 }
 
 // A work item is (head, q-cluster, chunk of ATTN_ROWS query rows); the NT/64
 // waves each own RB blocks of 16 rows (a block with no rows is skipped). K/V
-// tiles of 64 keys are double-buffered in LDS: the global loads of tile t+1
-// are in flight while tile t is computed, and the key rows of tile t+2 are
-// looked up by wave 0 at the same time, so one barrier per tile suffices.
-// PREC (f32 inputs): operands carried as bf16 hi + lo and every product of
-// order <= 1 accumulated (3 MFMAs per product instead of 1), near f32 accuracy.
-template <typename T, int D, typename TO, int NT, int RB>
-__global__ __launch_bounds__(NT) void attn_kernel(int N, int Cq, const T* __restrict__ Q,
-                                                  const int32_t* __restrict__ q_perm,
-                                                  const int32_t* __restrict__ q_off,
-                                                  const T* __restrict__ Kp, const T* __restrict__ Vp,
-                                                  const int32_t* __restrict__ run_start,
-                                                  const int32_t* __restrict__ run_pos,
-                                                  const int32_t* __restrict__ n_runs, int run_cap,
-                                                  const int32_t* __restrict__ items,
-                                                  const int32_t* __restrict__ n_items, int cap,
-                                                  float sl2, TO* __restrict__ O,
-                                                  float* __restrict__ lse) {
+// tiles of 64 keys are double-buffered in LDS; the global loads of tiles t+1
+// and t+2 are in flight in registers while tile t is computed, and wave 0
+// looks up the key rows of tile t+3 meanwhile, so one barrier per tile
+// suffices. Operands are 16-bit planes (NP = 1: K bf16, V fp16; NP = 2: bf16
+// hi and lo of f32 data, every product of order <= 1 accumulated, three
+// MFMAs per product, near f32 accuracy).
+template <typename T, int D, typename TO, int NT, int RB, int WPE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE, 8)))
+void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restrict__ q_perm,
+                 const int32_t* __restrict__ q_off, const u16* __restrict__ K0,
+                 const u16* __restrict__ K1, const u16* __restrict__ V0,
+                 const u16* __restrict__ V1, const int32_t* __restrict__ run_start,
+                 const int32_t* __restrict__ run_pos, const int32_t* __restrict__ n_runs,
+                 int run_cap, const int32_t* __restrict__ items,
+                 const int32_t* __restrict__ head_pos, int BH, int cap, float sl2,
+                 TO* __restrict__ O, float* __restrict__ lse) {
     static_assert((NT / 64) * RB * 16 == ATTN_ROWS, "waves x blocks must cover a work item");
     constexpr bool PREC = sizeof(T) == 4;
-    constexpr int NP = PREC ? 2 : 1;  // stored parts per operand
+    constexpr int NP = PREC ? 2 : 1;  // operand planes
     constexpr int KC = D / 32;        // 32-wide chunks of the head dimension
     constexpr int DB = D / 16;        // 16-row blocks of O^T
-    constexpr int LDK = D + 8;        // padded LDS strides (elements)
-    constexpr int LDV = 64 + 8;
+    constexpr int LDK = D + 8;        // padded LDS row stride (elements)
     __shared__ __attribute__((aligned(16))) u16 Ks[2][NP][64 * LDK];
-    __shared__ __attribute__((aligned(16))) u16 Vt[2][NP][D * LDV];
+    __shared__ __attribute__((aligned(16))) u16 Vs[2][NP][64 * LDK];
     __shared__ int krow[4][64];
 
-    const int bh = blockIdx.x / cap;
-    if ((int)(blockIdx.x % cap) >= n_items[bh]) return;
-    const int packed = items[blockIdx.x];
+    // Work item order: workgroup b runs on XCD b % 8 (round-robin dispatch), so
+    // it takes item (b % 8) * per + b / 8: each XCD walks one contiguous stretch
+    // of the list (a few heads, q-clusters in order), and the workgroups in
+    // flight on one XCD read overlapping key ranges through its own L2.
+    const int n_total = __builtin_amdgcn_readfirstlane(head_pos[BH]);
+    const int per = (n_total + 7) >> 3;
+    const int kx = blockIdx.x >> 3;
+    if (kx >= per) return;
+    const int item = (blockIdx.x & 7) * per + kx;
+    if (item >= n_total) return;
+    int hlo = 0, hhi = BH;  // head_pos[hlo] <= item < head_pos[hhi]
+    while (hhi - hlo > 1) {
+        const int mid = (hlo + hhi) >> 1;
+        if (__builtin_amdgcn_readfirstlane(head_pos[mid]) <= item) hlo = mid; else hhi = mid;
+    }
+    const int bh = hlo;
+    const int packed = __builtin_amdgcn_readfirstlane(
+        items[(int64_t)bh * cap + item - __builtin_amdgcn_readfirstlane(head_pos[bh])]);
     const int a = packed & 0xFFFF, ch = packed >> 16;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c16 = l & 15;
+    const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     const int32_t* qo = q_off + (int64_t)bh * (Cq + 1);
-    const int row0 = qo[a] + ch * ATTN_ROWS;
-    const int nrows = min(ATTN_ROWS, qo[a + 1] - row0);
+    const int row0 = __builtin_amdgcn_readfirstlane(qo[a]) + ch * ATTN_ROWS;
+    const int nrows = min(ATTN_ROWS, __builtin_amdgcn_readfirstlane(qo[a + 1]) - row0);
     bool live[RB];
     bf16x8 qf[RB][NP][KC];
     int64_t qtok[RB];
@@ -413,139 +462,157 @@ __global__ __launch_bounds__(NT) void attn_kernel(int N, int Cq, const T* __rest
     }
 
     const int64_t rbase = (int64_t)bh * Cq + a;
-    const int R = n_runs[rbase];
+    const int R = __builtin_amdgcn_readfirstlane(n_runs[rbase]);
     const int32_t* rs = run_start + rbase * run_cap;
     const int32_t* rp = run_pos + rbase * (run_cap + 1);
-    const int total = rp[R];
+    const int total = __builtin_amdgcn_readfirstlane(rp[R]);
     const int ntiles = (total + 63) / 64;
-    const T* Kh = Kp + (int64_t)bh * N * D;
-    const T* Vh = Vp + (int64_t)bh * N * D;
+    const int64_t hoff = (int64_t)bh * N * D;
+    const u16* const Kh0 = K0 + hoff;
+    const u16* const Vh0 = V0 + hoff;
+    const u16* const Kh1 = PREC ? K1 + hoff : Kh0;
+    const u16* const Vh1 = PREC ? V1 + hoff : Vh0;
 
-    float m_run[RB], l_part[RB];
-    f32x4 o[RB][DB];
+    float m_run[RB];
+    f32x4 o[RB][DB + 1];  // O^T blocks and the row-sum block
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         m_run[rb] = -INFINITY;
-        l_part[rb] = 0.0f;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int db = 0; db <= DB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // per-lane LDS offset of the transposed V reads (key row 4g + j, column 4a)
+    const int vlane = (4 * g + ((l & 15) >> 2)) * LDK + 4 * (l & 3);
 
-    // Key rows are looked up three tiles ahead; tiles t+1 and t+2 are in flight
-    // in two register sets while tile t is computed from LDS. Every wave issues
-    // the same loads every step (tiles past the end read clamped, valid rows and
-    // are never used) so the load counters stay exact and no wait reaches back
-    // past the tile being consumed. Every wave computes the row lookup; wave 0
-    // writes it.
     RunWindow wd;
-    load_window(l, 0, R, rs, rp, wd);
-    int r_next = tile_rows(l, 0, total, R, wd, krow[0], w == 0);
+    int r_next = 0;
+    if (w == 0) {
+        load_window(l, 0, R, rs, rp, wd);
+        r_next = tile_rows(l, 0, total, R, wd, krow[0]);
 #pragma unroll
-    for (int j = 1; j < 3; ++j) {
+        for (int j = 1; j < 3; ++j) {
+            load_window(l, r_next, R, rs, rp, wd);
+            r_next = tile_rows(l, j * 64, total, R, wd, krow[j]);
+        }
         load_window(l, r_next, R, rs, rp, wd);
-        r_next = tile_rows(l, j * 64, total, R, wd, krow[j], w == 0);
     }
-    load_window(l, r_next, R, rs, rp, wd);
     __syncthreads();
-    TileRegs<T, D, NT> tr0, tr1;
-    tile_load<T, D, NT>(tr0, tid, krow[0], Kh, Vh);
-    tile_load<T, D, NT>(tr1, tid, krow[1], Kh, Vh);
-    tile_store<T, D, NP, NT, LDK, LDV>(tr0, tid, Ks[0], Vt[0]);
+    TileRegs<D, NP, NT> tr0, tr1;
+    tile_load<D, NP, NT>(tr0, tid, krow[0], Kh0, Kh1, Vh0, Vh1);
+    tile_load<D, NP, NT>(tr1, tid, krow[1], Kh0, Kh1, Vh0, Vh1);
+    tile_store<D, NP, NT, LDK>(tr0, tid, Ks[0], Vs[0]);
     __syncthreads();
 
-    // one tile: look up t+3, prefetch t+2 into the register set tile t used,
-    // compute t, store t+1 into the other LDS buffer
-    auto step = [&](int t, auto& tr_mine, auto& tr_next) {
+    // one tile: look up t+3 (wave 0), prefetch t+2 into the register set tile t
+    // used, compute t, store t+1 into the other LDS buffer. Every wave issues
+    // the same tile loads every step (tiles past the end read clamped, valid
+    // rows and are never used), so the load counters stay exact.
+    auto step = [&](int t, auto& tr_mine, auto& tr_next) __attribute__((always_inline)) {
         const int b = t & 1;
         const int t0 = t * 64;
-        const int rn = tile_rows(l, t0 + 192, total, R, wd, krow[(t + 3) & 3], w == 0);
-        load_window(l, rn, R, rs, rp, wd);
-        tile_load<T, D, NT>(tr_mine, tid, krow[(t + 2) & 3], Kh, Vh);
-        if (t < ntiles && live[0]) {
-                const bool mask_tail = t0 + 64 > total;
-                f32x4 sc[RB][4];
-    #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-    #pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) sc[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    #pragma unroll
-                    for (int kc = 0; kc < KC; ++kc) {
-                        const int off = (kb * 16 + c16) * LDK + kc * 32 + g * 8;
-                        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[b][0][off]);
-                        bf16x8 kl;
-                        if constexpr (PREC) kl = *reinterpret_cast<const bf16x8*>(&Ks[b][NP - 1][off]);
-    #pragma unroll
-                        for (int rb = 0; rb < RB; ++rb) {
-                            if (rb > 0 && !live[rb]) continue;
-                            if constexpr (PREC) {
-                                sc[rb][kb] = mfma16(kl, qf[rb][0][kc], sc[rb][kb]);
-                                sc[rb][kb] = mfma16(ka, qf[rb][NP - 1][kc], sc[rb][kb]);
-                            }
-                            sc[rb][kb] = mfma16(ka, qf[rb][0][kc], sc[rb][kb]);
+        if (w == 0) {
+            const int rn = tile_rows(l, t0 + 192, total, R, wd, krow[(t + 3) & 3]);
+            load_window(l, rn, R, rs, rp, wd);
+        }
+        tile_load<D, NP, NT>(tr_mine, tid, krow[(t + 2) & 3], Kh0, Kh1, Vh0, Vh1);
+        auto compute = [&](auto mask_c) __attribute__((always_inline)) {
+            constexpr bool MASK = decltype(mask_c)::value;
+            f32x4 sc[RB][4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) sc[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) {
+                    const int off = (kb * 16 + c16) * LDK + kc * 32 + g * 8;
+                    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[b][0][off]);
+                    bf16x8 kl;
+                    if constexpr (PREC) kl = *reinterpret_cast<const bf16x8*>(&Ks[b][NP - 1][off]);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) {
+                        if (rb > 0 && !live[rb]) continue;
+                        if constexpr (PREC) {
+                            sc[rb][kb] = mfma16(kl, qf[rb][0][kc], sc[rb][kb]);
+                            sc[rb][kb] = mfma16(ka, qf[rb][NP - 1][kc], sc[rb][kb]);
                         }
-                    }
-                }
-    #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    if (rb > 0 && !live[rb]) continue;
-                    softmax_block<DB>(sc[rb], sl2, mask_tail, t0, g, total, m_run[rb], l_part[rb], o[rb]);
-                }
-    #pragma unroll
-                for (int kc2 = 0; kc2 < 2; ++kc2) {
-                    if constexpr (PREC) {
-                        bf16x8 pb[RB], pl[RB];
-    #pragma unroll
-                        for (int rb = 0; rb < RB; ++rb)
-    #pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                pb[rb][j] = f2bf(sc[rb][2 * kc2][j]);
-                                pb[rb][4 + j] = f2bf(sc[rb][2 * kc2 + 1][j]);
-                                pl[rb][j] = f2bf(sc[rb][2 * kc2][j] - bf2f(pb[rb][j]));
-                                pl[rb][4 + j] = f2bf(sc[rb][2 * kc2 + 1][j] - bf2f(pb[rb][4 + j]));
-                            }
-    #pragma unroll
-                        for (int db = 0; db < DB; ++db) {
-                            const int off = (db * 16 + c16) * LDV + kc2 * 32 + g * 4;
-                            const uint2 lo0 = *reinterpret_cast<const uint2*>(&Vt[b][0][off]);
-                            const uint2 hi0 = *reinterpret_cast<const uint2*>(&Vt[b][0][off + 16]);
-                            const uint2 lo1 = *reinterpret_cast<const uint2*>(&Vt[b][NP - 1][off]);
-                            const uint2 hi1 = *reinterpret_cast<const uint2*>(&Vt[b][NP - 1][off + 16]);
-                            const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo0.x, lo0.y, hi0.x, hi0.y));
-                            const bf16x8 vl = __builtin_bit_cast(bf16x8, make_uint4(lo1.x, lo1.y, hi1.x, hi1.y));
-    #pragma unroll
-                            for (int rb = 0; rb < RB; ++rb) {
-                                if (rb > 0 && !live[rb]) continue;
-                                o[rb][db] = mfma16(vl, pb[rb], o[rb][db]);
-                                o[rb][db] = mfma16(va, pl[rb], o[rb][db]);
-                                o[rb][db] = mfma16(va, pb[rb], o[rb][db]);
-                            }
-                        }
-                    } else {
-                        // P.V in fp16 (11-bit significand): probabilities lose at most 2^-12
-                        f16x8 ph[RB];
-    #pragma unroll
-                        for (int rb = 0; rb < RB; ++rb)
-                            ph[rb] = __builtin_bit_cast(
-                                f16x8, make_uint4(pack_h2(sc[rb][2 * kc2][0], sc[rb][2 * kc2][1]),
-                                                  pack_h2(sc[rb][2 * kc2][2], sc[rb][2 * kc2][3]),
-                                                  pack_h2(sc[rb][2 * kc2 + 1][0], sc[rb][2 * kc2 + 1][1]),
-                                                  pack_h2(sc[rb][2 * kc2 + 1][2], sc[rb][2 * kc2 + 1][3])));
-    #pragma unroll
-                        for (int db = 0; db < DB; ++db) {
-                            const int off = (db * 16 + c16) * LDV + kc2 * 32 + g * 4;
-                            const uint2 lo0 = *reinterpret_cast<const uint2*>(&Vt[b][0][off]);
-                            const uint2 hi0 = *reinterpret_cast<const uint2*>(&Vt[b][0][off + 16]);
-                            const f16x8 vh = __builtin_bit_cast(f16x8, make_uint4(lo0.x, lo0.y, hi0.x, hi0.y));
-    #pragma unroll
-                            for (int rb = 0; rb < RB; ++rb) {
-                                if (rb > 0 && !live[rb]) continue;
-                                o[rb][db] = mfma16h(vh, ph[rb], o[rb][db]);
-                            }
-                        }
+                        sc[rb][kb] = mfma16(ka, qf[rb][0][kc], sc[rb][kb]);
                     }
                 }
             }
-            tile_store<T, D, NP, NT, LDK, LDV>(tr_next, tid, Ks[b ^ 1], Vt[b ^ 1]);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                if (rb > 0 && !live[rb]) continue;
+                softmax_block<DB, MASK>(sc[rb], sl2, t0, g, total, m_run[rb], o[rb]);
+            }
+#pragma unroll
+            for (int kc2 = 0; kc2 < 2; ++kc2) {
+                const u16* vb0 = &Vs[b][0][vlane + kc2 * 32 * LDK];
+                if constexpr (PREC) {
+                    const u16* vb1 = &Vs[b][NP - 1][vlane + kc2 * 32 * LDK];
+                    const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u,
+                                                                              0x3F803F80u, 0x3F803F80u));
+                    bf16x8 pb[RB], pl[RB];
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            pb[rb][j] = f2bf(sc[rb][2 * kc2][j]);
+                            pb[rb][4 + j] = f2bf(sc[rb][2 * kc2 + 1][j]);
+                            pl[rb][j] = f2bf(sc[rb][2 * kc2][j] - bf2f(pb[rb][j]));
+                            pl[rb][4 + j] = f2bf(sc[rb][2 * kc2 + 1][j] - bf2f(pb[rb][4 + j]));
+                        }
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        const bf16x8 va = __builtin_bit_cast(bf16x8, v_frag<LDK>(vb0 + db * 16));
+                        const bf16x8 vl = __builtin_bit_cast(bf16x8, v_frag<LDK>(vb1 + db * 16));
+#pragma unroll
+                        for (int rb = 0; rb < RB; ++rb) {
+                            if (rb > 0 && !live[rb]) continue;
+                            o[rb][db] = mfma16(vl, pb[rb], o[rb][db]);
+                            o[rb][db] = mfma16(va, pl[rb], o[rb][db]);
+                            o[rb][db] = mfma16(va, pb[rb], o[rb][db]);
+                        }
+                    }
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) {
+                        if (rb > 0 && !live[rb]) continue;
+                        o[rb][DB] = mfma16(ones, pl[rb], o[rb][DB]);
+                        o[rb][DB] = mfma16(ones, pb[rb], o[rb][DB]);
+                    }
+                } else {
+                    // P.V in fp16 (11-bit significand): probabilities lose at most 2^-12
+                    const f16x8 ones = __builtin_bit_cast(f16x8, make_uint4(0x3C003C00u, 0x3C003C00u,
+                                                                            0x3C003C00u, 0x3C003C00u));
+                    f16x8 ph[RB];
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        ph[rb] = __builtin_bit_cast(
+                            f16x8, make_uint4(pack_h2(sc[rb][2 * kc2][0], sc[rb][2 * kc2][1]),
+                                              pack_h2(sc[rb][2 * kc2][2], sc[rb][2 * kc2][3]),
+                                              pack_h2(sc[rb][2 * kc2 + 1][0], sc[rb][2 * kc2 + 1][1]),
+                                              pack_h2(sc[rb][2 * kc2 + 1][2], sc[rb][2 * kc2 + 1][3])));
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        const f16x8 vh = __builtin_bit_cast(f16x8, v_frag<LDK>(vb0 + db * 16));
+#pragma unroll
+                        for (int rb = 0; rb < RB; ++rb) {
+                            if (rb > 0 && !live[rb]) continue;
+                            o[rb][db] = mfma16h(vh, ph[rb], o[rb][db]);
+                        }
+                    }
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) {
+                        if (rb > 0 && !live[rb]) continue;
+                        o[rb][DB] = mfma16h(ones, ph[rb], o[rb][DB]);
+                    }
+                }
+            }
+        };
+        if (t < ntiles && live[0]) {
+            if (t0 + 64 > total) compute(std::true_type{});
+            else compute(std::false_type{});
+        }
+        tile_store<D, NP, NT, LDK>(tr_next, tid, Ks[b ^ 1], Vs[b ^ 1]);
         __syncthreads();
     };
     for (int t = 0; t < ntiles; t += 2) {
@@ -555,8 +622,7 @@ __global__ __launch_bounds__(NT) void attn_kernel(int N, int Cq, const T* __rest
 
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        float l_tot = l_part[rb] + __shfl_xor(l_part[rb], 16);
-        l_tot += __shfl_xor(l_tot, 32);
+        const float l_tot = o[rb][DB][0];  // every row of the ones block holds the sum
         if (qok[rb]) {
             const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
             TO* orow = O + ((int64_t)bh * N + qtok[rb]) * D;
@@ -581,34 +647,40 @@ constexpr int ATTN_RB = ATTN_ROWS / 16 / (ATTN_NT / 64);
 
 template <typename T, typename TO>
 static void launch_attn_t(const Prob& p, dim3 grid, int Cq, const void* q, const int32_t* q_perm,
-                          const int32_t* q_offsets, const void* k_perm, const void* v_perm,
-                          const int32_t* run_start, const int32_t* run_pos, const int32_t* n_runs,
-                          int run_cap, const int32_t* items, const int32_t* n_items, int cap,
-                          float sl2, void* out, float* lse, hipStream_t s) {
-    auto k = p.D == 64 ? attn_kernel<T, 64, TO, ATTN_NT, ATTN_RB> : attn_kernel<T, 128, TO, ATTN_NT, ATTN_RB>;
-    hipLaunchKernelGGL(k, grid, dim3(ATTN_NT), 0, s, p.N, Cq, (const T*)q, q_perm, q_offsets,
-                       (const T*)k_perm, (const T*)v_perm, run_start, run_pos, n_runs, run_cap,
-                       items, n_items, cap, sl2, (TO*)out, lse);
+                          const int32_t* q_offsets, const u16* k0, const u16* k1, const u16* v0,
+                          const u16* v1, const int32_t* run_start, const int32_t* run_pos,
+                          const int32_t* n_runs, int run_cap, const int32_t* items,
+                          const int32_t* head_pos, int cap, float sl2, void* out, float* lse,
+                          hipStream_t s) {
+    // waves per SIMD: two workgroups per CU where the registers allow it
+    constexpr int W64 = sizeof(T) == 2 ? 4 : 2;
+    auto k = p.D == 64 ? attn_kernel<T, 64, TO, ATTN_NT, ATTN_RB, W64>
+                       : attn_kernel<T, 128, TO, ATTN_NT, ATTN_RB, 2>;
+    hipLaunchKernelGGL(k, grid, dim3(ATTN_NT), 0, s, p.N, Cq, (const T*)q, q_perm, q_offsets, k0, k1,
+                       v0, v1, run_start, run_pos, n_runs, run_cap, items, head_pos, p.BH, cap, sl2,
+                       (TO*)out, lse);
 }
 
 hipError_t launch_attention(const Prob& p, int Cq, const void* q, const int32_t* q_perm,
-                            const int32_t* q_offsets, const void* k_perm, const void* v_perm,
-                            const int32_t* run_start, const int32_t* run_pos, const int32_t* n_runs,
-                            int run_cap, const int32_t* items, const int32_t* n_items, int cap,
-                            float scale, void* out, int out_f32, float* lse, hipStream_t s) {
+                            const int32_t* q_offsets, const u16* k0, const u16* k1,
+                            const u16* v0, const u16* v1, const int32_t* run_start,
+                            const int32_t* run_pos, const int32_t* n_runs, int run_cap,
+                            const int32_t* items, const int32_t* head_pos, int cap, float scale,
+                            void* out, int out_f32, float* lse, hipStream_t s) {
     if (cap <= 0) return hipSuccess;
     const float sl2 = scale * 1.4426950408889634f;
-    dim3 grid((unsigned)((int64_t)p.BH * cap));
+    // at most BH * cap items; 8 workgroups per step of the XCD-strided order
+    dim3 grid((unsigned)(((int64_t)p.BH * cap + 7) / 8 * 8));
     if (p.bf16) {
         if (out_f32)
-            launch_attn_t<u16, float>(p, grid, Cq, q, q_perm, q_offsets, k_perm, v_perm, run_start,
-                                      run_pos, n_runs, run_cap, items, n_items, cap, sl2, out, lse, s);
+            launch_attn_t<u16, float>(p, grid, Cq, q, q_perm, q_offsets, k0, k1, v0, v1, run_start,
+                                      run_pos, n_runs, run_cap, items, head_pos, cap, sl2, out, lse, s);
         else
-            launch_attn_t<u16, u16>(p, grid, Cq, q, q_perm, q_offsets, k_perm, v_perm, run_start,
-                                    run_pos, n_runs, run_cap, items, n_items, cap, sl2, out, lse, s);
+            launch_attn_t<u16, u16>(p, grid, Cq, q, q_perm, q_offsets, k0, k1, v0, v1, run_start,
+                                    run_pos, n_runs, run_cap, items, head_pos, cap, sl2, out, lse, s);
     } else {
-        launch_attn_t<float, float>(p, grid, Cq, q, q_perm, q_offsets, k_perm, v_perm, run_start,
-                                    run_pos, n_runs, run_cap, items, n_items, cap, sl2, out, lse, s);
+        launch_attn_t<float, float>(p, grid, Cq, q, q_perm, q_offsets, k0, k1, v0, v1, run_start,
+                                    run_pos, n_runs, run_cap, items, head_pos, cap, sl2, out, lse, s);
     }
     return hipGetLastError();
 }

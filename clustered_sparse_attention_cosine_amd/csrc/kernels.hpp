@@ -139,13 +139,15 @@ hipError_t launch_build_runs(const Prob& p, int Cq, int Ck, const int32_t* k_off
                              const uint32_t* mask, int run_cap, int32_t* run_start,
                              int32_t* run_pos, int32_t* n_runs, hipStream_t s);
 hipError_t launch_worklist(const Prob& p, int Cq, int cap, const int32_t* q_offsets,
-                           int32_t* items, int32_t* n_items, hipStream_t s);
+                           int32_t* items, int32_t* n_items, int32_t* head_pos, hipStream_t s);
+hipError_t launch_planes(const Prob& p, const void* k, const void* v, uint16_t* k_hi, uint16_t* k_lo,
+                         uint16_t* v_hi, uint16_t* v_lo, hipStream_t s);
 hipError_t launch_attention(const Prob& p, int Cq, const void* q, const int32_t* q_perm,
-                            const int32_t* q_offsets, const void* k_perm, const void* v_perm,
-                            const int32_t* run_start, const int32_t* run_pos,
-                            const int32_t* n_runs, int run_cap, const int32_t* items,
-                            const int32_t* n_items, int cap, float scale, void* out,
-                            int out_f32, float* lse, hipStream_t s);
+                            const int32_t* q_offsets, const uint16_t* k0, const uint16_t* k1,
+                            const uint16_t* v0, const uint16_t* v1, const int32_t* run_start,
+                            const int32_t* run_pos, const int32_t* n_runs, int run_cap,
+                            const int32_t* items, const int32_t* head_pos, int cap, float scale,
+                            void* out, int out_f32, float* lse, hipStream_t s);
 
 constexpr int ATTN_ROWS = 128;  // query rows per attention work item
 
