@@ -222,53 +222,27 @@ __device__ __forceinline__ void load_row8_split<float>(const float* p, bool ok, 
     }
 }
 
-// Window of 64 runs starting at run r0, loaded by one wave: lane k fetches the
-// first position and first key row of run r0 + k, and every lane the first
-// position of run r0 + 64. Loads are clamped and unconditional; validity is
-// applied where the values are used (tile_rows).
-struct RunWindow {
-    int r0, vp, vs, v64;
-};
-
-__device__ __forceinline__ void load_window(int lane, int r0, int R, const int32_t* rs,
-                                            const int32_t* rp, RunWindow& wd) {
-    const int k = r0 + lane;
-    wd.r0 = r0;
-    wd.vp = rp[min(k, R)];
-    wd.vs = rs[max(min(k, R - 1), 0)];
-    wd.v64 = rp[min(r0 + 64, R)];
-}
-
 // Key rows of one 64-position tile of the concatenated selection, computed by
-// one wave without LDS. Lane k holds run r0 + k: its first position wp
-// (INT_MAX past the last run) and first key row ws; run r0 holds position t0.
-// The run holding position t0 + lane is (number of run starts <= t0 + lane) - 1,
-// counted from a 64-bit mask of the starts inside the tile. Writes krow[lane]
-// (-1 past the selection) and returns the run holding position t0 + 64.
-__device__ __forceinline__ int tile_rows(int lane, int t0, int total, int R, const RunWindow& wd,
-                                         int* krow) {
-    const int r0 = wd.r0;
-    const int wp = r0 + lane <= R ? wd.vp : 0x7fffffff;
-    const int ws = r0 + lane < R ? wd.vs : 0;
-    const int wp64 = r0 + 64 <= R ? wd.v64 : 0x7fffffff;
-    const int s = wp - t0;
-    uint32_t lo = 0, hi = 0;
-    if (lane == 0) lo = 1u;
-    if (s >= 0 && s < 32) lo |= 1u << s;
-    else if (s >= 32 && s < 64) hi |= 1u << (s - 32);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        lo |= __shfl_xor(lo, o);
-        hi |= __shfl_xor(hi, o);
-    }
+// one wave. rn is the run holding position t0 (uniform). Lane k looks at the
+// start of run rn + 1 + k; the offsets of the starts inside (t0, t0 + 64) are
+// gathered into a 64-bit mask (an OR over the wave), and lane p counts the
+// starts at offsets <= p: run rn + count holds position t0 + p. Writes
+// krow[p] (-1 past the selection) and returns the run holding position
+// t0 + 64. rs/rp may point to LDS or to global memory.
+__device__ __forceinline__ int tile_rows(int lane, int t0, int total, int R, int rn,
+                                         const int32_t* rs, const int32_t* rp, int* krow) {
+    const int rk = rn + 1 + lane;
+    const int off = rp[min(rk, R)] - t0;  // rp[R] = total; off >= 1
+    const bool inside = rk < R && off < 64;
+    const uint32_t lo = wave_or(inside && off < 32 ? 1u << off : 0u);
+    const uint32_t hi = wave_or(inside && off >= 32 ? 1u << (off - 32) : 0u);
     const uint64_t starts = ((uint64_t)hi << 32) | lo;
     const uint64_t upto = lane == 63 ? ~0ull : ((2ull << lane) - 1ull);
-    const int k = __popcll(starts & upto) - 1;
-    const int rs_k = __shfl(ws, k), rp_k = __shfl(wp, k);
+    const int r = min(rn + (int)__popcll(starts & upto), R - 1);
     const int P = t0 + lane;
-    krow[lane] = P < total ? rs_k + (P - rp_k) : -1;
-    const int c = __popcll(__ballot(wp <= t0 + 64));
-    return (c == 64 && wp64 <= t0 + 64) ? r0 + 64 : r0 + c - 1;
+    const int row = rs[max(r, 0)] + (P - rp[max(r, 0)]);
+    krow[lane] = P < total ? row : -1;
+    return rn + (int)__popcll(__ballot(rk < R && off <= 64));
 }
 
 // Global -> register staging of one K/V tile (64 key rows, NP 16-bit planes
@@ -390,8 +364,8 @@ __device__ __forceinline__ void softmax_block(f32x4 (&sc)[4], float sl2, int t0,
 // A work item is (head, q-cluster, chunk of ATTN_ROWS query rows); the NT/64
 // waves each own RB blocks of 16 rows (a block with no rows is skipped). K/V
 // tiles of 64 keys are double-buffered in LDS; the global loads of tiles t+1
-// and t+2 are in flight in registers while tile t is computed, and wave 0
-// looks up the key rows of tile t+3 meanwhile, so one barrier per tile
+// and t+2 are in flight in registers while tile t is computed, and the last
+// wave looks up the key rows of tile t+3 meanwhile, so one barrier per tile
 // suffices. Operands are 16-bit planes (NP = 1: K bf16, V fp16; NP = 2: bf16
 // hi and lo of f32 data, every product of order <= 1 accumulated, three
 // MFMAs per product, near f32 accuracy).
@@ -414,6 +388,9 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
     __shared__ __attribute__((aligned(16))) u16 Ks[2][NP][64 * LDK];
     __shared__ __attribute__((aligned(16))) u16 Vs[2][NP][64 * LDK];
     __shared__ int krow[4][64];
+    // the work item's runs (first key row, first position) when they fit
+    constexpr int RL = 2048;
+    __shared__ int run_s[RL], run_p[RL + 1];
 
     // Work item order: workgroup b runs on XCD b % 8 (round-robin dispatch), so
     // it takes item (b % 8) * per + b / 8: each XCD walks one contiguous stretch
@@ -484,17 +461,23 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
     // per-lane LDS offset of the transposed V reads (key row 4g + j, column 4a)
     const int vlane = (4 * g + ((l & 15) >> 2)) * LDK + 4 * (l & 3);
 
-    RunWindow wd;
-    int r_next = 0;
-    if (w == 0) {
-        load_window(l, 0, R, rs, rp, wd);
-        r_next = tile_rows(l, 0, total, R, wd, krow[0]);
-#pragma unroll
-        for (int j = 1; j < 3; ++j) {
-            load_window(l, r_next, R, rs, rp, wd);
-            r_next = tile_rows(l, j * 64, total, R, wd, krow[j]);
-        }
-        load_window(l, r_next, R, rs, rp, wd);
+    // Run lookups read the run list from LDS (copied once here; a list longer
+    // than RL is read from global memory instead). They are made by the last
+    // wave, which has no query rows in most work items.
+    const bool runs_lds = R <= RL;
+    constexpr int LW = NT / 64 - 1;
+    for (int i = tid; i < R && runs_lds; i += NT) run_s[i] = rs[i];
+    for (int i = tid; i <= R && runs_lds; i += NT) run_p[i] = rp[i];
+    __syncthreads();
+    int rn = 0;
+    auto lookup = [&](int t) __attribute__((always_inline)) {
+        if (runs_lds) rn = tile_rows(l, t * 64, total, R, rn, run_s, run_p, krow[t & 3]);
+        else rn = tile_rows(l, t * 64, total, R, rn, rs, rp, krow[t & 3]);
+    };
+    if (w == LW) {
+        lookup(0);
+        lookup(1);
+        lookup(2);
     }
     __syncthreads();
     TileRegs<D, NP, NT> tr0, tr1;
@@ -503,17 +486,14 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
     tile_store<D, NP, NT, LDK>(tr0, tid, Ks[0], Vs[0]);
     __syncthreads();
 
-    // one tile: look up t+3 (wave 0), prefetch t+2 into the register set tile t
+    // one tile: look up t+3 (last wave), prefetch t+2 into the register set tile t
     // used, compute t, store t+1 into the other LDS buffer. Every wave issues
     // the same tile loads every step (tiles past the end read clamped, valid
     // rows and are never used), so the load counters stay exact.
     auto step = [&](int t, auto& tr_mine, auto& tr_next) __attribute__((always_inline)) {
         const int b = t & 1;
         const int t0 = t * 64;
-        if (w == 0) {
-            const int rn = tile_rows(l, t0 + 192, total, R, wd, krow[(t + 3) & 3]);
-            load_window(l, rn, R, rs, rp, wd);
-        }
+        if (w == LW) lookup(t + 3);
         tile_load<D, NP, NT>(tr_mine, tid, krow[(t + 2) & 3], Kh0, Kh1, Vh0, Vh1);
         auto compute = [&](auto mask_c) __attribute__((always_inline)) {
             constexpr bool MASK = decltype(mask_c)::value;
@@ -644,6 +624,10 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
 #endif
 constexpr int ATTN_NT = ADC_ATTN_NT;
 constexpr int ATTN_RB = ATTN_ROWS / 16 / (ATTN_NT / 64);
+#ifndef ADC_ATTN_WPE64
+#define ADC_ATTN_WPE64 4
+#endif
+constexpr int ATTN_WPE64 = ADC_ATTN_WPE64;  // waves per SIMD asked of the bf16 D=64 kernel
 
 template <typename T, typename TO>
 static void launch_attn_t(const Prob& p, dim3 grid, int Cq, const void* q, const int32_t* q_perm,
@@ -653,7 +637,7 @@ static void launch_attn_t(const Prob& p, dim3 grid, int Cq, const void* q, const
                           const int32_t* head_pos, int cap, float sl2, void* out, float* lse,
                           hipStream_t s) {
     // waves per SIMD: two workgroups per CU where the registers allow it
-    constexpr int W64 = sizeof(T) == 2 ? 4 : 2;
+    constexpr int W64 = sizeof(T) == 2 ? ATTN_WPE64 : 2;
     auto k = p.D == 64 ? attn_kernel<T, 64, TO, ATTN_NT, ATTN_RB, W64>
                        : attn_kernel<T, 128, TO, ATTN_NT, ATTN_RB, 2>;
     hipLaunchKernelGGL(k, grid, dim3(ATTN_NT), 0, s, p.N, Cq, (const T*)q, q_perm, q_offsets, k0, k1,

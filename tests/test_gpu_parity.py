@@ -131,6 +131,46 @@ def test_sparse_attn_edge_cases():
     assert np.abs(lse[fin] - ref_lse[fin]).max() <= 1e-2
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sparse_attn_many_runs(dtype):
+    # one key per slot: an alternating selection gives 1300 separate key ranges
+    # (more than the kernel keeps in LDS, so they are read from global memory),
+    # next to a full selection (one range) and a random 30% selection
+    rng = np.random.default_rng(11)
+    Nq, Nk, D, Cq = 300, 2600, 64, 3
+    N = Nk
+    x = [rng.standard_normal((1, 1, N, D)).astype(np.float32) for _ in range(3)]
+    if dtype == "bf16":
+        q, k, v = (synth.f32_to_bf16_bits(t) for t in x)
+    else:
+        q, k, v = x
+    qlab = np.concatenate([np.zeros(100), np.ones(100), np.full(100, 2),
+                           np.full(N - Nq, Cq)]).astype(np.int32)   # tokens past Nq: no cluster
+    qlab = np.minimum(qlab, Cq - 1)
+    klab = np.arange(N, dtype=np.int32)
+    Ck = N
+    qperm, qoff = oracle.permute(qlab, Cq)
+    kperm, koff = oracle.permute(klab, Ck)
+    words = (Ck + 31) // 32
+    bits = np.zeros((Cq, Ck), bool)
+    bits[0, ::2] = True
+    bits[1, :] = True
+    bits[2] = rng.random(Ck) < 0.3
+    mask = np.zeros((Cq, words), np.uint32)
+    for a in range(Cq):
+        for j in np.nonzero(bits[a])[0]:
+            mask[a, j // 32] |= np.uint32(1) << np.uint32(j % 32)
+    scale = 0.125
+    out, lse = adc.sparse_attn(dev(q), dev(qperm[None, None]), dev(qoff[None, None]),
+                               dev(k[:, :, kperm]), dev(v[:, :, kperm]), dev(koff[None, None]),
+                               dev(mask[None, None].view(np.int32)), scale=scale)
+    out, lse = host(out)[0, 0], host(lse)[0, 0]
+    ref, ref_lse = oracle.sparse_attn(synth.as_f32(q[0, 0]), synth.as_f32(k[0, 0]),
+                                      synth.as_f32(v[0, 0]), qlab, klab, Cq, Ck, mask, scale)
+    assert rel_l2(out, ref) <= 1e-2 and np.abs(out - ref).max() <= 2e-2
+    assert np.abs(lse - ref_lse).max() <= 1e-2
+
+
 # ----------------------------------------------------------------- assignment (lockstep)
 @pytest.mark.parametrize("case", list(CASES))
 @pytest.mark.parametrize("normalize", [False, True])
