@@ -344,9 +344,7 @@ __device__ __forceinline__ void softmax_block(f32x4 (&sc)[4], float sl2, int t0,
     mx = fmaxf(fmaxf(mx, sc[2][3]), sc[3][0]);
     mx = fmaxf(fmaxf(mx, sc[3][1]), sc[3][2]);
     mx = fmaxf(mx, sc[3][3]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float ms = mx * sl2;
+    const float ms = col_max4(mx) * sl2;
     if (__ballot(ms > m_run + 8.0f) != 0) {
         const float m_new = fmaxf(m_run, ms);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);

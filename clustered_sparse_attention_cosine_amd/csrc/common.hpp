@@ -84,6 +84,16 @@ __device__ __forceinline__ uint32_t pack_h2(float x, float y) {
 }
 
 // ------------------------------------------------------------------ wave / block reductions
+// Max over the four lanes l, l^16, l^32, l^48 (lanes holding one MFMA output
+// column), with the gfx950 row-swap permutes: each swap exchanges a row of 16
+// lanes with its partner row, so max(pair) is the max over the two rows.
+__device__ __forceinline__ float col_max4(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Bitwise OR over the wave, returned uniform: DPP row shifts give each row's
 // OR in its lane 15, row broadcasts carry rows 0-2 into lane 63.
 __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
