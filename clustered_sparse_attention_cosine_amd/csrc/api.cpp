@@ -88,6 +88,8 @@ struct KmeansWs {
     float* flag_thr = nullptr;
     int32_t* over_list = nullptr;
     int32_t* over_count = nullptr;
+    int32_t* cand = nullptr;
+    int32_t* ccount = nullptr;
     uint8_t* valid = nullptr;
     uint16_t* c_hi = nullptr;
     uint16_t* c_lo = nullptr;
@@ -110,6 +112,8 @@ void plan_kmeans(Carver& c, const Prob& p, int cap, bool want_inv, bool kpp, boo
     w.flag_thr = c.take<float>(bhn);
     w.over_list = c.take<int32_t>(bhn);
     w.over_count = c.take<int32_t>(p.BH);
+    w.cand = c.take<int32_t>(bhn * CAND_CAP);
+    w.ccount = c.take<int32_t>(bhn);
     w.valid = c.take<uint8_t>(bhc);
     w.c_hi = c.take<uint16_t>(bhc * p.D);
     w.c_lo = c.take<uint16_t>(bhc * p.D);
@@ -144,7 +148,8 @@ void plan_stages(Carver& c, const Prob& p, StageWs& w) {
 }
 
 FlagSet flags_of(const KmeansWs& w) {
-    return FlagSet{w.flag_list, w.flag_count, w.flag_thr, w.over_list, w.over_count};
+    return FlagSet{w.flag_list, w.flag_count, w.flag_thr, w.over_list, w.over_count, w.cand,
+                   w.ccount};
 }
 
 CentView make_view(float* cent, const KmeansWs& w, int cap, int base, int m) {

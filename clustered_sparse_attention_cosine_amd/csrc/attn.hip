@@ -249,8 +249,6 @@ __device__ __forceinline__ int tile_rows(int lane, int t0, int total, int R, int
 // each), NT threads, 16-byte chunks. Rows past the selection (krow = -1) read
 // row 0: their scores are masked to -inf, so their probabilities are exactly 0
 // and the finite values they carry never reach the output.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 template <int D, int NP, int NT>
 struct TileRegs {
     static constexpr int TASK = 64 * (D / 8);

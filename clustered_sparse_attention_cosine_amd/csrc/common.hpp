@@ -9,6 +9,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int WAVE = 64;
 

@@ -73,7 +73,10 @@ struct FlagSet {
     float* thr;
     int32_t* over;
     int32_t* over_count;
+    int32_t* cand;    // [BH, N, CAND_CAP] candidate slots of each flagged row
+    int32_t* ccount;  // [BH, N] number of candidates found (may exceed CAND_CAP)
 };
+constexpr int CAND_CAP = 16;
 // Nearest centre by a bf16 hi/lo matrix-core contraction with a certified
 // error bound; uncertain rows are settled by exact f64 distances of the
 // centres inside their uncertainty band (labels are final on return).

@@ -347,12 +347,11 @@ hipError_t launch_finalize(const Prob& p, CentView cv, const uint8_t* active, in
 // thr = best - B + 3 err + 2^-17 best (in units of ||c||^2 - 2 s x.c).
 //
 // CAND mode runs the same contraction over the flagged rows only, without the
-// offset, and collects every centre with ||c_j||^2 - 2 s x.c_j <= thr. The
-// exact nearest centre is among them, so exact f64 distances of the candidates
-// decide the label; a row with more than CAND_CAP candidates goes to the full
-// exact scan (launch_refine).
-constexpr int CAND_CAP = 16;
-
+// offset, and appends every centre with ||c_j||^2 - 2 s x.c_j <= thr to the
+// row's candidate list; the centre tiles are split over gridDim.z workgroups.
+// The exact nearest centre is among the candidates, so exact f64 distances of
+// the candidates decide the label (cand_exact_kernel); a row with no or more
+// than CAND_CAP candidates goes to the full exact scan (launch_refine).
 template <typename T>
 __device__ double exact_d2(const T* xr, int D, int normalize, const float* c) {
 #pragma clang fp contract(off)
@@ -385,7 +384,8 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
                                                      const float* __restrict__ inv_norm,
                                                      int normalize, CentView cv,
                                                      const int32_t* __restrict__ mcount,
-                                                     int32_t* __restrict__ labels, FlagSet fs) {
+                                                     int32_t* __restrict__ labels, FlagSet fs,
+                                                     int tiles_per_split) {
     constexpr int KC = D / 32;
     constexpr int LD = D + 8;
     constexpr float ERR_X = F32X ? 0x1.0p-12f : 0x1.0p-13f;
@@ -394,8 +394,6 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
     __shared__ __attribute__((aligned(16))) u16 sh_lo[2][64 * LD];
     __shared__ float sh_c2[2][64];
     __shared__ float sh_red[2][4];
-    __shared__ int cand[CAND ? 256 : 1][CAND_CAP];
-    __shared__ int ccount[CAND ? 256 : 1];
 
     const int bh = blockIdx.y;
     if (rs.active && !rs.active[bh]) return;
@@ -405,7 +403,10 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c16 = l & 15;
     const int M = mcount ? min(mcount[bh], cv.m) : cv.m;
     const int64_t cbase = (int64_t)bh * cv.cap + cv.base;
-    if constexpr (CAND) ccount[tid] = 0;
+    const int ntiles_all = (M + 63) / 64;
+    const int t_begin = CAND ? blockIdx.z * tiles_per_split : 0;
+    const int t_end = CAND ? min(ntiles_all, t_begin + tiles_per_split) : ntiles_all;
+    if (CAND && t_begin >= t_end) return;
 
     bf16x8 xh[4][KC];
     bf16x8 xl[4][F32X ? KC : 1];
@@ -493,20 +494,19 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
     int tb[4];
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) { b1[pb] = 0xffffffffu; b2[pb] = 0xffffffffu; tb[pb] = 0; }
-    const int ntiles = (M + 63) / 64;
 
     // Centre tiles: double-buffered in LDS, the next tile in flight in registers
     // while the current one is contracted. The loads are unconditional, from
     // clamped slots; slots past M get ||c||^2 = +inf.
-    uint4 ph[D / 32], pl[D / 32];
+    u32x4 ph[D / 32], pl[D / 32];
     float pc2;
 #define ADC_LOAD_TILE(TILE)                                                                  \
     do {                                                                                   \
         _Pragma("unroll") for (int i = 0; i < D / 32; ++i) {                               \
             const int c = tid + i * 256;                                                   \
             const int64_t j = cbase + min((TILE) * 64 + c / (D / 8), M - 1);               \
-            ph[i] = *reinterpret_cast<const uint4*>(cv.c_hi + j * D + (c % (D / 8)) * 8);  \
-            pl[i] = *reinterpret_cast<const uint4*>(cv.c_lo + j * D + (c % (D / 8)) * 8);  \
+            ph[i] = *reinterpret_cast<const u32x4*>(cv.c_hi + j * D + (c % (D / 8)) * 8); \
+            pl[i] = *reinterpret_cast<const u32x4*>(cv.c_lo + j * D + (c % (D / 8)) * 8); \
         }                                                                                  \
         pc2 = cv.cn2[cbase + min((TILE) * 64 + (tid & 63), M - 1)];                        \
     } while (0)
@@ -515,23 +515,24 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
         _Pragma("unroll") for (int i = 0; i < D / 32; ++i) {                               \
             const int c = tid + i * 256;                                                   \
             const int o = (c / (D / 8)) * LD + (c % (D / 8)) * 8;                          \
-            *reinterpret_cast<uint4*>(&sh_hi[BUF][o]) = ph[i];                             \
-            *reinterpret_cast<uint4*>(&sh_lo[BUF][o]) = pl[i];                             \
+            *reinterpret_cast<u32x4*>(&sh_hi[BUF][o]) = ph[i];                             \
+            *reinterpret_cast<u32x4*>(&sh_lo[BUF][o]) = pl[i];                             \
         }                                                                                  \
         if (tid < 64) sh_c2[BUF][tid] = (TILE) * 64 + tid < M ? pc2 + bwg : INFINITY;      \
     } while (0)
-    if (ntiles > 0) {
-        ADC_LOAD_TILE(0);
-        ADC_STORE_TILE(0, 0);
+    if (t_begin < t_end) {
+        ADC_LOAD_TILE(t_begin);
+        ADC_STORE_TILE(t_begin, 0);
     }
     __syncthreads();
 
-    for (int tile = 0; tile < ntiles; ++tile) {
-        const int buf = tile & 1;
-        ADC_LOAD_TILE(min(tile + 1, ntiles - 1));
+    for (int tile = t_begin; tile < t_end; ++tile) {
+        const int buf = (tile - t_begin) & 1;
+        ADC_LOAD_TILE(min(tile + 1, t_end - 1));
         uint32_t prev[4];
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) prev[pb] = b1[pb];
+        uint64_t hits = 0;  // CAND: candidates of this tile, bit pb*16 + cb*4 + i
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
             f32x4 acc[4];
@@ -557,11 +558,7 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
                     const float dv = fmaf(kx[pb], acc[pb][i], c2v[i]);
                     if constexpr (CAND) {
                         const int j = tile * 64 + cb * 16 + g * 4 + i;
-                        if (j < M && dv <= thr[pb]) {
-                            const int prow = w * 64 + pb * 16 + c16;
-                            const int pos = atomicAdd(&ccount[prow], 1);
-                            if (pos < CAND_CAP) cand[prow][pos] = j;
-                        }
+                        if (j < M && dv <= thr[pb]) hits |= 1ull << (pb * 16 + cb * 4 + i);
                     } else {
                         const uint32_t key = dist_key(dv, (uint32_t)(cb * 4 + i));
                         b2[pb] = med3_u32(b1[pb], b2[pb], key);
@@ -573,6 +570,15 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
         if constexpr (!CAND) {
 #pragma unroll
             for (int pb = 0; pb < 4; ++pb) tb[pb] = b1[pb] != prev[pb] ? tile : tb[pb];
+        } else {
+            while (hits) {
+                const int bit = __ffsll((unsigned long long)hits) - 1;
+                hits &= hits - 1;
+                const int pb = bit >> 4, cb = (bit >> 2) & 3, i = bit & 3;
+                const int64_t fe = (int64_t)bh * N + row_base + w * 64 + pb * 16 + c16;
+                const int pos = atomicAdd(&fs.ccount[fe], 1);
+                if (pos < CAND_CAP) fs.cand[fe * CAND_CAP + pos] = tile * 64 + cb * 16 + g * 4 + i;
+            }
         }
         ADC_STORE_TILE(tile + 1, buf ^ 1);
         __syncthreads();
@@ -580,30 +586,7 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
 #undef ADC_LOAD_TILE
 #undef ADC_STORE_TILE
 
-    if constexpr (CAND) {
-        __syncthreads();
-        // one thread per row: exact f64 distances of its candidates
-        const int e = row_base + tid;
-        if (e < n) {
-            const int r = fs.list[(int64_t)bh * N + e];
-            const int nc = ccount[tid];
-            if (nc > CAND_CAP || nc == 0) {
-                const int pos = atomicAdd(&fs.over_count[bh], 1);
-                fs.over[(int64_t)bh * N + pos] = r;
-            } else {
-                const int64_t tok = rs.rows ? rs.rows[(int64_t)bh * N + r] : r;
-                const T* xr = row_ptr(X, N, D, bh, tok);
-                double best = INFINITY;
-                int bj = 0x7fffffff;
-                for (int q = 0; q < nc; ++q) {
-                    const int j = cand[tid][q];
-                    const double d2 = exact_d2(xr, D, normalize, cv.cent + (cbase + j) * D);
-                    if (d2 < best || (d2 == best && j < bj)) { best = d2; bj = j; }
-                }
-                labels[(int64_t)bh * N + r] = bj;
-            }
-        }
-    } else {
+    if constexpr (!CAND) {
         const float cmax = sqrtf(c2max);
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) {
@@ -632,6 +615,7 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
                 if (!finite || !(d2 - d1 > 2.0f * err + 0x1.0p-17f * d2)) {
                     const int fpos = atomicAdd(&fs.count[bh], 1);
                     fs.list[(int64_t)bh * N + fpos] = rr[pb];
+                    fs.ccount[(int64_t)bh * N + fpos] = 0;
                     // band edge in the units of ||c||^2 - 2 s x.c (the CAND pass has no B)
                     fs.thr[(int64_t)bh * N + fpos] =
                         finite ? (d1 - bwg) + 3.0f * err + 0x1.0p-17f * d1 : -INFINITY;
@@ -644,15 +628,59 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
 template <bool CAND>
 static void launch_assign_t(const Prob& p, dim3 grid, const void* x, RowSet rs,
                             const float* inv_norm, int normalize, CentView cv,
-                            const int32_t* mcount, int32_t* labels, FlagSet fs, hipStream_t s) {
+                            const int32_t* mcount, int32_t* labels, FlagSet fs, int tps,
+                            hipStream_t s) {
     if (p.bf16) {
         auto k = p.D == 64 ? assign_kernel<u16, 64, false, CAND> : assign_kernel<u16, 128, false, CAND>;
         hipLaunchKernelGGL(k, grid, dim3(256), 0, s, (const u16*)x, p.N, rs, inv_norm, normalize, cv,
-                           mcount, labels, fs);
+                           mcount, labels, fs, tps);
     } else {
         auto k = p.D == 64 ? assign_kernel<float, 64, true, CAND> : assign_kernel<float, 128, true, CAND>;
         hipLaunchKernelGGL(k, grid, dim3(256), 0, s, (const float*)x, p.N, rs, inv_norm, normalize,
-                           cv, mcount, labels, fs);
+                           cv, mcount, labels, fs, tps);
+    }
+}
+
+// Labels of the flagged rows from their candidate lists: lane (row, c) computes
+// the exact f64 distance (index order, as the definition) to candidate c, and
+// the 16 lanes of a row take the minimum, ties to the lowest slot. Rows with no
+// or too many candidates go to the full exact scan.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void cand_exact_kernel(const T* __restrict__ X, int N,
+                                                         int normalize, RowSet rs, CentView cv,
+                                                         FlagSet fs, int32_t* __restrict__ labels) {
+    const int bh = blockIdx.y;
+    if (rs.active && !rs.active[bh]) return;
+    const int count = fs.count[bh];
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, ci = l & 15;
+    const int64_t cbase = (int64_t)bh * cv.cap + cv.base;
+    for (int base = blockIdx.x * 16; base < count; base += gridDim.x * 16) {
+        const int e = base + w * 4 + (l >> 4);
+        const bool okr = e < count;
+        const int64_t fe = (int64_t)bh * N + (okr ? e : 0);
+        const int nc = okr ? fs.ccount[fe] : 0;
+        const int r = okr ? fs.list[fe] : 0;
+        double d = INFINITY;
+        int j = 0x7fffffff;
+        if (okr && nc <= CAND_CAP && ci < nc) {
+            j = fs.cand[fe * CAND_CAP + ci];
+            const int64_t tok = rs.rows ? rs.rows[(int64_t)bh * N + r] : r;
+            d = exact_d2(row_ptr(X, N, D, bh, tok), D, normalize, cv.cent + (cbase + j) * D);
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const double od = __shfl_xor(d, o);
+            const int oj = __shfl_xor(j, o);
+            if (od < d || (od == d && oj < j)) { d = od; j = oj; }
+        }
+        if (okr && ci == 0) {
+            if (nc > CAND_CAP || nc == 0) {
+                const int pos = atomicAdd(&fs.over_count[bh], 1);
+                fs.over[(int64_t)bh * N + pos] = r;
+            } else {
+                labels[(int64_t)bh * N + r] = j;
+            }
+        }
     }
 }
 
@@ -743,9 +771,22 @@ hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* i
     if (e != hipSuccess) return e;
     if ((e = fill_i32(fs.over_count, p.BH, 0, s)) != hipSuccess) return e;
     dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)p.BH);
-    launch_assign_t<false>(p, grid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, s);
+    launch_assign_t<false>(p, grid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, 0, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    launch_assign_t<true>(p, grid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, s);
+    // candidate pass: the centre tiles of the flagged rows are split 8 per workgroup
+    constexpr int TPS = 8;
+    const int tiles = (cv.m + 63) / 64;
+    dim3 cgrid((unsigned)((p.N + 255) / 256), (unsigned)p.BH, (unsigned)((tiles + TPS - 1) / TPS));
+    launch_assign_t<true>(p, cgrid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, TPS, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const dim3 egrid(32, (unsigned)p.BH);
+    if (p.bf16) {
+        auto k = p.D == 64 ? cand_exact_kernel<u16, 64> : cand_exact_kernel<u16, 128>;
+        hipLaunchKernelGGL(k, egrid, dim3(256), 0, s, (const u16*)x, p.N, normalize, rs, cv, fs, labels);
+    } else {
+        auto k = p.D == 64 ? cand_exact_kernel<float, 64> : cand_exact_kernel<float, 128>;
+        hipLaunchKernelGGL(k, egrid, dim3(256), 0, s, (const float*)x, p.N, normalize, rs, cv, fs, labels);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return launch_refine_full(p, x, normalize, rs, cv, mcount, fs.over, fs.over_count, labels, s);
 }
@@ -863,7 +904,11 @@ hipError_t launch_stage_begin(const Prob& p, StageState st, int t, int nmax, hip
     return hipGetLastError();
 }
 
-// Euclidean distance of each clustered row to its stage centre (f64, index order).
+// Euclidean distance of each clustered row to its stage centre, in f64. Eight
+// lanes share a row: each sums the squared differences of its chunks of 8
+// dimensions in index order, and the eight partial sums are combined in a
+// fixed tree, so the result is deterministic (it differs from an index-order
+// sum only by f64 rounding).
 template <typename T>
 __global__ __launch_bounds__(256) void stage_dist_kernel(const T* __restrict__ x, int N, int D,
                                                          RowSet rs, const int32_t* __restrict__ labels,
@@ -872,22 +917,36 @@ __global__ __launch_bounds__(256) void stage_dist_kernel(const T* __restrict__ x
     const int bh = blockIdx.y;
     if (rs.active && !rs.active[bh]) return;
     const int n = rs.nrows ? rs.nrows[bh] : N;
-    const int r = blockIdx.x * blockDim.x + threadIdx.x;
-    if (r >= n) return;
-    const int64_t tok = rs.rows ? rs.rows[(int64_t)bh * N + r] : r;
-    const T* xr = row_ptr(x, N, D, bh, tok);
-    const float* c = cv.cent + ((int64_t)bh * cv.cap + cv.base + labels[(int64_t)bh * N + r]) * D;
+    const int sub = threadIdx.x & 7;
+    const int r = blockIdx.x * 32 + (threadIdx.x >> 3);
+    const bool ok = r < n;
     double s = 0.0;
-    for (int d = 0; d < D; ++d) {
-        double df = (double)elem<T>::load(xr, d) - (double)c[d];
-        s += df * df;
+    if (ok) {
+        const int64_t tok = rs.rows ? rs.rows[(int64_t)bh * N + r] : r;
+        const T* xr = row_ptr(x, N, D, bh, tok);
+        const float* c = cv.cent + ((int64_t)bh * cv.cap + cv.base + labels[(int64_t)bh * N + r]) * D;
+        for (int d0 = sub * 8; d0 < D; d0 += 64) {
+            float xv[8];
+            load8<T>(xr + d0, xv);
+            const float4 c0 = *reinterpret_cast<const float4*>(c + d0);
+            const float4 c1 = *reinterpret_cast<const float4*>(c + d0 + 4);
+            const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const double df = (double)xv[i] - (double)cc[i];
+                s += df * df;
+            }
+        }
     }
-    dist[(int64_t)bh * N + r] = sqrt(s);
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    if (ok && sub == 0) dist[(int64_t)bh * N + r] = sqrt(s);
 }
 
 hipError_t launch_stage_dist(const Prob& p, const void* k, RowSet rs, const int32_t* labels,
                              CentView cv, double* dist, hipStream_t s) {
-    dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)p.BH);
+    dim3 grid((unsigned)((p.N + 31) / 32), (unsigned)p.BH);
     if (p.bf16)
         hipLaunchKernelGGL(stage_dist_kernel<u16>, grid, dim3(256), 0, s, (const u16*)k, p.N, p.D,
                            rs, labels, cv, dist);
