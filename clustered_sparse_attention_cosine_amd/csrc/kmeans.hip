@@ -792,14 +792,21 @@ hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* i
 }
 
 // ------------------------------------------------------------------ update
-// Each wave walks 64 consecutive rows with one lane per dimension, folding
-// runs of equal labels in registers before one atomic add per run.
+// Each wave takes 64 consecutive rows: it stages them in LDS (RS rows at a
+// time) with coalesced 16-byte loads, all in flight at once, then walks them
+// with one lane per dimension, folding runs of equal labels in registers
+// before one atomic add per run and dimension.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__ X, int N, RowSet rs,
                                                            const float* __restrict__ inv_norm,
                                                            const int32_t* __restrict__ labels,
                                                            CentView cv) {
     constexpr int E = D / 64;
+    constexpr int RS = D == 64 ? 64 : 32;          // rows staged at once
+    constexpr int LDX = D + 16 / (int)sizeof(T);   // padded row stride (elements)
+    constexpr int CPR = D / 8;                     // 8-element chunks per row
+    constexpr int RPI = 64 / CPR;                  // rows per wave instruction
+    __shared__ __attribute__((aligned(16))) T xs[4][RS * LDX];
     const int bh = blockIdx.y;
     if (rs.active && !rs.active[bh]) return;
     const int n = rs.nrows ? rs.nrows[bh] : N;
@@ -813,29 +820,48 @@ __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__
     const float s_l = (inv_norm && okr) ? inv_norm[(int64_t)bh * N + tok_l] : 1.0f;
     const int rows_here = min(64, n - base);
     const int64_t cbase = (int64_t)bh * cv.cap + cv.base;
+    T* xw = xs[w];
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0f;
     int cur = -1, run = 0;
-    for (int q = 0; q < rows_here; ++q) {
-        const int lab = __shfl(lab_l, q);
-        const int tok = __shfl(tok_l, q);
-        const float s = __shfl(s_l, q);
-        if (lab != cur) {
-            if (cur >= 0) {
+    for (int h0 = 0; h0 < rows_here; h0 += RS) {
+        // chunk c of row q goes to lane (q % RPI) * CPR + c; rows past the end read row 0
 #pragma unroll
-                for (int e = 0; e < E; ++e) atomicAdd(&cv.sums[(cbase + cur) * D + l + 64 * e], acc[e]);
-                if (l == 0) atomicAdd(&cv.cnt[cbase + cur], run);
-            }
-            cur = lab;
-            run = 0;
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+        for (int it = 0; it < RS / RPI; ++it) {
+            const int q = it * RPI + l / CPR, c = l % CPR;
+            const int tok = __shfl(tok_l, h0 + q);
+            const T* src = row_ptr(X, N, D, bh, tok) + c * 8;
+            *reinterpret_cast<u32x4*>(&xw[q * LDX + c * 8]) = *reinterpret_cast<const u32x4*>(src);
+            if constexpr (sizeof(T) == 4)
+                *reinterpret_cast<u32x4*>(&xw[q * LDX + c * 8 + 4]) = *reinterpret_cast<const u32x4*>(src + 4);
         }
-        const T* xp = row_ptr(X, N, D, bh, tok);
+        // lanes read rows other lanes wrote
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int qend = min(RS, rows_here - h0);
+        for (int q = 0; q < qend; ++q) {
+            const int lab = __builtin_amdgcn_readlane(lab_l, h0 + q);
+            const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_l), h0 + q));
+            if (lab != cur) {
+                if (cur >= 0) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] += s * elem<T>::load(xp, l + 64 * e);
-        run++;
+                    for (int e = 0; e < E; ++e) atomicAdd(&cv.sums[(cbase + cur) * D + l + 64 * e], acc[e]);
+                    if (l == 0) atomicAdd(&cv.cnt[cbase + cur], run);
+                }
+                cur = lab;
+                run = 0;
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] += s * elem<T>::load(xw, q * LDX + l + 64 * e);
+            run++;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     if (cur >= 0) {
 #pragma unroll

@@ -126,7 +126,12 @@ hipError_t launch_stable_rank(const Prob& p, const int32_t* labels, int M, const
     return hipGetLastError();
 }
 
-// One wave per cluster walks its members in permuted order.
+// One wave per cluster walks its members in permuted order, RS rows at a
+// time: the rows are copied to x_perm / v_perm and staged in LDS with
+// coalesced 16-byte accesses (all loads of a batch in flight at once); lane q
+// then takes the norm of staged row q (f64, index order) when the rows are
+// normalized, and the statistics are accumulated with one lane per dimension
+// in member order (f64 sums, as the definition).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void gather_stats_kernel(int N, int M,
                                                            const int32_t* __restrict__ offsets,
@@ -138,57 +143,91 @@ __global__ __launch_bounds__(256) void gather_stats_kernel(int N, int M,
                                                            T* __restrict__ xmax, T* __restrict__ xmin,
                                                            T* __restrict__ x_perm,
                                                            T* __restrict__ v_perm) {
+#pragma clang fp contract(off)
     constexpr int E = D / 64;
+    constexpr int RS = D == 64 ? 64 : 32;          // rows staged at once
+    constexpr int LDX = D + 16 / (int)sizeof(T);   // padded row stride (elements)
+    constexpr int CPR = D / 8;                     // 8-element chunks per row
+    constexpr int RPI = 64 / CPR;                  // rows per wave instruction
+    constexpr int W8 = 8 * (int)sizeof(T) / 16;    // 16-byte words per chunk
+    __shared__ __attribute__((aligned(16))) T xs[4][RS * LDX];
     const int bh = blockIdx.y;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int j = blockIdx.x * 4 + w;
     if (j >= M) return;
     const int32_t* off = offsets + (int64_t)bh * (M + 1);
     const int beg = off[j], end = off[j + 1];
+    T* xw = xs[w];
     double sum[E], rsum[E];
     float mx[E], mn[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) { sum[e] = 0.0; rsum[e] = 0.0; mx[e] = -INFINITY; mn[e] = INFINITY; }
-    for (int r = beg; r < end; ++r) {
-        const int64_t tok = perm[(int64_t)bh * N + r];
-        const T* xr = x + ((int64_t)bh * N + tok) * D;
-        T raw[E];
-        float val[E];
-        double ss = 0.0;
+    for (int h0 = beg; h0 < end; h0 += RS) {
+        const int nb = min(RS, end - h0);
+        const int tok_l = perm[(int64_t)bh * N + h0 + min(l, nb - 1)];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            raw[e] = xr[l + 64 * e];
-            val[e] = elem<T>::load(raw, e);
-            ss += (double)val[e] * (double)val[e];
+        for (int it = 0; it < RS / RPI; ++it) {
+            const int q = it * RPI + l / CPR, c = l % CPR;
+            const int64_t tok = __shfl(tok_l, q);
+            const int64_t src = ((int64_t)bh * N + tok) * D + c * 8;
+            const int64_t dst = ((int64_t)bh * N + h0 + q) * D + c * 8;
+            u32x4 xv[W8];
+#pragma unroll
+            for (int k = 0; k < W8; ++k) xv[k] = *reinterpret_cast<const u32x4*>(x + src + k * (16 / (int)sizeof(T)));
+#pragma unroll
+            for (int k = 0; k < W8; ++k) *reinterpret_cast<u32x4*>(&xw[q * LDX + c * 8 + k * (16 / (int)sizeof(T))]) = xv[k];
+            if (q < nb) {
+                if (x_perm) {
+#pragma unroll
+                    for (int k = 0; k < W8; ++k)
+                        *reinterpret_cast<u32x4*>(x_perm + dst + k * (16 / (int)sizeof(T))) = xv[k];
+                }
+                if (v_perm) {
+#pragma unroll
+                    for (int k = 0; k < W8; ++k)
+                        *reinterpret_cast<u32x4*>(v_perm + dst + k * (16 / (int)sizeof(T))) =
+                            *reinterpret_cast<const u32x4*>(v + src + k * (16 / (int)sizeof(T)));
+                }
+            }
         }
-        if (normalize) {
-            ss = wave_sum_d(ss);
-            double nrm = sqrt(ss);
-            if (nrm < 1e-12) nrm = 1e-12;
+        // lanes read rows other lanes wrote
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        double nrm_l = 1.0;
+        if (normalize && l < nb) {
+            double ss = 0.0;
+            for (int d = 0; d < D; ++d) {
+                const double vv = (double)elem<T>::load(xw, l * LDX + d);
+                ss += vv * vv;
+            }
+            nrm_l = sqrt(ss);
+            if (nrm_l < 1e-12) nrm_l = 1e-12;
+        }
+        for (int q = 0; q < nb; ++q) {
+            float val[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) val[e] = elem<T>::load(xw, q * LDX + l + 64 * e);
+            if (normalize) {
+                const double nrm = __shfl(nrm_l, q);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    sum[e] += (double)(float)((double)val[e] / nrm);
+                    rsum[e] += (double)val[e];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) sum[e] += (double)val[e];
+            }
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                sum[e] += (double)(float)((double)val[e] / nrm);
-                rsum[e] += (double)val[e];
+                mx[e] = fmaxf(mx[e], val[e]);
+                mn[e] = fminf(mn[e], val[e]);
             }
-        } else {
-#pragma unroll
-            for (int e = 0; e < E; ++e) sum[e] += (double)val[e];
         }
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            mx[e] = fmaxf(mx[e], val[e]);
-            mn[e] = fminf(mn[e], val[e]);
-        }
-        if (x_perm) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) x_perm[((int64_t)bh * N + r) * D + l + 64 * e] = raw[e];
-        }
-        if (v_perm) {
-            const T* vr = v + ((int64_t)bh * N + tok) * D;
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                v_perm[((int64_t)bh * N + r) * D + l + 64 * e] = vr[l + 64 * e];
-        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     const int cnt = end - beg;
     const int64_t slot = ((int64_t)bh * M + j) * D;
