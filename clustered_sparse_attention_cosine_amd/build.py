@@ -22,7 +22,8 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include")]
 # MFMA results in VGPRs (no accumulation-register copies before the epilogue VALU work)
-EXTRA = {"kmeans.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# attention: no NaN canonicalization around max (inputs are finite; -inf masks stay exact)
+EXTRA = {"kmeans.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "attn.hip": ["-fno-honor-nans"]}
 
 
 def build(verbose: bool = False) -> str:
