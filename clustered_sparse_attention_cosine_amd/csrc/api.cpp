@@ -100,6 +100,7 @@ struct KmeansWs {
     double* d2 = nullptr;
     uint8_t* chosen = nullptr;
     int32_t* hist = nullptr;
+    int32_t* m_eff = nullptr;
 };
 
 void plan_kmeans(Carver& c, const Prob& p, int cap, bool want_inv, bool kpp, bool want_xhat,
@@ -121,6 +122,7 @@ void plan_kmeans(Carver& c, const Prob& p, int cap, bool want_inv, bool kpp, boo
     w.sums = c.take<float>(bhc * p.D);
     w.cnt = c.take<int32_t>(bhc);
     w.hist = c.take<int32_t>(bhc);
+    w.m_eff = c.take<int32_t>(p.BH);
     if (kpp) {
         if (want_xhat) w.xhat = c.take<float>(bhn * p.D);
         w.d2 = c.take<double>(bhn);
@@ -377,7 +379,10 @@ int32_t adacluster_cluster_k(const adc_shape* shape, const adc_k_params* prm, co
         // final assignment over every slot that holds a centre (Algorithm 1 step 20)
         CentView cvf = make_view(centroids, w, nmax, 0, nmax);
         HIPCHK(launch_finalize(p, cvf, nullptr, 0, s));
-        HIPCHK(launch_assign(p, k, all, nullptr, 0, cvf, n_clusters, assign, flags_of(w), s));
+        // slots after the last one holding a centre (the unfilled end of the last
+        // stage) are left out of the contraction
+        HIPCHK(launch_last_valid(p, cvf, n_clusters, w.m_eff, s));
+        HIPCHK(launch_assign(p, k, all, nullptr, 0, cvf, w.m_eff, assign, flags_of(w), s));
     }
     HIPCHK(launch_histogram(p, assign, nmax, w.hist, s));
     HIPCHK(launch_scan_offsets(p, w.hist, nmax, sizes, offsets, s));

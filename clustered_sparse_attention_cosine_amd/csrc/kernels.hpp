@@ -80,6 +80,8 @@ constexpr int CAND_CAP = 16;
 // Nearest centre by a bf16 hi/lo matrix-core contraction with a certified
 // error bound; uncertain rows are settled by exact f64 distances of the
 // centres inside their uncertainty band (labels are final on return).
+hipError_t launch_last_valid(const Prob& p, CentView cv, const int32_t* mcount, int32_t* m_eff,
+                             hipStream_t s);
 hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
                          int normalize, CentView cv, const int32_t* mcount, int32_t* labels,
                          FlagSet fs, hipStream_t s);

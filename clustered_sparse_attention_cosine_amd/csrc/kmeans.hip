@@ -76,6 +76,31 @@ hipError_t launch_fixed_info(int BH, int N, int m, int32_t* n_clusters, uint8_t*
     return hipGetLastError();
 }
 
+// Slots past the last one holding a centre cannot win an assignment: m_eff =
+// min(mcount, last valid slot + 1), one workgroup per head.
+__global__ __launch_bounds__(256) void last_valid_kernel(int cap, int m, const uint8_t* __restrict__ valid,
+                                                         const int32_t* __restrict__ mcount,
+                                                         int32_t* __restrict__ m_eff) {
+    __shared__ int red[4];
+    const int bh = blockIdx.x;
+    const int lim = mcount ? min(mcount[bh], m) : m;
+    int last = -1;
+    for (int j = threadIdx.x; j < lim; j += 256)
+        if (valid[(int64_t)bh * cap + j]) last = j;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = last;
+    __syncthreads();
+    if (threadIdx.x == 0) m_eff[bh] = max(max(red[0], red[1]), max(red[2], red[3])) + 1;
+}
+
+hipError_t launch_last_valid(const Prob& p, CentView cv, const int32_t* mcount, int32_t* m_eff,
+                             hipStream_t s) {
+    hipLaunchKernelGGL(last_valid_kernel, dim3((unsigned)p.BH), dim3(256), 0, s, cv.cap, cv.m,
+                       cv.valid + cv.base, mcount, m_eff);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ norms
 template <typename T>
 __global__ __launch_bounds__(256) void inv_norm_kernel(const T* __restrict__ x, int64_t rows,
