@@ -312,10 +312,10 @@ __device__ __forceinline__ uint4 v_frag(const u16* p) {
     return make_uint4(xu.x, xu.y, yu.x, yu.y);
 }
 
-// Online-softmax update of one 16-query block over one 64-key tile (the lane
-// holds query c16 and keys kb*16 + 4g + i). Scores come in raw; sl2 = scale *
-// log2(e) is applied inside the exponent. MASK: the tile runs past the last
-// selected key (positions >= total get probability 0).
+// Online softmax of one 16-query block over NKB 16-key blocks of a tile (the
+// lane holds query c16 and keys (kb0 + kb)*16 + 4g + i). Scores come in raw;
+// sl2 = scale * log2(e) is applied inside the exponent. MASK: the tile runs
+// past the last selected key (positions >= total get probability 0).
 //
 // The running maximum m (log2 units) is raised only when some row of the wave
 // sees a score above m + 8; otherwise the stale m is kept, so every
@@ -324,24 +324,26 @@ __device__ __forceinline__ uint4 v_frag(const u16* p) {
 // denominator share the factor 2^-m whatever m is. The row sums are
 // accumulated by the matrix cores (a block of ones in the P.V product), so
 // they are part of o and rescaled with it.
-template <int DB, bool MASK>
-__device__ __forceinline__ void softmax_block(f32x4 (&sc)[4], float sl2, int t0, int g, int total,
+template <int DB, int NKB, bool MASK>
+__device__ __forceinline__ void softmax_block(f32x4 (&sc)[NKB], float sl2, int p0, int g, int total,
                                               float& m_run, f32x4 (&o)[DB + 1]) {
     if constexpr (MASK) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (t0 + kb * 16 + g * 4 + i >= total) sc[kb][i] = -INFINITY;
+                if (p0 + kb * 16 + g * 4 + i >= total) sc[kb][i] = -INFINITY;
     }
     float mx = fmaxf(fmaxf(sc[0][0], sc[0][1]), sc[0][2]);
     mx = fmaxf(fmaxf(mx, sc[0][3]), sc[1][0]);
     mx = fmaxf(fmaxf(mx, sc[1][1]), sc[1][2]);
-    mx = fmaxf(fmaxf(mx, sc[1][3]), sc[2][0]);
-    mx = fmaxf(fmaxf(mx, sc[2][1]), sc[2][2]);
-    mx = fmaxf(fmaxf(mx, sc[2][3]), sc[3][0]);
-    mx = fmaxf(fmaxf(mx, sc[3][1]), sc[3][2]);
-    mx = fmaxf(mx, sc[3][3]);
+    mx = fmaxf(mx, sc[1][3]);
+    if constexpr (NKB == 4) {
+        mx = fmaxf(fmaxf(mx, sc[2][0]), sc[2][1]);
+        mx = fmaxf(fmaxf(mx, sc[2][2]), sc[2][3]);
+        mx = fmaxf(fmaxf(mx, sc[3][0]), sc[3][1]);
+        mx = fmaxf(fmaxf(mx, sc[3][2]), sc[3][3]);
+    }
     const float ms = col_max4(mx) * sl2;
     if (__ballot(ms > m_run + 8.0f) != 0) {
         const float m_new = fmaxf(m_run, ms);
@@ -352,21 +354,23 @@ __device__ __forceinline__ void softmax_block(f32x4 (&sc)[4], float sl2, int t0,
     }
     const float nb = (m_run == -INFINITY) ? 0.0f : -m_run;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc[kb][i] = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], sl2, nb));
 }
 
-// A work item is (head, q-cluster, chunk of ATTN_ROWS query rows); the NT/64
-// waves each own RB blocks of 16 rows (a block with no rows is skipped). K/V
-// tiles of 64 keys are double-buffered in LDS; the global loads of tiles t+1
-// and t+2 are in flight in registers while tile t is computed, and the last
-// wave looks up the key rows of tile t+3 meanwhile, so one barrier per tile
-// suffices. Operands are 16-bit planes (NP = 1: K bf16, V fp16; NP = 2: bf16
-// hi and lo of f32 data, every product of order <= 1 accumulated, three
+// A work item is (head, q-cluster, chunk of ATTN_ROWS = 128 query rows); wave
+// w of the eight owns rows 16w..16w+15 (a wave past the item's rows only
+// helps with the tile staging and the run lookups).
+//
+// K/V tiles of 64 keys are double-buffered in LDS; the global loads of tiles
+// t+1 and t+2 are in flight in registers while tile t is computed, and the
+// last wave looks up the key rows of tile t+3 meanwhile, so one barrier per
+// tile suffices. Operands are 16-bit planes (NP = 1: K bf16, V fp16; NP = 2:
+// bf16 hi and lo of f32 data, every product of order <= 1 accumulated, three
 // MFMAs per product, near f32 accuracy).
-template <typename T, int D, typename TO, int NT, int RB, int WPE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE, 8)))
+template <typename T, int D, typename TO, int WPE>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, 8)))
 void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restrict__ q_perm,
                  const int32_t* __restrict__ q_off, const u16* __restrict__ K0,
                  const u16* __restrict__ K1, const u16* __restrict__ V0,
@@ -375,7 +379,8 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
                  int run_cap, const int32_t* __restrict__ items,
                  const int32_t* __restrict__ head_pos, int BH, int cap, float sl2,
                  TO* __restrict__ O, float* __restrict__ lse) {
-    static_assert((NT / 64) * RB * 16 == ATTN_ROWS, "waves x blocks must cover a work item");
+    constexpr int NT = 512;
+    static_assert((NT / 64) * 16 == ATTN_ROWS, "eight waves of 16 rows cover a work item");
     constexpr bool PREC = sizeof(T) == 4;
     constexpr int NP = PREC ? 2 : 1;  // operand planes
     constexpr int KC = D / 32;        // 32-wide chunks of the head dimension
@@ -385,7 +390,7 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
     __shared__ __attribute__((aligned(16))) u16 Vs[2][NP][64 * LDK];
     __shared__ int krow[4][64];
     // the work item's runs (first key row, first position) when they fit
-    constexpr int RL = 2048;
+    constexpr int RL = 512;
     __shared__ int run_s[RL], run_p[RL + 1];
 
     // Work item order: workgroup b runs on XCD b % 8 (round-robin dispatch), so
@@ -413,24 +418,20 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
     const int32_t* qo = q_off + (int64_t)bh * (Cq + 1);
     const int row0 = __builtin_amdgcn_readfirstlane(qo[a]) + ch * ATTN_ROWS;
     const int nrows = min(ATTN_ROWS, __builtin_amdgcn_readfirstlane(qo[a + 1]) - row0);
-    bool live[RB];
-    bf16x8 qf[RB][NP][KC];
-    int64_t qtok[RB];
-    bool qok[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        live[rb] = (w * RB + rb) * 16 < nrows;
-        const int rowi = (w * RB + rb) * 16 + c16;
-        qok[rb] = rowi < nrows;
-        qtok[rb] = qok[rb] ? q_perm[(int64_t)bh * N + row0 + rowi] : 0;
-        const T* qr = Q + ((int64_t)bh * N + qtok[rb]) * D;
+    const bool live = w * 16 < nrows;
+    const int rowi = w * 16 + c16;
+    const bool qok = rowi < nrows;
+    const int64_t qtok = qok ? q_perm[(int64_t)bh * N + row0 + rowi] : 0;
+    bf16x8 qf[NP][KC];
+    {
+        const T* qr = Q + ((int64_t)bh * N + qtok) * D;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
             uint32_t hv[4], lv[4];
-            load_row8_split<T>(qr + kc * 32 + g * 8, qok[rb], hv, lv);
-            qf[rb][0][kc] = __builtin_bit_cast(bf16x8, make_uint4(hv[0], hv[1], hv[2], hv[3]));
+            load_row8_split<T>(qr + kc * 32 + g * 8, qok, hv, lv);
+            qf[0][kc] = __builtin_bit_cast(bf16x8, make_uint4(hv[0], hv[1], hv[2], hv[3]));
             if constexpr (PREC)
-                qf[rb][NP - 1][kc] = __builtin_bit_cast(bf16x8, make_uint4(lv[0], lv[1], lv[2], lv[3]));
+                qf[NP - 1][kc] = __builtin_bit_cast(bf16x8, make_uint4(lv[0], lv[1], lv[2], lv[3]));
         }
     }
 
@@ -446,14 +447,10 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
     const u16* const Kh1 = PREC ? K1 + hoff : Kh0;
     const u16* const Vh1 = PREC ? V1 + hoff : Vh0;
 
-    float m_run[RB];
-    f32x4 o[RB][DB + 1];  // O^T blocks and the row-sum block
+    float m_run = -INFINITY;
+    f32x4 o[DB + 1];  // O^T blocks and the row-sum block
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        m_run[rb] = -INFINITY;
-#pragma unroll
-        for (int db = 0; db <= DB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int db = 0; db <= DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     // per-lane LDS offset of the transposed V reads (key row 4g + j, column 4a)
     const int vlane = (4 * g + ((l & 15) >> 2)) * LDK + 4 * (l & 3);
 
@@ -482,6 +479,72 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
     tile_store<D, NP, NT, LDK>(tr0, tid, Ks[0], Vs[0]);
     __syncthreads();
 
+    // Scores, softmax and P.V of NKB 16-key blocks starting at block kb0 of the
+    // tile in buffer b.
+    auto compute = [&](int b, int p0, int kb0, auto nkb_c, auto mask_c) __attribute__((always_inline)) {
+        constexpr int NKB = decltype(nkb_c)::value;
+        constexpr bool MASK = decltype(mask_c)::value;
+        f32x4 sc[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const int off = ((kb0 + kb) * 16 + c16) * LDK + kc * 32 + g * 8;
+                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[b][0][off]);
+                if constexpr (PREC) {
+                    const bf16x8 kl = *reinterpret_cast<const bf16x8*>(&Ks[b][NP - 1][off]);
+                    sc[kb] = mfma16(kl, qf[0][kc], sc[kb]);
+                    sc[kb] = mfma16(ka, qf[NP - 1][kc], sc[kb]);
+                }
+                sc[kb] = mfma16(ka, qf[0][kc], sc[kb]);
+            }
+        }
+        softmax_block<DB, NKB, MASK>(sc, sl2, p0, g, total, m_run, o);
+#pragma unroll
+        for (int h = 0; h < NKB / 2; ++h) {
+            const int kc2 = kb0 / 2 + h;
+            const u16* vb0 = &Vs[b][0][vlane + kc2 * 32 * LDK];
+            if constexpr (PREC) {
+                const u16* vb1 = &Vs[b][NP - 1][vlane + kc2 * 32 * LDK];
+                const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u,
+                                                                          0x3F803F80u, 0x3F803F80u));
+                bf16x8 pb, pl;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pb[j] = f2bf(sc[2 * h][j]);
+                    pb[4 + j] = f2bf(sc[2 * h + 1][j]);
+                    pl[j] = f2bf(sc[2 * h][j] - bf2f(pb[j]));
+                    pl[4 + j] = f2bf(sc[2 * h + 1][j] - bf2f(pb[4 + j]));
+                }
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const bf16x8 va = __builtin_bit_cast(bf16x8, v_frag<LDK>(vb0 + db * 16));
+                    const bf16x8 vl = __builtin_bit_cast(bf16x8, v_frag<LDK>(vb1 + db * 16));
+                    o[db] = mfma16(vl, pb, o[db]);
+                    o[db] = mfma16(va, pl, o[db]);
+                    o[db] = mfma16(va, pb, o[db]);
+                }
+                o[DB] = mfma16(ones, pl, o[DB]);
+                o[DB] = mfma16(ones, pb, o[DB]);
+            } else {
+                // P.V in fp16 (11-bit significand): probabilities lose at most 2^-12
+                const f16x8 ones = __builtin_bit_cast(f16x8, make_uint4(0x3C003C00u, 0x3C003C00u,
+                                                                        0x3C003C00u, 0x3C003C00u));
+                const f16x8 ph = __builtin_bit_cast(
+                    f16x8, make_uint4(pack_h2(sc[2 * h][0], sc[2 * h][1]), pack_h2(sc[2 * h][2], sc[2 * h][3]),
+                                      pack_h2(sc[2 * h + 1][0], sc[2 * h + 1][1]),
+                                      pack_h2(sc[2 * h + 1][2], sc[2 * h + 1][3])));
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const f16x8 vh = __builtin_bit_cast(f16x8, v_frag<LDK>(vb0 + db * 16));
+                    o[db] = mfma16h(vh, ph, o[db]);
+                }
+                o[DB] = mfma16h(ones, ph, o[DB]);
+            }
+        }
+    };
+
     // one tile: look up t+3 (last wave), prefetch t+2 into the register set tile t
     // used, compute t, store t+1 into the other LDS buffer. Every wave issues
     // the same tile loads every step (tiles past the end read clamped, valid
@@ -491,102 +554,9 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
         const int t0 = t * 64;
         if (w == LW) lookup(t + 3);
         tile_load<D, NP, NT>(tr_mine, tid, krow[(t + 2) & 3], Kh0, Kh1, Vh0, Vh1);
-        auto compute = [&](auto mask_c) __attribute__((always_inline)) {
-            constexpr bool MASK = decltype(mask_c)::value;
-            f32x4 sc[RB][4];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) sc[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-                    const int off = (kb * 16 + c16) * LDK + kc * 32 + g * 8;
-                    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[b][0][off]);
-                    bf16x8 kl;
-                    if constexpr (PREC) kl = *reinterpret_cast<const bf16x8*>(&Ks[b][NP - 1][off]);
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) {
-                        if (rb > 0 && !live[rb]) continue;
-                        if constexpr (PREC) {
-                            sc[rb][kb] = mfma16(kl, qf[rb][0][kc], sc[rb][kb]);
-                            sc[rb][kb] = mfma16(ka, qf[rb][NP - 1][kc], sc[rb][kb]);
-                        }
-                        sc[rb][kb] = mfma16(ka, qf[rb][0][kc], sc[rb][kb]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                if (rb > 0 && !live[rb]) continue;
-                softmax_block<DB, MASK>(sc[rb], sl2, t0, g, total, m_run[rb], o[rb]);
-            }
-#pragma unroll
-            for (int kc2 = 0; kc2 < 2; ++kc2) {
-                const u16* vb0 = &Vs[b][0][vlane + kc2 * 32 * LDK];
-                if constexpr (PREC) {
-                    const u16* vb1 = &Vs[b][NP - 1][vlane + kc2 * 32 * LDK];
-                    const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u,
-                                                                              0x3F803F80u, 0x3F803F80u));
-                    bf16x8 pb[RB], pl[RB];
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            pb[rb][j] = f2bf(sc[rb][2 * kc2][j]);
-                            pb[rb][4 + j] = f2bf(sc[rb][2 * kc2 + 1][j]);
-                            pl[rb][j] = f2bf(sc[rb][2 * kc2][j] - bf2f(pb[rb][j]));
-                            pl[rb][4 + j] = f2bf(sc[rb][2 * kc2 + 1][j] - bf2f(pb[rb][4 + j]));
-                        }
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const bf16x8 va = __builtin_bit_cast(bf16x8, v_frag<LDK>(vb0 + db * 16));
-                        const bf16x8 vl = __builtin_bit_cast(bf16x8, v_frag<LDK>(vb1 + db * 16));
-#pragma unroll
-                        for (int rb = 0; rb < RB; ++rb) {
-                            if (rb > 0 && !live[rb]) continue;
-                            o[rb][db] = mfma16(vl, pb[rb], o[rb][db]);
-                            o[rb][db] = mfma16(va, pl[rb], o[rb][db]);
-                            o[rb][db] = mfma16(va, pb[rb], o[rb][db]);
-                        }
-                    }
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) {
-                        if (rb > 0 && !live[rb]) continue;
-                        o[rb][DB] = mfma16(ones, pl[rb], o[rb][DB]);
-                        o[rb][DB] = mfma16(ones, pb[rb], o[rb][DB]);
-                    }
-                } else {
-                    // P.V in fp16 (11-bit significand): probabilities lose at most 2^-12
-                    const f16x8 ones = __builtin_bit_cast(f16x8, make_uint4(0x3C003C00u, 0x3C003C00u,
-                                                                            0x3C003C00u, 0x3C003C00u));
-                    f16x8 ph[RB];
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-                        ph[rb] = __builtin_bit_cast(
-                            f16x8, make_uint4(pack_h2(sc[rb][2 * kc2][0], sc[rb][2 * kc2][1]),
-                                              pack_h2(sc[rb][2 * kc2][2], sc[rb][2 * kc2][3]),
-                                              pack_h2(sc[rb][2 * kc2 + 1][0], sc[rb][2 * kc2 + 1][1]),
-                                              pack_h2(sc[rb][2 * kc2 + 1][2], sc[rb][2 * kc2 + 1][3])));
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const f16x8 vh = __builtin_bit_cast(f16x8, v_frag<LDK>(vb0 + db * 16));
-#pragma unroll
-                        for (int rb = 0; rb < RB; ++rb) {
-                            if (rb > 0 && !live[rb]) continue;
-                            o[rb][db] = mfma16h(vh, ph[rb], o[rb][db]);
-                        }
-                    }
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) {
-                        if (rb > 0 && !live[rb]) continue;
-                        o[rb][DB] = mfma16h(ones, ph[rb], o[rb][DB]);
-                    }
-                }
-            }
-        };
-        if (t < ntiles && live[0]) {
-            if (t0 + 64 > total) compute(std::true_type{});
-            else compute(std::false_type{});
+        if (t < ntiles && live) {
+            if (t0 + 64 > total) compute(b, t0, 0, std::integral_constant<int, 4>{}, std::true_type{});
+            else compute(b, t0, 0, std::integral_constant<int, 4>{}, std::false_type{});
         }
         tile_store<D, NP, NT, LDK>(tr_next, tid, Ks[b ^ 1], Vs[b ^ 1]);
         __syncthreads();
@@ -596,30 +566,20 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
         step(t + 1, tr1, tr0);
     }
 
+    if (qok) {
+        const float l_tot = o[DB][0];  // every row of the ones block holds the sum
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        TO* orow = O + ((int64_t)bh * N + qtok) * D;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const float l_tot = o[rb][DB][0];  // every row of the ones block holds the sum
-        if (qok[rb]) {
-            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-            TO* orow = O + ((int64_t)bh * N + qtok[rb]) * D;
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    elem<TO>::store(orow, db * 16 + g * 4 + i, o[rb][db][i] * inv);
-            if (g == 0 && lse)
-                lse[(int64_t)bh * N + qtok[rb]] =
-                    l_tot > 0.0f ? (m_run[rb] + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-        }
+            for (int i = 0; i < 4; ++i) elem<TO>::store(orow, db * 16 + g * 4 + i, o[db][i] * inv);
+        if (g == 0 && lse)
+            lse[(int64_t)bh * N + qtok] =
+                l_tot > 0.0f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
     }
 }
 
-// Threads per workgroup and 16-row blocks per wave of the attention kernel.
-#ifndef ADC_ATTN_NT
-#define ADC_ATTN_NT 512
-#endif
-constexpr int ATTN_NT = ADC_ATTN_NT;
-constexpr int ATTN_RB = ATTN_ROWS / 16 / (ATTN_NT / 64);
 #ifndef ADC_ATTN_WPE64
 #define ADC_ATTN_WPE64 4
 #endif
@@ -634,9 +594,8 @@ static void launch_attn_t(const Prob& p, dim3 grid, int Cq, const void* q, const
                           hipStream_t s) {
     // waves per SIMD: two workgroups per CU where the registers allow it
     constexpr int W64 = sizeof(T) == 2 ? ATTN_WPE64 : 2;
-    auto k = p.D == 64 ? attn_kernel<T, 64, TO, ATTN_NT, ATTN_RB, W64>
-                       : attn_kernel<T, 128, TO, ATTN_NT, ATTN_RB, 2>;
-    hipLaunchKernelGGL(k, grid, dim3(ATTN_NT), 0, s, p.N, Cq, (const T*)q, q_perm, q_offsets, k0, k1,
+    auto k = p.D == 64 ? attn_kernel<T, 64, TO, W64> : attn_kernel<T, 128, TO, 2>;
+    hipLaunchKernelGGL(k, grid, dim3(512), 0, s, p.N, Cq, (const T*)q, q_perm, q_offsets, k0, k1,
                        v0, v1, run_start, run_pos, n_runs, run_cap, items, head_pos, p.BH, cap, sl2,
                        (TO*)out, lse);
 }

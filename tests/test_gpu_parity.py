@@ -72,7 +72,7 @@ def test_sparse_attn_matches_oracle(case):
         assert np.abs(lse[0, h] - refs[h]["lse"]).max() <= 1e-2
 
 
-@pytest.mark.parametrize("D,dtype", [(64, "bf16"), (128, "bf16"), (64, "f32")])
+@pytest.mark.parametrize("D,dtype", [(64, "bf16"), (128, "bf16"), (64, "f32"), (128, "f32")])
 def test_select_all_equals_dense(D, dtype):
     # one q-cluster and one key slot holding every token: dense attention,
     # compared with a float64 softmax on the host
