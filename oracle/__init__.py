@@ -78,6 +78,8 @@ def lib():
             "orc_select_topk": (None, [f64p, i32, i32, i32p, i32, i32, u32p, i32p]),
             "orc_sparse_attn": (None, [f32p, f32p, f32p, i64, i32, i32p, i32p, i32, i32, u32p,
                                        f64, f32p, f32p]),
+            "orc_sparse_attn_q": (None, [f32p, i64, i32p, f32p, f32p, i64, i32, i32p, i32, i32,
+                                         u32p, f64, f32p, f32p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -312,6 +314,24 @@ def sparse_attn(q, k, v, qlab, klab, cq, ck, mask, scale):
                           _ptr(v, ctypes.c_float), n, d, _ptr(qlab, ctypes.c_int32),
                           _ptr(klab, ctypes.c_int32), cq, ck, _ptr(mask, ctypes.c_uint32),
                           float(scale), _ptr(out, ctypes.c_float), _ptr(lse, ctypes.c_float))
+    return out, lse
+
+
+def sparse_attn_rows(q_rows, qlab_rows, k, v, klab, cq, ck, mask, scale):
+    """Attention of selected query rows only (the same definition as sparse_attn,
+    queries given as their own set with their q-cluster labels)."""
+    q, k, v = _f32(q_rows), _f32(k), _f32(v)
+    nq, d = q.shape
+    n = k.shape[0]
+    qlab = np.ascontiguousarray(qlab_rows, dtype=np.int32)
+    klab = np.ascontiguousarray(klab, dtype=np.int32)
+    mask = np.ascontiguousarray(mask, dtype=np.uint32)
+    out = np.empty((nq, d), np.float32)
+    lse = np.empty(nq, np.float32)
+    lib().orc_sparse_attn_q(_ptr(q, ctypes.c_float), nq, _ptr(qlab, ctypes.c_int32),
+                            _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float), n, d,
+                            _ptr(klab, ctypes.c_int32), cq, ck, _ptr(mask, ctypes.c_uint32),
+                            float(scale), _ptr(out, ctypes.c_float), _ptr(lse, ctypes.c_float))
     return out, lse
 
 

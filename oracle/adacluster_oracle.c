@@ -519,14 +519,17 @@ void orc_select_topk(const double* S, int cq, int ck, const int32_t* ksizes, int
  * m_i = max z, l_i = sum exp(z - m_i), o_i = sum exp(z - m_i) v_j / l_i,
  * lse_i = m_i + ln l_i. Raw (unnormalised) queries are used. Rows whose J_a is
  * empty get o = 0 and lse = -inf. Output in the original token order. */
-void orc_sparse_attn(const float* q, const float* k, const float* v, int64_t n, int d,
-                     const int32_t* qlab, const int32_t* klab, int cq, int ck,
-                     const uint32_t* mask, double scale, float* out, float* lse) {
+/* Queries and keys as separate sets: nq query rows with their q-cluster
+ * labels qlab, nk key rows with their key-cluster labels klab (the same
+ * definition; orc_sparse_attn is the case nq = nk = n). */
+void orc_sparse_attn_q(const float* q, int64_t nq, const int32_t* qlab, const float* k,
+                       const float* v, int64_t n, int d, const int32_t* klab, int cq, int ck,
+                       const uint32_t* mask, double scale, float* out, float* lse) {
     int words = (ck + 31) / 32;
     int64_t* jcount = (int64_t*)calloc((size_t)cq, sizeof(int64_t));
     int64_t** jlist = (int64_t**)calloc((size_t)cq, sizeof(int64_t*));
     uint8_t* used = (uint8_t*)calloc((size_t)cq, 1);
-    for (int64_t i = 0; i < n; ++i) used[qlab[i]] = 1;
+    for (int64_t i = 0; i < nq; ++i) used[qlab[i]] = 1;
     #pragma omp parallel for schedule(dynamic, 1)
     for (int a = 0; a < cq; ++a) {
         if (!used[a]) continue;
@@ -549,7 +552,7 @@ void orc_sparse_attn(const float* q, const float* k, const float* v, int64_t n, 
         double* z = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
         double* acc = (double*)malloc(sizeof(double) * (size_t)d);
         #pragma omp for schedule(dynamic, 16)
-        for (int64_t i = 0; i < n; ++i) {
+        for (int64_t i = 0; i < nq; ++i) {
             int a = qlab[i];
             int64_t c = jcount[a];
             const int64_t* J = jlist[a];
@@ -583,4 +586,10 @@ void orc_sparse_attn(const float* q, const float* k, const float* v, int64_t n, 
     }
     for (int a = 0; a < cq; ++a) free(jlist[a]);
     free(jlist); free(jcount); free(used);
+}
+
+void orc_sparse_attn(const float* q, const float* k, const float* v, int64_t n, int d,
+                     const int32_t* qlab, const int32_t* klab, int cq, int ck,
+                     const uint32_t* mask, double scale, float* out, float* lse) {
+    orc_sparse_attn_q(q, n, qlab, k, v, n, d, klab, cq, ck, mask, scale, out, lse);
 }

@@ -504,6 +504,28 @@ def test_subset_attention_equals_masked_dense():
     assert np.allclose(rows, 1.0, atol=1e-5)
 
 
+def test_attention_of_query_subset_equals_masked_dense():
+    # queries given as their own set (a sample of rows) against all keys
+    rng = np.random.default_rng(19)
+    n, d = 500, 32
+    q, k, v = (rng.standard_normal((n, d)).astype(np.float32) for _ in range(3))
+    cq, ck = 5, 33
+    qlab = rng.integers(0, cq, n).astype(np.int32)
+    klab = rng.integers(0, ck, n).astype(np.int32)
+    bits = rng.random((cq, ck)) < 0.4
+    mask = np.zeros((cq, 2), np.uint32)
+    for a in range(cq):
+        for b in np.flatnonzero(bits[a]):
+            mask[a, b // 32] |= np.uint32(1) << np.uint32(b % 32)
+    rows = rng.choice(n, 40, replace=False)
+    out, lse = oracle.sparse_attn_rows(q[rows], qlab[rows], k, v, klab, cq, ck, mask, 0.3)
+    allowed = bits[qlab[rows]][:, klab]
+    ref, ref_lse = _dense(q[rows], k, v, 0.3, allowed)
+    empty = ~allowed.any(1)
+    assert np.allclose(out[~empty], ref[~empty], rtol=1e-6, atol=1e-6)
+    assert np.all(out[empty] == 0) and np.all(np.isneginf(lse[empty]))
+
+
 def test_layer_head_full_flag_gives_dense():
     # identical keys: tau = 0, F = 1, so the layer must equal dense attention
     rng = np.random.default_rng(18)
