@@ -85,6 +85,18 @@ __device__ __forceinline__ uint32_t pack_h2(float x, float y) {
 }
 
 // ------------------------------------------------------------------ wave / block reductions
+// Sum over the wave in a fixed order (DPP row shifts, then row broadcasts),
+// returned uniform.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // Max over the four lanes l, l^16, l^32, l^48 (lanes holding one MFMA output
 // column), with the gfx950 row-swap permutes: each swap exchanges a row of 16
 // lanes with its partner row, so max(pair) is the max over the two rows.

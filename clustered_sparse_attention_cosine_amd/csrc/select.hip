@@ -199,6 +199,10 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     const uint32_t u = __float_as_uint(f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+// inverse of order_key
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
 
 // One workgroup (256 threads) per (head, q-cluster); thread t owns slots
 // 32t .. 32t+31, i.e. mask word t.
@@ -326,19 +330,147 @@ __global__ __launch_bounds__(256) void select_kernel(int Cq, int Ck, const float
     if (t == 0) sel_keys[(int64_t)bh * Cq + a] = total;
 }
 
+// One wave per (head, q-cluster) row for Ck <= 64 * SPL: lane j owns slots
+// j + 64 i (i < SPL), so the slots of a mask word pair come out of one ballot.
+// The same rule as select_kernel, with wave-level fixed-order sums (no
+// workgroup barriers in the 32-step bisection).
+template <bool TOPK, int SPL>
+__global__ __launch_bounds__(256) void select_wave_kernel(int Cq, int Ck, const float* __restrict__ S,
+                                                          const int32_t* __restrict__ k_sizes,
+                                                          const int32_t* __restrict__ n_clusters,
+                                                          const uint8_t* __restrict__ full, float scale,
+                                                          float top_p, int top_k,
+                                                          uint32_t* __restrict__ mask,
+                                                          int32_t* __restrict__ sel_keys) {
+    const int bh = blockIdx.y;
+    const int l = threadIdx.x & 63;
+    const int a = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (a >= Cq) return;
+    const int words = (Ck + 31) / 32;
+    const int ncl = min(n_clusters[bh], Ck);
+    const float* row = S + ((int64_t)bh * Cq + a) * Ck;
+    const int32_t* ks = k_sizes + (int64_t)bh * Ck;
+
+    // keys (order-preserving integer images of l) are kept; l is recovered from
+    // them, so a lane holds SPL keys and SPL weights
+    uint32_t key[SPL];
+    uint64_t live = 0;
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+        const int b = l + 64 * i;
+        const int n = b < ncl ? ks[b] : 0;
+        const bool ok = n > 0;
+        if (ok) live |= 1ull << i;
+        float v = -INFINITY;
+        if (ok) v = TOPK ? row[b] : fmaf(row[b], scale, logf((float)n));
+        lmax = fmaxf(lmax, v);
+        key[i] = ok ? order_key(v) : 0u;
+    }
+    uint64_t sel = 0;
+    const bool take_all = full[bh] || (!TOPK && top_p >= 1.0f);
+    if (take_all) {
+        sel = live;
+    } else {
+        float e[SPL];
+        float target;
+        if (TOPK) {
+            const int nlive = wave_sum_i(__popcll(live));
+            target = (float)min(top_k, nlive);
+#pragma unroll
+            for (int i = 0; i < SPL; ++i) e[i] = ((live >> i) & 1) ? 1.0f : 0.0f;
+        } else {
+            const float mx = wave_max(lmax);
+            float part = 0.0f;
+#pragma unroll
+            for (int i = 0; i < SPL; ++i) {
+                e[i] = ((live >> i) & 1) ? __expf(key_value(key[i]) - mx) : 0.0f;
+                part += e[i];
+            }
+            target = top_p * wave_sum_dpp(part);
+        }
+        // largest T with mass(key >= T) >= target
+        uint32_t T = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = T | (1u << bit);
+            float part = 0.0f;
+#pragma unroll
+            for (int i = 0; i < SPL; ++i) part += key[i] >= cand ? e[i] : 0.0f;
+            if (wave_sum_dpp(part) >= target) T = cand;
+        }
+        float above = 0.0f, e_tie = 0.0f;
+        int nties = 0;
+#pragma unroll
+        for (int i = 0; i < SPL; ++i) {
+            if (((live >> i) & 1) && key[i] > T) { sel |= 1ull << i; above += e[i]; }
+            if (((live >> i) & 1) && key[i] == T) { ++nties; e_tie = e[i]; }
+        }
+        const float mass_above = wave_sum_dpp(above);
+        const int ties = wave_sum_i(nties);
+        // tied slots share one l, hence one e: take the first k of them in slot order
+        const uint64_t has = __ballot(nties > 0);
+        const float et = has ? __shfl(e_tie, __ffsll((unsigned long long)has) - 1) : 0.0f;
+        int take = 0;
+        {
+            float acc = mass_above;
+            while (take < ties) {
+                acc += et;
+                ++take;
+                if (acc >= target) break;
+            }
+        }
+        int before = 0;  // ties in slots before block i
+        const uint64_t below = l == 0 ? 0ull : (~0ull >> (64 - l));
+#pragma unroll
+        for (int i = 0; i < SPL; ++i) {
+            const bool tie = ((live >> i) & 1) && key[i] == T;
+            const uint64_t tb = __ballot(tie);
+            if (tie && before + __popcll(tb & below) < take) sel |= 1ull << i;
+            before += __popcll(tb);
+        }
+    }
+    int keys = 0;
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+        const bool si = (sel >> i) & 1;
+        if (si) keys += ks[l + 64 * i];
+        const uint64_t wb = __ballot(si);
+        const int wd = 2 * i + (l & 1);
+        if (l < 2 && wd < words)
+            mask[((int64_t)bh * Cq + a) * words + wd] = (uint32_t)(l ? (wb >> 32) : wb);
+    }
+    const int total = wave_sum_i(keys);
+    if (l == 0) sel_keys[(int64_t)bh * Cq + a] = total;
+}
+
+template <bool TOPK>
+static void launch_select_t(const Prob& p, int Cq, int Ck, const float* S, const int32_t* k_sizes,
+                            const int32_t* n_clusters, const uint8_t* full, float scale,
+                            float top_p, int top_k, uint32_t* mask, int32_t* sel_keys,
+                            hipStream_t s) {
+    const dim3 wgrid((unsigned)((Cq + 3) / 4), (unsigned)p.BH);
+    if (Ck <= 1024)
+        hipLaunchKernelGGL((select_wave_kernel<TOPK, 16>), wgrid, dim3(256), 0, s, Cq, Ck, S, k_sizes,
+                           n_clusters, full, scale, top_p, top_k, mask, sel_keys);
+    else if (Ck <= 4096)
+        hipLaunchKernelGGL((select_wave_kernel<TOPK, 64>), wgrid, dim3(256), 0, s, Cq, Ck, S, k_sizes,
+                           n_clusters, full, scale, top_p, top_k, mask, sel_keys);
+    else
+        hipLaunchKernelGGL(select_kernel<TOPK>, dim3((unsigned)Cq, (unsigned)p.BH), dim3(256), 0, s,
+                           Cq, Ck, S, k_sizes, n_clusters, full, scale, top_p, top_k, mask, sel_keys);
+}
+
 hipError_t launch_topp(const Prob& p, int Cq, int Ck, const float* S, const int32_t* k_sizes,
                        const int32_t* n_clusters, const uint8_t* full, float scale, float top_p,
                        uint32_t* mask, int32_t* sel_keys, hipStream_t s) {
-    hipLaunchKernelGGL(select_kernel<false>, dim3((unsigned)Cq, (unsigned)p.BH), dim3(256), 0, s, Cq,
-                       Ck, S, k_sizes, n_clusters, full, scale, top_p, 0, mask, sel_keys);
+    launch_select_t<false>(p, Cq, Ck, S, k_sizes, n_clusters, full, scale, top_p, 0, mask, sel_keys, s);
     return hipGetLastError();
 }
 
 hipError_t launch_topk(const Prob& p, int Cq, int Ck, const float* S, const int32_t* k_sizes,
                        const int32_t* n_clusters, const uint8_t* full, int top_k, uint32_t* mask,
                        int32_t* sel_keys, hipStream_t s) {
-    hipLaunchKernelGGL(select_kernel<true>, dim3((unsigned)Cq, (unsigned)p.BH), dim3(256), 0, s, Cq,
-                       Ck, S, k_sizes, n_clusters, full, 1.0f, 1.0f, top_k, mask, sel_keys);
+    launch_select_t<true>(p, Cq, Ck, S, k_sizes, n_clusters, full, 1.0f, 1.0f, top_k, mask, sel_keys, s);
     return hipGetLastError();
 }
 
