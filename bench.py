@@ -2,7 +2,9 @@
 
     python bench.py [--steps K] [--warmup W] [--workload cog76k] [--no-cpu] [--no-dense]
 
-A step is one cold layer call on seeded synthetic Q/K/V already resident in HBM:
+A step is one cold layer call on seeded synthetic Q/K/V already resident in HBM
+(3 warm-up + 20 timed steps by default; per-step median/p10/p90 from HIP events,
+and the latency/density spread over seeds 1 and 2):
 cluster_q -> cluster_k (threshold-adaptive) -> select (TensorQuest + top-p) ->
 sparse_attn. The headline value is the dense-equivalent throughput
 4 H N^2 D / t_layer. Prints one JSON line (last line of stdout).
@@ -33,12 +35,14 @@ def log(*a):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="cog76k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense comparisons")
+    ap.add_argument("--no-spread", action="store_true",
+                    help="skip the latency/density spread over seeds 1 and 2")
     ap.add_argument("--profile-steps", action="store_true",
                     help="only warmup + timed steps (for profiler runs)")
     args = ap.parse_args()
@@ -107,6 +111,10 @@ def main():
     stage_names = ["cluster_q", "cluster_k", "select", "sparse_attn"]
     stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events]))
                 for i, n in enumerate(stage_names)}
+    per_step = np.array([e[0].elapsed_time(e[4]) for e in events])
+    layer_stats = {"median": round(float(np.median(per_step)), 4),
+                   "p10": round(float(np.percentile(per_step, 10)), 4),
+                   "p90": round(float(np.percentile(per_step, 90)), 4)}
 
     # workload facts from the last step
     sizes_q = Q["sizes"].double()
@@ -149,6 +157,7 @@ def main():
                    "top_p": w.top_p, "lloyd_iters": w.iters, "init": w.init,
                    "layer_ms": round(ms, 4)},
         "stages_ms": {k2: round(v2, 4) for k2, v2 in stage_ms.items()},
+        "layer_ms_events": layer_stats,
         "selection": {"pairs": pairs, "density": round(density, 5), "full_heads": full_heads,
                       "k_slots": {str(s): slots.count(s) for s in sorted(set(slots))}},
         "roofline": {"kernel": "sparse_attn (run build + work list + attention)",
@@ -161,6 +170,10 @@ def main():
 
     if not args.no_dense:
         result["dense"] = dense_compare(torch, adc, q, k, v, w, dev, stream)
+
+    if not args.no_spread:
+        del q, k, v, Q, K, S, out
+        result["spread"] = seed_spread(torch, adc, synth, w, cfg, dev, stream)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, g, args.seed)
@@ -186,6 +199,37 @@ def measured_traffic(workload):
         if line.startswith("traffic_bytes = "):
             return int(line.split("=")[1])
     return None
+
+
+def seed_spread(torch, adc, synth, w, cfg, dev, stream, seeds=(1, 2), steps=5):
+    """Layer latency and achieved density on other seeds of the same workload."""
+    out = []
+    for seed in seeds:
+        g = synth.generate(w, seed=seed)
+        q, k, v = (torch.from_numpy(g[t].view(np.int16)).view(torch.bfloat16).to(dev)
+                   if g[t].dtype == np.uint16 else torch.from_numpy(g[t]).to(dev) for t in "qkv")
+        del g
+        times = []
+        for i in range(2 + steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            Q = adc.cluster_q(q, cfg.q_clusters, cfg.iters, cfg.init, seed)
+            K = adc.cluster_k(k, v, cfg.k_base, cfg.k_max, cfg.iters, cfg.tau_mult, cfg.adaptive,
+                              cfg.init, seed)
+            S = adc.select(Q["qrep"], K, cfg.top_p)
+            adc.sparse_attn(q, Q["perm"], Q["offsets"], K["k_perm"], K["v_perm"], K["offsets"],
+                            S["mask"], want_lse=False)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                times.append(e0.elapsed_time(e1))
+        pairs = float((Q["sizes"].double() * S["sel_keys"].double()).sum().item())
+        out.append({"seed": seed, "layer_ms_median": round(float(np.median(times)), 4),
+                    "density": round(pairs / (w.B * w.H * float(w.N) ** 2), 5),
+                    "full_heads": int(K["full"].sum().item())})
+        log(f"seed {seed}: {out[-1]}")
+        del q, k, v, Q, K, S
+    return out
 
 
 def dense_compare(torch, adc, q, k, v, w, dev, stream):
