@@ -30,6 +30,7 @@ ADC_F32, ADC_BF16 = 0, 1
 INIT = {"kmeanspp": 0, "sample": 1, "caller": 2}
 SCORE = {"quest": 0, "centroid": 1}
 RULE = {"topp": 0, "topk": 1}
+K_FIXED, K_STAGED, K_WARM = 0, 1, 2
 STATUS = {0: "ADC_OK", -1: "ADC_EINVAL", -2: "ADC_ESHAPE", -3: "ADC_EDTYPE",
           -4: "ADC_EWORKSPACE", -5: "ADC_EHIP", -6: "ADC_EUNSUPPORTED"}
 
@@ -142,6 +143,9 @@ def cluster_q(q, n_clusters, iters=5, init="sample", seed=0, init_centroids=None
     sh = _shape(q)
     B, H, N, D = q.shape
     dev = q.device
+    if init == "caller" and (init_centroids is None
+                             or tuple(init_centroids.shape) != (B, H, n_clusters, D)):
+        raise ValueError(f"init_centroids must have shape {(B, H, n_clusters, D)}")
     prm = QParams(n_clusters, iters, INIT[init], 0, seed & (2**64 - 1))
     ws_n = lib().adacluster_cluster_q_workspace(ctypes.byref(sh), ctypes.byref(prm))
     if ws_n == 0:
@@ -164,23 +168,45 @@ def cluster_q(q, n_clusters, iters=5, init="sample", seed=0, init_centroids=None
 
 
 def cluster_k(k, v, base_clusters, max_clusters=None, iters=5, tau_mult=1.5, adaptive=True,
-              init="sample", seed=0, init_centroids=None):
+              init="sample", seed=0, init_centroids=None, n_clusters=None, full=None, tau=None):
+    """adaptive: True (Algorithm 1), False (one k-means with base_clusters) or
+    "warm" (keep the per-head counts `n_clusters` and flags `full` of an earlier
+    adaptive call and start from its centres `init_centroids`; init is then
+    "caller"). The state tensors passed in are copied, not modified."""
     sh = _shape(k)
     if v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("k and v must share shape and dtype")
     _shape(v)
     B, H, N, D = k.shape
     dev = k.device
-    nmax = max_clusters if max_clusters is not None else (4 * base_clusters if adaptive else base_clusters)
-    prm = KParams(base_clusters, nmax, iters, tau_mult, int(bool(adaptive)), INIT[init],
-                  seed & (2**64 - 1))
+    warm = adaptive == "warm"
+    if warm:
+        if init_centroids is None or n_clusters is None or full is None:
+            raise ValueError("the warm mode needs init_centroids, n_clusters and full")
+        init = "caller"
+        mode = K_WARM
+        nmax = max_clusters if max_clusters is not None else init_centroids.shape[2]
+    else:
+        mode = K_STAGED if adaptive else K_FIXED
+        nmax = max_clusters if max_clusters is not None else (4 * base_clusters if adaptive else base_clusters)
+    if init == "caller":
+        rows = nmax if warm else base_clusters
+        if init_centroids is None or tuple(init_centroids.shape) != (B, H, rows, D):
+            raise ValueError(f"init_centroids must have shape {(B, H, rows, D)}")
+    prm = KParams(base_clusters, nmax, iters, tau_mult, mode, INIT[init], seed & (2**64 - 1))
     ws_n = lib().adacluster_cluster_k_workspace(ctypes.byref(sh), ctypes.byref(prm))
     if ws_n == 0:
         raise AdaClusterError("invalid cluster_k arguments: " + lib().adacluster_last_error().decode())
+
+    def state(t, dtype):
+        return (torch.empty(B, H, dtype=dtype, device=dev) if t is None
+                else t.to(device=dev, dtype=dtype).reshape(B, H).clone())
+
     out = dict(
-        n_clusters=torch.empty(B, H, dtype=torch.int32, device=dev),
-        full=torch.empty(B, H, dtype=torch.uint8, device=dev),
-        tau=torch.empty(B, H, dtype=torch.float32, device=dev),
+        n_clusters=state(n_clusters if warm else None, torch.int32),
+        full=state(full if warm else None, torch.uint8),
+        tau=(state(tau, torch.float32) if warm and tau is not None
+             else torch.zeros(B, H, dtype=torch.float32, device=dev)),
         assign=torch.empty(B, H, N, dtype=torch.int32, device=dev),
         centroids=torch.empty(B, H, nmax, D, dtype=torch.float32, device=dev),
         sizes=torch.empty(B, H, nmax, dtype=torch.int32, device=dev),
@@ -294,13 +320,27 @@ class LayerConfig:
     score: str = "quest"
     rule: str = "topp"
     top_k: int = 64
+    warm_iters: int = 5     # Lloyd iterations of the warm steps
 
 
-def layer(q, k, v, cfg: LayerConfig):
-    """One clustered-sparse-attention layer (Algorithm 3): returns (out, lse, state)."""
-    Q = cluster_q(q, cfg.q_clusters, cfg.iters, cfg.init, cfg.seed)
-    K = cluster_k(k, v, cfg.k_base, cfg.k_max, cfg.iters, cfg.tau_mult, cfg.adaptive, cfg.init,
-                  cfg.seed)
+def layer(q, k, v, cfg: LayerConfig, prev=None):
+    """One clustered-sparse-attention layer (Algorithm 3): returns (out, lse, state).
+
+    With `prev` (the state of this layer at the previous denoising step) the
+    layer runs its steady-state form (section 3.2.2): both clusterings start
+    from the previous centres, and the keys keep their per-head counts and
+    full-attention flags."""
+    if prev is None:
+        Q = cluster_q(q, cfg.q_clusters, cfg.iters, cfg.init, cfg.seed)
+        K = cluster_k(k, v, cfg.k_base, cfg.k_max, cfg.iters, cfg.tau_mult, cfg.adaptive,
+                      cfg.init, cfg.seed)
+    else:
+        pq, pk = prev["Q"], prev["K"]
+        Q = cluster_q(q, cfg.q_clusters, cfg.warm_iters, "caller",
+                      init_centroids=pq["centroids"])
+        K = cluster_k(k, v, cfg.k_base, pk["max_clusters"], cfg.warm_iters, adaptive="warm",
+                      init_centroids=pk["centroids"], n_clusters=pk["n_clusters"],
+                      full=pk["full"], tau=pk["tau"])
     S = select(Q["qrep"], K, cfg.top_p, cfg.score, cfg.rule, cfg.top_k)
     out, lse = sparse_attn(q, Q["perm"], Q["offsets"], K["k_perm"], K["v_perm"], K["offsets"],
                            S["mask"])

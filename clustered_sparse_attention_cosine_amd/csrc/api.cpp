@@ -174,10 +174,10 @@ CentView make_view(float* cent, const KmeansWs& w, int cap, int base, int m) {
 // last centres are left to the exact member means of the layout pass.
 hipError_t lloyd(const Prob& p, const void* x, int normalize, RowSet rs, const float* inv_norm,
                  CentView cv, int iters, bool final_update, int32_t* labels, const KmeansWs& w,
-                 hipStream_t s) {
+                 hipStream_t s, const int32_t* mcount = nullptr) {
     hipError_t e;
     for (int it = 0; it < iters; ++it) {
-        if ((e = launch_assign(p, x, rs, inv_norm, normalize, cv, nullptr, labels, flags_of(w), s)))
+        if ((e = launch_assign(p, x, rs, inv_norm, normalize, cv, mcount, labels, flags_of(w), s)))
             return e;
         if (it + 1 < iters || final_update) {
             if ((e = launch_update_accum(p, x, rs, inv_norm, labels, cv, s))) return e;
@@ -295,8 +295,12 @@ static int32_t check_k(const adc_shape* shape, const adc_k_params* prm) {
     if (prm->init < 0 || prm->init > 2) return fail(ADC_EINVAL, "init = %d unknown", prm->init);
     if (!(prm->tau_mult >= 0.0f) || prm->tau_mult > 1e6f)
         return fail(ADC_EINVAL, "tau_mult must be a finite value >= 0");
-    if (prm->adaptive && prm->init == ADC_INIT_CALLER)
-        return fail(ADC_EUNSUPPORTED, "caller centres need adaptive == 0 (warm steps keep counts fixed)");
+    if (prm->adaptive < ADC_K_FIXED || prm->adaptive > ADC_K_WARM)
+        return fail(ADC_EINVAL, "adaptive = %d unknown", prm->adaptive);
+    if (prm->adaptive == ADC_K_STAGED && prm->init == ADC_INIT_CALLER)
+        return fail(ADC_EUNSUPPORTED, "caller centres need FIXED or WARM (warm steps keep counts fixed)");
+    if (prm->adaptive == ADC_K_WARM && prm->init != ADC_INIT_CALLER)
+        return fail(ADC_EINVAL, "WARM starts from the previous centres: init must be ADC_INIT_CALLER");
     return ADC_OK;
 }
 
@@ -304,7 +308,7 @@ static void plan_k(Carver& c, const adc_shape* shape, const adc_k_params* prm, K
                    StageWs& sw) {
     Prob p = make_prob(shape);
     plan_kmeans(c, p, prm->max_clusters, false, prm->init == ADC_INIT_KMEANSPP, false, w);
-    if (prm->adaptive) plan_stages(c, p, sw);
+    if (prm->adaptive == ADC_K_STAGED) plan_stages(c, p, sw);
 }
 
 size_t adacluster_cluster_k_workspace(const adc_shape* shape, const adc_k_params* prm) {
@@ -346,7 +350,14 @@ int32_t adacluster_cluster_k(const adc_shape* shape, const adc_k_params* prm, co
     HIPCHK(fill_i32(w.cnt, (int64_t)p.BH * nmax, 0, s));
     RowSet all{nullptr, nullptr, nullptr};
 
-    if (!prm->adaptive) {
+    if (prm->adaptive == ADC_K_WARM) {
+        // steady state (section 3.2.2): per-head counts kept, previous centres as init
+        HIPCHK(launch_warm_info(p.BH, p.N, nmax, n_clusters, stage_sizes, s));
+        CentView cv = make_view(centroids, w, nmax, 0, nmax);
+        HIPCHK(launch_warm_init(p, init_centroids, n_clusters, cv, s));
+        HIPCHK(launch_finalize(p, cv, nullptr, 0, s));
+        HIPCHK(lloyd(p, k, 0, all, nullptr, cv, prm->iters, false, assign, w, s, n_clusters));
+    } else if (prm->adaptive == ADC_K_FIXED) {
         CentView cv = make_view(centroids, w, nmax, 0, m0);
         HIPCHK(init_centres(p, k, 0, all, cv, prm->init, init_centroids, prm->seed, TENSOR_K, 0, w, s));
         HIPCHK(launch_finalize(p, cv, nullptr, 0, s));

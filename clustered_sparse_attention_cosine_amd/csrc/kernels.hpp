@@ -23,6 +23,10 @@ hipError_t fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 hipError_t fill_u8(uint8_t* p, int64_t n, uint8_t v, hipStream_t s);
 hipError_t launch_fixed_info(int BH, int N, int m, int32_t* n_clusters, uint8_t* full, float* tau,
                              int32_t* stage_sizes, hipStream_t s);
+// Warm start: clamp the caller's per-head counts to [1, cap] in place and write
+// the fixed-path stage record.
+hipError_t launch_warm_info(int BH, int N, int cap, int32_t* n_clusters, int32_t* stage_sizes,
+                            hipStream_t s);
 
 // ---------------------------------------------------------------- k-means (kmeans.hip)
 // 1 / max(||x_i||, 1e-12) per row (norm in f64).
@@ -77,11 +81,16 @@ struct FlagSet {
     int32_t* ccount;  // [BH, N] number of candidates found (may exceed CAND_CAP)
 };
 constexpr int CAND_CAP = 16;
+// Warm start: slots [0, count[bh]) of cv (base 0) copy their centres from
+// init ([BH][cap][D]) and are marked as holding a centre, the rest are not.
+hipError_t launch_warm_init(const Prob& p, const float* init, const int32_t* count, CentView cv,
+                            hipStream_t s);
+// m_eff[bh] = min(mcount[bh], last slot holding a centre + 1).
+hipError_t launch_last_valid(const Prob& p, CentView cv, const int32_t* mcount, int32_t* m_eff,
+                             hipStream_t s);
 // Nearest centre by a bf16 hi/lo matrix-core contraction with a certified
 // error bound; uncertain rows are settled by exact f64 distances of the
 // centres inside their uncertainty band (labels are final on return).
-hipError_t launch_last_valid(const Prob& p, CentView cv, const int32_t* mcount, int32_t* m_eff,
-                             hipStream_t s);
 hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
                          int normalize, CentView cv, const int32_t* mcount, int32_t* labels,
                          FlagSet fs, hipStream_t s);

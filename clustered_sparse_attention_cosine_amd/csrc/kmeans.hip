@@ -76,6 +76,55 @@ hipError_t launch_fixed_info(int BH, int N, int m, int32_t* n_clusters, uint8_t*
     return hipGetLastError();
 }
 
+// Warm start (section 3.2.2): the per-head count from an earlier multi-stage
+// call is clamped to [1, cap] in place, and the fixed-path stage record (N,
+// then -1) is written.
+__global__ void warm_info_kernel(int BH, int N, int cap, int32_t* n_clusters, int32_t* stage_sizes) {
+    int bh = blockIdx.x * blockDim.x + threadIdx.x;
+    if (bh >= BH) return;
+    n_clusters[bh] = min(max(n_clusters[bh], 1), cap);
+    if (stage_sizes) {
+        stage_sizes[bh * 8] = N;
+        for (int i = 1; i < 8; ++i) stage_sizes[bh * 8 + i] = -1;
+    }
+}
+
+hipError_t launch_warm_info(int BH, int N, int cap, int32_t* n_clusters, int32_t* stage_sizes,
+                            hipStream_t s) {
+    hipLaunchKernelGGL(warm_info_kernel, dim3((BH + 63) / 64), dim3(64), 0, s, BH, N, cap,
+                       n_clusters, stage_sizes);
+    return hipGetLastError();
+}
+
+// Slots [0, count) of each head take the caller's centres and hold a centre;
+// the rest hold none (their centre rows were cleared beforehand). One wave per
+// slot.
+template <int D>
+__global__ __launch_bounds__(256) void warm_init_kernel(const float* __restrict__ init,
+                                                        const int32_t* __restrict__ count,
+                                                        CentView cv) {
+    const int bh = blockIdx.y;
+    const int j = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+    if (j >= cv.cap) return;
+    const int64_t slot = (int64_t)bh * cv.cap + j;
+    const bool used = j < count[bh];
+    if (used) {
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e) cv.cent[slot * D + l + 64 * e] = init[slot * D + l + 64 * e];
+    }
+    if (l == 0) cv.valid[slot] = used ? 1 : 0;
+}
+
+hipError_t launch_warm_init(const Prob& p, const float* init, const int32_t* count, CentView cv,
+                            hipStream_t s) {
+    dim3 grid((unsigned)((cv.cap + 3) / 4), (unsigned)p.BH);
+    if (p.D == 64)
+        hipLaunchKernelGGL(warm_init_kernel<64>, grid, dim3(256), 0, s, init, count, cv);
+    else
+        hipLaunchKernelGGL(warm_init_kernel<128>, grid, dim3(256), 0, s, init, count, cv);
+    return hipGetLastError();
+}
+
 // Slots past the last one holding a centre cannot win an assignment: m_eff =
 // min(mcount, last valid slot + 1), one workgroup per head.
 __global__ __launch_bounds__(256) void last_valid_kernel(int cap, int m, const uint8_t* __restrict__ valid,

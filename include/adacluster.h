@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define ADACLUSTER_ABI_VERSION 1
+#define ADACLUSTER_ABI_VERSION 2
 
 typedef enum {
     ADC_OK = 0,
@@ -58,7 +58,8 @@ typedef enum { ADC_F32 = 0, ADC_BF16 = 1 } adc_dtype;
  * section 3.2.2 "Efficient initialization"; see the DESIGN notes):
  *   KMEANSPP  seeded D^2 sampling (Arthur and Vassilvitskii 2007)
  *   SAMPLE    seeded systematic sample: slot j takes row floor((j n + r) / m)
- *   CALLER    centres supplied by the caller (warm start, fixed counts only) */
+ *   CALLER    centres supplied by the caller (the warm start of section 3.2.2:
+ *             later denoising steps begin from the previous step's centres) */
 typedef enum { ADC_INIT_KMEANSPP = 0, ADC_INIT_SAMPLE = 1, ADC_INIT_CALLER = 2 } adc_init;
 
 /* Cluster significance: QUEST = Eq. (1) of section 3.2.3 evaluated as the
@@ -69,6 +70,14 @@ typedef enum { ADC_SCORE_QUEST = 0, ADC_SCORE_CENTROID = 1 } adc_score;
 /* Selection rule: TOPP = shortest prefix (by l_b = score*scale + ln n_b)
  * whose softmax mass reaches top_p; TOPK = argtopk of Algorithm 3 step 7. */
 typedef enum { ADC_SELECT_TOPP = 0, ADC_SELECT_TOPK = 1 } adc_select;
+
+/* Key clustering mode (adc_k_params.adaptive).
+ *   FIXED  one k-means with m0 centres per head
+ *   STAGED Algorithm 1: counts chosen per head by the multi-stage loop
+ *   WARM   the steady state of section 3.2.2: each head keeps the count (and
+ *          the full-attention flag) found by an earlier STAGED call and runs
+ *          one k-means from that call's centres */
+typedef enum { ADC_K_FIXED = 0, ADC_K_STAGED = 1, ADC_K_WARM = 2 } adc_k_mode;
 
 typedef struct {
     int32_t B, H, N, D;
@@ -84,12 +93,14 @@ typedef struct {
 } adc_q_params;
 
 typedef struct {
-    int32_t base_clusters;  /* m0: first-stage count (the fixed count when adaptive == 0) */
+    int32_t base_clusters;  /* m0: first-stage count (the fixed count when adaptive == 0;
+                               unused when adaptive == 2) */
     int32_t max_clusters;   /* Nmax: slot capacity; adaptive stages are m0, m0, 2 m0, ... */
     int32_t iters;          /* Lloyd iterations per k-means call, >= 1 */
     float tau_mult;         /* tau = tau_mult x mean stage-0 distance (1.5 in section 4.1) */
-    int32_t adaptive;       /* 1: Algorithm 1 multi-stage, 0: one k-means with m0 */
-    int32_t init;           /* adc_init (CALLER requires adaptive == 0) */
+    int32_t adaptive;       /* adc_k_mode */
+    int32_t init;           /* adc_init (adaptive == 1 takes KMEANSPP or SAMPLE,
+                               adaptive == 2 takes CALLER only) */
     uint64_t seed;
 } adc_k_params;
 
@@ -131,10 +142,18 @@ int32_t adacluster_cluster_q(const adc_shape* shape, const adc_q_params* params,
  * its nearest slot holding a centre, centres are refreshed to member means,
  * and per-slot max/min and the cluster-contiguous K/V copies are built.
  *   k, v           [B,H,N,D] dtype
- *   init_centroids [B,H,m0,D] f32 iff init == CALLER (adaptive == 0), else NULL
- *   n_clusters     [B,H] int32   out: slots used (m0, 2 m0, 4 m0, ... <= Nmax)
- *   full_attn      [B,H] uint8   out: F of Algorithm 1
- *   tau            [B,H] f32     out: threshold (0 when adaptive == 0)
+ *   init_centroids f32 iff init == CALLER, else NULL: [B,H,m0,D] for FIXED,
+ *                  [B,H,Nmax,D] for WARM (normally the `centroids` output of
+ *                  the previous call; rows past the head's count are ignored)
+ *   n_clusters     [B,H] int32   FIXED/STAGED out: slots used (m0, 2 m0, 4 m0,
+ *                  ... <= Nmax). WARM in/out: the per-head count, clamped to
+ *                  [1, Nmax] and written back; slots [0, count) start from
+ *                  init_centroids and all of them hold a centre
+ *   full_attn      [B,H] uint8   FIXED/STAGED out: F of Algorithm 1 (0 for
+ *                  FIXED). WARM: read by nobody here and left unchanged (the
+ *                  flag found by the STAGED call stays the caller's state)
+ *   tau            [B,H] f32     out: threshold (0 for FIXED; left unchanged
+ *                  by WARM)
  *   assign         [B,H,N] int32 out: slot of each key
  *   centroids      [B,H,Nmax,D] f32 out: slot centres (unused slots: 0)
  *   sizes          [B,H,Nmax] int32 out: members per slot (0 for empty/unused)
@@ -145,7 +164,9 @@ int32_t adacluster_cluster_q(const adc_shape* shape, const adc_q_params* params,
  *                  n_clusters repeat N)
  *   k_perm, v_perm [B,H,N,D] dtype out: K and V rows in perm order
  *   stage_sizes    [B,H,8] int32 out (may be NULL): |U| at the start of each
- *                  stage and after the last one, -1 past the end
+ *                  stage and after the last one, -1 past the end (FIXED and
+ *                  WARM: N, then -1)
+ * WARM needs init == CALLER; the other modes reject CALLER with STAGED.
  */
 size_t adacluster_cluster_k_workspace(const adc_shape* shape, const adc_k_params* params);
 int32_t adacluster_cluster_k(const adc_shape* shape, const adc_k_params* params,

@@ -248,6 +248,21 @@ def cluster_k(k, m0, nmax, iters, tau_mult=1.5, adaptive=True, init="sample", se
                 kmax=kmax, kmin=kmin, perm=perm, off=off)
 
 
+def cluster_k_warm(k, prev, iters):
+    """A later denoising step (AdaCluster section 3.2.2, "Efficient
+    initialization"): the head keeps the slot count and full-attention flag its
+    multi-stage clustering found, and runs k-means over the new keys starting
+    from the previous step's centres. `prev` is an earlier cluster_k result of
+    this head (its n_slots, full and cent). Every one of the count's slots holds
+    a centre."""
+    m = prev["n_slots"]
+    nmax = prev["cent"].shape[0]
+    r = cluster_k(k, m, nmax, iters, adaptive=False, init="caller", init_cent=prev["cent"][:m])
+    r["full"] = prev["full"]
+    r["tau"] = prev["tau"]
+    return r
+
+
 def quest_scores(qrep, kmax, kmin, ksizes):
     qrep, kmax, kmin = _f32(qrep), _f32(kmax), _f32(kmin)
     cq, d = qrep.shape
@@ -344,13 +359,22 @@ def mask_bits(mask, ck):
 
 # ----------------------------------------------------------------- one layer, one head
 def layer_head(q, k, v, *, cq, m0, nmax, iters, top_p, init="sample", adaptive=True,
-               tau_mult=1.5, seed=0, b=0, h=0, score="quest", rule="topp", top_k=None):
-    """The whole clustered-attention layer for one head (Algorithm 3)."""
+               tau_mult=1.5, seed=0, b=0, h=0, score="quest", rule="topp", top_k=None,
+               prev=None, warm_iters=None):
+    """The whole clustered-attention layer for one head (Algorithm 3). With
+    `prev` (this function's result at the previous denoising step) both
+    clusterings start from the previous centres (section 3.2.2) and run
+    `warm_iters` Lloyd rounds."""
     d = q.shape[1]
     scale = 1.0 / np.sqrt(d)
-    Q = cluster_q(q, cq, iters, init=init, seed=seed, b=b, h=h)
-    K = cluster_k(k, m0, nmax, iters, tau_mult=tau_mult, adaptive=adaptive, init=init,
-                  seed=seed, b=b, h=h)
+    if prev is None:
+        Q = cluster_q(q, cq, iters, init=init, seed=seed, b=b, h=h)
+        K = cluster_k(k, m0, nmax, iters, tau_mult=tau_mult, adaptive=adaptive, init=init,
+                      seed=seed, b=b, h=h)
+    else:
+        wi = iters if warm_iters is None else warm_iters
+        Q = cluster_q(q, cq, wi, init="caller", init_cent=prev["Q"]["cent"])
+        K = cluster_k_warm(k, prev["K"], wi)
     ck = K["n_slots"]
     if score == "quest":
         S = quest_scores(Q["qrep"], K["kmax"][:ck], K["kmin"][:ck], K["sizes"][:ck])

@@ -17,6 +17,12 @@ available, so these fields stand in for them):
   an optional per-head scale s_h ~ U(0.5, 2) shared by Q, K and V
   (Wan-shaped case); optional i.i.d. N(0, 1) text tokens prepended
   (CogVideoX-shaped 17.7K case). bf16 workloads are rounded to nearest-even.
+
+Denoising steps (the warm start of section 3.2.2 relies on tokens moving
+little from one step to the next, Fig. 6): step s keeps every field's
+amplitude, direction and frequency, advances its phase by s * drift radians,
+and draws fresh noise from a sub-stream of its own; text tokens stay fixed.
+Step 0 is the plain recipe above.
 """
 from __future__ import annotations
 
@@ -97,22 +103,25 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def _tensor_head(rng: np.random.Generator, w: Workload, coords: np.ndarray) -> np.ndarray:
+def _tensor_head(rng: np.random.Generator, w: Workload, coords: np.ndarray, step: int = 0,
+                 drift: float = 0.0, step_rng: np.random.Generator | None = None) -> np.ndarray:
     """One head of one tensor as float32 [N, D] (before per-head scale / dtype)."""
     T, Hg, W = w.grid
     amp = rng.uniform(0.5, 1.5, size=N_FIELDS)
     dirs = rng.standard_normal((N_FIELDS, w.D))
     kap = rng.uniform(0.0, 2.0, size=(N_FIELDS, 3))
-    phi = rng.uniform(0.0, 2.0 * np.pi, size=N_FIELDS)
+    phi = rng.uniform(0.0, 2.0 * np.pi, size=N_FIELDS) + step * drift
     t, y, x = coords
     phase = 2.0 * np.pi * (np.outer(kap[:, 0], t / T) + np.outer(kap[:, 1], y / Hg)
                            + np.outer(kap[:, 2], x / W)) + phi[:, None]
     field = (np.sin(phase).T @ (amp[:, None] * dirs)).astype(np.float32)   # [Nv, D]
     nv = field.shape[0]
-    if w.noise == "student_t3":
-        eps = rng.standard_t(3, size=(nv, w.D)).astype(np.float32)
-    else:
-        eps = rng.standard_normal((nv, w.D), dtype=np.float32)
+    for g in ((rng,) if step == 0 else (rng, step_rng)):
+        # at step > 0 the step-0 draw only advances the base stream (text tokens follow it)
+        if w.noise == "student_t3":
+            eps = g.standard_t(3, size=(nv, w.D)).astype(np.float32)
+        else:
+            eps = g.standard_normal((nv, w.D), dtype=np.float32)
     field += np.float32(NOISE_STD) * eps
     if w.text_tokens:
         text = rng.standard_normal((w.text_tokens, w.D), dtype=np.float32)
@@ -120,8 +129,11 @@ def _tensor_head(rng: np.random.Generator, w: Workload, coords: np.ndarray) -> n
     return field
 
 
-def generate(w: Workload, seed: int = 0, heads=None):
-    """Q, K, V for workload ``w``.
+DRIFT = 0.05   # default phase advance per denoising step, radians
+
+
+def generate(w: Workload, seed: int = 0, heads=None, step: int = 0, drift: float = DRIFT):
+    """Q, K, V for workload ``w`` at denoising step ``step``.
 
     Returns a dict with ``q``, ``k``, ``v`` of shape [B, H', N, D] where H' is
     ``len(heads)`` (default: all heads). For bf16 workloads the arrays are
@@ -143,7 +155,8 @@ def generate(w: Workload, seed: int = 0, heads=None):
         for b in range(w.B):
             for hi, h in enumerate(heads):
                 rng = np.random.default_rng([seed, ti, b, h])
-                x = _tensor_head(rng, w, coords)
+                srng = np.random.default_rng([seed, ti, b, h, step]) if step else None
+                x = _tensor_head(rng, w, coords, step, drift, srng)
                 if head_scales is not None:
                     x *= np.float32(head_scales[b, h])
                 arr[b, hi] = f32_to_bf16_bits(x) if w.dtype == "bf16" else x

@@ -29,7 +29,7 @@ def test_library_exports_every_header_symbol():
 
 
 def test_abi_version():
-    assert adc.lib().adacluster_abi_version() == 1
+    assert adc.lib().adacluster_abi_version() == 2
 
 
 def _shape(B=1, H=2, N=1000, D=64, dt=adc.ADC_BF16):
@@ -105,6 +105,16 @@ def test_cluster_k_parameter_checks():
     assert call(adc.KParams(64, 32, 5, 1.5, 1, 1, 0)) == -2          # Nmax < m0
     assert call(adc.KParams(16, 64, 5, float("nan"), 1, 1, 0)) == -1  # tau_mult
     assert call(adc.KParams(16, 64, 5, 1.5, 1, 2, 0)) == -6          # caller + adaptive
+    assert call(adc.KParams(16, 64, 5, 1.5, 2, 1, 0)) == -1          # warm without caller init
+    assert call(adc.KParams(16, 64, 5, 1.5, 3, 2, 0)) == -1          # unknown mode
+    no_init = list(ptr)
+    no_init[2] = None                                                # init_centroids
+    assert L.adacluster_cluster_k(ctypes.byref(sh), ctypes.byref(adc.KParams(16, 64, 5, 1.5, 2, 2, 0)),
+                                  *no_init, ctypes.c_void_p(16), 1 << 40, None) == -1
+    # the warm mode needs no multi-stage state
+    ws = L.adacluster_cluster_k_workspace
+    assert 0 < ws(ctypes.byref(sh), ctypes.byref(adc.KParams(16, 64, 5, 1.5, 2, 2, 0))) \
+        < ws(ctypes.byref(sh), ctypes.byref(adc.KParams(16, 64, 5, 1.5, 1, 1, 0)))
 
 
 def test_select_and_attn_parameter_checks():

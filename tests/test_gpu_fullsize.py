@@ -99,14 +99,23 @@ def test_query_labels_agree_with_free_running_oracle(layer):
     assert agree >= 0.99
 
 
-def test_key_clustering_agrees_with_free_running_oracle(layer):
+KH = 13          # the head whose key clustering the oracle redoes in full
+
+
+@pytest.fixture(scope="module")
+def oracle_keys(layer):
+    w, g = layer["w"], layer["g"]
+    k = synth.as_f32(g["k"][0, KH])
+    return oracle.cluster_k(k, w.k_base, w.k_max, w.iters, adaptive=True, init=w.init, seed=0, h=KH)
+
+
+def test_key_clustering_agrees_with_free_running_oracle(layer, oracle_keys):
     # Algorithm 1 on head 13 by the oracle from the same seeded start: stage
     # sizes, slot count, F and tau must match; labels agree up to drift after
     # near ties
     w, g, K = layer["w"], layer["g"], layer["K"]
-    h = 13
-    k = synth.as_f32(g["k"][0, h])
-    r = oracle.cluster_k(k, w.k_base, w.k_max, w.iters, adaptive=True, init=w.init, seed=0, h=h)
+    h = KH
+    r = oracle_keys
     st = K["stage_sizes"][0, h]
     st = st[st >= 0]
     print(f"stages gpu {st.tolist()} oracle {r['stage_u'].tolist()}; slots {int(K['n_clusters'][0, h])} "
@@ -164,3 +173,48 @@ def test_selection_sampled_rows(layer):
         bad, differ = selection_ok(gb[:, :ns], sel, Sc, sizes, scale, w.top_p)
         print(f"head {h}: sampled selection rows differing {differ}, violating {bad}")
         assert bad == 0
+
+
+WARM_ITERS = 2
+
+
+def test_warm_step_at_full_size(layer, oracle_keys):
+    # the next denoising step (inputs drifted as the generator's step 1) run from
+    # the cold state above (section 3.2.2): counts and flags kept, layouts and
+    # member means exact, and head 13's labels agree with the oracle's own warm
+    # step from its own cold clustering
+    w = layer["w"]
+    g1 = synth.generate(w, seed=0, step=1)
+    q1, k1, v1 = (dev(g1[t]) for t in "qkv")
+    Kc = layer["K"]
+    K = adc.cluster_k(k1, v1, w.k_base, w.k_max, WARM_ITERS, adaptive="warm",
+                      init_centroids=torch.from_numpy(Kc["centroids"]).cuda(),
+                      n_clusters=torch.from_numpy(Kc["n_clusters"]).cuda(),
+                      full=torch.from_numpy(Kc["full"]).cuda())
+    Q = adc.cluster_q(q1, w.q_clusters, WARM_ITERS, "caller",
+                      init_centroids=torch.from_numpy(layer["Q"]["centroids"]).cuda())
+    Kh = {n: host(t) for n, t in K.items() if torch.is_tensor(t) and n not in ("k_perm", "v_perm")}
+    Qh = {n: host(t) for n, t in Q.items() if torch.is_tensor(t)}
+    assert np.array_equal(Kh["n_clusters"], Kc["n_clusters"])
+    assert np.array_equal(Kh["full"], Kc["full"])
+    perm = K["perm"].long()
+    assert torch.equal(K["k_perm"], torch.gather(k1, 2, perm[..., None].expand_as(k1)))
+    assert torch.equal(K["v_perm"], torch.gather(v1, 2, perm[..., None].expand_as(v1)))
+    rng = np.random.default_rng(9)
+    for h in range(w.H):
+        ns = int(Kh["n_clusters"][0, h])
+        assert Kh["assign"][0, h].max() < ns
+        _check_layout(Kh["assign"][0, h], Kh["sizes"][0, h], Kh["offsets"][0, h], Kh["perm"][0, h],
+                      w.k_max)
+        _check_layout(Qh["assign"][0, h], Qh["sizes"][0, h], Qh["offsets"][0, h], Qh["perm"][0, h],
+                      w.q_clusters)
+    for h in HEADS:
+        kf = synth.as_f32(g1["k"][0, h])
+        lab = Kh["assign"][0, h]
+        for b in rng.choice(np.flatnonzero(Kh["sizes"][0, h]), 40, replace=False):
+            mem = np.flatnonzero(lab == b)
+            assert rel_l2(Kh["centroids"][0, h, b], kf[mem].astype(np.float64).mean(0)) <= 1e-5
+    r = oracle.cluster_k_warm(synth.as_f32(g1["k"][0, KH]), oracle_keys, WARM_ITERS)
+    agree = float((r["lab"] == Kh["assign"][0, KH]).mean())
+    print(f"warm k-label agreement with the oracle on head {KH}: {agree:.4f}")
+    assert agree >= 0.99

@@ -537,3 +537,58 @@ def test_layer_head_full_flag_gives_dense():
     assert r["K"]["full"] == 1
     ref, _ = _dense(q, k, v, 1 / 8)
     assert np.allclose(r["out"], ref, rtol=1e-6, atol=1e-6)
+
+
+# ----------------------------------------------------------------- warm start
+def test_warm_step_is_lloyd_from_the_previous_centres():
+    # one warm round = brute-force nearest previous centre, then member means
+    # (section 3.2.2: later steps keep the count and start from the old centres)
+    w = synth.scaled(synth.WORKLOADS["cog17k"], grid=(3, 12, 20), text_tokens=17)
+    k0 = synth.as_f32(synth.generate(w, heads=[1])["k"][0, 0])
+    k1 = synth.as_f32(synth.generate(w, heads=[1], step=1)["k"][0, 0])
+    cold = oracle.cluster_k(k0, 16, 64, 5, adaptive=True, init="sample", h=1)
+    m = cold["n_slots"]
+    r = oracle.cluster_k_warm(k1, cold, 1)
+    assert r["n_slots"] == m and r["full"] == cold["full"] and r["tau"] == cold["tau"]
+    d2 = _brute_d2(k1, cold["cent"][:m])
+    lab = np.argmin(d2, axis=1)          # argmin keeps the lowest index on ties
+    assert np.array_equal(r["lab"], lab)
+    sizes = np.bincount(lab, minlength=m)
+    assert np.array_equal(r["sizes"][:m], sizes)
+    assert np.all(r["sizes"][m:] == 0)
+    for j in range(m):
+        want = k1[lab == j].astype(np.float64).mean(0) if sizes[j] else cold["cent"][j]
+        assert np.allclose(r["cent"][j], want, rtol=0, atol=1e-6)
+    _check_perm(r["perm"], r["off"], lab, m)
+
+
+def test_warm_step_keeps_a_converged_clustering():
+    # at a fixed point of Lloyd's map, warm rounds on the same keys change nothing
+    rng = np.random.default_rng(41)
+    k = rng.standard_normal((600, 64)).astype(np.float32)
+    cent, lab, _, _ = oracle.kmeans(k, 12, 200, init="sample", strm=oracle.stream(3, 2, 0, 0, 0))
+    cent2, lab2, _, _ = oracle.kmeans(k, 12, 1, init="caller", init_cent=cent)
+    assert np.array_equal(lab, lab2)          # converged within 200 rounds
+    prev = dict(n_slots=12, full=0, tau=0.0, cent=np.vstack([cent, np.zeros((4, 64), np.float32)]))
+    r = oracle.cluster_k_warm(k, prev, 3)
+    assert np.array_equal(r["lab"], lab)
+    assert np.array_equal(r["cent"][:12], cent)
+
+
+def test_denoising_steps_of_the_generator():
+    w = synth.scaled(synth.WORKLOADS["cog17k"], grid=(2, 10, 12), text_tokens=9)
+    g0 = synth.generate(w, heads=[0, 1])
+    assert all(np.array_equal(g0[t], synth.generate(w, heads=[0, 1], step=0)[t]) for t in "qkv")
+    g1 = synth.generate(w, heads=[0, 1], step=1)
+    for t in "qkv":
+        assert np.array_equal(g0[t][:, :, :9], g1[t][:, :, :9])      # text tokens fixed
+        a, b = synth.as_f32(g0[t][:, :, 9:]), synth.as_f32(g1[t][:, :, 9:])
+        rel = np.linalg.norm(a - b) / np.linalg.norm(a)
+        assert 0.01 < rel < 0.5                                     # small but real drift
+    # with no drift two steps differ by fresh noise only: the difference has the
+    # statistics of the difference of two N(0, 0.1^2) draws (bf16 rounding aside)
+    w32 = synth.scaled(w, dtype="f32")
+    a = synth.generate(w32, heads=[0], step=0)["k"][0, 0, 9:]
+    b = synth.generate(w32, heads=[0], step=3, drift=0.0)["k"][0, 0, 9:]
+    assert abs(np.std(a - b) - 0.1 * np.sqrt(2.0)) < 0.005
+    assert abs(np.mean(a - b)) < 0.005
