@@ -46,6 +46,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense comparisons")
     ap.add_argument("--no-spread", action="store_true",
                     help="skip the latency/density spread over seeds 1 and 2")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the 65-q-cluster / top-k / centroid-score variants")
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the warm-start steady-state steps (drifted inputs)")
     ap.add_argument("--profile-steps", action="store_true",
@@ -175,6 +177,11 @@ def main():
 
     if not args.no_dense:
         result["dense"] = dense_compare(torch, adc, q, k, v, w, dev, stream)
+
+    if not args.no_variants:
+        bits = np.unpackbits(S["mask"].cpu().numpy().view(np.uint8), bitorder="little")
+        mean_slots = float(bits.sum()) / (w.B * w.H * w.q_clusters)
+        result["variants"] = variants(torch, adc, w, cfg, q, k, v, stream, args.seed, mean_slots)
 
     if not args.no_warm:
         result["warm_steady_state"] = warm_steady_state(
@@ -306,6 +313,45 @@ def warm_steady_state(torch, adc, synth, w, cfg, dev, stream, cold, q0, k0, v0, 
         }
         log(f"warm steady state, {wi} Lloyd round(s): {res[f'lloyd_iters_{wi}']}")
     del steps
+    return res
+
+
+def variants(torch, adc, w, cfg, q, k, v, stream, seed, mean_slots, steps=5):
+    """Cold-layer latency under the pages' other settings: 65 query clusters
+    (section 4.1), the argtopk rule of Algorithm 3 step 7 with k equal to the
+    mean number of slots top-p selected above, and the centroid score of the
+    prior clustering method (section 2.3)."""
+    top_k = max(1, int(round(mean_slots)))
+    settings = {"q_clusters_65": dict(cq=65, score="quest", rule="topp"),
+                f"topk_{top_k}": dict(cq=cfg.q_clusters, score="quest", rule="topk"),
+                "centroid_score": dict(cq=cfg.q_clusters, score="centroid", rule="topp")}
+    res = {"topk_k": top_k}
+    for name, st in settings.items():
+        rows = []
+        for i in range(2 + steps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            ev[0].record(stream)
+            Q = adc.cluster_q(q, st["cq"], cfg.iters, cfg.init, seed)
+            ev[1].record(stream)
+            K = adc.cluster_k(k, v, cfg.k_base, cfg.k_max, cfg.iters, cfg.tau_mult, cfg.adaptive,
+                              cfg.init, seed)
+            ev[2].record(stream)
+            S = adc.select(Q["qrep"], K, cfg.top_p, score=st["score"], rule=st["rule"], top_k=top_k)
+            ev[3].record(stream)
+            adc.sparse_attn(q, Q["perm"], Q["offsets"], K["k_perm"], K["v_perm"], K["offsets"],
+                            S["mask"], want_lse=False)
+            ev[4].record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                rows.append([ev[j].elapsed_time(ev[j + 1]) for j in range(4)])
+        pairs = float((Q["sizes"].double() * S["sel_keys"].double()).sum().item())
+        res[name] = {"layer_ms_median": round(float(np.median([sum(r) for r in rows])), 4),
+                     "stages_ms_median": {n: round(float(np.median([r[j] for r in rows])), 4)
+                                          for j, n in enumerate(["cluster_q", "cluster_k", "select",
+                                                                 "sparse_attn"])},
+                     "density": round(pairs / (w.B * w.H * float(w.N) ** 2), 5)}
+        log(f"variant {name}: {res[name]}")
+        del Q, K, S
     return res
 
 

@@ -65,5 +65,21 @@ def selection_ok(gpu_bits, sel, S, sizes, scale, p):
     return bad, differ
 
 
+def topk_ok(gpu_bits, ora_bits, S, tol=NEAR_TIE):
+    """Per row: the top-k sets may differ only in slots whose oracle score is
+    within tol * max(1, |s|) of the row's cut (the k-th largest score), with the
+    same set size. Returns (rows violating, rows differing)."""
+    bad = differ = 0
+    for a in range(gpu_bits.shape[0]):
+        G, O = gpu_bits[a], ora_bits[a]
+        if np.array_equal(G, O):
+            continue
+        differ += 1
+        cut = S[a][O].min()
+        near = np.abs(S[a] - cut) <= tol * max(1.0, abs(cut))
+        bad += int(G.sum() != O.sum() or not np.all(near[G != O]))
+    return bad, differ
+
+
 def small_workload(name, **kw):
     return synth.scaled(synth.WORKLOADS[name], **kw)
