@@ -80,6 +80,7 @@ def lib():
                                        f64, f32p, f32p]),
             "orc_sparse_attn_q": (None, [f32p, i64, i32p, f32p, f32p, i64, i32, i32p, i32, i32,
                                          u32p, f64, f32p, f32p]),
+            "orc_compactness": (None, [f32p, i64, i32, i32p, f32p, i32, f64p, f64p, f64p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -261,6 +262,24 @@ def cluster_k_warm(k, prev, iters):
     r["full"] = prev["full"]
     r["tau"] = prev["tau"]
     return r
+
+
+def compactness(x, lab, cent):
+    """MSE, average intra-cluster distance and Davies-Bouldin index of one
+    head's clustering (section 3.2.1, Fig. 10; readings in the C source)."""
+    x, cent = _f32(x), _f32(cent)
+    n, d = x.shape
+    lab = np.ascontiguousarray(lab, dtype=np.int32)
+    out = np.zeros(3, np.float64)
+    lib().orc_compactness(_ptr(x, ctypes.c_float), n, d, _ptr(lab, ctypes.c_int32),
+                          _ptr(cent, ctypes.c_float), cent.shape[0], _ptr(out[0:], ctypes.c_double),
+                          _ptr(out[1:], ctypes.c_double), _ptr(out[2:], ctypes.c_double))
+    return dict(mse=float(out[0]), mean_dist=float(out[1]), db=float(out[2]))
+
+
+def layer_compactness(mses):
+    """Comp_l = 1 / (mean of the heads' MSE) (section 3.2.1)."""
+    return 1.0 / float(np.mean(mses))
 
 
 def quest_scores(qrep, kmax, kmin, ksizes):

@@ -12,6 +12,7 @@
  *   section 4.1 "Platform and configurations"  tau = 1.5 x mean distance
  *   section 3.2.3, Eq. (1)               Quest upper-bound score
  *   Algorithm 3 steps 3-9                 selection and attention over K*, V*
+ *   section 3.2.1 and Fig. 10             compactness diagnostics
  * Readings where the paper is silent or garbled are listed beside each step.
  *
  * Arithmetic: tensors are float32; every distance, sum, softmax denominator and
@@ -592,4 +593,58 @@ void orc_sparse_attn(const float* q, const float* k, const float* v, int64_t n, 
                      const int32_t* qlab, const int32_t* klab, int cq, int ck,
                      const uint32_t* mask, double scale, float* out, float* lse) {
     orc_sparse_attn_q(q, n, qlab, k, v, n, d, klab, cq, ck, mask, scale, out, lse);
+}
+
+/* ---------------------------------------------------------------- compactness
+ * Section 3.2.1 measures how tight the key clusters of a head are by the mean
+ * squared reconstruction error MSE = (1/N) sum_i ||k_i - c(k_i)||^2; a layer's
+ * compactness is Comp = 1 / (mean of its heads' MSE). Fig. 10 adds the average
+ * intra-cluster distance and the Davies-Bouldin index; the pages give neither
+ * formula, so the readings are:
+ *   mean_dist = (1/N) sum_i ||k_i - c(k_i)||  (the distance tau is built from),
+ *   DB (Davies & Bouldin 1979) over the clusters with members:
+ *     s_a = mean distance of a's members to c_a,
+ *     DB  = (1/K) sum_a max_{b != a} (s_a + s_b) / ||c_a - c_b||,
+ *   where a pair whose centres coincide is left out of the max (a cluster with
+ *   no such partner scores 0), and DB = 0 when fewer than two clusters have
+ *   members. c is the centre array handed in (slot lab[i] of cent).
+ * Outputs: mse, mean_dist, db (double). */
+void orc_compactness(const float* x, int64_t n, int d, const int32_t* lab, const float* cent,
+                     int m, double* mse, double* mean_dist, double* db) {
+    double* s = (double*)calloc((size_t)m, sizeof(double));
+    int64_t* cnt = (int64_t*)calloc((size_t)m, sizeof(int64_t));
+    double sq = 0.0, dist = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double v = sq_dist(x + i * d, cent + (size_t)lab[i] * d, d);
+        sq += v;
+        dist += sqrt(v);
+        s[lab[i]] += sqrt(v);
+        cnt[lab[i]] += 1;
+    }
+    *mse = n > 0 ? sq / (double)n : 0.0;
+    *mean_dist = n > 0 ? dist / (double)n : 0.0;
+    int k = 0;
+    for (int a = 0; a < m; ++a)
+        if (cnt[a] > 0) {
+            s[a] /= (double)cnt[a];
+            ++k;
+        }
+    double* best = (double*)calloc((size_t)m, sizeof(double));
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int a = 0; a < m; ++a) {
+        if (cnt[a] == 0) continue;
+        double mx = 0.0;
+        for (int b = 0; b < m; ++b) {
+            if (b == a || cnt[b] == 0) continue;
+            double dab = sqrt(sq_dist(cent + (size_t)a * d, cent + (size_t)b * d, d));
+            if (dab == 0.0) continue;
+            double r = (s[a] + s[b]) / dab;
+            if (r > mx) mx = r;
+        }
+        best[a] = mx;
+    }
+    double acc = 0.0;
+    for (int a = 0; a < m; ++a) acc += best[a];
+    *db = k >= 2 ? acc / (double)k : 0.0;
+    free(best); free(s); free(cnt);
 }

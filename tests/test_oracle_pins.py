@@ -592,3 +592,68 @@ def test_denoising_steps_of_the_generator():
     b = synth.generate(w32, heads=[0], step=3, drift=0.0)["k"][0, 0, 9:]
     assert abs(np.std(a - b) - 0.1 * np.sqrt(2.0)) < 0.005
     assert abs(np.mean(a - b)) < 0.005
+
+
+# ----------------------------------------------------------------- compactness
+def test_compactness_hand_case():
+    # 1-D pairs {0, 2} and {10, 12}: every member is 1 from its centre, centres 10 apart
+    x = np.zeros((4, 64), np.float32)
+    x[:, 0] = [0, 2, 10, 12]
+    cent = np.zeros((3, 64), np.float32)
+    cent[0, 0], cent[2, 0] = 1, 11          # slot 1 holds no members
+    r = oracle.compactness(x, np.array([0, 0, 2, 2]), cent)
+    assert r["mse"] == 1.0 and r["mean_dist"] == 1.0
+    assert r["db"] == pytest.approx((1 + 1) / 10, rel=1e-15)
+    assert oracle.layer_compactness([r["mse"], 3.0]) == 0.5
+
+
+def test_davies_bouldin_equals_library_routine():
+    from sklearn.metrics import davies_bouldin_score
+    rng = np.random.default_rng(23)
+    for trial in range(4):
+        m, n, d = 9, 400, 64
+        x = (rng.standard_normal((n, d)) + 4 * rng.standard_normal((m, d))[rng.integers(0, m, n)])
+        x = x.astype(np.float32)
+        lab = rng.integers(0, m, n).astype(np.int32) if trial == 0 else \
+            np.argmin(_brute_d2(x, x[:m]), axis=1).astype(np.int32)
+        lab[lab == 4] = 5                    # leave a hole: slot 4 holds no members
+        cent = np.zeros((m, d), np.float32)
+        for a in np.unique(lab):
+            cent[a] = x[lab == a].astype(np.float64).mean(0)
+        r = oracle.compactness(x, lab, cent)
+        assert r["db"] == pytest.approx(davies_bouldin_score(x.astype(np.float64), lab), rel=1e-6)
+
+
+def test_mse_and_mean_distance_brute_force_and_total_variance():
+    rng = np.random.default_rng(24)
+    x = rng.standard_normal((300, 64)).astype(np.float32)
+    cent = rng.standard_normal((7, 64)).astype(np.float32)
+    lab = rng.integers(0, 7, 300).astype(np.int32)
+    r = oracle.compactness(x, lab, cent)
+    diff = x.astype(np.float64) - cent[lab].astype(np.float64)
+    assert r["mse"] == pytest.approx((diff ** 2).sum(1).mean(), rel=1e-12)
+    assert r["mean_dist"] == pytest.approx(np.sqrt((diff ** 2).sum(1)).mean(), rel=1e-12)
+    # one cluster at the mean: MSE is the total variance; one cluster -> DB = 0
+    mean = x.astype(np.float64).mean(0).astype(np.float32)
+    r1 = oracle.compactness(x, np.zeros(300, np.int32), mean[None])
+    assert r1["mse"] == pytest.approx(x.astype(np.float64).var(0).sum(), rel=1e-6)
+    assert r1["db"] == 0.0
+
+
+def test_davies_bouldin_skips_coincident_centres():
+    x = np.zeros((4, 64), np.float32)
+    x[:, 0] = [-1, 1, -2, 2]                 # both clusters centred at 0
+    cent = np.zeros((2, 64), np.float32)
+    r = oracle.compactness(x, np.array([0, 0, 1, 1]), cent)
+    assert r["db"] == 0.0 and r["mean_dist"] == 1.5
+
+
+def test_tau_is_1p5_times_stage0_mean_distance():
+    # the threshold of section 4.1 is 1.5 x the average intra-cluster distance
+    # of the stage-0 clustering
+    w = synth.scaled(synth.WORKLOADS["cog17k"], grid=(3, 16, 20), text_tokens=10)
+    k = synth.as_f32(synth.generate(w, heads=[0])["k"][0, 0])
+    r = oracle.cluster_k(k, 24, 96, 5, adaptive=True, init="sample", seed=0)
+    cent0, lab0, _, _ = oracle.kmeans(k, 24, 5, init="sample", strm=oracle.stream(0, 2, 0, 0, 0))
+    c = oracle.compactness(k, lab0, cent0)
+    assert r["tau"] == pytest.approx(1.5 * c["mean_dist"], rel=1e-12)
