@@ -73,6 +73,8 @@ _SIGS = {
     "adacluster_assign": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "adacluster_permute_workspace": (_SZ, [_VP, _I32]),
     "adacluster_permute": (_I32, [_VP, _I32] + [_VP] * 11 + [_VP, _SZ, _VP]),
+    "adacluster_compactness_workspace": (_SZ, [_VP, _I32]),
+    "adacluster_compactness": (_I32, [_VP, _I32] + [_VP] * 7 + [_VP, _SZ, _VP]),
 }
 
 
@@ -303,6 +305,26 @@ def permute(labels, M, x, v=None):
                                     _p(out["means"]), _p(out["xmax"]), _p(out["xmin"]),
                                     _p(out["x_perm"]), _p(out["v_perm"]), _p(ws), ws.numel(),
                                     _stream(dev)))
+    return out
+
+
+def compactness(x_perm, offsets, centroids, want_comp=True):
+    """Compactness of a clustering given in cluster order (e.g. the `k_perm`,
+    `offsets` and `centroids` of cluster_k): per-head MSE, mean distance to the
+    centre and Davies-Bouldin index ([B,H] f64), and Comp ([B] f64)."""
+    sh = _shape(x_perm)
+    B, H, N, D = x_perm.shape
+    M = centroids.shape[2]
+    dev = x_perm.device
+    if tuple(offsets.shape) != (B, H, M + 1) or tuple(centroids.shape) != (B, H, M, D):
+        raise ValueError("offsets must be [B,H,M+1] and centroids [B,H,M,D]")
+    out = {n: torch.empty(B, H, dtype=torch.float64, device=dev) for n in ("mse", "mean_dist", "db")}
+    out["comp"] = torch.empty(B, dtype=torch.float64, device=dev) if want_comp else None
+    ws = _workspace(lib().adacluster_compactness_workspace(ctypes.byref(sh), M), dev)
+    _check(lib().adacluster_compactness(ctypes.byref(sh), M, _p(x_perm),
+                                        _p(offsets.contiguous()), _p(centroids.contiguous().float()),
+                                        _p(out["mse"]), _p(out["mean_dist"]), _p(out["db"]),
+                                        _p(out["comp"]), _p(ws), ws.numel(), _stream(dev)))
     return out
 
 

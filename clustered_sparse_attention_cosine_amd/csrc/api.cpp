@@ -599,4 +599,40 @@ int32_t adacluster_permute(const adc_shape* shape, int32_t M, const int32_t* ass
     return ADC_OK;
 }
 
+// ====================================================================== diagnostics
+size_t adacluster_compactness_workspace(const adc_shape* shape, int32_t M) {
+    if (check_shape(shape) || check_clusters("M", M)) return 0;
+    Carver c(nullptr);
+    const size_t n = (size_t)shape->B * shape->H * M;
+    c.take<double>(n);
+    c.take<double>(n);
+    c.take<float>(n);
+    c.take<float>(n);
+    return c.used + 256;
+}
+
+int32_t adacluster_compactness(const adc_shape* shape, int32_t M, const void* x_perm,
+                               const int32_t* offsets, const float* centroids, double* mse,
+                               double* mean_dist, double* db, double* comp, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    int32_t st = check_shape(shape);
+    if (st) return st;
+    if ((st = check_clusters("M", M))) return st;
+    REQ(x_perm); REQ(offsets); REQ(centroids); REQ(mse); REQ(mean_dist); REQ(db); REQ(workspace);
+    const size_t need = adacluster_compactness_workspace(shape, M);
+    if (workspace_bytes < need)
+        return fail(ADC_EWORKSPACE, "workspace of %zu bytes is below the %zu required", workspace_bytes, need);
+    hipStream_t s = (hipStream_t)stream;
+    Prob p = make_prob(shape);
+    Carver c(workspace);
+    const size_t n = (size_t)p.BH * M;
+    double* csq = c.take<double>(n);
+    double* cdist = c.take<double>(n);
+    float* smean = c.take<float>(n);
+    float* dbmax = c.take<float>(n);
+    HIPCHK(launch_compactness(p, M, x_perm, offsets, centroids, csq, cdist, smean, dbmax, mse,
+                              mean_dist, db, comp, s));
+    return ADC_OK;
+}
+
 }  // extern "C"

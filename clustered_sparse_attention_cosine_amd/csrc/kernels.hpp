@@ -122,6 +122,16 @@ hipError_t launch_stage_end(const Prob& p, StageState st, int t_total, int nmax,
                             int32_t* n_clusters, uint8_t* full_out, float* tau_out,
                             hipStream_t s);
 
+// ---------------------------------------------------------------- diagnostics (diag.hip)
+// Per head: MSE, mean distance to the centre and Davies-Bouldin index of a
+// clustering given as cluster-contiguous rows x_perm with offsets ([BH][M+1])
+// and centres cent ([BH][M][D]); comp[b] = 1 / mean over heads of MSE (may be
+// null). Scratch: csq, cdist [BH][M] f64; smean, dbmax [BH][M] f32.
+hipError_t launch_compactness(const Prob& p, int M, const void* x_perm, const int32_t* offsets,
+                              const float* cent, double* csq, double* cdist, float* smean,
+                              float* dbmax, double* mse, double* mean_dist, double* db,
+                              double* comp, hipStream_t s);
+
 // ---------------------------------------------------------------- layout (permute.hip)
 hipError_t launch_histogram(const Prob& p, const int32_t* labels, int M, int32_t* cnt,
                             hipStream_t s);

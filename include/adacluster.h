@@ -8,7 +8,9 @@
  *   adacluster_cluster_k    section 3.2.2, Algorithm 1, and section 4.1 (tau)
  *   adacluster_select       section 3.2.3 Eq. (1)/(2) and Algorithm 3 step 7
  *   adacluster_sparse_attn  Algorithm 3 steps 3-9
- * plus helpers that expose single steps (adacluster_assign, adacluster_permute).
+ * plus helpers that expose single steps (adacluster_assign, adacluster_permute)
+ * and the compactness diagnostics of section 3.2.1 / Fig. 10
+ * (adacluster_compactness).
  *
  * Conventions shared by every entry point
  *   - Tensor pointers are DEVICE pointers to contiguous row-major arrays; the
@@ -260,6 +262,34 @@ int32_t adacluster_permute(const adc_shape* shape, int32_t M, const int32_t* ass
                            int32_t* perm, float* means, void* xmax, void* xmin,
                            void* x_perm, void* v_perm, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Diagnostics: how compact a clustering is (section 3.2.1, where the mean
+ * squared reconstruction error of each head and the layer score Comp = 1 / the
+ * heads' mean MSE drive the case for per-layer cluster counts; Fig. 10, which
+ * compares the average intra-cluster distance and the Davies-Bouldin index).
+ * Per head, with c(i) the centre of row i's cluster and only clusters that
+ * have members taking part:
+ *   mse       = (1/N) sum_i ||x_i - c(i)||^2
+ *   mean_dist = (1/N) sum_i ||x_i - c(i)||
+ *   db        = (1/K) sum_a max_{b != a, c_b != c_a} (s_a + s_b) / ||c_a - c_b||
+ *               with s_a the mean member distance to c_a and K the number of
+ *               clusters with members; a cluster with no partner scores 0, and
+ *               db = 0 when K < 2 (Davies & Bouldin's index)
+ *   comp[b]   = 1 / (mean over the H heads of mse)
+ * Inputs are the cluster-contiguous rows and offsets the clusterings write:
+ *   x_perm    [B,H,N,D] dtype    rows in cluster order (k_perm of cluster_k)
+ *   offsets   [B,H,M+1] int32    cluster starts; must be non-decreasing, 0..N
+ *   centroids [B,H,M,D] f32      the centres c
+ *   mse, mean_dist, db [B,H] f64 out;  comp [B] f64 out or NULL
+ * Row distances are formed in f32 and summed in f64 in a fixed order (the
+ * result does not depend on scheduling); centre distances are f32.
+ */
+size_t adacluster_compactness_workspace(const adc_shape* shape, int32_t M);
+int32_t adacluster_compactness(const adc_shape* shape, int32_t M, const void* x_perm,
+                               const int32_t* offsets, const float* centroids, double* mse,
+                               double* mean_dist, double* db, double* comp, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

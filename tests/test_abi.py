@@ -15,6 +15,7 @@ EXPECTED = {
     "adacluster_sparse_attn_workspace", "adacluster_sparse_attn",
     "adacluster_assign_workspace", "adacluster_assign",
     "adacluster_permute_workspace", "adacluster_permute",
+    "adacluster_compactness_workspace", "adacluster_compactness",
 }
 
 

@@ -218,3 +218,27 @@ def test_warm_step_at_full_size(layer, oracle_keys):
     agree = float((r["lab"] == Kh["assign"][0, KH]).mean())
     print(f"warm k-label agreement with the oracle on head {KH}: {agree:.4f}")
     assert agree >= 0.99
+
+
+def test_compactness_at_full_size(layer, oracle_keys):
+    # the oracle's own clustering of head 13 through the HIP diagnostics, and
+    # properties of the layer's clustering: 0 <= mean_dist^2 <= mse (Jensen)
+    w, g = layer["w"], layer["g"]
+    k = synth.as_f32(g["k"][0, KH])
+    r = oracle_keys
+    ref = oracle.compactness(k, r["lab"], r["cent"])
+    perm, off = oracle.permute(r["lab"], w.k_max)
+    kb = g["k"][0, KH][perm][None, None]
+    out = adc.compactness(dev(kb), dev(off[None, None]), dev(r["cent"][None, None]))
+    got = {n: float(host(out[n])[0, 0]) for n in ("mse", "mean_dist", "db")}
+    print(f"head {KH}: gpu {got} oracle {ref}")
+    assert got["mse"] == pytest.approx(ref["mse"], rel=1e-5)
+    assert got["mean_dist"] == pytest.approx(ref["mean_dist"], rel=1e-5)
+    assert got["db"] == pytest.approx(ref["db"], rel=1e-4)
+    K = layer["K"]
+    res = adc.compactness(dev(np.ascontiguousarray(np.take_along_axis(
+        g["k"], K["perm"][..., None].astype(np.int64), axis=2))), dev(K["offsets"]),
+        dev(K["centroids"]))
+    mse, md, db = (host(res[n])[0] for n in ("mse", "mean_dist", "db"))
+    assert np.all(md > 0) and np.all(md ** 2 <= mse * (1 + 1e-6)) and np.all(db > 0)
+    assert float(host(res["comp"])[0]) == pytest.approx(1.0 / mse.mean(), rel=1e-12)
