@@ -254,8 +254,11 @@ def warm_steady_state(torch, adc, synth, w, cfg, dev, stream, cold, q0, k0, v0, 
     generator's steps 1..n_steps), both clusterings start from the previous
     step's centres and the keys keep their per-head counts and flags. Each chain
     (cold step on step 0, then the warm steps) runs twice; the second is timed.
-    Reports the warm-step latency and the latency amortised over the model's
-    denoising schedule (30 steps for HunyuanVideo, 50 otherwise)."""
+    Reports the warm-step latency, the latency amortised over the model's
+    denoising schedule (30 steps for HunyuanVideo, 50 otherwise), and the key
+    clusterings' compactness (mean MSE and Davies-Bouldin index over heads, the
+    diagnostics of section 3.2.1 and Fig. 10) beside a cold clustering of the
+    last step."""
     t0 = time.time()
     steps = []
     for s in range(1, n_steps + 1):
@@ -298,8 +301,11 @@ def warm_steady_state(torch, adc, synth, w, cfg, dev, stream, cold, q0, k0, v0, 
                 prev = dict(Q=Q, K=K)
                 torch.cuda.synchronize()
                 pairs = float((Q["sizes"].double() * S["sel_keys"].double()).sum().item())
+                C = adc.compactness(K["k_perm"], K["offsets"], K["centroids"])
                 rows.append(dict(t=[ev[i].elapsed_time(ev[i + 1]) for i in range(4)],
-                                 density=pairs / (w.B * w.H * float(w.N) ** 2)))
+                                 density=pairs / (w.B * w.H * float(w.N) ** 2),
+                                 key_mse=float(C["mse"].mean().item()),
+                                 key_db=float(C["db"].mean().item())))
         warm = rows[1:]
         layer = [sum(r["t"]) for r in warm]
         wm = float(np.median(layer))
@@ -309,10 +315,29 @@ def warm_steady_state(torch, adc, synth, w, cfg, dev, stream, cold, q0, k0, v0, 
             "stages_ms_median": {n: round(float(np.median([r["t"][i] for r in warm])), 4)
                                  for i, n in enumerate(names)},
             "density_per_step": [round(r["density"], 5) for r in warm],
+            "key_mse_per_step": [round(r["key_mse"], 5) for r in warm],
+            "key_db_per_step": [round(r["key_db"], 5) for r in warm],
             "amortized_layer_ms": round((cold + (total_steps - 1) * wm) / total_steps, 4),
         }
         log(f"warm steady state, {wi} Lloyd round(s): {res[f'lloyd_iters_{wi}']}")
-    del steps
+    # a cold clustering of the last drifted step, for the compactness comparison,
+    # and the cost of the diagnostic itself
+    q, k, v = steps[-1]
+    K = adc.cluster_k(k, v, cfg.k_base, cfg.k_max, cfg.iters, cfg.tau_mult, cfg.adaptive,
+                      cfg.init, seed)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    adc.compactness(K["k_perm"], K["offsets"], K["centroids"])
+    ev[0].record(stream)
+    C = adc.compactness(K["k_perm"], K["offsets"], K["centroids"])
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    res["cold_last_step"] = {"key_mse": round(float(C["mse"].mean().item()), 5),
+                             "key_db": round(float(C["db"].mean().item()), 5),
+                             "comp": round(float(C["comp"][0].item()), 6)}
+    res["compactness_ms"] = round(ev[0].elapsed_time(ev[1]), 4)
+    log(f"cold clustering of step {n_steps}: {res['cold_last_step']}, "
+        f"diagnostic {res['compactness_ms']} ms")
+    del steps, K, C
     return res
 
 
