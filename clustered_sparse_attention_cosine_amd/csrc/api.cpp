@@ -465,9 +465,7 @@ struct AttnWs {
     int32_t* run_start;
     int32_t* run_pos;
     int32_t* n_runs;
-    int32_t* items;
-    int32_t* n_items;
-    int32_t* head_pos;  // items before each head (BH + 1 entries)
+    AttnSched sched;
     uint16_t* planes[4];     // 16-bit operand planes: V fp16 (bf16 inputs); K hi, K lo, V hi, V lo (f32)
 };
 
@@ -478,9 +476,15 @@ static void plan_attn(Carver& c, const adc_shape* shape, int32_t Cq, int32_t Ck,
     w.run_start = c.take<int32_t>(rows * w.run_cap);
     w.run_pos = c.take<int32_t>(rows * (w.run_cap + 1));
     w.n_runs = c.take<int32_t>(rows);
-    w.items = c.take<int32_t>((size_t)shape->B * shape->H * w.cap);
-    w.n_items = c.take<int32_t>((size_t)shape->B * shape->H);
-    w.head_pos = c.take<int32_t>((size_t)shape->B * shape->H + 1);
+    const size_t BH = (size_t)shape->B * shape->H;
+    w.sched.items = c.take<int32_t>(BH * w.cap);
+    w.sched.n_items = c.take<int32_t>(BH);
+    w.sched.cost_pre = c.take<uint32_t>(BH * w.cap);
+    w.sched.n_cost = c.take<uint32_t>(BH);
+    w.sched.head_pos = c.take<int32_t>(BH + 1);
+    w.sched.head_cost = c.take<uint64_t>(BH + 1);
+    w.sched.xcd_start = c.take<int32_t>(9);
+    w.sched.xcd_ctr = c.take<int32_t>(8);
     const size_t elems = (size_t)shape->B * shape->H * shape->N * shape->D;
     for (int i = 0; i < 4; ++i) w.planes[i] = nullptr;
     if (shape->dtype == ADC_BF16) {
@@ -520,13 +524,12 @@ int32_t adacluster_sparse_attn(const adc_shape* shape, int32_t Cq, int32_t Ck, c
     AttnWs w;
     plan_attn(c, shape, Cq, Ck, w);
     HIPCHK(launch_build_runs(p, Cq, Ck, k_offsets, sel_mask, w.run_cap, w.run_start, w.run_pos, w.n_runs, s));
-    HIPCHK(launch_worklist(p, Cq, w.cap, q_offsets, w.items, w.n_items, w.head_pos, s));
+    HIPCHK(launch_worklist(p, Cq, w.cap, q_offsets, w.run_pos, w.n_runs, w.run_cap, w.sched, s));
     HIPCHK(launch_planes(p, k_perm, v_perm, w.planes[0], w.planes[1], w.planes[2], w.planes[3], s));
     const uint16_t* k0 = p.bf16 ? (const uint16_t*)k_perm : w.planes[0];
     HIPCHK(launch_attention(p, Cq, q, q_perm, q_offsets, k0, w.planes[1], w.planes[2], w.planes[3],
-                            w.run_start, w.run_pos, w.n_runs, w.run_cap, w.items, w.head_pos,
-                            w.cap, scale, out,
-                            out_dtype == ADC_F32, lse, s));
+                            w.run_start, w.run_pos, w.n_runs, w.run_cap, w.sched, w.cap, scale,
+                            out, out_dtype == ADC_F32, lse, s));
     return ADC_OK;
 }
 

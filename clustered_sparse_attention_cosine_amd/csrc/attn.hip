@@ -12,6 +12,7 @@
 // S^T = K Q^T with 16x16x32 bf16 MFMAs so that a lane owns one query column,
 // the output as O^T += V^T P^T reusing the score registers as the B operand.
 #include <math.h>
+#include <algorithm>
 #include <type_traits>
 #include "common.hpp"
 #include "kernels.hpp"
@@ -70,70 +71,178 @@ hipError_t launch_build_runs(const Prob& p, int Cq, int Ck, const int32_t* k_off
 // ------------------------------------------------------------------ work list
 // Work items (q-cluster a, chunk c of ATTN_ROWS rows) of head bh are written in
 // q-cluster order to items[bh * cap ...] (cap = Cq + ceil(N / ATTN_ROWS) bounds
-// their number), one workgroup per head. Launching the attention grid over
-// heads in order keeps the workgroups in flight on one or two heads at a time,
-// so their K'/V' stay in the last-level cache.
+// their number), one workgroup per head, with the inclusive prefix of their
+// estimated cost within the head. An item's cost is its number of 64-key tiles
+// times (4 + its live waves): the time per tile of a work item grows by about a
+// quarter of its 4-wave value per 16-row wave of query rows (measured on
+// uniform synthetic layouts).
+__device__ __forceinline__ uint32_t item_cost(int tiles, int rows) {
+    return (uint32_t)tiles * (uint32_t)(4 + (min(rows, ATTN_ROWS) + 15) / 16);
+}
+
 __global__ __launch_bounds__(256) void worklist_kernel(int Cq, int cap,
                                                        const int32_t* __restrict__ q_offsets,
-                                                       int32_t* __restrict__ items,
-                                                       int32_t* __restrict__ n_items) {
+                                                       const int32_t* __restrict__ run_pos,
+                                                       const int32_t* __restrict__ n_runs,
+                                                       int run_cap, int32_t* __restrict__ items,
+                                                       int32_t* __restrict__ n_items,
+                                                       uint32_t* __restrict__ cost_pre,
+                                                       uint32_t* __restrict__ n_cost) {
     __shared__ int wsum[4];
+    __shared__ uint32_t wcost[4];
     const int bh = blockIdx.x;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int32_t* qo = q_offsets + (int64_t)bh * (Cq + 1);
     int32_t* out = items + (int64_t)bh * cap;
+    uint32_t* cout = cost_pre + (int64_t)bh * cap;
     int running = 0;
+    uint32_t running_cost = 0;
     for (int base = 0; base < Cq; base += 256) {
         const int a = base + tid;
-        const int ch = a < Cq ? (qo[a + 1] - qo[a] + ATTN_ROWS - 1) / ATTN_ROWS : 0;
+        const int rows = a < Cq ? qo[a + 1] - qo[a] : 0;
+        const int ch = (rows + ATTN_ROWS - 1) / ATTN_ROWS;
+        int tiles = 0;
+        if (ch > 0) {
+            const int64_t row = (int64_t)bh * Cq + a;
+            tiles = (run_pos[row * (run_cap + 1) + n_runs[row]] + 63) / 64;
+        }
+        uint32_t cq = 0;
+        for (int c = 0; c < ch; ++c) cq += item_cost(tiles, rows - c * ATTN_ROWS);
         int incl = ch;
+        uint32_t cincl = cq;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const int v = __shfl_up(incl, o);
-            if (l >= o) incl += v;
+            const uint32_t vc = __shfl_up(cincl, o);
+            if (l >= o) {
+                incl += v;
+                cincl += vc;
+            }
         }
-        if (l == 63) wsum[w] = incl;
+        if (l == 63) {
+            wsum[w] = incl;
+            wcost[w] = cincl;
+        }
         __syncthreads();
         int before = running + incl - ch;
-        for (int i = 0; i < w; ++i) before += wsum[i];
-        for (int c = 0; c < ch; ++c) out[before + c] = a | (c << 16);
+        uint32_t cbefore = running_cost + cincl - cq;
+        for (int i = 0; i < w; ++i) {
+            before += wsum[i];
+            cbefore += wcost[i];
+        }
+        for (int c = 0; c < ch; ++c) {
+            cbefore += item_cost(tiles, rows - c * ATTN_ROWS);
+            out[before + c] = a | (c << 16);
+            cout[before + c] = cbefore;
+        }
         running += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        running_cost += wcost[0] + wcost[1] + wcost[2] + wcost[3];
         __syncthreads();
     }
-    if (tid == 0) n_items[bh] = running;
+    if (tid == 0) {
+        n_items[bh] = running;
+        n_cost[bh] = running_cost;
+    }
 }
 
-// head_pos[bh] = number of work items of the heads before bh; head_pos[BH] = total.
+// head_pos[bh] = number of work items of the heads before bh, head_cost[bh] =
+// their summed cost; entry BH holds the totals.
 __global__ __launch_bounds__(1024) void head_scan_kernel(int BH, const int32_t* __restrict__ n_items,
-                                                         int32_t* __restrict__ head_pos) {
+                                                         const uint32_t* __restrict__ n_cost,
+                                                         int32_t* __restrict__ head_pos,
+                                                         uint64_t* __restrict__ head_cost) {
     __shared__ int wsum[16];
+    __shared__ uint64_t wcost[16];
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     int running = 0;
-    if (tid == 0) head_pos[0] = 0;
+    uint64_t running_cost = 0;
+    if (tid == 0) {
+        head_pos[0] = 0;
+        head_cost[0] = 0;
+    }
     for (int base = 0; base < BH; base += 1024) {
         const int i = base + tid;
         const int v = i < BH ? n_items[i] : 0;
+        const uint64_t vc = i < BH ? n_cost[i] : 0;
         int incl = v;
+        uint64_t cincl = vc;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const int u = __shfl_up(incl, o);
-            if (l >= o) incl += u;
+            const uint64_t uc = __shfl_up(cincl, o);
+            if (l >= o) {
+                incl += u;
+                cincl += uc;
+            }
         }
-        if (l == 63) wsum[w] = incl;
+        if (l == 63) {
+            wsum[w] = incl;
+            wcost[w] = cincl;
+        }
         __syncthreads();
         int before = running;
-        for (int k = 0; k < w; ++k) before += wsum[k];
-        if (i < BH) head_pos[i + 1] = before + incl;
-        for (int k = 0; k < 16; ++k) running += wsum[k];
+        uint64_t cbefore = running_cost;
+        for (int k = 0; k < w; ++k) {
+            before += wsum[k];
+            cbefore += wcost[k];
+        }
+        if (i < BH) {
+            head_pos[i + 1] = before + incl;
+            head_cost[i + 1] = cbefore + cincl;
+        }
+        for (int k = 0; k < 16; ++k) {
+            running += wsum[k];
+            running_cost += wcost[k];
+        }
         __syncthreads();
     }
 }
 
+// The list (heads in order, q-clusters in order) is cut into eight stretches of
+// equal estimated cost, one per XCD: stretch x holds the items whose cost
+// prefix lies in [x C / 8, (x + 1) C / 8). Also clears the eight queue counters.
+__device__ __forceinline__ uint64_t cost_before(int i, int BH, int cap, const int32_t* head_pos,
+                                                const uint64_t* head_cost, const uint32_t* cost_pre) {
+    int lo = 0, hi = BH;  // head_pos[lo] <= i < head_pos[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (head_pos[mid] <= i) lo = mid; else hi = mid;
+    }
+    const int j = i - head_pos[lo];
+    return head_cost[lo] + (j > 0 ? cost_pre[(int64_t)lo * cap + j - 1] : 0u);
+}
+
+__global__ __launch_bounds__(64) void xcd_split_kernel(int BH, int cap, const int32_t* __restrict__ head_pos,
+                                                       const uint64_t* __restrict__ head_cost,
+                                                       const uint32_t* __restrict__ cost_pre,
+                                                       int32_t* __restrict__ xcd_start,
+                                                       int32_t* __restrict__ xcd_ctr) {
+    const int x = threadIdx.x;
+    if (x > 8) return;
+    const int n_total = head_pos[BH];
+    if (x < 8) xcd_ctr[x] = 0;
+    if (x == 8) {
+        xcd_start[8] = n_total;
+        return;
+    }
+    const uint64_t target = head_cost[BH] * (uint64_t)x / 8u;
+    int lo = 0, hi = n_total;  // smallest i in [0, n_total] with cost_before(i) >= target
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (cost_before(mid, BH, cap, head_pos, head_cost, cost_pre) >= target) hi = mid; else lo = mid + 1;
+    }
+    xcd_start[x] = lo;
+}
+
 hipError_t launch_worklist(const Prob& p, int Cq, int cap, const int32_t* q_offsets,
-                           int32_t* items, int32_t* n_items, int32_t* head_pos, hipStream_t s) {
+                           const int32_t* run_pos, const int32_t* n_runs, int run_cap,
+                           const AttnSched& sc, hipStream_t s) {
     hipLaunchKernelGGL(worklist_kernel, dim3((unsigned)p.BH), dim3(256), 0, s, Cq, cap, q_offsets,
-                       items, n_items);
-    hipLaunchKernelGGL(head_scan_kernel, dim3(1), dim3(1024), 0, s, p.BH, n_items, head_pos);
+                       run_pos, n_runs, run_cap, sc.items, sc.n_items, sc.cost_pre, sc.n_cost);
+    hipLaunchKernelGGL(head_scan_kernel, dim3(1), dim3(1024), 0, s, p.BH, sc.n_items, sc.n_cost,
+                       sc.head_pos, sc.head_cost);
+    hipLaunchKernelGGL(xcd_split_kernel, dim3(1), dim3(64), 0, s, p.BH, cap, sc.head_pos, sc.head_cost,
+                       sc.cost_pre, sc.xcd_start, sc.xcd_ctr);
     return hipGetLastError();
 }
 
@@ -377,7 +486,8 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
                  const u16* __restrict__ V1, const int32_t* __restrict__ run_start,
                  const int32_t* __restrict__ run_pos, const int32_t* __restrict__ n_runs,
                  int run_cap, const int32_t* __restrict__ items,
-                 const int32_t* __restrict__ head_pos, int BH, int cap, float sl2,
+                 const int32_t* __restrict__ head_pos, const int32_t* __restrict__ xcd_start,
+                 int32_t* __restrict__ xcd_ctr, int BH, int cap, float sl2,
                  TO* __restrict__ O, float* __restrict__ lse) {
     constexpr int NT = 512;
     static_assert((NT / 64) * 16 == ATTN_ROWS, "eight waves of 16 rows cover a work item");
@@ -393,16 +503,21 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
     constexpr int RL = 512;
     __shared__ int run_s[RL], run_p[RL + 1];
 
-    // Work item order: workgroup b runs on XCD b % 8 (round-robin dispatch), so
-    // it takes item (b % 8) * per + b / 8: each XCD walks one contiguous stretch
-    // of the list (a few heads, q-clusters in order), and the workgroups in
-    // flight on one XCD read overlapping key ranges through its own L2.
-    const int n_total = __builtin_amdgcn_readfirstlane(head_pos[BH]);
-    const int per = (n_total + 7) >> 3;
-    const int kx = blockIdx.x >> 3;
-    if (kx >= per) return;
-    const int item = (blockIdx.x & 7) * per + kx;
-    if (item >= n_total) return;
+    __shared__ int sh_item;
+
+    // Work order: workgroup b runs on XCD b % 8 (round-robin dispatch) and takes
+    // the items of stretch b % 8 in list order from that stretch's counter. The
+    // stretches are contiguous (a few heads, q-clusters in order), so the
+    // workgroups in flight on one XCD read overlapping key ranges through its
+    // own L2, and they carry equal estimated cost, so the XCDs finish together.
+    const int xq = blockIdx.x & 7;
+    const int s_beg = __builtin_amdgcn_readfirstlane(xcd_start[xq]);
+    const int s_end = __builtin_amdgcn_readfirstlane(xcd_start[xq + 1]);
+    for (;;) {
+    if (threadIdx.x == 0) sh_item = s_beg + atomicAdd(&xcd_ctr[xq], 1);
+    __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(sh_item);
+    if (item >= s_end) break;
     int hlo = 0, hhi = BH;  // head_pos[hlo] <= item < head_pos[hhi]
     while (hhi - hlo > 1) {
         const int mid = (hlo + hhi) >> 1;
@@ -578,6 +693,8 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
             lse[(int64_t)bh * N + qtok] =
                 l_tot > 0.0f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
     }
+    __syncthreads();  // LDS (runs, tiles, sh_item) is reused by the next item
+    }
 }
 
 #ifndef ADC_ATTN_WPE64
@@ -585,41 +702,57 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
 #endif
 constexpr int ATTN_WPE64 = ADC_ATTN_WPE64;  // waves per SIMD asked of the bf16 D=64 kernel
 
+// Compute units of the current device (read once per device).
+static int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 template <typename T, typename TO>
-static void launch_attn_t(const Prob& p, dim3 grid, int Cq, const void* q, const int32_t* q_perm,
+static void launch_attn_t(const Prob& p, int Cq, const void* q, const int32_t* q_perm,
                           const int32_t* q_offsets, const u16* k0, const u16* k1, const u16* v0,
                           const u16* v1, const int32_t* run_start, const int32_t* run_pos,
-                          const int32_t* n_runs, int run_cap, const int32_t* items,
-                          const int32_t* head_pos, int cap, float sl2, void* out, float* lse,
-                          hipStream_t s) {
+                          const int32_t* n_runs, int run_cap, const AttnSched& sc, int cap,
+                          float sl2, void* out, float* lse, hipStream_t s) {
     // waves per SIMD: two workgroups per CU where the registers allow it
     constexpr int W64 = sizeof(T) == 2 ? ATTN_WPE64 : 2;
+    const int wpe = p.D == 64 ? W64 : 2;
     auto k = p.D == 64 ? attn_kernel<T, 64, TO, W64> : attn_kernel<T, 128, TO, 2>;
+    // as many workgroups as fit at once (wpe * 4 SIMDs / 8 waves per CU), in
+    // whole rounds of the eight XCDs
+    const int per_cu = std::max(1, wpe / 2);
+    const dim3 grid((unsigned)(((cu_count() * per_cu) + 7) / 8 * 8));
     hipLaunchKernelGGL(k, grid, dim3(512), 0, s, p.N, Cq, (const T*)q, q_perm, q_offsets, k0, k1,
-                       v0, v1, run_start, run_pos, n_runs, run_cap, items, head_pos, p.BH, cap, sl2,
-                       (TO*)out, lse);
+                       v0, v1, run_start, run_pos, n_runs, run_cap, sc.items, sc.head_pos,
+                       sc.xcd_start, sc.xcd_ctr, p.BH, cap, sl2, (TO*)out, lse);
 }
 
 hipError_t launch_attention(const Prob& p, int Cq, const void* q, const int32_t* q_perm,
                             const int32_t* q_offsets, const u16* k0, const u16* k1,
                             const u16* v0, const u16* v1, const int32_t* run_start,
                             const int32_t* run_pos, const int32_t* n_runs, int run_cap,
-                            const int32_t* items, const int32_t* head_pos, int cap, float scale,
-                            void* out, int out_f32, float* lse, hipStream_t s) {
+                            const AttnSched& sc, int cap, float scale, void* out, int out_f32,
+                            float* lse, hipStream_t s) {
     if (cap <= 0) return hipSuccess;
     const float sl2 = scale * 1.4426950408889634f;
-    // at most BH * cap items; 8 workgroups per step of the XCD-strided order
-    dim3 grid((unsigned)(((int64_t)p.BH * cap + 7) / 8 * 8));
     if (p.bf16) {
         if (out_f32)
-            launch_attn_t<u16, float>(p, grid, Cq, q, q_perm, q_offsets, k0, k1, v0, v1, run_start,
-                                      run_pos, n_runs, run_cap, items, head_pos, cap, sl2, out, lse, s);
+            launch_attn_t<u16, float>(p, Cq, q, q_perm, q_offsets, k0, k1, v0, v1, run_start,
+                                      run_pos, n_runs, run_cap, sc, cap, sl2, out, lse, s);
         else
-            launch_attn_t<u16, u16>(p, grid, Cq, q, q_perm, q_offsets, k0, k1, v0, v1, run_start,
-                                    run_pos, n_runs, run_cap, items, head_pos, cap, sl2, out, lse, s);
+            launch_attn_t<u16, u16>(p, Cq, q, q_perm, q_offsets, k0, k1, v0, v1, run_start,
+                                    run_pos, n_runs, run_cap, sc, cap, sl2, out, lse, s);
     } else {
-        launch_attn_t<float, float>(p, grid, Cq, q, q_perm, q_offsets, k0, k1, v0, v1, run_start,
-                                    run_pos, n_runs, run_cap, items, head_pos, cap, sl2, out, lse, s);
+        launch_attn_t<float, float>(p, Cq, q, q_perm, q_offsets, k0, k1, v0, v1, run_start,
+                                    run_pos, n_runs, run_cap, sc, cap, sl2, out, lse, s);
     }
     return hipGetLastError();
 }

@@ -162,16 +162,30 @@ hipError_t launch_topk(const Prob& p, int Cq, int Ck, const float* S, const int3
 hipError_t launch_build_runs(const Prob& p, int Cq, int Ck, const int32_t* k_offsets,
                              const uint32_t* mask, int run_cap, int32_t* run_start,
                              int32_t* run_pos, int32_t* n_runs, hipStream_t s);
+// Attention schedule: the work items of each head (q-cluster, 128-row chunk),
+// their cost prefix, per-head totals and the eight cost-balanced stretches
+// (one per XCD) with their queue counters.
+struct AttnSched {
+    int32_t* items;      // [BH][cap] a | chunk << 16
+    int32_t* n_items;    // [BH]
+    uint32_t* cost_pre;  // [BH][cap] inclusive cost prefix inside the head
+    uint32_t* n_cost;    // [BH]
+    int32_t* head_pos;   // [BH + 1] items before each head
+    uint64_t* head_cost; // [BH + 1] cost before each head
+    int32_t* xcd_start;  // [9] first item of each stretch, then the total
+    int32_t* xcd_ctr;    // [8] items taken from each stretch
+};
 hipError_t launch_worklist(const Prob& p, int Cq, int cap, const int32_t* q_offsets,
-                           int32_t* items, int32_t* n_items, int32_t* head_pos, hipStream_t s);
+                           const int32_t* run_pos, const int32_t* n_runs, int run_cap,
+                           const AttnSched& sc, hipStream_t s);
 hipError_t launch_planes(const Prob& p, const void* k, const void* v, uint16_t* k_hi, uint16_t* k_lo,
                          uint16_t* v_hi, uint16_t* v_lo, hipStream_t s);
 hipError_t launch_attention(const Prob& p, int Cq, const void* q, const int32_t* q_perm,
                             const int32_t* q_offsets, const uint16_t* k0, const uint16_t* k1,
                             const uint16_t* v0, const uint16_t* v1, const int32_t* run_start,
                             const int32_t* run_pos, const int32_t* n_runs, int run_cap,
-                            const int32_t* items, const int32_t* head_pos, int cap, float scale,
-                            void* out, int out_f32, float* lse, hipStream_t s);
+                            const AttnSched& sc, int cap, float scale, void* out, int out_f32,
+                            float* lse, hipStream_t s);
 
 constexpr int ATTN_ROWS = 128;  // query rows per attention work item
 
