@@ -354,69 +354,83 @@ __device__ __forceinline__ int tile_rows(int lane, int t0, int total, int R, int
     return rn + (int)__popcll(__ballot(rk < R && off <= 64));
 }
 
-// Global -> register staging of one K/V tile (64 key rows, NP 16-bit planes
-// each), NT threads, 16-byte chunks. Rows past the selection (krow = -1) read
-// row 0: their scores are masked to -inf, so their probabilities are exactly 0
-// and the finite values they carry never reach the output.
+// K/V tiles in LDS. A tile is 64 key rows of NP 16-bit planes of K, then NP of
+// V, each plane row-major with unpadded rows of RB = 2 D bytes; the 16-byte
+// chunks of row r are stored XOR-swizzled (logical chunk c at physical chunk
+// c ^ (r & 7)) so that the column reads of the fragments below spread over
+// the banks. Tiles are copied from global memory straight into LDS by the
+// 16-byte global->LDS loads: one wave instruction fills 1 KB of a plane, lane
+// j the j-th 16 bytes, so the swizzle is applied by choosing which global
+// chunk each lane fetches. NB tiles are in flight (the copy of tile t + NB - 1
+// is issued while tile t is computed).
 template <int D, int NP, int NT>
-struct TileRegs {
-    static constexpr int TASK = 64 * (D / 8);
-    static constexpr int CT = TASK / NT;
-    static_assert(TASK % NT == 0, "tile chunks must divide among the threads");
-    u32x4 k[NP][CT], v[NP][CT];
+struct TileGeom {
+    static constexpr int RB = 2 * D;                    // bytes per row of a plane
+    static constexpr int PLANE = 64 * RB;               // bytes per plane of a tile
+    static constexpr int TILE = 2 * NP * PLANE;         // K planes, then V planes
+    static constexpr int NB = TILE <= 32768 ? 4 : 2;    // tiles resident
+    static constexpr int NW = NT / 64;
+    static constexpr int IPW = PLANE / 1024 / NW;       // 1 KB blocks per plane per wave
+    static constexpr int L = 2 * NP * IPW;              // copies per wave per tile
+    static_assert(IPW >= 1 && (PLANE / 1024) % NW == 0, "plane blocks must divide among the waves");
 };
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Issue the copy of one tile into the LDS buffer `buf`: wave w fills blocks
+// w * IPW .. w * IPW + IPW - 1 of every plane. Rows past the selection
+// (krow = -1) read row 0: their scores are masked to -inf, so their
+// probabilities are exactly 0 and the finite values they carry never reach
+// the output.
 template <int D, int NP, int NT>
-__device__ __forceinline__ void tile_load(TileRegs<D, NP, NT>& r, int tid, const int* krow,
+__device__ __forceinline__ void tile_copy(unsigned char* buf, int w, int lane, const int* krow,
                                           const u16* K0, const u16* K1, const u16* V0,
                                           const u16* V1) {
-    using TR = TileRegs<D, NP, NT>;
+    using G = TileGeom<D, NP, NT>;
 #pragma unroll
-    for (int i = 0; i < TR::CT; ++i) {
-        const int c = tid + i * NT;
-        const int row = max(krow[c / (D / 8)], 0);
-        const int64_t off = (int64_t)row * D + (c % (D / 8)) * 8;
-        r.k[0][i] = *reinterpret_cast<const u32x4*>(K0 + off);
-        r.v[0][i] = *reinterpret_cast<const u32x4*>(V0 + off);
+    for (int i = 0; i < G::IPW; ++i) {
+        const int blk = w * G::IPW + i;
+        const int off = blk * 1024 + 16 * lane;
+        const int r = off / G::RB;
+        const int lc = ((off % G::RB) / 16) ^ (r & 7);
+        const int64_t goff = (int64_t)max(krow[r], 0) * D + lc * 8;
+        unsigned char* dst = buf + blk * 1024;
+        __builtin_amdgcn_global_load_lds(K0 + goff, (lds_void*)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(V0 + goff, (lds_void*)(dst + NP * G::PLANE), 16, 0, 0);
         if constexpr (NP == 2) {
-            r.k[NP - 1][i] = *reinterpret_cast<const u32x4*>(K1 + off);
-            r.v[NP - 1][i] = *reinterpret_cast<const u32x4*>(V1 + off);
+            __builtin_amdgcn_global_load_lds(K1 + goff, (lds_void*)(dst + G::PLANE), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(V1 + goff, (lds_void*)(dst + 3 * G::PLANE), 16, 0, 0);
         }
     }
 }
 
-// Register -> LDS, both K and V row-major (padded stride LDK).
-template <int D, int NP, int NT, int LDK>
-__device__ __forceinline__ void tile_store(const TileRegs<D, NP, NT>& r, int tid,
-                                           u16 (*Ks)[64 * LDK], u16 (*Vs)[64 * LDK]) {
-    using TR = TileRegs<D, NP, NT>;
-#pragma unroll
-    for (int i = 0; i < TR::CT; ++i) {
-        const int c = tid + i * NT;
-        const int o = (c / (D / 8)) * LDK + (c % (D / 8)) * 8;
-#pragma unroll
-        for (int pl = 0; pl < NP; ++pl) {
-            *reinterpret_cast<u32x4*>(&Ks[pl][o]) = r.k[pl][i];
-            *reinterpret_cast<u32x4*>(&Vs[pl][o]) = r.v[pl][i];
-        }
-    }
+// Wait until at most N of this wave's tile copies are outstanding (copies
+// complete in issue order) and its LDS accesses are done, then meet the other
+// waves. The barrier is an opaque statement to the compiler (no memory access
+// moves across it), so it waits for exactly what is asked here instead of for
+// every copy in flight.
+template <int N>
+__device__ __forceinline__ void tiles_ready_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+    asm volatile("s_barrier" ::: "memory");
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// Transposed 16x32 fragment of a row-major V tile (stride LDK) for the A
-// operand of O^T += V^T P^T. Lane L (group G = L/16) receives V[key][d] for
-// d = L%16 of a 16-column block and the 8 keys 32c + 4G + {0..3},
-// 32c + 16 + 4G + {0..3}: the key order of the lane's probabilities. In each
-// 16-lane group of a ds_read_tr16_b64, source lane a + 4j points at columns
-// 4a..4a+3 of key row j and destination lane 4a + b collects column b of
-// source lanes a, a + 4, a + 8, a + 12. `p` is the lane's address for the
-// first four keys (row 32c + 4G + j, column block start + 4a).
-template <int LDK>
-__device__ __forceinline__ uint4 v_frag(const u16* p) {
+// Transposed 16x32 fragment of a row-major V plane for the A operand of
+// O^T += V^T P^T. Lane L (group G = L/16) receives V[key][d] for d = L%16 of a
+// 16-column block and the 8 keys 32c + 4G + {0..3}, 32c + 16 + 4G + {0..3}: the
+// key order of the lane's probabilities. In each 16-lane group of a
+// ds_read_tr16_b64, source lane a + 4j points at columns 4a..4a+3 of key row j
+// and destination lane 4a + b collects column b of source lanes a, a + 4,
+// a + 8, a + 12. `p` is the lane's address for the first four keys; the
+// second four are 16 rows further (same swizzle, as 16 is a multiple of 8).
+template <int RB>
+__device__ __forceinline__ uint4 v_frag(const unsigned char* p) {
     const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
-    const v4i16 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 16 * LDK));
+    const v4i16 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 16 * RB));
     const uint2 xu = __builtin_bit_cast(uint2, x), yu = __builtin_bit_cast(uint2, y);
     return make_uint4(xu.x, xu.y, yu.x, yu.y);
 }
@@ -472,10 +486,10 @@ __device__ __forceinline__ void softmax_block(f32x4 (&sc)[NKB], float sl2, int p
 // w of the eight owns rows 16w..16w+15 (a wave past the item's rows only
 // helps with the tile staging and the run lookups).
 //
-// K/V tiles of 64 keys are double-buffered in LDS; the global loads of tiles
-// t+1 and t+2 are in flight in registers while tile t is computed, and the
-// last wave looks up the key rows of tile t+3 meanwhile, so one barrier per
-// tile suffices. Operands are 16-bit planes (NP = 1: K bf16, V fp16; NP = 2:
+// K/V tiles of 64 keys are copied straight into NB LDS buffers: while tile t
+// is computed the copies of tiles t+1 .. t+NB-1 are in flight and the last
+// wave looks up the key rows of tile t+NB, so one barrier per tile suffices
+// and no register staging is needed. Operands are 16-bit planes (NP = 1: K bf16, V fp16; NP = 2:
 // bf16 hi and lo of f32 data, every product of order <= 1 accumulated, three
 // MFMAs per product, near f32 accuracy).
 template <typename T, int D, typename TO, int WPE>
@@ -495,9 +509,22 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
     constexpr int NP = PREC ? 2 : 1;  // operand planes
     constexpr int KC = D / 32;        // 32-wide chunks of the head dimension
     constexpr int DB = D / 16;        // 16-row blocks of O^T
-    constexpr int LDK = D + 8;        // padded LDS row stride (elements)
-    __shared__ __attribute__((aligned(16))) u16 Ks[2][NP][64 * LDK];
-    __shared__ __attribute__((aligned(16))) u16 Vs[2][NP][64 * LDK];
+    using TG = TileGeom<D, NP, NT>;
+    constexpr int RB = TG::RB;
+    constexpr int NB = TG::NB;
+    // one array per buffer, always indexed by a compile-time buffer number, so
+    // the compiler's wait analysis sees that a copy into one buffer does not
+    // touch the buffer being read
+    __shared__ __attribute__((aligned(1024))) unsigned char tb0[TG::TILE], tb1[TG::TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char tb2[NB > 2 ? TG::TILE : 16];
+    __shared__ __attribute__((aligned(1024))) unsigned char tb3[NB > 2 ? TG::TILE : 16];
+    auto buf = [&](auto j_c) __attribute__((always_inline)) -> unsigned char* {
+        constexpr int J = decltype(j_c)::value % NB;
+        if constexpr (J == 0) return tb0;
+        else if constexpr (J == 1) return tb1;
+        else if constexpr (J == 2) return tb2;
+        else return tb3;
+    };
     __shared__ int krow[4][64];
     // the work item's runs (first key row, first position) when they fit
     constexpr int RL = 512;
@@ -566,8 +593,18 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
     f32x4 o[DB + 1];  // O^T blocks and the row-sum block
 #pragma unroll
     for (int db = 0; db <= DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // per-lane LDS offset of the transposed V reads (key row 4g + j, column 4a)
-    const int vlane = (4 * g + ((l & 15) >> 2)) * LDK + 4 * (l & 3);
+    // per-lane byte offsets (swizzled) of the K fragment reads (key row c16,
+    // chunk 4 kc + g) and of the transposed V reads (key row 4g + j, columns
+    // 16 db + 4a .. + 3)
+    int koff[KC], voff[DB];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) koff[kc] = c16 * RB + 16 * ((4 * kc + g) ^ (c16 & 7));
+    {
+        const int rv = 4 * g + ((l & 15) >> 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            voff[db] = rv * RB + 16 * ((2 * db + ((l & 3) >> 1)) ^ (rv & 7)) + (l & 1) * 8;
+    }
 
     // Run lookups read the run list from LDS (copied once here; a list longer
     // than RL is read from global memory instead). They are made by the last
@@ -583,20 +620,19 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
         else rn = tile_rows(l, t * 64, total, R, rn, rs, rp, krow[t & 3]);
     };
     if (w == LW) {
-        lookup(0);
-        lookup(1);
-        lookup(2);
+#pragma unroll
+        for (int t = 0; t < NB; ++t) lookup(t);
     }
     __syncthreads();
-    TileRegs<D, NP, NT> tr0, tr1;
-    tile_load<D, NP, NT>(tr0, tid, krow[0], Kh0, Kh1, Vh0, Vh1);
-    tile_load<D, NP, NT>(tr1, tid, krow[1], Kh0, Kh1, Vh0, Vh1);
-    tile_store<D, NP, NT, LDK>(tr0, tid, Ks[0], Vs[0]);
-    __syncthreads();
+    tile_copy<D, NP, NT>(buf(std::integral_constant<int, 0>{}), w, l, krow[0], Kh0, Kh1, Vh0, Vh1);
+    if constexpr (NB > 2) {
+        tile_copy<D, NP, NT>(buf(std::integral_constant<int, 1>{}), w, l, krow[1], Kh0, Kh1, Vh0, Vh1);
+        tile_copy<D, NP, NT>(buf(std::integral_constant<int, 2>{}), w, l, krow[2], Kh0, Kh1, Vh0, Vh1);
+    }
 
     // Scores, softmax and P.V of NKB 16-key blocks starting at block kb0 of the
     // tile in buffer b.
-    auto compute = [&](int b, int p0, int kb0, auto nkb_c, auto mask_c) __attribute__((always_inline)) {
+    auto compute = [&](const unsigned char* tb, int p0, int kb0, auto nkb_c, auto mask_c) __attribute__((always_inline)) {
         constexpr int NKB = decltype(nkb_c)::value;
         constexpr bool MASK = decltype(mask_c)::value;
         f32x4 sc[NKB];
@@ -605,10 +641,10 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
             sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
-                const int off = ((kb0 + kb) * 16 + c16) * LDK + kc * 32 + g * 8;
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[b][0][off]);
+                const unsigned char* kp = tb + (kb0 + kb) * 16 * RB + koff[kc];
+                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kp);
                 if constexpr (PREC) {
-                    const bf16x8 kl = *reinterpret_cast<const bf16x8*>(&Ks[b][NP - 1][off]);
+                    const bf16x8 kl = *reinterpret_cast<const bf16x8*>(kp + TG::PLANE);
                     sc[kb] = mfma16(kl, qf[0][kc], sc[kb]);
                     sc[kb] = mfma16(ka, qf[NP - 1][kc], sc[kb]);
                 }
@@ -619,9 +655,9 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
 #pragma unroll
         for (int h = 0; h < NKB / 2; ++h) {
             const int kc2 = kb0 / 2 + h;
-            const u16* vb0 = &Vs[b][0][vlane + kc2 * 32 * LDK];
+            const unsigned char* vb0 = tb + NP * TG::PLANE + kc2 * 32 * RB;
             if constexpr (PREC) {
-                const u16* vb1 = &Vs[b][NP - 1][vlane + kc2 * 32 * LDK];
+                const unsigned char* vb1 = vb0 + TG::PLANE;
                 const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u,
                                                                           0x3F803F80u, 0x3F803F80u));
                 bf16x8 pb, pl;
@@ -634,8 +670,8 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
                 }
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const bf16x8 va = __builtin_bit_cast(bf16x8, v_frag<LDK>(vb0 + db * 16));
-                    const bf16x8 vl = __builtin_bit_cast(bf16x8, v_frag<LDK>(vb1 + db * 16));
+                    const bf16x8 va = __builtin_bit_cast(bf16x8, v_frag<RB>(vb0 + voff[db]));
+                    const bf16x8 vl = __builtin_bit_cast(bf16x8, v_frag<RB>(vb1 + voff[db]));
                     o[db] = mfma16(vl, pb, o[db]);
                     o[db] = mfma16(va, pl, o[db]);
                     o[db] = mfma16(va, pb, o[db]);
@@ -652,7 +688,7 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
                                       pack_h2(sc[2 * h + 1][2], sc[2 * h + 1][3])));
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const f16x8 vh = __builtin_bit_cast(f16x8, v_frag<LDK>(vb0 + db * 16));
+                    const f16x8 vh = __builtin_bit_cast(f16x8, v_frag<RB>(vb0 + voff[db]));
                     o[db] = mfma16h(vh, ph, o[db]);
                 }
                 o[DB] = mfma16h(ones, ph, o[DB]);
@@ -660,25 +696,33 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
         }
     };
 
-    // one tile: look up t+3 (last wave), prefetch t+2 into the register set tile t
-    // used, compute t, store t+1 into the other LDS buffer. Every wave issues
-    // the same tile loads every step (tiles past the end read clamped, valid
-    // rows and are never used), so the load counters stay exact.
-    auto step = [&](int t, auto& tr_mine, auto& tr_next) __attribute__((always_inline)) {
-        const int b = t & 1;
-        const int t0 = t * 64;
-        if (w == LW) lookup(t + 3);
-        tile_load<D, NP, NT>(tr_mine, tid, krow[(t + 2) & 3], Kh0, Kh1, Vh0, Vh1);
+    // One tile (t % NB == J): wait for this wave's copy of tile t (the copies of
+    // the NB - 2 later tiles already issued may stay in flight) and meet the
+    // other waves, so tile t is in LDS and buffer (t - 1) % NB is no longer
+    // read; then the last wave looks up tile t + NB, every wave issues its part
+    // of the copy of tile t + NB - 1 into buffer (t - 1) % NB, and tile t is
+    // computed. Steps run in whole rounds of NB, and every step copies a tile
+    // (past the selection: row 0 repeated, one cache line, never used), so every
+    // wait counts the same copies on every path.
+    auto step = [&](int t, auto j_c) __attribute__((always_inline)) {
+        constexpr int J = decltype(j_c)::value;
+        tiles_ready_barrier<TG::L * (NB - 2)>();
+        if (w == LW) lookup(t + NB);
+        tile_copy<D, NP, NT>(buf(std::integral_constant<int, J + NB - 1>{}), w, l,
+                             krow[(t + NB - 1) & 3], Kh0, Kh1, Vh0, Vh1);
         if (t < ntiles && live) {
-            if (t0 + 64 > total) compute(b, t0, 0, std::integral_constant<int, 4>{}, std::true_type{});
-            else compute(b, t0, 0, std::integral_constant<int, 4>{}, std::false_type{});
+            const int t0 = t * 64;
+            if (t0 + 64 > total) compute(buf(j_c), t0, 0, std::integral_constant<int, 4>{}, std::true_type{});
+            else compute(buf(j_c), t0, 0, std::integral_constant<int, 4>{}, std::false_type{});
         }
-        tile_store<D, NP, NT, LDK>(tr_next, tid, Ks[b ^ 1], Vs[b ^ 1]);
-        __syncthreads();
     };
-    for (int t = 0; t < ntiles; t += 2) {
-        step(t, tr0, tr1);
-        step(t + 1, tr1, tr0);
+    for (int t = 0; t < ntiles; t += NB) {
+        step(t, std::integral_constant<int, 0>{});
+        step(t + 1, std::integral_constant<int, 1>{});
+        if constexpr (NB > 2) {
+            step(t + 2, std::integral_constant<int, 2>{});
+            step(t + 3, std::integral_constant<int, 3>{});
+        }
     }
 
     if (qok) {
