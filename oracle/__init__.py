@@ -282,6 +282,35 @@ def layer_compactness(mses):
     return 1.0 / float(np.mean(mses))
 
 
+def layer_required_count(k_heads, m0, probe_max, iters=5, tau_mult=1.5, init="sample", seed=0,
+                         b=0):
+    """Section 3.2.2: Algorithm 1 on each head of a layer with the cap probe_max;
+    the layer needs the largest slot count of its heads, and more than the cap
+    (probe_max + 1) when some head still had keys left at the cap (F = 1)."""
+    worst = 0
+    for h, k in enumerate(k_heads):
+        r = cluster_k(k, m0, probe_max, iters, tau_mult=tau_mult, adaptive=True, init=init,
+                      seed=seed, b=b, h=h)
+        worst = max(worst, probe_max + 1 if r["full"] else r["n_slots"])
+    return worst
+
+
+def kmax_for_top_fraction(required, m0, probe_max, top_frac=0.15):
+    """Section 4.1: the cap is set so that the top top_frac of layers (the ones
+    needing the most clusters) use full attention. Counts come in stage
+    boundaries m0 * 2^j, so the cap is the smallest boundary (at most
+    probe_max) exceeded by no more than top_frac of the layers."""
+    n = len(required)
+    j = 0
+    while (m0 << j) <= probe_max:
+        cap = m0 << j
+        over = sum(1 for r in required if r > cap)
+        if over <= top_frac * n + 1e-9:
+            return cap
+        j += 1
+    return probe_max
+
+
 def quest_scores(qrep, kmax, kmin, ksizes):
     qrep, kmax, kmin = _f32(qrep), _f32(kmax), _f32(kmin)
     cq, d = qrep.shape

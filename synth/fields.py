@@ -17,6 +17,8 @@ available, so these fields stand in for them):
   an optional per-head scale s_h ~ U(0.5, 2) shared by Q, K and V
   (Wan-shaped case); optional i.i.d. N(0, 1) text tokens prepended
   (CogVideoX-shaped 17.7K case). bf16 workloads are rounded to nearest-even.
+  The noise scale 0.1 is the workloads' default; a synthetic stack of layers
+  (layer_stack) varies it from layer to layer.
 
 Denoising steps (the warm start of section 3.2.2 relies on tokens moving
 little from one step to the next, Fig. 6): step s keeps every field's
@@ -47,9 +49,11 @@ class Workload:
     iters: int           # Lloyd iterations per k-means call
     init: str            # "kmeanspp" or "sample"
     top_p: float
-    noise: str = "normal"        # "normal" | "student_t3"
+    noise: str = "normal"        # "normal" | "student_t3" | "student_t" (noise_df degrees of freedom)
     head_scale: bool = False     # per-head U(0.5, 2) scale shared by Q/K/V
     B: int = 1
+    noise_std: float = NOISE_STD  # scale of eps (layers of a synthetic stack differ in it)
+    noise_df: float = 3.0         # degrees of freedom of the "student_t" noise
 
     @property
     def N(self) -> int:
@@ -90,6 +94,24 @@ def scaled(w: Workload, **changes) -> Workload:
     return dataclasses.replace(w, **changes)
 
 
+def layer_stack(w: Workload, n_layers: int, noise_lo: float = 0.05, noise_hi: float = 0.4,
+                df_hi: float = 30.0, df_lo: float = 2.05):
+    """A synthetic stack of layers for the per-layer compactness study
+    (section 3.2.1, Fig. 4: key distributions differ much between layers):
+    layer l has the shape of ``w``, its own fields (input seed l) and Student-t
+    noise whose scale grows geometrically from noise_lo to noise_hi while its
+    degrees of freedom fall from df_hi to df_lo (2 + geometric in df - 2), so
+    later layers are more scattered and heavier-tailed. Returns
+    [(workload, seed)] per layer."""
+    out = []
+    for l in range(n_layers):
+        f = l / max(n_layers - 1, 1)
+        std = noise_lo * (noise_hi / noise_lo) ** f
+        df = 2.0 + (df_hi - 2.0) * ((df_lo - 2.0) / (df_hi - 2.0)) ** f
+        out.append((dataclasses.replace(w, noise="student_t", noise_std=float(std), noise_df=float(df)), l))
+    return out
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (nearest, ties to even); returns uint16 bit patterns."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
@@ -120,9 +142,11 @@ def _tensor_head(rng: np.random.Generator, w: Workload, coords: np.ndarray, step
         # at step > 0 the step-0 draw only advances the base stream (text tokens follow it)
         if w.noise == "student_t3":
             eps = g.standard_t(3, size=(nv, w.D)).astype(np.float32)
+        elif w.noise == "student_t":
+            eps = g.standard_t(w.noise_df, size=(nv, w.D)).astype(np.float32)
         else:
             eps = g.standard_normal((nv, w.D), dtype=np.float32)
-    field += np.float32(NOISE_STD) * eps
+    field += np.float32(w.noise_std) * eps
     if w.text_tokens:
         text = rng.standard_normal((w.text_tokens, w.D), dtype=np.float32)
         field = np.concatenate([text, field], axis=0)

@@ -657,3 +657,27 @@ def test_tau_is_1p5_times_stage0_mean_distance():
     cent0, lab0, _, _ = oracle.kmeans(k, 24, 5, init="sample", strm=oracle.stream(0, 2, 0, 0, 0))
     c = oracle.compactness(k, lab0, cent0)
     assert r["tau"] == pytest.approx(1.5 * c["mean_dist"], rel=1e-12)
+
+
+# ----------------------------------------------------------------- Nmax calibration
+def test_kmax_for_top_fraction_hand_cases():
+    # 8 layers needing 32, 32, 64, 32, 64, 128, 257 (past a 256 cap), 64 slots, m0 = 32
+    req = [32, 32, 64, 32, 64, 128, 257, 64]
+    assert oracle.kmax_for_top_fraction(req, 32, 256, 0.15) == 128   # one layer (12.5 %) over
+    assert oracle.kmax_for_top_fraction(req, 32, 256, 0.30) == 64    # two layers (25 %) over
+    assert oracle.kmax_for_top_fraction(req, 32, 256, 0.0) == 256    # nobody over: the cap
+    assert oracle.kmax_for_top_fraction([32] * 5, 32, 256, 0.15) == 32
+
+
+def test_layer_required_count_is_the_worst_head():
+    w = synth.scaled(synth.WORKLOADS["cog17k"], H=2, grid=(3, 20, 30), text_tokens=11)
+    lw, seed = synth.layer_stack(w, 8)[7]        # the most scattered layer of the stack
+    g = synth.generate(lw, seed=seed)
+    ks = [synth.as_f32(g["k"][0, h]) for h in range(w.H)]
+    per_head = [oracle.cluster_k(k, 16, 256, 5, adaptive=True, h=h) for h, k in enumerate(ks)]
+    assert oracle.layer_required_count(ks, 16, 256) == max(r["n_slots"] for r in per_head)
+    # with a cap below what the layer needs, some head ends with F = 1 and the
+    # layer needs more than that cap
+    need = oracle.layer_required_count(ks, 16, 256)
+    assert need > 32
+    assert oracle.layer_required_count(ks, 16, need // 2) == need // 2 + 1
