@@ -48,6 +48,8 @@ def main():
                     help="skip the latency/density spread over seeds 1 and 2")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the 65-q-cluster / top-k / centroid-score variants")
+    ap.add_argument("--no-calib", action="store_true",
+                    help="skip the per-layer count / Nmax calibration on a synthetic layer stack")
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the warm-start steady-state steps (drifted inputs)")
     ap.add_argument("--profile-steps", action="store_true",
@@ -186,6 +188,9 @@ def main():
     if not args.no_warm:
         result["warm_steady_state"] = warm_steady_state(
             torch, adc, synth, w, cfg, dev, stream, layer_stats["median"], q, k, v, args.seed)
+
+    if not args.no_calib:
+        result["calibration"] = calibration(torch, adc, synth, dev, stream)
 
     if not args.no_spread:
         del q, k, v, Q, K, S, out
@@ -378,6 +383,46 @@ def variants(torch, adc, w, cfg, q, k, v, stream, seed, mean_slots, steps=5):
         log(f"variant {name}: {res[name]}")
         del Q, K, S
     return res
+
+
+def calibration(torch, adc, synth, dev, stream, n_layers=8, top_frac=0.15, comp_clusters=400):
+    """The per-layer study of sections 3.2.1 and 4.1 on a synthetic stack of
+    CogVideoX-17.7K-shaped layers (keys more scattered and heavier-tailed from
+    layer to layer): each layer's required key-cluster count (Algorithm 1 with a
+    16 m0 cap), its compactness Comp_l at 400 centres (Fig. 4), the cap that
+    sends the top 15 % of layers to full attention, and the heads on full
+    attention at that cap."""
+    from clustered_sparse_attention_cosine_amd import calibrate
+    w = synth.WORKLOADS["cog17k"]
+    t0 = time.time()
+    layers = []
+    for lw, seed in synth.layer_stack(w, n_layers):
+        g = synth.generate(lw, seed=seed)
+        layers.append(tuple(torch.from_numpy(g[t].view(np.int16)).view(torch.bfloat16).to(dev)
+                            for t in "kv"))
+        del g
+    log(f"generated {n_layers} stacked layers in {time.time() - t0:.1f}s")
+    m0 = w.k_base
+    calibrate.calibrate_stack(layers[:1], m0, 16 * m0, top_frac, comp_clusters=comp_clusters)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    res = calibrate.calibrate_stack(layers, m0, 16 * m0, top_frac, comp_clusters=comp_clusters)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    out = {"workload": f"{w.name} stack of {n_layers} layers: B=1 H={w.H} N={w.N} D={w.D}",
+           "m0": m0, "probe_cap": 16 * m0, "top_frac": top_frac, "kmax": res["kmax"],
+           "ms": round(e0.elapsed_time(e1), 3), "layers": []}
+    for (lw, _), p in zip(synth.layer_stack(w, n_layers), res["layers"]):
+        out["layers"].append({"noise_std": round(lw.noise_std, 4), "noise_df": round(lw.noise_df, 3),
+                              "required": p["required"], "comp": round(p["comp"], 5),
+                              "head_counts": {str(c): int((p["head_counts"] == c).sum())
+                                              for c in sorted(set(p["head_counts"].tolist()))},
+                              "full_heads_at_kmax": int(p["full_at_kmax"].sum())})
+    log(f"calibration: kmax {res['kmax']}, " + "; ".join(
+        f"req {l['required']} comp {l['comp']} full {l['full_heads_at_kmax']}" for l in out["layers"]))
+    del layers
+    return out
 
 
 def dense_compare(torch, adc, q, k, v, w, dev, stream):
