@@ -100,6 +100,7 @@ struct KmeansWs {
     double* d2 = nullptr;
     uint8_t* chosen = nullptr;
     int32_t* hist = nullptr;
+    int32_t* seg_cnt = nullptr;
     int32_t* m_eff = nullptr;
 };
 
@@ -122,6 +123,7 @@ void plan_kmeans(Carver& c, const Prob& p, int cap, bool want_inv, bool kpp, boo
     w.sums = c.take<float>(bhc * p.D);
     w.cnt = c.take<int32_t>(bhc);
     w.hist = c.take<int32_t>(bhc);
+    w.seg_cnt = c.take<int32_t>(bhc * sort_segments(p.N));
     w.m_eff = c.take<int32_t>(p.BH);
     if (kpp) {
         if (want_xhat) w.xhat = c.take<float>(bhn * p.D);
@@ -202,14 +204,7 @@ hipError_t init_centres(const Prob& p, const void* x, int normalize, RowSet rs, 
         e = launch_init_kmeanspp(p, x, xf, rs, cv, seed, tensor, stage, w.d2, w.chosen, s);
     } else {
         // caller centres: [BH][m][D] copied into slots [base, base + m)
-        for (int bh = 0; bh < p.BH; ++bh) {
-            e = hipMemcpyAsync(cv.cent + ((size_t)bh * cv.cap + cv.base) * p.D,
-                               init_cent + (size_t)bh * cv.m * p.D, sizeof(float) * cv.m * p.D,
-                               hipMemcpyDeviceToDevice, s);
-            if (e) return e;
-            e = fill_u8(cv.valid + (size_t)bh * cv.cap + cv.base, cv.m, 1, s);
-            if (e) return e;
-        }
+        e = launch_caller_init(p, init_cent, cv, s);
     }
     return e;
 }
@@ -273,9 +268,7 @@ int32_t adacluster_cluster_q(const adc_shape* shape, const adc_q_params* prm, co
     HIPCHK(init_centres(p, q, 1, all, cv, prm->init, init_centroids, prm->seed, TENSOR_Q, 0, w, s));
     HIPCHK(launch_finalize(p, cv, nullptr, 0, s));
     HIPCHK(lloyd(p, q, 1, all, w.inv_norm, cv, prm->iters, false, assign, w, s));
-    HIPCHK(launch_histogram(p, assign, Cq, w.hist, s));
-    HIPCHK(launch_scan_offsets(p, w.hist, Cq, sizes, offsets, s));
-    HIPCHK(launch_stable_rank(p, assign, Cq, offsets, perm, s));
+    HIPCHK(launch_counting_sort(p, assign, Cq, w.seg_cnt, w.hist, sizes, offsets, perm, s));
     HIPCHK(launch_gather_stats(p, Cq, offsets, perm, q, nullptr, 1, centroids, qrep, nullptr,
                                nullptr, nullptr, nullptr, s));
     return ADC_OK;
@@ -395,9 +388,7 @@ int32_t adacluster_cluster_k(const adc_shape* shape, const adc_k_params* prm, co
         HIPCHK(launch_last_valid(p, cvf, n_clusters, w.m_eff, s));
         HIPCHK(launch_assign(p, k, all, nullptr, 0, cvf, w.m_eff, assign, flags_of(w), s));
     }
-    HIPCHK(launch_histogram(p, assign, nmax, w.hist, s));
-    HIPCHK(launch_scan_offsets(p, w.hist, nmax, sizes, offsets, s));
-    HIPCHK(launch_stable_rank(p, assign, nmax, offsets, perm, s));
+    HIPCHK(launch_counting_sort(p, assign, nmax, w.seg_cnt, w.hist, sizes, offsets, perm, s));
     HIPCHK(launch_gather_stats(p, nmax, offsets, perm, k, v, 0, centroids, nullptr, kmax, kmin,
                                k_perm, v_perm, s));
     return ADC_OK;
@@ -575,6 +566,7 @@ size_t adacluster_permute_workspace(const adc_shape* shape, int32_t M) {
     if (check_shape(shape) || check_clusters("M", M)) return 0;
     Carver c(nullptr);
     c.take<int32_t>((size_t)shape->B * shape->H * M);
+    c.take<int32_t>((size_t)shape->B * shape->H * M * sort_segments(shape->N));
     return c.used + 256;
 }
 
@@ -594,9 +586,8 @@ int32_t adacluster_permute(const adc_shape* shape, int32_t M, const int32_t* ass
     Prob p = make_prob(shape);
     Carver c(workspace);
     int32_t* hist = c.take<int32_t>((size_t)p.BH * M);
-    HIPCHK(launch_histogram(p, assign, M, hist, s));
-    HIPCHK(launch_scan_offsets(p, hist, M, sizes, offsets, s));
-    HIPCHK(launch_stable_rank(p, assign, M, offsets, perm, s));
+    int32_t* seg_cnt = c.take<int32_t>((size_t)p.BH * M * sort_segments(p.N));
+    HIPCHK(launch_counting_sort(p, assign, M, seg_cnt, hist, sizes, offsets, perm, s));
     HIPCHK(launch_gather_stats(p, M, offsets, perm, x, v, 0, means, nullptr, xmax, xmin, x_perm,
                                v_perm, s));
     return ADC_OK;

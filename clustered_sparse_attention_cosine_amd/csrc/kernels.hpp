@@ -81,6 +81,8 @@ struct FlagSet {
     int32_t* ccount;  // [BH, N] number of candidates found (may exceed CAND_CAP)
 };
 constexpr int CAND_CAP = 16;
+// Caller centres [BH][cv.m][D] into slots [cv.base, cv.base + cv.m), marked valid.
+hipError_t launch_caller_init(const Prob& p, const float* init, CentView cv, hipStream_t s);
 // Warm start: slots [0, count[bh]) of cv (base 0) copy their centres from
 // init ([BH][cap][D]) and are marked as holding a centre, the rest are not.
 hipError_t launch_warm_init(const Prob& p, const float* init, const int32_t* count, CentView cv,
@@ -133,12 +135,16 @@ hipError_t launch_compactness(const Prob& p, int M, const void* x_perm, const in
                               double* comp, hipStream_t s);
 
 // ---------------------------------------------------------------- layout (permute.hip)
-hipError_t launch_histogram(const Prob& p, const int32_t* labels, int M, int32_t* cnt,
-                            hipStream_t s);
 hipError_t launch_scan_offsets(const Prob& p, const int32_t* cnt, int M, int32_t* sizes_out,
                                int32_t* offsets, hipStream_t s);
-hipError_t launch_stable_rank(const Prob& p, const int32_t* labels, int M,
-                              const int32_t* offsets, int32_t* perm, hipStream_t s);
+// Stable counting sort by label (M <= 8192) over segments of SORT_SEG rows:
+// sizes [BH][M], offsets [BH][M+1], perm [BH][N] out; seg_cnt
+// [BH][sort_segments(N)][M] and total [BH][M] are scratch.
+constexpr int SORT_SEG = 4096;
+int sort_segments(int N);
+hipError_t launch_counting_sort(const Prob& p, const int32_t* labels, int M, int32_t* seg_cnt,
+                                int32_t* total, int32_t* sizes, int32_t* offsets, int32_t* perm,
+                                hipStream_t s);
 // Per cluster: member means (of normalised rows when normalize), raw means,
 // per-dimension max/min and the permuted copies of x and v.
 hipError_t launch_gather_stats(const Prob& p, int M, const int32_t* offsets, const int32_t* perm,

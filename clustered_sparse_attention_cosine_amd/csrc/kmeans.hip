@@ -125,6 +125,30 @@ hipError_t launch_warm_init(const Prob& p, const float* init, const int32_t* cou
     return hipGetLastError();
 }
 
+// Caller-supplied centres ([BH][m][D], m = cv.m) copied into slots
+// [base, base + m) of every head, each marked as holding a centre. One wave
+// per slot.
+template <int D>
+__global__ __launch_bounds__(256) void caller_init_kernel(const float* __restrict__ init, CentView cv) {
+    const int bh = blockIdx.y;
+    const int j = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+    if (j >= cv.m) return;
+    const int64_t slot = (int64_t)bh * cv.cap + cv.base + j;
+    const int64_t src = ((int64_t)bh * cv.m + j) * D;
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) cv.cent[slot * D + l + 64 * e] = init[src + l + 64 * e];
+    if (l == 0) cv.valid[slot] = 1;
+}
+
+hipError_t launch_caller_init(const Prob& p, const float* init, CentView cv, hipStream_t s) {
+    dim3 grid((unsigned)((cv.m + 3) / 4), (unsigned)p.BH);
+    if (p.D == 64)
+        hipLaunchKernelGGL(caller_init_kernel<64>, grid, dim3(256), 0, s, init, cv);
+    else
+        hipLaunchKernelGGL(caller_init_kernel<128>, grid, dim3(256), 0, s, init, cv);
+    return hipGetLastError();
+}
+
 // Slots past the last one holding a centre cannot win an assignment: m_eff =
 // min(mcount, last valid slot + 1), one workgroup per head.
 __global__ __launch_bounds__(256) void last_valid_kernel(int cap, int m, const uint8_t* __restrict__ valid,

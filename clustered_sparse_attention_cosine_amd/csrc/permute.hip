@@ -11,26 +11,6 @@ namespace adc {
 
 hipError_t fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 
-__global__ __launch_bounds__(256) void histogram_kernel(const int32_t* __restrict__ labels,
-                                                        int64_t total, int N, int M,
-                                                        int32_t* __restrict__ cnt) {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= total) return;
-    const int64_t bh = i / N;
-    const int lab = labels[i];
-    if (lab >= 0 && lab < M) atomicAdd(&cnt[bh * M + lab], 1);
-}
-
-hipError_t launch_histogram(const Prob& p, const int32_t* labels, int M, int32_t* cnt,
-                            hipStream_t s) {
-    hipError_t e = fill_i32(cnt, (int64_t)p.BH * M, 0, s);
-    if (e != hipSuccess) return e;
-    int64_t total = (int64_t)p.BH * p.N;
-    hipLaunchKernelGGL(histogram_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                       labels, total, p.N, M, cnt);
-    return hipGetLastError();
-}
-
 // Exclusive scan of the counts (one workgroup per head, M <= 8192).
 __global__ __launch_bounds__(1024) void scan_offsets_kernel(const int32_t* __restrict__ cnt, int M,
                                                             int32_t* __restrict__ sizes_out,
@@ -73,27 +53,66 @@ hipError_t launch_scan_offsets(const Prob& p, const int32_t* cnt, int M, int32_t
     return hipGetLastError();
 }
 
-// Stable rank: one workgroup per head sweeps the rows in chunks of 1024.
-// Inside a wave, lanes with equal labels are matched with ballots; the waves
-// of a chunk then take positions from per-label running counters in LDS in
-// wave order, so a row's rank counts exactly the earlier rows of its cluster.
-__global__ __launch_bounds__(1024) void stable_rank_kernel(const int32_t* __restrict__ labels,
-                                                           int N, int M,
-                                                           const int32_t* __restrict__ offsets,
-                                                           int32_t* __restrict__ perm) {
+// Stable counting sort over segments: the rows of a head are cut into
+// segments of SORT_SEG rows; (1) each segment counts its labels in LDS,
+// (2) for every label a column scan over the segments gives each segment's
+// start inside the label's range and the label's total, (3) the totals are
+// scanned into offsets, (4) each segment ranks its rows as the one-workgroup
+// sweep above does, starting every label's counter at offsets[label] plus the
+// rows of that label in the earlier segments. Same permutation, with
+// BH x segments workgroups instead of BH.
+__global__ __launch_bounds__(1024) void seg_hist_kernel(const int32_t* __restrict__ labels, int N, int M,
+                                                        int nseg, int32_t* __restrict__ seg_cnt) {
+    __shared__ int h[8192];
+    const int sg = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+    for (int j = tid; j < M; j += 1024) h[j] = 0;
+    __syncthreads();
+    const int beg = sg * SORT_SEG, end = min(N, beg + SORT_SEG);
+    const int32_t* lab = labels + (int64_t)bh * N;
+    for (int i = beg + tid; i < end; i += 1024) {
+        const int v = lab[i];
+        if (v >= 0 && v < M) atomicAdd(&h[v], 1);
+    }
+    __syncthreads();
+    int32_t* out = seg_cnt + ((int64_t)bh * nseg + sg) * M;
+    for (int j = tid; j < M; j += 1024) out[j] = h[j];
+}
+
+// In place: seg_cnt[s][j] <- rows of label j in segments before s; total[j].
+__global__ __launch_bounds__(256) void seg_scan_kernel(int M, int nseg, int32_t* __restrict__ seg_cnt,
+                                                       int32_t* __restrict__ total) {
+    const int bh = blockIdx.y;
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= M) return;
+    int32_t* c = seg_cnt + (int64_t)bh * nseg * M + j;
+    int run = 0;
+    for (int sg = 0; sg < nseg; ++sg) {
+        const int v = c[(int64_t)sg * M];
+        c[(int64_t)sg * M] = run;
+        run += v;
+    }
+    total[(int64_t)bh * M + j] = run;
+}
+
+__global__ __launch_bounds__(1024) void seg_rank_kernel(const int32_t* __restrict__ labels, int N, int M,
+                                                        int nseg, const int32_t* __restrict__ offsets,
+                                                        const int32_t* __restrict__ seg_cnt,
+                                                        int32_t* __restrict__ perm) {
     __shared__ int running[8192];
-    const int bh = blockIdx.x;
+    const int sg = blockIdx.x, bh = blockIdx.y;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-    for (int j = tid; j < M; j += 1024) running[j] = 0;
+    const int32_t* off = offsets + (int64_t)bh * (M + 1);
+    const int32_t* before = seg_cnt + ((int64_t)bh * nseg + sg) * M;
+    for (int j = tid; j < M; j += 1024) running[j] = off[j] + before[j];
     int nbits = 0;
     while ((1 << nbits) < M) ++nbits;
     const int32_t* lab_h = labels + (int64_t)bh * N;
-    const int32_t* off = offsets + (int64_t)bh * (M + 1);
     const uint64_t lt = (l == 0) ? 0ull : (~0ull >> (64 - l));
     __syncthreads();
-    for (int base = 0; base < N; base += 1024) {
+    const int beg = sg * SORT_SEG, end = min(N, beg + SORT_SEG);
+    for (int base = beg; base < end; base += 1024) {
         const int i = base + tid;
-        const int raw = i < N ? lab_h[i] : -1;
+        const int raw = i < end ? lab_h[i] : -1;
         const bool ok = raw >= 0 && raw < M;   // rows with out-of-range labels are left out
         const int lab = ok ? raw : 0;
         uint64_t m = __ballot(ok);
@@ -116,13 +135,23 @@ __global__ __launch_bounds__(1024) void stable_rank_kernel(const int32_t* __rest
             }
             __syncthreads();
         }
-        if (ok) perm[(int64_t)bh * N + off[lab] + pos] = i;
+        if (ok) perm[(int64_t)bh * N + pos] = i;
     }
 }
 
-hipError_t launch_stable_rank(const Prob& p, const int32_t* labels, int M, const int32_t* offsets,
-                              int32_t* perm, hipStream_t s) {
-    hipLaunchKernelGGL(stable_rank_kernel, dim3(p.BH), dim3(1024), 0, s, labels, p.N, M, offsets, perm);
+int sort_segments(int N) { return (N + SORT_SEG - 1) / SORT_SEG; }
+
+hipError_t launch_counting_sort(const Prob& p, const int32_t* labels, int M, int32_t* seg_cnt,
+                                int32_t* total, int32_t* sizes, int32_t* offsets, int32_t* perm,
+                                hipStream_t s) {
+    const int nseg = sort_segments(p.N);
+    hipLaunchKernelGGL(seg_hist_kernel, dim3(nseg, p.BH), dim3(1024), 0, s, labels, p.N, M, nseg, seg_cnt);
+    hipLaunchKernelGGL(seg_scan_kernel, dim3((M + 255) / 256, p.BH), dim3(256), 0, s, M, nseg, seg_cnt, total);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if ((e = launch_scan_offsets(p, total, M, sizes, offsets, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(seg_rank_kernel, dim3(nseg, p.BH), dim3(1024), 0, s, labels, p.N, M, nseg, offsets,
+                       seg_cnt, perm);
     return hipGetLastError();
 }
 
