@@ -407,6 +407,7 @@ size_t adacluster_select_workspace(const adc_shape* shape, int32_t Cq, int32_t C
     if (check_sel_dims(shape, Cq, Ck)) return 0;
     Carver c(nullptr);
     c.take<float>((size_t)shape->B * shape->H * Cq * Ck);
+    c.take<float>((size_t)shape->B * shape->H * Ck);
     return c.used + 256;
 }
 
@@ -441,11 +442,14 @@ int32_t adacluster_select(const adc_shape* shape, int32_t Cq, int32_t Ck, const 
     Prob p = make_prob(shape);
     Carver c(workspace);
     float* S = c.take<float>((size_t)p.BH * Cq * Ck);
+    float* ln_sizes = c.take<float>((size_t)p.BH * Ck);
     HIPCHK(launch_scores(p, Cq, Ck, qrep, kmax, kmin, centroids, score, k_sizes, n_clusters, S, s));
     if (rule == ADC_SELECT_TOPP)
-        HIPCHK(launch_topp(p, Cq, Ck, S, k_sizes, n_clusters, full_attn, scale, top_p, sel_mask, sel_keys, s));
+        HIPCHK(launch_topp(p, Cq, Ck, S, k_sizes, n_clusters, full_attn, scale, top_p, sel_mask, sel_keys,
+                           ln_sizes, s));
     else
-        HIPCHK(launch_topk(p, Cq, Ck, S, k_sizes, n_clusters, full_attn, top_k, sel_mask, sel_keys, s));
+        HIPCHK(launch_topk(p, Cq, Ck, S, k_sizes, n_clusters, full_attn, top_k, sel_mask, sel_keys,
+                           ln_sizes, s));
     return ADC_OK;
 }
 

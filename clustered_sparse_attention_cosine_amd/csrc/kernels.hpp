@@ -159,10 +159,10 @@ hipError_t launch_scores(const Prob& p, int Cq, int Ck, const float* qrep, const
                          hipStream_t s);
 hipError_t launch_topp(const Prob& p, int Cq, int Ck, const float* S, const int32_t* k_sizes,
                        const int32_t* n_clusters, const uint8_t* full, float scale, float top_p,
-                       uint32_t* mask, int32_t* sel_keys, hipStream_t s);
+                       uint32_t* mask, int32_t* sel_keys, float* ln_sizes, hipStream_t s);
 hipError_t launch_topk(const Prob& p, int Cq, int Ck, const float* S, const int32_t* k_sizes,
                        const int32_t* n_clusters, const uint8_t* full, int top_k,
-                       uint32_t* mask, int32_t* sel_keys, hipStream_t s);
+                       uint32_t* mask, int32_t* sel_keys, float* ln_sizes, hipStream_t s);
 
 // ---------------------------------------------------------------- attention (attn.hip)
 hipError_t launch_build_runs(const Prob& p, int Cq, int Ck, const int32_t* k_offsets,

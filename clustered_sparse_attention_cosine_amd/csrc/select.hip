@@ -333,22 +333,38 @@ __global__ __launch_bounds__(256) void select_kernel(int Cq, int Ck, const float
 // One wave per (head, q-cluster) row for Ck <= 64 * SPL: lane j owns slots
 // j + 64 i (i < SPL), so the slots of a mask word pair come out of one ballot.
 // The same rule as select_kernel, with wave-level fixed-order sums (no
-// workgroup barriers in the 32-step bisection).
+// workgroup barriers in the bisection); the last 16 of its 32 steps run over
+// the few slots that can still move the cut.
+// ln n_b of every slot with members (slots past the head's count or with no
+// members: -inf), once per head instead of once per row.
+__global__ __launch_bounds__(256) void ln_sizes_kernel(int Ck, const int32_t* __restrict__ k_sizes,
+                                                       const int32_t* __restrict__ n_clusters,
+                                                       float* __restrict__ ln_sizes) {
+    const int bh = blockIdx.y;
+    const int b = blockIdx.x * 256 + threadIdx.x;
+    if (b >= Ck) return;
+    const int n = b < min(n_clusters[bh], Ck) ? k_sizes[(int64_t)bh * Ck + b] : 0;
+    ln_sizes[(int64_t)bh * Ck + b] = n > 0 ? logf((float)n) : -INFINITY;
+}
+
 template <bool TOPK, int SPL>
 __global__ __launch_bounds__(256) void select_wave_kernel(int Cq, int Ck, const float* __restrict__ S,
+                                                          const float* __restrict__ ln_sizes,
                                                           const int32_t* __restrict__ k_sizes,
                                                           const int32_t* __restrict__ n_clusters,
                                                           const uint8_t* __restrict__ full, float scale,
                                                           float top_p, int top_k,
                                                           uint32_t* __restrict__ mask,
                                                           int32_t* __restrict__ sel_keys) {
+    __shared__ uint32_t bin_key[4][64];
+    __shared__ float bin_e[4][64];
     const int bh = blockIdx.y;
     const int l = threadIdx.x & 63;
     const int a = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (a >= Cq) return;
     const int words = (Ck + 31) / 32;
-    const int ncl = min(n_clusters[bh], Ck);
     const float* row = S + ((int64_t)bh * Cq + a) * Ck;
+    const float* lns = ln_sizes + (int64_t)bh * Ck;
     const int32_t* ks = k_sizes + (int64_t)bh * Ck;
 
     // keys (order-preserving integer images of l) are kept; l is recovered from
@@ -359,11 +375,11 @@ __global__ __launch_bounds__(256) void select_wave_kernel(int Cq, int Ck, const 
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
         const int b = l + 64 * i;
-        const int n = b < ncl ? ks[b] : 0;
-        const bool ok = n > 0;
+        const float ln = b < Ck ? lns[b] : -INFINITY;
+        const bool ok = ln > -INFINITY;
         if (ok) live |= 1ull << i;
         float v = -INFINITY;
-        if (ok) v = TOPK ? row[b] : fmaf(row[b], scale, logf((float)n));
+        if (ok) v = TOPK ? row[b] : fmaf(row[b], scale, ln);
         lmax = fmaxf(lmax, v);
         key[i] = ok ? order_key(v) : 0u;
     }
@@ -389,14 +405,61 @@ __global__ __launch_bounds__(256) void select_wave_kernel(int Cq, int Ck, const 
             }
             target = top_p * wave_sum_dpp(part);
         }
-        // largest T with mass(key >= T) >= target
+        // largest T with mass(key >= T) >= target: the top 16 bits by bisection
+        // over every owned slot, then the low 16 bits over the slots whose top
+        // bits equal T's (few: keys within 2^-7 relative of the cut), gathered
+        // into a per-wave list in LDS
         uint32_t T = 0;
-        for (int bit = 31; bit >= 0; --bit) {
+        for (int bit = 31; bit >= 16; --bit) {
             const uint32_t cand = T | (1u << bit);
             float part = 0.0f;
 #pragma unroll
             for (int i = 0; i < SPL; ++i) part += key[i] >= cand ? e[i] : 0.0f;
             if (wave_sum_dpp(part) >= target) T = cand;
+        }
+        {
+            const uint32_t hi = T >> 16;
+            float part_hi = 0.0f;
+            int nb = 0;
+            uint32_t* lk = bin_key[threadIdx.x >> 6];
+            float* le = bin_e[threadIdx.x >> 6];
+            const uint64_t below = l == 0 ? 0ull : (~0ull >> (64 - l));
+#pragma unroll
+            for (int i = 0; i < SPL; ++i) {
+                const bool lv = (live >> i) & 1;
+                part_hi += (lv && (key[i] >> 16) > hi) ? e[i] : 0.0f;
+                const bool in = lv && (key[i] >> 16) == hi;
+                const uint64_t m = __ballot(in);
+                const int pos = nb + __popcll(m & below);
+                if (in && pos < 64) {
+                    lk[pos] = key[i];
+                    le[pos] = e[i];
+                }
+                nb += __popcll(m);
+            }
+            const float mass_hi = wave_sum_dpp(part_hi);
+            if (nb <= 64) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                const uint32_t mk = l < nb ? lk[l] : 0u;
+                const float me = l < nb ? le[l] : 0.0f;
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                for (int bit = 15; bit >= 0; --bit) {
+                    const uint32_t cand = T | (1u << bit);
+                    if (mass_hi + wave_sum_dpp(mk >= cand ? me : 0.0f) >= target) T = cand;
+                }
+            } else {
+                for (int bit = 15; bit >= 0; --bit) {
+                    const uint32_t cand = T | (1u << bit);
+                    float part = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < SPL; ++i) part += key[i] >= cand ? e[i] : 0.0f;
+                    if (wave_sum_dpp(part) >= target) T = cand;
+                }
+            }
         }
         float above = 0.0f, e_tie = 0.0f;
         int nties = 0;
@@ -447,14 +510,17 @@ template <bool TOPK>
 static void launch_select_t(const Prob& p, int Cq, int Ck, const float* S, const int32_t* k_sizes,
                             const int32_t* n_clusters, const uint8_t* full, float scale,
                             float top_p, int top_k, uint32_t* mask, int32_t* sel_keys,
-                            hipStream_t s) {
+                            float* ln_sizes, hipStream_t s) {
     const dim3 wgrid((unsigned)((Cq + 3) / 4), (unsigned)p.BH);
+    if (Ck <= 4096)
+        hipLaunchKernelGGL(ln_sizes_kernel, dim3((unsigned)((Ck + 255) / 256), (unsigned)p.BH), dim3(256), 0,
+                           s, Ck, k_sizes, n_clusters, ln_sizes);
     if (Ck <= 1024)
-        hipLaunchKernelGGL((select_wave_kernel<TOPK, 16>), wgrid, dim3(256), 0, s, Cq, Ck, S, k_sizes,
-                           n_clusters, full, scale, top_p, top_k, mask, sel_keys);
+        hipLaunchKernelGGL((select_wave_kernel<TOPK, 16>), wgrid, dim3(256), 0, s, Cq, Ck, S, ln_sizes,
+                           k_sizes, n_clusters, full, scale, top_p, top_k, mask, sel_keys);
     else if (Ck <= 4096)
-        hipLaunchKernelGGL((select_wave_kernel<TOPK, 64>), wgrid, dim3(256), 0, s, Cq, Ck, S, k_sizes,
-                           n_clusters, full, scale, top_p, top_k, mask, sel_keys);
+        hipLaunchKernelGGL((select_wave_kernel<TOPK, 64>), wgrid, dim3(256), 0, s, Cq, Ck, S, ln_sizes,
+                           k_sizes, n_clusters, full, scale, top_p, top_k, mask, sel_keys);
     else
         hipLaunchKernelGGL(select_kernel<TOPK>, dim3((unsigned)Cq, (unsigned)p.BH), dim3(256), 0, s,
                            Cq, Ck, S, k_sizes, n_clusters, full, scale, top_p, top_k, mask, sel_keys);
@@ -462,15 +528,17 @@ static void launch_select_t(const Prob& p, int Cq, int Ck, const float* S, const
 
 hipError_t launch_topp(const Prob& p, int Cq, int Ck, const float* S, const int32_t* k_sizes,
                        const int32_t* n_clusters, const uint8_t* full, float scale, float top_p,
-                       uint32_t* mask, int32_t* sel_keys, hipStream_t s) {
-    launch_select_t<false>(p, Cq, Ck, S, k_sizes, n_clusters, full, scale, top_p, 0, mask, sel_keys, s);
+                       uint32_t* mask, int32_t* sel_keys, float* ln_sizes, hipStream_t s) {
+    launch_select_t<false>(p, Cq, Ck, S, k_sizes, n_clusters, full, scale, top_p, 0, mask, sel_keys,
+                           ln_sizes, s);
     return hipGetLastError();
 }
 
 hipError_t launch_topk(const Prob& p, int Cq, int Ck, const float* S, const int32_t* k_sizes,
                        const int32_t* n_clusters, const uint8_t* full, int top_k, uint32_t* mask,
-                       int32_t* sel_keys, hipStream_t s) {
-    launch_select_t<true>(p, Cq, Ck, S, k_sizes, n_clusters, full, 1.0f, 1.0f, top_k, mask, sel_keys, s);
+                       int32_t* sel_keys, float* ln_sizes, hipStream_t s) {
+    launch_select_t<true>(p, Cq, Ck, S, k_sizes, n_clusters, full, 1.0f, 1.0f, top_k, mask, sel_keys,
+                          ln_sizes, s);
     return hipGetLastError();
 }
 
