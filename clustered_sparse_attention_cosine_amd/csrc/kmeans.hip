@@ -44,6 +44,14 @@ hipError_t fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
     return hipGetLastError();
 }
 
+__global__ void zero2_i32_kernel(int32_t* a, int32_t* b, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        a[i] = 0;
+        b[i] = 0;
+    }
+}
+
 __global__ void fill_u8_kernel(uint8_t* p, int64_t n, uint8_t v) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = v;
@@ -865,9 +873,10 @@ static hipError_t launch_refine_full(const Prob& p, const void* x, int normalize
 hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
                          int normalize, CentView cv, const int32_t* mcount, int32_t* labels,
                          FlagSet fs, hipStream_t s) {
-    hipError_t e = fill_i32(fs.count, p.BH, 0, s);
+    hipLaunchKernelGGL(zero2_i32_kernel, dim3((unsigned)((p.BH + 255) / 256)), dim3(256), 0, s, fs.count,
+                       fs.over_count, p.BH);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if ((e = fill_i32(fs.over_count, p.BH, 0, s)) != hipSuccess) return e;
     dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)p.BH);
     launch_assign_t<false>(p, grid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, 0, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
