@@ -436,46 +436,47 @@ __device__ __forceinline__ uint4 v_frag(const unsigned char* p) {
 }
 
 // Online softmax of one 16-query block over NKB 16-key blocks of a tile (the
-// lane holds query c16 and keys (kb0 + kb)*16 + 4g + i). Scores come in raw;
-// sl2 = scale * log2(e) is applied inside the exponent. MASK: the tile runs
-// past the last selected key (positions >= total get probability 0).
+// lane holds query c16 and keys kb*16 + 4g + i of the blocks). Scores come in raw; sl2 = scale *
+// log2(e) is applied inside the exponent. LAST: positions >= total get
+// probability 0. FIRST: the first tile of the item sets the running maximum m.
 //
-// The running maximum m (log2 units) is raised only when some row of the wave
-// sees a score above m + 8; otherwise the stale m is kept, so every
-// probability is at most 2^8 (exact as an f32 summand, finite in fp16) and the
-// rescale of O is skipped. The result is the same softmax: numerator and
-// denominator share the factor 2^-m whatever m is. The row sums are
-// accumulated by the matrix cores (a block of ones in the P.V product), so
-// they are part of o and rescaled with it.
-template <int DB, int NKB, bool MASK>
-__device__ __forceinline__ void softmax_block(f32x4 (&sc)[NKB], float sl2, int p0, int g, int total,
-                                              float& m_run, f32x4 (&o)[DB + 1]) {
-    if constexpr (MASK) {
+// m (log2 units) is raised only when some score of the wave exceeds m + 8, a
+// test each lane makes on its own maximum against thr = (m + 8) / sl2 (the
+// maximum across the four lanes of a query is formed only then); otherwise
+// the stale m is kept, so every probability is at most 2^8 (exact as an f32
+// summand, finite in fp16) and O is not rescaled. The result is the same
+// softmax: numerator and denominator share the factor 2^-m whatever m is.
+// The row sums are accumulated by the matrix cores (a block of ones in the
+// P.V product), so they are part of o and rescaled with it.
+template <int DB, int NKB>
+__device__ __forceinline__ void softmax_tile(f32x4 (&sc)[NKB], float sl2, int lim, bool last,
+                                             bool first, float& m_run, float& thr,
+                                             f32x4 (&o)[DB + 1]) {
+    if (last) {
+        // lim = total - (block start + 4g): keys kb*16 + i >= lim are past the selection
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (p0 + kb * 16 + g * 4 + i >= total) sc[kb][i] = -INFINITY;
+                if (kb * 16 + i >= lim) sc[kb][i] = -INFINITY;
     }
     float mx = fmaxf(fmaxf(sc[0][0], sc[0][1]), sc[0][2]);
-    mx = fmaxf(fmaxf(mx, sc[0][3]), sc[1][0]);
-    mx = fmaxf(fmaxf(mx, sc[1][1]), sc[1][2]);
-    mx = fmaxf(mx, sc[1][3]);
-    if constexpr (NKB == 4) {
-        mx = fmaxf(fmaxf(mx, sc[2][0]), sc[2][1]);
-        mx = fmaxf(fmaxf(mx, sc[2][2]), sc[2][3]);
-        mx = fmaxf(fmaxf(mx, sc[3][0]), sc[3][1]);
-        mx = fmaxf(fmaxf(mx, sc[3][2]), sc[3][3]);
-    }
-    const float ms = col_max4(mx) * sl2;
-    if (__ballot(ms > m_run + 8.0f) != 0) {
-        const float m_new = fmaxf(m_run, ms);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (kb > 0 || i > 2) mx = fmaxf(mx, sc[kb][i]);
+    if (first || __ballot(mx > thr) != 0) {
+        // the first tile holds position 0 of the selection, so its maximum is finite
+        const float mq = col_max4(mx) * sl2;
+        const float m_new = first ? (mq > -INFINITY ? mq : 0.0f) : fmaxf(m_run, mq);
+        const float alpha = first ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
         for (int db = 0; db <= DB; ++db) o[db] *= alpha;
         m_run = m_new;
+        thr = (m_new + 8.0f) / sl2;
     }
-    const float nb = (m_run == -INFINITY) ? 0.0f : -m_run;
+    const float nb = -m_run;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -489,9 +490,9 @@ __device__ __forceinline__ void softmax_block(f32x4 (&sc)[NKB], float sl2, int p
 // K/V tiles of 64 keys are copied straight into NB LDS buffers: while tile t
 // is computed the copies of tiles t+1 .. t+NB-1 are in flight and the last
 // wave looks up the key rows of tile t+NB, so one barrier per tile suffices
-// and no register staging is needed. Operands are 16-bit planes (NP = 1: K bf16, V fp16; NP = 2:
-// bf16 hi and lo of f32 data, every product of order <= 1 accumulated, three
-// MFMAs per product, near f32 accuracy).
+// and no register staging is needed. Operands are 16-bit planes (NP = 1: K
+// bf16, V fp16; NP = 2: bf16 hi and lo of f32 data, every product of order
+// <= 1 accumulated, three MFMAs per product, near f32 accuracy).
 template <typename T, int D, typename TO, int WPE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, 8)))
 void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restrict__ q_perm,
@@ -589,7 +590,8 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
     const u16* const Kh1 = PREC ? K1 + hoff : Kh0;
     const u16* const Vh1 = PREC ? V1 + hoff : Vh0;
 
-    float m_run = -INFINITY;
+    float m_run = 0.0f;  // running maximum (log2 units), set by the first tile
+    float thr = 0.0f;    // (m_run + 8) / sl2: a raw score above it raises m_run
     f32x4 o[DB + 1];  // O^T blocks and the row-sum block
 #pragma unroll
     for (int db = 0; db <= DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -630,18 +632,16 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
         tile_copy<D, NP, NT>(buf(std::integral_constant<int, 2>{}), w, l, krow[2], Kh0, Kh1, Vh0, Vh1);
     }
 
-    // Scores, softmax and P.V of NKB 16-key blocks starting at block kb0 of the
-    // tile in buffer b.
-    auto compute = [&](const unsigned char* tb, int p0, int kb0, auto nkb_c, auto mask_c) __attribute__((always_inline)) {
-        constexpr int NKB = decltype(nkb_c)::value;
-        constexpr bool MASK = decltype(mask_c)::value;
+    // Scores, softmax and P.V of the tile in buffer tb (first position p0).
+    auto compute = [&](const unsigned char* tb, int p0, bool first) __attribute__((always_inline)) {
+        constexpr int NKB = 4;
         f32x4 sc[NKB];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
-                const unsigned char* kp = tb + (kb0 + kb) * 16 * RB + koff[kc];
+                const unsigned char* kp = tb + kb * 16 * RB + koff[kc];
                 const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kp);
                 if constexpr (PREC) {
                     const bf16x8 kl = *reinterpret_cast<const bf16x8*>(kp + TG::PLANE);
@@ -651,11 +651,10 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
                 sc[kb] = mfma16(ka, qf[0][kc], sc[kb]);
             }
         }
-        softmax_block<DB, NKB, MASK>(sc, sl2, p0, g, total, m_run, o);
+        softmax_tile<DB, NKB>(sc, sl2, total - p0 - 4 * g, p0 + 64 > total, first, m_run, thr, o);
 #pragma unroll
         for (int h = 0; h < NKB / 2; ++h) {
-            const int kc2 = kb0 / 2 + h;
-            const unsigned char* vb0 = tb + NP * TG::PLANE + kc2 * 32 * RB;
+            const unsigned char* vb0 = tb + NP * TG::PLANE + h * 32 * RB;
             if constexpr (PREC) {
                 const unsigned char* vb1 = vb0 + TG::PLANE;
                 const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u,
@@ -710,11 +709,7 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
         if (w == LW) lookup(t + NB);
         tile_copy<D, NP, NT>(buf(std::integral_constant<int, J + NB - 1>{}), w, l,
                              krow[(t + NB - 1) & 3], Kh0, Kh1, Vh0, Vh1);
-        if (t < ntiles && live) {
-            const int t0 = t * 64;
-            if (t0 + 64 > total) compute(buf(j_c), t0, 0, std::integral_constant<int, 4>{}, std::true_type{});
-            else compute(buf(j_c), t0, 0, std::integral_constant<int, 4>{}, std::false_type{});
-        }
+        if (t < ntiles && live) compute(buf(j_c), t * 64, t == 0);
     };
     for (int t = 0; t < ntiles; t += NB) {
         step(t, std::integral_constant<int, 0>{});
