@@ -368,7 +368,9 @@ struct TileGeom {
     static constexpr int RB = 2 * D;                    // bytes per row of a plane
     static constexpr int PLANE = 64 * RB;               // bytes per plane of a tile
     static constexpr int TILE = 2 * NP * PLANE;         // K planes, then V planes
-    static constexpr int NB = TILE <= 32768 ? 4 : 2;    // tiles resident
+    // tiles resident: three for 16 KB tiles (bf16, D = 64), so that three
+    // workgroups fit a CU's LDS; four up to 32 KB; two beyond
+    static constexpr int NB = TILE <= 16384 ? 3 : TILE <= 32768 ? 4 : 2;
     static constexpr int NW = NT / 64;
     static constexpr int IPW = PLANE / 1024 / NW;       // 1 KB blocks per plane per wave
     static constexpr int L = 2 * NP * IPW;              // copies per wave per tile
@@ -518,7 +520,7 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
     // touch the buffer being read
     __shared__ __attribute__((aligned(1024))) unsigned char tb0[TG::TILE], tb1[TG::TILE];
     __shared__ __attribute__((aligned(1024))) unsigned char tb2[NB > 2 ? TG::TILE : 16];
-    __shared__ __attribute__((aligned(1024))) unsigned char tb3[NB > 2 ? TG::TILE : 16];
+    __shared__ __attribute__((aligned(1024))) unsigned char tb3[NB > 3 ? TG::TILE : 16];
     auto buf = [&](auto j_c) __attribute__((always_inline)) -> unsigned char* {
         constexpr int J = decltype(j_c)::value % NB;
         if constexpr (J == 0) return tb0;
@@ -528,7 +530,7 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
     };
     __shared__ int krow[4][64];
     // the work item's runs (first key row, first position) when they fit
-    constexpr int RL = 512;
+    constexpr int RL = 256;
     __shared__ int run_s[RL], run_p[RL + 1];
 
     __shared__ int sh_item;
@@ -714,10 +716,8 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
     for (int t = 0; t < ntiles; t += NB) {
         step(t, std::integral_constant<int, 0>{});
         step(t + 1, std::integral_constant<int, 1>{});
-        if constexpr (NB > 2) {
-            step(t + 2, std::integral_constant<int, 2>{});
-            step(t + 3, std::integral_constant<int, 3>{});
-        }
+        if constexpr (NB > 2) step(t + 2, std::integral_constant<int, 2>{});
+        if constexpr (NB > 3) step(t + 3, std::integral_constant<int, 3>{});
     }
 
     if (qok) {
@@ -737,7 +737,7 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
 }
 
 #ifndef ADC_ATTN_WPE64
-#define ADC_ATTN_WPE64 4
+#define ADC_ATTN_WPE64 6
 #endif
 constexpr int ATTN_WPE64 = ADC_ATTN_WPE64;  // waves per SIMD asked of the bf16 D=64 kernel
 
@@ -761,7 +761,8 @@ static void launch_attn_t(const Prob& p, int Cq, const void* q, const int32_t* q
                           const u16* v1, const int32_t* run_start, const int32_t* run_pos,
                           const int32_t* n_runs, int run_cap, const AttnSched& sc, int cap,
                           float sl2, void* out, float* lse, hipStream_t s) {
-    // waves per SIMD: two workgroups per CU where the registers allow it
+    // waves per SIMD: three workgroups per CU for bf16 D = 64 (80 registers,
+    // three 16 KB tile buffers), one otherwise
     constexpr int W64 = sizeof(T) == 2 ? ATTN_WPE64 : 2;
     const int wpe = p.D == 64 ? W64 : 2;
     auto k = p.D == 64 ? attn_kernel<T, 64, TO, W64> : attn_kernel<T, 128, TO, 2>;
