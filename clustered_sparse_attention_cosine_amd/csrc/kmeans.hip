@@ -485,7 +485,13 @@ __device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c)
     return r;
 }
 
-template <typename T, int D, bool F32X, bool CAND>
+// FOLD (rows not rescaled, s = 1; assignment pass only): the MFMA accumulators
+// start at -(||c_j||^2 + B) / 2, so they end at a_j = x.c_j - (||c_j||^2 + B) / 2
+// = -d'_j / 2 < 0, and the bit patterns of these negative values, read as
+// unsigned integers, already order the distances ascending: the fma is
+// dropped (3 VALU ops per distance). The accumulator then carries the centre
+// term through the f32 accumulation, which the error bound allows for.
+template <typename T, int D, bool F32X, bool CAND, bool FOLD>
 __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
                                                      const float* __restrict__ inv_norm,
                                                      int normalize, CentView cv,
@@ -624,7 +630,9 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
             *reinterpret_cast<u32x4*>(&sh_hi[BUF][o]) = ph[i];                             \
             *reinterpret_cast<u32x4*>(&sh_lo[BUF][o]) = pl[i];                             \
         }                                                                                  \
-        if (tid < 64) sh_c2[BUF][tid] = (TILE) * 64 + tid < M ? pc2 + bwg : INFINITY;      \
+        if (tid < 64)                                                                      \
+            sh_c2[BUF][tid] = FOLD ? ((TILE) * 64 + tid < M ? -0.5f * (pc2 + bwg) : -INFINITY) \
+                                   : ((TILE) * 64 + tid < M ? pc2 + bwg : INFINITY);        \
     } while (0)
     if (t_begin < t_end) {
         ADC_LOAD_TILE(t_begin);
@@ -641,9 +649,10 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
         uint64_t hits = 0;  // CAND: candidates of this tile, bit pb*16 + cb*4 + i
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
+            const f32x4 c2v = *reinterpret_cast<const f32x4*>(&sh_c2[buf][cb * 16 + g * 4]);
             f32x4 acc[4];
 #pragma unroll
-            for (int pb = 0; pb < 4; ++pb) acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int pb = 0; pb < 4; ++pb) acc[pb] = FOLD ? c2v : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 const int off = (cb * 16 + c16) * LD + kc * 32 + g * 8;
@@ -656,12 +665,11 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
                     if constexpr (F32X) acc[pb] = mfma16(ah, xl[pb][kc], acc[pb]);
                 }
             }
-            const f32x4 c2v = *reinterpret_cast<const f32x4*>(&sh_c2[buf][cb * 16 + g * 4]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
 #pragma unroll
                 for (int pb = 0; pb < 4; ++pb) {
-                    const float dv = fmaf(kx[pb], acc[pb][i], c2v[i]);
+                    const float dv = FOLD ? acc[pb][i] : fmaf(kx[pb], acc[pb][i], c2v[i]);
                     if constexpr (CAND) {
                         const int j = tile * 64 + cb * 16 + g * 4 + i;
                         if (j < M && dv <= thr[pb]) hits |= 1ull << (pb * 16 + cb * 4 + i);
@@ -708,16 +716,21 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
                 if (take) { b1[pb] = ob1; bj = obj; }
             }
             if (g == 0 && ok[pb]) {
-                const bool finite = b1[pb] < 0x7f800000u;
+                // keys are d' >= 0, or (FOLD) -d'/2 < 0; +-inf and NaN are not finite
+                auto fin = [](uint32_t k) { return FOLD ? (k >= 0x80000000u && k < 0xff800000u) : k < 0x7f800000u; };
+                auto dec = [](uint32_t k) { return FOLD ? -2.0f * __uint_as_float(k) : __uint_as_float(k); };
+                const bool finite = fin(b1[pb]);
                 // no finite distance (no centre, or a NaN row): slot 0, and the row is flagged
                 labels[(int64_t)bh * N + rr[pb]] = finite ? bj : 0;
-                const float d1 = __uint_as_float(b1[pb]);
-                const float d2 = b2[pb] < 0x7f800000u ? __uint_as_float(b2[pb]) : INFINITY;
+                const float d1 = dec(b1[pb]);
+                const float d2 = fin(b2[pb]) ? dec(b2[pb]) : INFINITY;
                 // contraction error of one d' (hi/lo residual and f32 accumulation,
                 // plus the rounding of ||c||^2 + B and of the final fma); the key
                 // truncation moves a value by less than 2^-19 of itself
+                // (FOLD: up to 16 f32 roundings of accumulator values as large as
+                // (||c||^2 + B) / 2 + s||x|| ||c||, i.e. 2^-19 of the same sum in d' units)
                 const float err = ERR_X * xn[pb] * cmax + ERR_C * c2max +
-                                  0x1.0p-22f * (c2max + bwg + 2.0f * xn[pb] * cmax);
+                                  (FOLD ? 0x1.0p-19f : 0x1.0p-22f) * (c2max + bwg + 2.0f * xn[pb] * cmax);
                 if (!finite || !(d2 - d1 > 2.0f * err + 0x1.0p-17f * d2)) {
                     const int fpos = atomicAdd(&fs.count[bh], 1);
                     fs.list[(int64_t)bh * N + fpos] = rr[pb];
@@ -731,17 +744,17 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, in
     }
 }
 
-template <bool CAND>
+template <bool CAND, bool FOLD>
 static void launch_assign_t(const Prob& p, dim3 grid, const void* x, RowSet rs,
                             const float* inv_norm, int normalize, CentView cv,
                             const int32_t* mcount, int32_t* labels, FlagSet fs, int tps,
                             hipStream_t s) {
     if (p.bf16) {
-        auto k = p.D == 64 ? assign_kernel<u16, 64, false, CAND> : assign_kernel<u16, 128, false, CAND>;
+        auto k = p.D == 64 ? assign_kernel<u16, 64, false, CAND, FOLD> : assign_kernel<u16, 128, false, CAND, FOLD>;
         hipLaunchKernelGGL(k, grid, dim3(256), 0, s, (const u16*)x, p.N, rs, inv_norm, normalize, cv,
                            mcount, labels, fs, tps);
     } else {
-        auto k = p.D == 64 ? assign_kernel<float, 64, true, CAND> : assign_kernel<float, 128, true, CAND>;
+        auto k = p.D == 64 ? assign_kernel<float, 64, true, CAND, FOLD> : assign_kernel<float, 128, true, CAND, FOLD>;
         hipLaunchKernelGGL(k, grid, dim3(256), 0, s, (const float*)x, p.N, rs, inv_norm, normalize,
                            cv, mcount, labels, fs, tps);
     }
@@ -878,13 +891,17 @@ hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* i
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)p.BH);
-    launch_assign_t<false>(p, grid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, 0, s);
+    // rows that are not rescaled take the folded form of the assignment pass
+    if (!normalize && !inv_norm)
+        launch_assign_t<false, true>(p, grid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, 0, s);
+    else
+        launch_assign_t<false, false>(p, grid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, 0, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // candidate pass: the centre tiles of the flagged rows are split 8 per workgroup
     constexpr int TPS = 8;
     const int tiles = (cv.m + 63) / 64;
     dim3 cgrid((unsigned)((p.N + 255) / 256), (unsigned)p.BH, (unsigned)((tiles + TPS - 1) / TPS));
-    launch_assign_t<true>(p, cgrid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, TPS, s);
+    launch_assign_t<true, false>(p, cgrid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, TPS, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 egrid(32, (unsigned)p.BH);
     if (p.bf16) {
