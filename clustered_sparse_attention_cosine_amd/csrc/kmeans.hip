@@ -491,8 +491,10 @@ __device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c)
 // unsigned integers, already order the distances ascending: the fma is
 // dropped (3 VALU ops per distance). The accumulator then carries the centre
 // term through the f32 accumulation, which the error bound allows for.
+// bf16 rows, D = 64: 128 registers at most, four workgroups per CU
 template <typename T, int D, bool F32X, bool CAND, bool FOLD>
-__global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && !F32X ? 4 : 1, 8)))
+void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
                                                      const float* __restrict__ inv_norm,
                                                      int normalize, CentView cv,
                                                      const int32_t* __restrict__ mcount,
