@@ -97,8 +97,11 @@ hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* i
                          int normalize, CentView cv, const int32_t* mcount, int32_t* labels,
                          FlagSet fs, hipStream_t s);
 // Centroid sums (f32 atomics) and member counts for the current labels.
+// order (may be null): a permutation of the rows [BH][N] to take them in
+// (rows in one run of equal labels share one atomic per dimension).
 hipError_t launch_update_accum(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
-                               const int32_t* labels, CentView cv, hipStream_t s);
+                               const int32_t* labels, CentView cv, hipStream_t s,
+                               const int32_t* order = nullptr);
 
 // ---------------------------------------------------------------- multi-stage state
 struct StageState {

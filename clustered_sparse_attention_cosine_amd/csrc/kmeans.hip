@@ -921,12 +921,15 @@ hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* i
 // Each wave takes 64 consecutive rows: it stages them in LDS (RS rows at a
 // time) with coalesced 16-byte loads, all in flight at once, then walks them
 // with one lane per dimension, folding runs of equal labels in registers
-// before one atomic add per run and dimension.
+// before one atomic add per run and dimension. With `order` (a permutation of
+// the rows, e.g. sorted by an earlier assignment) the rows are taken in that
+// order, so runs of equal labels are long and few atomics remain.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__ X, int N, RowSet rs,
                                                            const float* __restrict__ inv_norm,
                                                            const int32_t* __restrict__ labels,
-                                                           CentView cv) {
+                                                           CentView cv,
+                                                           const int32_t* __restrict__ order) {
     constexpr int E = D / 64;
     constexpr int RS = D == 64 ? 64 : 32;          // rows staged at once
     constexpr int LDX = D + 16 / (int)sizeof(T);   // padded row stride (elements)
@@ -939,8 +942,9 @@ __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int base = blockIdx.x * 256 + w * 64;
     if (base >= n) return;
-    const int r = base + l;
-    const bool okr = r < n;
+    const int r0 = base + l;
+    const bool okr = r0 < n;
+    const int r = (okr && order) ? order[(int64_t)bh * N + r0] : r0;
     const int lab_l = okr ? labels[(int64_t)bh * N + r] : -1;
     const int tok_l = okr ? (rs.rows ? rs.rows[(int64_t)bh * N + r] : r) : 0;
     const float s_l = (inv_norm && okr) ? inv_norm[(int64_t)bh * N + tok_l] : 1.0f;
@@ -997,22 +1001,23 @@ __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__
 }
 
 hipError_t launch_update_accum(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
-                               const int32_t* labels, CentView cv, hipStream_t s) {
+                               const int32_t* labels, CentView cv, hipStream_t s,
+                               const int32_t* order) {
     dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)p.BH);
     if (p.bf16) {
         if (p.D == 64)
             hipLaunchKernelGGL((update_accum_kernel<u16, 64>), grid, dim3(256), 0, s, (const u16*)x,
-                               p.N, rs, inv_norm, labels, cv);
+                               p.N, rs, inv_norm, labels, cv, order);
         else
             hipLaunchKernelGGL((update_accum_kernel<u16, 128>), grid, dim3(256), 0, s,
-                               (const u16*)x, p.N, rs, inv_norm, labels, cv);
+                               (const u16*)x, p.N, rs, inv_norm, labels, cv, order);
     } else {
         if (p.D == 64)
             hipLaunchKernelGGL((update_accum_kernel<float, 64>), grid, dim3(256), 0, s,
-                               (const float*)x, p.N, rs, inv_norm, labels, cv);
+                               (const float*)x, p.N, rs, inv_norm, labels, cv, order);
         else
             hipLaunchKernelGGL((update_accum_kernel<float, 128>), grid, dim3(256), 0, s,
-                               (const float*)x, p.N, rs, inv_norm, labels, cv);
+                               (const float*)x, p.N, rs, inv_norm, labels, cv, order);
     }
     return hipGetLastError();
 }
