@@ -369,8 +369,9 @@ struct TileGeom {
     static constexpr int PLANE = 64 * RB;               // bytes per plane of a tile
     static constexpr int TILE = 2 * NP * PLANE;         // K planes, then V planes
     // tiles resident: three for 16 KB tiles (bf16, D = 64), so that three
-    // workgroups fit a CU's LDS; four up to 32 KB; two beyond
-    static constexpr int NB = TILE <= 16384 ? 3 : TILE <= 32768 ? 4 : 2;
+    // workgroups fit a CU's LDS; two beyond (two workgroups per CU for 32 KB
+    // tiles: bf16 D = 128, f32 D = 64)
+    static constexpr int NB = TILE <= 16384 ? 3 : 2;
     static constexpr int NW = NT / 64;
     static constexpr int IPW = PLANE / 1024 / NW;       // 1 KB blocks per plane per wave
     static constexpr int L = 2 * NP * IPW;              // copies per wave per tile
@@ -762,10 +763,12 @@ static void launch_attn_t(const Prob& p, int Cq, const void* q, const int32_t* q
                           const int32_t* n_runs, int run_cap, const AttnSched& sc, int cap,
                           float sl2, void* out, float* lse, hipStream_t s) {
     // waves per SIMD: three workgroups per CU for bf16 D = 64 (80 registers,
-    // three 16 KB tile buffers), one otherwise
-    constexpr int W64 = sizeof(T) == 2 ? ATTN_WPE64 : 2;
-    const int wpe = p.D == 64 ? W64 : 2;
-    auto k = p.D == 64 ? attn_kernel<T, 64, TO, W64> : attn_kernel<T, 128, TO, 2>;
+    // three 16 KB tile buffers), two for bf16 D = 128 and f32 D = 64 (at most
+    // 128 registers, two 32 KB buffers), one for f32 D = 128 (64 KB tiles)
+    constexpr int W64 = sizeof(T) == 2 ? ATTN_WPE64 : 4;
+    constexpr int W128 = sizeof(T) == 2 ? 4 : 2;
+    const int wpe = p.D == 64 ? W64 : W128;
+    auto k = p.D == 64 ? attn_kernel<T, 64, TO, W64> : attn_kernel<T, 128, TO, W128>;
     // as many workgroups as fit at once (wpe * 4 SIMDs / 8 waves per CU), in
     // whole rounds of the eight XCDs
     const int per_cu = std::max(1, wpe / 2);
