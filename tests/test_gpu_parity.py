@@ -366,6 +366,43 @@ def test_cluster_q_first_assignment_and_lockstep(case):
         assert np.array_equal(host(Q["offsets"])[0, h], off)
 
 
+# ----------------------------------------------------------------- every Lloyd round
+@pytest.mark.parametrize("case", ["bf16_d64", "bf16_d128"])
+@pytest.mark.parametrize("tensor", ["q", "k"])
+def test_lloyd_rounds_are_exact_assignments(case, tensor):
+    """Rounds 1..5 from the same caller centres: round r's labels are the exact
+    assignment (up to near ties) to the member means of round r-1's labels (a
+    slot left empty keeps its centre), so no round may keep a label the exact
+    assignment would change."""
+    w, g = _inputs(case)
+    H, D = w.H, w.D
+    m = w.q_clusters if tensor == "q" else w.k_base
+    rng = np.random.default_rng(3)
+    xs = []
+    c0 = np.zeros((1, H, m, D), np.float32)
+    for h in range(H):
+        xf = synth.as_f32(g[tensor][0, h])
+        xh = oracle.normalize(xf) if tensor == "q" else xf
+        xs.append(xh)
+        c0[0, h] = xh[rng.choice(w.N, m, replace=False)]
+    cent = [c0[0, h].astype(np.float64) for h in range(H)]
+    prev = None
+    for r in range(1, 6):
+        if tensor == "q":
+            out = adc.cluster_q(dev(g["q"]), m, iters=r, init="caller", init_centroids=dev(c0))
+        else:
+            out = adc.cluster_k(dev(g["k"]), dev(g["v"]), m, iters=r, adaptive=False, init="caller",
+                                init_centroids=dev(c0))
+        lab = host(out["assign"])
+        for h in range(H):
+            if prev is not None:
+                cent[h] = oracle.update(xs[h], prev[0, h], cent[h])[0]
+            bad, diff, ties = labels_match(lab[0, h], *oracle.assign(xs[h], cent[h]))
+            print(f"{case} {tensor} round {r} head {h}: differing {diff}, near ties {ties}, violating {bad}")
+            assert bad == 0
+        prev = lab
+
+
 # ----------------------------------------------------------------- key clustering
 def test_cluster_k_fixed_first_round_kmeanspp():
     w, g = _inputs("tiny")
