@@ -102,6 +102,12 @@ struct KmeansWs {
     int32_t* hist = nullptr;
     int32_t* seg_cnt = nullptr;
     int32_t* m_eff = nullptr;
+    // distance bounds of the Lloyd rounds over every row
+    float* ub = nullptr;
+    float* lb = nullptr;
+    int32_t* rlist = nullptr;
+    int32_t* rcount = nullptr;
+    float* drift = nullptr;
 };
 
 void plan_kmeans(Carver& c, const Prob& p, int cap, bool want_inv, bool kpp, bool want_xhat,
@@ -125,6 +131,11 @@ void plan_kmeans(Carver& c, const Prob& p, int cap, bool want_inv, bool kpp, boo
     w.hist = c.take<int32_t>(bhc);
     w.seg_cnt = c.take<int32_t>(bhc * sort_segments(p.N));
     w.m_eff = c.take<int32_t>(p.BH);
+    w.ub = c.take<float>(bhn);
+    w.lb = c.take<float>(bhn);
+    w.rlist = c.take<int32_t>(bhn);
+    w.rcount = c.take<int32_t>(p.BH);
+    w.drift = c.take<float>(bhc);
     if (kpp) {
         if (want_xhat) w.xhat = c.take<float>(bhn * p.D);
         w.d2 = c.take<double>(bhn);
@@ -188,14 +199,28 @@ struct SortScratch {
 // cluster is then one run, which the update folds into one atomic per
 // dimension and wave, so its f32 atomics (about 60 % of its time in row order)
 // nearly vanish. The sums are the same up to f32 rounding order.
+// On every row the rounds also keep distance bounds (Hamerly's test): from the
+// second round on, only rows whose bounds no longer prove their label are
+// assigned again; the others keep it, which the exact assignment would too.
 hipError_t lloyd(const Prob& p, const void* x, int normalize, RowSet rs, const float* inv_norm,
                  CentView cv, int iters, bool final_update, int32_t* labels, const KmeansWs& w,
                  hipStream_t s, const int32_t* mcount = nullptr, const SortScratch* ss = nullptr) {
     hipError_t e;
     const int32_t* order = nullptr;
+    const bool bounds = ss && !rs.rows;
+    FlagSet fs = flags_of(w);
+    if (bounds) {
+        fs.ub = w.ub;
+        fs.lb = w.lb;
+    }
     for (int it = 0; it < iters; ++it) {
-        if ((e = launch_assign(p, x, rs, inv_norm, normalize, cv, mcount, labels, flags_of(w), s)))
-            return e;
+        RowSet ra = rs;
+        if (bounds && it > 0) {
+            if ((e = launch_bound_filter(p, rs, cv, labels, w.ub, w.lb, w.drift, w.rlist, w.rcount, s)))
+                return e;
+            ra = RowSet{w.rlist, w.rcount, rs.active, 1};
+        }
+        if ((e = launch_assign(p, x, ra, inv_norm, normalize, cv, mcount, labels, fs, s))) return e;
         if (it + 1 < iters || final_update) {
             if (ss && !rs.rows) {
                 if ((e = launch_counting_sort(p, labels, cv.m, w.seg_cnt, w.hist, ss->sizes, ss->offsets,
@@ -204,7 +229,12 @@ hipError_t lloyd(const Prob& p, const void* x, int normalize, RowSet rs, const f
                 order = ss->perm;
             }
             if ((e = launch_update_accum(p, x, rs, inv_norm, labels, cv, s, order))) return e;
-            if ((e = launch_finalize(p, cv, rs.active, 1, s))) return e;
+            if (bounds && it + 1 < iters) {
+                if ((e = fill_i32(w.rcount, p.BH, 0, s))) return e;
+                if ((e = launch_finalize(p, cv, rs.active, 1, s, w.drift))) return e;
+            } else if ((e = launch_finalize(p, cv, rs.active, 1, s))) {
+                return e;
+            }
         }
     }
     return hipSuccess;

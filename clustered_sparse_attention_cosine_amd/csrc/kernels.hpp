@@ -51,10 +51,13 @@ struct CentView {
 
 // Rows a k-means call clusters: rows[bh*N + r] for r < nrows[bh] (NULL: all N
 // rows, identity), only for heads with active[bh] != 0 (NULL: all heads).
+// With by_token, labels (and the bounds below) are indexed by the row's token
+// rows[bh*N + r] rather than by its position r.
 struct RowSet {
     const int32_t* rows;
     const int32_t* nrows;
     const uint8_t* active;
+    int by_token;
 };
 
 // Seeded systematic sample of min(m, n) rows; slots beyond hold no centre.
@@ -67,9 +70,10 @@ hipError_t launch_init_kmeanspp(const Prob& p, const void* x, const float* xf, R
                                 CentView cv, uint64_t seed, uint32_t tensor, uint32_t stage,
                                 double* d2, uint8_t* chosen, hipStream_t s);
 // Centroid prep: split into bf16 hi/lo, squared norms (+inf where no centre).
-// With sums != NULL it first moves centres to sums/cnt (cnt > 0) and clears the sums.
+// With sums != NULL it first moves centres to sums/cnt (cnt > 0) and clears the sums;
+// then with drift != NULL also drift[slot] >= ||new - old|| (0 where no centre).
 hipError_t launch_finalize(const Prob& p, CentView cv, const uint8_t* active, int with_sums,
-                           hipStream_t s);
+                           hipStream_t s, float* drift = nullptr);
 // Flag lists of the certified assignment (see kmeans.hip).
 struct FlagSet {
     int32_t* list;
@@ -79,6 +83,11 @@ struct FlagSet {
     int32_t* over_count;
     int32_t* cand;    // [BH, N, CAND_CAP] candidate slots of each flagged row
     int32_t* ccount;  // [BH, N] number of candidates found (may exceed CAND_CAP)
+    // optional [BH, N]: upper bound on the distance of each row to the centre it
+    // is given and lower bound on its distance to every other centre (+inf / 0
+    // for a row the certified pass could not settle)
+    float* ub = nullptr;
+    float* lb = nullptr;
 };
 constexpr int CAND_CAP = 16;
 // Caller centres [BH][cv.m][D] into slots [cv.base, cv.base + cv.m), marked valid.
@@ -96,6 +105,13 @@ hipError_t launch_last_valid(const Prob& p, CentView cv, const int32_t* mcount, 
 hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
                          int normalize, CentView cv, const int32_t* mcount, int32_t* labels,
                          FlagSet fs, hipStream_t s);
+// Bound test between Lloyd rounds (every row, rs.rows NULL): a row whose bound on
+// its own centre, grown by that centre's drift, stays below its bound on every
+// other centre, shrunk by the largest drift, keeps its label and the moved
+// bounds; the others are appended to rlist (tokens, rcount[bh] cleared beforehand).
+hipError_t launch_bound_filter(const Prob& p, RowSet rs, CentView cv, const int32_t* labels,
+                               float* ub, float* lb, const float* drift, int32_t* rlist,
+                               int32_t* rcount, hipStream_t s);
 // Centroid sums (f32 atomics) and member counts for the current labels.
 // order (may be null): a permutation of the rows [BH][N] to take them in
 // (rows in one run of equal labels share one atomic per dimension).

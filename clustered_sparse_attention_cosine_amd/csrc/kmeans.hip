@@ -389,7 +389,7 @@ hipError_t launch_init_kmeanspp(const Prob& p, const void* x, const float* xf, R
 // squared norm (+inf where the slot holds no centre).
 template <int D>
 __global__ __launch_bounds__(256) void finalize_kernel(CentView cv, const uint8_t* active,
-                                                       int with_sums) {
+                                                       int with_sums, float* drift) {
     const int bh = blockIdx.y;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int j = blockIdx.x * 4 + w;
@@ -401,13 +401,25 @@ __global__ __launch_bounds__(256) void finalize_kernel(CentView cv, const uint8_
     float cvv[E];
     if (with_sums) {
         int n = cv.cnt[slot];
+        double dd = 0.0;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             float* sp = cv.sums + slot * D + l + 64 * e;
-            if (n > 0) c[l + 64 * e] = *sp / (float)n;
+            if (n > 0) {
+                const float nv = *sp / (float)n;
+                const double df = (double)(nv - c[l + 64 * e]);
+                dd += df * df;
+                c[l + 64 * e] = nv;
+            }
             *sp = 0.0f;
         }
         if (l == 0) cv.cnt[slot] = 0;
+        if (drift) {
+            // ||new - old|| from the f32 differences (each within 2^-24 of
+            // itself), rounded up by a margin
+            dd = wave_sum_d(dd);
+            if (l == 0) drift[slot] = cv.valid[slot] ? (float)sqrt(dd) * (1.0f + 0x1.0p-20f) : 0.0f;
+        }
     }
     double ss = 0.0;
 #pragma unroll
@@ -425,12 +437,92 @@ __global__ __launch_bounds__(256) void finalize_kernel(CentView cv, const uint8_
 }
 
 hipError_t launch_finalize(const Prob& p, CentView cv, const uint8_t* active, int with_sums,
-                           hipStream_t s) {
+                           hipStream_t s, float* drift) {
     dim3 grid((unsigned)((cv.m + 3) / 4), (unsigned)p.BH);
     if (p.D == 64)
-        hipLaunchKernelGGL(finalize_kernel<64>, grid, dim3(256), 0, s, cv, active, with_sums);
+        hipLaunchKernelGGL(finalize_kernel<64>, grid, dim3(256), 0, s, cv, active, with_sums, drift);
     else
-        hipLaunchKernelGGL(finalize_kernel<128>, grid, dim3(256), 0, s, cv, active, with_sums);
+        hipLaunchKernelGGL(finalize_kernel<128>, grid, dim3(256), 0, s, cv, active, with_sums, drift);
+    return hipGetLastError();
+}
+
+// Triangle inequality: the new distance to the row's centre is at most
+// ub + drift[label], and to any other centre at least lb - max drift, so
+// ub' < lb' keeps the label strictly nearest (the f32 sums and differences are
+// rounded outward by 2^-22 of themselves). A workgroup takes 2048 rows (8 per
+// thread), finds the largest drift of its head itself and appends its rows to
+// redo in row order with one atomic (same-address atomics cost about 0.3 us
+// each, so one per wave would dominate).
+constexpr int BF_ROWS = 8;
+__global__ __launch_bounds__(256) void bound_filter_kernel(int N, RowSet rs, CentView cv,
+                                                           const int32_t* __restrict__ labels,
+                                                           float* __restrict__ ub, float* __restrict__ lb,
+                                                           const float* __restrict__ drift,
+                                                           int32_t* __restrict__ rlist,
+                                                           int32_t* __restrict__ rcount) {
+    __shared__ float sh_m[4];
+    __shared__ int sh_c[4 * BF_ROWS];
+    __shared__ int sh_base;
+    const int bh = blockIdx.y;
+    if (rs.active && !rs.active[bh]) return;
+    const int n = rs.nrows ? rs.nrows[bh] : N;
+    const int r0 = blockIdx.x * 256 * BF_ROWS;
+    if (r0 >= n) return;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const float* dr = drift + (int64_t)bh * cv.cap + cv.base;
+    float dm = 0.0f;
+    for (int j = tid; j < cv.m; j += 256) {
+        const float v = dr[j];
+        dm = fmaxf(dm, v == v ? v : INFINITY);  // a NaN drift disables the test
+    }
+    dm = wave_max(dm);
+    if (lane == 0) sh_m[w] = dm;
+    __syncthreads();
+    dm = fmaxf(fmaxf(sh_m[0], sh_m[1]), fmaxf(sh_m[2], sh_m[3]));
+    uint64_t masks[BF_ROWS];
+#pragma unroll
+    for (int i = 0; i < BF_ROWS; ++i) {
+        const int r = r0 + i * 256 + tid;
+        bool redo = false;
+        if (r < n) {
+            const int64_t ix = (int64_t)bh * N + r;
+            const float u = (ub[ix] + dr[labels[ix]]) * (1.0f + 0x1.0p-22f);
+            const float lo = (lb[ix] - dm) * (1.0f - 0x1.0p-22f);
+            if (u < lo) {
+                ub[ix] = u;
+                lb[ix] = lo;
+            } else {
+                redo = true;
+            }
+        }
+        masks[i] = __ballot(redo);
+        if (lane == 0) sh_c[i * 4 + w] = __popcll(masks[i]);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int tot = 0;
+        for (int c = 0; c < 4 * BF_ROWS; ++c) {
+            const int v = sh_c[c];
+            sh_c[c] = tot;
+            tot += v;
+        }
+        sh_base = tot ? atomicAdd(&rcount[bh], tot) : 0;
+    }
+    __syncthreads();
+    const int base = sh_base;
+    const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int i = 0; i < BF_ROWS; ++i)
+        if ((masks[i] >> lane) & 1ull)
+            rlist[(int64_t)bh * N + base + sh_c[i * 4 + w] + __popcll(masks[i] & below)] = r0 + i * 256 + tid;
+}
+
+hipError_t launch_bound_filter(const Prob& p, RowSet rs, CentView cv, const int32_t* labels,
+                               float* ub, float* lb, const float* drift, int32_t* rlist,
+                               int32_t* rcount, hipStream_t s) {
+    dim3 grid((unsigned)((p.N + 256 * BF_ROWS - 1) / (256 * BF_ROWS)), (unsigned)p.BH);
+    hipLaunchKernelGGL(bound_filter_kernel, grid, dim3(256), 0, s, p.N, rs, cv, labels, ub, lb, drift,
+                       rlist, rcount);
     return hipGetLastError();
 }
 
@@ -722,8 +814,10 @@ void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
                 auto fin = [](uint32_t k) { return FOLD ? (k >= 0x80000000u && k < 0xff800000u) : k < 0x7f800000u; };
                 auto dec = [](uint32_t k) { return FOLD ? -2.0f * __uint_as_float(k) : __uint_as_float(k); };
                 const bool finite = fin(b1[pb]);
+                const int64_t li = (int64_t)bh * N +
+                                   (rs.by_token ? rs.rows[(int64_t)bh * N + rr[pb]] : rr[pb]);
                 // no finite distance (no centre, or a NaN row): slot 0, and the row is flagged
-                labels[(int64_t)bh * N + rr[pb]] = finite ? bj : 0;
+                labels[li] = finite ? bj : 0;
                 const float d1 = dec(b1[pb]);
                 const float d2 = fin(b2[pb]) ? dec(b2[pb]) : INFINITY;
                 // contraction error of one d' (hi/lo residual and f32 accumulation,
@@ -733,7 +827,22 @@ void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
                 // (||c||^2 + B) / 2 + s||x|| ||c||, i.e. 2^-19 of the same sum in d' units)
                 const float err = ERR_X * xn[pb] * cmax + ERR_C * c2max +
                                   (FOLD ? 0x1.0p-19f : 0x1.0p-22f) * (c2max + bwg + 2.0f * xn[pb] * cmax);
-                if (!finite || !(d2 - d1 > 2.0f * err + 0x1.0p-17f * d2)) {
+                const bool settled = finite && d2 - d1 > 2.0f * err + 0x1.0p-17f * d2;
+                if (fs.ub) {
+                    // distance bounds: squared distance = d' - B + (s||x||)^2; every d'
+                    // within err + 2^-19 d' of the contraction's, (s||x||)^2 within
+                    // (D + 4) 2^-24 of itself, f32 roundings far below the margin mg
+                    const float mg = err + 0x1.0p-15f * (c2max + bwg + 2.0f * xn[pb] * cmax);
+                    const float x2 = xn[pb] * xn[pb];
+                    float u = INFINITY, lo = 0.0f;
+                    if (settled) {
+                        u = sqrtf(fmaxf((d1 + mg - bwg) + x2 * (1.0f + 0x1.0p-15f), 0.0f)) * (1.0f + 0x1.0p-20f);
+                        lo = sqrtf(fmaxf((d2 - mg - bwg) + x2 * (1.0f - 0x1.0p-15f), 0.0f)) * (1.0f - 0x1.0p-20f);
+                    }
+                    fs.ub[li] = u;
+                    fs.lb[li] = lo;
+                }
+                if (!settled) {
                     const int fpos = atomicAdd(&fs.count[bh], 1);
                     fs.list[(int64_t)bh * N + fpos] = rr[pb];
                     fs.ccount[(int64_t)bh * N + fpos] = 0;
@@ -783,9 +892,9 @@ __global__ __launch_bounds__(256) void cand_exact_kernel(const T* __restrict__ X
         const int r = okr ? fs.list[fe] : 0;
         double d = INFINITY;
         int j = 0x7fffffff;
+        const int64_t tok = (okr && rs.rows) ? rs.rows[(int64_t)bh * N + r] : r;
         if (okr && nc <= CAND_CAP && ci < nc) {
             j = fs.cand[fe * CAND_CAP + ci];
-            const int64_t tok = rs.rows ? rs.rows[(int64_t)bh * N + r] : r;
             d = exact_d2(row_ptr(X, N, D, bh, tok), D, normalize, cv.cent + (cbase + j) * D);
         }
 #pragma unroll
@@ -799,7 +908,7 @@ __global__ __launch_bounds__(256) void cand_exact_kernel(const T* __restrict__ X
                 const int pos = atomicAdd(&fs.over_count[bh], 1);
                 fs.over[(int64_t)bh * N + pos] = r;
             } else {
-                labels[(int64_t)bh * N + r] = j;
+                labels[(int64_t)bh * N + (rs.by_token ? tok : r)] = j;
             }
         }
     }
@@ -829,9 +938,10 @@ __global__ __launch_bounds__(256) void refine_kernel(const T* __restrict__ X, in
         const int e = base + w;
         const bool live = e < cnt;
         int r = 0;
+        int64_t tok = 0;
         if (live) {
             r = flag_list[(int64_t)bh * N + e];
-            const int64_t tok = rs.rows ? rs.rows[(int64_t)bh * N + r] : r;
+            tok = rs.rows ? rs.rows[(int64_t)bh * N + r] : r;
             const T* xr = row_ptr(X, N, D, bh, tok);
             double nrm = 1.0;
             if (normalize) {
@@ -863,7 +973,7 @@ __global__ __launch_bounds__(256) void refine_kernel(const T* __restrict__ X, in
                 const int oj = __shfl_xor(bj, o);
                 if (ob < best || (ob == best && oj < bj)) { best = ob; bj = oj; }
             }
-            if (l == 0 && bj != 0x7fffffff) labels[(int64_t)bh * N + r] = bj;
+            if (l == 0 && bj != 0x7fffffff) labels[(int64_t)bh * N + (rs.by_token ? tok : r)] = bj;
         }
         __syncthreads();
     }
