@@ -15,6 +15,7 @@ Prints one JSON line (last line of stdout).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -33,6 +34,27 @@ CALIB_BYTES = 512 << 20   # plain copy used to calibrate the memory counters
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def timed_layer(torch, adc, q, k, v, cfg, stream, prev=None, select_kw=None, want_lse=True):
+    """One layer as the package schedules it (the two clusterings overlapped on
+    two streams, then selection and attention), with timing events. Returns
+    (Q, K, S, out, times) where times() gives the layer and per-stage
+    milliseconds once the stream has finished."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    ev[0].record(stream)
+    Q, K = adc.cluster_layer(q, k, v, cfg, prev=prev, events=ev[1:6])
+    S = adc.select(Q["qrep"], K, cfg.top_p, **(select_kw or {}))
+    ev[6].record(stream)
+    out, _ = adc.sparse_attn(q, Q["perm"], Q["offsets"], K["k_perm"], K["v_perm"], K["offsets"],
+                             S["mask"], want_lse=want_lse)
+    ev[7].record(stream)
+
+    def times():
+        return {"layer": ev[0].elapsed_time(ev[7]), "cluster_q": ev[1].elapsed_time(ev[2]),
+                "cluster_k": ev[3].elapsed_time(ev[4]), "select": ev[5].elapsed_time(ev[6]),
+                "sparse_attn": ev[6].elapsed_time(ev[7])}
+    return Q, K, S, out, times
 
 
 def main():
@@ -84,24 +106,9 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step(record=None):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record is not None else None
-        if ev:
-            ev[0].record(stream)
-        Q = adc.cluster_q(q, cfg.q_clusters, cfg.iters, cfg.init, cfg.seed)
-        if ev:
-            ev[1].record(stream)
-        K = adc.cluster_k(k, v, cfg.k_base, cfg.k_max, cfg.iters, cfg.tau_mult, cfg.adaptive,
-                          cfg.init, cfg.seed)
-        if ev:
-            ev[2].record(stream)
-        S = adc.select(Q["qrep"], K, cfg.top_p)
-        if ev:
-            ev[3].record(stream)
-        out, lse = adc.sparse_attn(q, Q["perm"], Q["offsets"], K["k_perm"], K["v_perm"],
-                                   K["offsets"], S["mask"])
-        if ev:
-            ev[4].record(stream)
-            record.append(ev)
+        Q, K, S, out, times = timed_layer(torch, adc, q, k, v, cfg, stream)
+        if record is not None:
+            record.append(times)
         return Q, K, S, out
 
     for i in range(args.warmup):
@@ -118,9 +125,9 @@ def main():
     log(f"timed {args.steps} steps in {t_total:.3f}s")
     ms = t_total * 1e3 / args.steps
     stage_names = ["cluster_q", "cluster_k", "select", "sparse_attn"]
-    stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events]))
-                for i, n in enumerate(stage_names)}
-    per_step = np.array([e[0].elapsed_time(e[4]) for e in events])
+    events = [t() for t in events]
+    stage_ms = {n: float(np.mean([e[n] for e in events])) for n in stage_names}
+    per_step = np.array([e["layer"] for e in events])
     layer_stats = {"median": round(float(np.median(per_step)), 4),
                    "p10": round(float(np.percentile(per_step, 10)), 4),
                    "p90": round(float(np.percentile(per_step, 90)), 4)}
@@ -166,6 +173,7 @@ def main():
                    "top_p": w.top_p, "lloyd_iters": w.iters, "init": w.init,
                    "layer_ms": round(ms, 4)},
         "stages_ms": {k2: round(v2, 4) for k2, v2 in stage_ms.items()},
+        "schedule": "cluster_q on a side stream beside cluster_k (their stage times overlap), then select and sparse_attn",
         "layer_ms_events": layer_stats,
         "selection": {"pairs": pairs, "density": round(density, 5), "full_heads": full_heads,
                       "k_slots": {str(s): slots.count(s) for s in sorted(set(slots))}},
@@ -231,19 +239,12 @@ def seed_spread(torch, adc, synth, w, cfg, dev, stream, seeds=(1, 2), steps=5):
                    if g[t].dtype == np.uint16 else torch.from_numpy(g[t]).to(dev) for t in "qkv")
         del g
         times = []
+        cs = dataclasses.replace(cfg, seed=seed)
         for i in range(2 + steps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            Q = adc.cluster_q(q, cfg.q_clusters, cfg.iters, cfg.init, seed)
-            K = adc.cluster_k(k, v, cfg.k_base, cfg.k_max, cfg.iters, cfg.tau_mult, cfg.adaptive,
-                              cfg.init, seed)
-            S = adc.select(Q["qrep"], K, cfg.top_p)
-            adc.sparse_attn(q, Q["perm"], Q["offsets"], K["k_perm"], K["v_perm"], K["offsets"],
-                            S["mask"], want_lse=False)
-            e1.record(stream)
+            Q, K, S, _, tm = timed_layer(torch, adc, q, k, v, cs, stream, want_lse=False)
             torch.cuda.synchronize()
             if i >= 2:
-                times.append(e0.elapsed_time(e1))
+                times.append(tm()["layer"])
         pairs = float((Q["sizes"].double() * S["sel_keys"].double()).sum().item())
         out.append({"seed": seed, "layer_ms_median": round(float(np.median(times)), 4),
                     "density": round(pairs / (w.B * w.H * float(w.N) ** 2), 5),
@@ -281,38 +282,21 @@ def warm_steady_state(torch, adc, synth, w, cfg, dev, stream, cold, q0, k0, v0, 
         for rep in range(2):
             prev = None
             rows = []
+            cw = dataclasses.replace(cfg, seed=seed, warm_iters=wi)
             for s, (q, k, v) in enumerate([(q0, k0, v0)] + steps):
-                ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-                ev[0].record(stream)
-                if prev is None:
-                    Q = adc.cluster_q(q, cfg.q_clusters, cfg.iters, cfg.init, seed)
-                    ev[1].record(stream)
-                    K = adc.cluster_k(k, v, cfg.k_base, cfg.k_max, cfg.iters, cfg.tau_mult,
-                                      cfg.adaptive, cfg.init, seed)
-                else:
-                    Q = adc.cluster_q(q, cfg.q_clusters, wi, "caller",
-                                      init_centroids=prev["Q"]["centroids"])
-                    ev[1].record(stream)
-                    pk = prev["K"]
-                    K = adc.cluster_k(k, v, cfg.k_base, pk["max_clusters"], wi, adaptive="warm",
-                                      init_centroids=pk["centroids"], n_clusters=pk["n_clusters"],
-                                      full=pk["full"], tau=pk["tau"])
-                ev[2].record(stream)
-                S = adc.select(Q["qrep"], K, cfg.top_p)
-                ev[3].record(stream)
-                adc.sparse_attn(q, Q["perm"], Q["offsets"], K["k_perm"], K["v_perm"], K["offsets"],
-                                S["mask"], want_lse=False)
-                ev[4].record(stream)
+                Q, K, S, _, tm = timed_layer(torch, adc, q, k, v, cw, stream, prev=prev,
+                                             want_lse=False)
                 prev = dict(Q=Q, K=K)
                 torch.cuda.synchronize()
+                tm = tm()
                 pairs = float((Q["sizes"].double() * S["sel_keys"].double()).sum().item())
                 C = adc.compactness(K["k_perm"], K["offsets"], K["centroids"])
-                rows.append(dict(t=[ev[i].elapsed_time(ev[i + 1]) for i in range(4)],
+                rows.append(dict(t=[tm[n] for n in names], layer=tm["layer"],
                                  density=pairs / (w.B * w.H * float(w.N) ** 2),
                                  key_mse=float(C["mse"].mean().item()),
                                  key_db=float(C["db"].mean().item())))
         warm = rows[1:]
-        layer = [sum(r["t"]) for r in warm]
+        layer = [r["layer"] for r in warm]
         wm = float(np.median(layer))
         res[f"lloyd_iters_{wi}"] = {
             "warm_layer_ms_median": round(wm, 4),
@@ -358,27 +342,19 @@ def variants(torch, adc, w, cfg, q, k, v, stream, seed, mean_slots, steps=5):
     res = {"topk_k": top_k}
     for name, st in settings.items():
         rows = []
+        cv = dataclasses.replace(cfg, seed=seed, q_clusters=st["cq"])
         for i in range(2 + steps):
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-            ev[0].record(stream)
-            Q = adc.cluster_q(q, st["cq"], cfg.iters, cfg.init, seed)
-            ev[1].record(stream)
-            K = adc.cluster_k(k, v, cfg.k_base, cfg.k_max, cfg.iters, cfg.tau_mult, cfg.adaptive,
-                              cfg.init, seed)
-            ev[2].record(stream)
-            S = adc.select(Q["qrep"], K, cfg.top_p, score=st["score"], rule=st["rule"], top_k=top_k)
-            ev[3].record(stream)
-            adc.sparse_attn(q, Q["perm"], Q["offsets"], K["k_perm"], K["v_perm"], K["offsets"],
-                            S["mask"], want_lse=False)
-            ev[4].record(stream)
+            Q, K, S, _, tm = timed_layer(torch, adc, q, k, v, cv, stream,
+                                         select_kw=dict(score=st["score"], rule=st["rule"],
+                                                        top_k=top_k), want_lse=False)
             torch.cuda.synchronize()
             if i >= 2:
-                rows.append([ev[j].elapsed_time(ev[j + 1]) for j in range(4)])
+                rows.append(tm())
         pairs = float((Q["sizes"].double() * S["sel_keys"].double()).sum().item())
-        res[name] = {"layer_ms_median": round(float(np.median([sum(r) for r in rows])), 4),
-                     "stages_ms_median": {n: round(float(np.median([r[j] for r in rows])), 4)
-                                          for j, n in enumerate(["cluster_q", "cluster_k", "select",
-                                                                 "sparse_attn"])},
+        res[name] = {"layer_ms_median": round(float(np.median([r["layer"] for r in rows])), 4),
+                     "stages_ms_median": {n: round(float(np.median([r[n] for r in rows])), 4)
+                                          for n in ["cluster_q", "cluster_k", "select",
+                                                    "sparse_attn"]},
                      "density": round(pairs / (w.B * w.H * float(w.N) ** 2), 5)}
         log(f"variant {name}: {res[name]}")
         del Q, K, S

@@ -345,6 +345,65 @@ class LayerConfig:
     warm_iters: int = 5     # Lloyd iterations of the warm steps
 
 
+_SIDE_STREAMS = {}
+
+
+def _side_stream(device):
+    """A second stream per device (default priority) for the query clustering."""
+    idx = torch.device(device).index
+    if idx is None:
+        idx = torch.cuda.current_device()
+    st = _SIDE_STREAMS.get(idx)
+    if st is None:
+        st = _SIDE_STREAMS[idx] = torch.cuda.Stream(device=idx)
+    return st
+
+
+def cluster_layer(q, k, v, cfg: LayerConfig, prev=None, events=None):
+    """Both clusterings of one layer (Algorithm 3 steps 1-2): returns (Q, K).
+
+    The query and key clusterings share no data, so the queries run on a side
+    stream while the keys run on the current one; the current stream waits for
+    both before this returns, and the query outputs are marked as used on it.
+    The key clustering's many small kernels (stages over few keys, sorts,
+    updates) leave most of the GPU idle, which the query clustering fills.
+    With `prev` both start from the previous step's state (section 3.2.2).
+    `events`, if given: five timing events recorded at the query start and end
+    (side stream), the key start and end, and the join (current stream)."""
+    main = torch.cuda.current_stream(q.device)
+    side = _side_stream(q.device)
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        if events is not None:
+            events[0].record(side)
+        if prev is None:
+            Q = cluster_q(q, cfg.q_clusters, cfg.iters, cfg.init, cfg.seed)
+        else:
+            Q = cluster_q(q, cfg.q_clusters, cfg.warm_iters, "caller",
+                          init_centroids=prev["Q"]["centroids"])
+        if events is not None:
+            events[1].record(side)
+    if events is not None:
+        events[2].record(main)
+    if prev is None:
+        K = cluster_k(k, v, cfg.k_base, cfg.k_max, cfg.iters, cfg.tau_mult, cfg.adaptive,
+                      cfg.init, cfg.seed)
+    else:
+        pk = prev["K"]
+        K = cluster_k(k, v, cfg.k_base, pk["max_clusters"], cfg.warm_iters, adaptive="warm",
+                      init_centroids=pk["centroids"], n_clusters=pk["n_clusters"],
+                      full=pk["full"], tau=pk["tau"])
+    if events is not None:
+        events[3].record(main)
+    main.wait_stream(side)
+    for t in Q.values():
+        if isinstance(t, torch.Tensor) and t.is_cuda:
+            t.record_stream(main)
+    if events is not None:
+        events[4].record(main)
+    return Q, K
+
+
 def layer(q, k, v, cfg: LayerConfig, prev=None):
     """One clustered-sparse-attention layer (Algorithm 3): returns (out, lse, state).
 
@@ -352,17 +411,7 @@ def layer(q, k, v, cfg: LayerConfig, prev=None):
     layer runs its steady-state form (section 3.2.2): both clusterings start
     from the previous centres, and the keys keep their per-head counts and
     full-attention flags."""
-    if prev is None:
-        Q = cluster_q(q, cfg.q_clusters, cfg.iters, cfg.init, cfg.seed)
-        K = cluster_k(k, v, cfg.k_base, cfg.k_max, cfg.iters, cfg.tau_mult, cfg.adaptive,
-                      cfg.init, cfg.seed)
-    else:
-        pq, pk = prev["Q"], prev["K"]
-        Q = cluster_q(q, cfg.q_clusters, cfg.warm_iters, "caller",
-                      init_centroids=pq["centroids"])
-        K = cluster_k(k, v, cfg.k_base, pk["max_clusters"], cfg.warm_iters, adaptive="warm",
-                      init_centroids=pk["centroids"], n_clusters=pk["n_clusters"],
-                      full=pk["full"], tau=pk["tau"])
+    Q, K = cluster_layer(q, k, v, cfg, prev)
     S = select(Q["qrep"], K, cfg.top_p, cfg.score, cfg.rule, cfg.top_k)
     out, lse = sparse_attn(q, Q["perm"], Q["offsets"], K["k_perm"], K["v_perm"], K["offsets"],
                            S["mask"])

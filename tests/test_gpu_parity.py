@@ -366,6 +366,28 @@ def test_cluster_q_first_assignment_and_lockstep(case):
         assert np.array_equal(host(Q["offsets"])[0, h], off)
 
 
+# ----------------------------------------------------------------- two-stream layer
+def test_layer_overlap_matches_sequential_calls():
+    """layer() runs the two clusterings on two streams; its outputs equal the
+    four calls made one after another on one stream, bit for bit, on two
+    layers in a row (the second reuses the side stream and freed memory)."""
+    w, g = _inputs("bf16_d64")
+    cfg = adc.LayerConfig(q_clusters=w.q_clusters, k_base=w.k_base, k_max=w.k_max, top_p=w.top_p,
+                          iters=w.iters, init=w.init, adaptive=w.k_adaptive)
+    q, k, v = (dev(g[t]) for t in "qkv")
+    Q = adc.cluster_q(q, cfg.q_clusters, cfg.iters, cfg.init, cfg.seed)
+    K = adc.cluster_k(k, v, cfg.k_base, cfg.k_max, cfg.iters, cfg.tau_mult, cfg.adaptive, cfg.init, cfg.seed)
+    S = adc.select(Q["qrep"], K, cfg.top_p)
+    ref, ref_lse = adc.sparse_attn(q, Q["perm"], Q["offsets"], K["k_perm"], K["v_perm"], K["offsets"],
+                                   S["mask"])
+    for _ in range(2):
+        out, lse, st = adc.layer(q, k, v, cfg)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref) and torch.equal(lse, ref_lse)
+        assert torch.equal(st["Q"]["assign"], Q["assign"]) and torch.equal(st["K"]["assign"], K["assign"])
+        assert torch.equal(st["S"]["mask"], S["mask"])
+
+
 # ----------------------------------------------------------------- every Lloyd round
 @pytest.mark.parametrize("case", ["bf16_d64", "bf16_d128"])
 @pytest.mark.parametrize("tensor", ["q", "k"])
