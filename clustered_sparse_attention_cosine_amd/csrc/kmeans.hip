@@ -1225,33 +1225,46 @@ hipError_t launch_stage_dist(const Prob& p, const void* k, RowSet rs, const int3
 
 // tau = tau_mult x mean distance over all N keys (stage 0 clusters every key).
 // Fixed reduction order: strided per-thread sums, then a tree.
-__global__ __launch_bounds__(256) void stage_tau_kernel(int N, StageState st, double tau_mult) {
-    __shared__ double part[256];
+__global__ __launch_bounds__(1024) void stage_tau_kernel(int N, StageState st, double tau_mult) {
+    __shared__ double part[16];
     const int bh = blockIdx.x;
     if (!st.active[bh]) return;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const double* dd = st.dist + (int64_t)bh * N;
-    double s = 0.0;
-    for (int r = threadIdx.x; r < N; r += 256) s += dd[r];
-    part[threadIdx.x] = s;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if (threadIdx.x < o) part[threadIdx.x] += part[threadIdx.x + o];
-        __syncthreads();
+    // fixed order: four interleaved sums per thread, a butterfly over the wave,
+    // then the 16 waves in order
+    double p0 = 0.0, p1 = 0.0, p2 = 0.0, p3 = 0.0;
+    int r = tid;
+    for (; r + 3 * 1024 < N; r += 4 * 1024) {
+        p0 += dd[r];
+        p1 += dd[r + 1024];
+        p2 += dd[r + 2048];
+        p3 += dd[r + 3072];
     }
-    if (threadIdx.x == 0) st.tau[bh] = tau_mult * part[0] / (double)N;
+    for (; r < N; r += 1024) p0 += dd[r];
+    const double sw = wave_sum_d((p0 + p1) + (p2 + p3));
+    if (l == 0) part[w] = sw;
+    __syncthreads();
+    if (tid == 0) {
+        double t = 0.0;
+        for (int i = 0; i < 16; ++i) t += part[i];
+        st.tau[bh] = tau_mult * t / (double)N;
+    }
 }
 
 hipError_t launch_stage_tau(const Prob& p, StageState st, double tau_mult, hipStream_t s) {
-    hipLaunchKernelGGL(stage_tau_kernel, dim3(p.BH), dim3(256), 0, s, p.N, st, tau_mult);
+    hipLaunchKernelGGL(stage_tau_kernel, dim3(p.BH), dim3(1024), 0, s, p.N, st, tau_mult);
     return hipGetLastError();
 }
 
 // U <- {u in U : dist(u) >= tau}, order kept (Algorithm 1 steps 11-16); slots += m_t.
+// Each thread takes 8 consecutive entries of a 8192-entry chunk; a wave scan and
+// the 16 wave totals give every kept entry its place.
 __global__ __launch_bounds__(1024) void stage_compact_kernel(int N, StageState st,
                                                              const int32_t* __restrict__ u_in,
                                                              int32_t* __restrict__ u_out, int m_t) {
+    constexpr int PER = 8;
     __shared__ int wsum[16];
-    __shared__ int sh_total;
     const int bh = blockIdx.x;
     if (!st.active[bh]) return;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -1259,26 +1272,40 @@ __global__ __launch_bounds__(1024) void stage_compact_kernel(int N, StageState s
     const double tau = st.tau[bh];
     const double* dd = st.dist + (int64_t)bh * N;
     int running = 0;
-    for (int base = 0; base < nu; base += 1024) {
-        const int r = base + tid;
-        const bool keep = r < nu && !(dd[r] < tau);
-        const uint64_t bal = __ballot(keep);
-        const int in_wave = __popcll(bal & ((1ull << l) - 1ull));
-        if (l == 0) wsum[w] = __popcll(bal);
-        __syncthreads();
-        int before = 0;
-        for (int i = 0; i < w; ++i) before += wsum[i];
-        if (tid == 0) {
-            int tot = 0;
-            for (int i = 0; i < 16; ++i) tot += wsum[i];
-            sh_total = tot;
+    for (int base = 0; base < nu; base += 1024 * PER) {
+        const int r0 = base + tid * PER;
+        uint32_t keepm = 0;
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int r = r0 + j;
+            const bool keep = r < nu && !(dd[r] < tau);
+            keepm |= (uint32_t)keep << j;
+            cnt += keep;
         }
-        if (keep) {
-            const int id = u_in ? u_in[(int64_t)bh * N + r] : r;
-            u_out[(int64_t)bh * N + running + before + in_wave] = id;
+        int incl = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(incl, o);
+            if (l >= o) incl += v;
         }
+        if (l == 63) wsum[w] = incl;
         __syncthreads();
-        running += sh_total;
+        int before = 0, tot = 0;
+        for (int i = 0; i < 16; ++i) {
+            const int v = wsum[i];
+            before += i < w ? v : 0;
+            tot += v;
+        }
+        int pos = running + before + incl - cnt;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            if ((keepm >> j) & 1u) {
+                const int r = r0 + j;
+                u_out[(int64_t)bh * N + pos++] = u_in ? u_in[(int64_t)bh * N + r] : r;
+            }
+        }
+        running += tot;
         __syncthreads();
     }
     if (tid == 0) {
