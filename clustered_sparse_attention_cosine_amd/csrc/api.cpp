@@ -220,7 +220,9 @@ hipError_t lloyd(const Prob& p, const void* x, int normalize, RowSet rs, const f
                 return e;
             ra = RowSet{w.rlist, w.rcount, rs.active, 1};
         }
-        if ((e = launch_assign(p, x, ra, inv_norm, normalize, cv, mcount, labels, fs, s))) return e;
+        // a row subset (later stages: the few keys left in U) also splits the centre tiles
+        if ((e = launch_assign(p, x, ra, inv_norm, normalize, cv, mcount, labels, fs, s, rs.rows ? 4 : 0)))
+            return e;
         if (it + 1 < iters || final_update) {
             if (ss && !rs.rows) {
                 if ((e = launch_counting_sort(p, labels, cv.m, w.seg_cnt, w.hist, ss->sizes, ss->offsets,

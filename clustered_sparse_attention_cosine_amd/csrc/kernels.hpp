@@ -102,9 +102,11 @@ hipError_t launch_last_valid(const Prob& p, CentView cv, const int32_t* mcount, 
 // Nearest centre by a bf16 hi/lo matrix-core contraction with a certified
 // error bound; uncertain rows are settled by exact f64 distances of the
 // centres inside their uncertainty band (labels are final on return).
+// split > 1: for calls over few rows, the centre tiles are also split over up to
+// `split` workgroups per row block (same labels; shorter serial chain per row).
 hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
                          int normalize, CentView cv, const int32_t* mcount, int32_t* labels,
-                         FlagSet fs, hipStream_t s);
+                         FlagSet fs, hipStream_t s, int split = 0);
 // Bound test between Lloyd rounds (every row, rs.rows NULL): a row whose bound on
 // its own centre, grown by that centre's drift, stays below its bound on every
 // other centre, shrunk by the largest drift, keeps its label and the moved

@@ -577,6 +577,57 @@ __device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c)
     return r;
 }
 
+// Settles one row from its best and second-best sort keys (merged over lanes,
+// or over centre-tile splits): label, flag list entry, distance bounds.
+template <bool FOLD, bool F32X>
+__device__ __forceinline__ void assign_settle(uint32_t k1, uint32_t k2, int bj, float xn, float c2max,
+                                              float bwg, int bh, int N, int rr, const RowSet& rs,
+                                              int32_t* __restrict__ labels, const FlagSet& fs) {
+    constexpr float ERR_X = F32X ? 0x1.0p-12f : 0x1.0p-13f;
+    constexpr float ERR_C = 0x1.0p-21f;
+    const float cmax = sqrtf(c2max);
+    // keys are d' >= 0, or (FOLD) -d'/2 < 0; +-inf and NaN are not finite
+    auto fin = [](uint32_t k) { return FOLD ? (k >= 0x80000000u && k < 0xff800000u) : k < 0x7f800000u; };
+    auto dec = [](uint32_t k) { return FOLD ? -2.0f * __uint_as_float(k) : __uint_as_float(k); };
+    const bool finite = fin(k1);
+    const int64_t li = (int64_t)bh * N +
+                       (rs.by_token ? rs.rows[(int64_t)bh * N + rr] : rr);
+    // no finite distance (no centre, or a NaN row): slot 0, and the row is flagged
+    labels[li] = finite ? bj : 0;
+    const float d1 = dec(k1);
+    const float d2 = fin(k2) ? dec(k2) : INFINITY;
+    // contraction error of one d' (hi/lo residual and f32 accumulation,
+    // plus the rounding of ||c||^2 + B and of the final fma); the key
+    // truncation moves a value by less than 2^-19 of itself
+    // (FOLD: up to 16 f32 roundings of accumulator values as large as
+    // (||c||^2 + B) / 2 + s||x|| ||c||, i.e. 2^-19 of the same sum in d' units)
+    const float err = ERR_X * xn * cmax + ERR_C * c2max +
+                      (FOLD ? 0x1.0p-19f : 0x1.0p-22f) * (c2max + bwg + 2.0f * xn * cmax);
+    const bool settled = finite && d2 - d1 > 2.0f * err + 0x1.0p-17f * d2;
+    if (fs.ub) {
+        // distance bounds: squared distance = d' - B + (s||x||)^2; every d'
+        // within err + 2^-19 d' of the contraction's, (s||x||)^2 within
+        // (D + 4) 2^-24 of itself, f32 roundings far below the margin mg
+        const float mg = err + 0x1.0p-15f * (c2max + bwg + 2.0f * xn * cmax);
+        const float x2 = xn * xn;
+        float u = INFINITY, lo = 0.0f;
+        if (settled) {
+            u = sqrtf(fmaxf((d1 + mg - bwg) + x2 * (1.0f + 0x1.0p-15f), 0.0f)) * (1.0f + 0x1.0p-20f);
+            lo = sqrtf(fmaxf((d2 - mg - bwg) + x2 * (1.0f - 0x1.0p-15f), 0.0f)) * (1.0f - 0x1.0p-20f);
+        }
+        fs.ub[li] = u;
+        fs.lb[li] = lo;
+    }
+    if (!settled) {
+        const int fpos = atomicAdd(&fs.count[bh], 1);
+        fs.list[(int64_t)bh * N + fpos] = rr;
+        fs.ccount[(int64_t)bh * N + fpos] = 0;
+        // band edge in the units of ||c||^2 - 2 s x.c (the CAND pass has no B)
+        fs.thr[(int64_t)bh * N + fpos] =
+            finite ? (d1 - bwg) + 3.0f * err + 0x1.0p-17f * d1 : -INFINITY;
+    }
+}
+
 // FOLD (rows not rescaled, s = 1; assignment pass only): the MFMA accumulators
 // start at -(||c_j||^2 + B) / 2, so they end at a_j = x.c_j - (||c_j||^2 + B) / 2
 // = -d'_j / 2 < 0, and the bit patterns of these negative values, read as
@@ -591,11 +642,9 @@ void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
                                                      int normalize, CentView cv,
                                                      const int32_t* __restrict__ mcount,
                                                      int32_t* __restrict__ labels, FlagSet fs,
-                                                     int tiles_per_split) {
+                                                     int tiles_per_split, int32_t* __restrict__ split_rec) {
     constexpr int KC = D / 32;
     constexpr int LD = D + 8;
-    constexpr float ERR_X = F32X ? 0x1.0p-12f : 0x1.0p-13f;
-    constexpr float ERR_C = 0x1.0p-21f;
     __shared__ __attribute__((aligned(16))) u16 sh_hi[2][64 * LD];
     __shared__ __attribute__((aligned(16))) u16 sh_lo[2][64 * LD];
     __shared__ float sh_c2[2][64];
@@ -610,9 +659,10 @@ void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
     const int M = mcount ? min(mcount[bh], cv.m) : cv.m;
     const int64_t cbase = (int64_t)bh * cv.cap + cv.base;
     const int ntiles_all = (M + 63) / 64;
-    const int t_begin = CAND ? blockIdx.z * tiles_per_split : 0;
-    const int t_end = CAND ? min(ntiles_all, t_begin + tiles_per_split) : ntiles_all;
-    if (CAND && t_begin >= t_end) return;
+    const bool tsplit = CAND || split_rec != nullptr;
+    const int t_begin = tsplit ? blockIdx.z * tiles_per_split : 0;
+    const int t_end = tsplit ? min(ntiles_all, t_begin + tiles_per_split) : ntiles_all;
+    if (tsplit && t_begin >= t_end) return;
 
     bf16x8 xh[4][KC];
     bf16x8 xl[4][F32X ? KC : 1];
@@ -795,7 +845,6 @@ void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
 #undef ADC_STORE_TILE
 
     if constexpr (!CAND) {
-        const float cmax = sqrtf(c2max);
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) {
             const uint32_t pos = b1[pb] & 15u;
@@ -810,45 +859,21 @@ void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
                 if (take) { b1[pb] = ob1; bj = obj; }
             }
             if (g == 0 && ok[pb]) {
-                // keys are d' >= 0, or (FOLD) -d'/2 < 0; +-inf and NaN are not finite
-                auto fin = [](uint32_t k) { return FOLD ? (k >= 0x80000000u && k < 0xff800000u) : k < 0x7f800000u; };
-                auto dec = [](uint32_t k) { return FOLD ? -2.0f * __uint_as_float(k) : __uint_as_float(k); };
-                const bool finite = fin(b1[pb]);
-                const int64_t li = (int64_t)bh * N +
-                                   (rs.by_token ? rs.rows[(int64_t)bh * N + rr[pb]] : rr[pb]);
-                // no finite distance (no centre, or a NaN row): slot 0, and the row is flagged
-                labels[li] = finite ? bj : 0;
-                const float d1 = dec(b1[pb]);
-                const float d2 = fin(b2[pb]) ? dec(b2[pb]) : INFINITY;
-                // contraction error of one d' (hi/lo residual and f32 accumulation,
-                // plus the rounding of ||c||^2 + B and of the final fma); the key
-                // truncation moves a value by less than 2^-19 of itself
-                // (FOLD: up to 16 f32 roundings of accumulator values as large as
-                // (||c||^2 + B) / 2 + s||x|| ||c||, i.e. 2^-19 of the same sum in d' units)
-                const float err = ERR_X * xn[pb] * cmax + ERR_C * c2max +
-                                  (FOLD ? 0x1.0p-19f : 0x1.0p-22f) * (c2max + bwg + 2.0f * xn[pb] * cmax);
-                const bool settled = finite && d2 - d1 > 2.0f * err + 0x1.0p-17f * d2;
-                if (fs.ub) {
-                    // distance bounds: squared distance = d' - B + (s||x||)^2; every d'
-                    // within err + 2^-19 d' of the contraction's, (s||x||)^2 within
-                    // (D + 4) 2^-24 of itself, f32 roundings far below the margin mg
-                    const float mg = err + 0x1.0p-15f * (c2max + bwg + 2.0f * xn[pb] * cmax);
-                    const float x2 = xn[pb] * xn[pb];
-                    float u = INFINITY, lo = 0.0f;
-                    if (settled) {
-                        u = sqrtf(fmaxf((d1 + mg - bwg) + x2 * (1.0f + 0x1.0p-15f), 0.0f)) * (1.0f + 0x1.0p-20f);
-                        lo = sqrtf(fmaxf((d2 - mg - bwg) + x2 * (1.0f - 0x1.0p-15f), 0.0f)) * (1.0f - 0x1.0p-20f);
+                if (split_rec) {
+                    // centre-tile split: this split's best two keys, merged by assign_merge_kernel
+                    const int64_t P = (int64_t)gridDim.y * N, e = (int64_t)bh * N + rr[pb];
+                    const int z = blockIdx.z, S = gridDim.z;
+                    split_rec[(3 * z) * P + e] = (int32_t)b1[pb];
+                    split_rec[(3 * z + 1) * P + e] = (int32_t)b2[pb];
+                    split_rec[(3 * z + 2) * P + e] = bj;
+                    if (z == 0) {
+                        split_rec[(3 * S) * P + e] = __float_as_int(xn[pb]);
+                        split_rec[(3 * S + 1) * P + e] = __float_as_int(bwg);
+                        split_rec[(3 * S + 2) * P + e] = __float_as_int(c2max);
                     }
-                    fs.ub[li] = u;
-                    fs.lb[li] = lo;
-                }
-                if (!settled) {
-                    const int fpos = atomicAdd(&fs.count[bh], 1);
-                    fs.list[(int64_t)bh * N + fpos] = rr[pb];
-                    fs.ccount[(int64_t)bh * N + fpos] = 0;
-                    // band edge in the units of ||c||^2 - 2 s x.c (the CAND pass has no B)
-                    fs.thr[(int64_t)bh * N + fpos] =
-                        finite ? (d1 - bwg) + 3.0f * err + 0x1.0p-17f * d1 : -INFINITY;
+                } else {
+                    assign_settle<FOLD, F32X>(b1[pb], b2[pb], bj, xn[pb], c2max, bwg, bh, N, rr[pb], rs,
+                                              labels, fs);
                 }
             }
         }
@@ -859,15 +884,15 @@ template <bool CAND, bool FOLD>
 static void launch_assign_t(const Prob& p, dim3 grid, const void* x, RowSet rs,
                             const float* inv_norm, int normalize, CentView cv,
                             const int32_t* mcount, int32_t* labels, FlagSet fs, int tps,
-                            hipStream_t s) {
+                            hipStream_t s, int32_t* rec = nullptr) {
     if (p.bf16) {
         auto k = p.D == 64 ? assign_kernel<u16, 64, false, CAND, FOLD> : assign_kernel<u16, 128, false, CAND, FOLD>;
         hipLaunchKernelGGL(k, grid, dim3(256), 0, s, (const u16*)x, p.N, rs, inv_norm, normalize, cv,
-                           mcount, labels, fs, tps);
+                           mcount, labels, fs, tps, rec);
     } else {
         auto k = p.D == 64 ? assign_kernel<float, 64, true, CAND, FOLD> : assign_kernel<float, 128, true, CAND, FOLD>;
         hipLaunchKernelGGL(k, grid, dim3(256), 0, s, (const float*)x, p.N, rs, inv_norm, normalize,
-                           cv, mcount, labels, fs, tps);
+                           cv, mcount, labels, fs, tps, rec);
     }
 }
 
@@ -995,19 +1020,66 @@ static hipError_t launch_refine_full(const Prob& p, const void* x, int normalize
     return hipGetLastError();
 }
 
+// One thread per row: merges the best two keys of the centre-tile splits (ties
+// to the lowest slot, as across lanes) and settles the row.
+template <bool FOLD, bool F32X>
+__global__ __launch_bounds__(256) void assign_merge_kernel(int N, RowSet rs, int M, const int32_t* __restrict__ rec,
+                                                           int nsplit, int tps, int32_t* __restrict__ labels,
+                                                           FlagSet fs) {
+    const int bh = blockIdx.y;
+    if (rs.active && !rs.active[bh]) return;
+    const int n = rs.nrows ? rs.nrows[bh] : N;
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= n) return;
+    const int nz = min(nsplit, ((M + 63) / 64 + tps - 1) / tps);
+    const int64_t P = (int64_t)gridDim.y * N, ix = (int64_t)bh * N + e;
+    uint32_t k1 = 0xffffffffu, k2 = 0xffffffffu;
+    int bj = 0;
+    for (int z = 0; z < nz; ++z) {
+        const uint32_t o1 = (uint32_t)rec[(3 * z) * P + ix], o2 = (uint32_t)rec[(3 * z + 1) * P + ix];
+        const int oj = rec[(3 * z + 2) * P + ix];
+        const bool take = o1 < k1 || (o1 == k1 && oj < bj);
+        k2 = min(max(k1, o1), min(k2, o2));
+        if (take) { k1 = o1; bj = oj; }
+    }
+    assign_settle<FOLD, F32X>(k1, k2, bj, __int_as_float(rec[(3 * nsplit) * P + ix]),
+                              __int_as_float(rec[(3 * nsplit + 2) * P + ix]),
+                              __int_as_float(rec[(3 * nsplit + 1) * P + ix]), bh, N, e, rs, labels, fs);
+}
+
 hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
                          int normalize, CentView cv, const int32_t* mcount, int32_t* labels,
-                         FlagSet fs, hipStream_t s) {
+                         FlagSet fs, hipStream_t s, int split) {
     hipLaunchKernelGGL(zero2_i32_kernel, dim3((unsigned)((p.BH + 255) / 256)), dim3(256), 0, s, fs.count,
                        fs.over_count, p.BH);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)p.BH);
-    // rows that are not rescaled take the folded form of the assignment pass
-    if (!normalize && !inv_norm)
+    const bool fold = !normalize && !inv_norm;  // rows not rescaled: folded assignment pass
+    const int tiles_m = (cv.m + 63) / 64;
+    if (split > 1 && !mcount && tiles_m >= 2) {
+        // few rows: the centre tiles are split over gridDim.z (at most 4, so the
+        // 3 per split + 3 record planes fit in the candidate scratch), the best
+        // two keys of every split go to that scratch and a merge settles the rows
+        const int ns = min(split, 4);
+        const int tps = (tiles_m + ns - 1) / ns;
+        const int nz = (tiles_m + tps - 1) / tps;
+        static_assert(3 * 4 + 3 <= CAND_CAP, "split records exceed the candidate scratch");
+        dim3 sgrid(grid.x, grid.y, (unsigned)nz);
+        if (fold)
+            launch_assign_t<false, true>(p, sgrid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, tps, s, fs.cand);
+        else
+            launch_assign_t<false, false>(p, sgrid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, tps, s, fs.cand);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        auto mk = fold ? (p.bf16 ? assign_merge_kernel<true, false> : assign_merge_kernel<true, true>)
+                       : (p.bf16 ? assign_merge_kernel<false, false> : assign_merge_kernel<false, true>);
+        hipLaunchKernelGGL(mk, grid, dim3(256), 0, s, p.N, rs, cv.m, (const int32_t*)fs.cand, nz, tps,
+                           labels, fs);
+    } else if (fold) {
         launch_assign_t<false, true>(p, grid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, 0, s);
-    else
+    } else {
         launch_assign_t<false, false>(p, grid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, 0, s);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // candidate pass: the centre tiles of the flagged rows are split 8 per workgroup
     constexpr int TPS = 8;
