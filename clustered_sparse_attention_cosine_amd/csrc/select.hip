@@ -128,15 +128,24 @@ __global__ __launch_bounds__(256) void scores_kernel(int Cq, int Ck, const float
                 }
                 acc = mfma16(a0, qb[0][kc], acc);
             }
-            // lane holds slots b0 + cb*16 + 4g + i for q-cluster a
+            // lane holds slots b0 + cb*16 + 4g + i for q-cluster a: one 16-byte
+            // store (and one 16-byte read of the slot sizes) where the four fit
             if (aok) {
                 float* dst = S + ((int64_t)bh * Cq + a) * Ck;
+                const int b = b0 + cb * 16 + g * 4;
+                const int32_t* ksz = k_sizes + (int64_t)bh * Ck;
+                if (b + 3 < Ck && ((reinterpret_cast<uintptr_t>(dst + b) | reinterpret_cast<uintptr_t>(ksz + b)) & 15) == 0) {
+                    const int4 ks = *reinterpret_cast<const int4*>(ksz + b);
+                    float4 out;
+                    out.x = (b < ncl && ks.x > 0) ? acc[0] : -INFINITY;
+                    out.y = (b + 1 < ncl && ks.y > 0) ? acc[1] : -INFINITY;
+                    out.z = (b + 2 < ncl && ks.z > 0) ? acc[2] : -INFINITY;
+                    out.w = (b + 3 < ncl && ks.w > 0) ? acc[3] : -INFINITY;
+                    *reinterpret_cast<float4*>(dst + b) = out;
+                } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int b = b0 + cb * 16 + g * 4 + i;
-                    if (b < Ck) {
-                        const bool live = b < ncl && k_sizes[(int64_t)bh * Ck + b] > 0;
-                        dst[b] = live ? acc[i] : -INFINITY;
+                    for (int i = 0; i < 4; ++i) {
+                        if (b + i < Ck) dst[b + i] = (b + i < ncl && ksz[b + i] > 0) ? acc[i] : -INFINITY;
                     }
                 }
             }
