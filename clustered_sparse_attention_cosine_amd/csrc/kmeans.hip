@@ -550,16 +550,44 @@ hipError_t launch_bound_filter(const Prob& p, RowSet rs, CentView cv, const int3
 // The exact nearest centre is among the candidates, so exact f64 distances of
 // the candidates decide the label (cand_exact_kernel); a row with no or more
 // than CAND_CAP candidates goes to the full exact scan (launch_refine).
-template <typename T>
-__device__ double exact_d2(const T* xr, int D, int normalize, const float* c) {
+// The row and the centre are read 16 elements at a time with 16-byte loads (a
+// few in flight per chunk instead of one dependent load per element); the f64
+// arithmetic is the definition's, in index order.
+template <typename T, int D>
+__device__ double exact_d2(const T* xr, int normalize, const float* c) {
 #pragma clang fp contract(off)
-    double nrm = normalize ? seq_norm(xr, D) : 1.0;
+    constexpr int CH = 16;
+    double nrm = 1.0;
+    if (normalize) {
+        // ||x|| as seq_norm: squares summed in index order in f64, floored at 1e-12
+        double q = 0.0;
+#pragma unroll 1
+        for (int k = 0; k < D; k += CH) {
+            float a[8], b[8];
+            load8<T>(xr + k, a);
+            load8<T>(xr + k + 8, b);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q += (double)a[i] * (double)a[i];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q += (double)b[i] * (double)b[i];
+        }
+        nrm = sqrt(q);
+        nrm = nrm < 1e-12 ? 1e-12 : nrm;
+    }
     double s = 0.0;
-    for (int d = 0; d < D; ++d) {
-        const float xv = elem<T>::load(xr, d);
-        const float xh = normalize ? (float)((double)xv / nrm) : xv;
-        const double df = (double)xh - (double)c[d];
-        s += df * df;
+#pragma unroll 1
+    for (int k = 0; k < D; k += CH) {
+        float xv[CH], cv[CH];
+        load8<T>(xr + k, *reinterpret_cast<float(*)[8]>(&xv[0]));
+        load8<T>(xr + k + 8, *reinterpret_cast<float(*)[8]>(&xv[8]));
+        load8<float>(c + k, *reinterpret_cast<float(*)[8]>(&cv[0]));
+        load8<float>(c + k + 8, *reinterpret_cast<float(*)[8]>(&cv[8]));
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const float xh = normalize ? (float)((double)xv[i] / nrm) : xv[i];
+            const double df = (double)xh - (double)cv[i];
+            s += df * df;
+        }
     }
     return s;
 }
@@ -920,7 +948,7 @@ __global__ __launch_bounds__(256) void cand_exact_kernel(const T* __restrict__ X
         const int64_t tok = (okr && rs.rows) ? rs.rows[(int64_t)bh * N + r] : r;
         if (okr && nc <= CAND_CAP && ci < nc) {
             j = fs.cand[fe * CAND_CAP + ci];
-            d = exact_d2(row_ptr(X, N, D, bh, tok), D, normalize, cv.cent + (cbase + j) * D);
+            d = exact_d2<T, D>(row_ptr(X, N, D, bh, tok), normalize, cv.cent + (cbase + j) * D);
         }
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) {
