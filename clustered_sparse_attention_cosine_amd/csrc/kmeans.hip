@@ -183,20 +183,24 @@ hipError_t launch_last_valid(const Prob& p, CentView cv, const int32_t* mcount, 
 }
 
 // ------------------------------------------------------------------ norms
+// 8 lanes per row, each reading 8-element chunks with 16-byte loads (32 rows
+// per workgroup); squares summed in f64, then over the 8 lanes.
 template <typename T>
 __global__ __launch_bounds__(256) void inv_norm_kernel(const T* __restrict__ x, int64_t rows,
                                                        int D, float* __restrict__ inv) {
-    int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    int sub = threadIdx.x & 15;
+    int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+    int sub = threadIdx.x & 7;
     if (row >= rows) return;
     const T* r = x + row * D;
     double s = 0.0;
-    for (int j = sub; j < D; j += 16) {
-        double v = (double)elem<T>::load(r, j);
-        s += v * v;
+    for (int j = sub * 8; j < D; j += 64) {
+        float v[8];
+        load8<T>(r + j, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s += (double)v[i] * (double)v[i];
     }
 #pragma unroll
-    for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    for (int o = 4; o > 0; o >>= 1) s += __shfl_xor(s, o);
     if (sub == 0) {
         double n = sqrt(s);
         if (n < 1e-12) n = 1e-12;
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(256) void inv_norm_kernel(const T* __restrict__ x, 
 
 hipError_t launch_inv_norm(const Prob& p, const void* x, float* inv, hipStream_t s) {
     int64_t rows = (int64_t)p.BH * p.N;
-    dim3 grid((unsigned)((rows + 15) / 16));
+    dim3 grid((unsigned)((rows + 31) / 32));
     if (p.bf16)
         hipLaunchKernelGGL(inv_norm_kernel<u16>, grid, dim3(256), 0, s, (const u16*)x, rows, p.D, inv);
     else
@@ -263,15 +267,24 @@ __global__ __launch_bounds__(256) void init_sample_kernel(const T* __restrict__ 
     int64_t idx = (n >= cv.m) ? (int64_t)(((uint64_t)j * (uint64_t)n + r) / (uint64_t)cv.m) : j;
     int64_t tok = rs.rows ? rs.rows[(int64_t)bh * N + idx] : idx;
     const T* xr = row_ptr(x, N, D, bh, tok);
+    // one coalesced load per lane and 64 elements; the norm as seq_norm (squares
+    // summed in index order in f64, floored at 1e-12) from the lanes in order
+    float xv[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) xv[e] = l + 64 * e < D ? elem<T>::load(xr, l + 64 * e) : 0.0f;
     double nrm = 1.0;
     if (normalize) {
-        double v = (l == 0) ? seq_norm(xr, D) : 0.0;
-        nrm = __shfl(v, 0);
+        double q = 0.0;
+        for (int d = 0; d < D; ++d) {
+            const double v = (double)__shfl(xv[d >> 6], d & 63);
+            q += v * v;
+        }
+        nrm = sqrt(q);
+        nrm = nrm < 1e-12 ? 1e-12 : nrm;
     }
-    for (int d = l; d < D; d += 64) {
-        float xv = elem<T>::load(xr, d);
-        c[d] = normalize ? (float)((double)xv / nrm) : xv;
-    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+        if (l + 64 * e < D) c[l + 64 * e] = normalize ? (float)((double)xv[e] / nrm) : xv[e];
     if (l == 0) cv.valid[slot] = 1;
 }
 
