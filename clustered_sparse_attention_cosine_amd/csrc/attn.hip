@@ -22,48 +22,101 @@ namespace adc {
 hipError_t fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 
 // ------------------------------------------------------------------ runs
+// The selected slots of one (head, q-cluster) row as contiguous key runs: a run
+// continues while the next selected non-empty slot starts where the previous
+// one ended. One wave per row; lane L owns slots 64 L .. 64 L + 63 of each
+// 4096-slot chunk (mask words 2 L and 2 L + 1). Pass 1: every lane counts its
+// runs and keys; wave scans give the run index and key position of each lane's
+// first new run (a lane's first run continues the last one of the lanes before
+// it when they touch). Pass 2 writes the runs. The result is that of a
+// sequential walk over the slots. run_cap (Ck / 2 + 2) exceeds the largest
+// possible number of runs, ceil(Ck / 2).
 __global__ __launch_bounds__(256) void build_runs_kernel(int64_t rows, int Cq, int Ck,
                                                          const int32_t* __restrict__ k_offsets,
                                                          const uint32_t* __restrict__ mask,
                                                          int run_cap, int32_t* __restrict__ run_start,
                                                          int32_t* __restrict__ run_pos,
                                                          int32_t* __restrict__ n_runs) {
-    const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
+    const int l = threadIdx.x & 63;
     const int64_t bh = row / Cq;
     const int words = (Ck + 31) / 32;
     const uint32_t* m = mask + row * words;
     const int32_t* off = k_offsets + bh * (Ck + 1);
     int32_t* rs = run_start + row * run_cap;
     int32_t* rp = run_pos + row * (run_cap + 1);
-    int nr = 0, pos = 0, cs = -1, ce = -1;
-    for (int wd = 0; wd < words; ++wd) {
-        uint32_t bits = m[wd];
-        while (bits) {
-            const int b = wd * 32 + __ffs(bits) - 1;
-            bits &= bits - 1;
-            if (b >= Ck) break;
+    int nr = 0, pos = 0, ce = -1;  // runs and keys so far, end of the last run (wave-uniform)
+    for (int c0 = 0; c0 < Ck; c0 += 4096) {
+        const int b0 = c0 + 64 * l;
+        uint64_t bits = 0;
+        if (b0 < Ck) {
+            const int w0 = b0 / 32;
+            const uint32_t lo = m[w0];
+            const uint32_t hi = w0 + 1 < words ? m[w0 + 1] : 0u;
+            bits = (uint64_t)lo | ((uint64_t)hi << 32);
+            if (Ck - b0 < 64) bits &= (1ull << (Ck - b0)) - 1ull;
+        }
+        int cnt = 0, keys = 0, fs = -1, le = -1;
+        for (uint64_t t = bits; t; t &= t - 1) {
+            const int b = b0 + __ffsll((unsigned long long)t) - 1;
             const int s = off[b], e = off[b + 1];
             if (e <= s) continue;
-            if (s == ce) {
-                ce = e;
-            } else {
-                if (cs >= 0 && nr < run_cap) { rs[nr] = cs; rp[nr] = pos; pos += ce - cs; ++nr; }
-                cs = s;
-                ce = e;
+            if (fs < 0) fs = s;
+            if (s != le) ++cnt;
+            le = e;
+            keys += e - s;
+        }
+        // end of the last run of the lanes before this one (key ends grow with the slot)
+        int pmax = le;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(pmax, o);
+            if (l >= o) pmax = max(pmax, v);
+        }
+        int prev_le = __shfl_up(pmax, 1);
+        prev_le = max(l == 0 ? -1 : prev_le, ce);
+        const int newr = cnt - ((cnt > 0 && fs == prev_le) ? 1 : 0);
+        int ir = newr, ik = keys;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int vr = __shfl_up(ir, o), vk = __shfl_up(ik, o);
+            if (l >= o) {
+                ir += vr;
+                ik += vk;
             }
         }
+        int idx = nr + ir - newr, p = pos + ik - keys, le2 = prev_le;
+        for (uint64_t t = bits; t; t &= t - 1) {
+            const int b = b0 + __ffsll((unsigned long long)t) - 1;
+            const int s = off[b], e = off[b + 1];
+            if (e <= s) continue;
+            if (s != le2) {
+                if (idx < run_cap) {
+                    rs[idx] = s;
+                    rp[idx] = p;
+                }
+                ++idx;
+            }
+            p += e - s;
+            le2 = e;
+        }
+        nr += __shfl(ir, 63);
+        pos += __shfl(ik, 63);
+        ce = max(ce, __shfl(pmax, 63));
     }
-    if (cs >= 0 && nr < run_cap) { rs[nr] = cs; rp[nr] = pos; pos += ce - cs; ++nr; }
-    rp[nr] = pos;
-    n_runs[row] = nr;
+    if (l == 0) {
+        const int n = min(nr, run_cap);
+        rp[n] = pos;
+        n_runs[row] = n;
+    }
 }
 
 hipError_t launch_build_runs(const Prob& p, int Cq, int Ck, const int32_t* k_offsets,
                              const uint32_t* mask, int run_cap, int32_t* run_start,
                              int32_t* run_pos, int32_t* n_runs, hipStream_t s) {
     const int64_t rows = (int64_t)p.BH * Cq;
-    hipLaunchKernelGGL(build_runs_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, rows,
+    hipLaunchKernelGGL(build_runs_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, rows,
                        Cq, Ck, k_offsets, mask, run_cap, run_start, run_pos, n_runs);
     return hipGetLastError();
 }
