@@ -194,28 +194,36 @@ __global__ __launch_bounds__(256) void gather_stats_kernel(int N, int M,
     for (int h0 = beg; h0 < end; h0 += RS) {
         const int nb = min(RS, end - h0);
         const int tok_l = perm[(int64_t)bh * N + h0 + min(l, nb - 1)];
+        // every load of the batch (x, and v when it is permuted too) is issued
+        // before the first store; rows past the cluster repeat its last row
+        constexpr int IT = RS / RPI;
+        constexpr int EW = 16 / (int)sizeof(T);  // elements per 16-byte word
+        u32x4 xv[IT][W8], vv[IT][W8];
 #pragma unroll
-        for (int it = 0; it < RS / RPI; ++it) {
+        for (int it = 0; it < IT; ++it) {
             const int q = it * RPI + l / CPR, c = l % CPR;
-            const int64_t tok = __shfl(tok_l, q);
-            const int64_t src = ((int64_t)bh * N + tok) * D + c * 8;
+            const int64_t src = ((int64_t)bh * N + __shfl(tok_l, q)) * D + c * 8;
+#pragma unroll
+            for (int k = 0; k < W8; ++k) xv[it][k] = *reinterpret_cast<const u32x4*>(x + src + k * EW);
+            if (v_perm) {
+#pragma unroll
+                for (int k = 0; k < W8; ++k) vv[it][k] = *reinterpret_cast<const u32x4*>(v + src + k * EW);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int q = it * RPI + l / CPR, c = l % CPR;
             const int64_t dst = ((int64_t)bh * N + h0 + q) * D + c * 8;
-            u32x4 xv[W8];
 #pragma unroll
-            for (int k = 0; k < W8; ++k) xv[k] = *reinterpret_cast<const u32x4*>(x + src + k * (16 / (int)sizeof(T)));
-#pragma unroll
-            for (int k = 0; k < W8; ++k) *reinterpret_cast<u32x4*>(&xw[q * LDX + c * 8 + k * (16 / (int)sizeof(T))]) = xv[k];
+            for (int k = 0; k < W8; ++k) *reinterpret_cast<u32x4*>(&xw[q * LDX + c * 8 + k * EW]) = xv[it][k];
             if (q < nb) {
                 if (x_perm) {
 #pragma unroll
-                    for (int k = 0; k < W8; ++k)
-                        *reinterpret_cast<u32x4*>(x_perm + dst + k * (16 / (int)sizeof(T))) = xv[k];
+                    for (int k = 0; k < W8; ++k) *reinterpret_cast<u32x4*>(x_perm + dst + k * EW) = xv[it][k];
                 }
                 if (v_perm) {
 #pragma unroll
-                    for (int k = 0; k < W8; ++k)
-                        *reinterpret_cast<u32x4*>(v_perm + dst + k * (16 / (int)sizeof(T))) =
-                            *reinterpret_cast<const u32x4*>(v + src + k * (16 / (int)sizeof(T)));
+                    for (int k = 0; k < W8; ++k) *reinterpret_cast<u32x4*>(v_perm + dst + k * EW) = vv[it][k];
                 }
             }
         }
