@@ -221,7 +221,9 @@ hipError_t lloyd(const Prob& p, const void* x, int normalize, RowSet rs, const f
             ra = RowSet{w.rlist, w.rcount, rs.active, 1};
         }
         // a row subset (later stages: the few keys left in U) also splits the centre tiles
-        if ((e = launch_assign(p, x, ra, inv_norm, normalize, cv, mcount, labels, fs, s, rs.rows ? 4 : 0)))
+        // from the second round on, the previous round's finalize cleared the flag counts
+        if ((e = launch_assign(p, x, ra, inv_norm, normalize, cv, mcount, labels, fs, s, rs.rows ? 4 : 0,
+                               it > 0)))
             return e;
         if (it + 1 < iters || final_update) {
             if (ss && !rs.rows) {
@@ -232,9 +234,10 @@ hipError_t lloyd(const Prob& p, const void* x, int normalize, RowSet rs, const f
             }
             if ((e = launch_update_accum(p, x, rs, inv_norm, labels, cv, s, order))) return e;
             if (bounds && it + 1 < iters) {
-                if ((e = fill_i32(w.rcount, p.BH, 0, s))) return e;
-                if ((e = launch_finalize(p, cv, rs.active, 1, s, w.drift))) return e;
-            } else if ((e = launch_finalize(p, cv, rs.active, 1, s))) {
+                if ((e = launch_finalize(p, cv, rs.active, 1, s, w.drift, w.flag_count, w.over_count,
+                                         w.rcount)))
+                    return e;
+            } else if ((e = launch_finalize(p, cv, rs.active, 1, s, nullptr, w.flag_count, w.over_count))) {
                 return e;
             }
         }

@@ -72,8 +72,10 @@ hipError_t launch_init_kmeanspp(const Prob& p, const void* x, const float* xf, R
 // Centroid prep: split into bf16 hi/lo, squared norms (+inf where no centre).
 // With sums != NULL it first moves centres to sums/cnt (cnt > 0) and clears the sums;
 // then with drift != NULL also drift[slot] >= ||new - old|| (0 where no centre).
+// zero_a/b/c (may be null): per-head counters [BH] cleared on the way.
 hipError_t launch_finalize(const Prob& p, CentView cv, const uint8_t* active, int with_sums,
-                           hipStream_t s, float* drift = nullptr);
+                           hipStream_t s, float* drift = nullptr, int32_t* zero_a = nullptr,
+                           int32_t* zero_b = nullptr, int32_t* zero_c = nullptr);
 // Flag lists of the certified assignment (see kmeans.hip).
 struct FlagSet {
     int32_t* list;
@@ -106,7 +108,7 @@ hipError_t launch_last_valid(const Prob& p, CentView cv, const int32_t* mcount, 
 // `split` workgroups per row block (same labels; shorter serial chain per row).
 hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
                          int normalize, CentView cv, const int32_t* mcount, int32_t* labels,
-                         FlagSet fs, hipStream_t s, int split = 0);
+                         FlagSet fs, hipStream_t s, int split = 0, bool counts_zeroed = false);
 // Bound test between Lloyd rounds (every row, rs.rows NULL): a row whose bound on
 // its own centre, grown by that centre's drift, stays below its bound on every
 // other centre, shrunk by the largest drift, keeps its label and the moved

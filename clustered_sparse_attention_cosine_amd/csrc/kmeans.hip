@@ -402,12 +402,20 @@ hipError_t launch_init_kmeanspp(const Prob& p, const void* x, const float* xf, R
 // squared norm (+inf where the slot holds no centre).
 template <int D>
 __global__ __launch_bounds__(256) void finalize_kernel(CentView cv, const uint8_t* active,
-                                                       int with_sums, float* drift) {
+                                                       int with_sums, float* drift, int32_t* zero_a,
+                                                       int32_t* zero_b, int32_t* zero_c) {
     const int bh = blockIdx.y;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int j = blockIdx.x * 4 + w;
     if (active && !active[bh]) return;
     if (j >= cv.m) return;
+    if (j == 0 && threadIdx.x == 0) {
+        // per-head counters of the next round (flag lists, rows to redo), so that
+        // no separate clearing launch sits between the rounds
+        if (zero_a) zero_a[bh] = 0;
+        if (zero_b) zero_b[bh] = 0;
+        if (zero_c) zero_c[bh] = 0;
+    }
     const int64_t slot = (int64_t)bh * cv.cap + cv.base + j;
     float* c = cv.cent + slot * D;
     constexpr int E = D / 64;
@@ -450,12 +458,15 @@ __global__ __launch_bounds__(256) void finalize_kernel(CentView cv, const uint8_
 }
 
 hipError_t launch_finalize(const Prob& p, CentView cv, const uint8_t* active, int with_sums,
-                           hipStream_t s, float* drift) {
+                           hipStream_t s, float* drift, int32_t* zero_a, int32_t* zero_b,
+                           int32_t* zero_c) {
     dim3 grid((unsigned)((cv.m + 3) / 4), (unsigned)p.BH);
     if (p.D == 64)
-        hipLaunchKernelGGL(finalize_kernel<64>, grid, dim3(256), 0, s, cv, active, with_sums, drift);
+        hipLaunchKernelGGL(finalize_kernel<64>, grid, dim3(256), 0, s, cv, active, with_sums, drift,
+                           zero_a, zero_b, zero_c);
     else
-        hipLaunchKernelGGL(finalize_kernel<128>, grid, dim3(256), 0, s, cv, active, with_sums, drift);
+        hipLaunchKernelGGL(finalize_kernel<128>, grid, dim3(256), 0, s, cv, active, with_sums, drift,
+                           zero_a, zero_b, zero_c);
     return hipGetLastError();
 }
 
@@ -1090,11 +1101,13 @@ __global__ __launch_bounds__(256) void assign_merge_kernel(int N, RowSet rs, int
 
 hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
                          int normalize, CentView cv, const int32_t* mcount, int32_t* labels,
-                         FlagSet fs, hipStream_t s, int split) {
-    hipLaunchKernelGGL(zero2_i32_kernel, dim3((unsigned)((p.BH + 255) / 256)), dim3(256), 0, s, fs.count,
-                       fs.over_count, p.BH);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+                         FlagSet fs, hipStream_t s, int split, bool counts_zeroed) {
+    hipError_t e = hipSuccess;
+    if (!counts_zeroed) {
+        hipLaunchKernelGGL(zero2_i32_kernel, dim3((unsigned)((p.BH + 255) / 256)), dim3(256), 0, s,
+                           fs.count, fs.over_count, p.BH);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)p.BH);
     const bool fold = !normalize && !inv_norm;  // rows not rescaled: folded assignment pass
     const int tiles_m = (cv.m + 63) / 64;
