@@ -99,6 +99,8 @@ __global__ __launch_bounds__(1024) void seg_rank_kernel(const int32_t* __restric
                                                         const int32_t* __restrict__ seg_cnt,
                                                         int32_t* __restrict__ perm) {
     __shared__ int running[8192];
+    __shared__ int grp_lab[16][64], grp_size[16][64], grp_base[16][64];
+    __shared__ int ngrp[16];
     const int sg = blockIdx.x, bh = blockIdx.y;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int32_t* off = offsets + (int64_t)bh * (M + 1);
@@ -124,18 +126,34 @@ __global__ __launch_bounds__(1024) void seg_rank_kernel(const int32_t* __restric
         const int rank = __popcll(m & lt);
         const int gsize = __popcll(m);
         const int leader = m ? __ffsll((unsigned long long)m) - 1 : 0;
-        int pos = 0;
-        for (int ww = 0; ww < 16; ++ww) {
-            if (w == ww) {
-                const bool is_leader = ok && l == leader;
-                const int bv = is_leader ? running[lab] : 0;
-                const int gb = __shfl(bv, leader);
-                if (is_leader) running[lab] = gb + gsize;
-                pos = gb + rank;
-            }
-            __syncthreads();
+        // each wave lists its groups (label, size) in lane order of their leaders;
+        // one wave then walks the 16 lists in wave order, one lane per group (the
+        // labels of one list are distinct), advancing the counters and writing
+        // back every group's base
+        const bool is_leader = ok && l == leader;
+        const uint64_t lm = __ballot(is_leader);
+        if (is_leader) {
+            const int slot = __popcll(lm & lt);
+            grp_lab[w][slot] = lab;
+            grp_size[w][slot] = gsize;
         }
-        if (ok) perm[(int64_t)bh * N + pos] = i;
+        if (l == 0) ngrp[w] = __popcll(lm);
+        __syncthreads();
+        if (w == 0) {
+            for (int ww = 0; ww < 16; ++ww) {
+                if (l < ngrp[ww]) {
+                    const int lb = grp_lab[ww][l];
+                    const int b = running[lb];
+                    grp_base[ww][l] = b;
+                    running[lb] = b + grp_size[ww][l];
+                }
+            }
+        }
+        __syncthreads();
+        if (ok) {
+            const int slot = __popcll(lm & ((leader == 0) ? 0ull : (~0ull >> (64 - leader))));
+            perm[(int64_t)bh * N + grp_base[w][slot] + rank] = i;
+        }
     }
 }
 
