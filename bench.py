@@ -78,8 +78,8 @@ def main():
                     help="only warmup + timed steps (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(heads would be sharded across GPUs with no exchange; see DESIGN.md)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the heads of a layer would be split across GPUs, with no exchange between them)",
               file=sys.stderr)
         sys.exit(2)
 
