@@ -45,6 +45,15 @@ class QParams(ctypes.Structure):
                 ("init", ctypes.c_int32), ("pad_", ctypes.c_int32), ("seed", ctypes.c_uint64)]
 
 
+TRACE_STAGES = 8
+
+
+class KTrace(ctypes.Structure):
+    _fields_ = [("stage_centroids", ctypes.c_void_p), ("last_centroids", ctypes.c_void_p),
+                ("slot_valid", ctypes.c_void_p), ("stage_labels", ctypes.c_void_p),
+                ("stage_base", ctypes.c_void_p)]
+
+
 class KParams(ctypes.Structure):
     _fields_ = [("base_clusters", ctypes.c_int32), ("max_clusters", ctypes.c_int32),
                 ("iters", ctypes.c_int32), ("tau_mult", ctypes.c_float),
@@ -64,8 +73,9 @@ _SIGS = {
     "adacluster_cluster_k_workspace": (_SZ, [_VP, _VP]),
     "adacluster_cluster_k": (_I32, [_VP, _VP] + [_VP] * 16 + [_VP, _SZ, _VP]),
     "adacluster_select_workspace": (_SZ, [_VP, _I32, _I32]),
-    "adacluster_select": (_I32, [_VP, _I32, _I32] + [_VP] * 7 + [_I32, _I32, _F32, _I32, _F32]
-                          + [_VP, _VP, _VP, _SZ, _VP]),
+    "adacluster_cluster_k_trace": (_I32, [_VP, _VP] + [_VP] * 16 + [_VP, _SZ, _VP]),
+    "adacluster_select": (_I32, [_VP, _I32, _I32] + [_VP] * 8 + [_I32, _I32, _F32, _I32, _F32]
+                          + [_VP, _VP, _VP, _VP, _SZ, _VP]),
     "adacluster_sparse_attn_workspace": (_SZ, [_VP, _I32, _I32]),
     "adacluster_sparse_attn": (_I32, [_VP, _I32, _I32] + [_VP] * 7
                                + [_F32, _VP, _I32, _VP, _VP, _SZ, _VP]),
@@ -170,11 +180,14 @@ def cluster_q(q, n_clusters, iters=5, init="sample", seed=0, init_centroids=None
 
 
 def cluster_k(k, v, base_clusters, max_clusters=None, iters=5, tau_mult=1.5, adaptive=True,
-              init="sample", seed=0, init_centroids=None, n_clusters=None, full=None, tau=None):
+              init="sample", seed=0, init_centroids=None, n_clusters=None, full=None, tau=None,
+              trace=False):
     """adaptive: True (Algorithm 1), False (one k-means with base_clusters) or
     "warm" (keep the per-head counts `n_clusters` and flags `full` of an earlier
     adaptive call and start from its centres `init_centroids`; init is then
-    "caller"). The state tensors passed in are copied, not modified."""
+    "caller"). The state tensors passed in are copied, not modified.
+    trace=True (adaptive only) also returns the record of Algorithm 1's
+    decisions under "trace" (adacluster_cluster_k_trace)."""
     sh = _shape(k)
     if v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("k and v must share shape and dtype")
@@ -222,17 +235,33 @@ def cluster_k(k, v, base_clusters, max_clusters=None, iters=5, tau_mult=1.5, ada
     )
     ws = _workspace(ws_n, dev)
     ic = None if init_centroids is None else init_centroids.contiguous().float()
-    _check(lib().adacluster_cluster_k(
-        ctypes.byref(sh), ctypes.byref(prm), _p(k), _p(v), _p(ic), _p(out["n_clusters"]),
-        _p(out["full"]), _p(out["tau"]), _p(out["assign"]), _p(out["centroids"]), _p(out["sizes"]),
-        _p(out["kmax"]), _p(out["kmin"]), _p(out["perm"]), _p(out["offsets"]), _p(out["k_perm"]),
-        _p(out["v_perm"]), _p(out["stage_sizes"]), _p(ws), ws.numel(), _stream(dev)))
+    common = [_p(out["n_clusters"]), _p(out["full"]), _p(out["tau"]), _p(out["assign"]),
+              _p(out["centroids"]), _p(out["sizes"]), _p(out["kmax"]), _p(out["kmin"]),
+              _p(out["perm"]), _p(out["offsets"]), _p(out["k_perm"]), _p(out["v_perm"]),
+              _p(out["stage_sizes"])]
+    if trace:
+        tr = dict(stage_centroids=torch.empty(B, H, nmax, D, dtype=torch.float32, device=dev),
+                  last_centroids=torch.empty(B, H, nmax, D, dtype=torch.float32, device=dev),
+                  slot_valid=torch.empty(B, H, nmax, dtype=torch.uint8, device=dev),
+                  stage_labels=torch.empty(B, H, TRACE_STAGES, N, dtype=torch.int32, device=dev),
+                  stage_base=torch.empty(B, H, TRACE_STAGES, dtype=torch.int32, device=dev))
+        rec = KTrace(*(t.data_ptr() for t in tr.values()))
+        _check(lib().adacluster_cluster_k_trace(
+            ctypes.byref(sh), ctypes.byref(prm), _p(k), _p(v), *common, ctypes.byref(rec), _p(ws),
+            ws.numel(), _stream(dev)))
+        out["trace"] = tr
+    else:
+        _check(lib().adacluster_cluster_k(
+            ctypes.byref(sh), ctypes.byref(prm), _p(k), _p(v), _p(ic), *common, _p(ws), ws.numel(),
+            _stream(dev)))
     out["max_clusters"] = nmax
     return out
 
 
-def select(qrep, K, top_p=0.9, score="quest", rule="topp", top_k=64, scale=None):
-    """K: the dict returned by cluster_k (or the same keys)."""
+def select(qrep, K, top_p=0.9, score="quest", rule="topp", top_k=64, scale=None, q_offsets=None):
+    """K: the dict returned by cluster_k (or the same keys). With q_offsets (the
+    query clustering's offsets) the result also holds "pairs" [B, H] int64, the
+    query-key pairs the attention will compute."""
     B, H, Cq, D = qrep.shape
     kmax = K["kmax"]
     Ck = kmax.shape[2]
@@ -241,13 +270,14 @@ def select(qrep, K, top_p=0.9, score="quest", rule="topp", top_k=64, scale=None)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     words = (Ck + 31) // 32
     out = dict(mask=torch.empty(B, H, Cq, words, dtype=torch.int32, device=dev),
-               sel_keys=torch.empty(B, H, Cq, dtype=torch.int32, device=dev))
+               sel_keys=torch.empty(B, H, Cq, dtype=torch.int32, device=dev),
+               pairs=None if q_offsets is None else torch.empty(B, H, dtype=torch.int64, device=dev))
     ws = _workspace(lib().adacluster_select_workspace(ctypes.byref(sh), Cq, Ck), dev)
     _check(lib().adacluster_select(
-        ctypes.byref(sh), Cq, Ck, _p(qrep.contiguous()), _p(kmax), _p(K["kmin"]),
+        ctypes.byref(sh), Cq, Ck, _p(qrep.contiguous()), _p(q_offsets), _p(kmax), _p(K["kmin"]),
         _p(K.get("centroids")), _p(K["sizes"]), _p(K["n_clusters"]), _p(K["full"]), SCORE[score],
         RULE[rule], float(top_p), int(top_k), float(scale), _p(out["mask"]), _p(out["sel_keys"]),
-        _p(ws), ws.numel(), _stream(dev)))
+        _p(out["pairs"]), _p(ws), ws.numel(), _stream(dev)))
     return out
 
 
@@ -414,7 +444,7 @@ def layer(q, k, v, cfg: LayerConfig, prev=None):
     from the previous centres, and the keys keep their per-head counts and
     full-attention flags."""
     Q, K = cluster_layer(q, k, v, cfg, prev)
-    S = select(Q["qrep"], K, cfg.top_p, cfg.score, cfg.rule, cfg.top_k)
+    S = select(Q["qrep"], K, cfg.top_p, cfg.score, cfg.rule, cfg.top_k, q_offsets=Q["offsets"])
     out, lse = sparse_attn(q, Q["perm"], Q["offsets"], K["k_perm"], K["v_perm"], K["offsets"],
                            S["mask"])
     return out, lse, dict(Q=Q, K=K, S=S)

@@ -35,12 +35,15 @@ int32_t fail(int32_t code, const char* fmt, ...) {
 constexpr int MAX_CLUSTERS = 8192;
 constexpr int MAX_N = 1 << 21;
 
-// Bump allocator over the caller's workspace (256-byte aligned pieces). With
-// base == nullptr it only measures.
+// Bump allocator over the caller's workspace: pieces at 256-byte aligned
+// device addresses. The base is first rounded up to a multiple of 256, which
+// the 256 bytes of slack every *_workspace() size adds to the measured total
+// cover. With base == nullptr it only measures.
 struct Carver {
     char* base;
     size_t used = 0;
-    explicit Carver(void* b) : base((char*)b) {}
+    explicit Carver(void* b)
+        : base(b ? (char*)(((uintptr_t)b + 255) & ~(uintptr_t)255) : nullptr) {}
     template <typename T>
     T* take(size_t count) {
         size_t off = (used + 255) & ~size_t(255);
@@ -95,7 +98,8 @@ struct KmeansWs {
     uint16_t* c_lo = nullptr;
     float* cn2 = nullptr;
     float* sums = nullptr;
-    int32_t* cnt = nullptr;
+    float* part = nullptr;
+    int nwav = 0;
     float* xhat = nullptr;
     double* d2 = nullptr;
     uint8_t* chosen = nullptr;
@@ -127,7 +131,8 @@ void plan_kmeans(Carver& c, const Prob& p, int cap, bool want_inv, bool kpp, boo
     w.c_lo = c.take<uint16_t>(bhc * p.D);
     w.cn2 = c.take<float>(bhc);
     w.sums = c.take<float>(bhc * p.D);
-    w.cnt = c.take<int32_t>(bhc);
+    w.nwav = (p.N + 63) / 64;
+    w.part = c.take<float>((size_t)p.BH * w.nwav * 2 * p.D);
     w.hist = c.take<int32_t>(bhc);
     w.seg_cnt = c.take<int32_t>(bhc * sort_segments(p.N));
     w.m_eff = c.take<int32_t>(p.BH);
@@ -175,7 +180,8 @@ CentView make_view(float* cent, const KmeansWs& w, int cap, int base, int m) {
     v.c_lo = w.c_lo;
     v.cn2 = w.cn2;
     v.sums = w.sums;
-    v.cnt = w.cnt;
+    v.part = w.part;
+    v.nwav = w.nwav;
     v.cap = cap;
     v.base = base;
     v.m = m;
@@ -193,21 +199,20 @@ struct SortScratch {
 
 // Lloyd rounds on one centroid view. With final_update the last round also
 // moves the centres (multi-stage stages need the stage centres); otherwise the
-// last centres are left to the exact member means of the layout pass. With
-// ss, on every row (rs.rows null), each update takes the rows sorted by the
-// round's labels (stable counting sort, about 47 us at 75.6K rows x 30 heads): every
-// cluster is then one run, which the update folds into one atomic per
-// dimension and wave, so its f32 atomics (about 60 % of its time in row order)
-// nearly vanish. The sums are the same up to f32 rounding order.
-// On every row the rounds also keep distance bounds (Hamerly's test): from the
-// second round on, only rows whose bounds no longer prove their label are
-// assigned again; the others keep it, which the exact assignment would too.
+// last centres are left to the exact member means of the layout pass. Each
+// update takes the rows sorted by the round's labels (stable counting sort,
+// about 47 us at 75.6K rows x 30 heads), so every cluster is one run of rows
+// and its sum is formed without atomics, in a fixed order.
+// On every row (rs.rows null) the rounds also keep distance bounds (Hamerly's
+// test): from the second round on, only rows whose bounds no longer prove
+// their label are assigned again; the others keep it, which the exact
+// assignment would too. snap (may be null, [BH][cap][D]) receives the centres
+// of view cv as they are just before the last assignment.
 hipError_t lloyd(const Prob& p, const void* x, int normalize, RowSet rs, const float* inv_norm,
                  CentView cv, int iters, bool final_update, int32_t* labels, const KmeansWs& w,
-                 hipStream_t s, const int32_t* mcount = nullptr, const SortScratch* ss = nullptr) {
+                 hipStream_t s, const int32_t* mcount, const SortScratch& ss, float* snap = nullptr) {
     hipError_t e;
-    const int32_t* order = nullptr;
-    const bool bounds = ss && !rs.rows;
+    const bool bounds = !rs.rows;
     FlagSet fs = flags_of(w);
     if (bounds) {
         fs.ub = w.ub;
@@ -220,24 +225,23 @@ hipError_t lloyd(const Prob& p, const void* x, int normalize, RowSet rs, const f
                 return e;
             ra = RowSet{w.rlist, w.rcount, rs.active, 1};
         }
+        if (snap && it + 1 == iters && (e = launch_copy_slots(p, cv, rs.active, snap, s))) return e;
         // a row subset (later stages: the few keys left in U) also splits the centre tiles
         // from the second round on, the previous round's finalize cleared the flag counts
         if ((e = launch_assign(p, x, ra, inv_norm, normalize, cv, mcount, labels, fs, s, rs.rows ? 4 : 0,
                                it > 0)))
             return e;
         if (it + 1 < iters || final_update) {
-            if (ss && !rs.rows) {
-                if ((e = launch_counting_sort(p, labels, cv.m, w.seg_cnt, w.hist, ss->sizes, ss->offsets,
-                                              ss->perm, s)))
-                    return e;
-                order = ss->perm;
-            }
-            if ((e = launch_update_accum(p, x, rs, inv_norm, labels, cv, s, order))) return e;
+            if ((e = launch_counting_sort(p, labels, cv.m, w.seg_cnt, w.hist, ss.sizes, ss.offsets, ss.perm,
+                                          s, rs.nrows, rs.active)))
+                return e;
+            if ((e = launch_update_accum(p, x, rs, inv_norm, labels, cv, ss.perm, s))) return e;
             if (bounds && it + 1 < iters) {
-                if ((e = launch_finalize(p, cv, rs.active, 1, s, w.drift, w.flag_count, w.over_count,
+                if ((e = launch_finalize(p, cv, rs.active, ss.offsets, s, w.drift, w.flag_count, w.over_count,
                                          w.rcount)))
                     return e;
-            } else if ((e = launch_finalize(p, cv, rs.active, 1, s, nullptr, w.flag_count, w.over_count))) {
+            } else if ((e = launch_finalize(p, cv, rs.active, ss.offsets, s, nullptr, w.flag_count,
+                                            w.over_count))) {
                 return e;
             }
         }
@@ -317,14 +321,12 @@ int32_t adacluster_cluster_q(const adc_shape* shape, const adc_q_params* prm, co
     plan_q(c, shape, prm, w);
 
     HIPCHK(launch_inv_norm(p, q, w.inv_norm, s));
-    HIPCHK(fill_i32((int32_t*)w.sums, (int64_t)p.BH * Cq * p.D, 0, s));
-    HIPCHK(fill_i32(w.cnt, (int64_t)p.BH * Cq, 0, s));
     CentView cv = make_view(centroids, w, Cq, 0, Cq);
     RowSet all{nullptr, nullptr, nullptr};
     HIPCHK(init_centres(p, q, 1, all, cv, prm->init, init_centroids, prm->seed, TENSOR_Q, 0, w, s));
-    HIPCHK(launch_finalize(p, cv, nullptr, 0, s));
+    HIPCHK(launch_finalize(p, cv, nullptr, nullptr, s));
     const SortScratch ss{sizes, offsets, perm};
-    HIPCHK(lloyd(p, q, 1, all, w.inv_norm, cv, prm->iters, false, assign, w, s, nullptr, &ss));
+    HIPCHK(lloyd(p, q, 1, all, w.inv_norm, cv, prm->iters, false, assign, w, s, nullptr, ss));
     HIPCHK(launch_counting_sort(p, assign, Cq, w.seg_cnt, w.hist, sizes, offsets, perm, s));
     HIPCHK(launch_gather_stats(p, Cq, offsets, perm, q, nullptr, 1, centroids, qrep, nullptr,
                                nullptr, nullptr, nullptr, s));
@@ -370,12 +372,13 @@ size_t adacluster_cluster_k_workspace(const adc_shape* shape, const adc_k_params
     return c.used + 256;
 }
 
-int32_t adacluster_cluster_k(const adc_shape* shape, const adc_k_params* prm, const void* k,
-                             const void* v, const float* init_centroids, int32_t* n_clusters,
-                             uint8_t* full_attn, float* tau, int32_t* assign, float* centroids,
-                             int32_t* sizes, void* kmax, void* kmin, int32_t* perm,
-                             int32_t* offsets, void* k_perm, void* v_perm, int32_t* stage_sizes,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+static int32_t cluster_k_impl(const adc_shape* shape, const adc_k_params* prm, const void* k,
+                              const void* v, const float* init_centroids, int32_t* n_clusters,
+                              uint8_t* full_attn, float* tau, int32_t* assign, float* centroids,
+                              int32_t* sizes, void* kmax, void* kmin, int32_t* perm,
+                              int32_t* offsets, void* k_perm, void* v_perm, int32_t* stage_sizes,
+                              const adc_k_trace* tr, void* workspace, size_t workspace_bytes,
+                              void* stream) {
     int32_t st = check_k(shape, prm);
     if (st) return st;
     REQ(k); REQ(v); REQ(n_clusters); REQ(full_attn); REQ(tau); REQ(assign); REQ(centroids);
@@ -383,6 +386,8 @@ int32_t adacluster_cluster_k(const adc_shape* shape, const adc_k_params* prm, co
     REQ(workspace);
     if (prm->init == ADC_INIT_CALLER && !init_centroids)
         return fail(ADC_EINVAL, "init == ADC_INIT_CALLER needs init_centroids");
+    if (tr && prm->adaptive != ADC_K_STAGED)
+        return fail(ADC_EUNSUPPORTED, "a stage record needs the STAGED mode");
     const size_t need = adacluster_cluster_k_workspace(shape, prm);
     if (workspace_bytes < need)
         return fail(ADC_EWORKSPACE, "workspace of %zu bytes is below the %zu required", workspace_bytes, need);
@@ -396,8 +401,6 @@ int32_t adacluster_cluster_k(const adc_shape* shape, const adc_k_params* prm, co
 
     HIPCHK(fill_i32((int32_t*)centroids, (int64_t)p.BH * nmax * p.D, 0, s));
     HIPCHK(fill_u8(w.valid, (int64_t)p.BH * nmax, 0, s));
-    HIPCHK(fill_i32((int32_t*)w.sums, (int64_t)p.BH * nmax * p.D, 0, s));
-    HIPCHK(fill_i32(w.cnt, (int64_t)p.BH * nmax, 0, s));
     RowSet all{nullptr, nullptr, nullptr};
     const SortScratch ss{sizes, offsets, perm};
 
@@ -406,15 +409,22 @@ int32_t adacluster_cluster_k(const adc_shape* shape, const adc_k_params* prm, co
         HIPCHK(launch_warm_info(p.BH, p.N, nmax, n_clusters, stage_sizes, s));
         CentView cv = make_view(centroids, w, nmax, 0, nmax);
         HIPCHK(launch_warm_init(p, init_centroids, n_clusters, cv, s));
-        HIPCHK(launch_finalize(p, cv, nullptr, 0, s));
-        HIPCHK(lloyd(p, k, 0, all, nullptr, cv, prm->iters, false, assign, w, s, n_clusters, &ss));
+        HIPCHK(launch_finalize(p, cv, nullptr, nullptr, s));
+        HIPCHK(lloyd(p, k, 0, all, nullptr, cv, prm->iters, false, assign, w, s, n_clusters, ss));
     } else if (prm->adaptive == ADC_K_FIXED) {
         CentView cv = make_view(centroids, w, nmax, 0, m0);
         HIPCHK(init_centres(p, k, 0, all, cv, prm->init, init_centroids, prm->seed, TENSOR_K, 0, w, s));
-        HIPCHK(launch_finalize(p, cv, nullptr, 0, s));
-        HIPCHK(lloyd(p, k, 0, all, nullptr, cv, prm->iters, false, assign, w, s, nullptr, &ss));
+        HIPCHK(launch_finalize(p, cv, nullptr, nullptr, s));
+        HIPCHK(lloyd(p, k, 0, all, nullptr, cv, prm->iters, false, assign, w, s, nullptr, ss));
         HIPCHK(launch_fixed_info(p.BH, p.N, m0, n_clusters, full_attn, tau, stage_sizes, s));
     } else {
+        if (tr) {
+            if (tr->stage_labels)
+                HIPCHK(fill_i32(tr->stage_labels, (int64_t)p.BH * TRACE_STAGES * p.N, -1, s));
+            if (tr->stage_base) HIPCHK(fill_i32(tr->stage_base, (int64_t)p.BH * TRACE_STAGES, -1, s));
+            if (tr->last_centroids)
+                HIPCHK(fill_i32((int32_t*)tr->last_centroids, (int64_t)p.BH * nmax * p.D, 0, s));
+        }
         StageState S = sw.st;
         S.stage_sizes = stage_sizes;
         HIPCHK(launch_stage_reset(p, S, s));
@@ -428,8 +438,10 @@ int32_t adacluster_cluster_k(const adc_shape* shape, const adc_k_params* prm, co
             RowSet rs{t == 0 ? nullptr : u_cur, S.nu, S.active};
             CentView cv = make_view(centroids, w, nmax, base, mt);
             HIPCHK(init_centres(p, k, 0, rs, cv, prm->init, nullptr, prm->seed, TENSOR_K, (uint32_t)t, w, s));
-            HIPCHK(launch_finalize(p, cv, S.active, 0, s));
-            HIPCHK(lloyd(p, k, 0, rs, nullptr, cv, prm->iters, true, sw.labels_u, w, s, nullptr, &ss));
+            HIPCHK(launch_finalize(p, cv, S.active, nullptr, s));
+            HIPCHK(lloyd(p, k, 0, rs, nullptr, cv, prm->iters, true, sw.labels_u, w, s, nullptr, ss,
+                         tr ? tr->last_centroids : nullptr));
+            if (tr) HIPCHK(launch_trace_stage(p, rs, sw.labels_u, base, t, tr->stage_labels, tr->stage_base, s));
             HIPCHK(launch_stage_dist(p, k, rs, sw.labels_u, cv, S.dist, s));
             if (t == 0) HIPCHK(launch_stage_tau(p, S, (double)prm->tau_mult, s));
             HIPCHK(launch_stage_compact(p, S, t == 0 ? nullptr : u_cur, u_next, mt, s));
@@ -440,7 +452,12 @@ int32_t adacluster_cluster_k(const adc_shape* shape, const adc_k_params* prm, co
         HIPCHK(launch_stage_end(p, S, t, nmax, n_clusters, full_attn, tau, s));
         // final assignment over every slot that holds a centre (Algorithm 1 step 20)
         CentView cvf = make_view(centroids, w, nmax, 0, nmax);
-        HIPCHK(launch_finalize(p, cvf, nullptr, 0, s));
+        if (tr) {
+            if (tr->stage_centroids) HIPCHK(launch_copy_slots(p, cvf, nullptr, tr->stage_centroids, s));
+            if (tr->slot_valid)
+                HIPCHK(hipMemcpyAsync(tr->slot_valid, w.valid, (size_t)p.BH * nmax, hipMemcpyDeviceToDevice, s));
+        }
+        HIPCHK(launch_finalize(p, cvf, nullptr, nullptr, s));
         // slots after the last one holding a centre (the unfilled end of the last
         // stage) are left out of the contraction
         HIPCHK(launch_last_valid(p, cvf, n_clusters, w.m_eff, s));
@@ -450,6 +467,30 @@ int32_t adacluster_cluster_k(const adc_shape* shape, const adc_k_params* prm, co
     HIPCHK(launch_gather_stats(p, nmax, offsets, perm, k, v, 0, centroids, nullptr, kmax, kmin,
                                k_perm, v_perm, s));
     return ADC_OK;
+}
+
+int32_t adacluster_cluster_k(const adc_shape* shape, const adc_k_params* prm, const void* k,
+                             const void* v, const float* init_centroids, int32_t* n_clusters,
+                             uint8_t* full_attn, float* tau, int32_t* assign, float* centroids,
+                             int32_t* sizes, void* kmax, void* kmin, int32_t* perm,
+                             int32_t* offsets, void* k_perm, void* v_perm, int32_t* stage_sizes,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    return cluster_k_impl(shape, prm, k, v, init_centroids, n_clusters, full_attn, tau, assign,
+                          centroids, sizes, kmax, kmin, perm, offsets, k_perm, v_perm, stage_sizes,
+                          nullptr, workspace, workspace_bytes, stream);
+}
+
+int32_t adacluster_cluster_k_trace(const adc_shape* shape, const adc_k_params* prm, const void* k,
+                                   const void* v, int32_t* n_clusters, uint8_t* full_attn,
+                                   float* tau, int32_t* assign, float* centroids, int32_t* sizes,
+                                   void* kmax, void* kmin, int32_t* perm, int32_t* offsets,
+                                   void* k_perm, void* v_perm, int32_t* stage_sizes,
+                                   const adc_k_trace* trace, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    if (!trace) return fail(ADC_EINVAL, "trace is NULL");
+    return cluster_k_impl(shape, prm, k, v, nullptr, n_clusters, full_attn, tau, assign, centroids,
+                          sizes, kmax, kmin, perm, offsets, k_perm, v_perm, stage_sizes, trace,
+                          workspace, workspace_bytes, stream);
 }
 
 // ====================================================================== select
@@ -470,14 +511,16 @@ size_t adacluster_select_workspace(const adc_shape* shape, int32_t Cq, int32_t C
 }
 
 int32_t adacluster_select(const adc_shape* shape, int32_t Cq, int32_t Ck, const float* qrep,
-                          const void* kmax, const void* kmin, const float* centroids,
-                          const int32_t* k_sizes, const int32_t* n_clusters,
-                          const uint8_t* full_attn, int32_t score, int32_t rule, float top_p,
-                          int32_t top_k, float scale, uint32_t* sel_mask, int32_t* sel_keys,
+                          const int32_t* q_offsets, const void* kmax, const void* kmin,
+                          const float* centroids, const int32_t* k_sizes,
+                          const int32_t* n_clusters, const uint8_t* full_attn, int32_t score,
+                          int32_t rule, float top_p, int32_t top_k, float scale,
+                          uint32_t* sel_mask, int32_t* sel_keys, int64_t* sel_pairs,
                           void* workspace, size_t workspace_bytes, void* stream) {
     int32_t st = check_sel_dims(shape, Cq, Ck);
     if (st) return st;
     REQ(qrep); REQ(k_sizes); REQ(n_clusters); REQ(full_attn); REQ(sel_mask); REQ(sel_keys); REQ(workspace);
+    if (sel_pairs && !q_offsets) return fail(ADC_EINVAL, "sel_pairs needs q_offsets");
     if (score == ADC_SCORE_QUEST) {
         REQ(kmax); REQ(kmin);
     } else if (score == ADC_SCORE_CENTROID) {
@@ -508,6 +551,7 @@ int32_t adacluster_select(const adc_shape* shape, int32_t Cq, int32_t Ck, const 
     else
         HIPCHK(launch_topk(p, Cq, Ck, S, k_sizes, n_clusters, full_attn, top_k, sel_mask, sel_keys,
                            ln_sizes, s));
+    if (sel_pairs) HIPCHK(launch_pairs(p, Cq, q_offsets, sel_keys, sel_pairs, s));
     return ADC_OK;
 }
 
@@ -520,6 +564,7 @@ struct AttnWs {
     int32_t* n_runs;
     AttnSched sched;
     uint16_t* planes[4];     // 16-bit operand planes: V fp16 (bf16 inputs); K hi, K lo, V hi, V lo (f32)
+    uint32_t* vmax;          // [BH] largest |v| per head (bf16 bits): the fp16 plane's scale
 };
 
 static void plan_attn(Carver& c, const adc_shape* shape, int32_t Cq, int32_t Ck, AttnWs& w) {
@@ -540,6 +585,7 @@ static void plan_attn(Carver& c, const adc_shape* shape, int32_t Cq, int32_t Ck,
     w.sched.xcd_ctr = c.take<int32_t>(8);
     const size_t elems = (size_t)shape->B * shape->H * shape->N * shape->D;
     for (int i = 0; i < 4; ++i) w.planes[i] = nullptr;
+    w.vmax = c.take<uint32_t>(BH);
     if (shape->dtype == ADC_BF16) {
         w.planes[2] = c.take<uint16_t>(elems);
     } else {
@@ -578,11 +624,11 @@ int32_t adacluster_sparse_attn(const adc_shape* shape, int32_t Cq, int32_t Ck, c
     plan_attn(c, shape, Cq, Ck, w);
     HIPCHK(launch_build_runs(p, Cq, Ck, k_offsets, sel_mask, w.run_cap, w.run_start, w.run_pos, w.n_runs, s));
     HIPCHK(launch_worklist(p, Cq, w.cap, q_offsets, w.run_pos, w.n_runs, w.run_cap, w.sched, s));
-    HIPCHK(launch_planes(p, k_perm, v_perm, w.planes[0], w.planes[1], w.planes[2], w.planes[3], s));
+    HIPCHK(launch_planes(p, k_perm, v_perm, w.planes[0], w.planes[1], w.planes[2], w.planes[3], w.vmax, s));
     const uint16_t* k0 = p.bf16 ? (const uint16_t*)k_perm : w.planes[0];
     HIPCHK(launch_attention(p, Cq, q, q_perm, q_offsets, k0, w.planes[1], w.planes[2], w.planes[3],
                             w.run_start, w.run_pos, w.n_runs, w.run_cap, w.sched, w.cap, scale,
-                            out, out_dtype == ADC_F32, lse, s));
+                            w.vmax, out, out_dtype == ADC_F32, lse, s));
     return ADC_OK;
 }
 
@@ -618,7 +664,7 @@ int32_t adacluster_assign(const adc_shape* shape, int32_t M, int32_t normalize, 
     CentView cv = make_view(const_cast<float*>(centroids), w, M, 0, M);
     RowSet all{nullptr, nullptr, nullptr};
     if (normalize) HIPCHK(launch_inv_norm(p, x, w.inv_norm, s));
-    HIPCHK(launch_finalize(p, cv, nullptr, 0, s));
+    HIPCHK(launch_finalize(p, cv, nullptr, nullptr, s));
     HIPCHK(launch_assign(p, x, all, normalize ? w.inv_norm : nullptr, normalize, cv, nullptr,
                          assign, flags_of(w), s));
     return ADC_OK;

@@ -6,11 +6,12 @@
 // are a list of contiguous key ranges ("runs"; slots with no members never
 // break a run). The queries of a q-cluster are read through its permutation.
 //
-// Kernel. A work item is (head, q-cluster, chunk of 64 query rows); four waves
-// own 16 rows each. Key/value tiles of 64 rows are staged in LDS (K row-major,
-// V transposed) and shared by the waves. Scores are computed as
-// S^T = K Q^T with 16x16x32 bf16 MFMAs so that a lane owns one query column,
-// the output as O^T += V^T P^T reusing the score registers as the B operand.
+// Kernel. A work item is (head, q-cluster, chunk of 128 query rows); eight
+// waves own 16 rows each. Key/value tiles of 64 rows are copied into LDS
+// (both row-major, 16-byte chunks swizzled) and shared by the waves. Scores
+// are computed as S^T = K Q^T with 16x16x32 MFMAs so that a lane owns one
+// query column, the output as O^T += V^T P^T with the probabilities of the
+// score registers as the B operand and V^T read by transposing LDS loads.
 #include <math.h>
 #include <algorithm>
 #include <type_traits>
@@ -301,20 +302,56 @@ hipError_t launch_worklist(const Prob& p, int Cq, int cap, const int32_t* q_offs
 
 // ------------------------------------------------------------------ operand planes
 // The attention kernel reads 16-bit operand planes. bf16 inputs: K' is used as
-// it is and V' is converted once to fp16 here (the P.V product runs in fp16;
-// the conversion is exact for |v| in the fp16 normal range). f32 inputs: K' and
-// V' are split into bf16 hi + lo planes (x = hi + lo to 2^-16 relative).
-__global__ __launch_bounds__(256) void planes_f16_kernel(const u16* __restrict__ x, int64_t n8,
+// it is and V' is converted once to fp16 here (the P.V product runs in fp16),
+// scaled per head by a power of two 2^e chosen from the head's largest |v|
+// so that it lands in [2^14, 2^15): no finite bf16 value overflows fp16, and
+// every value within 2^-28 of the largest keeps all its bits (smaller ones are
+// rounded to the fp16 subnormal grid, an absolute error below 2^-25 of the
+// largest |v|). The output is multiplied back by 2^-e, which is exact. f32
+// inputs: K' and V' are split into bf16 hi + lo planes (x = hi + lo to 2^-16
+// relative), which keep the f32 range.
+
+// Exponent e of the head's fp16 scale from its largest |v| (bf16 magnitude
+// bits; 0 for an all-zero head), kept where 2^e and 2^-e are normal floats.
+__device__ __forceinline__ int v_scale_exp(uint32_t vmax_bits) {
+    if (vmax_bits == 0) return 0;
+    const int E = vmax_bits >= 0x80u ? (int)(vmax_bits >> 7) - 127 : -127;  // floor(log2 |v|max)
+    return min(126, max(-126, 14 - E));
+}
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
+
+// Largest bf16 magnitude (as its bit pattern, which orders finite values) per head.
+__global__ __launch_bounds__(256) void vmax_kernel(const u16* __restrict__ x, int64_t per_head8,
+                                                   uint32_t* __restrict__ vmax) {
+    const int bh = blockIdx.y;
+    uint32_t m = 0;
+    const u16* xh = x + (int64_t)bh * per_head8 * 8;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < per_head8; i += (int64_t)gridDim.x * 256) {
+        const uint4 r = *reinterpret_cast<const uint4*>(xh + i * 8);
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m = max(m, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    if ((threadIdx.x & 63) == 0) atomicMax(&vmax[bh], m);
+}
+
+__global__ __launch_bounds__(256) void planes_f16_kernel(const u16* __restrict__ x, int64_t per_head8,
+                                                         const uint32_t* __restrict__ vmax,
                                                          u16* __restrict__ out) {
+    const int bh = blockIdx.y;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n8) return;
-    const uint4 r = *reinterpret_cast<const uint4*>(x + i * 8);
+    if (i >= per_head8) return;
+    const float sc = pow2f(v_scale_exp(vmax[bh]));
+    const int64_t o = ((int64_t)bh * per_head8 + i) * 8;
+    const uint4 r = *reinterpret_cast<const uint4*>(x + o);
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-    uint32_t o[4];
+    uint32_t h[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-        o[k] = pack_h2(__uint_as_float(w[k] << 16), __uint_as_float(w[k] & 0xFFFF0000u));
-    *reinterpret_cast<uint4*>(out + i * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+        h[k] = pack_h2(__uint_as_float(w[k] << 16) * sc, __uint_as_float(w[k] & 0xFFFF0000u) * sc);
+    *reinterpret_cast<uint4*>(out + o) = make_uint4(h[0], h[1], h[2], h[3]);
 }
 
 __global__ __launch_bounds__(256) void planes_split_kernel(const float* __restrict__ x, int64_t n8,
@@ -336,13 +373,19 @@ __global__ __launch_bounds__(256) void planes_split_kernel(const float* __restri
 }
 
 hipError_t launch_planes(const Prob& p, const void* k, const void* v, u16* k_hi, u16* k_lo,
-                         u16* v_hi, u16* v_lo, hipStream_t s) {
+                         u16* v_hi, u16* v_lo, uint32_t* vmax, hipStream_t s) {
     const int64_t n8 = (int64_t)p.BH * p.N * p.D / 8;
     if (n8 <= 0) return hipSuccess;
-    const dim3 grid((unsigned)((n8 + 255) / 256));
     if (p.bf16) {
-        hipLaunchKernelGGL(planes_f16_kernel, grid, dim3(256), 0, s, (const u16*)v, n8, v_hi);
+        const int64_t ph8 = (int64_t)p.N * p.D / 8;
+        hipError_t e = fill_i32((int32_t*)vmax, p.BH, 0, s);
+        if (e != hipSuccess) return e;
+        const unsigned gx = (unsigned)std::min<int64_t>((ph8 + 255) / 256, 64);
+        hipLaunchKernelGGL(vmax_kernel, dim3(gx, p.BH), dim3(256), 0, s, (const u16*)v, ph8, vmax);
+        hipLaunchKernelGGL(planes_f16_kernel, dim3((unsigned)((ph8 + 255) / 256), p.BH), dim3(256), 0, s,
+                           (const u16*)v, ph8, (const uint32_t*)vmax, v_hi);
     } else {
+        const dim3 grid((unsigned)((n8 + 255) / 256));
         hipLaunchKernelGGL(planes_split_kernel, grid, dim3(256), 0, s, (const float*)k, n8, k_hi, k_lo);
         hipLaunchKernelGGL(planes_split_kernel, grid, dim3(256), 0, s, (const float*)v, n8, v_hi, v_lo);
     }
@@ -559,7 +602,7 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
                  int run_cap, const int32_t* __restrict__ items,
                  const int32_t* __restrict__ head_pos, const int32_t* __restrict__ xcd_start,
                  int32_t* __restrict__ xcd_ctr, int BH, int cap, float sl2,
-                 TO* __restrict__ O, float* __restrict__ lse) {
+                 const uint32_t* __restrict__ vmax, TO* __restrict__ O, float* __restrict__ lse) {
     constexpr int NT = 512;
     static_assert((NT / 64) * 16 == ATTN_ROWS, "eight waves of 16 rows cover a work item");
     constexpr bool PREC = sizeof(T) == 4;
@@ -682,11 +725,12 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
         for (int t = 0; t < NB; ++t) lookup(t);
     }
     __syncthreads();
+    // tiles 0 .. NB - 2 here; step t issues tile t + NB - 1
     tile_copy<D, NP, NT>(buf(std::integral_constant<int, 0>{}), w, l, krow[0], Kh0, Kh1, Vh0, Vh1);
-    if constexpr (NB > 2) {
+    if constexpr (NB > 2)
         tile_copy<D, NP, NT>(buf(std::integral_constant<int, 1>{}), w, l, krow[1], Kh0, Kh1, Vh0, Vh1);
+    if constexpr (NB > 3)
         tile_copy<D, NP, NT>(buf(std::integral_constant<int, 2>{}), w, l, krow[2], Kh0, Kh1, Vh0, Vh1);
-    }
 
     // Scores, softmax and P.V of the tile in buffer tb (first position p0).
     auto compute = [&](const unsigned char* tb, int p0, bool first) __attribute__((always_inline)) {
@@ -776,7 +820,9 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
 
     if (qok) {
         const float l_tot = o[DB][0];  // every row of the ones block holds the sum
-        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        // the fp16 V plane of a bf16 head carries the factor 2^e: undo it here
+        const float vinv = PREC ? 1.0f : pow2f(-v_scale_exp(vmax[bh]));
+        const float inv = l_tot > 0.0f ? vinv / l_tot : 0.0f;
         TO* orow = O + ((int64_t)bh * N + qtok) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -814,7 +860,7 @@ static void launch_attn_t(const Prob& p, int Cq, const void* q, const int32_t* q
                           const int32_t* q_offsets, const u16* k0, const u16* k1, const u16* v0,
                           const u16* v1, const int32_t* run_start, const int32_t* run_pos,
                           const int32_t* n_runs, int run_cap, const AttnSched& sc, int cap,
-                          float sl2, void* out, float* lse, hipStream_t s) {
+                          float sl2, const uint32_t* vmax, void* out, float* lse, hipStream_t s) {
     // waves per SIMD: three workgroups per CU for bf16 D = 64 (80 registers,
     // three 16 KB tile buffers), two for bf16 D = 128 and f32 D = 64 (at most
     // 128 registers, two 32 KB buffers), one for f32 D = 128 (64 KB tiles)
@@ -828,27 +874,27 @@ static void launch_attn_t(const Prob& p, int Cq, const void* q, const int32_t* q
     const dim3 grid((unsigned)(((cu_count() * per_cu) + 7) / 8 * 8));
     hipLaunchKernelGGL(k, grid, dim3(512), 0, s, p.N, Cq, (const T*)q, q_perm, q_offsets, k0, k1,
                        v0, v1, run_start, run_pos, n_runs, run_cap, sc.items, sc.head_pos,
-                       sc.xcd_start, sc.xcd_ctr, p.BH, cap, sl2, (TO*)out, lse);
+                       sc.xcd_start, sc.xcd_ctr, p.BH, cap, sl2, vmax, (TO*)out, lse);
 }
 
 hipError_t launch_attention(const Prob& p, int Cq, const void* q, const int32_t* q_perm,
                             const int32_t* q_offsets, const u16* k0, const u16* k1,
                             const u16* v0, const u16* v1, const int32_t* run_start,
                             const int32_t* run_pos, const int32_t* n_runs, int run_cap,
-                            const AttnSched& sc, int cap, float scale, void* out, int out_f32,
-                            float* lse, hipStream_t s) {
+                            const AttnSched& sc, int cap, float scale, const uint32_t* vmax,
+                            void* out, int out_f32, float* lse, hipStream_t s) {
     if (cap <= 0) return hipSuccess;
     const float sl2 = scale * 1.4426950408889634f;
     if (p.bf16) {
         if (out_f32)
             launch_attn_t<u16, float>(p, Cq, q, q_perm, q_offsets, k0, k1, v0, v1, run_start,
-                                      run_pos, n_runs, run_cap, sc, cap, sl2, out, lse, s);
+                                      run_pos, n_runs, run_cap, sc, cap, sl2, vmax, out, lse, s);
         else
             launch_attn_t<u16, u16>(p, Cq, q, q_perm, q_offsets, k0, k1, v0, v1, run_start,
-                                    run_pos, n_runs, run_cap, sc, cap, sl2, out, lse, s);
+                                    run_pos, n_runs, run_cap, sc, cap, sl2, vmax, out, lse, s);
     } else {
         launch_attn_t<float, float>(p, Cq, q, q_perm, q_offsets, k0, k1, v0, v1, run_start,
-                                    run_pos, n_runs, run_cap, sc, cap, sl2, out, lse, s);
+                                    run_pos, n_runs, run_cap, sc, cap, sl2, vmax, out, lse, s);
     }
     return hipGetLastError();
 }

@@ -35,7 +35,9 @@ hipError_t launch_inv_norm(const Prob& p, const void* x, float* inv_norm, hipStr
 hipError_t launch_normalize(const Prob& p, const void* x, float* xhat, hipStream_t s);
 
 // Centroid-array view: cent/valid/c_hi/c_lo/cn2 hold `cap` slots per head;
-// kernels see slots [base, base + m).
+// kernels see slots [base, base + m). sums ([BH][cap][D]) and part
+// ([BH][ceil(N/64)][2][D]) hold the member sums of an update (see
+// launch_update_accum).
 struct CentView {
     float* cent;
     uint8_t* valid;
@@ -43,7 +45,8 @@ struct CentView {
     uint16_t* c_lo;
     float* cn2;
     float* sums;
-    int32_t* cnt;
+    float* part;
+    int nwav;   // waves of 64 sorted rows per head in part (ceil(N / 64))
     int cap;
     int base;
     int m;
@@ -70,10 +73,12 @@ hipError_t launch_init_kmeanspp(const Prob& p, const void* x, const float* xf, R
                                 CentView cv, uint64_t seed, uint32_t tensor, uint32_t stage,
                                 double* d2, uint8_t* chosen, hipStream_t s);
 // Centroid prep: split into bf16 hi/lo, squared norms (+inf where no centre).
-// With sums != NULL it first moves centres to sums/cnt (cnt > 0) and clears the sums;
-// then with drift != NULL also drift[slot] >= ||new - old|| (0 where no centre).
-// zero_a/b/c (may be null): per-head counters [BH] cleared on the way.
-hipError_t launch_finalize(const Prob& p, CentView cv, const uint8_t* active, int with_sums,
+// With soff != NULL (the offsets [BH][m + 1] of the rows sorted by label that
+// launch_update_accum walked) it first moves every slot with members to the
+// mean of its members' sums; then with drift != NULL also drift[slot] >=
+// ||new - old|| (0 where no centre). zero_a/b/c (may be null): per-head
+// counters [BH] cleared on the way.
+hipError_t launch_finalize(const Prob& p, CentView cv, const uint8_t* active, const int32_t* soff,
                            hipStream_t s, float* drift = nullptr, int32_t* zero_a = nullptr,
                            int32_t* zero_b = nullptr, int32_t* zero_c = nullptr);
 // Flag lists of the certified assignment (see kmeans.hip).
@@ -116,12 +121,28 @@ hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* i
 hipError_t launch_bound_filter(const Prob& p, RowSet rs, CentView cv, const int32_t* labels,
                                float* ub, float* lb, const float* drift, int32_t* rlist,
                                int32_t* rcount, hipStream_t s);
-// Centroid sums (f32 atomics) and member counts for the current labels.
-// order (may be null): a permutation of the rows [BH][N] to take them in
-// (rows in one run of equal labels share one atomic per dimension).
+// Member sums for the current labels, taken over the rows in `order` (the
+// stable sort of the rows by label, [BH][N]) with n rows per head (rs.nrows,
+// or N). Wave W sums the runs of equal labels among sorted rows
+// [64 W, 64 W + 64) in row order: a cluster whose rows all lie there is stored
+// to sums; the part of a longer cluster at the start of the range goes to
+// part[W][0], the part at the end to part[W][1], and finalize adds a long
+// cluster's parts in wave order. No atomics: the sums do not depend on
+// scheduling, so identical inputs give identical centres.
 hipError_t launch_update_accum(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
-                               const int32_t* labels, CentView cv, hipStream_t s,
-                               const int32_t* order = nullptr);
+                               const int32_t* labels, CentView cv, const int32_t* order,
+                               hipStream_t s);
+
+// Copy of the centres of view cv (slots [base, base + m) of every head with
+// active[bh] != 0, active may be null) into dst, same [BH][cap][D] layout.
+hipError_t launch_copy_slots(const Prob& p, CentView cv, const uint8_t* active, float* dst,
+                             hipStream_t s);
+// Record of one stage of Algorithm 1: stage_labels[bh][t][token] = base + the
+// stage label of each row of rs (labels by position), stage_base[bh][t] = base,
+// for heads running the stage.
+constexpr int TRACE_STAGES = 8;
+hipError_t launch_trace_stage(const Prob& p, RowSet rs, const int32_t* labels, int base, int t,
+                              int32_t* stage_labels, int32_t* stage_base, hipStream_t s);
 
 // ---------------------------------------------------------------- multi-stage state
 struct StageState {
@@ -159,15 +180,18 @@ hipError_t launch_compactness(const Prob& p, int M, const void* x_perm, const in
 
 // ---------------------------------------------------------------- layout (permute.hip)
 hipError_t launch_scan_offsets(const Prob& p, const int32_t* cnt, int M, int32_t* sizes_out,
-                               int32_t* offsets, hipStream_t s);
+                               int32_t* offsets, hipStream_t s, const uint8_t* active = nullptr);
 // Stable counting sort by label (M <= 8192) over segments of SORT_SEG rows:
 // sizes [BH][M], offsets [BH][M+1], perm [BH][N] out; seg_cnt
-// [BH][sort_segments(N)][M] and total [BH][M] are scratch.
+// [BH][sort_segments(N)][M] and total [BH][M] are scratch. With nrows (may be
+// null) only the first nrows[bh] rows of a head are sorted; heads with
+// active[bh] == 0 (active may be null) are skipped.
 constexpr int SORT_SEG = 4096;
 int sort_segments(int N);
 hipError_t launch_counting_sort(const Prob& p, const int32_t* labels, int M, int32_t* seg_cnt,
                                 int32_t* total, int32_t* sizes, int32_t* offsets, int32_t* perm,
-                                hipStream_t s);
+                                hipStream_t s, const int32_t* nrows = nullptr,
+                                const uint8_t* active = nullptr);
 // Per cluster: member means (of normalised rows when normalize), raw means,
 // per-dimension max/min and the permuted copies of x and v.
 hipError_t launch_gather_stats(const Prob& p, int M, const int32_t* offsets, const int32_t* perm,
@@ -186,6 +210,10 @@ hipError_t launch_topp(const Prob& p, int Cq, int Ck, const float* S, const int3
 hipError_t launch_topk(const Prob& p, int Cq, int Ck, const float* S, const int32_t* k_sizes,
                        const int32_t* n_clusters, const uint8_t* full, int top_k,
                        uint32_t* mask, int32_t* sel_keys, float* ln_sizes, hipStream_t s);
+
+// pairs[bh] = sum over q-clusters a of (q_offsets[a + 1] - q_offsets[a]) x sel_keys[a].
+hipError_t launch_pairs(const Prob& p, int Cq, const int32_t* q_offsets, const int32_t* sel_keys,
+                        int64_t* pairs, hipStream_t s);
 
 // ---------------------------------------------------------------- attention (attn.hip)
 hipError_t launch_build_runs(const Prob& p, int Cq, int Ck, const int32_t* k_offsets,
@@ -207,14 +235,17 @@ struct AttnSched {
 hipError_t launch_worklist(const Prob& p, int Cq, int cap, const int32_t* q_offsets,
                            const int32_t* run_pos, const int32_t* n_runs, int run_cap,
                            const AttnSched& sc, hipStream_t s);
+// Operand planes of the attention kernel. bf16: V' to fp16 scaled per head by
+// a power of two (vmax [BH] receives each head's largest |v| as bf16 bits);
+// f32: K' and V' split into bf16 hi/lo planes (vmax unused).
 hipError_t launch_planes(const Prob& p, const void* k, const void* v, uint16_t* k_hi, uint16_t* k_lo,
-                         uint16_t* v_hi, uint16_t* v_lo, hipStream_t s);
+                         uint16_t* v_hi, uint16_t* v_lo, uint32_t* vmax, hipStream_t s);
 hipError_t launch_attention(const Prob& p, int Cq, const void* q, const int32_t* q_perm,
                             const int32_t* q_offsets, const uint16_t* k0, const uint16_t* k1,
                             const uint16_t* v0, const uint16_t* v1, const int32_t* run_start,
                             const int32_t* run_pos, const int32_t* n_runs, int run_cap,
-                            const AttnSched& sc, int cap, float scale, void* out, int out_f32,
-                            float* lse, hipStream_t s);
+                            const AttnSched& sc, int cap, float scale, const uint32_t* vmax,
+                            void* out, int out_f32, float* lse, hipStream_t s);
 
 constexpr int ATTN_ROWS = 128;  // query rows per attention work item
 

@@ -398,12 +398,15 @@ hipError_t launch_init_kmeanspp(const Prob& p, const void* x, const float* xf, R
 }
 
 // ------------------------------------------------------------------ finalize / prep
-// One wave per slot: optional move to sums/cnt, then bf16 hi/lo split and the
-// squared norm (+inf where the slot holds no centre).
+// One wave per slot: optional move to the member mean, then bf16 hi/lo split
+// and the squared norm (+inf where the slot holds no centre). The members of
+// slot j are the sorted rows [soff[j], soff[j + 1]); their sum is in sums[j]
+// when one wave of the update covered them all, else it is the end part of
+// the first wave plus the start parts of the later ones, added in wave order.
 template <int D>
 __global__ __launch_bounds__(256) void finalize_kernel(CentView cv, const uint8_t* active,
-                                                       int with_sums, float* drift, int32_t* zero_a,
-                                                       int32_t* zero_b, int32_t* zero_c) {
+                                                       const int32_t* __restrict__ soff, float* drift,
+                                                       int32_t* zero_a, int32_t* zero_b, int32_t* zero_c) {
     const int bh = blockIdx.y;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int j = blockIdx.x * 4 + w;
@@ -419,22 +422,33 @@ __global__ __launch_bounds__(256) void finalize_kernel(CentView cv, const uint8_
     const int64_t slot = (int64_t)bh * cv.cap + cv.base + j;
     float* c = cv.cent + slot * D;
     constexpr int E = D / 64;
-    float cvv[E];
-    if (with_sums) {
-        int n = cv.cnt[slot];
+    if (soff) {
+        const int32_t* so = soff + (int64_t)bh * (cv.m + 1);
+        const int s0 = so[j], s1 = so[j + 1];
+        const int n = s1 - s0;
         double dd = 0.0;
+        if (n > 0) {
+            const int w1 = s0 >> 6, w2 = (s1 - 1) >> 6;
+            float acc[E];
+            if (w1 == w2) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            float* sp = cv.sums + slot * D + l + 64 * e;
-            if (n > 0) {
-                const float nv = *sp / (float)n;
+                for (int e = 0; e < E; ++e) acc[e] = cv.sums[slot * D + l + 64 * e];
+            } else {
+                const float* pb = cv.part + (int64_t)bh * cv.nwav * 2 * D;
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[e] = pb[((int64_t)w1 * 2 + 1) * D + l + 64 * e];
+                for (int ww = w1 + 1; ww <= w2; ++ww)
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[e] += pb[((int64_t)ww * 2) * D + l + 64 * e];
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float nv = acc[e] / (float)n;
                 const double df = (double)(nv - c[l + 64 * e]);
                 dd += df * df;
                 c[l + 64 * e] = nv;
             }
-            *sp = 0.0f;
         }
-        if (l == 0) cv.cnt[slot] = 0;
         if (drift) {
             // ||new - old|| from the f32 differences (each within 2^-24 of
             // itself), rounded up by a margin
@@ -446,7 +460,6 @@ __global__ __launch_bounds__(256) void finalize_kernel(CentView cv, const uint8_
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         float v = c[l + 64 * e];
-        cvv[e] = v;
         u16 h = f2bf_bits(v);
         u16 lo = f2bf_bits(v - bf_bits2f(h));
         cv.c_hi[slot * D + l + 64 * e] = h;
@@ -457,15 +470,15 @@ __global__ __launch_bounds__(256) void finalize_kernel(CentView cv, const uint8_
     if (l == 0) cv.cn2[slot] = cv.valid[slot] ? (float)ss : INFINITY;
 }
 
-hipError_t launch_finalize(const Prob& p, CentView cv, const uint8_t* active, int with_sums,
+hipError_t launch_finalize(const Prob& p, CentView cv, const uint8_t* active, const int32_t* soff,
                            hipStream_t s, float* drift, int32_t* zero_a, int32_t* zero_b,
                            int32_t* zero_c) {
     dim3 grid((unsigned)((cv.m + 3) / 4), (unsigned)p.BH);
     if (p.D == 64)
-        hipLaunchKernelGGL(finalize_kernel<64>, grid, dim3(256), 0, s, cv, active, with_sums, drift,
+        hipLaunchKernelGGL(finalize_kernel<64>, grid, dim3(256), 0, s, cv, active, soff, drift,
                            zero_a, zero_b, zero_c);
     else
-        hipLaunchKernelGGL(finalize_kernel<128>, grid, dim3(256), 0, s, cv, active, with_sums, drift,
+        hipLaunchKernelGGL(finalize_kernel<128>, grid, dim3(256), 0, s, cv, active, soff, drift,
                            zero_a, zero_b, zero_c);
     return hipGetLastError();
 }
@@ -1154,12 +1167,14 @@ hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* i
 }
 
 // ------------------------------------------------------------------ update
-// Each wave takes 64 consecutive rows: it stages them in LDS (RS rows at a
-// time) with coalesced 16-byte loads, all in flight at once, then walks them
-// with one lane per dimension, folding runs of equal labels in registers
-// before one atomic add per run and dimension. With `order` (a permutation of
-// the rows, e.g. sorted by an earlier assignment) the rows are taken in that
-// order, so runs of equal labels are long and few atomics remain.
+// Wave W takes the sorted rows [64 W, 64 W + 64): it stages them in LDS (RS
+// rows at a time) with coalesced 16-byte loads, all in flight at once, then
+// walks them with one lane per dimension, summing each run of equal labels in
+// row order. A run is a whole cluster unless it touches the start of the range
+// with the cluster begun in the wave before (its sum goes to part[W][0]) or
+// the end of the range with the cluster going on in the next wave
+// (part[W][1]); whole clusters are stored to sums. Every value has one
+// writer, so the sums do not depend on scheduling.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__ X, int N, RowSet rs,
                                                            const float* __restrict__ inv_norm,
@@ -1176,21 +1191,34 @@ __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__
     if (rs.active && !rs.active[bh]) return;
     const int n = rs.nrows ? rs.nrows[bh] : N;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int base = blockIdx.x * 256 + w * 64;
+    const int wv = blockIdx.x * 4 + w;  // W
+    const int base = wv * 64;
     if (base >= n) return;
+    const int32_t* ord = order + (int64_t)bh * N;
+    const int32_t* lab_h = labels + (int64_t)bh * N;
     const int r0 = base + l;
     const bool okr = r0 < n;
-    const int r = (okr && order) ? order[(int64_t)bh * N + r0] : r0;
-    const int lab_l = okr ? labels[(int64_t)bh * N + r] : -1;
+    const int r = okr ? ord[r0] : 0;
+    const int lab_l = okr ? lab_h[r] : -1;
     const int tok_l = okr ? (rs.rows ? rs.rows[(int64_t)bh * N + r] : r) : 0;
     const float s_l = (inv_norm && okr) ? inv_norm[(int64_t)bh * N + tok_l] : 1.0f;
     const int rows_here = min(64, n - base);
+    // labels of the sorted rows just before and just after the range
+    const int lab_prev = base > 0 ? lab_h[ord[base - 1]] : -1;
+    const int lab_next = base + 64 < n ? lab_h[ord[base + 64]] : -1;
     const int64_t cbase = (int64_t)bh * cv.cap + cv.base;
+    float* pw = cv.part + ((int64_t)bh * cv.nwav + wv) * 2 * D;
     T* xw = xs[w];
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-    int cur = -1, run = 0;
+    int cur = -1;
+    bool cur_lead = false;
+    auto flush = [&](bool trail) __attribute__((always_inline)) {
+        float* dst = cur_lead ? pw : (trail ? pw + D : cv.sums + (cbase + cur) * D);
+#pragma unroll
+        for (int e = 0; e < E; ++e) dst[l + 64 * e] = acc[e];
+    };
     for (int h0 = 0; h0 < rows_here; h0 += RS) {
         // chunk c of row q goes to lane (q % RPI) * CPR + c; rows past the end read row 0
 #pragma unroll
@@ -1211,34 +1239,25 @@ __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__
             const int lab = __builtin_amdgcn_readlane(lab_l, h0 + q);
             const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_l), h0 + q));
             if (lab != cur) {
-                if (cur >= 0) {
-#pragma unroll
-                    for (int e = 0; e < E; ++e) atomicAdd(&cv.sums[(cbase + cur) * D + l + 64 * e], acc[e]);
-                    if (l == 0) atomicAdd(&cv.cnt[cbase + cur], run);
-                }
+                if (cur >= 0) flush(false);
                 cur = lab;
-                run = 0;
+                cur_lead = h0 + q == 0 && lab == lab_prev;
 #pragma unroll
                 for (int e = 0; e < E; ++e) acc[e] = 0.0f;
             }
 #pragma unroll
             for (int e = 0; e < E; ++e) acc[e] += s * elem<T>::load(xw, q * LDX + l + 64 * e);
-            run++;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    if (cur >= 0) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) atomicAdd(&cv.sums[(cbase + cur) * D + l + 64 * e], acc[e]);
-        if (l == 0) atomicAdd(&cv.cnt[cbase + cur], run);
-    }
+    if (cur >= 0) flush(rows_here == 64 && cur == lab_next);
 }
 
 hipError_t launch_update_accum(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
-                               const int32_t* labels, CentView cv, hipStream_t s,
-                               const int32_t* order) {
+                               const int32_t* labels, CentView cv, const int32_t* order,
+                               hipStream_t s) {
     dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)p.BH);
     if (p.bf16) {
         if (p.D == 64)
@@ -1255,6 +1274,50 @@ hipError_t launch_update_accum(const Prob& p, const void* x, RowSet rs, const fl
             hipLaunchKernelGGL((update_accum_kernel<float, 128>), grid, dim3(256), 0, s,
                                (const float*)x, p.N, rs, inv_norm, labels, cv, order);
     }
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ stage records
+template <int D>
+__global__ __launch_bounds__(256) void copy_slots_kernel(CentView cv, const uint8_t* __restrict__ active,
+                                                         float* __restrict__ dst) {
+    const int bh = blockIdx.y;
+    if (active && !active[bh]) return;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)cv.m * D) return;
+    const int64_t o = ((int64_t)bh * cv.cap + cv.base) * D + i;
+    dst[o] = cv.cent[o];
+}
+
+hipError_t launch_copy_slots(const Prob& p, CentView cv, const uint8_t* active, float* dst,
+                             hipStream_t s) {
+    dim3 grid((unsigned)(((int64_t)cv.m * p.D + 255) / 256), (unsigned)p.BH);
+    if (p.D == 64)
+        hipLaunchKernelGGL(copy_slots_kernel<64>, grid, dim3(256), 0, s, cv, active, dst);
+    else
+        hipLaunchKernelGGL(copy_slots_kernel<128>, grid, dim3(256), 0, s, cv, active, dst);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void trace_stage_kernel(int N, RowSet rs, const int32_t* __restrict__ labels,
+                                                          int base, int t, int32_t* __restrict__ stage_labels,
+                                                          int32_t* __restrict__ stage_base) {
+    const int bh = blockIdx.y;
+    if (rs.active && !rs.active[bh]) return;
+    const int n = rs.nrows ? rs.nrows[bh] : N;
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r == 0 && stage_base) stage_base[bh * TRACE_STAGES + t] = base;
+    if (r >= n || !stage_labels) return;
+    const int64_t tok = rs.rows ? rs.rows[(int64_t)bh * N + r] : r;
+    stage_labels[((int64_t)bh * TRACE_STAGES + t) * N + tok] = base + labels[(int64_t)bh * N + r];
+}
+
+hipError_t launch_trace_stage(const Prob& p, RowSet rs, const int32_t* labels, int base, int t,
+                              int32_t* stage_labels, int32_t* stage_base, hipStream_t s) {
+    if (t >= TRACE_STAGES) return hipSuccess;
+    dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)p.BH);
+    hipLaunchKernelGGL(trace_stage_kernel, grid, dim3(256), 0, s, p.N, rs, labels, base, t, stage_labels,
+                       stage_base);
     return hipGetLastError();
 }
 

@@ -14,9 +14,11 @@ hipError_t fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 // Exclusive scan of the counts (one workgroup per head, M <= 8192).
 __global__ __launch_bounds__(1024) void scan_offsets_kernel(const int32_t* __restrict__ cnt, int M,
                                                             int32_t* __restrict__ sizes_out,
-                                                            int32_t* __restrict__ offsets) {
+                                                            int32_t* __restrict__ offsets,
+                                                            const uint8_t* __restrict__ active) {
     __shared__ int wsum[16];
     const int bh = blockIdx.x;
+    if (active && !active[bh]) return;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int per = (M + 1023) / 1024;
     const int beg = tid * per;
@@ -48,8 +50,9 @@ __global__ __launch_bounds__(1024) void scan_offsets_kernel(const int32_t* __res
 }
 
 hipError_t launch_scan_offsets(const Prob& p, const int32_t* cnt, int M, int32_t* sizes_out,
-                               int32_t* offsets, hipStream_t s) {
-    hipLaunchKernelGGL(scan_offsets_kernel, dim3(p.BH), dim3(1024), 0, s, cnt, M, sizes_out, offsets);
+                               int32_t* offsets, hipStream_t s, const uint8_t* active) {
+    hipLaunchKernelGGL(scan_offsets_kernel, dim3(p.BH), dim3(1024), 0, s, cnt, M, sizes_out, offsets,
+                       active);
     return hipGetLastError();
 }
 
@@ -62,12 +65,16 @@ hipError_t launch_scan_offsets(const Prob& p, const int32_t* cnt, int M, int32_t
 // rows of that label in the earlier segments. Same permutation, with
 // BH x segments workgroups instead of BH.
 __global__ __launch_bounds__(1024) void seg_hist_kernel(const int32_t* __restrict__ labels, int N, int M,
-                                                        int nseg, int32_t* __restrict__ seg_cnt) {
+                                                        int nseg, int32_t* __restrict__ seg_cnt,
+                                                        const int32_t* __restrict__ nrows,
+                                                        const uint8_t* __restrict__ active) {
     __shared__ int h[8192];
     const int sg = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+    if (active && !active[bh]) return;
+    const int n = nrows ? nrows[bh] : N;
     for (int j = tid; j < M; j += 1024) h[j] = 0;
     __syncthreads();
-    const int beg = sg * SORT_SEG, end = min(N, beg + SORT_SEG);
+    const int beg = sg * SORT_SEG, end = min(n, beg + SORT_SEG);
     const int32_t* lab = labels + (int64_t)bh * N;
     for (int i = beg + tid; i < end; i += 1024) {
         const int v = lab[i];
@@ -80,10 +87,11 @@ __global__ __launch_bounds__(1024) void seg_hist_kernel(const int32_t* __restric
 
 // In place: seg_cnt[s][j] <- rows of label j in segments before s; total[j].
 __global__ __launch_bounds__(256) void seg_scan_kernel(int M, int nseg, int32_t* __restrict__ seg_cnt,
-                                                       int32_t* __restrict__ total) {
+                                                       int32_t* __restrict__ total,
+                                                       const uint8_t* __restrict__ active) {
     const int bh = blockIdx.y;
     const int j = blockIdx.x * 256 + threadIdx.x;
-    if (j >= M) return;
+    if (j >= M || (active && !active[bh])) return;
     int32_t* c = seg_cnt + (int64_t)bh * nseg * M + j;
     int run = 0;
     for (int sg = 0; sg < nseg; ++sg) {
@@ -97,11 +105,16 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(int M, int nseg, int32_t*
 __global__ __launch_bounds__(1024) void seg_rank_kernel(const int32_t* __restrict__ labels, int N, int M,
                                                         int nseg, const int32_t* __restrict__ offsets,
                                                         const int32_t* __restrict__ seg_cnt,
-                                                        int32_t* __restrict__ perm) {
+                                                        int32_t* __restrict__ perm,
+                                                        const int32_t* __restrict__ nrows,
+                                                        const uint8_t* __restrict__ active) {
     __shared__ int running[8192];
     __shared__ int grp_lab[16][64], grp_size[16][64], grp_base[16][64];
     __shared__ int ngrp[16];
     const int sg = blockIdx.x, bh = blockIdx.y;
+    if (active && !active[bh]) return;
+    const int n = nrows ? nrows[bh] : N;
+    if (sg * SORT_SEG >= n) return;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int32_t* off = offsets + (int64_t)bh * (M + 1);
     const int32_t* before = seg_cnt + ((int64_t)bh * nseg + sg) * M;
@@ -111,7 +124,7 @@ __global__ __launch_bounds__(1024) void seg_rank_kernel(const int32_t* __restric
     const int32_t* lab_h = labels + (int64_t)bh * N;
     const uint64_t lt = (l == 0) ? 0ull : (~0ull >> (64 - l));
     __syncthreads();
-    const int beg = sg * SORT_SEG, end = min(N, beg + SORT_SEG);
+    const int beg = sg * SORT_SEG, end = min(n, beg + SORT_SEG);
     for (int base = beg; base < end; base += 1024) {
         const int i = base + tid;
         const int raw = i < end ? lab_h[i] : -1;
@@ -161,15 +174,17 @@ int sort_segments(int N) { return (N + SORT_SEG - 1) / SORT_SEG; }
 
 hipError_t launch_counting_sort(const Prob& p, const int32_t* labels, int M, int32_t* seg_cnt,
                                 int32_t* total, int32_t* sizes, int32_t* offsets, int32_t* perm,
-                                hipStream_t s) {
+                                hipStream_t s, const int32_t* nrows, const uint8_t* active) {
     const int nseg = sort_segments(p.N);
-    hipLaunchKernelGGL(seg_hist_kernel, dim3(nseg, p.BH), dim3(1024), 0, s, labels, p.N, M, nseg, seg_cnt);
-    hipLaunchKernelGGL(seg_scan_kernel, dim3((M + 255) / 256, p.BH), dim3(256), 0, s, M, nseg, seg_cnt, total);
+    hipLaunchKernelGGL(seg_hist_kernel, dim3(nseg, p.BH), dim3(1024), 0, s, labels, p.N, M, nseg, seg_cnt,
+                       nrows, active);
+    hipLaunchKernelGGL(seg_scan_kernel, dim3((M + 255) / 256, p.BH), dim3(256), 0, s, M, nseg, seg_cnt, total,
+                       active);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if ((e = launch_scan_offsets(p, total, M, sizes, offsets, s)) != hipSuccess) return e;
+    if ((e = launch_scan_offsets(p, total, M, sizes, offsets, s, active)) != hipSuccess) return e;
     hipLaunchKernelGGL(seg_rank_kernel, dim3(nseg, p.BH), dim3(1024), 0, s, labels, p.N, M, nseg, offsets,
-                       seg_cnt, perm);
+                       seg_cnt, perm, nrows, active);
     return hipGetLastError();
 }
 

@@ -551,4 +551,31 @@ hipError_t launch_topk(const Prob& p, int Cq, int Ck, const float* S, const int3
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ pairs
+// Query-key pairs the attention will compute per head: sum over q-clusters of
+// (members) x (selected keys), in int64, in a fixed order (per-thread strided
+// sums, a wave butterfly, then the four waves in order).
+__global__ __launch_bounds__(256) void pairs_kernel(int Cq, const int32_t* __restrict__ q_offsets,
+                                                    const int32_t* __restrict__ sel_keys,
+                                                    int64_t* __restrict__ pairs) {
+    __shared__ long long part[4];
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int32_t* qo = q_offsets + (int64_t)bh * (Cq + 1);
+    const int32_t* sk = sel_keys + (int64_t)bh * Cq;
+    long long acc = 0;
+    for (int a = tid; a < Cq; a += 256) acc += (long long)(qo[a + 1] - qo[a]) * (long long)sk[a];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+    if (l == 0) part[w] = acc;
+    __syncthreads();
+    if (tid == 0) pairs[bh] = (int64_t)(part[0] + part[1] + part[2] + part[3]);
+}
+
+hipError_t launch_pairs(const Prob& p, int Cq, const int32_t* q_offsets, const int32_t* sel_keys,
+                        int64_t* pairs, hipStream_t s) {
+    hipLaunchKernelGGL(pairs_kernel, dim3((unsigned)p.BH), dim3(256), 0, s, Cq, q_offsets, sel_keys, pairs);
+    return hipGetLastError();
+}
+
 }  // namespace adc

@@ -23,6 +23,12 @@
  *     stream). All work is enqueued on it; no call synchronises the host or
  *     copies device data to the host. Outputs are valid when the stream
  *     reaches the end of the call.
+ *   - Workspace: any device address; the library aligns its pieces itself
+ *     (the *_workspace() sizes include the slack for that).
+ *   - Determinism: identical inputs, parameters and shapes give bitwise
+ *     identical outputs, on any stream and at any concurrency: every sum is
+ *     formed in a fixed order (no floating-point atomics), and work queues
+ *     only decide which workgroup computes a result, never how.
  *   - Errors: arguments are validated before the first launch; on ADC_EINVAL,
  *     ADC_ESHAPE, ADC_EDTYPE, ADC_EWORKSPACE or ADC_EUNSUPPORTED nothing is
  *     launched and no output is written. ADC_EHIP reports a failed launch; the
@@ -42,7 +48,7 @@
 extern "C" {
 #endif
 
-#define ADACLUSTER_ABI_VERSION 2
+#define ADACLUSTER_ABI_VERSION 3
 
 typedef enum {
     ADC_OK = 0,
@@ -180,6 +186,46 @@ int32_t adacluster_cluster_k(const adc_shape* shape, const adc_k_params* params,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Key clustering with a record of Algorithm 1's decisions (STAGED mode only),
+ * so that each one can be recomputed from the values it was taken on: the
+ * labels of every stage's last Lloyd assignment from the centres that
+ * assignment measured against, the threshold test of each key (step 13,
+ * d(k_i, c(k_i)) < tau) from the stage centres, and the final assignment
+ * (step 20) from the slot centres before their refresh to member means.
+ * Arguments and results are those of adacluster_cluster_k (init may not be
+ * CALLER); every pointer of the record is a device pointer and may be NULL
+ * (that part is then not kept). Stages past ADC_TRACE_STAGES are not
+ * recorded. Returns ADC_EUNSUPPORTED unless adaptive == ADC_K_STAGED.
+ *   stage_centroids [B,H,Nmax,D] f32  each slot's centre as its stage left it
+ *                                     (the last update of the stage's k-means;
+ *                                     0 where no stage filled the slot)
+ *   last_centroids  [B,H,Nmax,D] f32  the centres each stage's last
+ *                                     assignment measured against (0 likewise)
+ *   slot_valid      [B,H,Nmax] uint8  1 where the slot holds a centre
+ *   stage_labels    [B,H,ADC_TRACE_STAGES,N] int32: the slot stage t gave each
+ *                                     key it clustered (the keys of U at stage
+ *                                     t), -1 for the other keys
+ *   stage_base      [B,H,ADC_TRACE_STAGES] int32: first slot of stage t, -1
+ *                                     for stages the head did not run
+ */
+#define ADC_TRACE_STAGES 8
+typedef struct {
+    float* stage_centroids;
+    float* last_centroids;
+    uint8_t* slot_valid;
+    int32_t* stage_labels;
+    int32_t* stage_base;
+} adc_k_trace;
+
+int32_t adacluster_cluster_k_trace(const adc_shape* shape, const adc_k_params* params,
+                                   const void* k, const void* v, int32_t* n_clusters,
+                                   uint8_t* full_attn, float* tau, int32_t* assign,
+                                   float* centroids, int32_t* sizes, void* kmax, void* kmin,
+                                   int32_t* perm, int32_t* offsets, void* k_perm, void* v_perm,
+                                   int32_t* stage_sizes, const adc_k_trace* trace,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Critical-cluster selection (section 3.2.3 and Algorithm 3 steps 6-7).
  * For q-cluster a and slot b with members (b < n_clusters[b,h]):
  *   QUEST     S_ab = qrep_a+ . kmax_b + qrep_a- . kmin_b   (Eq. (2) == Eq. (1))
@@ -189,20 +235,25 @@ int32_t adacluster_cluster_k(const adc_shape* shape, const adc_k_params* params,
  * TOPK: the top_k largest S_ab (ties to the lower b).
  * Heads with full_attn = 1, and top_p >= 1, select every slot with members.
  *   qrep       [B,H,Cq,D] f32          kmax, kmin [B,H,Ck,D] dtype (QUEST)
+ *   q_offsets  [B,H,Cq+1] int32 (the query clustering's offsets; needed only
+ *              for sel_pairs, else may be NULL)
  *   centroids  [B,H,Ck,D] f32 (CENTROID; may be NULL for QUEST)
  *   k_sizes    [B,H,Ck] int32          n_clusters [B,H] int32   full_attn [B,H] uint8
  *   sel_mask   [B,H,Cq,ceil(Ck/32)] uint32 out: bit b of row a set = selected
  *   sel_keys   [B,H,Cq] int32 out: keys covered by the selected slots
+ *   sel_pairs  [B,H] int64 out (may be NULL): query-key pairs the attention
+ *              computes, sum over a of (members of a) x sel_keys[a]
  * Ck is the slot capacity (Nmax); scale is normally 1/sqrt(D).
  */
 size_t adacluster_select_workspace(const adc_shape* shape, int32_t Cq, int32_t Ck);
 int32_t adacluster_select(const adc_shape* shape, int32_t Cq, int32_t Ck,
-                          const float* qrep, const void* kmax, const void* kmin,
-                          const float* centroids, const int32_t* k_sizes,
+                          const float* qrep, const int32_t* q_offsets, const void* kmax,
+                          const void* kmin, const float* centroids, const int32_t* k_sizes,
                           const int32_t* n_clusters, const uint8_t* full_attn,
                           int32_t score, int32_t rule, float top_p, int32_t top_k,
                           float scale, uint32_t* sel_mask, int32_t* sel_keys,
-                          void* workspace, size_t workspace_bytes, void* stream);
+                          int64_t* sel_pairs, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* ------------------------------------------------------------------------
  * Sparse attention over the selected key clusters (Algorithm 3 steps 8-9):
@@ -218,10 +269,16 @@ int32_t adacluster_select(const adc_shape* shape, int32_t Cq, int32_t Ck,
  *   out        [B,H,N,D] out, element type out_dtype (ADC_F32, or ADC_BF16 only
  *              when the inputs are bf16)
  *   lse        [B,H,N] f32 out (may be NULL)
- * Computation: bf16 matrix-core products with f32 accumulation and an online
- * softmax in f32. bf16 inputs are exact operands (the probabilities are
- * rounded to bf16 for the P.V product); f32 inputs are carried as bf16 hi + lo
- * pairs with three products per contraction, close to f32 accuracy.
+ * Computation: matrix-core products with f32 accumulation and an online
+ * softmax in f32. bf16 inputs: Q.K^T takes the bf16 values as they are (exact
+ * operands); for P.V the probabilities (each at most 2^8 after the running
+ * maximum) are rounded to fp16 (11-bit significand) and V to fp16 after a
+ * per-head power-of-two scaling that puts the head's largest |v| in
+ * [2^14, 2^15) (undone exactly on the output), so every finite bf16 V is in
+ * range and values down to 2^-28 of the largest keep all their bits; the
+ * result is accurate to about 2^-11 of the largest |v| of the head. f32
+ * inputs are carried as bf16 hi + lo pairs with three products per
+ * contraction, close to f32 accuracy. Inputs must be finite.
  */
 size_t adacluster_sparse_attn_workspace(const adc_shape* shape, int32_t Cq, int32_t Ck);
 int32_t adacluster_sparse_attn(const adc_shape* shape, int32_t Cq, int32_t Ck,

@@ -1,6 +1,7 @@
 """Helpers shared by the GPU tests: moving seeded inputs to the device and the
 parity rules (near-tie exemptions) used to compare with the oracle."""
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -83,3 +84,93 @@ def topk_ok(gpu_bits, ora_bits, S, tol=NEAR_TIE):
 
 def small_workload(name, **kw):
     return synth.scaled(synth.WORKLOADS[name], **kw)
+
+
+def check_alg1_head(kf, K, tr, h, m0, nmax, tau_mult=1.5, tag=""):
+    """Every decision of Algorithm 1 (AdaCluster section 3.2.2, tau from section
+    4.1) for head h of a traced STAGED key clustering, recomputed from the
+    values it was taken on:
+      - each stage's labels are the exact assignment (oracle.assign) of the
+        keys of U to the centres that stage's last assignment measured
+        against, except near ties (two best distances within 1e-4 relative);
+      - each stage's centres are the member means of those labels (rel-L2
+        1e-5 per centre; a slot with no member keeps its centre);
+      - tau = tau_mult x the mean distance of all keys to their stage-0 centre
+        (rel 1e-5);
+      - U after stage t is {i in U_t : d_i >= tau} except keys with
+        |d_i - tau| <= 1e-4 tau, and the loop runs, stops and sets F exactly as
+        those sets say (counts and F exact when no such key exists);
+      - the final labels are the exact assignment to every slot holding a
+        centre, before the refresh, except near ties.
+    kf: the head's keys as float32 [N, D]; K / tr: host copies of the
+    cluster_k outputs and of its record. Returns a short summary dict."""
+    N = kf.shape[0]
+    kd = kf.astype(np.float64)
+    base = tr["stage_base"][0, h]
+    labs = tr["stage_labels"][0, h]
+    last = tr["last_centroids"][0, h]
+    cent = tr["stage_centroids"][0, h]
+    valid = tr["slot_valid"][0, h].astype(bool)
+    st = K["stage_sizes"][0, h]
+    tau = float(K["tau"][0, h])
+    n_stages = int((base >= 0).sum())
+    assert n_stages >= 1 and np.all(base[:n_stages] >= 0) and np.all(base[n_stages:] == -1)
+    U = np.arange(N)
+    slots = 0
+    near_total = 0
+    summary = dict(stages=n_stages, U=[], near_tau=0, label_ties=0)
+    for t in range(n_stages):
+        mt = m0 if t == 0 else m0 << (t - 1)
+        mt = min(mt, nmax - slots)
+        assert base[t] == slots, (tag, h, t)
+        Ut = np.flatnonzero(labs[t] >= 0)
+        assert np.array_equal(Ut, U), (tag, h, t, "U differs from the previous stage's decision")
+        assert st[t] == len(Ut)
+        summary["U"].append(len(Ut))
+        lab = labs[t][Ut] - slots
+        assert lab.min() >= 0 and lab.max() < mt
+        sl = slice(slots, slots + mt)
+        # labels: exact assignment to the centres the last round measured against
+        lo, b1, b2 = oracle.assign(kf[Ut], last[sl], valid[sl])
+        bad, diff, ties = labels_match(lab, lo, b1, b2)
+        summary["label_ties"] += diff
+        assert bad == 0, (tag, h, t, "stage labels", bad)
+        # centres: member means (f32 sums in a fixed order vs the f64 mean)
+        ref, sizes = oracle.update(kf[Ut], lab, last[sl])
+        for j in np.flatnonzero(sizes):
+            assert rel_l2(cent[slots + j], ref[j]) <= 1e-5, (tag, h, t, j)
+        empty = np.flatnonzero(sizes == 0)
+        assert np.array_equal(cent[slots + empty], last[sl][empty])
+        # the threshold test of every key of U against its stage centre
+        d = np.sqrt(((kd[Ut] - cent[slots + lab].astype(np.float64)) ** 2).sum(1))
+        if t == 0:
+            assert tau == pytest.approx(tau_mult * d.mean(), rel=1e-5), (tag, h)
+        keep = d >= tau
+        near = np.abs(d - tau) <= 1e-4 * tau
+        near_total += int(near.sum())
+        slots += mt
+        if t + 1 < n_stages:
+            Un = np.flatnonzero(labs[t + 1] >= 0)
+            assert np.all(np.isin(Un, Ut)), (tag, h, t, "a removed key came back")
+            inn = np.isin(Ut, Un)
+            assert np.array_equal(inn[~near], keep[~near]), (tag, h, t, "threshold test")
+            assert len(Un) > 0 and slots < nmax  # the loop went on
+            U = Un
+        else:
+            left = int(st[t + 1]) if t + 1 < len(st) else None
+            if left is not None:
+                assert abs(left - int(keep.sum())) <= int(near.sum()), (tag, h, "U after the last stage")
+            # the loop ended: U empty, or Nmax slots with U left (F = 1)
+            full = int(K["full"][0, h])
+            if near.sum() == 0:
+                assert full == int(keep.sum() > 0 and slots >= nmax), (tag, h, "F")
+                assert keep.sum() == 0 or slots >= nmax
+            assert full in (0, 1)
+    summary["near_tau"] = near_total
+    assert int(K["n_clusters"][0, h]) == slots
+    # final assignment over every slot holding a centre, before the refresh
+    lo, b1, b2 = oracle.assign(kf, cent[:slots], valid[:slots])
+    bad, diff, ties = labels_match(K["assign"][0, h], lo, b1, b2)
+    summary["final_ties"] = diff
+    assert bad == 0, (tag, h, "final labels", bad)
+    return summary

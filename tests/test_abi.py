@@ -10,7 +10,7 @@ import clustered_sparse_attention_cosine_amd as adc
 EXPECTED = {
     "adacluster_abi_version", "adacluster_last_error",
     "adacluster_cluster_q_workspace", "adacluster_cluster_q",
-    "adacluster_cluster_k_workspace", "adacluster_cluster_k",
+    "adacluster_cluster_k_workspace", "adacluster_cluster_k", "adacluster_cluster_k_trace",
     "adacluster_select_workspace", "adacluster_select",
     "adacluster_sparse_attn_workspace", "adacluster_sparse_attn",
     "adacluster_assign_workspace", "adacluster_assign",
@@ -30,7 +30,7 @@ def test_library_exports_every_header_symbol():
 
 
 def test_abi_version():
-    assert adc.lib().adacluster_abi_version() == 2
+    assert adc.lib().adacluster_abi_version() == 3
 
 
 def _shape(B=1, H=2, N=1000, D=64, dt=adc.ADC_BF16):
@@ -123,9 +123,10 @@ def test_select_and_attn_parameter_checks():
     sh = _shape()
     P = ctypes.c_void_p(16)
 
-    def sel(score=0, rule=0, top_p=0.9, top_k=4, scale=0.125):
-        return L.adacluster_select(ctypes.byref(sh), 32, 64, P, P, P, P, P, P, P, score, rule,
-                                   top_p, top_k, scale, P, P, P, 1 << 40, None)
+    def sel(score=0, rule=0, top_p=0.9, top_k=4, scale=0.125, q_off=P, pairs=P):
+        return L.adacluster_select(ctypes.byref(sh), 32, 64, P, q_off, P, P, P, P, P, P, score, rule,
+                                   top_p, top_k, scale, P, P, pairs, P, 1 << 40, None)
+    assert sel(q_off=None) == -1          # sel_pairs needs q_offsets
     assert sel(top_p=0.0) == -1
     assert sel(top_p=1.5) == -1
     assert sel(rule=1, top_k=0) == -1
@@ -141,6 +142,20 @@ def test_select_and_attn_parameter_checks():
     assert attn(ws=1) == -4
     assert attn(odt=5) == -3
     assert attn(odt=adc.ADC_BF16, shape=_shape(dt=adc.ADC_F32)) == -3
+
+
+def test_cluster_k_trace_checks():
+    L = adc.lib()
+    sh = _shape()
+    P = ctypes.c_void_p(16)
+    rec = adc.KTrace(16, 16, 16, 16, 16)
+
+    def call(kp, trace=True):
+        return L.adacluster_cluster_k_trace(ctypes.byref(sh), ctypes.byref(kp), *([P] * 15),
+                                            ctypes.byref(rec) if trace else None, P, 1 << 40, None)
+    assert call(adc.KParams(16, 64, 5, 1.5, 1, 1, 0), trace=False) == -1  # no record
+    assert call(adc.KParams(16, 64, 5, 1.5, 0, 1, 0)) == -6               # FIXED has no stages
+    assert call(adc.KParams(64, 32, 5, 1.5, 1, 1, 0)) == -2               # Nmax < m0
 
 
 def test_binding_refuses_cpu_tensors():

@@ -11,7 +11,7 @@ import torch
 import clustered_sparse_attention_cosine_amd as adc
 import oracle
 import synth
-from gpu_util import dev, host, rel_l2, selection_ok
+from gpu_util import check_alg1_head, dev, host, rel_l2, selection_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -35,11 +35,31 @@ def layer():
     res = dict(w=w, g=g, Q={n: host(t) for n, t in Q.items() if torch.is_tensor(t)},
                K={n: host(t) for n, t in K.items() if torch.is_tensor(t) and n not in ("k_perm", "v_perm")},
                S={n: host(t) for n, t in S.items() if torch.is_tensor(t)}, out=host(out), lse=host(lse))
+    # the traced key clustering (the same kernels plus the stage record) gives
+    # the same bits as the plain call: outputs are reproducible run to run
+    Kt = adc.cluster_k(k, v, cfg.k_base, cfg.k_max, cfg.iters, cfg.tau_mult, cfg.adaptive, cfg.init,
+                       cfg.seed, trace=True)
+    torch.cuda.synchronize()
+    res["trace_same"] = all(torch.equal(t, Kt[n]) for n, t in K.items() if torch.is_tensor(t))
+    res["trace"] = {n: host(t) for n, t in Kt["trace"].items()}
+    del Kt
     # K', V' checked on device (exact gathers)
     perm = K["perm"].long()
     res["kperm_exact"] = bool(torch.equal(K["k_perm"], torch.gather(k, 2, perm[..., None].expand_as(k))))
     res["vperm_exact"] = bool(torch.equal(K["v_perm"], torch.gather(v, 2, perm[..., None].expand_as(v))))
     return res
+
+
+def test_alg1_every_decision_at_full_size(layer):
+    # Algorithm 1 on three heads of the headline layer, decision by decision
+    # (stage labels, stage centres, tau, the threshold test of every key, the
+    # loop's end and F, the final assignment) from the values each was taken on
+    w, g = layer["w"], layer["g"]
+    assert layer["trace_same"]
+    for h in HEADS:
+        kf = synth.as_f32(g["k"][0, h])
+        s = check_alg1_head(kf, layer["K"], layer["trace"], h, w.k_base, w.k_max, tag="cog76k")
+        print(f"cog76k head {h}: {s}")
 
 
 def test_attention_sampled_rows(layer):
