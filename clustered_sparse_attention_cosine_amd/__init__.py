@@ -79,6 +79,8 @@ _SIGS = {
     "adacluster_sparse_attn_workspace": (_SZ, [_VP, _I32, _I32]),
     "adacluster_sparse_attn": (_I32, [_VP, _I32, _I32] + [_VP] * 7
                                + [_F32, _VP, _I32, _VP, _VP, _SZ, _VP]),
+    "adacluster_sparse_attn_noalloc": (_I32, [_VP, _I32, _I32] + [_VP] * 7
+                                       + [_F32, _VP, _I32, _VP, _VP]),
     "adacluster_assign_workspace": (_SZ, [_VP, _I32]),
     "adacluster_assign": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "adacluster_permute_workspace": (_SZ, [_VP, _I32]),

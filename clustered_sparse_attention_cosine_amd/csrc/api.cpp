@@ -601,22 +601,33 @@ size_t adacluster_sparse_attn_workspace(const adc_shape* shape, int32_t Cq, int3
     return c.used + 256;
 }
 
-int32_t adacluster_sparse_attn(const adc_shape* shape, int32_t Cq, int32_t Ck, const void* q,
-                               const int32_t* q_perm, const int32_t* q_offsets, const void* k_perm,
-                               const void* v_perm, const int32_t* k_offsets,
-                               const uint32_t* sel_mask, float scale, void* out,
-                               int32_t out_dtype, float* lse, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+static int32_t sparse_attn_impl(const adc_shape* shape, int32_t Cq, int32_t Ck, const void* q,
+                                const int32_t* q_perm, const int32_t* q_offsets, const void* k_perm,
+                                const void* v_perm, const int32_t* k_offsets,
+                                const uint32_t* sel_mask, float scale, void* out, int32_t out_dtype,
+                                float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                                bool noalloc) {
     int32_t st = check_sel_dims(shape, Cq, Ck);
     if (st) return st;
     REQ(q); REQ(q_perm); REQ(q_offsets); REQ(k_perm); REQ(v_perm); REQ(k_offsets); REQ(sel_mask);
-    REQ(out); REQ(workspace);
+    REQ(out);
+    if (!noalloc) REQ(workspace);
     if (!(scale > 0.0f) || scale > 1e30f) return fail(ADC_EINVAL, "scale must be a finite value > 0");
     if (out_dtype != ADC_F32 && !(out_dtype == ADC_BF16 && shape->dtype == ADC_BF16))
         return fail(ADC_EDTYPE, "out_dtype must be ADC_F32, or ADC_BF16 with bf16 inputs");
     const size_t need = adacluster_sparse_attn_workspace(shape, Cq, Ck);
-    if (workspace_bytes < need)
+    if (noalloc) {
+        if (need > (size_t)ADC_NOALLOC_SCRATCH_BYTES)
+            return fail(ADC_EWORKSPACE,
+                        "this shape needs %zu bytes of scratch, above the %zu bytes the allocation-free "
+                        "entry point holds per device; call adacluster_sparse_attn with a workspace",
+                        need, (size_t)ADC_NOALLOC_SCRATCH_BYTES);
+        hipError_t e = noalloc_scratch(&workspace);
+        if (e != hipSuccess) return fail(ADC_EHIP, "scratch lookup: %s", hipGetErrorString(e));
+        workspace_bytes = ADC_NOALLOC_SCRATCH_BYTES;
+    } else if (workspace_bytes < need) {
         return fail(ADC_EWORKSPACE, "workspace of %zu bytes is below the %zu required", workspace_bytes, need);
+    }
     hipStream_t s = (hipStream_t)stream;
     Prob p = make_prob(shape);
     Carver c(workspace);
@@ -630,6 +641,26 @@ int32_t adacluster_sparse_attn(const adc_shape* shape, int32_t Cq, int32_t Ck, c
                             w.run_start, w.run_pos, w.n_runs, w.run_cap, w.sched, w.cap, scale,
                             w.vmax, out, out_dtype == ADC_F32, lse, s));
     return ADC_OK;
+}
+
+int32_t adacluster_sparse_attn(const adc_shape* shape, int32_t Cq, int32_t Ck, const void* q,
+                               const int32_t* q_perm, const int32_t* q_offsets, const void* k_perm,
+                               const void* v_perm, const int32_t* k_offsets,
+                               const uint32_t* sel_mask, float scale, void* out,
+                               int32_t out_dtype, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    return sparse_attn_impl(shape, Cq, Ck, q, q_perm, q_offsets, k_perm, v_perm, k_offsets, sel_mask,
+                            scale, out, out_dtype, lse, workspace, workspace_bytes, stream, false);
+}
+
+int32_t adacluster_sparse_attn_noalloc(const adc_shape* shape, int32_t Cq, int32_t Ck, const void* q,
+                                       const int32_t* q_perm, const int32_t* q_offsets,
+                                       const void* k_perm, const void* v_perm,
+                                       const int32_t* k_offsets, const uint32_t* sel_mask,
+                                       float scale, void* out, int32_t out_dtype, float* lse,
+                                       void* stream) {
+    return sparse_attn_impl(shape, Cq, Ck, q, q_perm, q_offsets, k_perm, v_perm, k_offsets, sel_mask,
+                            scale, out, out_dtype, lse, nullptr, 0, stream, true);
 }
 
 // ====================================================================== helpers

@@ -14,7 +14,9 @@
 // score registers as the B operand and V^T read by transposing LDS loads.
 #include <math.h>
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
+#include "../../include/adacluster.h"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -875,6 +877,34 @@ static void launch_attn_t(const Prob& p, int Cq, const void* q, const int32_t* q
     hipLaunchKernelGGL(k, grid, dim3(512), 0, s, p.N, Cq, (const T*)q, q_perm, q_offsets, k0, k1,
                        v0, v1, run_start, run_pos, n_runs, run_cap, sc.items, sc.head_pos,
                        sc.xcd_start, sc.xcd_ctr, p.BH, cap, sl2, vmax, (TO*)out, lse);
+}
+
+// ------------------------------------------------------------------ allocation-free scratch
+// Workspace of adacluster_sparse_attn_noalloc: one static array per device
+// (the code object's copy on each GPU), held until the process ends. Host code
+// never passes the array's name to a kernel: it takes the device address
+// hipGetSymbolAddress returns for the current device, once per device, and
+// hands that address on as the workspace.
+static __device__ __align__(256) unsigned char scratch[ADC_NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void** out) {
+    constexpr int MAX_DEVICES = 64;
+    static std::mutex mu;
+    static void* ptrs[MAX_DEVICES] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        ptrs[dev] = ptr;
+    }
+    *out = ptrs[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_attention(const Prob& p, int Cq, const void* q, const int32_t* q_perm,

@@ -249,4 +249,8 @@ hipError_t launch_attention(const Prob& p, int Cq, const void* q, const int32_t*
 
 constexpr int ATTN_ROWS = 128;  // query rows per attention work item
 
+// Device address of this device's static scratch array (ADC_NOALLOC_SCRATCH_BYTES
+// bytes), looked up once per device.
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace adc

@@ -289,6 +289,28 @@ int32_t adacluster_sparse_attn(const adc_shape* shape, int32_t Cq, int32_t Ck,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * adacluster_sparse_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments and results without the workspace, which is
+ * instead a static array of ADC_NOALLOC_SCRATCH_BYTES per device, held by
+ * every GPU the library runs on until the process ends. The call allocates
+ * nothing. A shape whose adacluster_sparse_attn_workspace() exceeds the array
+ * is rejected with ADC_EWORKSPACE before any launch (256 MiB holds, e.g.,
+ * H = 30, N = 17,776, D = 64, Cq = 256, Ck = 1024 and H = 12, N = 32,760,
+ * D = 128, Cq = 512, Ck = 2048). All calls on one device share its array:
+ * calls that overlap in time on one device (on different streams, or from
+ * different threads without ordering) race and give undefined results;
+ * calls ordered on one stream are safe, each starts from its own clears.
+ */
+#define ADC_NOALLOC_SCRATCH_BYTES (256u << 20)
+int32_t adacluster_sparse_attn_noalloc(const adc_shape* shape, int32_t Cq, int32_t Ck,
+                                       const void* q, const int32_t* q_perm,
+                                       const int32_t* q_offsets, const void* k_perm,
+                                       const void* v_perm, const int32_t* k_offsets,
+                                       const uint32_t* sel_mask, float scale, void* out,
+                                       int32_t out_dtype, float* lse, void* stream);
+
+/* ------------------------------------------------------------------------
  * Helper: one assignment step (argmin_j ||x_i - c_j||^2, ties to the lowest j)
  * of the k-means used by both cluster calls. normalize != 0 scales each row of
  * x to unit length first (the query side).

@@ -12,7 +12,7 @@ EXPECTED = {
     "adacluster_cluster_q_workspace", "adacluster_cluster_q",
     "adacluster_cluster_k_workspace", "adacluster_cluster_k", "adacluster_cluster_k_trace",
     "adacluster_select_workspace", "adacluster_select",
-    "adacluster_sparse_attn_workspace", "adacluster_sparse_attn",
+    "adacluster_sparse_attn_workspace", "adacluster_sparse_attn", "adacluster_sparse_attn_noalloc",
     "adacluster_assign_workspace", "adacluster_assign",
     "adacluster_permute_workspace", "adacluster_permute",
     "adacluster_compactness_workspace", "adacluster_compactness",
