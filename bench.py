@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "clustered-attn layer latency (ms) + dense-equiv TFLOP/s at 75.6K tokens"
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
 CALIB_BYTES = 512 << 20   # plain copy used to calibrate the memory counters
 
 
@@ -44,7 +45,7 @@ def timed_layer(torch, adc, q, k, v, cfg, stream, prev=None, select_kw=None, wan
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
     ev[0].record(stream)
     Q, K = adc.cluster_layer(q, k, v, cfg, prev=prev, events=ev[1:6])
-    S = adc.select(Q["qrep"], K, cfg.top_p, **(select_kw or {}))
+    S = adc.select(Q["qrep"], K, cfg.top_p, q_offsets=Q["offsets"], **(select_kw or {}))
     ev[6].record(stream)
     out, _ = adc.sparse_attn(q, Q["perm"], Q["offsets"], K["k_perm"], K["v_perm"], K["offsets"],
                              S["mask"], want_lse=want_lse)
@@ -74,6 +75,12 @@ def main():
                     help="skip the per-layer count / Nmax calibration on a synthetic layer stack")
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the warm-start steady-state steps (drifted inputs)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (a few layers each)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured GEMM and copy ceilings")
+    ap.add_argument("--cpu-heads", default=None,
+                    help="heads the oracle baseline runs: 'all', or a comma list (default: 4 spread heads)")
     ap.add_argument("--profile-steps", action="store_true",
                     help="only warmup + timed steps (for profiler runs)")
     args = ap.parse_args()
@@ -132,10 +139,8 @@ def main():
                    "p10": round(float(np.percentile(per_step, 10)), 4),
                    "p90": round(float(np.percentile(per_step, 90)), 4)}
 
-    # workload facts from the last step
-    sizes_q = Q["sizes"].double()
-    sel_keys = S["sel_keys"].double()
-    pairs = float((sizes_q * sel_keys).sum().item())
+    # workload facts from the last step (query-key pairs counted by adacluster_select)
+    pairs = float(S["pairs"].sum().item())
     density = pairs / (w.B * w.H * float(w.N) ** 2)
     slots = K["n_clusters"].flatten().tolist()
     full_heads = int(K["full"].sum().item())
@@ -183,6 +188,7 @@ def main():
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(w.name),
                      "algorithmic_flops": attn_flops},
+        "stage_rooflines": stage_rooflines(w.name),
     }
 
     if not args.no_dense:
@@ -200,12 +206,22 @@ def main():
     if not args.no_calib:
         result["calibration"] = calibration(torch, adc, synth, dev, stream)
 
-    if not args.no_spread:
+    if not args.no_spread or not args.no_configs or not args.no_ceilings:
         del q, k, v, Q, K, S, out
+    if not args.no_spread:
         result["spread"] = seed_spread(torch, adc, synth, w, cfg, dev, stream)
 
+    if not args.no_configs:
+        result["configs"] = other_configs(torch, adc, synth, dev, stream)
+
+    if not args.no_ceilings:
+        result["ceilings"] = ceilings(torch, dev, stream)
+
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(w, g, args.seed)
+        heads = args.cpu_heads
+        if heads not in (None, "all"):
+            heads = [int(x) for x in heads.split(",")]
+        result["cpu_baseline"] = cpu_baseline(w, g, args.seed, heads)
 
     print(json.dumps(result), flush=True)
 
@@ -245,7 +261,7 @@ def seed_spread(torch, adc, synth, w, cfg, dev, stream, seeds=(1, 2), steps=5):
             torch.cuda.synchronize()
             if i >= 2:
                 times.append(tm()["layer"])
-        pairs = float((Q["sizes"].double() * S["sel_keys"].double()).sum().item())
+        pairs = float(S["pairs"].sum().item())
         out.append({"seed": seed, "layer_ms_median": round(float(np.median(times)), 4),
                     "density": round(pairs / (w.B * w.H * float(w.N) ** 2), 5),
                     "full_heads": int(K["full"].sum().item())})
@@ -289,7 +305,7 @@ def warm_steady_state(torch, adc, synth, w, cfg, dev, stream, cold, q0, k0, v0, 
                 prev = dict(Q=Q, K=K)
                 torch.cuda.synchronize()
                 tm = tm()
-                pairs = float((Q["sizes"].double() * S["sel_keys"].double()).sum().item())
+                pairs = float(S["pairs"].sum().item())
                 C = adc.compactness(K["k_perm"], K["offsets"], K["centroids"])
                 rows.append(dict(t=[tm[n] for n in names], layer=tm["layer"],
                                  density=pairs / (w.B * w.H * float(w.N) ** 2),
@@ -350,7 +366,7 @@ def variants(torch, adc, w, cfg, q, k, v, stream, seed, mean_slots, steps=5):
             torch.cuda.synchronize()
             if i >= 2:
                 rows.append(tm())
-        pairs = float((Q["sizes"].double() * S["sel_keys"].double()).sum().item())
+        pairs = float(S["pairs"].sum().item())
         res[name] = {"layer_ms_median": round(float(np.median([r["layer"] for r in rows])), 4),
                      "stages_ms_median": {n: round(float(np.median([r[n] for r in rows])), 4)
                                           for n in ["cluster_q", "cluster_k", "select",
@@ -401,6 +417,50 @@ def calibration(torch, adc, synth, dev, stream, n_layers=8, top_frac=0.15, comp_
     return out
 
 
+def other_configs(torch, adc, synth, dev, stream, names=("tiny", "cog17k", "wan33k", "hun119k"),
+                  steps=5, warmup=2):
+    """The other workloads, a few cold layers each on seed 0: layer and stage
+    latency, density, the sparse attention's useful rate (4 D pairs / its
+    time) against the bf16 peak, and dense attention on the same inputs (this
+    library's kernel with everything selected; PyTorch SDPA, flash backend)."""
+    res = {}
+    for name in names:
+        w = synth.WORKLOADS[name]
+        t0 = time.time()
+        g = synth.generate(w, seed=0)
+        q, k, v = (torch.from_numpy(g[t].view(np.int16)).view(torch.bfloat16).to(dev)
+                   if g[t].dtype == np.uint16 else torch.from_numpy(g[t]).to(dev) for t in "qkv")
+        del g
+        cfg = adc.LayerConfig(q_clusters=w.q_clusters, k_base=w.k_base, k_max=w.k_max,
+                              top_p=w.top_p, iters=w.iters, init=w.init, adaptive=w.k_adaptive)
+        rows = []
+        for i in range(warmup + steps):
+            Q, K, S, _, tm = timed_layer(torch, adc, q, k, v, cfg, stream, want_lse=False)
+            torch.cuda.synchronize()
+            if i >= warmup:
+                rows.append(tm())
+        pairs = float(S["pairs"].sum().item())
+        stages = {n: round(float(np.median([r[n] for r in rows])), 4)
+                  for n in ["cluster_q", "cluster_k", "select", "sparse_attn"]}
+        lm = float(np.median([r["layer"] for r in rows]))
+        useful = 4.0 * w.D * pairs / (stages["sparse_attn"] * 1e-3) / 1e12
+        slots = K["n_clusters"].flatten().tolist()
+        entry = {"workload": f"B={w.B} H={w.H} N={w.N} D={w.D} {w.dtype}",
+                 "layer_ms_median": round(lm, 4),
+                 "dense_equiv_tflops": round(w.dense_flops() / (lm * 1e-3) / 1e12, 2),
+                 "stages_ms_median": stages, "density": round(pairs / (w.B * w.H * float(w.N) ** 2), 5),
+                 "full_heads": int(K["full"].sum().item()),
+                 "k_slots": {str(c): slots.count(c) for c in sorted(set(slots))},
+                 "sparse_attn_useful_tflops": round(useful, 2),
+                 "sparse_attn_frac_bf16_peak": round(useful / PEAK_BF16_TFLOPS, 4)}
+        del Q, K, S
+        entry["dense"] = dense_compare(torch, adc, q, k, v, w, dev, stream)
+        res[name] = entry
+        log(f"config {name} ({time.time() - t0:.1f}s): {entry}")
+        del q, k, v
+    return res
+
+
 def dense_compare(torch, adc, q, k, v, w, dev, stream):
     """Dense attention on the same GPU: this library's kernel with everything
     selected, and PyTorch's fused SDPA (flash backend only)."""
@@ -437,20 +497,52 @@ def dense_compare(torch, adc, q, k, v, w, dev, stream):
     return res
 
 
-def cpu_baseline(w, g, seed):
-    """The CPU oracle (as it stands) on head 0 of the same workload, all four
-    stages; scaled to the dense-equivalent unit as (4 N^2 D) / t_head."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(w, g, seed, heads=None):
+    """The CPU oracle (as it stands) on a sample of heads of the same workload,
+    all four stages, each timed on its own; scaled to the dense-equivalent unit
+    as (4 N^2 D) x heads / t. The sample keeps the default run to about 20 s of
+    host time; heads="all" times the whole layer. Threads: the host's share
+    for one GPU (at most 16, the worker budget of a one-GPU machine), OpenMP over
+    independent outputs."""
     import oracle
     import synth
-    threads = len(os.sched_getaffinity(0))
-    threads = min(threads, 16)
+    nproc = len(os.sched_getaffinity(0))
+    threads = min(nproc, 16)
     oracle.set_threads(threads)
-    heads = sorted({0, w.H // 3, (2 * w.H) // 3, w.H - 1})
+    if heads == "all":
+        heads = list(range(w.H))
+    elif heads is None:
+        heads = sorted({0, w.H // 3, (2 * w.H) // 3, w.H - 1})
+    scale = 1.0 / math.sqrt(w.D)
+    st = {"cluster_q": 0.0, "cluster_k": 0.0, "select": 0.0, "sparse_attn": 0.0}
     t0 = time.perf_counter()
     for h in heads:
         qh, kh, vh = (synth.as_f32(g[t][0, h]) for t in "qkv")
-        oracle.layer_head(qh, kh, vh, cq=w.q_clusters, m0=w.k_base, nmax=w.k_max, iters=w.iters,
-                          top_p=w.top_p, init=w.init, adaptive=w.k_adaptive, seed=seed, h=h)
+        ta = time.perf_counter()
+        Q = oracle.cluster_q(qh, w.q_clusters, w.iters, init=w.init, seed=seed, h=h)
+        tb = time.perf_counter()
+        K = oracle.cluster_k(kh, w.k_base, w.k_max if w.k_adaptive else w.k_base, w.iters,
+                             adaptive=w.k_adaptive, init=w.init, seed=seed, h=h)
+        tc = time.perf_counter()
+        ck = K["n_slots"]
+        S = oracle.quest_scores(Q["qrep"], K["kmax"][:ck], K["kmin"][:ck], K["sizes"][:ck])
+        sel = oracle.select_topp(S, K["sizes"][:ck], scale, w.top_p, full=bool(K["full"]))
+        td = time.perf_counter()
+        oracle.sparse_attn(qh, kh, vh, Q["lab"], K["lab"], w.q_clusters, ck, sel["mask"], scale)
+        te = time.perf_counter()
+        for n, dt in zip(st, (tb - ta, tc - tb, td - tc, te - td)):
+            st[n] += dt
         log(f"oracle head {h} done at {time.perf_counter() - t0:.1f}s")
     t = time.perf_counter() - t0
     flops = 4.0 * float(w.N) ** 2 * w.D * len(heads)
@@ -458,7 +550,72 @@ def cpu_baseline(w, g, seed):
             "cores": oracle.get_threads(), "kind": "oracle",
             "sample": f"heads {heads} of {w.H}, all four stages, N={w.N}: {t:.1f} s "
                       f"(layer estimate {t * w.H / len(heads):.0f} s)",
-            "seconds": round(t, 2)}
+            "seconds": round(t, 2), "layer_seconds_estimate": round(t * w.H / len(heads), 1),
+            "stage_seconds": {n: round(v, 2) for n, v in st.items()},
+            "nproc": nproc, "cpu_model": cpu_model()}
+
+
+def ceilings(torch, dev, stream):
+    """Measured ceilings of this GPU beside the spec peaks: a large bf16 GEMM
+    (torch.matmul, 8192^3) and a 1 GiB device-to-device copy (bytes read plus
+    bytes written)."""
+    res = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    reps = 10
+    e0.record(stream)
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps
+    res["bf16_gemm_tflops"] = round(2.0 * n ** 3 / (t * 1e-3) / 1e12, 1)
+    res["bf16_gemm_shape"] = f"{n}x{n}x{n} torch.matmul"
+    del a, b
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps
+    res["copy_gbs"] = round(2.0 * src.numel() * 4 / (t * 1e-3) / 1e9, 1)
+    res["copy_bytes"] = src.numel() * 4
+    res["spec_peaks"] = {"bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}
+    del src, dst
+    return res
+
+
+def stage_rooflines(workload):
+    """Per-kernel roofline entries of the other stages (k-means assignment on
+    the matrix cores; centroid update and cluster gather against HBM), read
+    from the committed counter summary profiles/clustering_<workload>_pmc.txt
+    while the kmeans.hip, permute.hip and select.hip it was taken on are the
+    ones in the tree; None otherwise."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"clustering_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    for src in ("kmeans.hip", "permute.hip", "select.hip"):
+        with open(os.path.join(ROOT, "clustered_sparse_attention_cosine_amd", "csrc", src), "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()[:16]
+        if f"{src} sha256[:16] = {digest}" not in text:
+            return None
+    out = []
+    for line in text.splitlines():
+        if line.startswith("roofline "):
+            out.append(json.loads(line[len("roofline "):]))
+    return out or None
 
 
 if __name__ == "__main__":

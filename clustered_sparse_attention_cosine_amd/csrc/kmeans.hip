@@ -302,24 +302,41 @@ hipError_t launch_init_sample(const Prob& p, const void* x, int normalize, RowSe
 
 // ------------------------------------------------------------------ KMEANSPP init
 // D^2 sampling (Arthur and Vassilvitskii 2007), one workgroup per head. The
-// running sums and the search run in one thread in row order, in f64, so the
-// chosen rows follow exactly from the draws.
+// chosen rows must follow from the draws exactly, so the running sums of D^2
+// are formed by one thread in row order, in f64, as the definition states;
+// everything around that chain is parallel. Per round: the workgroup stages
+// D^2 through LDS in chunks while thread 0 adds them up, keeping the running
+// sum at each chunk start; with u = draw * S the crossing chunk is found from
+// those starts and only that chunk is added up again to find the row. The
+// D^2 update of every row (index-order f64 sums of squared differences) is
+// spread over the workgroup.
+constexpr int KPP_THREADS = 1024;
+constexpr int KPP_CH = 2048;                 // f64 values per LDS chunk
+constexpr int KPP_MAXCH = (1 << 21) / KPP_CH;  // chunks for the largest N
+
 template <typename T>
-__device__ __forceinline__ float kpp_val(const T* x, const float* xf, int N, int D, int bh,
-                                         int64_t tok, int d) {
-    return xf ? xf[((int64_t)bh * N + tok) * D + d] : elem<T>::load(row_ptr(x, N, D, bh, tok), d);
+__device__ __forceinline__ void kpp_row(const T* x, const float* xf, int N, int D, int bh, int64_t tok,
+                                        float (&v)[8], int d0) {
+    if (xf) {
+        load8<float>(xf + ((int64_t)bh * N + tok) * D + d0, v);
+    } else {
+        load8<T>(row_ptr(x, N, D, bh, tok) + d0, v);
+    }
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void init_kmeanspp_kernel(const T* __restrict__ x,
-                                                            const float* __restrict__ xf, int N,
-                                                            int D, int H, RowSet rs, CentView cv,
-                                                            uint64_t seed, uint32_t tensor,
-                                                            uint32_t stage, double* __restrict__ d2g,
-                                                            uint8_t* __restrict__ chosen_g) {
+__global__ __launch_bounds__(KPP_THREADS) void init_kmeanspp_kernel(const T* __restrict__ x,
+                                                                    const float* __restrict__ xf, int N,
+                                                                    int D, int H, RowSet rs, CentView cv,
+                                                                    uint64_t seed, uint32_t tensor,
+                                                                    uint32_t stage, double* __restrict__ d2g,
+                                                                    uint8_t* __restrict__ chosen_g) {
 #pragma clang fp contract(off)
+    __shared__ double chunk[KPP_CH];
+    __shared__ double cstart[KPP_MAXCH + 1];
     __shared__ float cvec[128];
     __shared__ int64_t sh_idx;
+    __shared__ int sh_first;
     const int bh = blockIdx.x;
     const int tid = threadIdx.x;
     if (rs.active && !rs.active[bh]) return;
@@ -327,59 +344,99 @@ __global__ __launch_bounds__(256) void init_kmeanspp_kernel(const T* __restrict_
     const int cm = n < cv.m ? n : cv.m;
     double* d2 = d2g + (int64_t)bh * N;
     uint8_t* chosen = chosen_g + (int64_t)bh * N;
-    for (int i = tid; i < n; i += blockDim.x) chosen[i] = 0;
-    uint64_t strm = draw_stream(seed, tensor, stage, (uint32_t)(bh / H), (uint32_t)(bh % H));
+    for (int i = tid; i < n; i += KPP_THREADS) chosen[i] = 0;
+    const uint64_t strm = draw_stream(seed, tensor, stage, (uint32_t)(bh / H), (uint32_t)(bh % H));
+    const int nch = (n + KPP_CH - 1) / KPP_CH;
     __syncthreads();
     for (int t = 0; t < cm; ++t) {
-        if (tid == 0) {
-            int64_t idx;
-            if (t == 0) {
-                idx = (int64_t)(sm64_at(strm, 0) % (uint64_t)n);
+        if (t == 0) {
+            if (tid == 0) sh_idx = (int64_t)(sm64_at(strm, 0) % (uint64_t)n);
+        } else {
+            // running sums in row order, chunk by chunk through LDS
+            double run = 0.0;
+            for (int c = 0; c < nch; ++c) {
+                const int c0 = c * KPP_CH, cn = min(KPP_CH, n - c0);
+                for (int i = tid; i < cn; i += KPP_THREADS) chunk[i] = d2[c0 + i];
+                __syncthreads();
+                if (tid == 0) {
+                    cstart[c] = run;
+                    for (int i = 0; i < cn; ++i) run += chunk[i];
+                }
+                __syncthreads();
+            }
+            if (tid == 0) cstart[nch] = run;
+            __syncthreads();
+            const double S = cstart[nch];
+            if (S == 0.0) {
+                // the smallest row not chosen yet
+                if (tid == 0) sh_first = n;
+                __syncthreads();
+                int first = n;
+                for (int i = tid; i < n; i += KPP_THREADS)
+                    if (!chosen[i]) { first = i; break; }
+                atomicMin(&sh_first, first);
+                __syncthreads();
+                if (tid == 0) sh_idx = sh_first < n ? sh_first : -1;
             } else {
-                double S = 0.0;
-                for (int i = 0; i < n; ++i) S += d2[i];
-                if (S == 0.0) {
-                    idx = -1;
-                    for (int i = 0; i < n; ++i)
-                        if (!chosen[i]) { idx = i; break; }
+                const double u = (double)(sm64_at(strm, (uint64_t)t) >> 11) * 0x1.0p-53 * S;
+                // the running sum first exceeds u inside the first chunk whose end exceeds u
+                int cc = -1;
+                if (tid == 0)
+                    for (int c = 0; c < nch; ++c)
+                        if (cstart[c + 1] > u) { cc = c; break; }
+                if (tid == 0) sh_first = cc;
+                __syncthreads();
+                cc = sh_first;
+                if (cc < 0) {
+                    if (tid == 0) sh_idx = n - 1;
                 } else {
-                    double u = (double)(sm64_at(strm, (uint64_t)t) >> 11) * 0x1.0p-53 * S;
-                    double run = 0.0;
-                    idx = n - 1;
-                    for (int i = 0; i < n; ++i) {
-                        run += d2[i];
-                        if (run > u) { idx = i; break; }
+                    const int c0 = cc * KPP_CH, cn = min(KPP_CH, n - c0);
+                    for (int i = tid; i < cn; i += KPP_THREADS) chunk[i] = d2[c0 + i];
+                    __syncthreads();
+                    if (tid == 0) {
+                        double r = cstart[cc];
+                        int64_t idx = n - 1;
+                        for (int i = 0; i < cn; ++i) {
+                            r += chunk[i];
+                            if (r > u) { idx = c0 + i; break; }
+                        }
+                        sh_idx = idx;
                     }
                 }
             }
-            chosen[idx] = 1;
-            sh_idx = idx;
         }
         __syncthreads();
         const int64_t idx = sh_idx;
+        if (tid == 0) chosen[idx] = 1;
         const int64_t tok_c = rs.rows ? rs.rows[(int64_t)bh * N + idx] : idx;
         const int64_t slot = (int64_t)bh * cv.cap + cv.base + t;
-        for (int d = tid; d < D; d += blockDim.x) {
-            float v = kpp_val(x, xf, N, D, bh, tok_c, d);
+        for (int d = tid; d < D; d += KPP_THREADS) {
+            const float v = xf ? xf[((int64_t)bh * N + tok_c) * D + d]
+                               : elem<T>::load(row_ptr(x, N, D, bh, tok_c), d);
             cvec[d] = v;
             cv.cent[slot * D + d] = v;
         }
         if (tid == 0) cv.valid[slot] = 1;
         __syncthreads();
-        for (int i = tid; i < n; i += blockDim.x) {
+        for (int i = tid; i < n; i += KPP_THREADS) {
             const int64_t tok = rs.rows ? rs.rows[(int64_t)bh * N + i] : i;
-            double s = 0.0;
-            for (int d = 0; d < D; ++d) {
-                double df = (double)kpp_val(x, xf, N, D, bh, tok, d) - (double)cvec[d];
-                s += df * df;
+            double sacc = 0.0;
+            for (int d0 = 0; d0 < D; d0 += 8) {
+                float v[8];
+                kpp_row<T>(x, xf, N, D, bh, tok, v, d0);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const double df = (double)v[e] - (double)cvec[d0 + e];
+                    sacc += df * df;
+                }
             }
-            if (t == 0 || s < d2[i]) d2[i] = s;
+            if (t == 0 || sacc < d2[i]) d2[i] = sacc;
         }
         __syncthreads();
     }
     for (int j = cm; j < cv.m; ++j) {
         const int64_t slot = (int64_t)bh * cv.cap + cv.base + j;
-        for (int d = tid; d < D; d += blockDim.x) cv.cent[slot * D + d] = 0.0f;
+        for (int d = tid; d < D; d += KPP_THREADS) cv.cent[slot * D + d] = 0.0f;
         if (tid == 0) cv.valid[slot] = 0;
     }
 }
@@ -388,10 +445,10 @@ hipError_t launch_init_kmeanspp(const Prob& p, const void* x, const float* xf, R
                                 CentView cv, uint64_t seed, uint32_t tensor, uint32_t stage,
                                 double* d2, uint8_t* chosen, hipStream_t s) {
     if (p.bf16)
-        hipLaunchKernelGGL(init_kmeanspp_kernel<u16>, dim3(p.BH), dim3(256), 0, s, (const u16*)x,
+        hipLaunchKernelGGL(init_kmeanspp_kernel<u16>, dim3(p.BH), dim3(KPP_THREADS), 0, s, (const u16*)x,
                            xf, p.N, p.D, p.H, rs, cv, seed, tensor, stage, d2, chosen);
     else
-        hipLaunchKernelGGL(init_kmeanspp_kernel<float>, dim3(p.BH), dim3(256), 0, s,
+        hipLaunchKernelGGL(init_kmeanspp_kernel<float>, dim3(p.BH), dim3(KPP_THREADS), 0, s,
                            (const float*)x, xf, p.N, p.D, p.H, rs, cv, seed, tensor, stage, d2,
                            chosen);
     return hipGetLastError();

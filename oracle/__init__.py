@@ -18,7 +18,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "adacluster_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle_adacluster.so")
+# ORACLE_LIB selects another build of the same source (the sanitizer build of
+# oracle/sanitize.py); by default the library next to the source is used.
+_LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle_adacluster.so")
 
 INIT_KMEANSPP, INIT_SAMPLE, INIT_CALLER = 0, 1, 2
 INIT_BY_NAME = {"kmeanspp": INIT_KMEANSPP, "sample": INIT_SAMPLE, "caller": INIT_CALLER}

@@ -21,9 +21,12 @@ pytestmark = pytest.mark.gpu
 CASES = {
     "bf16_d64": ("cog17k", dict(H=2, grid=(3, 20, 50), text_tokens=37, q_clusters=40, k_base=24)),
     "bf16_d128": ("wan33k", dict(H=2, grid=(2, 31, 37), q_clusters=24, k_base=18)),
-    # keys scattered enough that stage 1 leaves keys for stage 2 and the head
-    # ends at the slot cap (F = 1)
-    "heavy_tail": ("hun119k", dict(H=2, grid=(2, 24, 30), q_clusters=20, k_base=6, noise_std=0.4)),
+    # heavy-tailed keys scattered enough that every head runs three stages;
+    # the oracle's own run ends head 0 at the slot cap with keys left (F = 1)
+    # and empties U on head 1 (F = 0)
+    "heavy_tail": ("hun119k", dict(H=2, grid=(2, 16, 20), q_clusters=20, k_base=2, noise_std=2.0)),
+    # both heads end at the cap with keys left
+    "full_cap": ("hun119k", dict(H=2, grid=(2, 24, 30), q_clusters=20, k_base=4, noise_std=1.5)),
 }
 
 

@@ -131,7 +131,7 @@ def test_select_all_equals_dense(D, dtype):
 
 
 def test_sparse_attn_edge_cases():
-    # empty q-clusters, a single-row q-cluster, a 150-row q-cluster (3 chunks), a
+    # empty q-clusters, a single-row q-cluster, a 150-row q-cluster (2 chunks of 128 rows), a
     # selection of empty slots only (row gets o = 0, lse = -inf), ragged Ck
     rng = np.random.default_rng(3)
     N, D, Cq, Ck = 200, 64, 5, 37
