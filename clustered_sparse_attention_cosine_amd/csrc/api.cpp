@@ -33,6 +33,13 @@ int32_t fail(int32_t code, const char* fmt, ...) {
     } while (0)
 
 constexpr int MAX_CLUSTERS = 8192;
+
+// Lloyd rounds after the first contract each row only with its label's
+// candidate slots (the full contraction gives the same labels).
+#ifndef ADC_PRUNE
+#define ADC_PRUNE 1
+#endif
+constexpr bool g_prune = ADC_PRUNE != 0;
 constexpr int MAX_N = 1 << 21;
 
 // Bump allocator over the caller's workspace: pieces at 256-byte aligned
@@ -112,6 +119,11 @@ struct KmeansWs {
     int32_t* rlist = nullptr;
     int32_t* rcount = nullptr;
     float* drift = nullptr;
+    // pruned assignment: slot radii and candidate lists
+    float* rad = nullptr;
+    float* part_rad = nullptr;
+    uint32_t* cbits = nullptr;
+    int cwords = 0;
 };
 
 void plan_kmeans(Carver& c, const Prob& p, int cap, bool want_inv, bool kpp, bool want_xhat,
@@ -141,6 +153,10 @@ void plan_kmeans(Carver& c, const Prob& p, int cap, bool want_inv, bool kpp, boo
     w.rlist = c.take<int32_t>(bhn);
     w.rcount = c.take<int32_t>(p.BH);
     w.drift = c.take<float>(bhc);
+    w.rad = c.take<float>(bhc);
+    w.part_rad = c.take<float>((size_t)p.BH * w.nwav * 2);
+    w.cwords = (cap + 31) / 32;
+    w.cbits = c.take<uint32_t>(bhc * w.cwords);
     if (kpp) {
         if (want_xhat) w.xhat = c.take<float>(bhn * p.D);
         w.d2 = c.take<double>(bhn);
@@ -220,25 +236,40 @@ hipError_t lloyd(const Prob& p, const void* x, int normalize, RowSet rs, const f
     }
     for (int it = 0; it < iters; ++it) {
         RowSet ra = rs;
+        CentView ca = cv;
         if (bounds && it > 0) {
-            if ((e = launch_bound_filter(p, rs, cv, labels, w.ub, w.lb, w.drift, w.rlist, w.rcount, s)))
-                return e;
-            ra = RowSet{w.rlist, w.rcount, rs.active, 1};
+            if (g_prune) {
+                // pruned round: the rows in the order of the previous round's sort,
+                // each contracted only with the slots its label's radius allows
+                if ((e = launch_cand_bits(p, cv, mcount, w.rad, w.drift, w.cbits, w.cwords, s))) return e;
+                ra = RowSet{ss.perm, nullptr, rs.active, 1};
+                ca.cbits = w.cbits;
+                ca.cwords = w.cwords;
+            } else {
+                if ((e = launch_bound_filter(p, rs, cv, labels, w.ub, w.lb, w.drift, w.rlist, w.rcount, s)))
+                    return e;
+                ra = RowSet{w.rlist, w.rcount, rs.active, 1};
+            }
         }
         if (snap && it + 1 == iters && (e = launch_copy_slots(p, cv, rs.active, snap, s))) return e;
         // a row subset (later stages: the few keys left in U) also splits the centre tiles
         // from the second round on, the previous round's finalize cleared the flag counts
-        if ((e = launch_assign(p, x, ra, inv_norm, normalize, cv, mcount, labels, fs, s, rs.rows ? 4 : 0,
+        if ((e = launch_assign(p, x, ra, inv_norm, normalize, ca, mcount, labels, fs, s, rs.rows ? 4 : 0,
                                it > 0)))
             return e;
         if (it + 1 < iters || final_update) {
+            // the next round's candidate sets need each cluster's radius (the
+            // largest upper bound of its rows), taken by the same sorted walk
+            const bool radii = bounds && g_prune && it + 1 < iters;
             if ((e = launch_counting_sort(p, labels, cv.m, w.seg_cnt, w.hist, ss.sizes, ss.offsets, ss.perm,
                                           s, rs.nrows, rs.active)))
                 return e;
-            if ((e = launch_update_accum(p, x, rs, inv_norm, labels, cv, ss.perm, s))) return e;
+            if ((e = launch_update_accum(p, x, rs, inv_norm, labels, cv, ss.perm, s, radii ? w.ub : nullptr,
+                                         w.rad, w.part_rad)))
+                return e;
             if (bounds && it + 1 < iters) {
                 if ((e = launch_finalize(p, cv, rs.active, ss.offsets, s, w.drift, w.flag_count, w.over_count,
-                                         w.rcount)))
+                                         w.rcount, radii ? w.rad : nullptr, w.part_rad)))
                     return e;
             } else if ((e = launch_finalize(p, cv, rs.active, ss.offsets, s, nullptr, w.flag_count,
                                             w.over_count))) {

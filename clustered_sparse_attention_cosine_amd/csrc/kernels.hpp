@@ -50,7 +50,13 @@ struct CentView {
     int cap;
     int base;
     int m;
+    // Pruned assignment (may be null): per slot a, a bit set over the view's
+    // slots (cbits [BH][cap][cwords]) of the slots that can be the nearest
+    // centre of a row now labelled a.
+    const uint32_t* cbits = nullptr;
+    int cwords = 0;
 };
+constexpr int UCAP = 512;   // candidate slots a pruned workgroup gathers
 
 // Rows a k-means call clusters: rows[bh*N + r] for r < nrows[bh] (NULL: all N
 // rows, identity), only for heads with active[bh] != 0 (NULL: all heads).
@@ -78,9 +84,12 @@ hipError_t launch_init_kmeanspp(const Prob& p, const void* x, const float* xf, R
 // mean of its members' sums; then with drift != NULL also drift[slot] >=
 // ||new - old|| (0 where no centre). zero_a/b/c (may be null): per-head
 // counters [BH] cleared on the way.
+// With rad (and part_rad, the update's part radii) it also completes each
+// slot's radius: the largest ub of its rows (0 for a slot without rows).
 hipError_t launch_finalize(const Prob& p, CentView cv, const uint8_t* active, const int32_t* soff,
                            hipStream_t s, float* drift = nullptr, int32_t* zero_a = nullptr,
-                           int32_t* zero_b = nullptr, int32_t* zero_c = nullptr);
+                           int32_t* zero_b = nullptr, int32_t* zero_c = nullptr,
+                           float* rad = nullptr, const float* part_rad = nullptr);
 // Flag lists of the certified assignment (see kmeans.hip).
 struct FlagSet {
     int32_t* list;
@@ -111,9 +120,21 @@ hipError_t launch_last_valid(const Prob& p, CentView cv, const int32_t* mcount, 
 // centres inside their uncertainty band (labels are final on return).
 // split > 1: for calls over few rows, the centre tiles are also split over up to
 // `split` workgroups per row block (same labels; shorter serial chain per row).
+// With cv.clist set (pruned assignment): rs.rows lists the rows sorted by
+// their current label (by token), and each workgroup contracts its rows only
+// with the union of their labels' candidate lists (labels is read for the
+// current labels and then overwritten with the new ones).
 hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
                          int normalize, CentView cv, const int32_t* mcount, int32_t* labels,
                          FlagSet fs, hipStream_t s, int split = 0, bool counts_zeroed = false);
+// Candidate sets for the pruned assignment (Elkan's first lemma): for slot a
+// with radius R = rad[a] + drift[a] (drift may be null), every slot j holding
+// a centre with ||c_j - c_a|| <= 2 R (up to a rounding margin taken in the
+// safe direction), as bits of cbits [BH][cv.cap][cwords]. A row of a is
+// strictly closer to c_a than to any slot left out, so its nearest centre,
+// ties included, is in the set.
+hipError_t launch_cand_bits(const Prob& p, CentView cv, const int32_t* mcount, const float* rad,
+                            const float* drift, uint32_t* cbits, int cwords, hipStream_t s);
 // Bound test between Lloyd rounds (every row, rs.rows NULL): a row whose bound on
 // its own centre, grown by that centre's drift, stays below its bound on every
 // other centre, shrunk by the largest drift, keeps its label and the moved
@@ -129,9 +150,14 @@ hipError_t launch_bound_filter(const Prob& p, RowSet rs, CentView cv, const int3
 // part[W][0], the part at the end to part[W][1], and finalize adds a long
 // cluster's parts in wave order. No atomics: the sums do not depend on
 // scheduling, so identical inputs give identical centres.
+// With ub (an upper bound on each row's distance to its centre, by token) it
+// also takes each slot's radius, the largest ub of its rows: rad [BH][cap]
+// for clusters inside one wave, part_rad [BH][nwav][2] for the parts that
+// finalize combines.
 hipError_t launch_update_accum(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
                                const int32_t* labels, CentView cv, const int32_t* order,
-                               hipStream_t s);
+                               hipStream_t s, const float* ub = nullptr, float* rad = nullptr,
+                               float* part_rad = nullptr);
 
 // Copy of the centres of view cv (slots [base, base + m) of every head with
 // active[bh] != 0, active may be null) into dst, same [BH][cap][D] layout.

@@ -463,7 +463,9 @@ hipError_t launch_init_kmeanspp(const Prob& p, const void* x, const float* xf, R
 template <int D>
 __global__ __launch_bounds__(256) void finalize_kernel(CentView cv, const uint8_t* active,
                                                        const int32_t* __restrict__ soff, float* drift,
-                                                       int32_t* zero_a, int32_t* zero_b, int32_t* zero_c) {
+                                                       int32_t* zero_a, int32_t* zero_b, int32_t* zero_c,
+                                                       float* __restrict__ rad,
+                                                       const float* __restrict__ part_rad) {
     const int bh = blockIdx.y;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int j = blockIdx.x * 4 + w;
@@ -497,6 +499,13 @@ __global__ __launch_bounds__(256) void finalize_kernel(CentView cv, const uint8_
                 for (int ww = w1 + 1; ww <= w2; ++ww)
 #pragma unroll
                     for (int e = 0; e < E; ++e) acc[e] += pb[((int64_t)ww * 2) * D + l + 64 * e];
+                if (rad && l == 0) {
+                    // the radius of a cluster over several update waves: the largest part
+                    const float* pr = part_rad + (int64_t)bh * cv.nwav * 2;
+                    float r = pr[(int64_t)w1 * 2 + 1];
+                    for (int ww = w1 + 1; ww <= w2; ++ww) r = fmaxf(r, pr[(int64_t)ww * 2]);
+                    rad[slot] = r;
+                }
             }
 #pragma unroll
             for (int e = 0; e < E; ++e) {
@@ -505,6 +514,8 @@ __global__ __launch_bounds__(256) void finalize_kernel(CentView cv, const uint8_
                 dd += df * df;
                 c[l + 64 * e] = nv;
             }
+        } else if (rad && l == 0) {
+            rad[slot] = 0.0f;
         }
         if (drift) {
             // ||new - old|| from the f32 differences (each within 2^-24 of
@@ -529,14 +540,109 @@ __global__ __launch_bounds__(256) void finalize_kernel(CentView cv, const uint8_
 
 hipError_t launch_finalize(const Prob& p, CentView cv, const uint8_t* active, const int32_t* soff,
                            hipStream_t s, float* drift, int32_t* zero_a, int32_t* zero_b,
-                           int32_t* zero_c) {
+                           int32_t* zero_c, float* rad, const float* part_rad) {
     dim3 grid((unsigned)((cv.m + 3) / 4), (unsigned)p.BH);
     if (p.D == 64)
         hipLaunchKernelGGL(finalize_kernel<64>, grid, dim3(256), 0, s, cv, active, soff, drift,
-                           zero_a, zero_b, zero_c);
+                           zero_a, zero_b, zero_c, rad, part_rad);
     else
         hipLaunchKernelGGL(finalize_kernel<128>, grid, dim3(256), 0, s, cv, active, soff, drift,
-                           zero_a, zero_b, zero_c);
+                           zero_a, zero_b, zero_c, rad, part_rad);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ pruned assignment
+// Pairwise centre distances on the matrix cores: a workgroup takes 64 slots
+// a (16 per wave, as the B operand) against every tile of 64 slots j (the A
+// operand, staged in LDS), with the bf16 hi/lo parts finalize keeps:
+// G = hi_j.hi_a + lo_j.hi_a + hi_j.lo_a, ||c_j - c_a||^2 = ||c_j||^2 +
+// ||c_a||^2 - 2 G. The dropped lo.lo term, the hi/lo residuals and the f32
+// accumulation stay below 2^-15 ||c_a|| ||c_j||, the roundings of the sum
+// below 2^-21 (||c_a||^2 + ||c_j||^2), so subtracting 2^-13 (||c_a||^2 +
+// ||c_j||^2) gives a lower bound: j joins a's set when that bound is at most
+// (2 R)^2 (1 + 2^-12) with R rounded up, so every slot the lemma does not
+// exclude is kept. Slots without a centre join no set and have none; only the
+// words of slots below the count are written (and read).
+template <int D>
+__global__ __launch_bounds__(256) void cand_bits_kernel(CentView cv, const int32_t* __restrict__ mcount,
+                                                        const float* __restrict__ rad,
+                                                        const float* __restrict__ drift,
+                                                        uint32_t* __restrict__ cbits, int cwords) {
+    constexpr int KC = D / 32;
+    constexpr int LD = D + 8;
+    __shared__ __attribute__((aligned(16))) u16 sh_hi[64 * LD];
+    __shared__ __attribute__((aligned(16))) u16 sh_lo[64 * LD];
+    __shared__ float sh_n2[64];
+    const int bh = blockIdx.y;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c16 = l & 15;
+    const int M = mcount ? min(mcount[bh], cv.m) : cv.m;
+    const int a0 = blockIdx.x * 64;
+    if (a0 >= M) return;  // no row carries these labels
+    const int64_t sbase = (int64_t)bh * cv.cap + cv.base;
+    const int a = a0 + w * 16 + c16;
+    const int ac = min(a, M - 1);
+    bf16x8 ah[KC], al[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+        ah[kc] = ld_bf16x8(cv.c_hi + (sbase + ac) * D + kc * 32 + g * 8);
+        al[kc] = ld_bf16x8(cv.c_lo + (sbase + ac) * D + kc * 32 + g * 8);
+    }
+    const float na2 = cv.cn2[sbase + ac];
+    float lim = -INFINITY;  // no set for slots without a centre or past the count
+    if (a < M && na2 < INFINITY) {
+        const float R = (rad[sbase + a] + (drift ? drift[sbase + a] : 0.0f)) * (1.0f + 0x1.0p-20f);
+        lim = 4.0f * R * R * (1.0f + 0x1.0p-12f);
+    }
+    for (int j0 = 0; j0 < M; j0 += 64) {
+        __syncthreads();
+        for (int i = tid; i < 64 * (D / 8); i += 256) {
+            const int r = i / (D / 8), c = (i % (D / 8)) * 8;
+            const int64_t j = sbase + min(j0 + r, M - 1);
+            *reinterpret_cast<u32x4*>(&sh_hi[r * LD + c]) = *reinterpret_cast<const u32x4*>(cv.c_hi + j * D + c);
+            *reinterpret_cast<u32x4*>(&sh_lo[r * LD + c]) = *reinterpret_cast<const u32x4*>(cv.c_lo + j * D + c);
+        }
+        if (tid < 64) sh_n2[tid] = j0 + tid < M ? cv.cn2[sbase + j0 + tid] : INFINITY;
+        __syncthreads();
+        uint32_t bits[2] = {0u, 0u};
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const int off = (cb * 16 + c16) * LD + kc * 32 + g * 8;
+                const bf16x8 jh = *reinterpret_cast<const bf16x8*>(&sh_hi[off]);
+                const bf16x8 jl = *reinterpret_cast<const bf16x8*>(&sh_lo[off]);
+                acc = mfma16(jh, ah[kc], acc);
+                acc = mfma16(jl, ah[kc], acc);
+                acc = mfma16(jh, al[kc], acc);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float nj2 = sh_n2[cb * 16 + g * 4 + i];  // +inf: no centre, never kept
+                const float s2 = (na2 + nj2) - 2.0f * acc[i];
+                const bool keep = nj2 < INFINITY && s2 - 0x1.0p-13f * (na2 + nj2) <= lim;
+                const int jb = cb * 16 + g * 4 + i;  // position in the tile
+                bits[jb >> 5] |= (uint32_t)keep << (jb & 31);
+            }
+        }
+        // the four lanes holding column c16 cover disjoint bits: OR them together
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            bits[h] |= __shfl_xor(bits[h], 16);
+            bits[h] |= __shfl_xor(bits[h], 32);
+        }
+        const int wd = (j0 >> 5) + (g & 1);
+        if (g < 2 && a < M && wd < cwords) cbits[(sbase + a) * cwords + wd] = bits[g & 1];
+    }
+}
+
+hipError_t launch_cand_bits(const Prob& p, CentView cv, const int32_t* mcount, const float* rad,
+                            const float* drift, uint32_t* cbits, int cwords, hipStream_t s) {
+    dim3 grid((unsigned)((cv.m + 63) / 64), (unsigned)p.BH);
+    if (p.D == 64)
+        hipLaunchKernelGGL(cand_bits_kernel<64>, grid, dim3(256), 0, s, cv, mcount, rad, drift, cbits, cwords);
+    else
+        hipLaunchKernelGGL(cand_bits_kernel<128>, grid, dim3(256), 0, s, cv, mcount, rad, drift, cbits, cwords);
     return hipGetLastError();
 }
 
@@ -757,7 +863,17 @@ __device__ __forceinline__ void assign_settle(uint32_t k1, uint32_t k2, int bj, 
 // dropped (3 VALU ops per distance). The accumulator then carries the centre
 // term through the f32 accumulation, which the error bound allows for.
 // bf16 rows, D = 64: 128 registers at most, four workgroups per CU
-template <typename T, int D, bool F32X, bool CAND, bool FOLD>
+//
+// GATHER (pruned assignment): the rows come sorted by their current label, so
+// a workgroup's 256 rows carry a short range of labels [a0, a1]; the centres
+// it contracts with are the union of those labels' candidate sets, gathered
+// by index into the same LDS tiles (the union of the bit sets is compacted to
+// an index list in slot order; a workgroup whose union passes UCAP takes every
+// slot). Every row's nearest centre is in its own label's set, so the argmin,
+// the certificate and the row's upper bound are those of the full
+// contraction; the lower bound covers only the gathered centres and is not
+// used after a pruned round.
+template <typename T, int D, bool F32X, bool CAND, bool FOLD, bool GATHER>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && !F32X ? 4 : 1, 8)))
 void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
                                                      const float* __restrict__ inv_norm,
@@ -771,6 +887,7 @@ void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
     __shared__ __attribute__((aligned(16))) u16 sh_lo[2][64 * LD];
     __shared__ float sh_c2[2][64];
     __shared__ float sh_red[2][4];
+    __shared__ int ulist[GATHER ? UCAP : 1];
 
     const int bh = blockIdx.y;
     if (rs.active && !rs.active[bh]) return;
@@ -843,6 +960,56 @@ void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
         xn[pb] = sc[pb] * sqrtf(ss);
     }
 
+    // GATHER: the centres of this workgroup (see above); U = -1 means every slot
+    int U = -1;
+    if constexpr (GATHER) {
+        uint32_t* bits = reinterpret_cast<uint32_t*>(&sh_hi[1][0]);  // free until the first tile swap
+        const int nwords = (M + 31) / 32;
+        const int last = min(row_base + 255, n - 1);
+        const int a0 = labels[(int64_t)bh * N + rs.rows[(int64_t)bh * N + row_base]];
+        const int a1 = labels[(int64_t)bh * N + rs.rows[(int64_t)bh * N + last]];
+        const int64_t sbase = (int64_t)bh * cv.cap + cv.base;
+        for (int i = tid; i < nwords; i += 256) {
+            uint32_t word = 0u;
+            for (int a = a0; a <= a1; ++a) word |= cv.cbits[(sbase + a) * cv.cwords + i];
+            bits[i] = word;
+        }
+        __syncthreads();
+        // compaction in slot order: thread i takes words i, i + 256, ...; a wave
+        // scan and the four wave totals place them
+        int total = 0;
+        for (int w0 = 0; w0 < nwords; w0 += 256) {
+            const int wi = w0 + tid;
+            const uint32_t word = wi < nwords ? bits[wi] : 0u;
+            const int cnt = __popc(word);
+            int incl = cnt;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int v = __shfl_up(incl, o);
+                if (l >= o) incl += v;
+            }
+            if (l == 63) sh_red[0][w] = __int_as_float(incl);
+            __syncthreads();
+            int before = total + incl - cnt;
+            for (int i = 0; i < w; ++i) before += __float_as_int(sh_red[0][i]);
+            int tot = 0;
+            for (int i = 0; i < 4; ++i) tot += __float_as_int(sh_red[0][i]);
+            uint32_t wd = word;
+            while (wd) {
+                const int b = __ffs(wd) - 1;
+                wd &= wd - 1;
+                if (before < UCAP) ulist[before] = wi * 32 + b;
+                ++before;
+            }
+            total += tot;
+            __syncthreads();
+        }
+        U = (total > UCAP || total == 0) ? -1 : total;
+        __syncthreads();
+    }
+    const int ntiles_g = U >= 0 ? (U + 63) / 64 : ntiles_all;
+    const int t_end_g = GATHER ? ntiles_g : t_end;
+
     // Assignment pass: d'_j = ||c_j||^2 + B - 2 s (x . c_j) with one offset B per
     // workgroup, B = max_rows (s||x||)^2 + 2^-10 (max_rows s||x|| + max||c||)^2.
     // d'_j - B + (s||x||)^2 is the squared distance, so d' > 0 by a margin far
@@ -878,15 +1045,23 @@ void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
     // clamped slots; slots past M get ||c||^2 = +inf.
     u32x4 ph[D / 32], pl[D / 32];
     float pc2;
+    // slot of tile position q (GATHER: through the index list)
+    auto slot_at = [&](int q) __attribute__((always_inline)) -> int {
+        if constexpr (GATHER) {
+            if (U >= 0) return ulist[min(q, U - 1)];
+        }
+        return min(q, M - 1);
+    };
+    const int lim = (GATHER && U >= 0) ? U : M;  // tile positions that hold a slot
 #define ADC_LOAD_TILE(TILE)                                                                  \
     do {                                                                                   \
         _Pragma("unroll") for (int i = 0; i < D / 32; ++i) {                               \
             const int c = tid + i * 256;                                                   \
-            const int64_t j = cbase + min((TILE) * 64 + c / (D / 8), M - 1);               \
+            const int64_t j = cbase + slot_at((TILE) * 64 + c / (D / 8));                  \
             ph[i] = *reinterpret_cast<const u32x4*>(cv.c_hi + j * D + (c % (D / 8)) * 8); \
             pl[i] = *reinterpret_cast<const u32x4*>(cv.c_lo + j * D + (c % (D / 8)) * 8); \
         }                                                                                  \
-        pc2 = cv.cn2[cbase + min((TILE) * 64 + (tid & 63), M - 1)];                        \
+        pc2 = cv.cn2[cbase + slot_at((TILE) * 64 + (tid & 63))];                           \
     } while (0)
 #define ADC_STORE_TILE(TILE, BUF)                                                          \
     do {                                                                                   \
@@ -897,18 +1072,18 @@ void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
             *reinterpret_cast<u32x4*>(&sh_lo[BUF][o]) = pl[i];                             \
         }                                                                                  \
         if (tid < 64)                                                                      \
-            sh_c2[BUF][tid] = FOLD ? ((TILE) * 64 + tid < M ? -0.5f * (pc2 + bwg) : -INFINITY) \
-                                   : ((TILE) * 64 + tid < M ? pc2 + bwg : INFINITY);        \
+            sh_c2[BUF][tid] = FOLD ? ((TILE) * 64 + tid < lim ? -0.5f * (pc2 + bwg) : -INFINITY) \
+                                   : ((TILE) * 64 + tid < lim ? pc2 + bwg : INFINITY);        \
     } while (0)
-    if (t_begin < t_end) {
+    if (t_begin < t_end_g) {
         ADC_LOAD_TILE(t_begin);
         ADC_STORE_TILE(t_begin, 0);
     }
     __syncthreads();
 
-    for (int tile = t_begin; tile < t_end; ++tile) {
+    for (int tile = t_begin; tile < t_end_g; ++tile) {
         const int buf = (tile - t_begin) & 1;
-        ADC_LOAD_TILE(min(tile + 1, t_end - 1));
+        ADC_LOAD_TILE(min(tile + 1, t_end_g - 1));
         uint32_t prev[4];
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) prev[pb] = b1[pb];
@@ -971,6 +1146,7 @@ void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
         for (int pb = 0; pb < 4; ++pb) {
             const uint32_t pos = b1[pb] & 15u;
             int bj = tb[pb] * 64 + (int)(pos >> 2) * 16 + g * 4 + (int)(pos & 3u);
+            if constexpr (GATHER) bj = slot_at(bj);
 #pragma unroll
             for (int o = 16; o <= 32; o <<= 1) {
                 const uint32_t ob1 = __shfl_xor(b1[pb], o);
@@ -1002,17 +1178,19 @@ void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
     }
 }
 
-template <bool CAND, bool FOLD>
+template <bool CAND, bool FOLD, bool GATHER = false>
 static void launch_assign_t(const Prob& p, dim3 grid, const void* x, RowSet rs,
                             const float* inv_norm, int normalize, CentView cv,
                             const int32_t* mcount, int32_t* labels, FlagSet fs, int tps,
                             hipStream_t s, int32_t* rec = nullptr) {
     if (p.bf16) {
-        auto k = p.D == 64 ? assign_kernel<u16, 64, false, CAND, FOLD> : assign_kernel<u16, 128, false, CAND, FOLD>;
+        auto k = p.D == 64 ? assign_kernel<u16, 64, false, CAND, FOLD, GATHER>
+                           : assign_kernel<u16, 128, false, CAND, FOLD, GATHER>;
         hipLaunchKernelGGL(k, grid, dim3(256), 0, s, (const u16*)x, p.N, rs, inv_norm, normalize, cv,
                            mcount, labels, fs, tps, rec);
     } else {
-        auto k = p.D == 64 ? assign_kernel<float, 64, true, CAND, FOLD> : assign_kernel<float, 128, true, CAND, FOLD>;
+        auto k = p.D == 64 ? assign_kernel<float, 64, true, CAND, FOLD, GATHER>
+                           : assign_kernel<float, 128, true, CAND, FOLD, GATHER>;
         hipLaunchKernelGGL(k, grid, dim3(256), 0, s, (const float*)x, p.N, rs, inv_norm, normalize,
                            cv, mcount, labels, fs, tps, rec);
     }
@@ -1056,6 +1234,9 @@ __global__ __launch_bounds__(256) void cand_exact_kernel(const T* __restrict__ X
                 fs.over[(int64_t)bh * N + pos] = r;
             } else {
                 labels[(int64_t)bh * N + (rs.by_token ? tok : r)] = j;
+                // an upper bound on the row's distance to its centre (the exact
+                // value, rounded up)
+                if (fs.ub) fs.ub[(int64_t)bh * N + (rs.by_token ? tok : r)] = (float)sqrt(d) * (1.0f + 0x1.0p-20f);
             }
         }
     }
@@ -1072,7 +1253,7 @@ __global__ __launch_bounds__(256) void refine_kernel(const T* __restrict__ X, in
                                                      const int32_t* __restrict__ mcount,
                                                      const int32_t* __restrict__ flag_list,
                                                      const int32_t* __restrict__ flag_count,
-                                                     int32_t* __restrict__ labels) {
+                                                     int32_t* __restrict__ labels, float* __restrict__ ub) {
 #pragma clang fp contract(off)
     __shared__ float xs[4][D];
     const int bh = blockIdx.y;
@@ -1120,7 +1301,10 @@ __global__ __launch_bounds__(256) void refine_kernel(const T* __restrict__ X, in
                 const int oj = __shfl_xor(bj, o);
                 if (ob < best || (ob == best && oj < bj)) { best = ob; bj = oj; }
             }
-            if (l == 0 && bj != 0x7fffffff) labels[(int64_t)bh * N + (rs.by_token ? tok : r)] = bj;
+            if (l == 0 && bj != 0x7fffffff) {
+                labels[(int64_t)bh * N + (rs.by_token ? tok : r)] = bj;
+                if (ub) ub[(int64_t)bh * N + (rs.by_token ? tok : r)] = (float)sqrt(best) * (1.0f + 0x1.0p-20f);
+            }
         }
         __syncthreads();
     }
@@ -1128,16 +1312,16 @@ __global__ __launch_bounds__(256) void refine_kernel(const T* __restrict__ X, in
 
 static hipError_t launch_refine_full(const Prob& p, const void* x, int normalize, RowSet rs,
                                      CentView cv, const int32_t* mcount, const int32_t* list,
-                                     const int32_t* count, int32_t* labels, hipStream_t s) {
+                                     const int32_t* count, int32_t* labels, float* ub, hipStream_t s) {
     dim3 grid(8u, (unsigned)p.BH);
     if (p.bf16) {
         auto k = p.D == 64 ? refine_kernel<u16, 64> : refine_kernel<u16, 128>;
         hipLaunchKernelGGL(k, grid, dim3(256), 0, s, (const u16*)x, p.N, normalize, rs, cv, mcount,
-                           list, count, labels);
+                           list, count, labels, ub);
     } else {
         auto k = p.D == 64 ? refine_kernel<float, 64> : refine_kernel<float, 128>;
         hipLaunchKernelGGL(k, grid, dim3(256), 0, s, (const float*)x, p.N, normalize, rs, cv, mcount,
-                           list, count, labels);
+                           list, count, labels, ub);
     }
     return hipGetLastError();
 }
@@ -1199,6 +1383,11 @@ hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* i
                        : (p.bf16 ? assign_merge_kernel<false, false> : assign_merge_kernel<false, true>);
         hipLaunchKernelGGL(mk, grid, dim3(256), 0, s, p.N, rs, cv.m, (const int32_t*)fs.cand, nz, tps,
                            labels, fs);
+    } else if (cv.cbits) {
+        if (fold)
+            launch_assign_t<false, true, true>(p, grid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, 0, s);
+        else
+            launch_assign_t<false, false, true>(p, grid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, 0, s);
     } else if (fold) {
         launch_assign_t<false, true>(p, grid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, 0, s);
     } else {
@@ -1206,6 +1395,7 @@ hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* i
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // candidate pass: the centre tiles of the flagged rows are split 8 per workgroup
+    // (over every slot, also after a pruned pass)
     constexpr int TPS = 8;
     const int tiles = (cv.m + 63) / 64;
     dim3 cgrid((unsigned)((p.N + 255) / 256), (unsigned)p.BH, (unsigned)((tiles + TPS - 1) / TPS));
@@ -1220,7 +1410,7 @@ hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* i
         hipLaunchKernelGGL(k, egrid, dim3(256), 0, s, (const float*)x, p.N, normalize, rs, cv, fs, labels);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    return launch_refine_full(p, x, normalize, rs, cv, mcount, fs.over, fs.over_count, labels, s);
+    return launch_refine_full(p, x, normalize, rs, cv, mcount, fs.over, fs.over_count, labels, fs.ub, s);
 }
 
 // ------------------------------------------------------------------ update
@@ -1232,12 +1422,17 @@ hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* i
 // the end of the range with the cluster going on in the next wave
 // (part[W][1]); whole clusters are stored to sums. Every value has one
 // writer, so the sums do not depend on scheduling.
+// With ub (by token; may be null) the same walk also takes the largest ub of
+// each run: rad[slot] for whole clusters, part radii beside the part sums.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__ X, int N, RowSet rs,
                                                            const float* __restrict__ inv_norm,
                                                            const int32_t* __restrict__ labels,
                                                            CentView cv,
-                                                           const int32_t* __restrict__ order) {
+                                                           const int32_t* __restrict__ order,
+                                                           const float* __restrict__ ub,
+                                                           float* __restrict__ rad,
+                                                           float* __restrict__ part_rad) {
     constexpr int E = D / 64;
     constexpr int RS = D == 64 ? 64 : 32;          // rows staged at once
     constexpr int LDX = D + 16 / (int)sizeof(T);   // padded row stride (elements)
@@ -1259,6 +1454,7 @@ __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__
     const int lab_l = okr ? lab_h[r] : -1;
     const int tok_l = okr ? (rs.rows ? rs.rows[(int64_t)bh * N + r] : r) : 0;
     const float s_l = (inv_norm && okr) ? inv_norm[(int64_t)bh * N + tok_l] : 1.0f;
+    const float u_l = (ub && okr) ? ub[(int64_t)bh * N + tok_l] : 0.0f;
     const int rows_here = min(64, n - base);
     // labels of the sorted rows just before and just after the range
     const int lab_prev = base > 0 ? lab_h[ord[base - 1]] : -1;
@@ -1271,10 +1467,16 @@ __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__
     for (int e = 0; e < E; ++e) acc[e] = 0.0f;
     int cur = -1;
     bool cur_lead = false;
+    float umax = 0.0f;  // largest ub of the current run (lane 0's copy is used)
     auto flush = [&](bool trail) __attribute__((always_inline)) {
         float* dst = cur_lead ? pw : (trail ? pw + D : cv.sums + (cbase + cur) * D);
 #pragma unroll
         for (int e = 0; e < E; ++e) dst[l + 64 * e] = acc[e];
+        if (ub && l == 0) {
+            float* rd = cur_lead ? part_rad + ((int64_t)bh * cv.nwav + wv) * 2
+                                 : (trail ? part_rad + ((int64_t)bh * cv.nwav + wv) * 2 + 1 : rad + cbase + cur);
+            *rd = umax;
+        }
     };
     for (int h0 = 0; h0 < rows_here; h0 += RS) {
         // chunk c of row q goes to lane (q % RPI) * CPR + c; rows past the end read row 0
@@ -1299,9 +1501,11 @@ __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__
                 if (cur >= 0) flush(false);
                 cur = lab;
                 cur_lead = h0 + q == 0 && lab == lab_prev;
+                umax = 0.0f;
 #pragma unroll
                 for (int e = 0; e < E; ++e) acc[e] = 0.0f;
             }
+            if (ub) umax = fmaxf(umax, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u_l), h0 + q)));
 #pragma unroll
             for (int e = 0; e < E; ++e) acc[e] += s * elem<T>::load(xw, q * LDX + l + 64 * e);
         }
@@ -1314,22 +1518,22 @@ __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__
 
 hipError_t launch_update_accum(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
                                const int32_t* labels, CentView cv, const int32_t* order,
-                               hipStream_t s) {
+                               hipStream_t s, const float* ub, float* rad, float* part_rad) {
     dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)p.BH);
     if (p.bf16) {
         if (p.D == 64)
             hipLaunchKernelGGL((update_accum_kernel<u16, 64>), grid, dim3(256), 0, s, (const u16*)x,
-                               p.N, rs, inv_norm, labels, cv, order);
+                               p.N, rs, inv_norm, labels, cv, order, ub, rad, part_rad);
         else
             hipLaunchKernelGGL((update_accum_kernel<u16, 128>), grid, dim3(256), 0, s,
-                               (const u16*)x, p.N, rs, inv_norm, labels, cv, order);
+                               (const u16*)x, p.N, rs, inv_norm, labels, cv, order, ub, rad, part_rad);
     } else {
         if (p.D == 64)
             hipLaunchKernelGGL((update_accum_kernel<float, 64>), grid, dim3(256), 0, s,
-                               (const float*)x, p.N, rs, inv_norm, labels, cv, order);
+                               (const float*)x, p.N, rs, inv_norm, labels, cv, order, ub, rad, part_rad);
         else
             hipLaunchKernelGGL((update_accum_kernel<float, 128>), grid, dim3(256), 0, s,
-                               (const float*)x, p.N, rs, inv_norm, labels, cv, order);
+                               (const float*)x, p.N, rs, inv_norm, labels, cv, order, ub, rad, part_rad);
     }
     return hipGetLastError();
 }
