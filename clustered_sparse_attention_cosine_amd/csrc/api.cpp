@@ -536,8 +536,7 @@ static int32_t check_sel_dims(const adc_shape* shape, int32_t Cq, int32_t Ck) {
 size_t adacluster_select_workspace(const adc_shape* shape, int32_t Cq, int32_t Ck) {
     if (check_sel_dims(shape, Cq, Ck)) return 0;
     Carver c(nullptr);
-    c.take<float>((size_t)shape->B * shape->H * Cq * Ck);
-    c.take<float>((size_t)shape->B * shape->H * Ck);
+    c.take<uint32_t>((size_t)shape->B * shape->H * Cq * Ck);
     return c.used + 256;
 }
 
@@ -573,15 +572,15 @@ int32_t adacluster_select(const adc_shape* shape, int32_t Cq, int32_t Ck, const 
     hipStream_t s = (hipStream_t)stream;
     Prob p = make_prob(shape);
     Carver c(workspace);
-    float* S = c.take<float>((size_t)p.BH * Cq * Ck);
-    float* ln_sizes = c.take<float>((size_t)p.BH * Ck);
-    HIPCHK(launch_scores(p, Cq, Ck, qrep, kmax, kmin, centroids, score, k_sizes, n_clusters, S, s));
-    if (rule == ADC_SELECT_TOPP)
-        HIPCHK(launch_topp(p, Cq, Ck, S, k_sizes, n_clusters, full_attn, scale, top_p, sel_mask, sel_keys,
-                           ln_sizes, s));
+    // the ranking keys of every (q-cluster, slot) pair; the selection reads them once
+    uint32_t* keys = c.take<uint32_t>((size_t)p.BH * Cq * Ck);
+    const bool topp = rule == ADC_SELECT_TOPP;
+    HIPCHK(launch_scores(p, Cq, Ck, qrep, kmax, kmin, centroids, score, topp, scale, k_sizes, n_clusters, keys,
+                         s));
+    if (topp)
+        HIPCHK(launch_topp(p, Cq, Ck, keys, k_sizes, full_attn, top_p, sel_mask, sel_keys, s));
     else
-        HIPCHK(launch_topk(p, Cq, Ck, S, k_sizes, n_clusters, full_attn, top_k, sel_mask, sel_keys,
-                           ln_sizes, s));
+        HIPCHK(launch_topk(p, Cq, Ck, keys, k_sizes, full_attn, scale, top_k, sel_mask, sel_keys, s));
     if (sel_pairs) HIPCHK(launch_pairs(p, Cq, q_offsets, sel_keys, sel_pairs, s));
     return ADC_OK;
 }

@@ -227,15 +227,14 @@ hipError_t launch_gather_stats(const Prob& p, int M, const int32_t* offsets, con
 
 // ---------------------------------------------------------------- selection (select.hip)
 hipError_t launch_scores(const Prob& p, int Cq, int Ck, const float* qrep, const void* kmax,
-                         const void* kmin, const float* kcent, int score_mode,
-                         const int32_t* k_sizes, const int32_t* n_clusters, float* S,
+                         const void* kmin, const float* kcent, int score_mode, bool logn, float scale,
+                         const int32_t* k_sizes, const int32_t* n_clusters, uint32_t* keys,
                          hipStream_t s);
-hipError_t launch_topp(const Prob& p, int Cq, int Ck, const float* S, const int32_t* k_sizes,
-                       const int32_t* n_clusters, const uint8_t* full, float scale, float top_p,
-                       uint32_t* mask, int32_t* sel_keys, float* ln_sizes, hipStream_t s);
-hipError_t launch_topk(const Prob& p, int Cq, int Ck, const float* S, const int32_t* k_sizes,
-                       const int32_t* n_clusters, const uint8_t* full, int top_k,
-                       uint32_t* mask, int32_t* sel_keys, float* ln_sizes, hipStream_t s);
+hipError_t launch_topp(const Prob& p, int Cq, int Ck, const uint32_t* keys, const int32_t* k_sizes,
+                       const uint8_t* full, float top_p, uint32_t* mask, int32_t* sel_keys, hipStream_t s);
+hipError_t launch_topk(const Prob& p, int Cq, int Ck, const uint32_t* keys, const int32_t* k_sizes,
+                       const uint8_t* full, float scale, int top_k, uint32_t* mask, int32_t* sel_keys,
+                       hipStream_t s);
 
 // pairs[bh] = sum over q-clusters a of (q_offsets[a + 1] - q_offsets[a]) x sel_keys[a].
 hipError_t launch_pairs(const Prob& p, int Cq, const int32_t* q_offsets, const int32_t* sel_keys,

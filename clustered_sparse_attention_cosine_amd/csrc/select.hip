@@ -10,26 +10,41 @@
 // order <= 2 is accumulated, which keeps the scores at about f32 accuracy.
 //
 // Top-p. For each q-cluster row: l_b = S_ab * scale + ln n_b over slots with
-// members; the cut value T (the l of the last selected slot) is found by
-// bisection on the order-preserving integer image of l, using deterministic
-// block sums of exp(l - max l); slots with l above T are selected, slots equal
-// to T are taken in index order until the mass reaches top_p.
+// members; the cut value T (the l of the last selected slot) is the largest l
+// whose mass, the sum of exp(l' - max l) over l' >= l, reaches top_p of the
+// total; slots with l above T are selected, slots equal to T are taken in
+// index order until the mass reaches top_p. Top-k takes the k largest scores
+// by the same rule with unit weights.
 #include <math.h>
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace adc {
 
+// Order-preserving 32-bit image of a float (larger float, larger image;
+// never 0 for a non-NaN value, so 0 can mark a slot without members).
+__device__ __forceinline__ uint32_t order_key(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// inverse of order_key
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 // ------------------------------------------------------------------ scores
 // Grid: (Cq / 64, Ck / 256, BH); 4 waves, each 16 q-clusters x 256 slots.
-template <typename TK, int D, int MODE>  // MODE 0: quest (width 2D), 1: centroid (width D)
+// Output: the order key of what the selection ranks, per (q-cluster, slot):
+// l = S * scale + ln n_b for top-p (LOGN), the score S itself for top-k; 0 for
+// slots without members.
+template <typename TK, int D, int MODE, bool LOGN>  // MODE 0: quest (width 2D), 1: centroid (width D)
 __global__ __launch_bounds__(256) void scores_kernel(int Cq, int Ck, const float* __restrict__ qrep,
                                                      const TK* __restrict__ kmax,
                                                      const TK* __restrict__ kmin,
                                                      const float* __restrict__ kcent,
                                                      const int32_t* __restrict__ k_sizes,
                                                      const int32_t* __restrict__ n_clusters,
-                                                     float* __restrict__ S) {
+                                                     float scale, uint32_t* __restrict__ keys) {
     constexpr int KD = MODE == 0 ? 2 * D : D;
     constexpr int KC = KD / 32;
     constexpr bool AF32 = (MODE == 1) || sizeof(TK) == 4;  // key side needs a split
@@ -131,21 +146,25 @@ __global__ __launch_bounds__(256) void scores_kernel(int Cq, int Ck, const float
             // lane holds slots b0 + cb*16 + 4g + i for q-cluster a: one 16-byte
             // store (and one 16-byte read of the slot sizes) where the four fit
             if (aok) {
-                float* dst = S + ((int64_t)bh * Cq + a) * Ck;
+                uint32_t* dst = keys + ((int64_t)bh * Cq + a) * Ck;
                 const int b = b0 + cb * 16 + g * 4;
                 const int32_t* ksz = k_sizes + (int64_t)bh * Ck;
+                auto key_of = [&](int i, int n) __attribute__((always_inline)) -> uint32_t {
+                    if (b + i >= ncl || n <= 0) return 0u;
+                    return order_key(LOGN ? fmaf(acc[i], scale, logf((float)n)) : acc[i]);
+                };
                 if (b + 3 < Ck && ((reinterpret_cast<uintptr_t>(dst + b) | reinterpret_cast<uintptr_t>(ksz + b)) & 15) == 0) {
                     const int4 ks = *reinterpret_cast<const int4*>(ksz + b);
-                    float4 out;
-                    out.x = (b < ncl && ks.x > 0) ? acc[0] : -INFINITY;
-                    out.y = (b + 1 < ncl && ks.y > 0) ? acc[1] : -INFINITY;
-                    out.z = (b + 2 < ncl && ks.z > 0) ? acc[2] : -INFINITY;
-                    out.w = (b + 3 < ncl && ks.w > 0) ? acc[3] : -INFINITY;
-                    *reinterpret_cast<float4*>(dst + b) = out;
+                    uint4 out;
+                    out.x = key_of(0, ks.x);
+                    out.y = key_of(1, ks.y);
+                    out.z = key_of(2, ks.z);
+                    out.w = key_of(3, ks.w);
+                    *reinterpret_cast<uint4*>(dst + b) = out;
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        if (b + i < Ck) dst[b + i] = (b + i < ncl && ksz[b + i] > 0) ? acc[i] : -INFINITY;
+                        if (b + i < Ck) dst[b + i] = key_of(i, ksz[b + i]);
                     }
                 }
             }
@@ -154,400 +173,470 @@ __global__ __launch_bounds__(256) void scores_kernel(int Cq, int Ck, const float
 }
 
 hipError_t launch_scores(const Prob& p, int Cq, int Ck, const float* qrep, const void* kmax,
-                         const void* kmin, const float* kcent, int score_mode,
-                         const int32_t* k_sizes, const int32_t* n_clusters, float* S,
+                         const void* kmin, const float* kcent, int score_mode, bool logn, float scale,
+                         const int32_t* k_sizes, const int32_t* n_clusters, uint32_t* keys,
                          hipStream_t s) {
     dim3 grid((unsigned)((Cq + 63) / 64), (unsigned)((Ck + 255) / 256), (unsigned)p.BH);
+#define ADC_SCORES(TK, MODE, KMAX, KMIN)                                                              \
+    do {                                                                                            \
+        auto k = p.D == 64 ? (logn ? scores_kernel<TK, 64, MODE, true> : scores_kernel<TK, 64, MODE, false>)   \
+                           : (logn ? scores_kernel<TK, 128, MODE, true> : scores_kernel<TK, 128, MODE, false>); \
+        hipLaunchKernelGGL(k, grid, dim3(256), 0, s, Cq, Ck, qrep, (const TK*)(KMAX), (const TK*)(KMIN),  \
+                           kcent, k_sizes, n_clusters, scale, keys);                                  \
+    } while (0)
     if (score_mode == 0) {
-        if (p.bf16) {
-            auto k = p.D == 64 ? scores_kernel<u16, 64, 0> : scores_kernel<u16, 128, 0>;
-            hipLaunchKernelGGL(k, grid, dim3(256), 0, s, Cq, Ck, qrep, (const u16*)kmax,
-                               (const u16*)kmin, kcent, k_sizes, n_clusters, S);
-        } else {
-            auto k = p.D == 64 ? scores_kernel<float, 64, 0> : scores_kernel<float, 128, 0>;
-            hipLaunchKernelGGL(k, grid, dim3(256), 0, s, Cq, Ck, qrep, (const float*)kmax,
-                               (const float*)kmin, kcent, k_sizes, n_clusters, S);
-        }
+        if (p.bf16)
+            ADC_SCORES(u16, 0, kmax, kmin);
+        else
+            ADC_SCORES(float, 0, kmax, kmin);
     } else {
-        auto k = p.D == 64 ? scores_kernel<float, 64, 1> : scores_kernel<float, 128, 1>;
-        hipLaunchKernelGGL(k, grid, dim3(256), 0, s, Cq, Ck, qrep, (const float*)nullptr,
-                           (const float*)nullptr, kcent, k_sizes, n_clusters, S);
+        ADC_SCORES(float, 1, nullptr, nullptr);
     }
+#undef ADC_SCORES
     return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ block reductions
-// Deterministic: per-thread partial, xor-butterfly inside each wave, then the
-// four wave results added in wave order.
-__device__ __forceinline__ float block_sum4(float v, float* red) {
-    v = wave_sum(v);
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    __syncthreads();
-    if (l == 0) red[w] = v;
-    __syncthreads();
-    return ((red[0] + red[1]) + red[2]) + red[3];
+// ------------------------------------------------------------------ top-p / top-k
+// Wave reductions and scans on DPP row shifts and row broadcasts (no lane
+// index arithmetic, nothing for the compiler to keep in registers). The scan
+// is the inclusive Hillis-Steele sum inside each row of 16 lanes (lanes
+// shifted in from outside the row read 0), then the row totals carried
+// forward by the two row broadcasts; lane 63 ends with the total.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, ROWS == 0xf);
 }
-__device__ __forceinline__ int block_sum4_i(int v, int* red) {
-    v = wave_sum_i(v);
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    __syncthreads();
-    if (l == 0) red[w] = v;
-    __syncthreads();
-    return red[0] + red[1] + red[2] + red[3];
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    return ((uint64_t)dpp_u32<CTRL, ROWS>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL, ROWS>((uint32_t)v);
 }
-__device__ __forceinline__ float block_max4(float v, float* red) {
-    v = wave_max(v);
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    __syncthreads();
-    if (l == 0) red[w] = v;
-    __syncthreads();
-    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+__device__ __forceinline__ uint64_t wave_scan_u64(uint64_t v) {
+    v += dpp_u64<0x111, 0xf>(v);  // row_shr:1
+    v += dpp_u64<0x112, 0xf>(v);  // row_shr:2
+    v += dpp_u64<0x114, 0xf>(v);  // row_shr:4
+    v += dpp_u64<0x118, 0xf>(v);  // row_shr:8
+    v += dpp_u64<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_u64<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
 }
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int lane) {
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), lane) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
 }
-// inverse of order_key
-__device__ __forceinline__ float key_value(uint32_t k) {
-    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) { return lane_u64(wave_scan_u64(v), 63); }
+__device__ __forceinline__ int wave_sum_i32(int v) {
+    v += (int)dpp_u32<0x111, 0xf>((uint32_t)v);
+    v += (int)dpp_u32<0x112, 0xf>((uint32_t)v);
+    v += (int)dpp_u32<0x114, 0xf>((uint32_t)v);
+    v += (int)dpp_u32<0x118, 0xf>((uint32_t)v);
+    v += (int)dpp_u32<0x142, 0xa>((uint32_t)v);
+    v += (int)dpp_u32<0x143, 0xc>((uint32_t)v);
+    return __builtin_amdgcn_readlane(v, 63);
 }
-
-// One workgroup (256 threads) per (head, q-cluster); thread t owns slots
-// 32t .. 32t+31, i.e. mask word t.
-template <bool TOPK>
-__global__ __launch_bounds__(256) void select_kernel(int Cq, int Ck, const float* __restrict__ S,
-                                                     const int32_t* __restrict__ k_sizes,
-                                                     const int32_t* __restrict__ n_clusters,
-                                                     const uint8_t* __restrict__ full, float scale,
-                                                     float top_p, int top_k,
-                                                     uint32_t* __restrict__ mask,
-                                                     int32_t* __restrict__ sel_keys) {
-    __shared__ float redf[4];
-    __shared__ int redi[4];
-    const int a = blockIdx.x, bh = blockIdx.y;
-    const int t = threadIdx.x;
-    const int words = (Ck + 31) / 32;
-    const int ncl = min(n_clusters[bh], Ck);
-    const float* row = S + ((int64_t)bh * Cq + a) * Ck;
-    const int32_t* ks = k_sizes + (int64_t)bh * Ck;
-
-    float lv[32];
-    uint32_t live = 0;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const int b = t * 32 + i;
-        const bool ok = t < words && b < ncl && ks[b] > 0;
-        if (ok) live |= 1u << i;
-        float v = -INFINITY;
-        if (ok) v = TOPK ? row[b] : fmaf(row[b], scale, logf((float)ks[b]));
-        lv[i] = v;
-    }
-    uint32_t selw = 0;
-    const bool take_all = full[bh] || (!TOPK && top_p >= 1.0f);
-    if (take_all) {
-        selw = live;
-    } else {
-        // target: mass (top-p) or count (top-k) the selected set must reach
-        float e[32];
-        float target;
-        if (TOPK) {
-            const int nlive = block_sum4_i(__popc(live), redi);
-            target = (float)min(top_k, nlive);
-#pragma unroll
-            for (int i = 0; i < 32; ++i) e[i] = ((live >> i) & 1) ? 1.0f : 0.0f;
-        } else {
-            float lmax = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < 32; ++i) lmax = fmaxf(lmax, lv[i]);
-            const float mx = block_max4(lmax, redf);
-            float part = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 32; ++i) {
-                e[i] = ((live >> i) & 1) ? __expf(lv[i] - mx) : 0.0f;
-                part += e[i];
-            }
-            const float Z = block_sum4(part, redf);
-            target = top_p * Z;
-        }
-        uint32_t key[32];
-#pragma unroll
-        for (int i = 0; i < 32; ++i) key[i] = ((live >> i) & 1) ? order_key(lv[i]) : 0u;
-        // largest T with mass(key >= T) >= target
-        uint32_t T = 0;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cand = T | (1u << bit);
-            float part = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 32; ++i) part += key[i] >= cand ? e[i] : 0.0f;
-            const float mass = block_sum4(part, redf);
-            if (mass >= target) T = cand;
-        }
-        float above = 0.0f;
-        int nties = 0;
-        float e_tie = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            if (((live >> i) & 1) && key[i] > T) { selw |= 1u << i; above += e[i]; }
-            if (((live >> i) & 1) && key[i] == T) { ++nties; e_tie = e[i]; }
-        }
-        const float mass_above = block_sum4(above, redf);
-        // tied slots share one l, hence one e: take the first k of them in slot order
-        __shared__ float sh_etie;
-        __shared__ int sh_take;
-        __shared__ int wpre[4];
-        if (nties > 0) sh_etie = e_tie;
-        int incl = nties;
-        const int l = t & 63, w = t >> 6;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int v = __shfl_up(incl, o);
-            if (l >= o) incl += v;
-        }
-        if (l == 63) wpre[w] = incl;
-        __syncthreads();
-        int before = incl - nties;
-        for (int i = 0; i < w; ++i) before += wpre[i];
-        const int ties = wpre[0] + wpre[1] + wpre[2] + wpre[3];
-        if (t == 0) {
-            int k = 0;
-            float acc = mass_above;
-            while (k < ties) {
-                acc += sh_etie;
-                ++k;
-                if (acc >= target) break;
-            }
-            sh_take = k;
-        }
-        __syncthreads();
-        const int take = sh_take;
-        int rank = before;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            if (((live >> i) & 1) && key[i] == T) {
-                if (rank < take) selw |= 1u << i;
-                ++rank;
-            }
-        }
-    }
-    int keys = 0;
-#pragma unroll
-    for (int i = 0; i < 32; ++i)
-        if ((selw >> i) & 1) keys += ks[t * 32 + i];
-    const int total = block_sum4_i(keys, redi);
-    if (t < words) mask[((int64_t)bh * Cq + a) * words + t] = selw;
-    if (t == 0) sel_keys[(int64_t)bh * Cq + a] = total;
+// max (unsigned) over the wave: shifted-in zeros are the identity
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<0x111, 0xf>(v));
+    v = max(v, dpp_u32<0x112, 0xf>(v));
+    v = max(v, dpp_u32<0x114, 0xf>(v));
+    v = max(v, dpp_u32<0x118, 0xf>(v));
+    v = max(v, dpp_u32<0x142, 0xa>(v));
+    v = max(v, dpp_u32<0x143, 0xc>(v));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// One wave per (head, q-cluster) row for Ck <= 64 * SPL: lane j owns slots
-// j + 64 i (i < SPL), so the slots of a mask word pair come out of one ballot.
-// The same rule as select_kernel, with wave-level fixed-order sums (no
-// workgroup barriers in the bisection); the last 16 of its 32 steps run over
-// the few slots that can still move the cut.
-// ln n_b of every slot with members (slots past the head's count or with no
-// members: -inf), once per head instead of once per row.
-__global__ __launch_bounds__(256) void ln_sizes_kernel(int Ck, const int32_t* __restrict__ k_sizes,
-                                                       const int32_t* __restrict__ n_clusters,
-                                                       float* __restrict__ ln_sizes) {
+// Selection by a mass histogram. A workgroup of W waves, W = ceil(Ck / 1024),
+// takes the rows (q-clusters) a = blockIdx.x + gridDim.x j of head blockIdx.y
+// one after another: thread t owns slots t + 64 W i (i < 16), so it holds 16
+// keys of a row in registers (and the sizes of its slots, the same for every
+// row of the head), each of the workgroup's loads of a row is contiguous, and
+// the next row's keys are loaded while the current one is worked on.
+//
+// Weights are fixed point: e_b = exp(l_b - max l) as an integer multiple of
+// 2^-31 (top-k: e_b = 1), so every mass below is an exact integer sum and the
+// result does not depend on the order of the additions. The rule is the one
+// stated above: T = the largest order key with mass(key >= T) >= target,
+// target = top_p * Z (top-k: min(k, live slots)); keys above T are selected,
+// keys equal to T in slot order until the mass reaches the target.
+//
+// 1. The live slots go into SEL_NB buckets by (max l - l) * width (the last
+//    bucket takes everything further down), their weights summed per bucket
+//    with LDS atomics (exact: integers).
+// 2. Each wave scans the histogram for the cut bucket: the first whose
+//    cumulative mass reaches the target. Buckets are monotone in l, so every
+//    key of an earlier bucket is above every key of the cut bucket.
+// 3. The cut bucket's slots (a few dozen, usually) are gathered in LDS; lane j
+//    takes the j-th and sums the weights of the gathered keys >= its own,
+//    which gives T directly. A cut bucket with more than SEL_LIST slots (many
+//    keys within one bucket width) is settled by bisection over the 32-bit
+//    images instead, with the same integer masses.
+constexpr int SEL_NB = 1024;
+constexpr int SEL_LIST = 64;
+constexpr int SEL_KPL = 16;         // keys per thread
+constexpr float SEL_WIDTH = 64.0f;  // buckets per unit of l
+
+__device__ __forceinline__ uint32_t sel_weight(float v, float mx) {
+    // exp(v - mx) in (0, 1] times 2^31, truncated (fits 32 bits)
+    return (uint32_t)(__expf(v - mx) * 2147483648.0f);
+}
+__device__ __forceinline__ int sel_bucket(float v, float mx, float width) {
+    const float x = (mx - v) * width;  // >= 0, monotone in v; NaN (no key) -> last
+    return x < (float)(SEL_NB - 1) ? (int)x : SEL_NB - 1;
+}
+
+template <bool TOPK, int W>
+__global__ __launch_bounds__(64 * W) void select_hist_kernel(int Cq, int Ck, const uint32_t* __restrict__ K,
+                                                             const int32_t* __restrict__ k_sizes,
+                                                             const uint8_t* __restrict__ full, float scale,
+                                                             float top_p, int top_k,
+                                                             uint32_t* __restrict__ mask,
+                                                             int32_t* __restrict__ sel_keys) {
+    constexpr int NT = 64 * W;
+    // histogram plus one spare counter per thread: the last bucket and the
+    // slots without members go to the thread's spare, so no lane contends for
+    // them; the spares are summed as the last bucket. Bucket k sits at
+    // k + k / 16: lane l's 16 buckets in the scan are then 17 words apart, not
+    // 16 (which put every lane on the same two banks).
+    constexpr int HB = SEL_NB + SEL_NB / 16;  // padded buckets; spares follow
+    __shared__ uint64_t H[HB + NT];
+    __shared__ uint32_t LK[W][SEL_LIST];  // per wave: the cut bucket's keys,
+    __shared__ uint32_t LE[W][SEL_LIST];  // weights
+    __shared__ uint32_t LS[W][SEL_LIST];  // and slots, in the wave's slot order
+    __shared__ uint64_t red64[2][W];
+    __shared__ uint32_t redu[W];
+    __shared__ int redi[W];
+    __shared__ int redk[W];
+    __shared__ int tcnt[W][SEL_KPL];
+    __shared__ uint64_t mw[W][SEL_KPL];  // per wave: the mask ballots of a row
+    __shared__ int sh_tie;
     const int bh = blockIdx.y;
-    const int b = blockIdx.x * 256 + threadIdx.x;
-    if (b >= Ck) return;
-    const int n = b < min(n_clusters[bh], Ck) ? k_sizes[(int64_t)bh * Ck + b] : 0;
-    ln_sizes[(int64_t)bh * Ck + b] = n > 0 ? logf((float)n) : -INFINITY;
-}
-
-template <bool TOPK, int SPL>
-__global__ __launch_bounds__(256) void select_wave_kernel(int Cq, int Ck, const float* __restrict__ S,
-                                                          const float* __restrict__ ln_sizes,
-                                                          const int32_t* __restrict__ k_sizes,
-                                                          const int32_t* __restrict__ n_clusters,
-                                                          const uint8_t* __restrict__ full, float scale,
-                                                          float top_p, int top_k,
-                                                          uint32_t* __restrict__ mask,
-                                                          int32_t* __restrict__ sel_keys) {
-    __shared__ uint32_t bin_key[4][64];
-    __shared__ float bin_e[4][64];
-    const int bh = blockIdx.y;
-    const int l = threadIdx.x & 63;
-    const int a = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (a >= Cq) return;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int words = (Ck + 31) / 32;
-    const float* row = S + ((int64_t)bh * Cq + a) * Ck;
-    const float* lns = ln_sizes + (int64_t)bh * Ck;
-    const int32_t* ks = k_sizes + (int64_t)bh * Ck;
-
-    // keys (order-preserving integer images of l) are kept; l is recovered from
-    // them, so a lane holds SPL keys and SPL weights
-    uint32_t key[SPL];
-    uint64_t live = 0;
-    float lmax = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < SPL; ++i) {
-        const int b = l + 64 * i;
-        const float ln = b < Ck ? lns[b] : -INFINITY;
-        const bool ok = ln > -INFINITY;
-        if (ok) live |= 1ull << i;
-        float v = -INFINITY;
-        if (ok) v = TOPK ? row[b] : fmaf(row[b], scale, ln);
-        lmax = fmaxf(lmax, v);
-        key[i] = ok ? order_key(v) : 0u;
-    }
-    uint64_t sel = 0;
+    // top-k orders by the score itself and buckets by score * scale
+    const float width = TOPK ? SEL_WIDTH * scale : SEL_WIDTH;
     const bool take_all = full[bh] || (!TOPK && top_p >= 1.0f);
-    if (take_all) {
-        sel = live;
-    } else {
-        float e[SPL];
-        float target;
+    // Rows and sizes are read through buffer resources of one row (Ck words):
+    // a slot past Ck reads 0 (no key, no members) without any per-slot test,
+    // and the per-slot offsets are scalars, so no address registers are held.
+    auto row_rsrc = [&](int r) __attribute__((always_inline)) {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(K + ((int64_t)bh * Cq + r) * Ck), (short)0, Ck * 4,
+                                                 0x00020000);
+    };
+    int ksz[SEL_KPL];
+    uint32_t nxt[SEL_KPL];
+    {
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)(k_sizes + (int64_t)bh * Ck), (short)0, Ck * 4,
+                                                          0x00020000);
+        const auto rk = row_rsrc(min((int)blockIdx.x, Cq - 1));
+#pragma unroll
+        for (int i = 0; i < SEL_KPL; ++i) {
+            ksz[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, tid * 4, NT * i * 4, 0);
+            nxt[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, tid * 4, NT * i * 4, 0);
+        }
+    }
+    for (int a = blockIdx.x; a < Cq; a += gridDim.x) {
+    // thread indices hidden from the compiler per row, so that what derives
+    // from them (slot numbers, LDS addresses, lane masks) is recomputed per row
+    // instead of held in registers across the loop
+    int tr = tid;
+    asm volatile("" : "+v"(tr));
+    const int lr = tr & 63;
+    const uint64_t below_r = lr == 0 ? 0ull : (~0ull >> (64 - lr));
+    // order keys of lr (0: no members, never selected)
+    uint32_t key[SEL_KPL];
+    uint32_t kmx = 0u;
+    int nlive = 0;
+#pragma unroll
+    for (int i = 0; i < SEL_KPL; ++i) {
+        key[i] = nxt[i];
+        kmx = max(kmx, key[i]);
+        nlive += key[i] != 0u;
+    }
+    if (a + (int)gridDim.x < Cq) {
+        // the next row's keys, in flight while this row is worked on
+        const auto rk = row_rsrc(a + gridDim.x);
+#pragma unroll
+        for (int i = 0; i < SEL_KPL; ++i) nxt[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, tr * 4, NT * i * 4, 0);
+    }
+    for (int j = tr; j < HB + NT; j += NT) H[j] = 0ull;
+    kmx = wave_max_u32(kmx);
+    nlive = wave_sum_i32(nlive);
+    if (lr == 0) {
+        redu[w] = kmx;
+        redi[w] = nlive;
+    }
+    __syncthreads();
+    kmx = redu[0];
+    nlive = redi[0];
+#pragma unroll
+    for (int v = 1; v < W; ++v) {
+        kmx = max(kmx, redu[v]);
+        nlive += redi[v];
+    }
+    const float mx = kmx ? key_value(kmx) : -INFINITY;
+
+    // selected: key > T, or key == T in a slot up to last_tie
+    uint32_t T = 1u;  // every live key is > 1: all of them
+    int last_tie = -1;
+    if (!(take_all || kmx == 0u)) {
+        uint64_t zp = 0;
+#pragma unroll
+        for (int i = 0; i < SEL_KPL; ++i) {
+            const bool lv = key[i] != 0u;
+            const float v = key_value(key[i]);
+            const uint32_t e = lv ? (TOPK ? 1u : sel_weight(v, mx)) : 0u;
+            const int bk = sel_bucket(v, mx, width);
+            zp += e;
+            atomicAdd(reinterpret_cast<unsigned long long*>(&H[(lv && bk < SEL_NB - 1) ? bk + (bk >> 4) : HB + tr]),
+                      (unsigned long long)e);
+        }
+        zp = wave_sum_u64(zp);
+        if (lr == 0) red64[0][w] = zp;
+        __syncthreads();
+        uint64_t Z = 0, tail = 0;
+#pragma unroll
+        for (int v = 0; v < W; ++v) {
+            Z += red64[0][v];
+            tail += H[HB + 64 * v + lr];
+        }
+        tail = wave_sum_u64(tail);
+        uint64_t tq;
         if (TOPK) {
-            const int nlive = wave_sum_i(__popcll(live));
-            target = (float)min(top_k, nlive);
-#pragma unroll
-            for (int i = 0; i < SPL; ++i) e[i] = ((live >> i) & 1) ? 1.0f : 0.0f;
+            tq = (uint64_t)min(top_k, nlive);
         } else {
-            const float mx = wave_max(lmax);
-            float part = 0.0f;
-#pragma unroll
-            for (int i = 0; i < SPL; ++i) {
-                e[i] = ((live >> i) & 1) ? __expf(key_value(key[i]) - mx) : 0.0f;
-                part += e[i];
-            }
-            target = top_p * wave_sum_dpp(part);
+            tq = (uint64_t)ceil((double)top_p * (double)Z);
+            tq = max(tq, (uint64_t)1);
         }
-        // largest T with mass(key >= T) >= target: the top 16 bits by bisection
-        // over every owned slot, then the low 16 bits over the slots whose top
-        // bits equal T's (few: keys within 2^-7 relative of the cut), gathered
-        // into a per-wave list in LDS
-        uint32_t T = 0;
-        for (int bit = 31; bit >= 16; --bit) {
-            const uint32_t cand = T | (1u << bit);
-            float part = 0.0f;
+        // cut bucket (every wave alike): lane lr holds buckets 16 lr .. 16 lr + 15
+        constexpr int PB = SEL_NB / 64;
+        auto hval = [&](int j) __attribute__((always_inline)) -> uint64_t {
+            const int bk = lr * PB + j;
+            return bk == SEL_NB - 1 ? tail : H[bk + (bk >> 4)];
+        };
+        uint64_t part = 0;
 #pragma unroll
-            for (int i = 0; i < SPL; ++i) part += key[i] >= cand ? e[i] : 0.0f;
-            if (wave_sum_dpp(part) >= target) T = cand;
-        }
-        {
-            const uint32_t hi = T >> 16;
-            float part_hi = 0.0f;
-            int nb = 0;
-            uint32_t* lk = bin_key[threadIdx.x >> 6];
-            float* le = bin_e[threadIdx.x >> 6];
-            const uint64_t below = l == 0 ? 0ull : (~0ull >> (64 - l));
+        for (int j = 0; j < PB; ++j) part += hval(j);
+        uint64_t c = wave_scan_u64(part) - part;
+        int cut = SEL_NB;
+        uint64_t before = 0;
 #pragma unroll
-            for (int i = 0; i < SPL; ++i) {
-                const bool lv = (live >> i) & 1;
-                part_hi += (lv && (key[i] >> 16) > hi) ? e[i] : 0.0f;
-                const bool in = lv && (key[i] >> 16) == hi;
-                const uint64_t m = __ballot(in);
-                const int pos = nb + __popcll(m & below);
-                if (in && pos < 64) {
-                    lk[pos] = key[i];
-                    le[pos] = e[i];
-                }
-                nb += __popcll(m);
+        for (int j = 0; j < PB; ++j) {
+            const uint64_t hj = hval(j);
+            if (cut == SEL_NB && c + hj >= tq) {
+                cut = lr * PB + j;
+                before = c;
             }
-            const float mass_hi = wave_sum_dpp(part_hi);
-            if (nb <= 64) {
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                const uint32_t mk = l < nb ? lk[l] : 0u;
-                const float me = l < nb ? le[l] : 0.0f;
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                for (int bit = 15; bit >= 0; --bit) {
-                    const uint32_t cand = T | (1u << bit);
-                    if (mass_hi + wave_sum_dpp(mk >= cand ? me : 0.0f) >= target) T = cand;
+            c += hj;
+        }
+        // the first lane with a cut (the totals reach Z >= tq, so one has)
+        const uint64_t has_cut = __ballot(cut < SEL_NB);
+        const int cl = (int)__ffsll((unsigned long long)has_cut) - 1;
+        cut = __builtin_amdgcn_readlane(cut, cl);
+        const uint64_t above = lane_u64(before, cl);
+
+        // gather the cut bucket per wave, in the wave's slot order
+        int nw = 0;
+#pragma unroll
+        for (int i = 0; i < SEL_KPL; ++i) {
+            const float v = key_value(key[i]);
+            const bool in = key[i] != 0u && sel_bucket(v, mx, width) == cut;
+            const uint64_t m = __ballot(in);
+            const int pos = nw + __popcll(m & below_r);
+            if (in && pos < SEL_LIST) {
+                LK[w][pos] = key[i];
+                LE[w][pos] = TOPK ? 1u : sel_weight(v, mx);
+                LS[w][pos] = (uint32_t)(tr + NT * i);
+            }
+            nw += __popcll(m);
+        }
+        if (lr == 0) redi[w] = nw;
+        __syncthreads();
+        int n = 0;
+        int nv[W];
+#pragma unroll
+        for (int v = 0; v < W; ++v) {
+            nv[v] = redi[v];
+            n += nv[v];
+        }
+        uint64_t gt;    // mass of the keys above T
+        uint64_t take;  // ties of T to take
+        if (n <= SEL_LIST) {
+            // lane j takes entry j of the waves' lists one after another
+            // (every wave alike)
+            uint32_t kj = 0u, ej = 0u, sj = 0u;
+            {
+                int off = 0;
+#pragma unroll
+                for (int v = 0; v < W; ++v) {
+                    if (lr >= off && lr < off + nv[v]) {
+                        kj = LK[v][lr - off];
+                        ej = LE[v][lr - off];
+                        sj = LS[v][lr - off];
+                    }
+                    off += nv[v];
                 }
+            }
+            const bool has = lr < n;
+            uint64_t M = 0;  // weight of the gathered keys >= kj
+#pragma unroll
+            for (int v = 0; v < W; ++v)
+                for (int p = 0; p < nv[v]; ++p) M += LK[v][p] >= kj ? (uint64_t)LE[v][p] : 0ull;
+            T = wave_max_u32((has && above + M >= tq) ? kj : 0u);
+            gt = above + wave_sum_u64((has && kj > T) ? (uint64_t)ej : 0ull);
+            const uint64_t eT = TOPK ? 1ull : (uint64_t)sel_weight(key_value(T), mx);
+            take = eT > 0 ? (tq - gt + eT - 1) / eT : ~0ull;
+            // the take-th tie by slot: its rank among the ties is take - 1
+            int rank = 0;
+#pragma unroll
+            for (int v = 0; v < W; ++v)
+                for (int p = 0; p < nv[v]; ++p) rank += (LK[v][p] == T && LS[v][p] < sj) ? 1 : 0;
+            const bool tie = has && kj == T;
+            const uint64_t ntie = __popcll(__ballot(tie));
+            if (take >= ntie) last_tie = Ck;
+            else last_tie = (int)wave_max_u32((tie && (uint64_t)rank == take - 1) ? sj + 1 : 0u) - 1;
+        } else {
+            // bisection: the largest T whose mass (buckets above + the cut
+            // bucket's keys >= T) reaches tq; T lies in the cut bucket
+            T = 0u;
+#pragma unroll 1
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t cand = T | (1u << bit);
+                uint64_t mp = 0;
+#pragma unroll
+                for (int i = 0; i < SEL_KPL; ++i) {
+                    const float v = key_value(key[i]);
+                    const bool in = key[i] >= cand && sel_bucket(v, mx, width) == cut;
+                    mp += in ? (TOPK ? 1u : sel_weight(v, mx)) : 0u;
+                }
+                mp = wave_sum_u64(mp);
+                const int buf = bit & 1;  // alternate buffers: one barrier per step
+                if (lr == 0) red64[buf][w] = mp;
+                __syncthreads();
+                uint64_t m = 0;
+#pragma unroll
+                for (int v = 0; v < W; ++v) m += red64[buf][v];
+                if (above + m >= tq) T = cand;
+            }
+            uint64_t gp = 0;
+#pragma unroll
+            for (int i = 0; i < SEL_KPL; ++i) {
+                const float v = key_value(key[i]);
+                const bool in = key[i] > T && sel_bucket(v, mx, width) == cut;
+                gp += in ? (TOPK ? 1u : sel_weight(v, mx)) : 0u;
+            }
+            gp = wave_sum_u64(gp);
+            // tie counts per (wave, block) for the last tie taken
+#pragma unroll
+            for (int i = 0; i < SEL_KPL; ++i) {
+                const int c2 = __popcll(__ballot(key[i] == T));
+                if (lr == 0) tcnt[w][i] = c2;
+            }
+            __syncthreads();  // every wave has read red64[1] of the last step
+            if (lr == 0) red64[1][w] = gp;
+            __syncthreads();
+            gt = above;
+#pragma unroll
+            for (int v = 0; v < W; ++v) gt += red64[1][v];
+            const uint64_t eT = TOPK ? 1ull : (uint64_t)sel_weight(key_value(T), mx);
+            take = eT > 0 ? (tq - gt + eT - 1) / eT : ~0ull;
+            // slot order: block i, then wave, then lane
+            uint64_t seen = 0;
+            int fi = -1, fw = -1;
+            uint64_t r = 0;
+            for (int i = 0; i < SEL_KPL && fi < 0; ++i)
+                for (int v = 0; v < W && fi < 0; ++v) {
+                    const uint64_t c2 = (uint64_t)tcnt[v][i];
+                    if (seen + c2 >= take) {
+                        fi = i;
+                        fw = v;
+                        r = take - seen;
+                    }
+                    seen += c2;
+                }
+            if (fi < 0) {
+                last_tie = Ck;  // fewer ties than take: all of them
             } else {
-                for (int bit = 15; bit >= 0; --bit) {
-                    const uint32_t cand = T | (1u << bit);
-                    float part = 0.0f;
+                if (w == fw) {
+                    // the r-th tie of this wave's block fi
+                    uint64_t mm = 0;
 #pragma unroll
-                    for (int i = 0; i < SPL; ++i) part += key[i] >= cand ? e[i] : 0.0f;
-                    if (wave_sum_dpp(part) >= target) T = cand;
+                    for (int i = 0; i < SEL_KPL; ++i) {
+                        const uint64_t bb = __ballot(key[i] == T);
+                        if (i == fi) mm = bb;
+                    }
+                    for (uint64_t q = r; q > 1; --q) mm &= mm - 1;
+                    if (lr == 0) sh_tie = NT * fi + 64 * fw + (int)__ffsll((unsigned long long)mm) - 1;
                 }
+                __syncthreads();
+                last_tie = sh_tie;
             }
-        }
-        float above = 0.0f, e_tie = 0.0f;
-        int nties = 0;
-#pragma unroll
-        for (int i = 0; i < SPL; ++i) {
-            if (((live >> i) & 1) && key[i] > T) { sel |= 1ull << i; above += e[i]; }
-            if (((live >> i) & 1) && key[i] == T) { ++nties; e_tie = e[i]; }
-        }
-        const float mass_above = wave_sum_dpp(above);
-        const int ties = wave_sum_i(nties);
-        // tied slots share one l, hence one e: take the first k of them in slot order
-        const uint64_t has = __ballot(nties > 0);
-        const float et = has ? __shfl(e_tie, __ffsll((unsigned long long)has) - 1) : 0.0f;
-        int take = 0;
-        {
-            float acc = mass_above;
-            while (take < ties) {
-                acc += et;
-                ++take;
-                if (acc >= target) break;
-            }
-        }
-        int before = 0;  // ties in slots before block i
-        const uint64_t below = l == 0 ? 0ull : (~0ull >> (64 - l));
-#pragma unroll
-        for (int i = 0; i < SPL; ++i) {
-            const bool tie = ((live >> i) & 1) && key[i] == T;
-            const uint64_t tb = __ballot(tie);
-            if (tie && before + __popcll(tb & below) < take) sel |= 1ull << i;
-            before += __popcll(tb);
         }
     }
+    // mark: key > T, or key == T up to the last tie taken. Wave w's ballot over
+    // block i is mask word 2 W i + 2 w + h (half h): staged in LDS, then lane
+    // 2 i + h stores it.
     int keys = 0;
 #pragma unroll
-    for (int i = 0; i < SPL; ++i) {
-        const bool si = (sel >> i) & 1;
-        if (si) keys += ks[l + 64 * i];
+    for (int i = 0; i < SEL_KPL; ++i) {
+        const int b = tr + NT * i;
+        const bool si = key[i] > T || (key[i] == T && b <= last_tie);
+        keys += si ? ksz[i] : 0;
         const uint64_t wb = __ballot(si);
-        const int wd = 2 * i + (l & 1);
-        if (l < 2 && wd < words)
-            mask[((int64_t)bh * Cq + a) * words + wd] = (uint32_t)(l ? (wb >> 32) : wb);
+        if (lr == 0) mw[w][i] = wb;
     }
-    const int total = wave_sum_i(keys);
-    if (l == 0) sel_keys[(int64_t)bh * Cq + a] = total;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lr < 2 * SEL_KPL) {
+        const int wd = 2 * W * (lr >> 1) + 2 * w + (lr & 1);
+        if (wd < words) mask[((int64_t)bh * Cq + a) * words + wd] = reinterpret_cast<const uint32_t*>(mw[w])[lr];
+    }
+    keys = wave_sum_i32(keys);
+    if (lr == 0) redk[w] = keys;
+    // also the end of every use of this row's shared data
+    __syncthreads();
+    if (tr == 0) {
+        int total = 0;
+#pragma unroll
+        for (int v = 0; v < W; ++v) total += redk[v];
+        sel_keys[(int64_t)bh * Cq + a] = total;
+    }
+    }
 }
 
 template <bool TOPK>
-static void launch_select_t(const Prob& p, int Cq, int Ck, const float* S, const int32_t* k_sizes,
-                            const int32_t* n_clusters, const uint8_t* full, float scale,
-                            float top_p, int top_k, uint32_t* mask, int32_t* sel_keys,
-                            float* ln_sizes, hipStream_t s) {
-    const dim3 wgrid((unsigned)((Cq + 3) / 4), (unsigned)p.BH);
-    if (Ck <= 4096)
-        hipLaunchKernelGGL(ln_sizes_kernel, dim3((unsigned)((Ck + 255) / 256), (unsigned)p.BH), dim3(256), 0,
-                           s, Ck, k_sizes, n_clusters, ln_sizes);
-    if (Ck <= 1024)
-        hipLaunchKernelGGL((select_wave_kernel<TOPK, 16>), wgrid, dim3(256), 0, s, Cq, Ck, S, ln_sizes,
-                           k_sizes, n_clusters, full, scale, top_p, top_k, mask, sel_keys);
-    else if (Ck <= 4096)
-        hipLaunchKernelGGL((select_wave_kernel<TOPK, 64>), wgrid, dim3(256), 0, s, Cq, Ck, S, ln_sizes,
-                           k_sizes, n_clusters, full, scale, top_p, top_k, mask, sel_keys);
+static void launch_select_t(const Prob& p, int Cq, int Ck, const uint32_t* keys, const int32_t* k_sizes,
+                            const uint8_t* full, float scale, float top_p, int top_k, uint32_t* mask,
+                            int32_t* sel_keys, hipStream_t s) {
+    const int W = (Ck + 64 * SEL_KPL - 1) / (64 * SEL_KPL);
+    // about 3072 / W workgroups of W waves (three waves per SIMD over the
+    // chip, what the registers allow), each over a strided share of one
+    // head's rows
+    const int per_head = max(1, min(Cq, (3072 / W + p.BH - 1) / p.BH));
+    const dim3 grid((unsigned)per_head, (unsigned)p.BH);
+#define ADC_SEL(WW)                                                                                     \
+    hipLaunchKernelGGL((select_hist_kernel<TOPK, WW>), grid, dim3(64 * WW), 0, s, Cq, Ck, keys, k_sizes, \
+                       full, scale, top_p, top_k, mask, sel_keys)
+    if (W <= 1)
+        ADC_SEL(1);
+    else if (W <= 2)
+        ADC_SEL(2);
+    else if (W <= 4)
+        ADC_SEL(4);
     else
-        hipLaunchKernelGGL(select_kernel<TOPK>, dim3((unsigned)Cq, (unsigned)p.BH), dim3(256), 0, s,
-                           Cq, Ck, S, k_sizes, n_clusters, full, scale, top_p, top_k, mask, sel_keys);
+        ADC_SEL(8);
+#undef ADC_SEL
 }
 
-hipError_t launch_topp(const Prob& p, int Cq, int Ck, const float* S, const int32_t* k_sizes,
-                       const int32_t* n_clusters, const uint8_t* full, float scale, float top_p,
-                       uint32_t* mask, int32_t* sel_keys, float* ln_sizes, hipStream_t s) {
-    launch_select_t<false>(p, Cq, Ck, S, k_sizes, n_clusters, full, scale, top_p, 0, mask, sel_keys,
-                           ln_sizes, s);
+hipError_t launch_topp(const Prob& p, int Cq, int Ck, const uint32_t* keys, const int32_t* k_sizes,
+                       const uint8_t* full, float top_p, uint32_t* mask, int32_t* sel_keys, hipStream_t s) {
+    launch_select_t<false>(p, Cq, Ck, keys, k_sizes, full, 1.0f, top_p, 0, mask, sel_keys, s);
     return hipGetLastError();
 }
 
-hipError_t launch_topk(const Prob& p, int Cq, int Ck, const float* S, const int32_t* k_sizes,
-                       const int32_t* n_clusters, const uint8_t* full, int top_k, uint32_t* mask,
-                       int32_t* sel_keys, float* ln_sizes, hipStream_t s) {
-    launch_select_t<true>(p, Cq, Ck, S, k_sizes, n_clusters, full, 1.0f, 1.0f, top_k, mask, sel_keys,
-                          ln_sizes, s);
+hipError_t launch_topk(const Prob& p, int Cq, int Ck, const uint32_t* keys, const int32_t* k_sizes,
+                       const uint8_t* full, float scale, int top_k, uint32_t* mask, int32_t* sel_keys,
+                       hipStream_t s) {
+    launch_select_t<true>(p, Cq, Ck, keys, k_sizes, full, scale, 1.0f, top_k, mask, sel_keys, s);
     return hipGetLastError();
 }
 
