@@ -167,6 +167,10 @@ void plan_kmeans(Carver& c, const Prob& p, int cap, bool want_inv, bool kpp, boo
 struct StageWs {
     StageState st{};
     int32_t* labels_u = nullptr;
+    // stage 0: the labels of every key and the keys sorted by them, kept for the
+    // pruned final assignment
+    int32_t* lab0 = nullptr;
+    int32_t* perm0 = nullptr;
 };
 
 void plan_stages(Carver& c, const Prob& p, StageWs& w) {
@@ -181,6 +185,8 @@ void plan_stages(Carver& c, const Prob& p, StageWs& w) {
     w.st.u_b = c.take<int32_t>(bhn);
     w.st.dist = c.take<double>(bhn);
     w.labels_u = c.take<int32_t>(bhn);
+    w.lab0 = c.take<int32_t>(bhn);
+    w.perm0 = c.take<int32_t>(bhn);
 }
 
 FlagSet flags_of(const KmeansWs& w) {
@@ -223,10 +229,14 @@ struct SortScratch {
 // test): from the second round on, only rows whose bounds no longer prove
 // their label are assigned again; the others keep it, which the exact
 // assignment would too. snap (may be null, [BH][cap][D]) receives the centres
-// of view cv as they are just before the last assignment.
+// of view cv as they are just before the last assignment. With final_radii
+// (every row, final_update) the last update also leaves each cluster's radius
+// and drift for candidate sets of a later pruned assignment, and ss.perm holds
+// the rows sorted by the last labels.
 hipError_t lloyd(const Prob& p, const void* x, int normalize, RowSet rs, const float* inv_norm,
                  CentView cv, int iters, bool final_update, int32_t* labels, const KmeansWs& w,
-                 hipStream_t s, const int32_t* mcount, const SortScratch& ss, float* snap = nullptr) {
+                 hipStream_t s, const int32_t* mcount, const SortScratch& ss, float* snap = nullptr,
+                 bool final_radii = false) {
     hipError_t e;
     const bool bounds = !rs.rows;
     FlagSet fs = flags_of(w);
@@ -260,14 +270,15 @@ hipError_t lloyd(const Prob& p, const void* x, int normalize, RowSet rs, const f
         if (it + 1 < iters || final_update) {
             // the next round's candidate sets need each cluster's radius (the
             // largest upper bound of its rows), taken by the same sorted walk
-            const bool radii = bounds && g_prune && it + 1 < iters;
+            const bool keep = it + 1 < iters || final_radii;  // bounds move on
+            const bool radii = bounds && g_prune && keep;
             if ((e = launch_counting_sort(p, labels, cv.m, w.seg_cnt, w.hist, ss.sizes, ss.offsets, ss.perm,
                                           s, rs.nrows, rs.active)))
                 return e;
             if ((e = launch_update_accum(p, x, rs, inv_norm, labels, cv, ss.perm, s, radii ? w.ub : nullptr,
                                          w.rad, w.part_rad)))
                 return e;
-            if (bounds && it + 1 < iters) {
+            if (bounds && keep) {
                 if ((e = launch_finalize(p, cv, rs.active, ss.offsets, s, w.drift, w.flag_count, w.over_count,
                                          w.rcount, radii ? w.rad : nullptr, w.part_rad)))
                     return e;
@@ -470,10 +481,14 @@ static int32_t cluster_k_impl(const adc_shape* shape, const adc_k_params* prm, c
             CentView cv = make_view(centroids, w, nmax, base, mt);
             HIPCHK(init_centres(p, k, 0, rs, cv, prm->init, nullptr, prm->seed, TENSOR_K, (uint32_t)t, w, s));
             HIPCHK(launch_finalize(p, cv, S.active, nullptr, s));
-            HIPCHK(lloyd(p, k, 0, rs, nullptr, cv, prm->iters, true, sw.labels_u, w, s, nullptr, ss,
-                         tr ? tr->last_centroids : nullptr));
-            if (tr) HIPCHK(launch_trace_stage(p, rs, sw.labels_u, base, t, tr->stage_labels, tr->stage_base, s));
-            HIPCHK(launch_stage_dist(p, k, rs, sw.labels_u, cv, S.dist, s));
+            // stage 0 (every key) keeps its labels, its row order and its radii for
+            // the pruned final assignment
+            int32_t* lab = t == 0 ? sw.lab0 : sw.labels_u;
+            const SortScratch ss_t{sizes, offsets, t == 0 ? sw.perm0 : perm};
+            HIPCHK(lloyd(p, k, 0, rs, nullptr, cv, prm->iters, true, lab, w, s, nullptr, ss_t,
+                         tr ? tr->last_centroids : nullptr, t == 0 && g_prune));
+            if (tr) HIPCHK(launch_trace_stage(p, rs, lab, base, t, tr->stage_labels, tr->stage_base, s));
+            HIPCHK(launch_stage_dist(p, k, rs, lab, cv, S.dist, s));
             if (t == 0) HIPCHK(launch_stage_tau(p, S, (double)prm->tau_mult, s));
             HIPCHK(launch_stage_compact(p, S, t == 0 ? nullptr : u_cur, u_next, mt, s));
             std::swap(u_cur, u_next);
@@ -492,7 +507,20 @@ static int32_t cluster_k_impl(const adc_shape* shape, const adc_k_params* prm, c
         // slots after the last one holding a centre (the unfilled end of the last
         // stage) are left out of the contraction
         HIPCHK(launch_last_valid(p, cvf, n_clusters, w.m_eff, s));
-        HIPCHK(launch_assign(p, k, all, nullptr, 0, cvf, w.m_eff, assign, flags_of(w), s));
+        if (g_prune) {
+            // pruned: every key is within its stage-0 cluster's radius of that
+            // centre, so only the slots within twice the radius can be nearer
+            // (Elkan's lemma); the keys go in the order of their stage-0 labels
+            HIPCHK(launch_cand_bits(p, cvf, w.m_eff, w.rad, w.drift, w.cbits, w.cwords, s, m0));
+            CentView cg = cvf;
+            cg.cbits = w.cbits;
+            cg.cwords = w.cwords;
+            cg.glab = sw.lab0;
+            HIPCHK(launch_assign(p, k, RowSet{sw.perm0, nullptr, nullptr, 1}, nullptr, 0, cg, w.m_eff, assign,
+                                 flags_of(w), s));
+        } else {
+            HIPCHK(launch_assign(p, k, all, nullptr, 0, cvf, w.m_eff, assign, flags_of(w), s));
+        }
     }
     HIPCHK(launch_counting_sort(p, assign, nmax, w.seg_cnt, w.hist, sizes, offsets, perm, s));
     HIPCHK(launch_gather_stats(p, nmax, offsets, perm, k, v, 0, centroids, nullptr, kmax, kmin,

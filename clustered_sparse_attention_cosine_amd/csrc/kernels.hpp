@@ -55,8 +55,13 @@ struct CentView {
     // centre of a row now labelled a.
     const uint32_t* cbits = nullptr;
     int cwords = 0;
+    // labels the pruned assignment gathers by (may be null: the labels it
+    // writes, read before they are overwritten)
+    const int32_t* glab = nullptr;
 };
-constexpr int UCAP = 512;   // candidate slots a pruned workgroup gathers
+// candidate slots a pruned workgroup gathers (an index list of 16-bit slots in LDS)
+template <int D>
+constexpr int ucap() { return D == 64 ? 1024 : 4096; }
 
 // Rows a k-means call clusters: rows[bh*N + r] for r < nrows[bh] (NULL: all N
 // rows, identity), only for heads with active[bh] != 0 (NULL: all heads).
@@ -132,9 +137,10 @@ hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* i
 // a centre with ||c_j - c_a|| <= 2 R (up to a rounding margin taken in the
 // safe direction), as bits of cbits [BH][cv.cap][cwords]. A row of a is
 // strictly closer to c_a than to any slot left out, so its nearest centre,
-// ties included, is in the set.
+// ties included, is in the set. Sets are formed for the slots a < am (am < 0:
+// every slot of the view), over every slot of the view.
 hipError_t launch_cand_bits(const Prob& p, CentView cv, const int32_t* mcount, const float* rad,
-                            const float* drift, uint32_t* cbits, int cwords, hipStream_t s);
+                            const float* drift, uint32_t* cbits, int cwords, hipStream_t s, int am = -1);
 // Bound test between Lloyd rounds (every row, rs.rows NULL): a row whose bound on
 // its own centre, grown by that centre's drift, stays below its bound on every
 // other centre, shrunk by the largest drift, keeps its label and the moved

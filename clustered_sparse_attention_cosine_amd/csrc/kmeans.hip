@@ -567,7 +567,7 @@ template <int D>
 __global__ __launch_bounds__(256) void cand_bits_kernel(CentView cv, const int32_t* __restrict__ mcount,
                                                         const float* __restrict__ rad,
                                                         const float* __restrict__ drift,
-                                                        uint32_t* __restrict__ cbits, int cwords) {
+                                                        uint32_t* __restrict__ cbits, int cwords, int am) {
     constexpr int KC = D / 32;
     constexpr int LD = D + 8;
     __shared__ __attribute__((aligned(16))) u16 sh_hi[64 * LD];
@@ -576,11 +576,12 @@ __global__ __launch_bounds__(256) void cand_bits_kernel(CentView cv, const int32
     const int bh = blockIdx.y;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c16 = l & 15;
     const int M = mcount ? min(mcount[bh], cv.m) : cv.m;
+    const int MA = min(M, am);  // slots that get a set
     const int a0 = blockIdx.x * 64;
-    if (a0 >= M) return;  // no row carries these labels
+    if (a0 >= MA) return;  // no row carries these labels
     const int64_t sbase = (int64_t)bh * cv.cap + cv.base;
     const int a = a0 + w * 16 + c16;
-    const int ac = min(a, M - 1);
+    const int ac = min(a, MA - 1);
     bf16x8 ah[KC], al[KC];
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
@@ -589,7 +590,7 @@ __global__ __launch_bounds__(256) void cand_bits_kernel(CentView cv, const int32
     }
     const float na2 = cv.cn2[sbase + ac];
     float lim = -INFINITY;  // no set for slots without a centre or past the count
-    if (a < M && na2 < INFINITY) {
+    if (a < MA && na2 < INFINITY) {
         const float R = (rad[sbase + a] + (drift ? drift[sbase + a] : 0.0f)) * (1.0f + 0x1.0p-20f);
         lim = 4.0f * R * R * (1.0f + 0x1.0p-12f);
     }
@@ -632,17 +633,19 @@ __global__ __launch_bounds__(256) void cand_bits_kernel(CentView cv, const int32
             bits[h] |= __shfl_xor(bits[h], 32);
         }
         const int wd = (j0 >> 5) + (g & 1);
-        if (g < 2 && a < M && wd < cwords) cbits[(sbase + a) * cwords + wd] = bits[g & 1];
+        if (g < 2 && a < MA && wd < cwords) cbits[(sbase + a) * cwords + wd] = bits[g & 1];
     }
 }
 
 hipError_t launch_cand_bits(const Prob& p, CentView cv, const int32_t* mcount, const float* rad,
-                            const float* drift, uint32_t* cbits, int cwords, hipStream_t s) {
-    dim3 grid((unsigned)((cv.m + 63) / 64), (unsigned)p.BH);
+                            const float* drift, uint32_t* cbits, int cwords, hipStream_t s, int am) {
+    if (am < 0 || am > cv.m) am = cv.m;
+    if (am == 0) return hipSuccess;
+    dim3 grid((unsigned)((am + 63) / 64), (unsigned)p.BH);
     if (p.D == 64)
-        hipLaunchKernelGGL(cand_bits_kernel<64>, grid, dim3(256), 0, s, cv, mcount, rad, drift, cbits, cwords);
+        hipLaunchKernelGGL(cand_bits_kernel<64>, grid, dim3(256), 0, s, cv, mcount, rad, drift, cbits, cwords, am);
     else
-        hipLaunchKernelGGL(cand_bits_kernel<128>, grid, dim3(256), 0, s, cv, mcount, rad, drift, cbits, cwords);
+        hipLaunchKernelGGL(cand_bits_kernel<128>, grid, dim3(256), 0, s, cv, mcount, rad, drift, cbits, cwords, am);
     return hipGetLastError();
 }
 
@@ -887,7 +890,8 @@ void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
     __shared__ __attribute__((aligned(16))) u16 sh_lo[2][64 * LD];
     __shared__ float sh_c2[2][64];
     __shared__ float sh_red[2][4];
-    __shared__ int ulist[GATHER ? UCAP : 1];
+    constexpr int UCAP = ucap<D>();
+    __shared__ uint16_t ulist[GATHER ? UCAP : 1];
 
     const int bh = blockIdx.y;
     if (rs.active && !rs.active[bh]) return;
@@ -966,8 +970,9 @@ void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
         uint32_t* bits = reinterpret_cast<uint32_t*>(&sh_hi[1][0]);  // free until the first tile swap
         const int nwords = (M + 31) / 32;
         const int last = min(row_base + 255, n - 1);
-        const int a0 = labels[(int64_t)bh * N + rs.rows[(int64_t)bh * N + row_base]];
-        const int a1 = labels[(int64_t)bh * N + rs.rows[(int64_t)bh * N + last]];
+        const int32_t* gl = cv.glab ? cv.glab : labels;
+        const int a0 = gl[(int64_t)bh * N + rs.rows[(int64_t)bh * N + row_base]];
+        const int a1 = gl[(int64_t)bh * N + rs.rows[(int64_t)bh * N + last]];
         const int64_t sbase = (int64_t)bh * cv.cap + cv.base;
         for (int i = tid; i < nwords; i += 256) {
             uint32_t word = 0u;
@@ -998,7 +1003,7 @@ void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
             while (wd) {
                 const int b = __ffs(wd) - 1;
                 wd &= wd - 1;
-                if (before < UCAP) ulist[before] = wi * 32 + b;
+                if (before < UCAP) ulist[before] = (uint16_t)(wi * 32 + b);
                 ++before;
             }
             total += tot;
