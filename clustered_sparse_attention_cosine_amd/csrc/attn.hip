@@ -455,12 +455,23 @@ __device__ __forceinline__ int tile_rows(int lane, int t0, int total, int R, int
 // K/V tiles in LDS. A tile is 64 key rows of NP 16-bit planes of K, then NP of
 // V, each plane row-major with unpadded rows of RB = 2 D bytes; the 16-byte
 // chunks of row r are stored XOR-swizzled (logical chunk c at physical chunk
-// c ^ (r & 7)) so that the column reads of the fragments below spread over
-// the banks. Tiles are copied from global memory straight into LDS by the
+// c ^ tile_swz<D>(r)) so that the column reads of the fragments below spread
+// over the banks. With 128-byte rows (D = 64) the row parity already splits
+// the banks and the XOR is r & 7; with 256-byte rows every row starts on the
+// same bank, and the transposing V reads (four rows, two 16-byte chunks and
+// both 8-byte halves per 16 lanes) need the 8 chunk pairs they touch to be
+// distinct, which 2 (r & 7) gives and r & 7 does not (it maps two rows onto
+// one pair: measured as LDS bank conflicts on every V read of the D = 128
+// kernel). Tiles are copied from global memory straight into LDS by the
 // 16-byte global->LDS loads: one wave instruction fills 1 KB of a plane, lane
 // j the j-th 16 bytes, so the swizzle is applied by choosing which global
 // chunk each lane fetches. NB tiles are in flight (the copy of tile t + NB - 1
 // is issued while tile t is computed).
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+    return D == 64 ? (r & 7) : 2 * (r & 7);
+}
+
 template <int D, int NP, int NT>
 struct TileGeom {
     static constexpr int RB = 2 * D;                    // bytes per row of a plane
@@ -493,7 +504,7 @@ __device__ __forceinline__ void tile_copy(unsigned char* buf, int w, int lane, c
         const int blk = w * G::IPW + i;
         const int off = blk * 1024 + 16 * lane;
         const int r = off / G::RB;
-        const int lc = ((off % G::RB) / 16) ^ (r & 7);
+        const int lc = ((off % G::RB) / 16) ^ tile_swz<D>(r);
         const int64_t goff = (int64_t)max(krow[r], 0) * D + lc * 8;
         unsigned char* dst = buf + blk * 1024;
         __builtin_amdgcn_global_load_lds(K0 + goff, (lds_void*)dst, 16, 0, 0);
@@ -701,12 +712,12 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
     // 16 db + 4a .. + 3)
     int koff[KC], voff[DB];
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) koff[kc] = c16 * RB + 16 * ((4 * kc + g) ^ (c16 & 7));
+    for (int kc = 0; kc < KC; ++kc) koff[kc] = c16 * RB + 16 * ((4 * kc + g) ^ tile_swz<D>(c16));
     {
         const int rv = 4 * g + ((l & 15) >> 2);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-            voff[db] = rv * RB + 16 * ((2 * db + ((l & 3) >> 1)) ^ (rv & 7)) + (l & 1) * 8;
+            voff[db] = rv * RB + 16 * ((2 * db + ((l & 3) >> 1)) ^ tile_swz<D>(rv)) + (l & 1) * 8;
     }
 
     // Run lookups read the run list from LDS (copied once here; a list longer
