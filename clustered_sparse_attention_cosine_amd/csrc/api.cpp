@@ -692,7 +692,7 @@ static int32_t sparse_attn_impl(const adc_shape* shape, int32_t Cq, int32_t Ck, 
     AttnWs w;
     plan_attn(c, shape, Cq, Ck, w);
     HIPCHK(launch_build_runs(p, Cq, Ck, k_offsets, sel_mask, w.run_cap, w.run_start, w.run_pos, w.n_runs, s));
-    HIPCHK(launch_worklist(p, Cq, w.cap, q_offsets, w.run_pos, w.n_runs, w.run_cap, w.sched, s));
+    HIPCHK(launch_worklist(p, Cq, w.cap, q_offsets, w.run_start, w.run_pos, w.n_runs, w.run_cap, w.sched, s));
     HIPCHK(launch_planes(p, k_perm, v_perm, w.planes[0], w.planes[1], w.planes[2], w.planes[3], w.vmax, s));
     const uint16_t* k0 = p.bf16 ? (const uint16_t*)k_perm : w.planes[0];
     HIPCHK(launch_attention(p, Cq, q, q_perm, q_offsets, k0, w.planes[1], w.planes[2], w.planes[3],

@@ -125,10 +125,13 @@ hipError_t launch_build_runs(const Prob& p, int Cq, int Ck, const int32_t* k_off
 }
 
 // ------------------------------------------------------------------ work list
-// Work items (q-cluster a, chunk c of ATTN_ROWS rows) of head bh are written in
-// q-cluster order to items[bh * cap ...] (cap = Cq + ceil(N / ATTN_ROWS) bounds
-// their number), one workgroup per head, with the inclusive prefix of their
-// estimated cost within the head. An item's cost is its number of 64-key tiles
+// Work items (q-cluster a, chunk c of ATTN_ROWS rows) of head bh are written to
+// items[bh * cap ...] (cap = Cq + ceil(N / ATTN_ROWS) bounds their number), one
+// workgroup per head, with the inclusive prefix of their estimated cost within
+// the head. The q-clusters go in the order of the middle key of their selection
+// (the key row at half of the selected keys, K being slot-ordered): items that
+// run at the same time on one XCD then read nearby key tiles, which its L2
+// can share. Ties keep q-cluster order. An item's cost is its number of 64-key tiles
 // times (4 + its live waves): the time per tile of a work item grows by about a
 // quarter of its 4-wave value per 16-row wave of query rows (measured on
 // uniform synthetic layouts).
@@ -136,8 +139,11 @@ __device__ __forceinline__ uint32_t item_cost(int tiles, int rows) {
     return (uint32_t)tiles * (uint32_t)(4 + (min(rows, ATTN_ROWS) + 15) / 16);
 }
 
+constexpr int WL_SORT = 8192;  // q-clusters a head can have (the slot capacity)
+
 __global__ __launch_bounds__(256) void worklist_kernel(int Cq, int cap,
                                                        const int32_t* __restrict__ q_offsets,
+                                                       const int32_t* __restrict__ run_start,
                                                        const int32_t* __restrict__ run_pos,
                                                        const int32_t* __restrict__ n_runs,
                                                        int run_cap, int32_t* __restrict__ items,
@@ -146,15 +152,60 @@ __global__ __launch_bounds__(256) void worklist_kernel(int Cq, int cap,
                                                        uint32_t* __restrict__ n_cost) {
     __shared__ int wsum[4];
     __shared__ uint32_t wcost[4];
+    __shared__ uint64_t order[WL_SORT];
     const int bh = blockIdx.x;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int32_t* qo = q_offsets + (int64_t)bh * (Cq + 1);
     int32_t* out = items + (int64_t)bh * cap;
     uint32_t* cout = cost_pre + (int64_t)bh * cap;
+    // sort keys: (middle key row of the selection, q-cluster); q-clusters with
+    // no selection sort first (they make no items)
+    int np2 = 1;
+    while (np2 < Cq) np2 <<= 1;
+    for (int a = tid; a < np2; a += 256) {
+        uint64_t key = ~0ull;  // padding sorts last
+        if (a < Cq) {
+            const int64_t row = (int64_t)bh * Cq + a;
+            const int R = n_runs[row];
+            const int32_t* rp = run_pos + row * (run_cap + 1);
+            const int total = rp[R];
+            uint32_t mid = 0;
+            if (total > 0) {
+                // the run holding position total / 2: largest r with rp[r] <= total / 2
+                const int half = total / 2;
+                int lo = 0, hi = R - 1;
+                while (lo < hi) {
+                    const int m = (lo + hi + 1) >> 1;
+                    if (rp[m] <= half) lo = m; else hi = m - 1;
+                }
+                mid = (uint32_t)(run_start[row * run_cap + lo] + (half - rp[lo]));
+            }
+            key = ((uint64_t)mid << 32) | (uint32_t)a;
+        }
+        order[a] = key;
+    }
+    __syncthreads();
+    // bitonic sort of np2 keys in LDS
+    for (int k = 2; k <= np2; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < np2; i += 256) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const uint64_t x = order[i], y = order[ixj];
+                    const bool up = (i & k) == 0;
+                    if ((x > y) == up) {
+                        order[i] = y;
+                        order[ixj] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
     int running = 0;
     uint32_t running_cost = 0;
     for (int base = 0; base < Cq; base += 256) {
-        const int a = base + tid;
+        const int a = base + tid < Cq ? (int)(uint32_t)order[base + tid] : Cq;
         const int rows = a < Cq ? qo[a + 1] - qo[a] : 0;
         const int ch = (rows + ATTN_ROWS - 1) / ATTN_ROWS;
         int tiles = 0;
@@ -291,10 +342,11 @@ __global__ __launch_bounds__(64) void xcd_split_kernel(int BH, int cap, const in
 }
 
 hipError_t launch_worklist(const Prob& p, int Cq, int cap, const int32_t* q_offsets,
-                           const int32_t* run_pos, const int32_t* n_runs, int run_cap,
-                           const AttnSched& sc, hipStream_t s) {
+                           const int32_t* run_start, const int32_t* run_pos, const int32_t* n_runs,
+                           int run_cap, const AttnSched& sc, hipStream_t s) {
+    if (Cq > WL_SORT) return hipErrorInvalidValue;
     hipLaunchKernelGGL(worklist_kernel, dim3((unsigned)p.BH), dim3(256), 0, s, Cq, cap, q_offsets,
-                       run_pos, n_runs, run_cap, sc.items, sc.n_items, sc.cost_pre, sc.n_cost);
+                       run_start, run_pos, n_runs, run_cap, sc.items, sc.n_items, sc.cost_pre, sc.n_cost);
     hipLaunchKernelGGL(head_scan_kernel, dim3(1), dim3(1024), 0, s, p.BH, sc.n_items, sc.n_cost,
                        sc.head_pos, sc.head_cost);
     hipLaunchKernelGGL(xcd_split_kernel, dim3(1), dim3(64), 0, s, p.BH, cap, sc.head_pos, sc.head_cost,

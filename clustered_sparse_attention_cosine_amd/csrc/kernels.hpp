@@ -264,8 +264,8 @@ struct AttnSched {
     int32_t* xcd_ctr;    // [8] items taken from each stretch
 };
 hipError_t launch_worklist(const Prob& p, int Cq, int cap, const int32_t* q_offsets,
-                           const int32_t* run_pos, const int32_t* n_runs, int run_cap,
-                           const AttnSched& sc, hipStream_t s);
+                           const int32_t* run_start, const int32_t* run_pos, const int32_t* n_runs,
+                           int run_cap, const AttnSched& sc, hipStream_t s);
 // Operand planes of the attention kernel. bf16: V' to fp16 scaled per head by
 // a power of two (vmax [BH] receives each head's largest |v| as bf16 bits);
 // f32: K' and V' split into bf16 hi/lo planes (vmax unused).
