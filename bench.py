@@ -155,7 +155,23 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        log(json.dumps(dict(ms_per_step=ms, stages_ms=stage_ms, calib_copy_bytes=CALIB_BYTES)))
+        # shapes of the timed layer's assignment passes, for counter summaries:
+        # rows, centres per query/key stage-0 round, and the final key
+        # assignment's slots (every slot up to the last one holding a centre)
+        ss = K["stage_sizes"].cpu().numpy().reshape(-1, 8)
+        meff = []
+        for row in ss:
+            base, t, last = 0, 0, 0
+            while base < nmax and t < 8 and row[t] > 0:
+                mt = min(w.k_base if t == 0 else w.k_base << (t - 1), nmax - base)
+                last = base + min(mt, int(row[t]))
+                base += mt
+                t += 1
+            meff.append(last)
+        log(json.dumps(dict(ms_per_step=ms, stages_ms=stage_ms, calib_copy_bytes=CALIB_BYTES,
+                            shapes=dict(rows=w.B * w.H * w.N, D=w.D, q_clusters=w.q_clusters,
+                                        k_base=w.k_base, iters=w.iters,
+                                        k_final_slots_mean=float(np.mean(meff))))))
         return
 
     result = {
