@@ -360,7 +360,16 @@ __global__ __launch_bounds__(KPP_THREADS) void init_kmeanspp_kernel(const T* __r
                 __syncthreads();
                 if (tid == 0) {
                     cstart[c] = run;
-                    for (int i = 0; i < cn; ++i) run += chunk[i];
+                    // in row order; the LDS reads go out 16 at a time ahead of the adds
+                    int i = 0;
+                    for (; i + 16 <= cn; i += 16) {
+                        double v[16];
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) v[j] = chunk[i + j];
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) run += v[j];
+                    }
+                    for (; i < cn; ++i) run += chunk[i];
                 }
                 __syncthreads();
             }
@@ -396,9 +405,35 @@ __global__ __launch_bounds__(KPP_THREADS) void init_kmeanspp_kernel(const T* __r
                     if (tid == 0) {
                         double r = cstart[cc];
                         int64_t idx = n - 1;
-                        for (int i = 0; i < cn; ++i) {
+                        bool found = false;
+                        int i = 0;
+                        // blocks of 16: the running sums of the block (the same
+                        // additions in the same order), then its first one above u
+                        for (; i + 16 <= cn; i += 16) {
+                            double v[16], pr[16];
+#pragma unroll
+                            for (int j = 0; j < 16; ++j) v[j] = chunk[i + j];
+#pragma unroll
+                            for (int j = 0; j < 16; ++j) {
+                                r += v[j];
+                                pr[j] = r;
+                            }
+                            int hit = -1;
+#pragma unroll
+                            for (int j = 15; j >= 0; --j)
+                                if (pr[j] > u) hit = j;
+                            if (hit >= 0) {
+                                idx = c0 + i + hit;
+                                found = true;
+                                break;
+                            }
+                        }
+                        for (; i < cn && !found; ++i) {
                             r += chunk[i];
-                            if (r > u) { idx = c0 + i; break; }
+                            if (r > u) {
+                                idx = c0 + i;
+                                found = true;
+                            }
                         }
                         sh_idx = idx;
                     }
