@@ -234,6 +234,10 @@ int32_t adacluster_cluster_k_trace(const adc_shape* shape, const adc_k_params* p
  * (ties to the lower b) whose softmax mass reaches top_p, at least one slot.
  * TOPK: the top_k largest S_ab (ties to the lower b).
  * Heads with full_attn = 1, and top_p >= 1, select every slot with members.
+ * Precision: the softmax weights exp(l_b - max l) are taken in f32 and
+ * truncated to multiples of 2^-31; masses are their exact integer sums, so a
+ * cut whose mass is within about 1e-6 of top_p may differ from an exact
+ * real-number evaluation by one slot.
  *   qrep       [B,H,Cq,D] f32          kmax, kmin [B,H,Ck,D] dtype (QUEST)
  *   q_offsets  [B,H,Cq+1] int32 (the query clustering's offsets; needed only
  *              for sel_pairs, else may be NULL)
