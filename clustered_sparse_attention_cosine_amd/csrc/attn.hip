@@ -677,6 +677,7 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
     using TG = TileGeom<D, NP, NT>;
     constexpr int RB = TG::RB;
     constexpr int NB = TG::NB;
+    constexpr bool LATE_COPY = D == 128;
     // one array per buffer, always indexed by a compile-time buffer number, so
     // the compiler's wait analysis sees that a copy into one buffer does not
     // touch the buffer being read
@@ -797,10 +798,9 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
     if constexpr (NB > 3)
         tile_copy<D, NP, NT>(buf(std::integral_constant<int, 2>{}), w, l, krow[2], Kh0, Kh1, Vh0, Vh1);
 
-    // Scores, softmax and P.V of the tile in buffer tb (first position p0).
-    auto compute = [&](const unsigned char* tb, int p0, bool first) __attribute__((always_inline)) {
-        constexpr int NKB = 4;
-        f32x4 sc[NKB];
+    // Scores of the tile in buffer tb, then its softmax and P.V (first position p0).
+    constexpr int NKB = 4;
+    auto scores = [&](const unsigned char* tb, f32x4 (&sc)[NKB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -816,6 +816,8 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
                 sc[kb] = mfma16(ka, qf[0][kc], sc[kb]);
             }
         }
+    };
+    auto finish = [&](const unsigned char* tb, f32x4 (&sc)[NKB], int p0, bool first) __attribute__((always_inline)) {
         softmax_tile<DB, NKB>(sc, sl2, total - p0 - 4 * g, p0 + 64 > total, first, m_run, thr, o);
 #pragma unroll
         for (int h = 0; h < NKB / 2; ++h) {
@@ -879,9 +881,18 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
         constexpr int J = decltype(j_c)::value;
         tiles_ready_barrier<TG::L * (NB - 2)>();
         if (w == LW) lookup(t + NB);
+        const bool act = t < ntiles && live;
+        f32x4 sc[NKB];
+        // D = 128: the score fragments are read before the key rows of the
+        // copy, so the two LDS latencies overlap (measured 4 % faster on
+        // 32.8K tokens; at D = 64 the later copy issue cost 2 %)
+        if (LATE_COPY && act) scores(buf(j_c), sc);
         tile_copy<D, NP, NT>(buf(std::integral_constant<int, J + NB - 1>{}), w, l,
                              krow[(t + NB - 1) & 3], Kh0, Kh1, Vh0, Vh1);
-        if (t < ntiles && live) compute(buf(j_c), t * 64, t == 0);
+        if (act) {
+            if (!LATE_COPY) scores(buf(j_c), sc);
+            finish(buf(j_c), sc, t * 64, t == 0);
+        }
     };
     for (int t = 0; t < ntiles; t += NB) {
         step(t, std::integral_constant<int, 0>{});
