@@ -58,24 +58,19 @@ __global__ __launch_bounds__(256) void scores_kernel(int Cq, int Ck, const float
     const bool aok = a < Cq;
     const int ncl = min(n_clusters[bh], Ck);
 
-    // query side: 3-term split of [q+, q-] (or q)
+    // query side: 3-term split of [q+, q-] (or q); each 8-wide chunk lies in
+    // one half of the width, read as two 16-byte loads
     bf16x8 qb[3][KC];
     const float* qp = qrep + ((int64_t)bh * Cq + (aok ? a : 0)) * D;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
+        const int k0 = kc * 32 + g * 8;
         float v[8];
+        load8<float>(qp + (k0 < D ? k0 : k0 - D), v);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int k = kc * 32 + g * 8 + i;
-            float x = 0.0f;
-            if (aok) {
-                if (MODE == 0) {
-                    const float qv = qp[k < D ? k : k - D];
-                    x = k < D ? fmaxf(qv, 0.0f) : fminf(qv, 0.0f);
-                } else {
-                    x = qp[k];
-                }
-            }
+            float x = aok ? v[i] : 0.0f;
+            if (MODE == 0) x = k0 < D ? fmaxf(x, 0.0f) : fminf(x, 0.0f);
             v[i] = x;
         }
         float r1[8], r2[8];
@@ -88,39 +83,59 @@ __global__ __launch_bounds__(256) void scores_kernel(int Cq, int Ck, const float
         qb[2][kc] = pack_bf16x8(r2);
     }
 
+    // per staged slot: ln n (top-p) or 0 (top-k), NaN for a slot without members
+    __shared__ float lgn[64];
+    const int32_t* ksz = k_sizes + (int64_t)bh * Ck;
     for (int tile = 0; tile < 4; ++tile) {
         const int b0 = blockIdx.y * 256 + tile * 64;
         if (b0 >= Ck) break;
         __syncthreads();
-        // stage 64 slots x KD of the key side (KA terms)
+        if (tid < 64) {
+            const int b = b0 + tid;
+            const int n = b < Ck ? ksz[b] : 0;
+            lgn[tid] = (b < ncl && n > 0) ? (LOGN ? logf((float)n) : 0.0f) : __builtin_nanf("");
+        }
+        // stage 64 slots x KD of the key side (KA terms); bf16 statistics are
+        // copied as they are
         for (int c = tid; c < 64 * (KD / 8); c += 256) {
             const int row = c / (KD / 8), col8 = c % (KD / 8);
             const int b = b0 + row;
-            float v[8];
-            if (b < Ck) {
-                const int k0 = col8 * 8;
-                const int64_t base = ((int64_t)bh * Ck + b) * D;
-                if (MODE == 0) {
+            if constexpr (MODE == 0 && KA == 1) {
+                uint4 r = make_uint4(0u, 0u, 0u, 0u);
+                if (b < Ck) {
+                    const int k0 = col8 * 8;
+                    const int64_t base = ((int64_t)bh * Ck + b) * D;
                     const TK* src = k0 < D ? kmax + base + k0 : kmin + base + (k0 - D);
-                    load8<TK>(src, v);
-                } else {
-                    load8<float>(kcent + base + k0, v);
+                    r = *reinterpret_cast<const uint4*>(src);
                 }
+                *reinterpret_cast<uint4*>(&sa[0][row * LD + col8 * 8]) = r;
             } else {
+                float v[8];
+                if (b < Ck) {
+                    const int k0 = col8 * 8;
+                    const int64_t base = ((int64_t)bh * Ck + b) * D;
+                    if (MODE == 0) {
+                        const TK* src = k0 < D ? kmax + base + k0 : kmin + base + (k0 - D);
+                        load8<TK>(src, v);
+                    } else {
+                        load8<float>(kcent + base + k0, v);
+                    }
+                } else {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-            }
-            bf16x8 t0 = pack_bf16x8(v);
-            *reinterpret_cast<bf16x8*>(&sa[0][row * LD + col8 * 8]) = t0;
-            if constexpr (KA == 3) {
-                float r1[8], r2[8];
+                    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+                }
+                bf16x8 t0 = pack_bf16x8(v);
+                *reinterpret_cast<bf16x8*>(&sa[0][row * LD + col8 * 8]) = t0;
+                if constexpr (KA == 3) {
+                    float r1[8], r2[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) r1[i] = v[i] - bf2f(t0[i]);
-                bf16x8 t1 = pack_bf16x8(r1);
+                    for (int i = 0; i < 8; ++i) r1[i] = v[i] - bf2f(t0[i]);
+                    bf16x8 t1 = pack_bf16x8(r1);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) r2[i] = r1[i] - bf2f(t1[i]);
-                *reinterpret_cast<bf16x8*>(&sa[1][row * LD + col8 * 8]) = t1;
-                *reinterpret_cast<bf16x8*>(&sa[KA - 1][row * LD + col8 * 8]) = pack_bf16x8(r2);
+                    for (int i = 0; i < 8; ++i) r2[i] = r1[i] - bf2f(t1[i]);
+                    *reinterpret_cast<bf16x8*>(&sa[1][row * LD + col8 * 8]) = t1;
+                    *reinterpret_cast<bf16x8*>(&sa[KA - 1][row * LD + col8 * 8]) = pack_bf16x8(r2);
+                }
             }
         }
         __syncthreads();
@@ -148,23 +163,23 @@ __global__ __launch_bounds__(256) void scores_kernel(int Cq, int Ck, const float
             if (aok) {
                 uint32_t* dst = keys + ((int64_t)bh * Cq + a) * Ck;
                 const int b = b0 + cb * 16 + g * 4;
-                const int32_t* ksz = k_sizes + (int64_t)bh * Ck;
-                auto key_of = [&](int i, int n) __attribute__((always_inline)) -> uint32_t {
-                    if (b + i >= ncl || n <= 0) return 0u;
-                    return order_key(LOGN ? fmaf(acc[i], scale, logf((float)n)) : acc[i]);
+                const float4 lg4 = *reinterpret_cast<const float4*>(&lgn[cb * 16 + g * 4]);
+                const float lg[4] = {lg4.x, lg4.y, lg4.z, lg4.w};
+                auto key_of = [&](int i) __attribute__((always_inline)) -> uint32_t {
+                    if (lg[i] != lg[i]) return 0u;
+                    return order_key(LOGN ? fmaf(acc[i], scale, lg[i]) : acc[i]);
                 };
-                if (b + 3 < Ck && ((reinterpret_cast<uintptr_t>(dst + b) | reinterpret_cast<uintptr_t>(ksz + b)) & 15) == 0) {
-                    const int4 ks = *reinterpret_cast<const int4*>(ksz + b);
+                if (b + 3 < Ck && (reinterpret_cast<uintptr_t>(dst + b) & 15) == 0) {
                     uint4 out;
-                    out.x = key_of(0, ks.x);
-                    out.y = key_of(1, ks.y);
-                    out.z = key_of(2, ks.z);
-                    out.w = key_of(3, ks.w);
+                    out.x = key_of(0);
+                    out.y = key_of(1);
+                    out.z = key_of(2);
+                    out.w = key_of(3);
                     *reinterpret_cast<uint4*>(dst + b) = out;
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        if (b + i < Ck) dst[b + i] = key_of(i, ksz[b + i]);
+                        if (b + i < Ck) dst[b + i] = key_of(i);
                     }
                 }
             }
@@ -309,7 +324,7 @@ __global__ __launch_bounds__(64 * W) void select_hist_kernel(int Cq, int Ck, con
     __shared__ uint64_t mw[W][SEL_KPL];  // per wave: the mask ballots of a row
     __shared__ int sh_tie;
     const int bh = blockIdx.y;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int tid = threadIdx.x, w = tid >> 6;
     const int words = (Ck + 31) / 32;
     // top-k orders by the score itself and buckets by score * scale
     const float width = TOPK ? SEL_WIDTH * scale : SEL_WIDTH;
