@@ -79,6 +79,8 @@ def main():
                     help="skip the other workloads (a few layers each)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured GEMM and copy ceilings")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-captured layer (LayerGraph replays)")
     ap.add_argument("--cpu-heads", default=None,
                     help="heads the oracle baseline runs: 'all', or a comma list (default: 4 spread heads)")
     ap.add_argument("--profile-steps", action="store_true",
@@ -207,6 +209,9 @@ def main():
         "stage_rooflines": stage_rooflines(w.name),
     }
 
+    if not args.no_graph:
+        result["graph"] = graph_replay(torch, adc, q, k, v, cfg, out, args.steps, dense_flops)
+
     if not args.no_dense:
         result["dense"] = dense_compare(torch, adc, q, k, v, w, dev, stream)
 
@@ -240,6 +245,27 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, g, args.seed, heads)
 
     print(json.dumps(result), flush=True)
+
+
+def graph_replay(torch, adc, q, k, v, cfg, eager_out, steps, dense_flops):
+    """The same layer captured once in a HIP graph (LayerGraph) and replayed
+    `steps` times on the same inputs: wall time per replay, and whether the
+    replays' output equals the eager layer's bit for bit."""
+    lg = adc.LayerGraph(q, k, v, cfg)
+    lg.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        out, _, _ = lg.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    same = bool(torch.equal(out, eager_out))
+    del lg
+    torch.cuda.empty_cache()
+    log(f"graph replay {ms:.3f} ms per layer, same output as eager: {same}")
+    return {"layer_ms": round(ms, 4), "dense_equiv_tflops": round(dense_flops / (ms * 1e-3) / 1e12, 3),
+            "same_output_as_eager": same, "steps": steps,
+            "note": "every kernel of the layer recorded once (LayerGraph), one graph launch per layer"}
 
 
 def measured_traffic(workload):

@@ -450,3 +450,39 @@ def layer(q, k, v, cfg: LayerConfig, prev=None):
     out, lse = sparse_attn(q, Q["perm"], Q["offsets"], K["k_perm"], K["v_perm"], K["offsets"],
                            S["mask"])
     return out, lse, dict(Q=Q, K=K, S=S)
+
+
+class LayerGraph:
+    """One layer (Algorithm 3, cold form) captured once in a HIP graph and
+    replayed. The capture records every kernel of both clusterings (the query
+    clustering on the side stream, joined back), the selection and the
+    attention, about 270 launches at 75.6K tokens, so a replay is one graph
+    launch; no kernel of the path issues a memory-set node (buffers are cleared
+    by fill kernels) and none synchronizes with the host.
+
+    q, k and v are the graph's input buffers: write the next step's inputs into
+    them in place (same shapes, dtypes and device) before replay(). Each replay
+    writes the same output tensors (out, lse and the state dict), so copy what
+    must outlive the next replay. The workspace of every call is held by the
+    graph's memory pool for the graph's lifetime."""
+
+    def __init__(self, q, k, v, cfg: LayerConfig, warmup: int = 2):
+        self.q, self.k, self.v, self.cfg = q, k, v, cfg
+        main = torch.cuda.current_stream(q.device)
+        # warm-up calls outside the capture: library load, side stream, allocator
+        s = torch.cuda.Stream(device=q.device)
+        s.wait_stream(main)
+        with torch.cuda.stream(s):
+            for _ in range(max(1, warmup)):
+                layer(q, k, v, cfg)
+        main.wait_stream(s)
+        torch.cuda.synchronize(q.device)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.out, self.lse, self.state = layer(q, k, v, cfg)
+
+    def replay(self):
+        """Run the captured layer on the current contents of q, k and v; returns
+        (out, lse, state), the tensors the capture produced."""
+        self.graph.replay()
+        return self.out, self.lse, self.state
