@@ -702,15 +702,26 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
     // the items of stretch b % 8 in list order from that stretch's counter. The
     // stretches are contiguous (a few heads, q-clusters in order), so the
     // workgroups in flight on one XCD read overlapping key ranges through its
-    // own L2, and they carry equal estimated cost, so the XCDs finish together.
-    const int xq = blockIdx.x & 7;
-    const int s_beg = __builtin_amdgcn_readfirstlane(xcd_start[xq]);
-    const int s_end = __builtin_amdgcn_readfirstlane(xcd_start[xq + 1]);
+    // own L2, and they carry about equal estimated cost. A workgroup whose
+    // stretch is used up takes items from the next stretches in turn (x + 1,
+    // x + 2, ... mod 8) until all are: the cost estimate is off by a few
+    // percent per XCD (the XCDs finished 4-14 % of the kernel apart without
+    // this). Every counter value names at most one item, so each item is taken
+    // once; a workgroup exits after it has found all eight stretches used up.
+    int xs = blockIdx.x & 7;  // stretch being drained (thread 0's copy is used)
+    int tried = 0;            // stretches found used up
     for (;;) {
-    if (threadIdx.x == 0) sh_item = s_beg + atomicAdd(&xcd_ctr[xq], 1);
+    if (threadIdx.x == 0) {
+        int it = xcd_start[xs] + atomicAdd(&xcd_ctr[xs], 1);
+        while (it >= xcd_start[xs + 1] && ++tried < 8) {
+            xs = (xs + 1) & 7;
+            it = xcd_start[xs] + atomicAdd(&xcd_ctr[xs], 1);
+        }
+        sh_item = tried < 8 ? it : -1;
+    }
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(sh_item);
-    if (item >= s_end) break;
+    if (item < 0) break;
     int hlo = 0, hhi = BH;  // head_pos[hlo] <= item < head_pos[hhi]
     while (hhi - hlo > 1) {
         const int mid = (hlo + hhi) >> 1;
