@@ -633,14 +633,14 @@ static void plan_attn(Carver& c, const adc_shape* shape, int32_t Cq, int32_t Ck,
     w.run_pos = c.take<int32_t>(rows * (w.run_cap + 1));
     w.n_runs = c.take<int32_t>(rows);
     const size_t BH = (size_t)shape->B * shape->H;
-    w.sched.items = c.take<int32_t>(BH * w.cap);
-    w.sched.n_items = c.take<int32_t>(BH);
-    w.sched.cost_pre = c.take<uint32_t>(BH * w.cap);
-    w.sched.n_cost = c.take<uint32_t>(BH);
-    w.sched.head_pos = c.take<int32_t>(BH + 1);
-    w.sched.head_cost = c.take<uint64_t>(BH + 1);
-    w.sched.xcd_start = c.take<int32_t>(9);
-    w.sched.xcd_ctr = c.take<int32_t>(8);
+    w.sched.items = c.take<int32_t>(2 * BH * w.cap);
+    w.sched.n_items = c.take<int32_t>(2 * BH);
+    w.sched.cost_pre = c.take<uint32_t>(2 * BH * w.cap);
+    w.sched.n_cost = c.take<uint32_t>(2 * BH);
+    w.sched.head_pos = c.take<int32_t>(2 * BH + 1);
+    w.sched.head_cost = c.take<uint64_t>(2 * BH + 1);
+    w.sched.xcd_start = c.take<int32_t>(17);
+    w.sched.xcd_ctr = c.take<int32_t>(16);
     const size_t elems = (size_t)shape->B * shape->H * shape->N * shape->D;
     for (int i = 0; i < 4; ++i) w.planes[i] = nullptr;
     w.vmax = c.take<uint32_t>(BH);

@@ -125,23 +125,27 @@ hipError_t launch_build_runs(const Prob& p, int Cq, int Ck, const int32_t* k_off
 }
 
 // ------------------------------------------------------------------ work list
-// Work items (q-cluster a, chunk c of ATTN_ROWS rows) of head bh are written to
-// items[bh * cap ...] (cap = Cq + ceil(N / ATTN_ROWS) bounds their number), one
-// workgroup per head, with the inclusive prefix of their estimated cost within
-// the head. The q-clusters go in the order of the middle key of their selection
-// (the key row at half of the selected keys, K being slot-ordered): items that
-// run at the same time on one XCD then read nearby key tiles, which its L2
-// can share. Ties keep q-cluster order. An item's cost is its number of 64-key tiles
-// times (4 + its live waves): the time per tile of a work item grows by about a
-// quarter of its 4-wave value per 16-row wave of query rows (measured on
-// uniform synthetic layouts).
+// Work items (q-cluster a, chunk c of ATTN_ROWS rows) of head bh, one
+// workgroup per head, with the inclusive prefix of their estimated cost. The
+// list has two parts: first the items of the head's large q-clusters (those
+// whose first item costs more than twice the head's mean item cost), written
+// to part bh = items[bh * cap ...], then the others, part BH + bh (cap = Cq +
+// ceil(N / ATTN_ROWS) bounds each part). Within a part the q-clusters go in
+// the order of the middle key of their selection (the key row at half of the
+// selected keys, K being slot-ordered): items that run at the same time on one
+// XCD then read nearby key tiles, which its L2 can share; ties keep q-cluster
+// order. Running the large items first leaves the small ones for the end of
+// the kernel, where the last item of each workgroup sets when it finishes.
+// An item's cost is its number of 64-key tiles times (4 + its live waves): the
+// time per tile of a work item grows by about a quarter of its 4-wave value
+// per 16-row wave of query rows (measured on uniform synthetic layouts).
 __device__ __forceinline__ uint32_t item_cost(int tiles, int rows) {
     return (uint32_t)tiles * (uint32_t)(4 + (min(rows, ATTN_ROWS) + 15) / 16);
 }
 
 constexpr int WL_SORT = 8192;  // q-clusters a head can have (the slot capacity)
 
-__global__ __launch_bounds__(256) void worklist_kernel(int Cq, int cap,
+__global__ __launch_bounds__(256) void worklist_kernel(int Cq, int cap, int BH,
                                                        const int32_t* __restrict__ q_offsets,
                                                        const int32_t* __restrict__ run_start,
                                                        const int32_t* __restrict__ run_pos,
@@ -152,14 +156,45 @@ __global__ __launch_bounds__(256) void worklist_kernel(int Cq, int cap,
                                                        uint32_t* __restrict__ n_cost) {
     __shared__ int wsum[4];
     __shared__ uint32_t wcost[4];
+    __shared__ uint64_t wtot[4];
     __shared__ uint64_t order[WL_SORT];
     const int bh = blockIdx.x;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int32_t* qo = q_offsets + (int64_t)bh * (Cq + 1);
-    int32_t* out = items + (int64_t)bh * cap;
-    uint32_t* cout = cost_pre + (int64_t)bh * cap;
-    // sort keys: (middle key row of the selection, q-cluster); q-clusters with
-    // no selection sort first (they make no items)
+    auto tiles_of = [&](int a) __attribute__((always_inline)) -> int {
+        const int64_t row = (int64_t)bh * Cq + a;
+        return (run_pos[row * (run_cap + 1) + n_runs[row]] + 63) / 64;
+    };
+    // the head's item count and summed cost, for the mean item cost
+    uint64_t tot_cost = 0;
+    int tot_items = 0;
+    for (int a = tid; a < Cq; a += 256) {
+        const int rows = qo[a + 1] - qo[a];
+        const int ch = (rows + ATTN_ROWS - 1) / ATTN_ROWS;
+        if (ch == 0) continue;
+        const int tiles = tiles_of(a);
+        for (int c = 0; c < ch; ++c) tot_cost += item_cost(tiles, rows - c * ATTN_ROWS);
+        tot_items += ch;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        tot_cost += __shfl_xor(tot_cost, o);
+        tot_items += __shfl_xor(tot_items, o);
+    }
+    if (l == 0) {
+        wtot[w] = tot_cost;
+        wsum[w] = tot_items;
+    }
+    __syncthreads();
+    const uint64_t head_cost_sum = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+    const int head_items = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    // large: first item cost > 2 * mean item cost, i.e. cost * items > 2 * sum
+    auto large = [&](int tiles, int rows) __attribute__((always_inline)) -> bool {
+        return (uint64_t)item_cost(tiles, rows) * (uint64_t)head_items > 2ull * head_cost_sum;
+    };
+    __syncthreads();
+    // sort keys: (small?, middle key row of the selection, q-cluster); the
+    // q-clusters with no selection make no items
     int np2 = 1;
     while (np2 < Cq) np2 <<= 1;
     for (int a = tid; a < np2; a += 256) {
@@ -180,7 +215,8 @@ __global__ __launch_bounds__(256) void worklist_kernel(int Cq, int cap,
                 }
                 mid = (uint32_t)(run_start[row * run_cap + lo] + (half - rp[lo]));
             }
-            key = ((uint64_t)mid << 32) | (uint32_t)a;
+            const bool big = large((total + 63) / 64, qo[a + 1] - qo[a]);
+            key = ((uint64_t)(big ? 0u : 1u) << 63) | ((uint64_t)mid << 32) | (uint32_t)a;
         }
         order[a] = key;
     }
@@ -202,58 +238,62 @@ __global__ __launch_bounds__(256) void worklist_kernel(int Cq, int cap,
             __syncthreads();
         }
     }
-    int running = 0;
-    uint32_t running_cost = 0;
-    for (int base = 0; base < Cq; base += 256) {
-        const int a = base + tid < Cq ? (int)(uint32_t)order[base + tid] : Cq;
-        const int rows = a < Cq ? qo[a + 1] - qo[a] : 0;
-        const int ch = (rows + ATTN_ROWS - 1) / ATTN_ROWS;
-        int tiles = 0;
-        if (ch > 0) {
-            const int64_t row = (int64_t)bh * Cq + a;
-            tiles = (run_pos[row * (run_cap + 1) + n_runs[row]] + 63) / 64;
-        }
-        uint32_t cq = 0;
-        for (int c = 0; c < ch; ++c) cq += item_cost(tiles, rows - c * ATTN_ROWS);
-        int incl = ch;
-        uint32_t cincl = cq;
+    // one pass per part over the sorted q-clusters, each taking those of its part
+    for (int part = 0; part < 2; ++part) {
+        const int vh = part * BH + bh;
+        int32_t* out = items + (int64_t)vh * cap;
+        uint32_t* cout = cost_pre + (int64_t)vh * cap;
+        int running = 0;
+        uint32_t running_cost = 0;
+        for (int base = 0; base < Cq; base += 256) {
+            const uint64_t key = base + tid < Cq ? order[base + tid] : ~0ull;
+            const int a = base + tid < Cq ? (int)(uint32_t)key : Cq;
+            const bool mine = a < Cq && (int)(key >> 63) == part;
+            const int rows = mine ? qo[a + 1] - qo[a] : 0;
+            const int ch = (rows + ATTN_ROWS - 1) / ATTN_ROWS;
+            const int tiles = ch > 0 ? tiles_of(a) : 0;
+            uint32_t cq = 0;
+            for (int c = 0; c < ch; ++c) cq += item_cost(tiles, rows - c * ATTN_ROWS);
+            int incl = ch;
+            uint32_t cincl = cq;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int v = __shfl_up(incl, o);
-            const uint32_t vc = __shfl_up(cincl, o);
-            if (l >= o) {
-                incl += v;
-                cincl += vc;
+            for (int o = 1; o < 64; o <<= 1) {
+                const int v = __shfl_up(incl, o);
+                const uint32_t vc = __shfl_up(cincl, o);
+                if (l >= o) {
+                    incl += v;
+                    cincl += vc;
+                }
             }
+            if (l == 63) {
+                wsum[w] = incl;
+                wcost[w] = cincl;
+            }
+            __syncthreads();
+            int before = running + incl - ch;
+            uint32_t cbefore = running_cost + cincl - cq;
+            for (int i = 0; i < w; ++i) {
+                before += wsum[i];
+                cbefore += wcost[i];
+            }
+            for (int c = 0; c < ch; ++c) {
+                cbefore += item_cost(tiles, rows - c * ATTN_ROWS);
+                out[before + c] = a | (c << 16);
+                cout[before + c] = cbefore;
+            }
+            running += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+            running_cost += wcost[0] + wcost[1] + wcost[2] + wcost[3];
+            __syncthreads();
         }
-        if (l == 63) {
-            wsum[w] = incl;
-            wcost[w] = cincl;
+        if (tid == 0) {
+            n_items[vh] = running;
+            n_cost[vh] = running_cost;
         }
-        __syncthreads();
-        int before = running + incl - ch;
-        uint32_t cbefore = running_cost + cincl - cq;
-        for (int i = 0; i < w; ++i) {
-            before += wsum[i];
-            cbefore += wcost[i];
-        }
-        for (int c = 0; c < ch; ++c) {
-            cbefore += item_cost(tiles, rows - c * ATTN_ROWS);
-            out[before + c] = a | (c << 16);
-            cout[before + c] = cbefore;
-        }
-        running += wsum[0] + wsum[1] + wsum[2] + wsum[3];
-        running_cost += wcost[0] + wcost[1] + wcost[2] + wcost[3];
-        __syncthreads();
-    }
-    if (tid == 0) {
-        n_items[bh] = running;
-        n_cost[bh] = running_cost;
     }
 }
 
-// head_pos[bh] = number of work items of the heads before bh, head_cost[bh] =
-// their summed cost; entry BH holds the totals.
+// head_pos[v] = number of work items of the list parts before part v,
+// head_cost[v] = their summed cost; entry NP holds the totals (NP parts).
 __global__ __launch_bounds__(1024) void head_scan_kernel(int BH, const int32_t* __restrict__ n_items,
                                                          const uint32_t* __restrict__ n_cost,
                                                          int32_t* __restrict__ head_pos,
@@ -305,12 +345,14 @@ __global__ __launch_bounds__(1024) void head_scan_kernel(int BH, const int32_t* 
     }
 }
 
-// The list (heads in order, q-clusters in order) is cut into eight stretches of
-// equal estimated cost, one per XCD: stretch x holds the items whose cost
-// prefix lies in [x C / 8, (x + 1) C / 8). Also clears the eight queue counters.
-__device__ __forceinline__ uint64_t cost_before(int i, int BH, int cap, const int32_t* head_pos,
+// Each half of the list (the large items of every head, then the others) is
+// cut into eight stretches of equal estimated cost, one per XCD: stretch
+// 8 h + x holds the items of half h whose cost prefix lies in the x-th eighth
+// of that half's cost, so every XCD has its share of both. Also clears the
+// sixteen stretch counters.
+__device__ __forceinline__ uint64_t cost_before(int i, int NV, int cap, const int32_t* head_pos,
                                                 const uint64_t* head_cost, const uint32_t* cost_pre) {
-    int lo = 0, hi = BH;  // head_pos[lo] <= i < head_pos[hi]
+    int lo = 0, hi = NV;  // head_pos[lo] <= i < head_pos[hi]
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (head_pos[mid] <= i) lo = mid; else hi = mid;
@@ -325,18 +367,22 @@ __global__ __launch_bounds__(64) void xcd_split_kernel(int BH, int cap, const in
                                                        int32_t* __restrict__ xcd_start,
                                                        int32_t* __restrict__ xcd_ctr) {
     const int x = threadIdx.x;
-    if (x > 8) return;
-    const int n_total = head_pos[BH];
-    if (x < 8) xcd_ctr[x] = 0;
-    if (x == 8) {
-        xcd_start[8] = n_total;
+    if (x > 16) return;
+    const int NV = 2 * BH;
+    const int n_total = head_pos[NV];
+    if (x < 16) xcd_ctr[x] = 0;
+    if (x == 16) {
+        xcd_start[16] = n_total;
         return;
     }
-    const uint64_t target = head_cost[BH] * (uint64_t)x / 8u;
-    int lo = 0, hi = n_total;  // smallest i in [0, n_total] with cost_before(i) >= target
+    const int h = x >> 3, j = x & 7;
+    const int i_lo = h == 0 ? 0 : head_pos[BH], i_hi = h == 0 ? head_pos[BH] : n_total;
+    const uint64_t c_lo = h == 0 ? 0 : head_cost[BH], c_hi = h == 0 ? head_cost[BH] : head_cost[NV];
+    const uint64_t target = c_lo + (c_hi - c_lo) * (uint64_t)j / 8u;
+    int lo = i_lo, hi = i_hi;  // smallest i in [i_lo, i_hi] with cost_before(i) >= target
     while (lo < hi) {
         const int mid = (lo + hi) >> 1;
-        if (cost_before(mid, BH, cap, head_pos, head_cost, cost_pre) >= target) hi = mid; else lo = mid + 1;
+        if (cost_before(mid, NV, cap, head_pos, head_cost, cost_pre) >= target) hi = mid; else lo = mid + 1;
     }
     xcd_start[x] = lo;
 }
@@ -345,9 +391,9 @@ hipError_t launch_worklist(const Prob& p, int Cq, int cap, const int32_t* q_offs
                            const int32_t* run_start, const int32_t* run_pos, const int32_t* n_runs,
                            int run_cap, const AttnSched& sc, hipStream_t s) {
     if (Cq > WL_SORT) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(worklist_kernel, dim3((unsigned)p.BH), dim3(256), 0, s, Cq, cap, q_offsets,
+    hipLaunchKernelGGL(worklist_kernel, dim3((unsigned)p.BH), dim3(256), 0, s, Cq, cap, p.BH, q_offsets,
                        run_start, run_pos, n_runs, run_cap, sc.items, sc.n_items, sc.cost_pre, sc.n_cost);
-    hipLaunchKernelGGL(head_scan_kernel, dim3(1), dim3(1024), 0, s, p.BH, sc.n_items, sc.n_cost,
+    hipLaunchKernelGGL(head_scan_kernel, dim3(1), dim3(1024), 0, s, 2 * p.BH, sc.n_items, sc.n_cost,
                        sc.head_pos, sc.head_cost);
     hipLaunchKernelGGL(xcd_split_kernel, dim3(1), dim3(64), 0, s, p.BH, cap, sc.head_pos, sc.head_cost,
                        sc.cost_pre, sc.xcd_start, sc.xcd_ctr);
@@ -698,38 +744,41 @@ void attn_kernel(int N, int Cq, const T* __restrict__ Q, const int32_t* __restri
 
     __shared__ int sh_item;
 
-    // Work order: workgroup b runs on XCD b % 8 (round-robin dispatch) and takes
-    // the items of stretch b % 8 in list order from that stretch's counter. The
-    // stretches are contiguous (a few heads, q-clusters in order), so the
-    // workgroups in flight on one XCD read overlapping key ranges through its
-    // own L2, and they carry about equal estimated cost. A workgroup whose
-    // stretch is used up takes items from the next stretches in turn (x + 1,
-    // x + 2, ... mod 8) until all are: the cost estimate is off by a few
-    // percent per XCD (the XCDs finished 4-14 % of the kernel apart without
-    // this). Every counter value names at most one item, so each item is taken
-    // once; a workgroup exits after it has found all eight stretches used up.
-    int xs = blockIdx.x & 7;  // stretch being drained (thread 0's copy is used)
-    int tried = 0;            // stretches found used up
+    // Work order: workgroup b runs on XCD x = b % 8 (round-robin dispatch) and
+    // takes the items of stretch x (its share of the large items) in list
+    // order from that stretch's counter, then those of stretch 8 + x (its
+    // share of the others). The stretches are contiguous (a few heads,
+    // q-clusters in order), so the workgroups in flight on one XCD read
+    // overlapping key ranges through its own L2, and they carry about equal
+    // estimated cost. A workgroup whose stretch is used up takes items from
+    // the other XCDs' stretches of the same half in turn (x + 1, x + 2, ...
+    // mod 8): the cost estimate is off by a few percent per XCD (the XCDs
+    // finished 4-14 % of the kernel apart without this). Every counter value
+    // names at most one item, so each item is taken once; a workgroup exits
+    // after it has found all sixteen stretches used up.
+    const int xq = blockIdx.x & 7;
+    int kk = 0;  // position in this workgroup's order of stretches (thread 0's copy is used)
     for (;;) {
     if (threadIdx.x == 0) {
+        int xs = (kk & 8) | ((xq + kk) & 7);
         int it = xcd_start[xs] + atomicAdd(&xcd_ctr[xs], 1);
-        while (it >= xcd_start[xs + 1] && ++tried < 8) {
-            xs = (xs + 1) & 7;
+        while (it >= xcd_start[xs + 1] && ++kk < 16) {
+            xs = (kk & 8) | ((xq + kk) & 7);
             it = xcd_start[xs] + atomicAdd(&xcd_ctr[xs], 1);
         }
-        sh_item = tried < 8 ? it : -1;
+        sh_item = kk < 16 ? it : -1;
     }
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(sh_item);
     if (item < 0) break;
-    int hlo = 0, hhi = BH;  // head_pos[hlo] <= item < head_pos[hhi]
+    int hlo = 0, hhi = 2 * BH;  // list part: head_pos[hlo] <= item < head_pos[hhi]
     while (hhi - hlo > 1) {
         const int mid = (hlo + hhi) >> 1;
         if (__builtin_amdgcn_readfirstlane(head_pos[mid]) <= item) hlo = mid; else hhi = mid;
     }
-    const int bh = hlo;
+    const int bh = hlo < BH ? hlo : hlo - BH;
     const int packed = __builtin_amdgcn_readfirstlane(
-        items[(int64_t)bh * cap + item - __builtin_amdgcn_readfirstlane(head_pos[bh])]);
+        items[(int64_t)hlo * cap + item - __builtin_amdgcn_readfirstlane(head_pos[hlo])]);
     const int a = packed & 0xFFFF, ch = packed >> 16;
     const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -254,14 +254,16 @@ hipError_t launch_build_runs(const Prob& p, int Cq, int Ck, const int32_t* k_off
 // their cost prefix, per-head totals and the eight cost-balanced stretches
 // (one per XCD) with their queue counters.
 struct AttnSched {
-    int32_t* items;      // [BH][cap] a | chunk << 16
-    int32_t* n_items;    // [BH]
-    uint32_t* cost_pre;  // [BH][cap] inclusive cost prefix inside the head
-    uint32_t* n_cost;    // [BH]
-    int32_t* head_pos;   // [BH + 1] items before each head
-    uint64_t* head_cost; // [BH + 1] cost before each head
-    int32_t* xcd_start;  // [9] first item of each stretch, then the total
-    int32_t* xcd_ctr;    // [8] items taken from each stretch
+    // the list holds 2 BH parts: the items of the large q-clusters of every
+    // head (part bh), then those of the others (part BH + bh)
+    int32_t* items;      // [2 BH][cap] a | chunk << 16
+    int32_t* n_items;    // [2 BH]
+    uint32_t* cost_pre;  // [2 BH][cap] inclusive cost prefix inside the part
+    uint32_t* n_cost;    // [2 BH]
+    int32_t* head_pos;   // [2 BH + 1] items before each part
+    uint64_t* head_cost; // [2 BH + 1] cost before each part
+    int32_t* xcd_start;  // [17] first item of each of the 16 stretches, then the total
+    int32_t* xcd_ctr;    // [16] items taken from each stretch
 };
 hipError_t launch_worklist(const Prob& p, int Cq, int cap, const int32_t* q_offsets,
                            const int32_t* run_start, const int32_t* run_pos, const int32_t* n_runs,
