@@ -641,6 +641,7 @@ static void plan_attn(Carver& c, const adc_shape* shape, int32_t Cq, int32_t Ck,
     w.sched.head_cost = c.take<uint64_t>(2 * BH + 1);
     w.sched.xcd_start = c.take<int32_t>(17);
     w.sched.xcd_ctr = c.take<int32_t>(16);
+    w.sched.load = c.take<uint64_t>(2 * BH);
     const size_t elems = (size_t)shape->B * shape->H * shape->N * shape->D;
     for (int i = 0; i < 4; ++i) w.planes[i] = nullptr;
     w.vmax = c.take<uint32_t>(BH);

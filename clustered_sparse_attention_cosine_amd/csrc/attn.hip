@@ -128,7 +128,9 @@ hipError_t launch_build_runs(const Prob& p, int Cq, int Ck, const int32_t* k_off
 // Work items (q-cluster a, chunk c of ATTN_ROWS rows) of head bh, one
 // workgroup per head, with the inclusive prefix of their estimated cost. The
 // list has two parts: first the items of the head's large q-clusters (those
-// whose first item costs more than twice the head's mean item cost), written
+// whose first item costs more than twice the mean item cost over all heads:
+// heads differ, and on some workloads one head's q-clusters select most of
+// its keys), written
 // to part bh = items[bh * cap ...], then the others, part BH + bh (cap = Cq +
 // ceil(N / ATTN_ROWS) bounds each part). Within a part the q-clusters go in
 // the order of the middle key of their selection (the key row at half of the
@@ -145,7 +147,46 @@ __device__ __forceinline__ uint32_t item_cost(int tiles, int rows) {
 
 constexpr int WL_SORT = 8192;  // q-clusters a head can have (the slot capacity)
 
+// Items and summed item cost of head bh (one workgroup per head), for the mean
+// item cost over every head that the work list compares against.
+__global__ __launch_bounds__(256) void item_load_kernel(int Cq, const int32_t* __restrict__ q_offsets,
+                                                        const int32_t* __restrict__ run_pos,
+                                                        const int32_t* __restrict__ n_runs, int run_cap,
+                                                        uint64_t* __restrict__ load) {
+    __shared__ uint64_t wl[4];
+    __shared__ int wn[4];
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int32_t* qo = q_offsets + (int64_t)bh * (Cq + 1);
+    uint64_t cost = 0;
+    int n = 0;
+    for (int a = tid; a < Cq; a += 256) {
+        const int rows = qo[a + 1] - qo[a];
+        const int ch = (rows + ATTN_ROWS - 1) / ATTN_ROWS;
+        if (ch == 0) continue;
+        const int64_t row = (int64_t)bh * Cq + a;
+        const int tiles = (run_pos[row * (run_cap + 1) + n_runs[row]] + 63) / 64;
+        for (int c = 0; c < ch; ++c) cost += item_cost(tiles, rows - c * ATTN_ROWS);
+        n += ch;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        cost += __shfl_xor(cost, o);
+        n += __shfl_xor(n, o);
+    }
+    if (l == 0) {
+        wl[w] = cost;
+        wn[w] = n;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        load[2 * bh] = wl[0] + wl[1] + wl[2] + wl[3];
+        load[2 * bh + 1] = (uint64_t)(wn[0] + wn[1] + wn[2] + wn[3]);
+    }
+}
+
 __global__ __launch_bounds__(256) void worklist_kernel(int Cq, int cap, int BH,
+                                                       const uint64_t* __restrict__ load,
                                                        const int32_t* __restrict__ q_offsets,
                                                        const int32_t* __restrict__ run_start,
                                                        const int32_t* __restrict__ run_pos,
@@ -156,7 +197,7 @@ __global__ __launch_bounds__(256) void worklist_kernel(int Cq, int cap, int BH,
                                                        uint32_t* __restrict__ n_cost) {
     __shared__ int wsum[4];
     __shared__ uint32_t wcost[4];
-    __shared__ uint64_t wtot[4];
+    __shared__ uint64_t wtot[4], wtot2[4];
     __shared__ uint64_t order[WL_SORT];
     const int bh = blockIdx.x;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -165,16 +206,11 @@ __global__ __launch_bounds__(256) void worklist_kernel(int Cq, int cap, int BH,
         const int64_t row = (int64_t)bh * Cq + a;
         return (run_pos[row * (run_cap + 1) + n_runs[row]] + 63) / 64;
     };
-    // the head's item count and summed cost, for the mean item cost
-    uint64_t tot_cost = 0;
-    int tot_items = 0;
-    for (int a = tid; a < Cq; a += 256) {
-        const int rows = qo[a + 1] - qo[a];
-        const int ch = (rows + ATTN_ROWS - 1) / ATTN_ROWS;
-        if (ch == 0) continue;
-        const int tiles = tiles_of(a);
-        for (int c = 0; c < ch; ++c) tot_cost += item_cost(tiles, rows - c * ATTN_ROWS);
-        tot_items += ch;
+    // item count and summed cost over every head, for the mean item cost
+    uint64_t tot_cost = 0, tot_items = 0;
+    for (int i = tid; i < BH; i += 256) {
+        tot_cost += load[2 * i];
+        tot_items += load[2 * i + 1];
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -183,14 +219,14 @@ __global__ __launch_bounds__(256) void worklist_kernel(int Cq, int cap, int BH,
     }
     if (l == 0) {
         wtot[w] = tot_cost;
-        wsum[w] = tot_items;
+        wtot2[w] = tot_items;
     }
     __syncthreads();
-    const uint64_t head_cost_sum = wtot[0] + wtot[1] + wtot[2] + wtot[3];
-    const int head_items = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    const uint64_t all_cost = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+    const uint64_t all_items = wtot2[0] + wtot2[1] + wtot2[2] + wtot2[3];
     // large: first item cost > 2 * mean item cost, i.e. cost * items > 2 * sum
     auto large = [&](int tiles, int rows) __attribute__((always_inline)) -> bool {
-        return (uint64_t)item_cost(tiles, rows) * (uint64_t)head_items > 2ull * head_cost_sum;
+        return (uint64_t)item_cost(tiles, rows) * all_items > 2ull * all_cost;
     };
     __syncthreads();
     // sort keys: (small?, middle key row of the selection, q-cluster); the
@@ -391,7 +427,10 @@ hipError_t launch_worklist(const Prob& p, int Cq, int cap, const int32_t* q_offs
                            const int32_t* run_start, const int32_t* run_pos, const int32_t* n_runs,
                            int run_cap, const AttnSched& sc, hipStream_t s) {
     if (Cq > WL_SORT) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(worklist_kernel, dim3((unsigned)p.BH), dim3(256), 0, s, Cq, cap, p.BH, q_offsets,
+    hipLaunchKernelGGL(item_load_kernel, dim3((unsigned)p.BH), dim3(256), 0, s, Cq, q_offsets, run_pos, n_runs,
+                       run_cap, sc.load);
+    hipLaunchKernelGGL(worklist_kernel, dim3((unsigned)p.BH), dim3(256), 0, s, Cq, cap, p.BH,
+                       (const uint64_t*)sc.load, q_offsets,
                        run_start, run_pos, n_runs, run_cap, sc.items, sc.n_items, sc.cost_pre, sc.n_cost);
     hipLaunchKernelGGL(head_scan_kernel, dim3(1), dim3(1024), 0, s, 2 * p.BH, sc.n_items, sc.n_cost,
                        sc.head_pos, sc.head_cost);

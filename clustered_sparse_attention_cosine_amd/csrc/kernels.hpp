@@ -264,6 +264,7 @@ struct AttnSched {
     uint64_t* head_cost; // [2 BH + 1] cost before each part
     int32_t* xcd_start;  // [17] first item of each of the 16 stretches, then the total
     int32_t* xcd_ctr;    // [16] items taken from each stretch
+    uint64_t* load;      // [BH][2] summed item cost and item count per head
 };
 hipError_t launch_worklist(const Prob& p, int Cq, int cap, const int32_t* q_offsets,
                            const int32_t* run_start, const int32_t* run_pos, const int32_t* n_runs,
