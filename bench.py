@@ -37,14 +37,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def timed_layer(torch, adc, q, k, v, cfg, stream, prev=None, select_kw=None, want_lse=True):
+def timed_layer(torch, adc, q, k, v, cfg, stream, prev=None, select_kw=None, want_lse=True,
+                serial=False):
     """One layer as the package schedules it (the two clusterings overlapped on
     two streams, then selection and attention), with timing events. Returns
     (Q, K, S, out, times) where times() gives the layer and per-stage
-    milliseconds once the stream has finished."""
+    milliseconds once the stream has finished. serial: the query clustering,
+    then the key clustering, on the one stream (each stage's kernels alone on
+    the GPU, for profiles)."""
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
     ev[0].record(stream)
-    Q, K = adc.cluster_layer(q, k, v, cfg, prev=prev, events=ev[1:6])
+    if serial and prev is None:
+        ev[1].record(stream)
+        Q = adc.cluster_q(q, cfg.q_clusters, cfg.iters, cfg.init, cfg.seed)
+        ev[2].record(stream)
+        ev[3].record(stream)
+        K = adc.cluster_k(k, v, cfg.k_base, cfg.k_max, cfg.iters, cfg.tau_mult, cfg.adaptive, cfg.init,
+                          cfg.seed)
+        ev[4].record(stream)
+        ev[5].record(stream)
+    else:
+        Q, K = adc.cluster_layer(q, k, v, cfg, prev=prev, events=ev[1:6])
     S = adc.select(Q["qrep"], K, cfg.top_p, q_offsets=Q["offsets"], **(select_kw or {}))
     ev[6].record(stream)
     out, _ = adc.sparse_attn(q, Q["perm"], Q["offsets"], K["k_perm"], K["v_perm"], K["offsets"],
@@ -85,6 +98,8 @@ def main():
                     help="heads the oracle baseline runs: 'all', or a comma list (default: 4 spread heads)")
     ap.add_argument("--profile-steps", action="store_true",
                     help="only warmup + timed steps (for profiler runs)")
+    ap.add_argument("--serial-clustering", action="store_true",
+                    help="run the query and key clusterings one after the other on one stream")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -115,7 +130,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step(record=None):
-        Q, K, S, out, times = timed_layer(torch, adc, q, k, v, cfg, stream)
+        Q, K, S, out, times = timed_layer(torch, adc, q, k, v, cfg, stream, serial=args.serial_clustering)
         if record is not None:
             record.append(times)
         return Q, K, S, out
@@ -171,8 +186,10 @@ def main():
                 t += 1
             meff.append(last)
         log(json.dumps(dict(ms_per_step=ms, stages_ms=stage_ms, calib_copy_bytes=CALIB_BYTES,
+                            schedule="serial" if args.serial_clustering else "two streams",
                             shapes=dict(rows=w.B * w.H * w.N, D=w.D, q_clusters=w.q_clusters,
-                                        k_base=w.k_base, iters=w.iters,
+                                        k_base=w.k_base, k_max=nmax, heads=w.B * w.H,
+                                        elem_bytes=2 if w.dtype == "bf16" else 4, iters=w.iters,
                                         k_final_slots_mean=float(np.mean(meff))))))
         return
 
@@ -196,7 +213,9 @@ def main():
                    "top_p": w.top_p, "lloyd_iters": w.iters, "init": w.init,
                    "layer_ms": round(ms, 4)},
         "stages_ms": {k2: round(v2, 4) for k2, v2 in stage_ms.items()},
-        "schedule": "cluster_q on a side stream beside cluster_k (their stage times overlap), then select and sparse_attn",
+        "schedule": ("cluster_q, then cluster_k, on one stream, then select and sparse_attn"
+                     if args.serial_clustering else
+                     "cluster_q on a side stream beside cluster_k (their stage times overlap), then select and sparse_attn"),
         "layer_ms_events": layer_stats,
         "selection": {"pairs": pairs, "density": round(density, 5), "full_heads": full_heads,
                       "k_slots": {str(s): slots.count(s) for s in sorted(set(slots))}},
