@@ -1050,10 +1050,12 @@ static void launch_attn_t(const Prob& p, int Cq, const void* q, const int32_t* q
     constexpr int W128 = sizeof(T) == 2 ? 4 : 2;
     const int wpe = p.D == 64 ? W64 : W128;
     auto k = p.D == 64 ? attn_kernel<T, 64, TO, W64> : attn_kernel<T, 128, TO, W128>;
-    // as many workgroups as fit at once (wpe * 4 SIMDs / 8 waves per CU), in
-    // whole rounds of the eight XCDs
+    // as many workgroups as fit at once (wpe * 4 SIMDs / 8 waves per CU), but
+    // no more than the work items can be (cap per head), in whole rounds of the
+    // eight XCDs: a workgroup without an item still visits every stretch
     const int per_cu = std::max(1, wpe / 2);
-    const dim3 grid((unsigned)(((cu_count() * per_cu) + 7) / 8 * 8));
+    const int64_t wgs = std::min<int64_t>((int64_t)cu_count() * per_cu, (int64_t)p.BH * cap);
+    const dim3 grid((unsigned)((wgs + 7) / 8 * 8));
     hipLaunchKernelGGL(k, grid, dim3(512), 0, s, p.N, Cq, (const T*)q, q_perm, q_offsets, k0, k1,
                        v0, v1, run_start, run_pos, n_runs, run_cap, sc.items, sc.head_pos,
                        sc.xcd_start, sc.xcd_ctr, p.BH, cap, sl2, vmax, (TO*)out, lse);
