@@ -250,9 +250,10 @@ hipError_t launch_pairs(const Prob& p, int Cq, const int32_t* q_offsets, const i
 hipError_t launch_build_runs(const Prob& p, int Cq, int Ck, const int32_t* k_offsets,
                              const uint32_t* mask, int run_cap, int32_t* run_start,
                              int32_t* run_pos, int32_t* n_runs, hipStream_t s);
-// Attention schedule: the work items of each head (q-cluster, 128-row chunk),
-// their cost prefix, per-head totals and the eight cost-balanced stretches
-// (one per XCD) with their queue counters.
+// Attention schedule: the work items of each head (q-cluster, 128-row chunk)
+// in two halves (large q-clusters first), their cost prefix, per-part totals
+// and the sixteen cost-balanced stretches (one per XCD and half) with their
+// queue counters.
 struct AttnSched {
     // the list holds 2 BH parts: the items of the large q-clusters of every
     // head (part bh), then those of the others (part BH + bh)
