@@ -199,6 +199,53 @@ def test_sparse_attn_many_runs(dtype):
     assert np.abs(lse - ref_lse).max() <= 1e-2
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_sparse_attn_mixed_head_densities(D):
+    """Heads of very different selection densities in one call: a head whose
+    q-clusters select every slot, a sparse head, a head with one dense
+    q-cluster among sparse ones, and random ones. Their items land in both
+    halves of the work list (large q-clusters first, judged against the mean
+    over all heads) and in several XCD stretches, so workgroups also take
+    items of other stretches; every head is compared with the oracle."""
+    rng = np.random.default_rng(21 + D)
+    H, N, Cq, Ck = 6, 1500, 24, 96
+    q, k, v = (synth.f32_to_bf16_bits(rng.standard_normal((1, H, N, D)).astype(np.float32)) for _ in range(3))
+    qlab = rng.integers(0, Cq, (H, N)).astype(np.int32)
+    klab = rng.integers(0, Ck, (H, N)).astype(np.int32)
+    bits = np.zeros((H, Cq, Ck), bool)
+    bits[0] = True                                  # every slot
+    bits[1] = rng.random((Cq, Ck)) < 0.03           # sparse
+    bits[2] = rng.random((Cq, Ck)) < 0.05
+    bits[2, 7] = True                               # one dense q-cluster
+    bits[3:] = rng.random((H - 3, Cq, Ck)) < rng.uniform(0.2, 0.5, (H - 3, 1, 1))
+    words = (Ck + 31) // 32
+    mask = np.zeros((H, Cq, words), np.uint32)
+    for h in range(H):
+        for a in range(Cq):
+            for j in np.nonzero(bits[h, a])[0]:
+                mask[h, a, j // 32] |= np.uint32(1) << np.uint32(j % 32)
+    qperm = np.zeros((1, H, N), np.int32)
+    qoff = np.zeros((1, H, Cq + 1), np.int32)
+    kperm = np.zeros((1, H, N), np.int32)
+    koff = np.zeros((1, H, Ck + 1), np.int32)
+    for h in range(H):
+        qperm[0, h], qoff[0, h] = oracle.permute(qlab[h], Cq)
+        kperm[0, h], koff[0, h] = oracle.permute(klab[h], Ck)
+    kp = np.stack([k[0, h, kperm[0, h]] for h in range(H)])[None]
+    vp = np.stack([v[0, h, kperm[0, h]] for h in range(H)])[None]
+    scale = float(1 / np.sqrt(D))
+    out, lse = adc.sparse_attn(dev(q), dev(qperm), dev(qoff), dev(kp), dev(vp), dev(koff),
+                               dev(mask[None].view(np.int32)), scale=scale)
+    out, lse = host(out)[0], host(lse)[0]
+    for h in range(H):
+        ref, ref_lse = oracle.sparse_attn(synth.as_f32(q[0, h]), synth.as_f32(k[0, h]), synth.as_f32(v[0, h]),
+                                          qlab[h], klab[h], Cq, Ck, mask[h], scale)
+        assert rel_l2(out[h], ref) <= 1e-2 and np.abs(out[h] - ref).max() <= 2e-2, h
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(fin, np.isfinite(lse[h])), h
+        assert np.abs(lse[h][fin] - ref_lse[fin]).max() <= 1e-2, h
+
+
 # ----------------------------------------------------------------- assignment (lockstep)
 @pytest.mark.parametrize("case", list(CASES))
 @pytest.mark.parametrize("normalize", [False, True])
