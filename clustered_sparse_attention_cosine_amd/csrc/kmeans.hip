@@ -1464,6 +1464,13 @@ hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* i
 // writer, so the sums do not depend on scheduling.
 // With ub (by token; may be null) the same walk also takes the largest ub of
 // each run: rad[slot] for whole clusters, part radii beside the part sums.
+#ifndef ADC_UPD_RS64
+#define ADC_UPD_RS64 32
+#endif
+#ifndef ADC_UPD_RS128
+#define ADC_UPD_RS128 32
+#endif
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__ X, int N, RowSet rs,
                                                            const float* __restrict__ inv_norm,
@@ -1474,10 +1481,11 @@ __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__
                                                            float* __restrict__ rad,
                                                            float* __restrict__ part_rad) {
     constexpr int E = D / 64;
-    constexpr int RS = D == 64 ? 64 : 32;          // rows staged at once
+    constexpr int RS = D == 64 ? ADC_UPD_RS64 : ADC_UPD_RS128;  // rows staged at once
     constexpr int LDX = D + 16 / (int)sizeof(T);   // padded row stride (elements)
     constexpr int CPR = D / 8;                     // 8-element chunks per row
     constexpr int RPI = 64 / CPR;                  // rows per wave instruction
+    constexpr int W8 = (int)sizeof(T) / 2;         // 16-byte words per 8-element chunk
     __shared__ __attribute__((aligned(16))) T xs[4][RS * LDX];
     const int bh = blockIdx.y;
     if (rs.active && !rs.active[bh]) return;
@@ -1518,17 +1526,29 @@ __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__
             *rd = umax;
         }
     };
-    for (int h0 = 0; h0 < rows_here; h0 += RS) {
-        // chunk c of row q goes to lane (q % RPI) * CPR + c; rows past the end read row 0
+    // the rows of the next batch are loaded into registers while the current
+    // batch is walked; chunk c of row q goes to lane (q % RPI) * CPR + c, and
+    // rows past the end read row 0
+    u32x4 pre[RS / RPI][W8];
+    auto load_batch = [&](int h0) __attribute__((always_inline)) {
 #pragma unroll
         for (int it = 0; it < RS / RPI; ++it) {
             const int q = it * RPI + l / CPR, c = l % CPR;
             const int tok = __shfl(tok_l, h0 + q);
             const T* src = row_ptr(X, N, D, bh, tok) + c * 8;
-            *reinterpret_cast<u32x4*>(&xw[q * LDX + c * 8]) = *reinterpret_cast<const u32x4*>(src);
-            if constexpr (sizeof(T) == 4)
-                *reinterpret_cast<u32x4*>(&xw[q * LDX + c * 8 + 4]) = *reinterpret_cast<const u32x4*>(src + 4);
+#pragma unroll
+            for (int k = 0; k < W8; ++k) pre[it][k] = *reinterpret_cast<const u32x4*>(src + 4 * k);
         }
+    };
+    load_batch(0);
+    for (int h0 = 0; h0 < rows_here; h0 += RS) {
+#pragma unroll
+        for (int it = 0; it < RS / RPI; ++it) {
+            const int q = it * RPI + l / CPR, c = l % CPR;
+#pragma unroll
+            for (int k = 0; k < W8; ++k) *reinterpret_cast<u32x4*>(&xw[q * LDX + c * 8 + 4 * k]) = pre[it][k];
+        }
+        if (h0 + RS < rows_here) load_batch(h0 + RS);
         // lanes read rows other lanes wrote
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
