@@ -1464,13 +1464,6 @@ hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* i
 // writer, so the sums do not depend on scheduling.
 // With ub (by token; may be null) the same walk also takes the largest ub of
 // each run: rad[slot] for whole clusters, part radii beside the part sums.
-#ifndef ADC_UPD_RS64
-#define ADC_UPD_RS64 32
-#endif
-#ifndef ADC_UPD_RS128
-#define ADC_UPD_RS128 32
-#endif
-
 template <typename T, int D>
 __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__ X, int N, RowSet rs,
                                                            const float* __restrict__ inv_norm,
@@ -1481,7 +1474,7 @@ __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__
                                                            float* __restrict__ rad,
                                                            float* __restrict__ part_rad) {
     constexpr int E = D / 64;
-    constexpr int RS = D == 64 ? ADC_UPD_RS64 : ADC_UPD_RS128;  // rows staged at once
+    constexpr int RS = 32;                         // rows staged at once (two batches per wave)
     constexpr int LDX = D + 16 / (int)sizeof(T);   // padded row stride (elements)
     constexpr int CPR = D / 8;                     // 8-element chunks per row
     constexpr int RPI = 64 / CPR;                  // rows per wave instruction

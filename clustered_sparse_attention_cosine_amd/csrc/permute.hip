@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void gather_stats_kernel(int N, int M,
                                                            T* __restrict__ v_perm) {
 #pragma clang fp contract(off)
     constexpr int E = D / 64;
-    constexpr int RS = D == 64 ? 64 : 32;          // rows staged at once
+    constexpr int RS = 32;  // rows staged at once (half the LDS of 64 rows: twice the workgroups per CU)
     constexpr int LDX = D + 16 / (int)sizeof(T);   // padded row stride (elements)
     constexpr int CPR = D / 8;                     // 8-element chunks per row
     constexpr int RPI = 64 / CPR;                  // rows per wave instruction
