@@ -183,34 +183,46 @@ hipError_t launch_last_valid(const Prob& p, CentView cv, const int32_t* mcount, 
 }
 
 // ------------------------------------------------------------------ norms
-// 8 lanes per row, each reading 8-element chunks with 16-byte loads (32 rows
-// per workgroup); squares summed in f64, then over the 8 lanes.
+// 8 lanes per row, each reading 8-element chunks with 16-byte loads; a
+// workgroup takes 8 rows per group of 8 lanes (256 rows), every load issued
+// before the first product so enough bytes are in flight. Squares summed in
+// f64 over each lane's chunks, then over the 8 lanes.
 template <typename T>
 __global__ __launch_bounds__(256) void inv_norm_kernel(const T* __restrict__ x, int64_t rows,
                                                        int D, float* __restrict__ inv) {
-    int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
-    int sub = threadIdx.x & 7;
-    if (row >= rows) return;
-    const T* r = x + row * D;
-    double s = 0.0;
-    for (int j = sub * 8; j < D; j += 64) {
-        float v[8];
-        load8<T>(r + j, v);
+    constexpr int RPG = 8;  // rows per lane group
+    const int grp = threadIdx.x >> 3, sub = threadIdx.x & 7;
+    const int64_t row0 = (int64_t)blockIdx.x * (32 * RPG) + grp;  // rows row0 + 32 r
+    double s[RPG];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) s += (double)v[i] * (double)v[i];
+    for (int r = 0; r < RPG; ++r) s[r] = 0.0;
+    for (int j = sub * 8; j < D; j += 64) {
+        // rows past the end read the last row (unconditional loads stay in flight
+        // together; their sums are not stored)
+        float v[RPG][8];
+#pragma unroll
+        for (int r = 0; r < RPG; ++r) load8<T>(x + min(row0 + 32 * r, rows - 1) * D + j, v[r]);
+#pragma unroll
+        for (int r = 0; r < RPG; ++r)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s[r] += (double)v[r][i] * (double)v[r][i];
     }
 #pragma unroll
-    for (int o = 4; o > 0; o >>= 1) s += __shfl_xor(s, o);
-    if (sub == 0) {
-        double n = sqrt(s);
-        if (n < 1e-12) n = 1e-12;
-        inv[row] = (float)(1.0 / n);
+    for (int r = 0; r < RPG; ++r) {
+#pragma unroll
+        for (int o = 4; o > 0; o >>= 1) s[r] += __shfl_xor(s[r], o);
+        const int64_t row = row0 + 32 * r;
+        if (sub == 0 && row < rows) {
+            double n = sqrt(s[r]);
+            if (n < 1e-12) n = 1e-12;
+            inv[row] = (float)(1.0 / n);
+        }
     }
 }
 
 hipError_t launch_inv_norm(const Prob& p, const void* x, float* inv, hipStream_t s) {
     int64_t rows = (int64_t)p.BH * p.N;
-    dim3 grid((unsigned)((rows + 31) / 32));
+    dim3 grid((unsigned)((rows + 255) / 256));
     if (p.bf16)
         hipLaunchKernelGGL(inv_norm_kernel<u16>, grid, dim3(256), 0, s, (const u16*)x, rows, p.D, inv);
     else

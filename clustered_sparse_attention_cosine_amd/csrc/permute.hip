@@ -188,18 +188,43 @@ hipError_t launch_counting_sort(const Prob& p, const int32_t* labels, int M, int
     return hipGetLastError();
 }
 
+// The f32 rounding of a quotient v / n (v exact in f64) formed as p = v * r,
+// r = RN64(1 / n): p lies within 3 f64 units in the last place of RN64(v / n)
+// (relative errors 2^-53 of r and of the product, 2^-53 of the exact
+// quotient), so both round to the same f32 unless an f32 rounding midpoint
+// (the 29 bits below f32 precision equal to 2^28) lies that close, or the
+// value is below the normal f32 range. Returns true when p is more than 16
+// units from any midpoint and normal (or zero): then RN32(p) = RN32(RN64(v / n)).
+__device__ __forceinline__ bool f32_rounding_settled(double p) {
+    const uint64_t b = (uint64_t)__double_as_longlong(p);
+    const uint32_t low = (uint32_t)b & 0x1FFFFFFFu;
+    const uint32_t hi = (uint32_t)(b >> 32) & 0x7FFFFFFFu;
+    const bool normal = hi >= (898u << 20) || (hi | (uint32_t)b) == 0u;  // |p| >= 2^-125, or p = 0
+    return normal && (low - (0x10000000u - 16u)) > 32u;
+}
+
 // One wave per cluster walks its members in permuted order, RS rows at a
 // time: the rows are copied to x_perm / v_perm and staged in LDS with
-// coalesced 16-byte accesses (all loads of a batch in flight at once); lane q
-// then takes the norm of staged row q (f64, index order) when the rows are
-// normalized, and the statistics are accumulated with one lane per dimension
-// in member order (f64 sums, as the definition).
-template <typename T, int D>
+// coalesced 16-byte accesses (all loads of a batch in flight at once), and the
+// statistics are accumulated with one lane per dimension in member order (f64
+// sums, as the definition).
+//
+// NORM (queries; sums of the normalized and of the raw rows, no max/min): lane
+// q first takes the norm of staged row q (f64, index order) and its
+// reciprocal; then, QB rows at a time, every lane forms its dimension of the
+// QB normalized values, each rounded to f32 as the definition has it, before
+// the member-order adds, so only the adds form a dependent chain (the last
+// nb mod QB rows of a cluster one by one). A quotient
+// is taken as a product with the reciprocal when that provably rounds to the
+// same f32 (f32_rounding_settled), else by division for the whole block. With
+// a division per member on the chain this pass ran at under a fifth of the key
+// pass's bandwidth.
+template <typename T, int D, bool NORM>
 __global__ __launch_bounds__(256) void gather_stats_kernel(int N, int M,
                                                            const int32_t* __restrict__ offsets,
                                                            const int32_t* __restrict__ perm,
                                                            const T* __restrict__ x,
-                                                           const T* __restrict__ v, int normalize,
+                                                           const T* __restrict__ v,
                                                            float* __restrict__ means,
                                                            float* __restrict__ raw_means,
                                                            T* __restrict__ xmax, T* __restrict__ xmin,
@@ -207,14 +232,20 @@ __global__ __launch_bounds__(256) void gather_stats_kernel(int N, int M,
                                                            T* __restrict__ v_perm) {
 #pragma clang fp contract(off)
     constexpr int E = D / 64;
-    constexpr int RS = 32;  // rows staged at once (half the LDS of 64 rows: twice the workgroups per CU)
+    // rows staged at once: 32 for the copies (half the LDS of 64 rows, twice
+    // the workgroups per CU); 64 for bf16 D = 64 queries, one row per lane
+    // for the norms
+    constexpr int RS = (NORM && sizeof(T) == 2 && D == 64) ? 64 : 32;
     constexpr int LDX = D + 16 / (int)sizeof(T);   // padded row stride (elements)
     constexpr int CPR = D / 8;                     // 8-element chunks per row
     constexpr int RPI = 64 / CPR;                  // rows per wave instruction
     constexpr int W8 = 8 * (int)sizeof(T) / 16;    // 16-byte words per chunk
+    constexpr int QB = D == 64 ? 16 : 8;           // rows per block of quotients (NORM)
     __shared__ __attribute__((aligned(16))) T xs[4][RS * LDX];
+    __shared__ double nrm_s[NORM ? 4 : 1][NORM ? RS : 1];
+    __shared__ double rcp_s[NORM ? 4 : 1][NORM ? RS : 1];
     const int bh = blockIdx.y;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
     const int j = blockIdx.x * 4 + w;
     if (j >= M) return;
     const int32_t* off = offsets + (int64_t)bh * (M + 1);
@@ -238,7 +269,7 @@ __global__ __launch_bounds__(256) void gather_stats_kernel(int N, int M,
             const int64_t src = ((int64_t)bh * N + __shfl(tok_l, q)) * D + c * 8;
 #pragma unroll
             for (int k = 0; k < W8; ++k) xv[it][k] = *reinterpret_cast<const u32x4*>(x + src + k * EW);
-            if (v_perm) {
+            if (!NORM && v_perm) {
 #pragma unroll
                 for (int k = 0; k < W8; ++k) vv[it][k] = *reinterpret_cast<const u32x4*>(v + src + k * EW);
             }
@@ -254,7 +285,7 @@ __global__ __launch_bounds__(256) void gather_stats_kernel(int N, int M,
 #pragma unroll
                     for (int k = 0; k < W8; ++k) *reinterpret_cast<u32x4*>(x_perm + dst + k * EW) = xv[it][k];
                 }
-                if (v_perm) {
+                if (!NORM && v_perm) {
 #pragma unroll
                     for (int k = 0; k < W8; ++k) *reinterpret_cast<u32x4*>(v_perm + dst + k * EW) = vv[it][k];
                 }
@@ -264,35 +295,67 @@ __global__ __launch_bounds__(256) void gather_stats_kernel(int N, int M,
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        double nrm_l = 1.0;
-        if (normalize && l < nb) {
-            double ss = 0.0;
-            for (int d = 0; d < D; ++d) {
-                const double vv = (double)elem<T>::load(xw, l * LDX + d);
-                ss += vv * vv;
+        if constexpr (NORM) {
+            for (int q = l; q < RS; q += 64) {
+                double nrm = 1.0;
+                if (q < nb) {
+                    double ss = 0.0;
+                    for (int d = 0; d < D; ++d) {
+                        const double vd = (double)elem<T>::load(xw, q * LDX + d);
+                        ss += vd * vd;
+                    }
+                    nrm = sqrt(ss);
+                    if (nrm < 1e-12) nrm = 1e-12;
+                }
+                nrm_s[w][q] = nrm;
+                rcp_s[w][q] = 1.0 / nrm;
             }
-            nrm_l = sqrt(ss);
-            if (nrm_l < 1e-12) nrm_l = 1e-12;
-        }
-        for (int q = 0; q < nb; ++q) {
-            float val[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e) val[e] = elem<T>::load(xw, q * LDX + l + 64 * e);
-            if (normalize) {
-                const double nrm = __shfl(nrm_l, q);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // full blocks of QB rows, then the cluster's last rows one by one
+            const int nfull = nb / QB * QB;
+            for (int q0 = 0; q0 < nfull; q0 += QB) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    sum[e] += (double)(float)((double)val[e] / nrm);
-                    rsum[e] += (double)val[e];
+                    float val[QB], nv[QB];
+#pragma unroll
+                    for (int i = 0; i < QB; ++i) val[i] = elem<T>::load(xw, (q0 + i) * LDX + l + 64 * e);
+                    bool exact = true;
+#pragma unroll
+                    for (int i = 0; i < QB; ++i) {
+                        const double qd = (double)val[i] * rcp_s[w][q0 + i];
+                        nv[i] = (float)qd;
+                        exact = exact && f32_rounding_settled(qd);
+                    }
+                    if (__builtin_expect(__ballot(!exact) != 0, 0)) {
+#pragma unroll
+                        for (int i = 0; i < QB; ++i) nv[i] = (float)((double)val[i] / nrm_s[w][q0 + i]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < QB; ++i) {
+                        sum[e] += (double)nv[i];
+                        rsum[e] += (double)val[i];
+                    }
                 }
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e) sum[e] += (double)val[e];
             }
+            for (int q = nfull; q < nb; ++q) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                mx[e] = fmaxf(mx[e], val[e]);
-                mn[e] = fminf(mn[e], val[e]);
+                for (int e = 0; e < E; ++e) {
+                    const float val = elem<T>::load(xw, q * LDX + l + 64 * e);
+                    sum[e] += (double)(float)((double)val / nrm_s[w][q]);
+                    rsum[e] += (double)val;
+                }
+            }
+        } else {
+            for (int q = 0; q < nb; ++q) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float val = elem<T>::load(xw, q * LDX + l + 64 * e);
+                    sum[e] += (double)val;
+                    mx[e] = fmaxf(mx[e], val);
+                    mn[e] = fminf(mn[e], val);
+                }
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -316,15 +379,19 @@ hipError_t launch_gather_stats(const Prob& p, int M, const int32_t* offsets, con
                                float* raw_means, void* xmax, void* xmin, void* x_perm, void* v_perm,
                                hipStream_t s) {
     dim3 grid((unsigned)((M + 3) / 4), (unsigned)p.BH);
+    // the normalized pass copies one tensor and takes no max/min
+    if (normalize && (v_perm || xmax || xmin)) return hipErrorInvalidValue;
     if (p.bf16) {
-        auto k = p.D == 64 ? gather_stats_kernel<u16, 64> : gather_stats_kernel<u16, 128>;
+        auto k = normalize ? (p.D == 64 ? gather_stats_kernel<u16, 64, true> : gather_stats_kernel<u16, 128, true>)
+                           : (p.D == 64 ? gather_stats_kernel<u16, 64, false> : gather_stats_kernel<u16, 128, false>);
         hipLaunchKernelGGL(k, grid, dim3(256), 0, s, p.N, M, offsets, perm, (const u16*)x,
-                           (const u16*)v, normalize, means, raw_means, (u16*)xmax, (u16*)xmin,
+                           (const u16*)v, means, raw_means, (u16*)xmax, (u16*)xmin,
                            (u16*)x_perm, (u16*)v_perm);
     } else {
-        auto k = p.D == 64 ? gather_stats_kernel<float, 64> : gather_stats_kernel<float, 128>;
+        auto k = normalize ? (p.D == 64 ? gather_stats_kernel<float, 64, true> : gather_stats_kernel<float, 128, true>)
+                           : (p.D == 64 ? gather_stats_kernel<float, 64, false> : gather_stats_kernel<float, 128, false>);
         hipLaunchKernelGGL(k, grid, dim3(256), 0, s, p.N, M, offsets, perm, (const float*)x,
-                           (const float*)v, normalize, means, raw_means, (float*)xmax,
+                           (const float*)v, means, raw_means, (float*)xmax,
                            (float*)xmin, (float*)x_perm, (float*)v_perm);
     }
     return hipGetLastError();

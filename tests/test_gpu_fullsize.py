@@ -97,6 +97,13 @@ def test_query_clusters_layout_and_means(layer):
         q = synth.as_f32(g["q"][0, h])
         qhat = oracle.normalize(q)
         lab = Q["assign"][0, h]
+        # every cluster's means over the GPU labels, bit for bit (normalized rows
+        # rounded to f32, f64 sums in row order, one rounding)
+        cent, sizes = oracle.update(qhat, lab, Q["centroids"][0, h])
+        assert np.array_equal(Q["sizes"][0, h], sizes)
+        assert np.array_equal(Q["centroids"][0, h], cent)
+        qrep, _ = oracle.update(q, lab, np.zeros((Cq, w.D), np.float32))
+        assert np.array_equal(Q["qrep"][0, h], qrep)
         for a in rng.choice(Cq, 40, replace=False):
             mem = np.flatnonzero(lab == a)
             if mem.size == 0:
