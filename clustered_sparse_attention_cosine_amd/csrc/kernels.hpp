@@ -219,6 +219,7 @@ hipError_t launch_scan_offsets(const Prob& p, const int32_t* cnt, int M, int32_t
 // null) only the first nrows[bh] rows of a head are sorted; heads with
 // active[bh] == 0 (active may be null) are skipped.
 constexpr int SORT_SEG = 4096;
+static_assert(SORT_SEG % 1024 == 0, "the ranking pass takes 1024 rows per step");
 int sort_segments(int N);
 hipError_t launch_counting_sort(const Prob& p, const int32_t* labels, int M, int32_t* seg_cnt,
                                 int32_t* total, int32_t* sizes, int32_t* offsets, int32_t* perm,

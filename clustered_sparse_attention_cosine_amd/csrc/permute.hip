@@ -94,10 +94,19 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(int M, int nseg, int32_t*
     if (j >= M || (active && !active[bh])) return;
     int32_t* c = seg_cnt + (int64_t)bh * nseg * M + j;
     int run = 0;
-    for (int sg = 0; sg < nseg; ++sg) {
-        const int v = c[(int64_t)sg * M];
-        c[(int64_t)sg * M] = run;
-        run += v;
+    // eight segments' counts loaded at once (clamped reads, so the loads are
+    // unconditional and in flight together), then scanned
+    for (int s0 = 0; s0 < nseg; s0 += 8) {
+        int v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = c[(int64_t)min(s0 + k, nseg - 1) * M];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (s0 + k < nseg) {
+                c[(int64_t)(s0 + k) * M] = run;
+                run += v[k];
+            }
+        }
     }
     total[(int64_t)bh * M + j] = run;
 }
@@ -125,9 +134,17 @@ __global__ __launch_bounds__(1024) void seg_rank_kernel(const int32_t* __restric
     const uint64_t lt = (l == 0) ? 0ull : (~0ull >> (64 - l));
     __syncthreads();
     const int beg = sg * SORT_SEG, end = min(n, beg + SORT_SEG);
-    for (int base = beg; base < end; base += 1024) {
+    // the segment's labels, all loads issued at once (clamped to the segment)
+    constexpr int IT = SORT_SEG / 1024;
+    int raws[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) raws[it] = lab_h[min(beg + it * 1024 + tid, end - 1)];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int base = beg + it * 1024;
+        if (base >= end) break;
         const int i = base + tid;
-        const int raw = i < end ? lab_h[i] : -1;
+        const int raw = i < end ? raws[it] : -1;
         const bool ok = raw >= 0 && raw < M;   // rows with out-of-range labels are left out
         const int lab = ok ? raw : 0;
         uint64_t m = __ballot(ok);
