@@ -491,21 +491,29 @@ __global__ __launch_bounds__(64 * W) void select_hist_kernel(int Cq, int Ck, con
                 }
             }
             const bool has = lr < n;
-            uint64_t M = 0;  // weight of the gathered keys >= kj
-#pragma unroll
-            for (int v = 0; v < W; ++v)
-                for (int p = 0; p < nv[v]; ++p) M += LK[v][p] >= kj ? (uint64_t)LE[v][p] : 0ull;
+            // weight of the gathered keys >= kj: entry i broadcast from lane i
+            // (registers, no LDS round trip per entry)
+            const int nu = __builtin_amdgcn_readfirstlane(n);
+            uint64_t M = 0;
+            for (int i = 0; i < nu; ++i) {
+                const uint32_t ki = (uint32_t)__builtin_amdgcn_readlane((int)kj, i);
+                const uint32_t ei = (uint32_t)__builtin_amdgcn_readlane((int)ej, i);
+                M += ki >= kj ? (uint64_t)ei : 0ull;
+            }
             T = wave_max_u32((has && above + M >= tq) ? kj : 0u);
             gt = above + wave_sum_u64((has && kj > T) ? (uint64_t)ej : 0ull);
             const uint64_t eT = TOPK ? 1ull : (uint64_t)sel_weight(key_value(T), mx);
             take = eT > 0 ? (tq - gt + eT - 1) / eT : ~0ull;
-            // the take-th tie by slot: its rank among the ties is take - 1
-            int rank = 0;
-#pragma unroll
-            for (int v = 0; v < W; ++v)
-                for (int p = 0; p < nv[v]; ++p) rank += (LK[v][p] == T && LS[v][p] < sj) ? 1 : 0;
+            // the take-th tie by slot: its rank among the ties is take - 1 (the
+            // ties are the lanes holding T; usually one)
             const bool tie = has && kj == T;
-            const uint64_t ntie = __popcll(__ballot(tie));
+            const uint64_t tmask = __ballot(tie);
+            int rank = 0;
+            for (uint64_t m = tmask; m; m &= m - 1) {
+                const int i = (int)__ffsll((unsigned long long)m) - 1;
+                rank += (uint32_t)__builtin_amdgcn_readlane((int)sj, i) < sj ? 1 : 0;
+            }
+            const uint64_t ntie = __popcll(tmask);
             if (take >= ntie) last_tie = Ck;
             else last_tie = (int)wave_max_u32((tie && (uint64_t)rank == take - 1) ? sj + 1 : 0u) - 1;
         } else {
