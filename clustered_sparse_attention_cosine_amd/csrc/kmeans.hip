@@ -1476,7 +1476,10 @@ hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* i
 // writer, so the sums do not depend on scheduling.
 // With ub (by token; may be null) the same walk also takes the largest ub of
 // each run: rad[slot] for whole clusters, part radii beside the part sums.
-template <typename T, int D>
+// LOOP (row lists whose size is on the device: the keys left in U, a few
+// percent of N): a capped grid whose waves walk W, W + 4 gridDim.x, ...
+constexpr int UPDATE_LOOP_BLOCKS = 32;
+template <typename T, int D, bool LOOP = false>
 __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__ X, int N, RowSet rs,
                                                            const float* __restrict__ inv_norm,
                                                            const int32_t* __restrict__ labels,
@@ -1496,9 +1499,8 @@ __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__
     if (rs.active && !rs.active[bh]) return;
     const int n = rs.nrows ? rs.nrows[bh] : N;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int wv = blockIdx.x * 4 + w;  // W
+    auto range = [&](const int wv) __attribute__((always_inline)) {  // wave range W = wv
     const int base = wv * 64;
-    if (base >= n) return;
     const int32_t* ord = order + (int64_t)bh * N;
     const int32_t* lab_h = labels + (int64_t)bh * N;
     const int r0 = base + l;
@@ -1579,27 +1581,33 @@ __global__ __launch_bounds__(256) void update_accum_kernel(const T* __restrict__
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     if (cur >= 0) flush(rows_here == 64 && cur == lab_next);
+    };
+    if constexpr (LOOP) {
+        for (int wv = blockIdx.x * 4 + w; wv * 64 < n; wv += gridDim.x * 4) range(wv);
+    } else {
+        const int wv = blockIdx.x * 4 + w;
+        if (wv * 64 < n) range(wv);
+    }
 }
 
 hipError_t launch_update_accum(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
                                const int32_t* labels, CentView cv, const int32_t* order,
                                hipStream_t s, const float* ub, float* rad, float* part_rad) {
     dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)p.BH);
+    // a row list with its size on the device walks wave ranges from a capped grid
+    const bool subset = rs.rows != nullptr && rs.nrows != nullptr;
+    if (subset) grid.x = min(grid.x, (unsigned)UPDATE_LOOP_BLOCKS);
+#define ADC_UPD(TT, DD)                                                                                   \
+    hipLaunchKernelGGL((subset ? update_accum_kernel<TT, DD, true> : update_accum_kernel<TT, DD, false>), grid, \
+                       dim3(256), 0, s, (const TT*)x, p.N, rs, inv_norm, labels, cv, order, ub, rad, part_rad)
     if (p.bf16) {
-        if (p.D == 64)
-            hipLaunchKernelGGL((update_accum_kernel<u16, 64>), grid, dim3(256), 0, s, (const u16*)x,
-                               p.N, rs, inv_norm, labels, cv, order, ub, rad, part_rad);
-        else
-            hipLaunchKernelGGL((update_accum_kernel<u16, 128>), grid, dim3(256), 0, s,
-                               (const u16*)x, p.N, rs, inv_norm, labels, cv, order, ub, rad, part_rad);
+        if (p.D == 64) ADC_UPD(u16, 64);
+        else ADC_UPD(u16, 128);
     } else {
-        if (p.D == 64)
-            hipLaunchKernelGGL((update_accum_kernel<float, 64>), grid, dim3(256), 0, s,
-                               (const float*)x, p.N, rs, inv_norm, labels, cv, order, ub, rad, part_rad);
-        else
-            hipLaunchKernelGGL((update_accum_kernel<float, 128>), grid, dim3(256), 0, s,
-                               (const float*)x, p.N, rs, inv_norm, labels, cv, order, ub, rad, part_rad);
+        if (p.D == 64) ADC_UPD(float, 64);
+        else ADC_UPD(float, 128);
     }
+#undef ADC_UPD
     return hipGetLastError();
 }
 
@@ -1700,7 +1708,10 @@ __global__ __launch_bounds__(256) void stage_dist_kernel(const T* __restrict__ x
     if (rs.active && !rs.active[bh]) return;
     const int n = rs.nrows ? rs.nrows[bh] : N;
     const int sub = threadIdx.x & 7;
-    const int r = blockIdx.x * 32 + (threadIdx.x >> 3);
+    // a row list (the keys left in U) comes with a capped grid: blocks of 32
+    // rows, grid-strided
+    for (int r0 = blockIdx.x * 32; r0 < n; r0 += gridDim.x * 32) {
+    const int r = r0 + (threadIdx.x >> 3);
     const bool ok = r < n;
     double s = 0.0;
     if (ok) {
@@ -1724,11 +1735,13 @@ __global__ __launch_bounds__(256) void stage_dist_kernel(const T* __restrict__ x
     s += __shfl_xor(s, 2);
     s += __shfl_xor(s, 4);
     if (ok && sub == 0) dist[(int64_t)bh * N + r] = sqrt(s);
+    }
 }
 
 hipError_t launch_stage_dist(const Prob& p, const void* k, RowSet rs, const int32_t* labels,
                              CentView cv, double* dist, hipStream_t s) {
     dim3 grid((unsigned)((p.N + 31) / 32), (unsigned)p.BH);
+    if (rs.rows && rs.nrows) grid.x = min(grid.x, 256u);
     if (p.bf16)
         hipLaunchKernelGGL(stage_dist_kernel<u16>, grid, dim3(256), 0, s, (const u16*)k, p.N, p.D,
                            rs, labels, cv, dist);
