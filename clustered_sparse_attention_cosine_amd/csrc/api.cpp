@@ -485,7 +485,9 @@ static int32_t cluster_k_impl(const adc_shape* shape, const adc_k_params* prm, c
             // the pruned final assignment
             int32_t* lab = t == 0 ? sw.lab0 : sw.labels_u;
             const SortScratch ss_t{sizes, offsets, t == 0 ? sw.perm0 : perm};
-            HIPCHK(lloyd(p, k, 0, rs, nullptr, cv, prm->iters, true, lab, w, s, nullptr, ss_t,
+            // from stage 1 on, slots at or past the stage's row count hold no
+            // centre (the init fills min(m_t, |U_t|)), so the contractions stop there
+            HIPCHK(lloyd(p, k, 0, rs, nullptr, cv, prm->iters, true, lab, w, s, t == 0 ? nullptr : S.nu, ss_t,
                          tr ? tr->last_centroids : nullptr, t == 0 && g_prune));
             if (tr) HIPCHK(launch_trace_stage(p, rs, lab, base, t, tr->stage_labels, tr->stage_base, s));
             HIPCHK(launch_stage_dist(p, k, rs, lab, cv, S.dist, s));

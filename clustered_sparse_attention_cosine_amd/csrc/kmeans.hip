@@ -1381,7 +1381,8 @@ static hipError_t launch_refine_full(const Prob& p, const void* x, int normalize
 // One thread per row: merges the best two keys of the centre-tile splits (ties
 // to the lowest slot, as across lanes) and settles the row.
 template <bool FOLD, bool F32X>
-__global__ __launch_bounds__(256) void assign_merge_kernel(int N, RowSet rs, int M, const int32_t* __restrict__ rec,
+__global__ __launch_bounds__(256) void assign_merge_kernel(int N, RowSet rs, int M, const int32_t* __restrict__ mcount,
+                                                           const int32_t* __restrict__ rec,
                                                            int nsplit, int tps, int32_t* __restrict__ labels,
                                                            FlagSet fs) {
     const int bh = blockIdx.y;
@@ -1389,7 +1390,9 @@ __global__ __launch_bounds__(256) void assign_merge_kernel(int N, RowSet rs, int
     const int n = rs.nrows ? rs.nrows[bh] : N;
     const int e = blockIdx.x * 256 + threadIdx.x;
     if (e >= n) return;
-    const int nz = min(nsplit, ((M + 63) / 64 + tps - 1) / tps);
+    // the splits that ran: those holding a tile of the head's first M slots
+    const int Mh = mcount ? min(mcount[bh], M) : M;
+    const int nz = min(nsplit, ((Mh + 63) / 64 + tps - 1) / tps);
     const int64_t P = (int64_t)gridDim.y * N, ix = (int64_t)bh * N + e;
     uint32_t k1 = 0xffffffffu, k2 = 0xffffffffu;
     int bj = 0;
@@ -1417,10 +1420,12 @@ hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* i
     dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)p.BH);
     const bool fold = !normalize && !inv_norm;  // rows not rescaled: folded assignment pass
     const int tiles_m = (cv.m + 63) / 64;
-    if (split > 1 && !mcount && tiles_m >= 2) {
+    if (split > 1 && tiles_m >= 2) {
         // few rows: the centre tiles are split over gridDim.z (at most 4, so the
         // 3 per split + 3 record planes fit in the candidate scratch), the best
         // two keys of every split go to that scratch and a merge settles the rows
+        // (with mcount, splits past a head's first mcount slots do not run and
+        // the merge leaves them out)
         const int ns = min(split, 4);
         const int tps = (tiles_m + ns - 1) / ns;
         const int nz = (tiles_m + tps - 1) / tps;
@@ -1433,7 +1438,7 @@ hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* i
         if ((e = hipGetLastError()) != hipSuccess) return e;
         auto mk = fold ? (p.bf16 ? assign_merge_kernel<true, false> : assign_merge_kernel<true, true>)
                        : (p.bf16 ? assign_merge_kernel<false, false> : assign_merge_kernel<false, true>);
-        hipLaunchKernelGGL(mk, grid, dim3(256), 0, s, p.N, rs, cv.m, (const int32_t*)fs.cand, nz, tps,
+        hipLaunchKernelGGL(mk, grid, dim3(256), 0, s, p.N, rs, cv.m, mcount, (const int32_t*)fs.cand, nz, tps,
                            labels, fs);
     } else if (cv.cbits) {
         if (fold)
