@@ -459,21 +459,34 @@ __device__ __forceinline__ int v_scale_exp(uint32_t vmax_bits) {
 }
 __device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
 
-// Largest bf16 magnitude (as its bit pattern, which orders finite values) per head.
+// Largest bf16 magnitude (as its bit pattern, which orders finite values) per
+// head: each thread takes VMAX_PER 16-byte words, all loads in flight at once,
+// and each workgroup meets the others in one atomic.
+constexpr int VMAX_PER = 8;
 __global__ __launch_bounds__(256) void vmax_kernel(const u16* __restrict__ x, int64_t per_head8,
                                                    uint32_t* __restrict__ vmax) {
     const int bh = blockIdx.y;
+    const uint4* xh = reinterpret_cast<const uint4*>(x + (int64_t)bh * per_head8 * 8);
+    const int64_t i0 = (int64_t)blockIdx.x * 256 * VMAX_PER + threadIdx.x;
+    uint4 r[VMAX_PER];
+#pragma unroll
+    for (int u = 0; u < VMAX_PER; ++u) {
+        const int64_t i = i0 + u * 256;
+        r[u] = i < per_head8 ? xh[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
     uint32_t m = 0;
-    const u16* xh = x + (int64_t)bh * per_head8 * 8;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < per_head8; i += (int64_t)gridDim.x * 256) {
-        const uint4 r = *reinterpret_cast<const uint4*>(xh + i * 8);
-        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int u = 0; u < VMAX_PER; ++u) {
+        const uint32_t w[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) m = max(m, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-    if ((threadIdx.x & 63) == 0) atomicMax(&vmax[bh], m);
+    __shared__ uint32_t wm[4];
+    if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) atomicMax(&vmax[bh], max(max(wm[0], wm[1]), max(wm[2], wm[3])));
 }
 
 __global__ __launch_bounds__(256) void planes_f16_kernel(const u16* __restrict__ x, int64_t per_head8,
@@ -519,7 +532,7 @@ hipError_t launch_planes(const Prob& p, const void* k, const void* v, u16* k_hi,
         const int64_t ph8 = (int64_t)p.N * p.D / 8;
         hipError_t e = fill_i32((int32_t*)vmax, p.BH, 0, s);
         if (e != hipSuccess) return e;
-        const unsigned gx = (unsigned)std::min<int64_t>((ph8 + 255) / 256, 64);
+        const unsigned gx = (unsigned)((ph8 + 256 * VMAX_PER - 1) / (256 * VMAX_PER));
         hipLaunchKernelGGL(vmax_kernel, dim3(gx, p.BH), dim3(256), 0, s, (const u16*)v, ph8, vmax);
         hipLaunchKernelGGL(planes_f16_kernel, dim3((unsigned)((ph8 + 255) / 256), p.BH), dim3(256), 0, s,
                            (const u16*)v, ph8, (const uint32_t*)vmax, v_hi);

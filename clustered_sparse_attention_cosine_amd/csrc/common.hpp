@@ -14,11 +14,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int WAVE = 64;
 
 // ------------------------------------------------------------------ bf16
-// Round-to-nearest-even float -> bf16 bit pattern (inputs here are finite).
+// Round-to-nearest-even float -> bf16 bit pattern (inputs here are finite). The
+// conversion is gfx950's v_cvt_pk_bf16_f32 (RNE, f32 denormals kept), which
+// the compiler emits for a float -> __bf16 cast; for finite inputs it equals
+// the integer rounding u + 0x7FFF + ((u >> 16) & 1) of the bit pattern.
 __device__ __forceinline__ u16 f2bf_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (u16)(u >> 16);
+    return __builtin_bit_cast(u16, (__bf16)f);
 }
 __device__ __forceinline__ float bf_bits2f(u16 b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ __bf16 f2bf(float f) { return __builtin_bit_cast(__bf16, f2bf_bits(f)); }
@@ -55,10 +56,9 @@ template <> __device__ __forceinline__ void load8<float>(const float* p, float (
 
 // Pack 8 floats to bf16x8 (RNE).
 __device__ __forceinline__ bf16x8 pack_bf16x8(const float (&v)[8]) {
-    bf16x8 r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = f2bf(v[i]);
-    return r;
+    typedef float f32x8 __attribute__((ext_vector_type(8)));
+    const f32x8 t = {v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
+    return __builtin_convertvector(t, bf16x8);  // four v_cvt_pk_bf16_f32
 }
 
 // Raw 16-byte load of 8 bf16 words as a bf16x8 operand.

@@ -22,10 +22,11 @@
 namespace adc {
 
 // Order-preserving 32-bit image of a float (larger float, larger image;
-// never 0 for a non-NaN value, so 0 can mark a slot without members).
+// never 0 for a non-NaN value, so 0 can mark a slot without members):
+// negative values have every bit flipped, others only the sign bit.
 __device__ __forceinline__ uint32_t order_key(float f) {
     const uint32_t u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 // inverse of order_key
 __device__ __forceinline__ float key_value(uint32_t k) {
@@ -33,112 +34,153 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 }
 
 // ------------------------------------------------------------------ scores
-// Grid: (Cq / 64, Ck / 256, BH); 4 waves, each 16 q-clusters x 256 slots.
+// A workgroup (4 waves, each 16 q-clusters) scores 64 q-clusters against a
+// chunk of tpw consecutive 64-slot tiles of one head. The query side is split
+// once and held in registers over the chunk; the key side of each tile is
+// staged in LDS, the next tile's loads in flight while the current one is
+// contracted.
+//
+// Work order. A column is (head, chunk): its nqb q-blocks all read the same
+// key statistics. Block b runs on XCD b % 8 (round-robin dispatch); columns
+// are dealt to the XCDs in turn and each XCD takes its columns one after
+// another, q-blocks fastest, so the statistics of the few columns in flight
+// on an XCD stay in its L2 while every q-block reads them.
+//
 // Output: the order key of what the selection ranks, per (q-cluster, slot):
 // l = S * scale + ln n_b for top-p (LOGN), the score S itself for top-k; 0 for
 // slots without members.
+template <typename TK, int D, int MODE>
+struct ScoreGeom {
+    static constexpr int KD = MODE == 0 ? 2 * D : D;             // contraction width
+    static constexpr int CPR = KD / 8;                           // 8-wide chunks per slot row
+    static constexpr int RPP = 256 / CPR;                        // slot rows per workgroup pass
+    static constexpr int NPASS = 64 / RPP;                       // passes per 64-slot tile
+    static constexpr bool SPLIT = (MODE == 1) || sizeof(TK) == 4;  // key side needs a split
+    static constexpr int RW = SPLIT ? 2 : 1;                     // 16-byte words per chunk
+};
+
 template <typename TK, int D, int MODE, bool LOGN>  // MODE 0: quest (width 2D), 1: centroid (width D)
-__global__ __launch_bounds__(256) void scores_kernel(int Cq, int Ck, const float* __restrict__ qrep,
+__global__ __launch_bounds__(256) void scores_kernel(int Cq, int Ck, int nkc, int ncols, int nqb, int tpw,
+                                                     const float* __restrict__ qrep,
                                                      const TK* __restrict__ kmax,
                                                      const TK* __restrict__ kmin,
                                                      const float* __restrict__ kcent,
                                                      const int32_t* __restrict__ k_sizes,
                                                      const int32_t* __restrict__ n_clusters,
                                                      float scale, uint32_t* __restrict__ keys) {
-    constexpr int KD = MODE == 0 ? 2 * D : D;
+    using G = ScoreGeom<TK, D, MODE>;
+    constexpr int KD = G::KD;
     constexpr int KC = KD / 32;
-    constexpr bool AF32 = (MODE == 1) || sizeof(TK) == 4;  // key side needs a split
-    constexpr int KA = AF32 ? 3 : 1;
+    constexpr int KA = G::SPLIT ? 3 : 1;
     constexpr int LD = KD + 8;
     __shared__ __attribute__((aligned(16))) u16 sa[KA][64 * LD];
+    __shared__ __attribute__((aligned(16))) float lgn[64];      // ln n (top-p) or 0
+    __shared__ __attribute__((aligned(16))) uint32_t lmask[64];  // ~0 for a slot with members
 
-    const int bh = blockIdx.z;
+    const int xcd = blockIdx.x & 7, jb = blockIdx.x >> 3;
+    const int cl = jb / nqb, qb = jb - cl * nqb;
+    const int col = cl * 8 + xcd;
+    if (col >= ncols) return;
+    const int bh = col / nkc, chunk = col - bh * nkc;
+    const int t0 = chunk * tpw;
+    const int ntl = min(tpw, (Ck + 63) / 64 - t0);  // >= 1: chunk < nkc
+
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c16 = l & 15;
-    const int a = blockIdx.x * 64 + w * 16 + c16;
+    const int a = qb * 64 + w * 16 + c16;
     const bool aok = a < Cq;
     const int ncl = min(n_clusters[bh], Ck);
 
+    // key side: this thread's chunk column and its rows tid / CPR + RPP p
+    const int col8 = tid % G::CPR, row0 = tid / G::CPR, k0 = col8 * 8;
+    const TK* ksrc;
+    if constexpr (MODE == 0) ksrc = (k0 < D ? kmax + k0 : kmin + (k0 - D)) + (int64_t)bh * Ck * D;
+    else ksrc = reinterpret_cast<const TK*>(kcent + k0 + (int64_t)bh * Ck * D);
+    u32x4 raw[G::NPASS * G::RW];
+    // the key-side words of tile t of the chunk into raw (clamped to the last slot)
+#define ADC_LOAD_TILE(t)                                                                   \
+    do {                                                                                   \
+        _Pragma("unroll") for (int ps = 0; ps < G::NPASS; ++ps) {                          \
+            const int slot = min((t0 + (t)) * 64 + row0 + G::RPP * ps, Ck - 1);            \
+            const u32x4* src = reinterpret_cast<const u32x4*>(ksrc + (int64_t)slot * D);   \
+            _Pragma("unroll") for (int r = 0; r < G::RW; ++r) raw[ps * G::RW + r] = src[r]; \
+        }                                                                                  \
+    } while (0)
+    ADC_LOAD_TILE(0);
+
     // query side: 3-term split of [q+, q-] (or q); each 8-wide chunk lies in
     // one half of the width, read as two 16-byte loads
-    bf16x8 qb[3][KC];
+    bf16x8 qb3[3][KC];
     const float* qp = qrep + ((int64_t)bh * Cq + (aok ? a : 0)) * D;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-        const int k0 = kc * 32 + g * 8;
+        const int q0 = kc * 32 + g * 8;
         float v[8];
-        load8<float>(qp + (k0 < D ? k0 : k0 - D), v);
+        load8<float>(qp + (q0 < D ? q0 : q0 - D), v);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             float x = aok ? v[i] : 0.0f;
-            if (MODE == 0) x = k0 < D ? fmaxf(x, 0.0f) : fminf(x, 0.0f);
+            if (MODE == 0) x = q0 < D ? fmaxf(x, 0.0f) : fminf(x, 0.0f);
             v[i] = x;
         }
         float r1[8], r2[8];
-        qb[0][kc] = pack_bf16x8(v);
+        qb3[0][kc] = pack_bf16x8(v);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) r1[i] = v[i] - bf2f(qb[0][kc][i]);
-        qb[1][kc] = pack_bf16x8(r1);
+        for (int i = 0; i < 8; ++i) r1[i] = v[i] - bf2f(qb3[0][kc][i]);
+        qb3[1][kc] = pack_bf16x8(r1);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) r2[i] = r1[i] - bf2f(qb[1][kc][i]);
-        qb[2][kc] = pack_bf16x8(r2);
+        for (int i = 0; i < 8; ++i) r2[i] = r1[i] - bf2f(qb3[1][kc][i]);
+        qb3[2][kc] = pack_bf16x8(r2);
     }
 
-    // per staged slot: ln n (top-p) or 0 (top-k), NaN for a slot without members
-    __shared__ float lgn[64];
     const int32_t* ksz = k_sizes + (int64_t)bh * Ck;
-    for (int tile = 0; tile < 4; ++tile) {
-        const int b0 = blockIdx.y * 256 + tile * 64;
-        if (b0 >= Ck) break;
-        __syncthreads();
+    uint32_t* const dst = keys + ((int64_t)bh * Cq + (aok ? a : 0)) * Ck;
+    const bool vec4 = (Ck & 3) == 0;  // rows 16-byte aligned: whole 4-slot groups stored at once
+    for (int t = 0; t < ntl; ++t) {
+        const int b0 = (t0 + t) * 64;
+        __syncthreads();  // the previous tile is no longer read
         if (tid < 64) {
             const int b = b0 + tid;
             const int n = b < Ck ? ksz[b] : 0;
-            lgn[tid] = (b < ncl && n > 0) ? (LOGN ? logf((float)n) : 0.0f) : __builtin_nanf("");
+            const bool live = b < ncl && n > 0;
+            lgn[tid] = (live && LOGN) ? logf((float)n) : 0.0f;
+            lmask[tid] = live ? ~0u : 0u;
         }
-        // stage 64 slots x KD of the key side (KA terms); bf16 statistics are
-        // copied as they are
-        for (int c = tid; c < 64 * (KD / 8); c += 256) {
-            const int row = c / (KD / 8), col8 = c % (KD / 8);
-            const int b = b0 + row;
-            if constexpr (MODE == 0 && KA == 1) {
-                uint4 r = make_uint4(0u, 0u, 0u, 0u);
-                if (b < Ck) {
-                    const int k0 = col8 * 8;
-                    const int64_t base = ((int64_t)bh * Ck + b) * D;
-                    const TK* src = k0 < D ? kmax + base + k0 : kmin + base + (k0 - D);
-                    r = *reinterpret_cast<const uint4*>(src);
-                }
-                *reinterpret_cast<uint4*>(&sa[0][row * LD + col8 * 8]) = r;
+#pragma unroll
+        for (int ps = 0; ps < G::NPASS; ++ps) {
+            u16* d0 = &sa[0][(row0 + G::RPP * ps) * LD + k0];
+            if constexpr (!G::SPLIT) {
+                // bf16 statistics are copied as they are
+                *reinterpret_cast<u32x4*>(d0) = raw[ps];
             } else {
                 float v[8];
-                if (b < Ck) {
-                    const int k0 = col8 * 8;
-                    const int64_t base = ((int64_t)bh * Ck + b) * D;
-                    if (MODE == 0) {
-                        const TK* src = k0 < D ? kmax + base + k0 : kmin + base + (k0 - D);
-                        load8<TK>(src, v);
-                    } else {
-                        load8<float>(kcent + base + k0, v);
-                    }
+                if constexpr (G::RW == 2) {
+                    const float4 x0 = __builtin_bit_cast(float4, raw[2 * ps]);
+                    const float4 x1 = __builtin_bit_cast(float4, raw[2 * ps + 1]);
+                    v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+                    v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
                 } else {
+                    const uint32_t wd[4] = {raw[ps].x, raw[ps].y, raw[ps].z, raw[ps].w};
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+                    for (int i = 0; i < 4; ++i) {
+                        v[2 * i] = __uint_as_float(wd[i] << 16);
+                        v[2 * i + 1] = __uint_as_float(wd[i] & 0xFFFF0000u);
+                    }
                 }
-                bf16x8 t0 = pack_bf16x8(v);
-                *reinterpret_cast<bf16x8*>(&sa[0][row * LD + col8 * 8]) = t0;
-                if constexpr (KA == 3) {
-                    float r1[8], r2[8];
+                const bf16x8 s0 = pack_bf16x8(v);
+                float r1[8], r2[8];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) r1[i] = v[i] - bf2f(t0[i]);
-                    bf16x8 t1 = pack_bf16x8(r1);
+                for (int i = 0; i < 8; ++i) r1[i] = v[i] - bf2f(s0[i]);
+                const bf16x8 s1 = pack_bf16x8(r1);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) r2[i] = r1[i] - bf2f(t1[i]);
-                    *reinterpret_cast<bf16x8*>(&sa[1][row * LD + col8 * 8]) = t1;
-                    *reinterpret_cast<bf16x8*>(&sa[KA - 1][row * LD + col8 * 8]) = pack_bf16x8(r2);
-                }
+                for (int i = 0; i < 8; ++i) r2[i] = r1[i] - bf2f(s1[i]);
+                const int o = (row0 + G::RPP * ps) * LD + k0;
+                *reinterpret_cast<bf16x8*>(&sa[0][o]) = s0;
+                *reinterpret_cast<bf16x8*>(&sa[1][o]) = s1;
+                *reinterpret_cast<bf16x8*>(&sa[KA - 1][o]) = pack_bf16x8(r2);
             }
         }
         __syncthreads();
+        if (t + 1 < ntl) ADC_LOAD_TILE(t + 1);  // in flight during the contraction
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -147,57 +189,63 @@ __global__ __launch_bounds__(256) void scores_kernel(int Cq, int Ck, const float
                 const int off = (cb * 16 + c16) * LD + kc * 32 + g * 8;
                 const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&sa[0][off]);
                 // smallest terms first
-                acc = mfma16(a0, qb[2][kc], acc);
-                acc = mfma16(a0, qb[1][kc], acc);
+                acc = mfma16(a0, qb3[2][kc], acc);
+                acc = mfma16(a0, qb3[1][kc], acc);
                 if constexpr (KA == 3) {
                     const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&sa[1][off]);
                     const bf16x8 a2 = *reinterpret_cast<const bf16x8*>(&sa[KA - 1][off]);
-                    acc = mfma16(a2, qb[0][kc], acc);
-                    acc = mfma16(a1, qb[1][kc], acc);
-                    acc = mfma16(a1, qb[0][kc], acc);
+                    acc = mfma16(a2, qb3[0][kc], acc);
+                    acc = mfma16(a1, qb3[1][kc], acc);
+                    acc = mfma16(a1, qb3[0][kc], acc);
                 }
-                acc = mfma16(a0, qb[0][kc], acc);
+                acc = mfma16(a0, qb3[0][kc], acc);
             }
             // lane holds slots b0 + cb*16 + 4g + i for q-cluster a: one 16-byte
-            // store (and one 16-byte read of the slot sizes) where the four fit
+            // store where the four fit
             if (aok) {
-                uint32_t* dst = keys + ((int64_t)bh * Cq + a) * Ck;
                 const int b = b0 + cb * 16 + g * 4;
                 const float4 lg4 = *reinterpret_cast<const float4*>(&lgn[cb * 16 + g * 4]);
-                const float lg[4] = {lg4.x, lg4.y, lg4.z, lg4.w};
-                auto key_of = [&](int i) __attribute__((always_inline)) -> uint32_t {
-                    if (lg[i] != lg[i]) return 0u;
-                    return order_key(LOGN ? fmaf(acc[i], scale, lg[i]) : acc[i]);
-                };
-                if (b + 3 < Ck && (reinterpret_cast<uintptr_t>(dst + b) & 15) == 0) {
-                    uint4 out;
-                    out.x = key_of(0);
-                    out.y = key_of(1);
-                    out.z = key_of(2);
-                    out.w = key_of(3);
-                    *reinterpret_cast<uint4*>(dst + b) = out;
+                const uint4 m4 = *reinterpret_cast<const uint4*>(&lmask[cb * 16 + g * 4]);
+                uint4 out;
+                out.x = order_key(LOGN ? fmaf(acc[0], scale, lg4.x) : acc[0]) & m4.x;
+                out.y = order_key(LOGN ? fmaf(acc[1], scale, lg4.y) : acc[1]) & m4.y;
+                out.z = order_key(LOGN ? fmaf(acc[2], scale, lg4.z) : acc[2]) & m4.z;
+                out.w = order_key(LOGN ? fmaf(acc[3], scale, lg4.w) : acc[3]) & m4.w;
+                if (vec4) {
+                    if (b < Ck) *reinterpret_cast<uint4*>(dst + b) = out;
                 } else {
+                    const uint32_t o4[4] = {out.x, out.y, out.z, out.w};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        if (b + i < Ck) dst[b + i] = key_of(i);
-                    }
+                    for (int i = 0; i < 4; ++i)
+                        if (b + i < Ck) dst[b + i] = o4[i];
                 }
             }
         }
     }
 }
 
+#undef ADC_LOAD_TILE
+
 hipError_t launch_scores(const Prob& p, int Cq, int Ck, const float* qrep, const void* kmax,
                          const void* kmin, const float* kcent, int score_mode, bool logn, float scale,
                          const int32_t* k_sizes, const int32_t* n_clusters, uint32_t* keys,
                          hipStream_t s) {
-    dim3 grid((unsigned)((Cq + 63) / 64), (unsigned)((Ck + 255) / 256), (unsigned)p.BH);
+    // tiles per workgroup: the largest of 16, 8, 4, 2, 1 that still gives 2048
+    // workgroups (the query split is amortised over the chunk; below that the
+    // grid would not fill the chip)
+    const int nqb = (Cq + 63) / 64;
+    const int ntiles = (Ck + 63) / 64;
+    int tpw = 16;
+    while (tpw > 1 && (int64_t)p.BH * nqb * ((ntiles + tpw - 1) / tpw) < 2048) tpw >>= 1;
+    const int nkc = (ntiles + tpw - 1) / tpw;
+    const int ncols = p.BH * nkc;
+    const dim3 grid((unsigned)(8 * ((ncols + 7) / 8) * nqb));
 #define ADC_SCORES(TK, MODE, KMAX, KMIN)                                                              \
     do {                                                                                            \
         auto k = p.D == 64 ? (logn ? scores_kernel<TK, 64, MODE, true> : scores_kernel<TK, 64, MODE, false>)   \
                            : (logn ? scores_kernel<TK, 128, MODE, true> : scores_kernel<TK, 128, MODE, false>); \
-        hipLaunchKernelGGL(k, grid, dim3(256), 0, s, Cq, Ck, qrep, (const TK*)(KMAX), (const TK*)(KMIN),  \
-                           kcent, k_sizes, n_clusters, scale, keys);                                  \
+        hipLaunchKernelGGL(k, grid, dim3(256), 0, s, Cq, Ck, nkc, ncols, nqb, tpw, qrep, (const TK*)(KMAX), \
+                           (const TK*)(KMIN), kcent, k_sizes, n_clusters, scale, keys);               \
     } while (0)
     if (score_mode == 0) {
         if (p.bf16)
