@@ -124,6 +124,11 @@ struct KmeansWs {
     float* part_rad = nullptr;
     uint32_t* cbits = nullptr;
     int cwords = 0;
+    // row-subset rounds (later key stages): each row's previous label, and per
+    // head whether it is still iterating and whether a label changed
+    int32_t* prev_lab = nullptr;
+    uint8_t* lact = nullptr;
+    int32_t* chg = nullptr;
 };
 
 void plan_kmeans(Carver& c, const Prob& p, int cap, bool want_inv, bool kpp, bool want_xhat,
@@ -244,8 +249,20 @@ hipError_t lloyd(const Prob& p, const void* x, int normalize, RowSet rs, const f
         fs.ub = w.ub;
         fs.lb = w.lb;
     }
+    // Row subsets (the later key stages): a head whose round leaves every label
+    // as the previous round left it has reached its fixed point: the update
+    // would give the centres it already holds and every later round the same
+    // labels again. It is marked done on the device (rl.active), and the
+    // remaining kernels of its rounds return at once; results are those of
+    // running every round.
+    const bool conv = rs.rows && w.lact;
+    RowSet rl = rs;
+    if (conv) {
+        if ((e = launch_conv_init(p, rs.active, w.lact, w.chg, s))) return e;
+        rl.active = w.lact;
+    }
     for (int it = 0; it < iters; ++it) {
-        RowSet ra = rs;
+        RowSet ra = rl;
         CentView ca = cv;
         if (bounds && it > 0) {
             if (g_prune) {
@@ -268,21 +285,22 @@ hipError_t lloyd(const Prob& p, const void* x, int normalize, RowSet rs, const f
                                it > 0)))
             return e;
         if (it + 1 < iters || final_update) {
+            if (conv && (e = launch_conv_round(p, rl, labels, w.prev_lab, w.lact, w.chg, it > 0, s))) return e;
             // the next round's candidate sets need each cluster's radius (the
             // largest upper bound of its rows), taken by the same sorted walk
             const bool keep = it + 1 < iters || final_radii;  // bounds move on
             const bool radii = bounds && g_prune && keep;
             if ((e = launch_counting_sort(p, labels, cv.m, w.seg_cnt, w.hist, ss.sizes, ss.offsets, ss.perm,
-                                          s, rs.nrows, rs.active)))
+                                          s, rl.nrows, rl.active)))
                 return e;
-            if ((e = launch_update_accum(p, x, rs, inv_norm, labels, cv, ss.perm, s, radii ? w.ub : nullptr,
+            if ((e = launch_update_accum(p, x, rl, inv_norm, labels, cv, ss.perm, s, radii ? w.ub : nullptr,
                                          w.rad, w.part_rad)))
                 return e;
             if (bounds && keep) {
-                if ((e = launch_finalize(p, cv, rs.active, ss.offsets, s, w.drift, w.flag_count, w.over_count,
+                if ((e = launch_finalize(p, cv, rl.active, ss.offsets, s, w.drift, w.flag_count, w.over_count,
                                          w.rcount, radii ? w.rad : nullptr, w.part_rad)))
                     return e;
-            } else if ((e = launch_finalize(p, cv, rs.active, ss.offsets, s, nullptr, w.flag_count,
+            } else if ((e = launch_finalize(p, cv, rl.active, ss.offsets, s, nullptr, w.flag_count,
                                             w.over_count))) {
                 return e;
             }
@@ -402,7 +420,12 @@ static void plan_k(Carver& c, const adc_shape* shape, const adc_k_params* prm, K
                    StageWs& sw) {
     Prob p = make_prob(shape);
     plan_kmeans(c, p, prm->max_clusters, false, prm->init == ADC_INIT_KMEANSPP, false, w);
-    if (prm->adaptive == ADC_K_STAGED) plan_stages(c, p, sw);
+    if (prm->adaptive == ADC_K_STAGED) {
+        plan_stages(c, p, sw);
+        w.prev_lab = c.take<int32_t>((size_t)p.BH * p.N);
+        w.lact = c.take<uint8_t>(p.BH);
+        w.chg = c.take<int32_t>(p.BH);
+    }
 }
 
 size_t adacluster_cluster_k_workspace(const adc_shape* shape, const adc_k_params* prm) {

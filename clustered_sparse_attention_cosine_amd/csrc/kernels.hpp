@@ -95,6 +95,12 @@ hipError_t launch_finalize(const Prob& p, CentView cv, const uint8_t* active, co
                            hipStream_t s, float* drift = nullptr, int32_t* zero_a = nullptr,
                            int32_t* zero_b = nullptr, int32_t* zero_c = nullptr,
                            float* rad = nullptr, const float* part_rad = nullptr);
+// Fixed points of Lloyd rounds over row subsets (see kmeans.hip): lact = active
+// (1 for all without), chg = 0; after each round's assignment prev <- labels,
+// and from the second round a head whose labels all stayed gets lact = 0.
+hipError_t launch_conv_init(const Prob& p, const uint8_t* active, uint8_t* lact, int32_t* chg, hipStream_t s);
+hipError_t launch_conv_round(const Prob& p, RowSet rs, const int32_t* labels, int32_t* prev, uint8_t* lact,
+                             int32_t* chg, bool compare, hipStream_t s);
 // Flag lists of the certified assignment (see kmeans.hip).
 struct FlagSet {
     int32_t* list;

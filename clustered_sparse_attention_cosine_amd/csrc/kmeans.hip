@@ -1408,6 +1408,64 @@ __global__ __launch_bounds__(256) void assign_merge_kernel(int N, RowSet rs, int
                               __int_as_float(rec[(3 * nsplit + 1) * P + ix]), bh, N, e, rs, labels, fs);
 }
 
+// ------------------------------------------------------------------ fixed points
+// Lloyd rounds over a row subset (the later key stages): lact[bh] says whether
+// head bh still iterates. A round whose labels all equal the previous round's
+// leaves the head at its fixed point (the update would reproduce the centres,
+// every later round the labels), so the head's remaining round kernels can
+// return at once.
+__global__ void conv_init_kernel(int BH, const uint8_t* __restrict__ active, uint8_t* __restrict__ lact,
+                                 int32_t* __restrict__ chg) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < BH) {
+        lact[i] = active ? active[i] : 1;
+        chg[i] = 0;
+    }
+}
+
+// prev <- labels over the head's rows; with compare, chg[bh] = 1 if any differed
+__global__ __launch_bounds__(256) void label_cmp_kernel(int N, RowSet rs, const int32_t* __restrict__ labels,
+                                                        int32_t* __restrict__ prev, int32_t* __restrict__ chg,
+                                                        int compare) {
+    const int bh = blockIdx.y;
+    if (rs.active && !rs.active[bh]) return;
+    const int n = rs.nrows ? rs.nrows[bh] : N;
+    bool diff = false;
+    for (int r = blockIdx.x * 256 + threadIdx.x; r < n; r += gridDim.x * 256) {
+        const int64_t ix = (int64_t)bh * N + (rs.by_token ? rs.rows[(int64_t)bh * N + r] : r);
+        const int lab = labels[ix];
+        diff |= compare && prev[ix] != lab;
+        prev[ix] = lab;
+    }
+    if (__ballot(diff) != 0 && (threadIdx.x & 63) == 0) chg[bh] = 1;
+}
+
+// after a compared round: a head whose labels did not change stops
+__global__ void conv_step_kernel(int BH, uint8_t* __restrict__ lact, int32_t* __restrict__ chg) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < BH) {
+        if (lact[i] && chg[i] == 0) lact[i] = 0;
+        chg[i] = 0;
+    }
+}
+
+hipError_t launch_conv_init(const Prob& p, const uint8_t* active, uint8_t* lact, int32_t* chg, hipStream_t s) {
+    hipLaunchKernelGGL(conv_init_kernel, dim3((unsigned)((p.BH + 255) / 256)), dim3(256), 0, s, p.BH, active,
+                       lact, chg);
+    return hipGetLastError();
+}
+
+hipError_t launch_conv_round(const Prob& p, RowSet rs, const int32_t* labels, int32_t* prev, uint8_t* lact,
+                             int32_t* chg, bool compare, hipStream_t s) {
+    const unsigned gx = (unsigned)std::min(32, (p.N + 255) / 256);
+    hipLaunchKernelGGL(label_cmp_kernel, dim3(gx, (unsigned)p.BH), dim3(256), 0, s, p.N, rs, labels, prev, chg,
+                       compare ? 1 : 0);
+    if (compare)
+        hipLaunchKernelGGL(conv_step_kernel, dim3((unsigned)((p.BH + 255) / 256)), dim3(256), 0, s, p.BH, lact,
+                           chg);
+    return hipGetLastError();
+}
+
 hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* inv_norm,
                          int normalize, CentView cv, const int32_t* mcount, int32_t* labels,
                          FlagSet fs, hipStream_t s, int split, bool counts_zeroed) {

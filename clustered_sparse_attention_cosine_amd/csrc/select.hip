@@ -16,6 +16,7 @@
 // index order until the mass reaches top_p. Top-k takes the k largest scores
 // by the same rule with unit weights.
 #include <math.h>
+#include <mutex>
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -674,19 +675,41 @@ __global__ __launch_bounds__(64 * W) void select_hist_kernel(int Cq, int Ck, con
     }
 }
 
+// Workgroups of `threads` threads of kernel k resident at once on the current
+// device (its compute units times what registers and LDS allow per unit);
+// found once per (kernel, device).
+static int resident_blocks(const void* k, int threads) {
+    struct Entry { const void* k; int dev, n; };
+    static Entry cache[64];
+    static int used = 0;
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+        if (cache[i].k == k && cache[i].dev == dev) return cache[i].n;
+    int cus = 256, per_cu = 1, n = 0, b = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) cus = n;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k, threads, 0) == hipSuccess && b > 0) per_cu = b;
+    if (used < 64) cache[used++] = Entry{k, dev, cus * per_cu};
+    return cus * per_cu;
+}
+
 template <bool TOPK>
 static void launch_select_t(const Prob& p, int Cq, int Ck, const uint32_t* keys, const int32_t* k_sizes,
                             const uint8_t* full, float scale, float top_p, int top_k, uint32_t* mask,
                             int32_t* sel_keys, hipStream_t s) {
     const int W = (Ck + 64 * SEL_KPL - 1) / (64 * SEL_KPL);
-    // about 3072 / W workgroups of W waves (three waves per SIMD over the
-    // chip, what the registers allow), each over a strided share of one
+    // as many workgroups of W waves as are resident at once over the chip
+    // (no second, partly filled round), each over a strided share of one
     // head's rows
-    const int per_head = max(1, min(Cq, (3072 / W + p.BH - 1) / p.BH));
-    const dim3 grid((unsigned)per_head, (unsigned)p.BH);
-#define ADC_SEL(WW)                                                                                     \
-    hipLaunchKernelGGL((select_hist_kernel<TOPK, WW>), grid, dim3(64 * WW), 0, s, Cq, Ck, keys, k_sizes, \
-                       full, scale, top_p, top_k, mask, sel_keys)
+#define ADC_SEL(WW)                                                                                      \
+    do {                                                                                                 \
+        auto k = select_hist_kernel<TOPK, WW>;                                                           \
+        const int per_head = max(1, min(Cq, resident_blocks((const void*)k, 64 * WW) / p.BH));          \
+        hipLaunchKernelGGL(k, dim3((unsigned)per_head, (unsigned)p.BH), dim3(64 * WW), 0, s, Cq, Ck,    \
+                           keys, k_sizes, full, scale, top_p, top_k, mask, sel_keys);                    \
+    } while (0)
     if (W <= 1)
         ADC_SEL(1);
     else if (W <= 2)
