@@ -923,6 +923,14 @@ __device__ __forceinline__ void assign_settle(uint32_t k1, uint32_t k2, int bj, 
 // the certificate and the row's upper bound are those of the full
 // contraction; the lower bound covers only the gathered centres and is not
 // used after a pruned round.
+#ifndef ADC_CAND_BLOCKS
+#define ADC_CAND_BLOCKS 8
+#endif
+#ifndef ADC_CAND_TPS
+#define ADC_CAND_TPS 2
+#endif
+constexpr int CAND_BLOCKS = ADC_CAND_BLOCKS;  // candidate pass: workgroups per head along the rows
+constexpr int CAND_TPS = ADC_CAND_TPS;        // and 64-slot centre tiles per workgroup
 template <typename T, int D, bool F32X, bool CAND, bool FOLD, bool GATHER>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && !F32X ? 4 : 1, 8)))
 void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
@@ -943,8 +951,7 @@ void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
     const int bh = blockIdx.y;
     if (rs.active && !rs.active[bh]) return;
     const int n = CAND ? fs.count[bh] : (rs.nrows ? rs.nrows[bh] : N);
-    const int row_base = blockIdx.x * 256;
-    if (row_base >= n) return;
+    if ((int)blockIdx.x * 256 >= n) return;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c16 = l & 15;
     const int M = mcount ? min(mcount[bh], cv.m) : cv.m;
     const int64_t cbase = (int64_t)bh * cv.cap + cv.base;
@@ -953,6 +960,11 @@ void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
     const int t_begin = tsplit ? blockIdx.z * tiles_per_split : 0;
     const int t_end = tsplit ? min(ntiles_all, t_begin + tiles_per_split) : ntiles_all;
     if (tsplit && t_begin >= t_end) return;
+    // one 256-row block (CAND: a small grid walks the flagged rows' blocks x,
+    // x + gridDim.x, ... through the jump at the end; every other pass covers
+    // its one block and has no such jump)
+    int row_base = blockIdx.x * 256;
+[[maybe_unused]] next_block:
 
     bf16x8 xh[4][KC];
     bf16x8 xl[4][F32X ? KC : 1];
@@ -1227,6 +1239,11 @@ void assign_kernel(const T* __restrict__ X, int N, RowSet rs,
                 }
             }
         }
+    }
+    if constexpr (CAND) {
+        __syncthreads();  // the next block reuses the LDS tiles
+        row_base += (int)gridDim.x * 256;
+        if (row_base < n) goto next_block;
     }
 }
 
@@ -1509,12 +1526,13 @@ hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* i
         launch_assign_t<false, false>(p, grid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, 0, s);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // candidate pass: the centre tiles of the flagged rows are split 8 per workgroup
-    // (over every slot, also after a pruned pass)
-    constexpr int TPS = 8;
+    // candidate pass over every slot (also after a pruned pass): the flagged rows
+    // are a few percent, so a grid of CAND_BLOCKS workgroups per head walks their
+    // 256-row blocks, and the centre tiles are split CAND_TPS per workgroup
     const int tiles = (cv.m + 63) / 64;
-    dim3 cgrid((unsigned)((p.N + 255) / 256), (unsigned)p.BH, (unsigned)((tiles + TPS - 1) / TPS));
-    launch_assign_t<true, false>(p, cgrid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, TPS, s);
+    const int cbx = std::min(CAND_BLOCKS, (p.N + 255) / 256);
+    dim3 cgrid((unsigned)cbx, (unsigned)p.BH, (unsigned)((tiles + CAND_TPS - 1) / CAND_TPS));
+    launch_assign_t<true, false>(p, cgrid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, CAND_TPS, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 egrid(32, (unsigned)p.BH);
     if (p.bf16) {
