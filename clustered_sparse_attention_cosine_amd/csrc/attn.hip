@@ -460,26 +460,30 @@ __device__ __forceinline__ int v_scale_exp(uint32_t vmax_bits) {
 __device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
 
 // Largest bf16 magnitude (as its bit pattern, which orders finite values) per
-// head: each thread takes VMAX_PER 16-byte words, all loads in flight at once,
-// and each workgroup meets the others in one atomic.
+// head: VMAX_WG workgroups per head, each thread with VMAX_PER independent
+// 16-byte loads in flight per step, and one atomic per workgroup (atomics on
+// one address serialise, so their number is kept small).
 constexpr int VMAX_PER = 8;
+constexpr int VMAX_WG = 32;
 __global__ __launch_bounds__(256) void vmax_kernel(const u16* __restrict__ x, int64_t per_head8,
                                                    uint32_t* __restrict__ vmax) {
     const int bh = blockIdx.y;
     const uint4* xh = reinterpret_cast<const uint4*>(x + (int64_t)bh * per_head8 * 8);
-    const int64_t i0 = (int64_t)blockIdx.x * 256 * VMAX_PER + threadIdx.x;
-    uint4 r[VMAX_PER];
-#pragma unroll
-    for (int u = 0; u < VMAX_PER; ++u) {
-        const int64_t i = i0 + u * 256;
-        r[u] = i < per_head8 ? xh[i] : make_uint4(0u, 0u, 0u, 0u);
-    }
+    const int64_t stride = (int64_t)gridDim.x * 256;
     uint32_t m = 0;
+    for (int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x; i0 < per_head8; i0 += VMAX_PER * stride) {
+        uint4 r[VMAX_PER];
 #pragma unroll
-    for (int u = 0; u < VMAX_PER; ++u) {
-        const uint32_t w[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
+        for (int u = 0; u < VMAX_PER; ++u) {
+            const int64_t i = i0 + u * stride;
+            r[u] = i < per_head8 ? xh[i] : make_uint4(0u, 0u, 0u, 0u);
+        }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) m = max(m, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
+        for (int u = 0; u < VMAX_PER; ++u) {
+            const uint32_t w[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) m = max(m, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
+        }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
@@ -532,7 +536,7 @@ hipError_t launch_planes(const Prob& p, const void* k, const void* v, u16* k_hi,
         const int64_t ph8 = (int64_t)p.N * p.D / 8;
         hipError_t e = fill_i32((int32_t*)vmax, p.BH, 0, s);
         if (e != hipSuccess) return e;
-        const unsigned gx = (unsigned)((ph8 + 256 * VMAX_PER - 1) / (256 * VMAX_PER));
+        const unsigned gx = (unsigned)std::min<int64_t>(VMAX_WG, (ph8 + 256 * VMAX_PER - 1) / (256 * VMAX_PER));
         hipLaunchKernelGGL(vmax_kernel, dim3(gx, p.BH), dim3(256), 0, s, (const u16*)v, ph8, vmax);
         hipLaunchKernelGGL(planes_f16_kernel, dim3((unsigned)((ph8 + 255) / 256), p.BH), dim3(256), 0, s,
                            (const u16*)v, ph8, (const uint32_t*)vmax, v_hi);
