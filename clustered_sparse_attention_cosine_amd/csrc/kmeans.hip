@@ -325,6 +325,7 @@ hipError_t launch_init_sample(const Prob& p, const void* x, int normalize, RowSe
 constexpr int KPP_THREADS = 1024;
 constexpr int KPP_CH = 2048;                 // f64 values per LDS chunk
 constexpr int KPP_MAXCH = (1 << 21) / KPP_CH;  // chunks for the largest N
+constexpr int KPP_FAST = 4096;  // up to this many rows D^2 and its running sums stay in LDS
 
 template <typename T>
 __device__ __forceinline__ void kpp_row(const T* x, const float* xf, int N, int D, int bh, int64_t tok,
@@ -346,13 +347,17 @@ __global__ __launch_bounds__(KPP_THREADS) void init_kmeanspp_kernel(const T* __r
 #pragma clang fp contract(off)
     __shared__ double chunk[KPP_CH];
     __shared__ double cstart[KPP_MAXCH + 1];
+    // n <= KPP_FAST: D^2 of every row and the running sums, in LDS for the whole init
+    __shared__ double d2f[KPP_FAST], pre[KPP_FAST];
     __shared__ float cvec[128];
     __shared__ int64_t sh_idx;
     __shared__ int sh_first;
+    __shared__ double sh_S;
     const int bh = blockIdx.x;
     const int tid = threadIdx.x;
     if (rs.active && !rs.active[bh]) return;
     const int n = rs.nrows ? rs.nrows[bh] : N;
+    const bool fast = n <= KPP_FAST;
     const int cm = n < cv.m ? n : cv.m;
     double* d2 = d2g + (int64_t)bh * N;
     uint8_t* chosen = chosen_g + (int64_t)bh * N;
@@ -363,6 +368,53 @@ __global__ __launch_bounds__(KPP_THREADS) void init_kmeanspp_kernel(const T* __r
     for (int t = 0; t < cm; ++t) {
         if (t == 0) {
             if (tid == 0) sh_idx = (int64_t)(sm64_at(strm, 0) % (uint64_t)n);
+        } else if (fast) {
+            // running sums in row order (thread 0, the LDS reads 16 ahead of the
+            // adds), each kept; the sums never decrease (D^2 >= 0), so the first
+            // row whose sum exceeds u is the number of sums <= u
+            if (tid == 0) {
+                double run = 0.0;
+                int i = 0;
+                for (; i + 16 <= n; i += 16) {
+                    double v[16];
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) v[j] = d2f[i + j];
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        run += v[j];
+                        pre[i + j] = run;
+                    }
+                }
+                for (; i < n; ++i) {
+                    run += d2f[i];
+                    pre[i] = run;
+                }
+                sh_S = run;
+                sh_first = n;
+            }
+            __syncthreads();
+            const double S = sh_S;
+            if (S == 0.0) {
+                // the smallest row not chosen yet
+                int first = n;
+                for (int i = tid; i < n; i += KPP_THREADS)
+                    if (!chosen[i]) { first = i; break; }
+                atomicMin(&sh_first, first);
+                __syncthreads();
+                if (tid == 0) sh_idx = sh_first < n ? sh_first : -1;
+            } else {
+                const double u = (double)(sm64_at(strm, (uint64_t)t) >> 11) * 0x1.0p-53 * S;
+                int cnt = 0;
+                for (int i = tid; i < n; i += KPP_THREADS) cnt += pre[i] <= u ? 1 : 0;
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+                __syncthreads();  // every thread has read sh_first above
+                if (tid == 0) sh_first = 0;
+                __syncthreads();
+                if ((tid & 63) == 0) atomicAdd(&sh_first, cnt);
+                __syncthreads();
+                if (tid == 0) sh_idx = min(sh_first, n - 1);
+            }
         } else {
             // running sums in row order, chunk by chunk through LDS
             double run = 0.0;
@@ -477,7 +529,11 @@ __global__ __launch_bounds__(KPP_THREADS) void init_kmeanspp_kernel(const T* __r
                     sacc += df * df;
                 }
             }
-            if (t == 0 || sacc < d2[i]) d2[i] = sacc;
+            if (fast) {
+                if (t == 0 || sacc < d2f[i]) d2f[i] = sacc;
+            } else if (t == 0 || sacc < d2[i]) {
+                d2[i] = sacc;
+            }
         }
         __syncthreads();
     }
