@@ -558,23 +558,29 @@ hipError_t launch_init_kmeanspp(const Prob& p, const void* x, const float* xf, R
 }
 
 // ------------------------------------------------------------------ finalize / prep
-// One wave per slot: optional move to the member mean, then bf16 hi/lo split
-// and the squared norm (+inf where the slot holds no centre). The members of
-// slot j are the sorted rows [soff[j], soff[j + 1]); their sum is in sums[j]
-// when one wave of the update covered them all, else it is the end part of
-// the first wave plus the start parts of the later ones, added in wave order.
+// Sixteen lanes per slot, four slots per wave (lane L of a group holds
+// dimensions 4L .. 4L + 3, and 64 + 4L .. 67 + 4L at D = 128, as 16-byte
+// accesses): optional move to the member mean, then bf16 hi/lo split and the
+// squared norm (+inf where the slot holds no centre). The members of slot j
+// are the sorted rows [soff[j], soff[j + 1]); their sum is in sums[j] when one
+// wave of the update covered them all, else it is the end part of the first
+// wave plus the start parts of the later ones, added in wave order. The f64
+// norms and drifts are summed in a fixed order (each lane's dimensions, then
+// the group's lanes by a butterfly).
+constexpr int FIN_LANES = 16;
 template <int D>
 __global__ __launch_bounds__(256) void finalize_kernel(CentView cv, const uint8_t* active,
                                                        const int32_t* __restrict__ soff, float* drift,
                                                        int32_t* zero_a, int32_t* zero_b, int32_t* zero_c,
                                                        float* __restrict__ rad,
                                                        const float* __restrict__ part_rad) {
+    constexpr int E = D / 64;  // float4 chunks per lane
     const int bh = blockIdx.y;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int j = blockIdx.x * 4 + w;
+    const int l = threadIdx.x & (FIN_LANES - 1);
+    const int j = blockIdx.x * (256 / FIN_LANES) + (threadIdx.x / FIN_LANES);
     if (active && !active[bh]) return;
     if (j >= cv.m) return;
-    if (j == 0 && threadIdx.x == 0) {
+    if (j == 0 && l == 0) {
         // per-head counters of the next round (flag lists, rows to redo), so that
         // no separate clearing launch sits between the rounds
         if (zero_a) zero_a[bh] = 0;
@@ -583,7 +589,14 @@ __global__ __launch_bounds__(256) void finalize_kernel(CentView cv, const uint8_
     }
     const int64_t slot = (int64_t)bh * cv.cap + cv.base + j;
     float* c = cv.cent + slot * D;
-    constexpr int E = D / 64;
+    auto group_sum = [](double v) {
+#pragma unroll
+        for (int o = 1; o < FIN_LANES; o <<= 1) v += __shfl_xor(v, o);
+        return v;
+    };
+    float4 cur[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) cur[e] = *reinterpret_cast<const float4*>(c + 64 * e + 4 * l);
     if (soff) {
         const int32_t* so = soff + (int64_t)bh * (cv.m + 1);
         const int s0 = so[j], s1 = so[j + 1];
@@ -591,17 +604,25 @@ __global__ __launch_bounds__(256) void finalize_kernel(CentView cv, const uint8_
         double dd = 0.0;
         if (n > 0) {
             const int w1 = s0 >> 6, w2 = (s1 - 1) >> 6;
-            float acc[E];
+            float4 acc[E];
             if (w1 == w2) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[e] = cv.sums[slot * D + l + 64 * e];
+                for (int e = 0; e < E; ++e)
+                    acc[e] = *reinterpret_cast<const float4*>(cv.sums + slot * D + 64 * e + 4 * l);
             } else {
                 const float* pb = cv.part + (int64_t)bh * cv.nwav * 2 * D;
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[e] = pb[((int64_t)w1 * 2 + 1) * D + l + 64 * e];
+                for (int e = 0; e < E; ++e)
+                    acc[e] = *reinterpret_cast<const float4*>(pb + ((int64_t)w1 * 2 + 1) * D + 64 * e + 4 * l);
                 for (int ww = w1 + 1; ww <= w2; ++ww)
 #pragma unroll
-                    for (int e = 0; e < E; ++e) acc[e] += pb[((int64_t)ww * 2) * D + l + 64 * e];
+                    for (int e = 0; e < E; ++e) {
+                        const float4 q = *reinterpret_cast<const float4*>(pb + ((int64_t)ww * 2) * D + 64 * e + 4 * l);
+                        acc[e].x += q.x;
+                        acc[e].y += q.y;
+                        acc[e].z += q.z;
+                        acc[e].w += q.w;
+                    }
                 if (rad && l == 0) {
                     // the radius of a cluster over several update waves: the largest part
                     const float* pr = part_rad + (int64_t)bh * cv.nwav * 2;
@@ -610,12 +631,18 @@ __global__ __launch_bounds__(256) void finalize_kernel(CentView cv, const uint8_
                     rad[slot] = r;
                 }
             }
+            const float fn = (float)n;
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                const float nv = acc[e] / (float)n;
-                const double df = (double)(nv - c[l + 64 * e]);
-                dd += df * df;
-                c[l + 64 * e] = nv;
+                const float nv[4] = {acc[e].x / fn, acc[e].y / fn, acc[e].z / fn, acc[e].w / fn};
+                const float ov[4] = {cur[e].x, cur[e].y, cur[e].z, cur[e].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const double df = (double)(nv[i] - ov[i]);
+                    dd += df * df;
+                }
+                cur[e] = make_float4(nv[0], nv[1], nv[2], nv[3]);
+                *reinterpret_cast<float4*>(c + 64 * e + 4 * l) = cur[e];
             }
         } else if (rad && l == 0) {
             rad[slot] = 0.0f;
@@ -623,28 +650,35 @@ __global__ __launch_bounds__(256) void finalize_kernel(CentView cv, const uint8_
         if (drift) {
             // ||new - old|| from the f32 differences (each within 2^-24 of
             // itself), rounded up by a margin
-            dd = wave_sum_d(dd);
+            dd = group_sum(dd);
             if (l == 0) drift[slot] = cv.valid[slot] ? (float)sqrt(dd) * (1.0f + 0x1.0p-20f) : 0.0f;
         }
     }
     double ss = 0.0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        float v = c[l + 64 * e];
-        u16 h = f2bf_bits(v);
-        u16 lo = f2bf_bits(v - bf_bits2f(h));
-        cv.c_hi[slot * D + l + 64 * e] = h;
-        cv.c_lo[slot * D + l + 64 * e] = lo;
-        ss += (double)v * (double)v;
+        const float v[4] = {cur[e].x, cur[e].y, cur[e].z, cur[e].w};
+        u16 h[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            h[i] = f2bf_bits(v[i]);
+            lo[i] = f2bf_bits(v[i] - bf_bits2f(h[i]));
+            ss += (double)v[i] * (double)v[i];
+        }
+        *reinterpret_cast<uint2*>(cv.c_hi + slot * D + 64 * e + 4 * l) =
+            make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+        *reinterpret_cast<uint2*>(cv.c_lo + slot * D + 64 * e + 4 * l) =
+            make_uint2((uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16));
     }
-    ss = wave_sum_d(ss);
+    ss = group_sum(ss);
     if (l == 0) cv.cn2[slot] = cv.valid[slot] ? (float)ss : INFINITY;
 }
 
 hipError_t launch_finalize(const Prob& p, CentView cv, const uint8_t* active, const int32_t* soff,
                            hipStream_t s, float* drift, int32_t* zero_a, int32_t* zero_b,
                            int32_t* zero_c, float* rad, const float* part_rad) {
-    dim3 grid((unsigned)((cv.m + 3) / 4), (unsigned)p.BH);
+    constexpr int SPB = 256 / FIN_LANES;  // slots per workgroup
+    dim3 grid((unsigned)((cv.m + SPB - 1) / SPB), (unsigned)p.BH);
     if (p.D == 64)
         hipLaunchKernelGGL(finalize_kernel<64>, grid, dim3(256), 0, s, cv, active, soff, drift,
                            zero_a, zero_b, zero_c, rad, part_rad);

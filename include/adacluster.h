@@ -23,6 +23,10 @@
  *     stream). All work is enqueued on it; no call synchronises the host or
  *     copies device data to the host. Outputs are valid when the stream
  *     reaches the end of the call.
+ *   - Alignment: rows and centres are read and written with 16-byte
+ *     accesses, so tensor pointers are expected to be 16-byte aligned (as
+ *     every hipMalloc and PyTorch allocation is); a less aligned pointer is
+ *     still read correctly but slowly.
  *   - Workspace: any device address; the library aligns its pieces itself
  *     (the *_workspace() sizes include the slack for that).
  *   - Determinism: identical inputs, parameters and shapes give bitwise
