@@ -699,7 +699,9 @@ hipError_t launch_finalize(const Prob& p, CentView cv, const uint8_t* active, co
 // ||c_j||^2) gives a lower bound: j joins a's set when that bound is at most
 // (2 R)^2 (1 + 2^-12) with R rounded up, so every slot the lemma does not
 // exclude is kept. Slots without a centre join no set and have none; only the
-// words of slots below the count are written (and read).
+// words of slots below the count are written (and read). The tiles j are split
+// over gridDim.z workgroups (each writes its own words), so that a head's few
+// 64-slot blocks a still give the chip enough workgroups.
 template <int D>
 __global__ __launch_bounds__(256) void cand_bits_kernel(CentView cv, const int32_t* __restrict__ mcount,
                                                         const float* __restrict__ rad,
@@ -725,13 +727,16 @@ __global__ __launch_bounds__(256) void cand_bits_kernel(CentView cv, const int32
         ah[kc] = ld_bf16x8(cv.c_hi + (sbase + ac) * D + kc * 32 + g * 8);
         al[kc] = ld_bf16x8(cv.c_lo + (sbase + ac) * D + kc * 32 + g * 8);
     }
+    const int jtiles = ((M + 63) / 64 + gridDim.z - 1) / gridDim.z;
+    const int jb0 = blockIdx.z * jtiles * 64, jb1 = min(M, jb0 + jtiles * 64);
+    if (jb0 >= jb1) return;
     const float na2 = cv.cn2[sbase + ac];
     float lim = -INFINITY;  // no set for slots without a centre or past the count
     if (a < MA && na2 < INFINITY) {
         const float R = (rad[sbase + a] + (drift ? drift[sbase + a] : 0.0f)) * (1.0f + 0x1.0p-20f);
         lim = 4.0f * R * R * (1.0f + 0x1.0p-12f);
     }
-    for (int j0 = 0; j0 < M; j0 += 64) {
+    for (int j0 = jb0; j0 < jb1; j0 += 64) {
         __syncthreads();
         for (int i = tid; i < 64 * (D / 8); i += 256) {
             const int r = i / (D / 8), c = (i % (D / 8)) * 8;
@@ -778,7 +783,10 @@ hipError_t launch_cand_bits(const Prob& p, CentView cv, const int32_t* mcount, c
                             const float* drift, uint32_t* cbits, int cwords, hipStream_t s, int am) {
     if (am < 0 || am > cv.m) am = cv.m;
     if (am == 0) return hipSuccess;
-    dim3 grid((unsigned)((am + 63) / 64), (unsigned)p.BH);
+    // split the j tiles so that the grid has about 2048 workgroups (at most 8 splits)
+    const int ablocks = (am + 63) / 64;
+    const int js = std::max(1, std::min(8, (2048 + ablocks * p.BH - 1) / (ablocks * p.BH)));
+    dim3 grid((unsigned)ablocks, (unsigned)p.BH, (unsigned)js);
     if (p.D == 64)
         hipLaunchKernelGGL(cand_bits_kernel<64>, grid, dim3(256), 0, s, cv, mcount, rad, drift, cbits, cwords, am);
     else
