@@ -470,8 +470,15 @@ def test_lloyd_rounds_are_exact_assignments(case, tensor):
 
 
 # ----------------------------------------------------------------- key clustering
-def test_cluster_k_fixed_first_round_kmeanspp():
-    w, g = _inputs("tiny")
+# 4096 rows: the init keeps D^2 and its running sums in LDS; 5120 rows (one head):
+# it streams them through LDS in chunks and re-adds the crossing chunk
+@pytest.mark.parametrize("grid,H", [(None, None), ((5, 32, 32), 1)])
+def test_cluster_k_fixed_first_round_kmeanspp(grid, H):
+    if grid is None:
+        w, g = _inputs("tiny")
+    else:
+        w = small_workload("tiny", grid=grid, H=H)
+        g = synth.generate(w, seed=0)
     K = adc.cluster_k(dev(g["k"]), dev(g["v"]), w.k_base, iters=1, adaptive=False, init="kmeanspp")
     lab = host(K["assign"])
     for h in range(w.H):
