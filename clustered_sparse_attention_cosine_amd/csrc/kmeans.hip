@@ -1632,7 +1632,9 @@ hipError_t launch_assign(const Prob& p, const void* x, RowSet rs, const float* i
     dim3 cgrid((unsigned)cbx, (unsigned)p.BH, (unsigned)((tiles + CAND_TPS - 1) / CAND_TPS));
     launch_assign_t<true, false>(p, cgrid, x, rs, inv_norm, normalize, cv, mcount, labels, fs, CAND_TPS, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const dim3 egrid(32, (unsigned)p.BH);
+    // 16 flagged rows per workgroup step; 128 workgroups per head take the usual
+    // 1-3 % of the rows in one step each
+    const dim3 egrid(128, (unsigned)p.BH);
     if (p.bf16) {
         auto k = p.D == 64 ? cand_exact_kernel<u16, 64> : cand_exact_kernel<u16, 128>;
         hipLaunchKernelGGL(k, egrid, dim3(256), 0, s, (const u16*)x, p.N, normalize, rs, cv, fs, labels);
